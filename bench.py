@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of fused linear cross-entropy forward + backward on one MI355X.
+
+Workload: the large-vocabulary case -- h bf16 [2, 4096, 4096] ~ N(0, 1),
+W bf16 [131072, 4096] ~ N(0, 0.02), Zipf(1.1) labels, the first quarter of
+each sequence ignored, reduction 'mean' (N = 8192 tokens, H = 4096,
+V = 131072). Synthetic, seeded, generated on the host and copied to HBM
+before the timed region. One step = one call of flce_forward_backward
+(label scan, forward GEMM + log-sum-exp, merge + loss, and per vocabulary
+chunk the logit-gradient GEMM, the dW GEMM and the dH GEMM).
+
+Prints one JSON line (the last line of stdout). `value` is tokens/s of the
+whole step; `roofline` covers the kernel with the largest share of the step
+time, timed with HIP events on the stream it runs on; `cpu_baseline` times
+the float64 oracle on a bounded token sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FLCE fwd+bwd tokens/sec @ H=4096,V=131072 bf16; % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0
+GEMM_KINDS = ("lse_fwd_gemm", "grad_logits_gemm", "dW_gemm", "dH_gemm")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_large_vocab.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "lm_head_linear_amd", "csrc", f)
+                  for f in ("kernels_bf16.hip", "kernels_common.hip", "flce_api.hip",
+                            "flce_check.cpp", "flce_plan.h", "flce_internal.h")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str):
+    """Per-launch HBM bytes of `kernel` from the committed counter summary, or
+    None when there is none or the kernels changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != kernel_source_digest():
+        return None
+    if vals.get("kernel_kind") != kernel:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def blas_threads() -> int:
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        n = [d["num_threads"] for d in info if d.get("user_api") == "blas"]
+        if n:
+            return int(n[0])
+    except Exception:
+        pass
+    return os.cpu_count() or 1
+
+
+def cpu_baseline(w, n_sample: int):
+    """The float64 oracle, as it stands, on every (N // n_sample)-th token of the
+    workload with the full weight; tokens/s = sampled tokens / oracle time."""
+    import numpy as np
+    import torch
+    from oracle import flce_oracle as orc
+    N = w.N
+    stride = max(1, N // n_sample)
+    idx = torch.arange(0, N, stride)[:n_sample]
+    h = w.h.reshape(-1, w.H)[idx].to(torch.float64).numpy()
+    W = w.W.to(torch.float64).numpy()
+    y = w.labels.reshape(-1)[idx].numpy()
+    t0 = time.perf_counter()
+    r = orc.flce_reference(h, W, y, ignore_index=w.ignore_index, softcap=w.softcap,
+                           reduction=w.reduction)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(r.loss64)
+    return {
+        "value": len(idx) / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+        "sample": (f"{len(idx)} tokens (every {stride}th of the {N}) with the full W "
+                   f"[{w.V},{w.H}]: one float64 forward+backward of the oracle in {dt:.1f} s; "
+                   "bf16->float64 widening not timed"),
+        "seconds": dt,
+    }
+
+
+def copy_calibration(size_mib: int, reps: int):
+    """A plain device copy of known size, to scale the HBM byte counters."""
+    import torch
+    n = size_mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} copies of {size_mib} MiB")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="do not bracket kernels with events in the timed region")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
+                    help="only run a plain copy of this size (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 10)
+        return
+
+    import flce_inputs as fi
+    import lm_head_linear_amd as m
+    from lm_head_linear_amd import _lib
+    _lib.load()
+
+    dev = torch.device("cuda:0")
+    t = time.perf_counter()
+    w = fi.make_workload(3)
+    N, H, V = w.N, w.H, w.V
+    log(f"workload {w.name}: N={N} H={H} V={V} generated in {time.perf_counter() - t:.1f} s")
+    h = w.h.reshape(N, H).to(dev)
+    W = w.W.to(dev)
+    y = w.labels.reshape(N).to(dev)
+    dH = torch.empty_like(h)
+    dW = torch.empty_like(W)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    nt = torch.empty((), dtype=torch.int64, device=dev)
+    ws_bytes = m.flce_workspace_size(N, H, V, W.dtype)
+    torch.cuda.synchronize()
+    base_mem = torch.cuda.memory_allocated(dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def step():
+        m.flce_forward_backward(h, W, y, ignore_index=w.ignore_index, softcap=w.softcap,
+                                reduction=w.reduction, dH=dH, dW=dW, workspace=ws, loss=loss,
+                                num_tokens=nt)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps); loss={loss.item():.6f} num_tokens={nt.item()}")
+
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    timing = not args.no_kernel_timing
+    if timing:
+        m.flce_profile_begin()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if timing:
+        m.flce_profile_end()
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    peak_extra = torch.cuda.max_memory_allocated(dev) - base_mem
+    log(f"timed {args.steps} steps: {wall_ms:.3f} ms/step (host clock), {ev_ms:.3f} ms/step (events)")
+
+    nhv = float(N) * H * V
+    tflops_8 = 8 * nhv / (wall_ms * 1e-3) / 1e12
+    tflops_6 = 6 * nhv / (wall_ms * 1e-3) / 1e12
+    kernels = {}
+    roofline = None
+    if timing:
+        prof = m.flce_profile_query()
+        for name, (ms, n) in prof.items():
+            if n == 0:
+                continue
+            e = {"ms_per_step": ms / args.steps, "launches_per_step": n / args.steps,
+                 "avg_launch_ms": ms / n}
+            if name in GEMM_KINDS:
+                e["tflops"] = 2 * nhv * args.steps / (ms * 1e-3) / 1e12
+            kernels[name] = e
+        dom = max(GEMM_KINDS, key=lambda k: kernels.get(k, {}).get("ms_per_step", 0.0))
+        d = kernels[dom]
+        flops_per_launch = 2 * nhv / d["launches_per_step"]
+        achieved = flops_per_launch / (d["avg_launch_ms"] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": read_traffic(dom), "kernel": dom,
+                    "flops_per_launch": flops_per_launch,
+                    "avg_launch_ms": round(d["avg_launch_ms"], 4)}
+    for k, v in kernels.items():
+        log(f"  {k:18s} {v['ms_per_step']:8.3f} ms/step  {v['launches_per_step']:.0f} launches"
+            + (f"  {v['tflops']:7.1f} TFLOP/s" if "tflops" in v else ""))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_sample_tokens} sampled tokens ...")
+        cpu = cpu_baseline(w, args.cpu_sample_tokens)
+        log(f"cpu baseline: {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC,
+        "value": round(N * args.steps / (t1 - t0), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": (f"large_vocab: h bf16 [2,4096,4096], W bf16 [131072,4096], "
+                                "Zipf(1.1) labels, first quarter of each sequence ignored, "
+                                "reduction=mean"),
+                   "N": N, "H": H, "V": V, "vocab_chunk": m.flce_vocab_chunk(N, H, V, W.dtype)},
+        "mfma_frac_8nhv": round(tflops_8 / PEAK_BF16_TFLOPS, 4),
+        "mfma_frac_6nhv": round(tflops_6 / PEAK_BF16_TFLOPS, 4),
+        "tflops_8nhv": round(tflops_8, 1),
+        "event_ms_per_step": round(ev_ms, 4),
+        "extra_memory_bytes": int(peak_extra),
+        "workspace_bytes": int(ws_bytes),
+        "roofline": roofline,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "cpu_baseline": ({k: (round(v, 3) if isinstance(v, float) else v)
+                          for k, v in cpu.items() if k != "seconds"} if cpu else None),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * flce.h -- fused linear cross-entropy (LM-head projection + token-level
+ * cross-entropy, forward and backward) on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (one call = one forward + backward pass):
+ *
+ *   Z  = h . W^T                        logits, never stored in device memory
+ *   Z' = s * tanh(Z / s)  if s > 0      softcap ("logit_softcapping", NeMo
+ *        Z                otherwise     AutoModel linear_ce page, API)
+ *   lse_i = log sum_v exp(Z'_iv)
+ *   l_i   = lse_i - Z'_{i,y_i}  if y_i != ignore_index, else 0
+ *   loss  = c * sum_i l_i                (accumulated in float64, returned fp32)
+ *   G     = c * valid * (softmax(Z') - onehot(y)) * dZ'/dZ
+ *   dH    = G . W,   dW = G^T . h
+ *
+ * with the scale c fixed by the reduction contract:
+ *   'sum'  : c = mb_scale / T if num_label_tokens T > 0, else mb_scale
+ *            (NeMo AutoModel linear_ce page, API, forward parameter
+ *            num_label_tokens: the global count normalises a sum loss)
+ *   'mean' : c = mb_scale / max(n, 1), n = number of non-ignored tokens
+ *            (the clamped count gives an empty target set loss 0, not NaN:
+ *            Ling-3.1-flash discussion 7, "Why use num_items_in_batch")
+ * and num_tokens = n for 'sum' and 0 for 'mean' (twinkle PR 335,
+ * "PR information", item 1). mb_scale is the token-weighted micro-batch scale
+ * (same PR, item 2: 1.0 for 'sum'). The loss is float32 also for bf16 inputs
+ * and no logit is ever rounded to bf16 (Modalities PR 464, "The problem" and
+ * "Tests"). The softcap is applied identically to the log-sum-exp, the target
+ * logit and the gradient (twinkle PR 335, item 3).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     keeps no pointer after a call returns and allocates no device memory.
+ *   - Matrices are dense row-major: h [N,H], W [V,H], dH [N,H], dW [V,H];
+ *     labels int64 [N]. Batch/sequence dimensions are flattened by the caller;
+ *     labels are already aligned row-for-row with h (no internal shift).
+ *   - dtype FLCE_BF16: h, W, dH, dW are bfloat16 (dH/dW rounded to nearest
+ *     even from float32 accumulators); FLCE_F32: all four are float32.
+ *   - stream is a hipStream_t (NULL = the null stream). All work is queued on
+ *     it; outputs are valid once the stream reaches that point.
+ *   - Return value: an flce_status_t. A non-OK value from the synchronous
+ *     argument checks means nothing was launched and nothing was written.
+ */
+#ifndef FLCE_H
+#define FLCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FLCE_F32 = 0, FLCE_BF16 = 1 } flce_dtype_t;
+typedef enum { FLCE_SUM = 0, FLCE_MEAN = 1 } flce_reduction_t;
+
+typedef enum {
+  FLCE_OK = 0,
+  FLCE_ERR_ARG = 1,          /* invalid argument (shape, pointer, option)   */
+  FLCE_ERR_UNSUPPORTED = 2,  /* valid but not supported (alignment, H%8)    */
+  FLCE_ERR_WORKSPACE = 3,    /* workspace missing, misaligned or too small  */
+  FLCE_ERR_HIP = 4,          /* a HIP runtime call or launch failed         */
+  FLCE_ERR_LABEL = 5         /* device-detected: a non-ignored label is
+                                outside [0, V); reported through *status     */
+} flce_status_t;
+
+/*
+ * flce_workspace_size -- bytes of device scratch that flce_forward_backward
+ * needs for this problem (256-byte aligned base required). It holds the
+ * per-tile log-sum-exp partials, the per-token lse and target logits, one
+ * vocabulary chunk of the logit gradient and (bf16, several chunks) a float32
+ * dH accumulator. Never O(N*V): the chunk is sized to at most ~256 MiB.
+ * Returns 0 for invalid sizes (N < 0, H <= 0, V <= 0, unknown dtype).
+ * Pure host arithmetic; callable without a GPU.
+ */
+size_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype);
+
+/*
+ * flce_check_args -- the synchronous argument checks of flce_forward_backward,
+ * with the same parameter list, without touching the GPU (pointers are only
+ * compared, never dereferenced). Returns FLCE_OK or the error that
+ * flce_forward_backward would return before launching anything:
+ *   FLCE_ERR_ARG         N < 0, H <= 0, V <= 0; a required pointer is NULL
+ *                        (h, W, labels, dH when N > 0; loss, num_tokens, dW
+ *                        always); unknown dtype/reduction; softcap < 0 or not
+ *                        finite; mb_scale not finite; num_label_tokens > 0
+ *                        with 'mean'; dH aliasing h or dW aliasing W.
+ *   FLCE_ERR_UNSUPPORTED bf16 with H % 8 != 0 or a matrix pointer not 16-byte
+ *                        aligned.
+ *   FLCE_ERR_WORKSPACE   workspace NULL, not 256-byte aligned, or
+ *                        workspace_bytes < flce_workspace_size(...).
+ */
+int flce_check_args(const void* h, const void* W, const int64_t* labels,
+                    int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                    float softcap, int reduction, int64_t num_label_tokens,
+                    float* loss, int64_t* num_tokens, void* dH, void* dW,
+                    void* stream, int dtype, float mb_scale, int accumulate_dW,
+                    void* workspace, size_t workspace_bytes, int32_t* status,
+                    float* lse_out);
+
+/*
+ * flce_forward_backward -- the whole fused linear cross-entropy step.
+ *
+ * Inputs  h [N,H], W [V,H], labels [N] (int64), ignore_index (compared by
+ *         equality; may name a vocabulary row), softcap s >= 0 (0 = off),
+ *         reduction (flce_reduction_t), num_label_tokens T (<= 0: absent;
+ *         only with 'sum'), dtype (flce_dtype_t), mb_scale (finite; 1.0 for
+ *         a plain call), accumulate_dW (0: dW is overwritten; 1: the computed
+ *         gradient is added to the dW already in memory, for micro-batching).
+ * Outputs *loss (fp32 scalar), *num_tokens (int64 scalar), dH [N,H],
+ *         dW [V,H], optional lse_out [N] fp32 (per-token log-sum-exp of the
+ *         softcapped logits; NULL = not written), optional *status (int32:
+ *         FLCE_OK, or FLCE_ERR_LABEL when a non-ignored label is outside
+ *         [0, V); NULL = not written). All are device pointers.
+ * Workspace caller-owned device scratch of workspace_bytes >=
+ *         flce_workspace_size(N, H, V, dtype); its contents on entry do not
+ *         matter and are garbage on exit. Two calls may run concurrently only
+ *         with distinct workspaces.
+ * Edge cases N = 0: loss 0, num_tokens 0, dW zero-filled unless
+ *         accumulate_dW. Every label ignored: loss 0 and zero gradients for
+ *         both reductions (no NaN).
+ * Data errors (detected on the device, after launch): a non-ignored label
+ *         outside [0, V) makes *status = FLCE_ERR_LABEL, *loss = NaN, that
+ *         token's dH row NaN and dW NaN (fail closed); nothing is read or
+ *         written out of bounds.
+ * Errors  see flce_check_args; FLCE_ERR_HIP if a launch fails.
+ */
+int flce_forward_backward(const void* h, const void* W, const int64_t* labels,
+                          int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                          float softcap, int reduction, int64_t num_label_tokens,
+                          float* loss, int64_t* num_tokens, void* dH, void* dW,
+                          void* stream, int dtype, float mb_scale, int accumulate_dW,
+                          void* workspace, size_t workspace_bytes, int32_t* status,
+                          float* lse_out);
+
+/* flce_status_string -- a static, human-readable name for a status code. */
+const char* flce_status_string(int status);
+
+/*
+ * flce_vocab_chunk -- the vocabulary chunk (rows of W per backward chunk) the
+ * library uses for this problem; informational (host arithmetic only).
+ */
+int64_t flce_vocab_chunk(int64_t N, int64_t H, int64_t V, int dtype);
+
+/*
+ * Per-kernel timing (diagnostics for benchmarks; not thread-safe).
+ * flce_profile_begin() clears the record and makes subsequent
+ * flce_forward_backward calls bracket every kernel launch with a pair of
+ * HIP events on the call's stream. flce_profile_end() stops recording.
+ * flce_profile_query(kind, &ms, &launches) waits for the recorded events and
+ * returns the summed elapsed milliseconds and launch count of one kernel kind
+ * (0 <= kind < flce_profile_kinds()); flce_kernel_kind_name(kind) names it.
+ * Events are created on first use and reused; no device memory is allocated.
+ */
+int flce_profile_begin(void);
+int flce_profile_end(void);
+int flce_profile_kinds(void);
+const char* flce_kernel_kind_name(int kind);
+int flce_profile_query(int kind, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H */

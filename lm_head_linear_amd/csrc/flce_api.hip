@@ -1,0 +1,151 @@
+// C-ABI entry points: argument checks, workspace carving, launch sequence,
+// optional per-kernel timing.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <vector>
+
+#include "../../include/flce.h"
+#include "flce_internal.h"
+#include "flce_plan.h"
+
+namespace {
+
+// ---- per-kernel timing ------------------------------------------------------
+struct Rec {
+  int kind;
+  hipEvent_t a, b;
+};
+struct Prof {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<Rec> recs;
+  int pending_kind = -1;
+  hipEvent_t pending = nullptr;
+  bool failed = false;
+};
+Prof g_prof;
+
+hipEvent_t take_event() {
+  if (g_prof.used == g_prof.pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) { g_prof.failed = true; return nullptr; }
+    g_prof.pool.push_back(e);
+  }
+  return g_prof.pool[g_prof.used++];
+}
+
+void prof_before(int kind, hipStream_t s) {
+  hipEvent_t e = take_event();
+  if (!e) return;
+  hipEventRecord(e, s);
+  g_prof.pending = e;
+  g_prof.pending_kind = kind;
+}
+
+void prof_after(int kind, hipStream_t s) {
+  if (!g_prof.pending || g_prof.pending_kind != kind) return;
+  hipEvent_t e = take_event();
+  if (!e) return;
+  hipEventRecord(e, s);
+  g_prof.recs.push_back(Rec{kind, g_prof.pending, e});
+  g_prof.pending = nullptr;
+}
+
+const char* kKindNames[flce::kNumKinds] = {"label_scan", "lse_fwd_gemm", "lse_merge",
+                                           "loss_final", "grad_logits_gemm", "dW_gemm",
+                                           "dH_gemm", "fill"};
+
+}  // namespace
+
+extern "C" {
+
+int flce_forward_backward(const void* h, const void* W, const int64_t* labels, int64_t N,
+                          int64_t H, int64_t V, int64_t ignore_index, float softcap,
+                          int reduction, int64_t num_label_tokens, float* loss,
+                          int64_t* num_tokens, void* dH, void* dW, void* stream, int dtype,
+                          float mb_scale, int accumulate_dW, void* workspace,
+                          size_t workspace_bytes, int32_t* status, float* lse_out) {
+  int st = flce_check_args(h, W, labels, N, H, V, ignore_index, softcap, reduction,
+                           num_label_tokens, loss, num_tokens, dH, dW, stream, dtype, mb_scale,
+                           accumulate_dW, workspace, workspace_bytes, status, lse_out);
+  if (st != FLCE_OK) return st;
+  flce::Plan p;
+  if (!flce::make_plan(N, H, V, dtype, &p)) return FLCE_ERR_ARG;
+
+  flce::Launcher L{static_cast<hipStream_t>(stream), nullptr, nullptr};
+  if (g_prof.on) { L.before = prof_before; L.after = prof_after; }
+
+  char* ws = static_cast<char*>(workspace);
+  flce::Args a{};
+  a.h = h; a.W = W; a.labels = labels;
+  a.N = N; a.H = H; a.V = V;
+  a.ignore_index = ignore_index; a.softcap = softcap; a.reduction = reduction;
+  a.num_label_tokens = num_label_tokens;
+  a.loss = loss; a.num_tokens = num_tokens; a.dH = dH; a.dW = dW;
+  a.mb_scale = mb_scale; a.accumulate_dW = accumulate_dW ? 1 : 0;
+  a.status = status; a.lse_out = lse_out;
+  a.sc = reinterpret_cast<flce::Scalars*>(ws + p.off_scalars);
+
+  hipError_t e;
+  if (N == 0) {
+    e = flce::launch_empty(p, a, L);
+    if (e == hipSuccess && !a.accumulate_dW)
+      e = flce::launch_zero_bytes(dW, size_t(V) * H * p.elem, L);
+    return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+  }
+  a.part = reinterpret_cast<float2*>(ws + p.off_part);
+  a.zt = reinterpret_cast<float*>(ws + p.off_zt);
+  a.lse = reinterpret_cast<float*>(ws + p.off_lse);
+  a.lsum = reinterpret_cast<double*>(ws + p.off_lsum);
+  a.g = ws + p.off_g;
+  a.dh_acc = p.need_dh_acc ? reinterpret_cast<float*>(ws + p.off_dhacc) : nullptr;
+
+  const bool bf16 = dtype == FLCE_BF16;
+  e = flce::launch_label_scan(p, a, L);
+  if (e == hipSuccess) e = bf16 ? flce::bf16_forward(p, a, L) : flce::f32_forward(p, a, L);
+  if (e == hipSuccess) e = flce::launch_merge_and_loss(p, a, L);
+  for (int64_t c = 0; e == hipSuccess && c < p.n_chunks; ++c)
+    e = bf16 ? flce::bf16_backward_chunk(p, a, c, L) : flce::f32_backward_chunk(p, a, c, L);
+  return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+int flce_profile_begin(void) {
+  g_prof.on = true;
+  g_prof.used = 0;
+  g_prof.recs.clear();
+  g_prof.pending = nullptr;
+  g_prof.failed = false;
+  return FLCE_OK;
+}
+
+int flce_profile_end(void) {
+  g_prof.on = false;
+  return g_prof.failed ? FLCE_ERR_HIP : FLCE_OK;
+}
+
+int flce_profile_kinds(void) { return flce::kNumKinds; }
+
+const char* flce_kernel_kind_name(int kind) {
+  return (kind >= 0 && kind < flce::kNumKinds) ? kKindNames[kind] : "unknown";
+}
+
+int flce_profile_query(int kind, double* total_ms, int64_t* launches) {
+  if (kind < 0 || kind >= flce::kNumKinds || !total_ms || !launches) return FLCE_ERR_ARG;
+  double sum = 0.0;
+  int64_t n = 0;
+  for (const Rec& r : g_prof.recs) {
+    if (r.kind != kind) continue;
+    if (hipEventSynchronize(r.b) != hipSuccess) return FLCE_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return FLCE_ERR_HIP;
+    sum += ms;
+    ++n;
+  }
+  *total_ms = sum;
+  *launches = n;
+  return FLCE_OK;
+}
+
+}  // extern "C"

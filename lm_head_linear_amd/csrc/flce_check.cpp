@@ -1,0 +1,139 @@
+// Synchronous argument checks and workspace planning (no HIP calls).
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/flce.h"
+#include "flce_plan.h"
+
+namespace flce {
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Optional override of the backward vocabulary chunk (rows of W), for tuning
+// and for tests of the multi-chunk path; 0 = automatic. Read on every plan,
+// so flce_workspace_size and flce_forward_backward must see the same value
+// (a mismatch is caught as FLCE_ERR_WORKSPACE).
+int64_t env_vchunk() {
+  const char* s = std::getenv("FLCE_VCHUNK");
+  if (!s || !*s) return 0;
+  const long long x = std::atoll(s);
+  return x > 0 ? int64_t(x) : int64_t(0);
+}
+
+}  // namespace
+
+bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p) {
+  if (N < 0 || H <= 0 || V <= 0) return false;
+  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return false;
+  // Keep every size product far from int64 overflow.
+  if (N > (int64_t(1) << 31) || H > (int64_t(1) << 24) || V > (int64_t(1) << 31)) return false;
+  Plan q;
+  q.N = N; q.H = H; q.V = V; q.dtype = dtype;
+  q.tile = dtype == FLCE_BF16 ? kTileBF16 : kTileF32;
+  q.elem = dtype == FLCE_BF16 ? 2 : 4;
+  q.n_tok_tiles = ceil_div(N, q.tile);
+  q.n_voc_tiles = ceil_div(V, q.tile);
+  q.ld_part = round_up(N > 0 ? N : 1, q.tile);
+  q.ldg = round_up(N > 0 ? N : 1, 8);
+  // Backward chunk: at most kChunkElems elements of G^T, a multiple of the
+  // tile, at least one tile, at most the (tile-rounded) vocabulary.
+  int64_t vmax = round_up(V, q.tile);
+  int64_t vc = env_vchunk();
+  if (vc <= 0) vc = (kChunkElems / (N > 0 ? q.ldg : 1)) / q.tile * q.tile;
+  else vc = round_up(vc, q.tile);
+  if (vc < q.tile) vc = q.tile;
+  if (vc > vmax) vc = vmax;
+  q.vchunk = vc;
+  q.n_chunks = ceil_div(V, vc);
+  q.n_loss_blocks = ceil_div(N > 0 ? N : 1, 256);
+  q.need_dh_acc = (dtype == FLCE_BF16) && q.n_chunks > 1 && N > 0;
+
+  size_t off = 0;
+  q.off_scalars = off; off = align256(off + sizeof(Scalars));
+  if (N > 0) {
+    q.off_part = off;  off = align256(off + size_t(q.n_voc_tiles) * q.ld_part * 2 * sizeof(float));
+    q.off_zt = off;    off = align256(off + size_t(q.ld_part) * sizeof(float));
+    q.off_lse = off;   off = align256(off + size_t(q.ld_part) * sizeof(float));
+    q.off_lsum = off;  off = align256(off + size_t(q.n_loss_blocks) * sizeof(double));
+    q.off_g = off;     off = align256(off + size_t(q.vchunk) * q.ldg * q.elem);
+    if (q.need_dh_acc) { q.off_dhacc = off; off = align256(off + size_t(N) * H * sizeof(float)); }
+  }
+  q.total = off;
+  *p = q;
+  return true;
+}
+
+}  // namespace flce
+
+extern "C" {
+
+size_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype) {
+  flce::Plan p;
+  if (!flce::make_plan(N, H, V, dtype, &p)) return 0;
+  return p.total;
+}
+
+int64_t flce_vocab_chunk(int64_t N, int64_t H, int64_t V, int dtype) {
+  flce::Plan p;
+  if (!flce::make_plan(N, H, V, dtype, &p)) return 0;
+  return p.vchunk;
+}
+
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  auto x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int flce_check_args(const void* h, const void* W, const int64_t* labels,
+                    int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                    float softcap, int reduction, int64_t num_label_tokens,
+                    float* loss, int64_t* num_tokens, void* dH, void* dW,
+                    void* stream, int dtype, float mb_scale, int accumulate_dW,
+                    void* workspace, size_t workspace_bytes, int32_t* status,
+                    float* lse_out) {
+  (void)ignore_index; (void)stream; (void)accumulate_dW; (void)status; (void)lse_out;
+  if (N < 0 || H <= 0 || V <= 0) return FLCE_ERR_ARG;
+  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_ERR_ARG;
+  if (reduction != FLCE_SUM && reduction != FLCE_MEAN) return FLCE_ERR_ARG;
+  if (!(softcap >= 0.0f) || !std::isfinite(softcap)) return FLCE_ERR_ARG;
+  if (!std::isfinite(mb_scale)) return FLCE_ERR_ARG;
+  if (reduction == FLCE_MEAN && num_label_tokens > 0) return FLCE_ERR_ARG;
+  if (!loss || !num_tokens || !W || !dW) return FLCE_ERR_ARG;
+  if (N > 0 && (!h || !labels || !dH)) return FLCE_ERR_ARG;
+  flce::Plan p;
+  if (!flce::make_plan(N, H, V, dtype, &p)) return FLCE_ERR_ARG;
+  const size_t es = p.elem;
+  if (overlaps(dH, size_t(N) * H * es, h, size_t(N) * H * es)) return FLCE_ERR_ARG;
+  if (overlaps(dW, size_t(V) * H * es, W, size_t(V) * H * es)) return FLCE_ERR_ARG;
+  if (dtype == FLCE_BF16) {
+    if (H % 8 != 0) return FLCE_ERR_UNSUPPORTED;
+    auto mis = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) != 0; };
+    if (mis(W) || mis(dW) || (N > 0 && (mis(h) || mis(dH)))) return FLCE_ERR_UNSUPPORTED;
+  } else {
+    auto mis = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 3u) != 0; };
+    if (mis(W) || mis(dW) || (N > 0 && (mis(h) || mis(dH)))) return FLCE_ERR_UNSUPPORTED;
+  }
+  if (!workspace) return FLCE_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FLCE_ERR_WORKSPACE;
+  if (workspace_bytes < p.total) return FLCE_ERR_WORKSPACE;
+  return FLCE_OK;
+}
+
+const char* flce_status_string(int s) {
+  switch (s) {
+    case FLCE_OK: return "FLCE_OK";
+    case FLCE_ERR_ARG: return "FLCE_ERR_ARG: invalid argument";
+    case FLCE_ERR_UNSUPPORTED: return "FLCE_ERR_UNSUPPORTED: unsupported shape or alignment";
+    case FLCE_ERR_WORKSPACE: return "FLCE_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case FLCE_ERR_HIP: return "FLCE_ERR_HIP: HIP runtime error";
+    case FLCE_ERR_LABEL: return "FLCE_ERR_LABEL: non-ignored label outside [0, V)";
+    default: return "FLCE: unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Internal launch interface between the C-ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "flce_plan.h"
+
+namespace flce {
+
+// Kernel kinds, for per-kernel timing.
+enum Kind : int {
+  kLabelScan = 0,
+  kLseFwd = 1,
+  kLseMerge = 2,
+  kLossFinal = 3,
+  kGradLogits = 4,
+  kGemmDW = 5,
+  kGemmDH = 6,
+  kFill = 7,
+  kNumKinds = 8,
+};
+
+// Everything one call needs on the device side.
+struct Args {
+  const void* h;
+  const void* W;
+  const int64_t* labels;
+  int64_t N, H, V;
+  int64_t ignore_index;
+  float softcap;
+  int reduction;
+  int64_t num_label_tokens;
+  float* loss;
+  int64_t* num_tokens;
+  void* dH;
+  void* dW;
+  float mb_scale;
+  int accumulate_dW;
+  int32_t* status;
+  float* lse_out;
+  // carved workspace
+  Scalars* sc;
+  float2* part;
+  float* zt;
+  float* lse;
+  double* lsum;
+  void* g;        // G^T chunk [vchunk][ldg]
+  float* dh_acc;  // [N][H] (bf16 path with several chunks)
+};
+
+// Launch hook: the C-ABI layer brackets launches with timing events.
+struct Launcher {
+  hipStream_t stream;
+  void (*before)(int kind, hipStream_t s);
+  void (*after)(int kind, hipStream_t s);
+  void pre(int kind) const { if (before) before(kind, stream); }
+  void post(int kind) const { if (after) after(kind, stream); }
+};
+
+// Common kernels (dtype independent).
+hipError_t launch_empty(const Plan& p, const Args& a, const Launcher& L);
+hipError_t launch_label_scan(const Plan& p, const Args& a, const Launcher& L);
+hipError_t launch_merge_and_loss(const Plan& p, const Args& a, const Launcher& L);
+hipError_t launch_zero_bytes(void* ptr, size_t bytes, const Launcher& L);
+
+// bf16 MFMA path.
+hipError_t bf16_forward(const Plan& p, const Args& a, const Launcher& L);
+hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, const Launcher& L);
+
+// float32 path.
+hipError_t f32_forward(const Plan& p, const Args& a, const Launcher& L);
+hipError_t f32_backward_chunk(const Plan& p, const Args& a, int64_t chunk, const Launcher& L);
+
+}  // namespace flce

@@ -1,0 +1,49 @@
+// Host-side problem plan for fused linear cross-entropy: tile counts, the
+// backward vocabulary chunk and the carving of the caller's workspace.
+// HIP-free so that it builds and is unit-tested on a machine without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace flce {
+
+// Tile edge of the bf16 MFMA kernels (tokens x vocab and vocab/tokens x hidden).
+constexpr int64_t kTileBF16 = 256;
+// Tile edge of the float32 kernels.
+constexpr int64_t kTileF32 = 64;
+// Upper bound on the elements of one chunk of the logit gradient G^T.
+constexpr int64_t kChunkElems = int64_t(1) << 27;
+
+// Scalars shared by the kernels of one call (first 256 bytes of the workspace).
+struct Scalars {
+  int64_t n_valid;    // non-ignored tokens
+  int64_t n_bad;      // non-ignored tokens whose label is outside [0, V)
+  double c64;         // loss = c64 * sum of per-token losses
+  float c32;          // the same factor for the gradient epilogue
+  int32_t pad0;
+  double reserved[4];
+};
+
+struct Plan {
+  int64_t N = 0, H = 0, V = 0;
+  int dtype = 0;
+  int64_t tile = 0;     // tile edge for this dtype
+  int64_t n_tok_tiles = 0;   // ceil(N / tile)
+  int64_t n_voc_tiles = 0;   // ceil(V / tile), forward partials per token
+  int64_t ld_part = 0;       // tokens per partial row (multiple of tile)
+  int64_t ldg = 0;           // leading dimension of G^T (tokens, multiple of 8)
+  int64_t vchunk = 0;        // vocabulary rows per backward chunk
+  int64_t n_chunks = 0;
+  int64_t n_loss_blocks = 0; // blocks of the lse-merge kernel (256 tokens each)
+  bool need_dh_acc = false;  // float32 dH accumulator needed (bf16, >1 chunk)
+  size_t elem = 0;           // bytes per element of h/W/G
+  // byte offsets into the workspace
+  size_t off_scalars = 0, off_part = 0, off_zt = 0, off_lse = 0, off_lsum = 0,
+         off_g = 0, off_dhacc = 0, total = 0;
+};
+
+// Builds the plan; returns false for invalid sizes or dtype.
+bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p);
+
+}  // namespace flce

@@ -1,0 +1,51 @@
+// Host-only driver for the argument checks and the workspace planner; built
+// with AddressSanitizer and UndefinedBehaviorSanitizer by the CPU tests.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <initializer_list>
+#include <limits>
+
+#include "flce.h"
+
+static int failures = 0;
+#define EXPECT(cond)                                              \
+  do {                                                            \
+    if (!(cond)) { std::printf("FAIL %s:%d %s\n", __FILE__, __LINE__, #cond); ++failures; } \
+  } while (0)
+
+static int call(int64_t N, int64_t H, int64_t V, int dtype, int red, int64_t T, float s,
+                float mb, size_t wsb, uintptr_t ws = uintptr_t(1) << 40) {
+  const uintptr_t b = uintptr_t(1) << 32;
+  return flce_check_args((void*)b, (void*)(b * 2), (int64_t*)(b * 3), N, H, V, -100, s, red, T,
+                         (float*)(b * 4), (int64_t*)(b * 5), (void*)(b * 6), (void*)(b * 7),
+                         nullptr, dtype, mb, 0, (void*)ws, wsb, nullptr, nullptr);
+}
+
+int main() {
+  const size_t big = size_t(1) << 40;
+  EXPECT(call(8192, 4096, 131072, FLCE_BF16, FLCE_MEAN, 0, 0.f, 1.f, big) == FLCE_OK);
+  EXPECT(call(8192, 4096, 131072, FLCE_BF16, FLCE_MEAN, 5, 0.f, 1.f, big) == FLCE_ERR_ARG);
+  EXPECT(call(1, 12, 5, FLCE_BF16, FLCE_SUM, 0, 0.f, 1.f, big) == FLCE_ERR_UNSUPPORTED);
+  EXPECT(call(1, 12, 5, FLCE_F32, FLCE_SUM, 0, 0.f, 1.f, big) == FLCE_OK);
+  EXPECT(call(1, 8, 5, FLCE_BF16, FLCE_SUM, 0, -0.5f, 1.f, big) == FLCE_ERR_ARG);
+  EXPECT(call(1, 8, 5, FLCE_BF16, FLCE_SUM, 0, std::numeric_limits<float>::quiet_NaN(), 1.f,
+              big) == FLCE_ERR_ARG);
+  EXPECT(call(1, 8, 5, FLCE_BF16, FLCE_SUM, 0, 0.f, INFINITY, big) == FLCE_ERR_ARG);
+  EXPECT(call(1, 8, 5, FLCE_BF16, FLCE_SUM, 0, 0.f, 1.f, 10) == FLCE_ERR_WORKSPACE);
+  EXPECT(call(1, 8, 5, FLCE_BF16, FLCE_SUM, 0, 0.f, 1.f, big, 4096 + 16) == FLCE_ERR_WORKSPACE);
+  // extreme sizes are refused, never overflow
+  EXPECT(call(int64_t(1) << 40, 8, 5, FLCE_BF16, FLCE_SUM, 0, 0.f, 1.f, big) == FLCE_ERR_ARG);
+  EXPECT(call(8, int64_t(1) << 40, 5, FLCE_BF16, FLCE_SUM, 0, 0.f, 1.f, big) == FLCE_ERR_ARG);
+  EXPECT(flce_workspace_size(INT64_MAX, INT64_MAX, INT64_MAX, FLCE_BF16) == 0);
+  for (int64_t n : {0, 1, 7, 255, 256, 257, 4096, 16384})
+    for (int64_t v : {1, 2, 255, 256, 257, 32000, 131072, 256000}) {
+      const size_t w = flce_workspace_size(n, 64, v, FLCE_BF16);
+      EXPECT(w > 0 && w % 256 == 0);
+      const int64_t c = flce_vocab_chunk(n, 64, v, FLCE_BF16);
+      EXPECT(c >= 256 && c % 256 == 0);
+    }
+  for (int s = -1; s < 8; ++s) EXPECT(flce_status_string(s) != nullptr);
+  if (failures == 0) std::printf("all checks passed\n");
+  return failures ? 1 : 0;
+}

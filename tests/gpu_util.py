@@ -1,0 +1,91 @@
+"""Helpers shared by the GPU parity tests: run the HIP path, run the oracle on
+the same seeded values, compare to the stated tolerances."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import flce_inputs as fi
+from oracle import flce_oracle as orc
+
+# Tolerances (written here, used by every parity test):
+#   loss       |gpu - ref| <= 1e-5 * |ref|   (exactly 0 when ref is 0)
+#   bf16 grads max|gpu - ref| <= 2e-2 * max|ref| per tensor
+#   fp32 grads max|gpu - ref| <= 1e-4 * max|ref| per tensor
+#   num_tokens bit-exact; ignored rows of dH exactly zero
+LOSS_RTOL = 1e-5
+GRAD_TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
+
+
+def device():
+    return torch.device("cuda:0")
+
+
+def to_np64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def run_gpu(w: fi.Workload, *, mb_scale=1.0, lse=True, dev=None, **kw):
+    import lm_head_linear_amd as m
+    dev = dev or device()
+    H = w.H
+    h = w.h.reshape(-1, H).to(dev)
+    W = w.W.to(dev)
+    y = w.labels.reshape(-1).to(dev)
+    lse_out = torch.full((h.shape[0],), float("nan"), dtype=torch.float32, device=dev) if lse else None
+    status = torch.full((), -1, dtype=torch.int32, device=dev)
+    args = dict(ignore_index=w.ignore_index, softcap=w.softcap, reduction=w.reduction,
+                num_label_tokens=w.num_label_tokens, mb_scale=mb_scale, lse_out=lse_out,
+                status=status)
+    args.update(kw)
+    loss, nt, dH, dW = m.flce_forward_backward(h, W, y, **args)
+    torch.cuda.synchronize(dev)
+    return dict(loss=float(loss.item()), loss_t=loss, num_tokens=int(nt.item()), dH=dH, dW=dW,
+                lse=lse_out, status=int(status.item()))
+
+
+def run_oracle(w: fi.Workload, *, mb_scale=1.0, **kw):
+    h = w.h.reshape(-1, w.H).to(torch.float64).numpy()
+    W = w.W.to(torch.float64).numpy()
+    y = w.labels.reshape(-1).numpy()
+    args = dict(ignore_index=w.ignore_index, softcap=w.softcap, reduction=w.reduction,
+                num_label_tokens=w.num_label_tokens, mb_scale=mb_scale)
+    args.update(kw)
+    return orc.flce_reference(h, W, y, **args)
+
+
+def assert_loss(gpu_loss: float, ref: float, rtol: float = LOSS_RTOL):
+    if ref == 0.0:
+        assert gpu_loss == 0.0, f"loss {gpu_loss} != exact 0"
+    else:
+        err = abs(gpu_loss - ref)
+        assert err <= rtol * abs(ref), f"loss {gpu_loss} vs ref {ref}: rel err {err / abs(ref):.3e}"
+
+
+def assert_grad(name: str, gpu: torch.Tensor, ref: np.ndarray, tol: float):
+    g = to_np64(gpu)
+    assert g.shape == ref.shape, (name, g.shape, ref.shape)
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    err = float(np.abs(g - ref).max()) if ref.size else 0.0
+    if scale == 0.0:
+        assert err == 0.0, f"{name}: reference is zero, max |gpu| = {err}"
+    else:
+        assert err <= tol * scale, f"{name}: max err {err:.3e} > {tol} * {scale:.3e} (ratio {err / scale:.3e})"
+
+
+def assert_parity(w: fi.Workload, g: dict, r, *, check_lse=True):
+    tol = GRAD_TOL[w.dtype]
+    assert g["status"] == 0
+    assert g["num_tokens"] == r.num_tokens
+    assert_loss(g["loss"], r.loss64)
+    assert_grad("dH", g["dH"], r.dH, tol)
+    assert_grad("dW", g["dW"], r.dW, tol)
+    y = w.labels.reshape(-1).numpy()
+    ign = y == w.ignore_index
+    if ign.any():
+        dh = g["dH"][torch.from_numpy(np.flatnonzero(ign)).to(g["dH"].device)]
+        assert bool((dh == 0).all()), "ignored rows of dH must be exactly zero"
+    if check_lse and g["lse"] is not None and r.lse.size:
+        lse = to_np64(g["lse"])
+        err = np.abs(lse - r.lse).max()
+        assert err <= 1e-5 * max(1.0, np.abs(r.lse).max()), f"lse max err {err:.3e}"

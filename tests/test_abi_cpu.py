@@ -1,0 +1,184 @@
+"""CPU-only tests of the C-ABI library: it loads, exports every declared symbol,
+and its synchronous checks and workspace planner behave as documented. No GPU
+compute call is made here (pointers are fake integers, never dereferenced)."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flce.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from lm_head_linear_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from lm_head_linear_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(flce_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("flce_forward_backward", "flce_workspace_size", "flce_check_args",
+                 "flce_status_string"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from lm_head_linear_amd import _lib
+    names = declared_functions()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, f"{n} has no ctypes signature in the binding"
+    nm = shutil.which("nm")
+    if nm:
+        out = subprocess.run([nm, "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                             text=True).stdout
+        exported = set(re.findall(r"\bT\s+(\w+)", out))
+        for n in names:
+            assert n in exported, n
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        s = lib.flce_status_string(code).decode()
+        assert s.startswith("FLCE_")
+    assert "unknown" in lib.flce_status_string(99).decode()
+
+
+GiB = 1 << 30
+MiB = 1 << 20
+
+
+@pytest.mark.parametrize("N,H,V,limit", [
+    (8192, 4096, 131072, 512 * MiB),      # N*V*4/8 for the large-vocab case
+    (8192, 3584, 256000, 1 * GiB),        # softcapped case
+    (16384, 4096, 131072, 1 * GiB),       # the [2, 8192, 131072] case
+])
+def test_workspace_far_below_logits(lib, N, H, V, limit):
+    """Extra memory stays at or below 1/8 of the float32 logits it avoids.
+
+    Modalities PR 464, "Memory note": a [2, 8192, 131072] float32 logit tensor
+    is 8 GiB; the workspace here is bounded by 1/8 of N*V*4.
+    """
+    ws = lib.flce_workspace_size(N, H, V, 1)
+    assert 0 < ws <= limit
+    assert ws <= N * V * 4 // 8
+    if (N, V) == (16384, 131072):
+        assert N * V * 4 == 8 * GiB
+
+
+def test_workspace_invalid_sizes(lib):
+    assert lib.flce_workspace_size(-1, 8, 8, 1) == 0
+    assert lib.flce_workspace_size(8, 0, 8, 1) == 0
+    assert lib.flce_workspace_size(8, 8, 0, 1) == 0
+    assert lib.flce_workspace_size(8, 8, 8, 7) == 0
+    assert lib.flce_workspace_size(0, 8, 8, 1) > 0
+
+
+def test_vocab_chunk_plan(lib):
+    assert lib.flce_vocab_chunk(8192, 4096, 131072, 1) == 16384
+    assert lib.flce_vocab_chunk(16384, 4096, 131072, 1) == 8192
+    assert lib.flce_vocab_chunk(2048, 1024, 32000, 1) == 32000
+    assert lib.flce_vocab_chunk(32, 64, 1024, 0) == 1024
+    c = lib.flce_vocab_chunk(8192, 3584, 256000, 1)
+    assert c % 256 == 0 and 256 <= c <= 256000
+
+
+# -------------------------------------------------------------- check_args
+A16 = 1 << 20          # fake, 256-aligned "device" addresses (never dereferenced)
+
+
+def _args(**kw):
+    N, H, V = kw.get("N", 64), kw.get("H", 64), kw.get("V", 128)
+    dtype = kw.get("dtype", 1)
+    base = dict(h=A16, W=A16 * 64, labels=A16 * 128, N=N, H=H, V=V, ignore=-100, softcap=0.0,
+                red=0, T=0, loss=A16 * 129, nt=A16 * 130, dH=A16 * 256, dW=A16 * 512,
+                stream=None, dtype=dtype, mb=1.0, acc=0, ws=A16 * 1024, wsb=1 << 40,
+                status=None, lse=None)
+    base.update({k: v for k, v in kw.items() if k in base})
+    return [base[k] for k in ("h", "W", "labels", "N", "H", "V", "ignore", "softcap", "red",
+                              "T", "loss", "nt", "dH", "dW", "stream", "dtype", "mb", "acc",
+                              "ws", "wsb", "status", "lse")]
+
+
+def test_check_args_ok(lib):
+    assert lib.flce_check_args(*_args()) == 0
+    assert lib.flce_check_args(*_args(dtype=0, H=3)) == 0      # fp32: any H
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), 1), (dict(H=0), 1), (dict(V=0), 1),
+    (dict(red=2), 1), (dict(dtype=5), 1),
+    (dict(softcap=-1.0), 1), (dict(softcap=float("inf")), 1), (dict(softcap=float("nan")), 1),
+    (dict(mb=float("nan")), 1),
+    (dict(red=1, T=10), 1),
+    (dict(h=None), 1), (dict(W=None), 1), (dict(labels=None), 1), (dict(loss=None), 1),
+    (dict(nt=None), 1), (dict(dH=None), 1), (dict(dW=None), 1),
+    (dict(dH=A16), 1),                 # dH aliases h
+    (dict(dW=A16 * 64 + 256), 1),      # dW overlaps W
+    (dict(H=12), 2),                   # bf16 needs H % 8 == 0
+    (dict(h=A16 + 8), 2),              # misaligned bf16 matrix
+    (dict(ws=None), 3), (dict(ws=A16 * 1024 + 128), 3), (dict(wsb=16), 3),
+])
+def test_check_args_errors(lib, kw, code):
+    assert lib.flce_check_args(*_args(**kw)) == code
+
+
+def test_check_args_empty_batch(lib):
+    # N = 0: h, labels, dH may be NULL
+    assert lib.flce_check_args(*_args(N=0, h=None, labels=None, dH=None)) == 0
+
+
+def test_mean_with_T_rejected_sum_with_T_ok(lib):
+    assert lib.flce_check_args(*_args(red=0, T=123)) == 0
+    assert lib.flce_check_args(*_args(red=1, T=0)) == 0
+    assert lib.flce_check_args(*_args(red=1, T=-5)) == 0
+
+
+def test_forward_backward_rejects_before_launch(lib):
+    """Synchronous errors return before any HIP call, so this runs without a GPU."""
+    assert lib.flce_forward_backward(*_args(N=-1)) == 1
+    assert lib.flce_forward_backward(*_args(wsb=1)) == 3
+
+
+def test_python_binding_validation_without_gpu():
+    import lm_head_linear_amd as m
+    h = torch.zeros(4, 8, dtype=torch.bfloat16)
+    W = torch.zeros(16, 8, dtype=torch.bfloat16)
+    y = torch.zeros(4, dtype=torch.int64)
+    with pytest.raises(ValueError):
+        m.flce_forward_backward(h, W, y)          # CPU tensors: refused, no fallback
+    with pytest.raises(ValueError):
+        m.FusedLinearCrossEntropy(reduction="avg")
+    assert m.micro_batch_scale(3, 12, "mean") == 0.25
+    assert m.micro_batch_scale(3, 12, "sum") == 1.0
+
+
+def test_sanitized_host_checks(tmp_path):
+    """flce_check.cpp under AddressSanitizer + UBSan, driven by a C test program."""
+    gpp = shutil.which("g++")
+    if gpp is None:
+        pytest.skip("no g++")
+    src = os.path.join(ROOT, "lm_head_linear_amd", "csrc", "flce_check.cpp")
+    drv = os.path.join(ROOT, "tests", "csrc", "check_driver.cpp")
+    exe = str(tmp_path / "check_driver")
+    r = subprocess.run([gpp, "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined",
+                        "-fno-sanitize-recover=all", "-I", os.path.join(ROOT, "include"),
+                        src, drv, "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "all checks passed" in r.stdout
