@@ -126,7 +126,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="do not bracket kernels with events in the timed region")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",

@@ -23,6 +23,7 @@
 
 #include "../../include/flce.h"
 #include "flce_internal.h"
+#include "gemm_index.h"
 
 namespace flce {
 namespace {
@@ -31,10 +32,9 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
-constexpr int kBM = 256;
-constexpr int kBK = 64;
+constexpr int kBM = gemm::kBM;
 constexpr int kThreads = 256;
-constexpr int kTileBytes = kBM * kBK * 2;  // one operand, one stage: 32 KiB
+constexpr int kTileBytes = kBM * gemm::kBK * 2;  // one operand, one stage: 32 KiB
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -45,103 +45,95 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, __bf16(f));
 }
 
-// An operand of the GEMM. Stored either [rows][K] (K contiguous, "N" form)
-// or [K][rows] (rows contiguous, "T" form), with `ld` elements between
-// consecutive stored rows. Rows >= `rows` and k >= `K` read as zero.
+using gemm::Geom;
+using gemm::kBK;
+using gemm::kLoadsPerOperand;
+using gemm::swz_n;
+using gemm::swz_t;
+
+// An operand of the GEMM: a pointer and its geometry (see gemm_index.h).
 struct Operand {
   const uint16_t* ptr;
-  int64_t ld;
-  int64_t rows;
-  int64_t K;
+  Geom g;
 };
 
-// ---- global -> registers -> LDS -------------------------------------------
-// LDS tile layout: 256 rows x 64 k (128 B per row) as 8 chunks of 16 B; the
-// chunk c of row r is stored at chunk position c ^ (r & 7).
+// Per-thread state of one operand's direct-to-LDS loads: a wave-uniform tile
+// base advanced by `kstep` bytes per K tile, and one 32-bit byte offset per
+// load (see gemm::direct_lane for the layout and the edge clamping).
+struct DirectLoads {
+  const char* base;
+  int64_t kstep;
+  uint32_t off[kLoadsPerOperand];
+};
 
-// N form: thread loads rows (tid>>3) + 32 i, k chunk (tid & 7).
-__device__ __forceinline__ void load_n(u32x4 (&r)[8], const Operand& op, int64_t row0,
-                                       int64_t k0, int tid) {
-  const int c = tid & 7, rr = tid >> 3;
-  const int64_t gk = k0 + 8 * c;
-  const bool kok = gk < op.K;
+template <int FORM>
+__device__ __forceinline__ DirectLoads setup_direct(const Operand& op, int64_t row0, int wave,
+                                                    int lane) {
+  DirectLoads d;
+  d.base = reinterpret_cast<const char*>(op.ptr + gemm::direct_base(FORM, op.g, row0));
+  d.kstep = gemm::direct_kstep(FORM, op.g) * 2;
+#pragma unroll
+  for (int q = 0; q < kLoadsPerOperand; ++q)
+    d.off[q] = uint32_t(gemm::direct_lane(FORM, op.g, row0, wave, lane, q) * 2);
+  return d;
+}
+
+// Issue one K tile of direct loads into an LDS tile (32 KiB): load q of wave
+// w fills LDS bytes [(8w + q) KiB, +1 KiB), lane l writing 16 B at 16 l.
+__device__ __forceinline__ void issue_direct(const DirectLoads& d, int64_t kt, char* lds,
+                                             int wave) {
+  const char* b = d.base + kt * d.kstep;
+#pragma unroll
+  for (int q = 0; q < kLoadsPerOperand; ++q)
+    __builtin_amdgcn_global_load_lds(
+        b + d.off[q], (__attribute__((address_space(3))) void*)(lds + (8 * wave + q) * 1024), 16,
+        0, 0);
+}
+
+// Register path for a partial last K tile: zero-filled past K (and past the
+// matrix edge), then stored into the same LDS layout.
+template <int FORM>
+__device__ __forceinline__ void load_tail(u32x4 (&r)[8], const Operand& op, int64_t row0,
+                                          int64_t k0, int tid) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int64_t gr = row0 + rr + 32 * i;
-    if (kok && gr < op.rows)
-      r[i] = *reinterpret_cast<const u32x4*>(op.ptr + gr * op.ld + gk);
-    else
-      r[i] = u32x4{0u, 0u, 0u, 0u};
+    int64_t off;
+    const bool ok = gemm::tail_src(FORM, op.g, row0, k0, tid + 256 * i, off);
+    r[i] = ok ? *reinterpret_cast<const u32x4*>(op.ptr + off) : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
-__device__ __forceinline__ void store_n(char* lds, const u32x4 (&r)[8], int tid) {
-  const int c = tid & 7, rr = tid >> 3;
+template <int FORM>
+__device__ __forceinline__ void store_tail(char* lds, const u32x4 (&r)[8], int tid) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = rr + 32 * i;
-    *reinterpret_cast<u32x4*>(lds + (row * 8 + (c ^ (row & 7))) * 16) = r[i];
-  }
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<u32x4*>(lds + gemm::tail_lds_pos(FORM, tid + 256 * i) * 16) = r[i];
 }
 
-// T form: thread owns k rows 8*(tid&7) + i (i < 8) and 8 consecutive stored
-// columns starting at 8*(tid>>3).
-__device__ __forceinline__ void load_t(u32x4 (&r)[8], const Operand& op, int64_t row0,
-                                       int64_t k0, int tid) {
-  const int kb = tid & 7, mb = tid >> 3;
-  const int64_t gm = row0 + 8 * mb;
-  const bool mok = gm < op.rows;
+// MFMA fragment of 32 rows (block b of the wave's 128) for K substep s.
+template <int FORM>
+__device__ __forceinline__ bf16x8 read_frag(const char* lds, int row_base, int s, int lane) {
+  if (FORM == 0) {
+    const int row = row_base + (lane & 31);
+    const int c = 2 * s + (lane >> 5);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + (row * 8 + (c ^ swz_n(row))) * 16);
+    return __builtin_bit_cast(bf16x8, v);
+  } else {
+    typedef __attribute__((ext_vector_type(4))) short s16x4;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int g = lane >> 4, i = lane & 15;
+    const int col = row_base + 16 * (g & 1) + 4 * (i & 3);
+    s16x4 h[2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t gk = k0 + 8 * kb + i;
-    if (mok && gk < op.K)
-      r[i] = *reinterpret_cast<const u32x4*>(op.ptr + gk * op.ld + gm);
-    else
-      r[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
-// 8x8 transpose of 16-bit values: output m holds the 8 k values of column m.
-__device__ __forceinline__ void store_t(char* lds, const u32x4 (&r)[8], int tid) {
-  const int kb = tid & 7, mb = tid >> 3;
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    u32x4 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t x = r[2 * e][m >> 1];
-      const uint32_t y = r[2 * e + 1][m >> 1];
-      o[e] = (m & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
+    for (int r = 0; r < 2; ++r) {
+      const int k = 16 * s + 8 * (g >> 1) + 4 * r + (i >> 2);
+      const int off = (k * 32 + ((col >> 3) ^ swz_t(k))) * 16 + ((col >> 2) & 1) * 8;
+      h[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + off));
     }
-    const int row = 8 * mb + m;
-    *reinterpret_cast<u32x4*>(lds + (row * 8 + (kb ^ (row & 7))) * 16) = o;
+    typedef __attribute__((ext_vector_type(8))) short s16x8;
+    const s16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+    return __builtin_bit_cast(bf16x8, v);
   }
-}
-
-__device__ __forceinline__ bf16x8 read_frag(const char* lds, int row, int chunk) {
-  const u32x4 v = *reinterpret_cast<const u32x4*>(lds + (row * 8 + (chunk ^ (row & 7))) * 16);
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-// ---- tile scheduling --------------------------------------------------------
-// Workgroups are handed to the 8 XCDs round-robin. Give each XCD a contiguous
-// range of tiles, and order tiles within a range in groups of `group_m`
-// M-tiles so that the workgroups resident on one XCD share operand tiles in
-// that XCD's L2.
-__device__ __forceinline__ void tile_coords(int64_t M, int64_t Nn, int group_m, int64_t& m0,
-                                            int64_t& n0) {
-  const int64_t num_m = (M + kBM - 1) / kBM, num_n = (Nn + kBM - 1) / kBM;
-  const int64_t total = num_m * num_n;
-  const int64_t b = blockIdx.x;
-  const int64_t q = total / 8, rem = total % 8, x = b % 8, local = b / 8;
-  const int64_t tile = x * q + (x < rem ? x : rem) + local;
-  const int64_t per_group = int64_t(group_m) * num_n;
-  const int64_t g = tile / per_group;
-  const int64_t first_m = g * group_m;
-  const int64_t gs = (num_m - first_m) < group_m ? (num_m - first_m) : group_m;
-  const int64_t in = tile - g * per_group;
-  m0 = (first_m + in % gs) * kBM;
-  n0 = (in / gs) * kBM;
 }
 
 // Element (i, j, r) of the accumulators of a wave sits at tile row
@@ -154,14 +146,67 @@ __device__ __forceinline__ int acc_col(int wn, int j, int lane) {
   return wn * 128 + j * 32 + (lane & 31);
 }
 
-template <bool AT, bool BT, class Epi>
+// vmcnt(0), other counters untouched (gfx9 s_waitcnt encoding).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int FA, int FB>
+__device__ __forceinline__ void compute_tile(f32x16 (&acc)[4][4], const char* sa, const char* sb,
+                                             int wm, int wn, int lane) {
+  // let the scheduler interleave the fragment reads with the MFMAs
+  __builtin_amdgcn_iglp_opt(0);
+  bf16x8 af[2][4], bfr[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) af[0][i] = read_frag<FA>(sa, wm * 128 + i * 32, 0, lane);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bfr[0][j] = read_frag<FB>(sb, wn * 128 + j * 32, 0, lane);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int cur = s & 1, nxt = cur ^ 1;
+    if (s < 3) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[nxt][i] = read_frag<FA>(sa, wm * 128 + i * 32, s + 1, lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[nxt][j] = read_frag<FB>(sb, wn * 128 + j * 32, s + 1, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+  }
+}
+
+// One full K step: start the direct loads of tile kt+1 into the other LDS
+// buffers, then multiply tile kt. The buffers are __restrict__ so the
+// compiler can tell the direct-to-LDS writes of tile kt+1 from the reads of
+// tile kt and does not wait for the former before the latter; the real
+// dependency is the explicit vmcnt(0) + barrier at the top of the next step.
+template <int FA, int FB>
+__device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], const DirectLoads& da,
+                                       const DirectLoads& db, int64_t kt, int64_t nfull,
+                                       int wave, int wm, int wn, int lane,
+                                       const char* __restrict__ ca, const char* __restrict__ cb,
+                                       char* __restrict__ na, char* __restrict__ nb) {
+  if (kt + 1 < nfull) {
+    issue_direct(da, kt + 1, na, wave);
+    issue_direct(db, kt + 1, nb, wave);
+  }
+  compute_tile<FA, FB>(acc, ca, cb, wm, wn, lane);
+}
+
+template <int FA, int FB, class Epi>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A, Operand B, int64_t M,
                                                       int64_t Nn, int64_t K, int group_m,
                                                       Epi epi) {
-  __shared__ __attribute__((aligned(16))) char smem[4 * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_a0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_b0[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_a1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_b1[kTileBytes];
   int64_t m0, n0;
-  tile_coords(M, Nn, group_m, m0, n0);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  gemm::tile_coords(blockIdx.x, M, Nn, group_m, m0, n0);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
 
   f32x16 acc[4][4];
@@ -172,45 +217,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A, Operand B, int6
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  u32x4 ra[8], rb[8];
-  const int64_t nk = (K + kBK - 1) / kBK;
-  if (AT) load_t(ra, A, m0, 0, tid); else load_n(ra, A, m0, 0, tid);
-  if (BT) load_t(rb, B, n0, 0, tid); else load_n(rb, B, n0, 0, tid);
-  if (AT) store_t(smem, ra, tid); else store_n(smem, ra, tid);
-  if (BT) store_t(smem + kTileBytes, rb, tid); else store_n(smem + kTileBytes, rb, tid);
-  __syncthreads();
+  const DirectLoads da = setup_direct<FA>(A, m0, wave, lane);
+  const DirectLoads db = setup_direct<FB>(B, n0, wave, lane);
+  const int64_t nfull = K / kBK;               // K tiles loaded directly
+  const int64_t nk = (K + kBK - 1) / kBK;      // plus a zero-filled partial tile
 
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const char* sa = smem + (kt & 1) * 2 * kTileBytes;
-    const char* sb = sa + kTileBytes;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int64_t k1 = (kt + 1) * kBK;
-      if (AT) load_t(ra, A, m0, k1, tid); else load_n(ra, A, m0, k1, tid);
-      if (BT) load_t(rb, B, n0, k1, tid); else load_n(rb, B, n0, k1, tid);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 af[4], bfr[4];
-      const int ch = 2 * s + (lane >> 5);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = read_frag(sa, wm * 128 + i * 32 + (lane & 31), ch);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[j] = read_frag(sb, wn * 128 + j * 32 + (lane & 31), ch);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      char* da = smem + ((kt + 1) & 1) * 2 * kTileBytes;
-      if (AT) store_t(da, ra, tid); else store_n(da, ra, tid);
-      if (BT) store_t(da + kTileBytes, rb, tid); else store_n(da + kTileBytes, rb, tid);
-    }
-    __syncthreads();
+  if (nfull > 0) {
+    issue_direct(da, 0, lds_a0, wave);
+    issue_direct(db, 0, lds_b0, wave);
   }
-  epi(acc, m0, n0, wm, wn, lane, smem);
+  for (int64_t kt = 0; kt < nfull; ++kt) {
+    wait_vmem();
+    __syncthreads();
+    const bool odd = kt & 1;
+    k_step<FA, FB>(acc, da, db, kt, nfull, wave, wm, wn, lane, odd ? lds_a1 : lds_a0,
+                   odd ? lds_b1 : lds_b0, odd ? lds_a0 : lds_a1, odd ? lds_b0 : lds_b1);
+  }
+  if (nk > nfull) {
+    // The partial last K tile goes through registers, zero-filled past K. Its
+    // LDS buffers were last read two steps ago, behind the last barrier.
+    char* la = (nfull & 1) ? lds_a1 : lds_a0;
+    char* lb = (nfull & 1) ? lds_b1 : lds_b0;
+    u32x4 ta[8], tb[8];
+    load_tail<FA>(ta, A, m0, nfull * kBK, tid);
+    load_tail<FB>(tb, B, n0, nfull * kBK, tid);
+    store_tail<FA>(la, ta, tid);
+    store_tail<FB>(lb, tb, tid);
+    __syncthreads();
+    compute_tile<FA, FB>(acc, la, lb, wm, wn, lane);
+  }
+  __syncthreads();
+  epi(acc, m0, n0, wm, wn, lane, lds_a0);
 }
 
 __device__ __forceinline__ float softcap_fwd(float z, float s, float inv_s) {
@@ -407,68 +444,61 @@ struct EpiDH {
   }
 };
 
-int64_t n_tiles(int64_t M, int64_t Nn) { return ((M + kBM - 1) / kBM) * ((Nn + kBM - 1) / kBM); }
+const uint16_t* buf_ptr(const Args& a, int buf) {
+  return buf == gemm::kBufW ? static_cast<const uint16_t*>(a.W)
+       : buf == gemm::kBufH ? static_cast<const uint16_t*>(a.h)
+                            : static_cast<const uint16_t*>(a.g);
+}
+
+// A T-form operand is read in 16-byte column chunks: it needs rows % 8 == 0.
+bool launch_ok(const gemm::Launch& l) {
+  if (l.fa == gemm::kFormT && (l.a.rows % 8 != 0 || l.a.rows < 8)) return false;
+  if (l.fb == gemm::kFormT && (l.b.rows % 8 != 0 || l.b.rows < 8)) return false;
+  return l.M > 0 && l.Nn > 0 && l.K > 0;
+}
+
+template <int FA, int FB, class Epi>
+hipError_t run_gemm(const gemm::Launch& l, const Args& a, const Epi& e, int kind,
+                    const Launcher& L) {
+  if (!launch_ok(l)) return hipErrorInvalidValue;
+  Operand A{buf_ptr(a, l.buf_a) + l.off_a, l.a};
+  Operand B{buf_ptr(a, l.buf_b) + l.off_b, l.b};
+  L.pre(kind);
+  hipLaunchKernelGGL((k_gemm<FA, FB, Epi>), dim3(unsigned(gemm::num_tiles(l.M, l.Nn))),
+                     dim3(kThreads), 0, L.stream, A, B, l.M, l.Nn, l.K, gemm::kGroupM, e);
+  L.post(kind);
+  return hipGetLastError();
+}
 
 }  // namespace
 
 hipError_t bf16_forward(const Plan& p, const Args& a, const Launcher& L) {
-  const uint16_t* W = static_cast<const uint16_t*>(a.W);
-  const uint16_t* h = static_cast<const uint16_t*>(a.h);
-  Operand A{W, p.H, p.V, p.H};
-  Operand B{h, p.H, p.N, p.H};
+  const gemm::Launch l = gemm::forward_launch(p);
   EpiLse e{a.labels, p.N, p.V, a.ignore_index, a.softcap,
            a.softcap > 0.f ? 1.f / a.softcap : 0.f, a.part, p.ld_part, a.zt};
-  L.pre(kLseFwd);
-  hipLaunchKernelGGL((k_gemm<false, false, EpiLse>), dim3(unsigned(n_tiles(p.V, p.N))),
-                     dim3(kThreads), 0, L.stream, A, B, p.V, p.N, p.H, 4, e);
-  L.post(kLseFwd);
-  return hipGetLastError();
+  return run_gemm<gemm::kFormN, gemm::kFormN>(l, a, e, kLseFwd, L);
 }
 
 hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, const Launcher& L) {
-  const uint16_t* W = static_cast<const uint16_t*>(a.W);
-  const uint16_t* h = static_cast<const uint16_t*>(a.h);
-  uint16_t* gt = static_cast<uint16_t*>(a.g);
   const int64_t v0 = chunk * p.vchunk;
-  const int64_t vcur = (p.V - v0) < p.vchunk ? (p.V - v0) : p.vchunk;
-
+  const int64_t vcur = gemm::chunk_rows(p, chunk);
+  uint16_t* gt = static_cast<uint16_t*>(a.g);
   // 1) recompute the logits of the chunk and form G^T[vcur][ldg]
-  {
-    Operand A{W + v0 * p.H, p.H, vcur, p.H};
-    Operand B{h, p.H, p.N, p.H};
-    EpiGrad e{a.labels, a.lse, a.sc, p.N, p.V, a.ignore_index, v0, vcur, p.ldg, a.softcap,
-              a.softcap > 0.f ? 1.f / a.softcap : 0.f, gt};
-    L.pre(kGradLogits);
-    hipLaunchKernelGGL((k_gemm<false, false, EpiGrad>), dim3(unsigned(n_tiles(vcur, p.N))),
-                       dim3(kThreads), 0, L.stream, A, B, vcur, p.N, p.H, 4, e);
-    L.post(kGradLogits);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  // 2) dW[v0:v0+vcur] = G^T . h   (M = vcur, N = H, K = tokens)
-  {
-    Operand A{gt, p.ldg, vcur, p.N};           // [vcur][ldg], K contiguous
-    Operand B{h, p.H, p.H, p.N};               // h [N][H]: [K][cols], T form
-    EpiDW e{static_cast<uint16_t*>(a.dW), p.H, v0, vcur, a.accumulate_dW};
-    L.pre(kGemmDW);
-    hipLaunchKernelGGL((k_gemm<false, true, EpiDW>), dim3(unsigned(n_tiles(vcur, p.H))),
-                       dim3(kThreads), 0, L.stream, A, B, vcur, p.H, p.N, 4, e);
-    L.post(kGemmDW);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  // 3) dH (+)= G[:, chunk] . W[chunk]   (M = tokens, N = H, K = vcur)
-  {
-    Operand A{gt, p.ldg, p.N, vcur};           // G^T [K = vcur][rows = tokens], T form
-    Operand B{W + v0 * p.H, p.H, p.H, vcur};   // W chunk [K = vcur][cols = H], T form
-    EpiDH e{static_cast<uint16_t*>(a.dH), a.dh_acc, p.N, p.H, chunk == 0 ? 1 : 0,
-            chunk == p.n_chunks - 1 ? 1 : 0};
-    L.pre(kGemmDH);
-    hipLaunchKernelGGL((k_gemm<true, true, EpiDH>), dim3(unsigned(n_tiles(p.N, p.H))),
-                       dim3(kThreads), 0, L.stream, A, B, p.N, p.H, vcur, 4, e);
-    L.post(kGemmDH);
-    return hipGetLastError();
-  }
+  EpiGrad eg{a.labels, a.lse, a.sc, p.N, p.V, a.ignore_index, v0, vcur, p.ldg, a.softcap,
+             a.softcap > 0.f ? 1.f / a.softcap : 0.f, gt};
+  hipError_t err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a,
+                                                         eg, kGradLogits, L);
+  if (err != hipSuccess) return err;
+  // 2) dW[v0:v0+vcur] = G^T . h
+  EpiDW ew{static_cast<uint16_t*>(a.dW), p.H, v0, vcur, a.accumulate_dW};
+  err = run_gemm<gemm::kFormN, gemm::kFormT>(gemm::backward_launch(p, chunk, 1), a, ew, kGemmDW,
+                                             L);
+  if (err != hipSuccess) return err;
+  // 3) dH (+)= G[:, chunk] . W[chunk]
+  EpiDH eh{static_cast<uint16_t*>(a.dH), a.dh_acc, p.N, p.H, chunk == 0 ? 1 : 0,
+           chunk == p.n_chunks - 1 ? 1 : 0};
+  return run_gemm<gemm::kFormT, gemm::kFormT>(gemm::backward_launch(p, chunk, 2), a, eh, kGemmDH,
+                                              L);
 }
 
 }  // namespace flce

@@ -1,0 +1,108 @@
+// Host-side check of every global address the bf16 GEMM kernels load, using
+// the kernels' own index arithmetic (gemm_index.h) and the library's planner.
+// For each problem shape: every launch (forward, and the three launches of
+// every backward chunk), every workgroup, wave, lane and load. Direct loads
+// are affine in the K tile, so the first and the last full K tile are checked.
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#include "../../lm_head_linear_amd/csrc/gemm_index.h"
+
+using namespace flce;
+using namespace flce::gemm;
+
+static long failures = 0;
+
+static void fail(const char* what, int64_t a, int64_t b, int64_t c) {
+  if (failures < 20) std::printf("FAIL %s (%lld %lld %lld)\n", what, (long long)a, (long long)b, (long long)c);
+  ++failures;
+}
+
+static int64_t alloc_of(const Plan& p, int buf) {
+  return buf == kBufW ? p.V * p.H : buf == kBufH ? p.N * p.H : p.vchunk * p.ldg;
+}
+
+static void check_operand(const Plan& p, const Launch& l, int which, int64_t row0) {
+  const int form = which == 0 ? l.fa : l.fb;
+  const Geom& g = which == 0 ? l.a : l.b;
+  const int64_t base_off = which == 0 ? l.off_a : l.off_b;
+  const int64_t alloc = alloc_of(p, which == 0 ? l.buf_a : l.buf_b);
+  if (form == kFormT && (g.rows % 8 != 0 || g.rows < 8)) fail("T-form rows % 8", g.rows, 0, 0);
+  const int64_t nfull = l.K / kBK, nk = (l.K + kBK - 1) / kBK;
+  const int64_t tb = direct_base(form, g, row0), ks = direct_kstep(form, g);
+  for (int wave = 0; wave < 4; ++wave)
+    for (int lane = 0; lane < 64; ++lane)
+      for (int q = 0; q < kLoadsPerOperand; ++q) {
+        const int64_t lo = direct_lane(form, g, row0, wave, lane, q);
+        if (lo < 0 || lo * 2 > int64_t(0xFFFFFFFFll) - 16) fail("lane offset", lo, row0, q);
+        if (nfull == 0) continue;
+        for (int64_t kt : {int64_t(0), nfull - 1}) {
+          const int64_t e = base_off + tb + kt * ks + lo;
+          if (e < 0 || e + 8 > alloc) fail("direct load out of bounds", e, alloc, kt);
+        }
+      }
+  if (nk > nfull)
+    for (int z = 0; z < 256 * 8; ++z) {
+      int64_t off;
+      if (tail_src(form, g, row0, nfull * kBK, z, off)) {
+        const int64_t e = base_off + off;
+        if (e < 0 || e + 8 > alloc) fail("tail load out of bounds", e, alloc, z);
+      }
+      const int pos = tail_lds_pos(form, z);
+      if (pos < 0 || pos >= 2048) fail("tail lds position", pos, z, 0);
+    }
+}
+
+static void check_launch(const Plan& p, const Launch& l) {
+  const int64_t nt = num_tiles(l.M, l.Nn);
+  const int64_t num_m = (l.M + kBM - 1) / kBM;
+  std::vector<char> seen(size_t(nt), 0);
+  for (int64_t b = 0; b < nt; ++b) {
+    int64_t m0, n0;
+    tile_coords(b, l.M, l.Nn, kGroupM, m0, n0);
+    if (m0 < 0 || m0 >= l.M || n0 < 0 || n0 >= l.Nn || m0 % kBM || n0 % kBM) {
+      fail("tile out of range", b, m0, n0);
+      continue;
+    }
+    char& s = seen[size_t((n0 / kBM) * num_m + m0 / kBM)];
+    if (s) fail("tile visited twice", b, m0, n0);
+    s = 1;
+    check_operand(p, l, 0, m0);
+    check_operand(p, l, 1, n0);
+  }
+}
+
+int main(int argc, char** argv) {
+  // N H V [vchunk]
+  struct Shape { int64_t N, H, V, vc; };
+  std::vector<Shape> shapes = {
+      {1, 8, 1, 0},        {1, 8, 2, 0},        {3, 8, 7, 0},       {257, 64, 257, 0},
+      {600, 264, 1500, 512}, {513, 136, 777, 256}, {1000, 512, 3000, 1024},
+      {255, 8, 255, 0},    {257, 8, 300, 256},  {8, 8, 8, 0},       {7, 16, 513, 256},
+      {300, 136, 1000, 0}, {700, 128, 1500, 512}, {1024, 256, 4096, 0}, {1100, 128, 2000, 0},
+      {100, 16, 1, 0},     {100, 16, 2, 0},     {333, 64, 1024, 0},  {256, 64, 512, 0},
+      {2048, 1024, 32000, 0}, {4096, 4096, 131072, 0}, {8192, 4096, 131072, 0},
+      {8192, 3584, 256000, 0}, {16384, 4096, 131072, 0}};
+  if (argc == 5) shapes = {{std::atoll(argv[1]), std::atoll(argv[2]), std::atoll(argv[3]), std::atoll(argv[4])}};
+  for (const Shape& s : shapes) {
+    if (s.vc > 0) {
+      char buf[32];
+      std::snprintf(buf, sizeof buf, "%lld", (long long)s.vc);
+      setenv("FLCE_VCHUNK", buf, 1);
+    } else {
+      unsetenv("FLCE_VCHUNK");
+    }
+    Plan p;
+    if (!make_plan(s.N, s.H, s.V, 1, &p)) { fail("plan", s.N, s.H, s.V); continue; }
+    check_launch(p, forward_launch(p));
+    for (int64_t c = 0; c < p.n_chunks; ++c)
+      for (int w = 0; w < 3; ++w) check_launch(p, backward_launch(p, c, w));
+    std::printf("shape N=%lld H=%lld V=%lld chunk=%lld chunks=%lld: %s\n", (long long)s.N,
+                (long long)s.H, (long long)s.V, (long long)p.vchunk, (long long)p.n_chunks,
+                failures ? "FAILURES" : "ok");
+  }
+  if (failures == 0) std::printf("all loads in bounds\n");
+  return failures ? 1 : 0;
+}
