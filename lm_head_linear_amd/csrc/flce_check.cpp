@@ -49,7 +49,7 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p) {
   if (vc > vmax) vc = vmax;
   q.vchunk = vc;
   q.n_chunks = ceil_div(V, vc);
-  q.n_loss_blocks = ceil_div(N > 0 ? N : 1, 256);
+  q.n_loss_blocks = ceil_div(N > 0 ? N : 1, 32);   // tokens per lse-merge block
   q.need_dh_acc = (dtype == FLCE_BF16) && q.n_chunks > 1 && N > 0;
 
   size_t off = 0;

@@ -35,7 +35,7 @@ struct Plan {
   int64_t ldg = 0;           // leading dimension of G^T (tokens, multiple of 8)
   int64_t vchunk = 0;        // vocabulary rows per backward chunk
   int64_t n_chunks = 0;
-  int64_t n_loss_blocks = 0; // blocks of the lse-merge kernel (256 tokens each)
+  int64_t n_loss_blocks = 0; // blocks of the lse-merge kernel (32 tokens each)
   bool need_dh_acc = false;  // float32 dH accumulator needed (bf16, >1 chunk)
   size_t elem = 0;           // bytes per element of h/W/G
   // byte offsets into the workspace

@@ -59,13 +59,15 @@ inline Launch backward_launch(const Plan& p, int64_t c, int which) {
   if (which == 0)  // Z^T[chunk] = W[chunk] . h^T, then the gradient epilogue
     return Launch{vcur, p.N, p.H, kFormN, kFormN, kBufW, kBufH, v0 * p.H, 0,
                   Geom{p.H, vcur, p.H}, Geom{p.H, p.N, p.H}};
-  if (which == 1)  // dW[chunk] = G^T[chunk] . h  (K = tokens)
-    return Launch{vcur, p.H, p.N, kFormN, kFormT, kBufG, kBufH, 0, 0,
-                  Geom{p.ldg, vcur, p.N}, Geom{p.H, p.H, p.N}};
-  // dH += G[:, chunk] . W[chunk]  (K = chunk rows). G^T's token columns run to
-  // ldg (a multiple of 8); the columns past N hold zeros.
-  return Launch{p.N, p.H, vcur, kFormT, kFormT, kBufG, kBufW, 0, v0 * p.H,
-                Geom{p.ldg, p.ldg, vcur}, Geom{p.H, p.H, vcur}};
+  // G is stored token-major, G[t][v - v0] with row length vchunk (a multiple
+  // of 8; columns from vcur to the row end are never multiplied into a
+  // stored output).
+  if (which == 1)  // dW[chunk] = G[:, chunk]^T . h  (K = tokens)
+    return Launch{vcur, p.H, p.N, kFormT, kFormT, kBufG, kBufH, 0, 0,
+                  Geom{p.vchunk, p.vchunk, p.N}, Geom{p.H, p.H, p.N}};
+  // dH += G[:, chunk] . W[chunk]  (K = chunk rows)
+  return Launch{p.N, p.H, vcur, kFormN, kFormT, kBufG, kBufW, 0, v0 * p.H,
+                Geom{p.vchunk, p.N, vcur}, Geom{p.H, p.H, vcur}};
 }
 
 inline int64_t num_tiles(int64_t M, int64_t Nn) {

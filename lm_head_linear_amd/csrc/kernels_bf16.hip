@@ -199,10 +199,11 @@ template <int FA, int FB, class Epi>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A, Operand B, int64_t M,
                                                       int64_t Nn, int64_t K, int group_m,
                                                       Epi epi) {
-  __shared__ __attribute__((aligned(1024))) char lds_a0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_b0[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_a1[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_b1[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];
+  char* const lds_a0 = smem;
+  char* const lds_b0 = smem + kTileBytes;
+  char* const lds_a1 = smem + 2 * kTileBytes;
+  char* const lds_b1 = smem + 3 * kTileBytes;
   int64_t m0, n0;
   gemm::tile_coords(blockIdx.x, M, Nn, group_m, m0, n0);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A, Operand B, int6
     compute_tile<FA, FB>(acc, la, lb, wm, wn, lane);
   }
   __syncthreads();
-  epi(acc, m0, n0, wm, wn, lane, lds_a0);
+  epi(acc, m0, n0, wm, wn, lane, smem);
 }
 
 __device__ __forceinline__ float softcap_fwd(float z, float s, float inv_s) {
@@ -336,23 +337,30 @@ struct EpiLse {
   }
 };
 
-// ---- backward epilogue: the logit gradient G^T for one vocabulary chunk ----
+// ---- backward epilogue: the logit gradient G for one vocabulary chunk ----
 // G[t, v] = c * valid_t * (exp(z'_tv - lse_t) - [v = y_t]) * dz'/dz, stored
-// bf16 as G^T[v - v0][t]. Tile rows are chunk-relative vocab ids.
+// bf16 token-major as G[t][v - v0] (row length ldgv). Tile rows are
+// chunk-relative vocab ids, columns tokens. Each wave stages its 128 x 128
+// block in its own 32 KiB of LDS as [token][vocab] (a lane packs its 4
+// consecutive vocab values into 8 bytes; 8-byte slots XOR-swizzled by token),
+// then writes whole 16-byte runs of a token row to global memory.
 struct EpiGrad {
   const int64_t* labels;
   const float* lse;
   const Scalars* sc;
-  int64_t N, V, ignore_index, v0, vcur, ldg;
+  int64_t N, V, ignore_index, v0, vcur, ldgv;
   float softcap, inv_softcap;
-  uint16_t* gt;
+  uint16_t* g;
 
   __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm,
-                                             int wn, int lane, char*) const {
+                                             int wn, int lane, char* smem) const {
     const float c = sc->c32;
+    const int half = lane >> 5;
+    char* reg = smem + (wm + 2 * wn) * kTileBytes;   // this wave's 32 KiB
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t t = n0 + acc_col(wn, j, lane);
+      const int tl = j * 32 + (lane & 31);             // token within the wave block
+      const int64_t t = n0 + wn * 128 + tl;
       int64_t y = ignore_index;
       float l = 0.f, coef = 0.f;
       bool valid = false;
@@ -364,24 +372,46 @@ struct EpiGrad {
           l = lse[t];
         }
       }
-      const bool tok = t < ldg;
+      // target column relative to this wave's first vocab row (or out of range)
+      const int64_t ydiff = y - (v0 + m0 + wm * 128);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = m0 + acc_row(wm, i, r, lane);
-          float z = acc[i][j][r];
-          float d = 1.f;
-          if (softcap > 0.f) {
-            const float th = tanhf(z * inv_softcap);
-            z = softcap * th;
-            d = 1.f - th * th;
+        for (int rq = 0; rq < 4; ++rq) {
+          uint32_t packed[2];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rq + e;
+            const int vl = i * 32 + 8 * rq + 4 * half + e;   // vocab within the wave block
+            float z = acc[i][j][r];
+            float d = 1.f;
+            if (softcap > 0.f) {
+              const float th = tanhf(z * inv_softcap);
+              z = softcap * th;
+              d = 1.f - th * th;
+            }
+            const float p = __builtin_amdgcn_exp2f((z - l) * kLog2e);
+            const float oh = (ydiff == vl) ? 1.f : 0.f;
+            const float gv = valid ? (p - oh) * coef * d : 0.f;
+            const uint32_t b = f32_to_bf16(gv);
+            if (e & 1) packed[e >> 1] |= b << 16;
+            else packed[e >> 1] = b;
           }
-          const float p = __builtin_amdgcn_exp2f((z - l) * kLog2e);
-          const float oh = (v0 + m == y) ? 1.f : 0.f;
-          const float g = valid ? (p - oh) * coef * d : 0.f;
-          if (tok && m < vcur) gt[m * ldg + t] = f32_to_bf16(g);
+          const int slot = (i * 8 + 2 * rq + half) ^ (tl & 31);
+          *reinterpret_cast<uint2*>(reg + tl * 256 + slot * 8) = make_uint2(packed[0], packed[1]);
         }
+    }
+    __syncthreads();
+    // read back 16-byte runs of token rows and store them
+#pragma unroll 4
+    for (int q = 0; q < 32; ++q) {
+      const int idx = q * 64 + lane;
+      const int tl = idx >> 4, ch = idx & 15, x = tl & 31;
+      u32x4 v = *reinterpret_cast<const u32x4*>(reg + tl * 256 + (((2 * ch) ^ x) & ~1) * 8);
+      if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+      const int64_t t = n0 + wn * 128 + tl;
+      const int64_t vl = m0 + wm * 128 + 8 * ch;
+      if (t < N && vl < vcur) *reinterpret_cast<u32x4*>(g + t * ldgv + vl) = v;
     }
   }
 };
@@ -482,22 +512,22 @@ hipError_t bf16_forward(const Plan& p, const Args& a, const Launcher& L) {
 hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, const Launcher& L) {
   const int64_t v0 = chunk * p.vchunk;
   const int64_t vcur = gemm::chunk_rows(p, chunk);
-  uint16_t* gt = static_cast<uint16_t*>(a.g);
-  // 1) recompute the logits of the chunk and form G^T[vcur][ldg]
-  EpiGrad eg{a.labels, a.lse, a.sc, p.N, p.V, a.ignore_index, v0, vcur, p.ldg, a.softcap,
-             a.softcap > 0.f ? 1.f / a.softcap : 0.f, gt};
+  uint16_t* g = static_cast<uint16_t*>(a.g);
+  // 1) recompute the logits of the chunk and form G[N][vchunk]
+  EpiGrad eg{a.labels, a.lse, a.sc, p.N, p.V, a.ignore_index, v0, vcur, p.vchunk, a.softcap,
+             a.softcap > 0.f ? 1.f / a.softcap : 0.f, g};
   hipError_t err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a,
                                                          eg, kGradLogits, L);
   if (err != hipSuccess) return err;
   // 2) dW[v0:v0+vcur] = G^T . h
   EpiDW ew{static_cast<uint16_t*>(a.dW), p.H, v0, vcur, a.accumulate_dW};
-  err = run_gemm<gemm::kFormN, gemm::kFormT>(gemm::backward_launch(p, chunk, 1), a, ew, kGemmDW,
+  err = run_gemm<gemm::kFormT, gemm::kFormT>(gemm::backward_launch(p, chunk, 1), a, ew, kGemmDW,
                                              L);
   if (err != hipSuccess) return err;
   // 3) dH (+)= G[:, chunk] . W[chunk]
   EpiDH eh{static_cast<uint16_t*>(a.dH), a.dh_acc, p.N, p.H, chunk == 0 ? 1 : 0,
            chunk == p.n_chunks - 1 ? 1 : 0};
-  return run_gemm<gemm::kFormT, gemm::kFormT>(gemm::backward_launch(p, chunk, 2), a, eh, kGemmDH,
+  return run_gemm<gemm::kFormN, gemm::kFormT>(gemm::backward_launch(p, chunk, 2), a, eh, kGemmDH,
                                               L);
 }
 

@@ -56,36 +56,56 @@ __global__ __launch_bounds__(1024) void k_label_scan(
 // Per token: merge the per-vocab-tile (max m_j, sum_j of exp(x - m_j))
 // partials into lse = M + log(sum_j s_j exp(m_j - M)), form the token loss
 // lse - z'_target on non-ignored tokens (NaN for an out-of-range label), and
-// sum 256 tokens in float64 in a fixed tree order.
+// sum the block's tokens in float64 in a fixed order. A block handles
+// kMergeTokens tokens; its 8 thread groups each merge every 8th tile of them
+// (online max/rescale), then the groups are combined in a fixed order.
+constexpr int kMergeTokens = 32;
+
 __global__ __launch_bounds__(256) void k_lse_merge(
     const float2* __restrict__ part, int64_t n_tiles, int64_t ld_part,
     const float* __restrict__ zt, const int64_t* __restrict__ labels, int64_t N,
     int64_t V, int64_t ignore_index, float* __restrict__ lse, float* __restrict__ lse_out,
     double* __restrict__ lsum) {
-  __shared__ double red[256];
-  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  double ell = 0.0;
+  __shared__ float2 grp[8][kMergeTokens];
+  __shared__ double red[kMergeTokens];
+  const int tk = threadIdx.x % kMergeTokens, g = threadIdx.x / kMergeTokens;
+  const int64_t t = int64_t(blockIdx.x) * kMergeTokens + tk;
+  float M = -INFINITY, S = 0.f;
   if (t < N) {
-    float M = -INFINITY;
-    for (int64_t j = 0; j < n_tiles; ++j) M = fmaxf(M, part[j * ld_part + t].x);
-    float S = 0.f;
-    for (int64_t j = 0; j < n_tiles; ++j) {
+    for (int64_t j = g; j < n_tiles; j += 8) {
       const float2 q = part[j * ld_part + t];
-      if (q.y > 0.f) S += q.y * exp2f((q.x - M) * kLog2e);
+      if (q.x > M) {
+        S = (M == -INFINITY ? 0.f : S * exp2f((M - q.x) * kLog2e)) + q.y;
+        M = q.x;
+      } else {
+        S += q.y * exp2f((q.x - M) * kLog2e);
+      }
     }
-    const float l = M + log2f(S) * kLn2;
-    lse[t] = l;
-    if (lse_out) lse_out[t] = l;
-    const int64_t y = labels[t];
-    if (y != ignore_index) ell = (y < 0 || y >= V) ? double(NAN) : double(l) - double(zt[t]);
   }
-  red[threadIdx.x] = ell;
+  grp[g][tk] = make_float2(M, S);
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
+  if (g == 0) {
+    double ell = 0.0;
+    if (t < N) {
+      float Mx = -INFINITY;
+      for (int i = 0; i < 8; ++i) Mx = fmaxf(Mx, grp[i][tk].x);
+      float St = 0.f;
+      for (int i = 0; i < 8; ++i)
+        if (grp[i][tk].x != -INFINITY) St += grp[i][tk].y * exp2f((grp[i][tk].x - Mx) * kLog2e);
+      const float l = Mx + log2f(St) * kLn2;
+      lse[t] = l;
+      if (lse_out) lse_out[t] = l;
+      const int64_t y = labels[t];
+      if (y != ignore_index) ell = (y < 0 || y >= V) ? double(NAN) : double(l) - double(zt[t]);
+    }
+    red[tk] = ell;
   }
-  if (threadIdx.x == 0) lsum[blockIdx.x] = red[0];
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double s = 0.0;
+    for (int i = 0; i < kMergeTokens; ++i) s += red[i];
+    lsum[blockIdx.x] = s;
+  }
 }
 
 // loss = c * sum(lsum) in float64, fixed order; NaN when a label was invalid.
