@@ -18,8 +18,10 @@ namespace flce {
 namespace gemm {
 
 constexpr int kBM = 256;                // tile edge (M and N)
-constexpr int kBK = 64;                 // K step
-constexpr int kLoadsPerOperand = 8;     // 16-byte loads per thread per operand per K tile
+constexpr int kBK = 32;                 // K step
+constexpr int kStages = 4;              // LDS stages (prefetch distance kStages - 1)
+constexpr int kLoadsPerOperand = 4;     // 16-byte loads per thread per operand per K tile
+constexpr int kTailLoads = 4;           // register loads per thread for a partial K tile
 constexpr int kGroupM = 4;              // M tiles per raster group
 
 enum Form : int { kFormN = 0, kFormT = 1 };
@@ -93,18 +95,18 @@ FLCE_HD void tile_coords(int64_t b, int64_t M, int64_t Nn, int group_m, int64_t&
   n0 = (in / gs) * kBM;
 }
 
-// LDS swizzles. N form: 256 rows x 64 k, 128 B per row, 8 chunks of 16 B;
-// logical chunk c of row r at position c ^ swz_n(r). T form: 64 k-rows x 256
+// LDS swizzles. N form: 256 rows x 32 k, 64 B per row, 4 chunks of 16 B;
+// logical chunk c of row r at position c ^ swz_n(r). T form: 32 k-rows x 256
 // columns, 512 B per k-row, 32 chunks; logical chunk c of k-row k at
 // c ^ swz_t(k). Both keep the fragment reads conflict-free whether the LDS
 // serves 128 B or 256 B per clock.
-FLCE_HD int swz_n(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+FLCE_HD int swz_n(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 FLCE_HD int swz_t(int k) { return (0xCA60 >> (4 * (k & 3))) & 15; }  // {0,6,10,12}[k%4]
 
 // Direct-to-LDS loads: element offset of the tile base (k = 0) from the
 // operand pointer, elements to advance per K tile, and the element offset of
 // load q of (wave, lane) from the tile base. Load q of wave w fills LDS bytes
-// [(8w + q) KiB, +1 KiB), lane l writing 16 B at 16 l, so a lane fetches the
+// [(4w + q) KiB, +1 KiB), lane l writing 16 B at 16 l, so a lane fetches the
 // logical chunk that the swizzle puts at its LDS position. Rows (N form) or
 // column chunks (T form) past the edge are clamped to the last valid one:
 // their products land outside the output and are never stored.
@@ -116,13 +118,13 @@ FLCE_HD int64_t direct_kstep(int form, const Geom& g) {
 }
 FLCE_HD int64_t direct_lane(int form, const Geom& g, int64_t row0, int wave, int lane, int q) {
   if (form == kFormN) {
-    const int lr = 64 * wave + 8 * q + (lane >> 3);
-    const int c = (lane & 7) ^ swz_n(lr);
+    const int lr = 16 * (4 * wave + q) + (lane >> 2);
+    const int c = (lane & 3) ^ swz_n(lr);
     int64_t r = row0 + lr;
     if (r > g.rows - 1) r = g.rows - 1;
     return (r - row0) * g.ld + 8 * c;
   }
-  const int kr = 2 * (8 * wave + q) + (lane >> 5);
+  const int kr = 2 * (4 * wave + q) + (lane >> 5);
   const int c = (lane & 31) ^ swz_t(kr);
   int64_t col = 8 * c;
   if (row0 + col > g.rows - 8) col = g.rows - 8 - row0;
@@ -130,11 +132,11 @@ FLCE_HD int64_t direct_lane(int form, const Geom& g, int64_t row0, int wave, int
 }
 
 // Register path of a partial last K tile: thread tid's load i covers
-// z = tid + 256 i. Returns whether it reads memory (else it stores zeros) and
-// the element offset from the operand pointer.
+// z = tid + 256 i (i < kTailLoads). Returns whether it reads memory (else it
+// stores zeros) and the element offset from the operand pointer.
 FLCE_HD bool tail_src(int form, const Geom& g, int64_t row0, int64_t k0, int z, int64_t& off) {
-  if (form == kFormN) {  // z -> (row z / 8, chunk z % 8)
-    const int64_t gr = row0 + (z >> 3), gk = k0 + 8 * (z & 7);
+  if (form == kFormN) {  // z -> (row z / 4, chunk z % 4)
+    const int64_t gr = row0 + (z >> 2), gk = k0 + 8 * (z & 3);
     off = gr * g.ld + gk;
     return gr < g.rows && gk < g.K;
   }
@@ -145,7 +147,7 @@ FLCE_HD bool tail_src(int form, const Geom& g, int64_t row0, int64_t k0, int z, 
 
 // LDS chunk position (16-byte units) of the tail element z.
 FLCE_HD int tail_lds_pos(int form, int z) {
-  return form == kFormN ? (z >> 3) * 8 + ((z & 7) ^ swz_n(z >> 3))
+  return form == kFormN ? (z >> 2) * 4 + ((z & 3) ^ swz_n(z >> 2))
                         : (z >> 5) * 32 + ((z & 31) ^ swz_t(z >> 5));
 }
 

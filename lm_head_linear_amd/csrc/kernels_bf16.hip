@@ -34,7 +34,9 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 constexpr int kBM = gemm::kBM;
 constexpr int kThreads = 256;
-constexpr int kTileBytes = kBM * gemm::kBK * 2;  // one operand, one stage: 32 KiB
+constexpr int kTileBytes = kBM * gemm::kBK * 2;  // one operand, one stage: 16 KiB
+constexpr int kStages = gemm::kStages;
+constexpr int kWaveScratch = 32768;               // LDS bytes per wave in the epilogues
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -78,25 +80,25 @@ __device__ __forceinline__ DirectLoads setup_direct(const Operand& op, int64_t r
   return d;
 }
 
-// Issue one K tile of direct loads into an LDS tile (32 KiB): load q of wave
-// w fills LDS bytes [(8w + q) KiB, +1 KiB), lane l writing 16 B at 16 l.
+// Issue one K tile of direct loads into an LDS tile (16 KiB): load q of wave
+// w fills LDS bytes [(4w + q) KiB, +1 KiB), lane l writing 16 B at 16 l.
 __device__ __forceinline__ void issue_direct(const DirectLoads& d, int64_t kt, char* lds,
                                              int wave) {
   const char* b = d.base + kt * d.kstep;
 #pragma unroll
   for (int q = 0; q < kLoadsPerOperand; ++q)
     __builtin_amdgcn_global_load_lds(
-        b + d.off[q], (__attribute__((address_space(3))) void*)(lds + (8 * wave + q) * 1024), 16,
+        b + d.off[q], (__attribute__((address_space(3))) void*)(lds + (4 * wave + q) * 1024), 16,
         0, 0);
 }
 
 // Register path for a partial last K tile: zero-filled past K (and past the
 // matrix edge), then stored into the same LDS layout.
 template <int FORM>
-__device__ __forceinline__ void load_tail(u32x4 (&r)[8], const Operand& op, int64_t row0,
-                                          int64_t k0, int tid) {
+__device__ __forceinline__ void load_tail(u32x4 (&r)[gemm::kTailLoads], const Operand& op,
+                                          int64_t row0, int64_t k0, int tid) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < gemm::kTailLoads; ++i) {
     int64_t off;
     const bool ok = gemm::tail_src(FORM, op.g, row0, k0, tid + 256 * i, off);
     r[i] = ok ? *reinterpret_cast<const u32x4*>(op.ptr + off) : u32x4{0u, 0u, 0u, 0u};
@@ -104,9 +106,10 @@ __device__ __forceinline__ void load_tail(u32x4 (&r)[8], const Operand& op, int6
 }
 
 template <int FORM>
-__device__ __forceinline__ void store_tail(char* lds, const u32x4 (&r)[8], int tid) {
+__device__ __forceinline__ void store_tail(char* lds, const u32x4 (&r)[gemm::kTailLoads],
+                                           int tid) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < gemm::kTailLoads; ++i)
     *reinterpret_cast<u32x4*>(lds + gemm::tail_lds_pos(FORM, tid + 256 * i) * 16) = r[i];
 }
 
@@ -116,7 +119,7 @@ __device__ __forceinline__ bf16x8 read_frag(const char* lds, int row_base, int s
   if (FORM == 0) {
     const int row = row_base + (lane & 31);
     const int c = 2 * s + (lane >> 5);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + (row * 8 + (c ^ swz_n(row))) * 16);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + (row * 4 + (c ^ swz_n(row))) * 16);
     return __builtin_bit_cast(bf16x8, v);
   } else {
     typedef __attribute__((ext_vector_type(4))) short s16x4;
@@ -146,64 +149,104 @@ __device__ __forceinline__ int acc_col(int wn, int j, int lane) {
   return wn * 128 + j * 32 + (lane & 31);
 }
 
-// vmcnt(0), other counters untouched (gfx9 s_waitcnt encoding).
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most `tiles` K tiles of direct loads (2 * kLoadsPerOperand
+// per thread each) are still in flight; other counters untouched (gfx9
+// s_waitcnt encoding: vmcnt bits [3:0] and [15:14]).
+__device__ __forceinline__ void wait_loads_in_flight(int64_t tiles) {
+  static_assert(2 * gemm::kLoadsPerOperand == 8 && kStages == 4, "waitcnt immediates");
+  if (tiles <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
+  else if (tiles == 1) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+  else __builtin_amdgcn_s_waitcnt(0x4F70);                   // vmcnt(16)
+}
+
+// Workgroup barrier for the K loop. Unlike __syncthreads() it carries no
+// memory fence, which would wait for every load in flight (vmcnt(0)) and
+// undo the prefetch. What it must order: (1) this wave's direct loads of the
+// tile about to be read have landed -- the counted vmcnt wait before it;
+// (2) every wave's reads of the stage about to be overwritten are done --
+// they were consumed by that wave's MFMAs before it reached the barrier.
+// The empty asm statements keep the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// MFMA fragments of one 16-wide K substep for the wave's 128 x 128 block.
+struct Frags {
+  bf16x8 a[4], b[4];
+};
 
 template <int FA, int FB>
-__device__ __forceinline__ void compute_tile(f32x16 (&acc)[4][4], const char* sa, const char* sb,
+__device__ __forceinline__ void read_substep(Frags& f, const char* sa, const char* sb, int s,
                                              int wm, int wn, int lane) {
-  // let the scheduler interleave the fragment reads with the MFMAs
-  __builtin_amdgcn_iglp_opt(0);
-  bf16x8 af[2][4], bfr[2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) af[0][i] = read_frag<FA>(sa, wm * 128 + i * 32, 0, lane);
+  for (int i = 0; i < 4; ++i) f.a[i] = read_frag<FA>(sa, wm * 128 + i * 32, s, lane);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) bfr[0][j] = read_frag<FB>(sb, wn * 128 + j * 32, 0, lane);
+  for (int j = 0; j < 4; ++j) f.b[j] = read_frag<FB>(sb, wn * 128 + j * 32, s, lane);
+}
+
+__device__ __forceinline__ void mfma_substep(f32x16 (&acc)[4][4], const Frags& f) {
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const int cur = s & 1, nxt = cur ^ 1;
-    if (s < 3) {
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[nxt][i] = read_frag<FA>(sa, wm * 128 + i * 32, s + 1, lane);
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// Scheduling hints for one half K step: its 16 MFMAs, each followed by up to
+// one LDS fragment read and, in the second half, one direct global load, so
+// the reads for the next half and the loads for a later tile issue under the
+// MFMAs instead of stalling the wave's in-order stream.
+template <int FA, int FB, bool LOADS>
+__device__ __forceinline__ void interleave_hints() {
+  constexpr int kReads = (FA == 0 ? 4 : 8) + (FB == 0 ? 4 : 8);
+  constexpr int kLoads = LOADS ? 2 * kLoadsPerOperand : 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[nxt][j] = read_frag<FB>(sb, wn * 128 + j * 32, s + 1, lane);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
+  for (int q = 0; q < 16; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+    if (q < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read
+    if (q < kReads) __builtin_amdgcn_sched_group_barrier(0x100, (kReads + 15) / 16, 0);  // DS read
   }
 }
 
-// One full K step: start the direct loads of tile kt+1 into the other LDS
-// buffers, then multiply tile kt. The buffers are __restrict__ so the
-// compiler can tell the direct-to-LDS writes of tile kt+1 from the reads of
-// tile kt and does not wait for the former before the latter; the real
-// dependency is the explicit vmcnt(0) + barrier at the top of the next step.
+// First half of K step kt: read the fragments of substep 1 of tile kt while
+// multiplying substep 0 (already in registers).
 template <int FA, int FB>
-__device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], const DirectLoads& da,
-                                       const DirectLoads& db, int64_t kt, int64_t nfull,
-                                       int wave, int wm, int wn, int lane,
-                                       const char* __restrict__ ca, const char* __restrict__ cb,
-                                       char* __restrict__ na, char* __restrict__ nb) {
-  if (kt + 1 < nfull) {
-    issue_direct(da, kt + 1, na, wave);
-    issue_direct(db, kt + 1, nb, wave);
-  }
-  compute_tile<FA, FB>(acc, ca, cb, wm, wn, lane);
+__device__ __forceinline__ void half_a(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
+                                       const char* __restrict__ sa, const char* __restrict__ sb,
+                                       int wm, int wn, int lane) {
+  read_substep<FA, FB>(f1, sa, sb, 1, wm, wn, lane);
+  mfma_substep(acc, f0);
+  interleave_hints<FA, FB, false>();
+}
+
+// Second half of K step kt: start the direct loads of a later tile into its
+// (free) stage and read substep 0 of tile kt+1, while multiplying substep 1.
+// The stages are __restrict__ so the compiler does not order the
+// direct-to-LDS writes against these reads; the real dependencies are the
+// counted vmcnt waits and the barriers.
+template <int FA, int FB>
+__device__ __forceinline__ void half_b(f32x16 (&acc)[4][4], Frags& f0, const Frags& f1,
+                                       const DirectLoads& da, const DirectLoads& db,
+                                       int64_t load_tile, const char* __restrict__ na,
+                                       const char* __restrict__ nb, char* __restrict__ la,
+                                       char* __restrict__ lb, int wave, int wm, int wn, int lane) {
+  issue_direct(da, load_tile, la, wave);
+  issue_direct(db, load_tile, lb, wave);
+  read_substep<FA, FB>(f0, na, nb, 0, wm, wn, lane);
+  mfma_substep(acc, f1);
+  interleave_hints<FA, FB, true>();
 }
 
 template <int FA, int FB, class Epi>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A, Operand B, int64_t M,
                                                       int64_t Nn, int64_t K, int group_m,
                                                       Epi epi) {
-  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];
-  char* const lds_a0 = smem;
-  char* const lds_b0 = smem + kTileBytes;
-  char* const lds_a1 = smem + 2 * kTileBytes;
-  char* const lds_b1 = smem + 3 * kTileBytes;
+  // kStages stages of (A tile, B tile); reused by the epilogues (32 KiB per wave)
+  __shared__ __attribute__((aligned(1024))) char smem[kStages * 2 * kTileBytes];
+  static_assert(kStages * 2 * kTileBytes >= 4 * kWaveScratch, "epilogue staging");
   int64_t m0, n0;
   gemm::tile_coords(blockIdx.x, M, Nn, group_m, m0, n0);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -223,29 +266,57 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A, Operand B, int6
   const int64_t nfull = K / kBK;               // K tiles loaded directly
   const int64_t nk = (K + kBK - 1) / kBK;      // plus a zero-filled partial tile
 
+  auto st_a = [&](int64_t t) { return smem + (t % kStages) * 2 * kTileBytes; };
+  auto st_b = [&](int64_t t) { return smem + (t % kStages) * 2 * kTileBytes + kTileBytes; };
+  static_assert(gemm::kBK == 32, "two 16-wide substeps per K step");
+  // Software pipeline over the full K tiles. Tile t is loaded (direct to LDS)
+  // kStages - 1 steps ahead. The barrier that makes tile kt+1 visible sits in
+  // the middle of step kt, so substep 0 of tile kt+1 is read while substep 1
+  // of tile kt is multiplied. The stage step kt loads into held tile kt-1,
+  // whose fragments every wave consumed before that step's barrier. Every
+  // step issues exactly one tile -- past the last tile it re-loads the last
+  // one into a free stage -- so the number of loads in flight at each wait is
+  // the same, and the body has no branches for the scheduler to stop at.
   if (nfull > 0) {
-    issue_direct(da, 0, lds_a0, wave);
-    issue_direct(db, 0, lds_b0, wave);
-  }
-  for (int64_t kt = 0; kt < nfull; ++kt) {
-    wait_vmem();
-    __syncthreads();
-    const bool odd = kt & 1;
-    k_step<FA, FB>(acc, da, db, kt, nfull, wave, wm, wn, lane, odd ? lds_a1 : lds_a0,
-                   odd ? lds_b1 : lds_b0, odd ? lds_a0 : lds_a1, odd ? lds_b0 : lds_b1);
+    const int64_t last = nfull - 1;
+#pragma unroll
+    for (int t = 0; t < kStages - 1; ++t) {
+      issue_direct(da, t < last ? t : last, st_a(t), wave);
+      issue_direct(db, t < last ? t : last, st_b(t), wave);
+    }
+    Frags f0, f1;
+    wait_loads_in_flight(kStages - 2);             // tile 0 landed
+    stage_barrier();
+    read_substep<FA, FB>(f0, st_a(0), st_b(0), 0, wm, wn, lane);
+    for (int64_t kt = 0; kt < nfull; ++kt) {
+      half_a<FA, FB>(acc, f0, f1, st_a(kt), st_b(kt), wm, wn, lane);
+      wait_loads_in_flight(kStages - 3);           // tile kt+1 landed
+      stage_barrier();
+      const int64_t lt = kt + kStages - 1;
+      half_b<FA, FB>(acc, f0, f1, da, db, lt < last ? lt : last, st_a(kt + 1), st_b(kt + 1),
+                     st_a(lt), st_b(lt), wave, wm, wn, lane);
+    }
+    // the re-loads past the last tile may still be in flight
+    wait_loads_in_flight(0);
+    stage_barrier();
   }
   if (nk > nfull) {
     // The partial last K tile goes through registers, zero-filled past K. Its
-    // LDS buffers were last read two steps ago, behind the last barrier.
-    char* la = (nfull & 1) ? lds_a1 : lds_a0;
-    char* lb = (nfull & 1) ? lds_b1 : lds_b0;
-    u32x4 ta[8], tb[8];
+    // LDS stage was last read kStages - 1 steps ago, behind the last barrier.
+    char* la = st_a(nfull);
+    char* lb = st_b(nfull);
+    u32x4 ta[gemm::kTailLoads], tb[gemm::kTailLoads];
     load_tail<FA>(ta, A, m0, nfull * kBK, tid);
     load_tail<FB>(tb, B, n0, nfull * kBK, tid);
     store_tail<FA>(la, ta, tid);
     store_tail<FB>(lb, tb, tid);
     __syncthreads();
-    compute_tile<FA, FB>(acc, la, lb, wm, wn, lane);
+    Frags ft;
+#pragma unroll
+    for (int sub = 0; sub < gemm::kBK / 16; ++sub) {
+      read_substep<FA, FB>(ft, la, lb, sub, wm, wn, lane);
+      mfma_substep(acc, ft);
+    }
   }
   __syncthreads();
   epi(acc, m0, n0, wm, wn, lane, smem);
@@ -356,7 +427,7 @@ struct EpiGrad {
                                              int wn, int lane, char* smem) const {
     const float c = sc->c32;
     const int half = lane >> 5;
-    char* reg = smem + (wm + 2 * wn) * kTileBytes;   // this wave's 32 KiB
+    char* reg = smem + (wm + 2 * wn) * kWaveScratch;   // this wave's 32 KiB
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int tl = j * 32 + (lane & 31);             // token within the wave block

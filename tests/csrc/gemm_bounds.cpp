@@ -44,14 +44,14 @@ static void check_operand(const Plan& p, const Launch& l, int which, int64_t row
         }
       }
   if (nk > nfull)
-    for (int z = 0; z < 256 * 8; ++z) {
+    for (int z = 0; z < 256 * kTailLoads; ++z) {
       int64_t off;
       if (tail_src(form, g, row0, nfull * kBK, z, off)) {
         const int64_t e = base_off + off;
         if (e < 0 || e + 8 > alloc) fail("tail load out of bounds", e, alloc, z);
       }
       const int pos = tail_lds_pos(form, z);
-      if (pos < 0 || pos >= 2048) fail("tail lds position", pos, z, 0);
+      if (pos < 0 || pos >= 256 * kTailLoads) fail("tail lds position", pos, z, 0);
     }
 }
 
