@@ -98,9 +98,9 @@ FLCE_HD void tile_coords(int64_t b, int64_t M, int64_t Nn, int group_m, int64_t&
 // LDS swizzles. N form: 256 rows x 32 k, 64 B per row, 4 chunks of 16 B;
 // logical chunk c of row r at position c ^ swz_n(r). T form: 32 k-rows x 256
 // columns, 512 B per k-row, 32 chunks; logical chunk c of k-row k at
-// c ^ swz_t(k). Both keep the fragment reads conflict-free whether the LDS
-// serves 128 B or 256 B per clock.
-FLCE_HD int swz_n(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// c ^ swz_t(k). Both were chosen by measuring the LDS bank-conflict counter
+// on gfx950 for the fragment read patterns: zero conflicts.
+FLCE_HD int swz_n(int r) { return (r >> 2) & 3; }
 FLCE_HD int swz_t(int k) { return (0xCA60 >> (4 * (k & 3))) & 15; }  // {0,6,10,12}[k%4]
 
 // Direct-to-LDS loads: element offset of the tile base (k = 0) from the

@@ -322,12 +322,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A, Operand B, int6
   epi(acc, m0, n0, wm, wn, lane, smem);
 }
 
-__device__ __forceinline__ float softcap_fwd(float z, float s, float inv_s) {
-  return s * tanhf(z * inv_s);
+// tanh(x) = 1 - 2 / (exp(2x) + 1), from the hardware exp2 and reciprocal.
+// Exact limits +-1 for large |x|; absolute error a few 1e-7, which the
+// softcap scale s turns into a logit error of a few s * 1e-7.
+__device__ __forceinline__ float tanh_fast(float x) {
+  const float e = __builtin_amdgcn_exp2f(x * (2.f * kLog2e));
+  return 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
 }
 
 // ---- forward epilogue: per (vocab tile, token) max and sum-exp ------------
 // Tile rows are vocabulary ids (relative to v_off), columns are tokens.
+// SOFTCAP selects the s * tanh(z / s) variant at compile time.
+template <bool SOFTCAP>
 struct EpiLse {
   const int64_t* labels;
   int64_t N, V, ignore_index;
@@ -349,7 +355,7 @@ struct EpiLse {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float z = acc[i][j][r];
-          if (softcap > 0.f) z = softcap_fwd(z, softcap, inv_softcap);
+          if (SOFTCAP) z = softcap * tanh_fast(z * inv_softcap);
           const int64_t v = m0 + acc_row(wm, i, r, lane);
           acc[i][j][r] = v < V ? z : -INFINITY;
         }
@@ -415,6 +421,7 @@ struct EpiLse {
 // block in its own 32 KiB of LDS as [token][vocab] (a lane packs its 4
 // consecutive vocab values into 8 bytes; 8-byte slots XOR-swizzled by token),
 // then writes whole 16-byte runs of a token row to global memory.
+template <bool SOFTCAP>
 struct EpiGrad {
   const int64_t* labels;
   const float* lse;
@@ -456,8 +463,8 @@ struct EpiGrad {
             const int vl = i * 32 + 8 * rq + 4 * half + e;   // vocab within the wave block
             float z = acc[i][j][r];
             float d = 1.f;
-            if (softcap > 0.f) {
-              const float th = tanhf(z * inv_softcap);
+            if (SOFTCAP) {
+              const float th = tanh_fast(z * inv_softcap);
               z = softcap * th;
               d = 1.f - th * th;
             }
@@ -575,8 +582,12 @@ hipError_t run_gemm(const gemm::Launch& l, const Args& a, const Epi& e, int kind
 
 hipError_t bf16_forward(const Plan& p, const Args& a, const Launcher& L) {
   const gemm::Launch l = gemm::forward_launch(p);
-  EpiLse e{a.labels, p.N, p.V, a.ignore_index, a.softcap,
-           a.softcap > 0.f ? 1.f / a.softcap : 0.f, a.part, p.ld_part, a.zt};
+  if (a.softcap > 0.f) {
+    EpiLse<true> e{a.labels, p.N, p.V, a.ignore_index, a.softcap, 1.f / a.softcap, a.part,
+                   p.ld_part, a.zt};
+    return run_gemm<gemm::kFormN, gemm::kFormN>(l, a, e, kLseFwd, L);
+  }
+  EpiLse<false> e{a.labels, p.N, p.V, a.ignore_index, 0.f, 0.f, a.part, p.ld_part, a.zt};
   return run_gemm<gemm::kFormN, gemm::kFormN>(l, a, e, kLseFwd, L);
 }
 
@@ -585,10 +596,18 @@ hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, cons
   const int64_t vcur = gemm::chunk_rows(p, chunk);
   uint16_t* g = static_cast<uint16_t*>(a.g);
   // 1) recompute the logits of the chunk and form G[N][vchunk]
-  EpiGrad eg{a.labels, a.lse, a.sc, p.N, p.V, a.ignore_index, v0, vcur, p.vchunk, a.softcap,
-             a.softcap > 0.f ? 1.f / a.softcap : 0.f, g};
-  hipError_t err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a,
-                                                         eg, kGradLogits, L);
+  hipError_t err;
+  if (a.softcap > 0.f) {
+    EpiGrad<true> eg{a.labels, a.lse, a.sc, p.N, p.V, a.ignore_index, v0, vcur, p.vchunk,
+                     a.softcap, 1.f / a.softcap, g};
+    err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
+                                               kGradLogits, L);
+  } else {
+    EpiGrad<false> eg{a.labels, a.lse, a.sc, p.N, p.V, a.ignore_index, v0, vcur, p.vchunk,
+                      0.f, 0.f, g};
+    err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
+                                               kGradLogits, L);
+  }
   if (err != hipSuccess) return err;
   // 2) dW[v0:v0+vcur] = G^T . h
   EpiDW ew{static_cast<uint16_t*>(a.dW), p.H, v0, vcur, a.accumulate_dW};
