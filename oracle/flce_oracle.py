@@ -61,6 +61,7 @@ __all__ = [
     "grad_logits_rows",
     "flce_reference",
     "dW_rows",
+    "dH_rows",
     "micro_batch_scale",
 ]
 
@@ -246,6 +247,20 @@ def dW_rows(h, W, labels, lse, vocab_rows, *, c: float, ignore_index: int = -100
     if dcap is not None:
         G = G * dcap
     return G.T @ h
+
+
+def dH_rows(h_rows, W, labels_rows, lse_rows, *, c: float, ignore_index: int = -100,
+            softcap: float = 0.0) -> np.ndarray:
+    """dH for selected tokens: dH_i = sum_v G[i, v] W_v, with G from the token's own
+    logits row and its lse (only the token's row of the logits is needed)."""
+    h_rows = np.asarray(h_rows, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    labels_rows = np.asarray(labels_rows, dtype=np.int64).reshape(-1)
+    valid = valid_mask(labels_rows, ignore_index)
+    Zp, dcap = softcap_logits(h_rows @ W.T, softcap)
+    y = np.where(valid, labels_rows, 0)
+    G = grad_logits_rows(Zp, dcap, np.asarray(lse_rows, dtype=np.float64), y, valid, c)
+    return G @ W
 
 
 def micro_batch_scale(n_mb: int, n_total: int, reduction: str) -> float:

@@ -378,3 +378,6 @@ def test_forward_rows_and_dW_rows_match_full():
         rows = np.array([0, 5, 18])
         dw = orc.dW_rows(h, W, y, lse, rows, c=full.c, softcap=s)
         np.testing.assert_allclose(dw, full.dW[rows], rtol=1e-11, atol=1e-15)
+        toks = np.array([1, 4, 25])
+        dh = orc.dH_rows(h[toks], W, y[toks], lse[toks], c=full.c, softcap=s)
+        np.testing.assert_allclose(dh, full.dH[toks], rtol=1e-11, atol=1e-15)
