@@ -62,10 +62,8 @@ def read_traffic(kernel: str):
                 vals[k.strip()] = v.strip()
     if vals.get("source_digest") != kernel_source_digest():
         return None
-    if vals.get("kernel_kind") != kernel:
-        return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals[f"hbm_bytes_per_launch.{kernel}"])
     except (KeyError, ValueError):
         return None
 
