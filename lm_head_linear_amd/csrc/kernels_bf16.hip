@@ -46,6 +46,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   // Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
   return __builtin_bit_cast(uint16_t, __bf16(f));
 }
+// Two values rounded to nearest even and packed (lo = a) in one instruction.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const bf16x2 v = {__bf16(a), __bf16(b)};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 using gemm::Geom;
 using gemm::kBK;
@@ -168,9 +174,11 @@ __device__ __forceinline__ void wait_loads_in_flight(int64_t tiles) {
 // The empty asm statements keep the compiler from moving memory accesses
 // across it.
 __device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_sched_barrier(0);   // keep the step's MFMAs ahead of the wait
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // MFMA fragments of one 16-wide K substep for the wave's 128 x 128 block.
@@ -195,49 +203,52 @@ __device__ __forceinline__ void mfma_substep(f32x16 (&acc)[4][4], const Frags& f
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
-// Scheduling hints for one half K step: its 16 MFMAs, each followed by up to
-// one LDS fragment read and, in the second half, one direct global load, so
-// the reads for the next half and the loads for a later tile issue under the
-// MFMAs instead of stalling the wave's in-order stream.
-template <int FA, int FB, bool LOADS>
+// Fragments of a whole K step (two 16-wide substeps).
+struct StepFrags {
+  Frags s[2];
+};
+
+template <int FA, int FB>
+__device__ __forceinline__ void read_step(StepFrags& f, const char* sa, const char* sb, int wm,
+                                          int wn, int lane) {
+  read_substep<FA, FB>(f.s[0], sa, sb, 0, wm, wn, lane);
+  read_substep<FA, FB>(f.s[1], sa, sb, 1, wm, wn, lane);
+}
+
+// Scheduling hints for one K step: its 32 MFMAs, each followed by at most one
+// direct global load and one LDS fragment read, so the loads of a later tile
+// and the reads of the next step issue under the MFMAs instead of stalling
+// the wave's in-order stream.
+template <int FA, int FB>
 __device__ __forceinline__ void interleave_hints() {
-  constexpr int kReads = (FA == 0 ? 4 : 8) + (FB == 0 ? 4 : 8);
-  constexpr int kLoads = LOADS ? 2 * kLoadsPerOperand : 0;
+  constexpr int kReads = 2 * ((FA == 0 ? 4 : 8) + (FB == 0 ? 4 : 8));
+  constexpr int kLoads = 2 * kLoadsPerOperand;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
+  for (int q = 0; q < 32; ++q) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
     if (q < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read
-    if (q < kReads) __builtin_amdgcn_sched_group_barrier(0x100, (kReads + 15) / 16, 0);  // DS read
+    if (q < kReads) __builtin_amdgcn_sched_group_barrier(0x100, (kReads + 31) / 32, 0);  // DS read
   }
 }
 
-// First half of K step kt: read the fragments of substep 1 of tile kt while
-// multiplying substep 0 (already in registers).
+// One K step: start the direct loads of a later tile into its (free) stage,
+// read all fragments of the next tile, and multiply the current tile whose
+// fragments were read during the previous step. The stages are __restrict__
+// so the compiler does not order the direct-to-LDS writes against the reads;
+// the real dependencies are the counted vmcnt wait and the barrier at the top
+// of each step.
 template <int FA, int FB>
-__device__ __forceinline__ void half_a(f32x16 (&acc)[4][4], Frags& f0, Frags& f1,
-                                       const char* __restrict__ sa, const char* __restrict__ sb,
-                                       int wm, int wn, int lane) {
-  read_substep<FA, FB>(f1, sa, sb, 1, wm, wn, lane);
-  mfma_substep(acc, f0);
-  interleave_hints<FA, FB, false>();
-}
-
-// Second half of K step kt: start the direct loads of a later tile into its
-// (free) stage and read substep 0 of tile kt+1, while multiplying substep 1.
-// The stages are __restrict__ so the compiler does not order the
-// direct-to-LDS writes against these reads; the real dependencies are the
-// counted vmcnt waits and the barriers.
-template <int FA, int FB>
-__device__ __forceinline__ void half_b(f32x16 (&acc)[4][4], Frags& f0, const Frags& f1,
+__device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], const StepFrags& cur, StepFrags& nxt,
                                        const DirectLoads& da, const DirectLoads& db,
                                        int64_t load_tile, const char* __restrict__ na,
                                        const char* __restrict__ nb, char* __restrict__ la,
                                        char* __restrict__ lb, int wave, int wm, int wn, int lane) {
   issue_direct(da, load_tile, la, wave);
   issue_direct(db, load_tile, lb, wave);
-  read_substep<FA, FB>(f0, na, nb, 0, wm, wn, lane);
-  mfma_substep(acc, f1);
-  interleave_hints<FA, FB, true>();
+  read_step<FA, FB>(nxt, na, nb, wm, wn, lane);
+  mfma_substep(acc, cur.s[0]);
+  mfma_substep(acc, cur.s[1]);
+  interleave_hints<FA, FB>();
 }
 
 template <int FA, int FB, class Epi>
@@ -270,13 +281,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A, Operand B, int6
   auto st_b = [&](int64_t t) { return smem + (t % kStages) * 2 * kTileBytes + kTileBytes; };
   static_assert(gemm::kBK == 32, "two 16-wide substeps per K step");
   // Software pipeline over the full K tiles. Tile t is loaded (direct to LDS)
-  // kStages - 1 steps ahead. The barrier that makes tile kt+1 visible sits in
-  // the middle of step kt, so substep 0 of tile kt+1 is read while substep 1
-  // of tile kt is multiplied. The stage step kt loads into held tile kt-1,
-  // whose fragments every wave consumed before that step's barrier. Every
-  // step issues exactly one tile -- past the last tile it re-loads the last
-  // one into a free stage -- so the number of loads in flight at each wait is
-  // the same, and the body has no branches for the scheduler to stop at.
+  // kStages - 1 steps ahead; the fragments of tile kt+1 are read from LDS
+  // during step kt, a whole step before the MFMAs that use them. The barrier
+  // at the top of step kt publishes tile kt+1; the stage step kt loads into
+  // held tile kt-1, whose fragments every wave consumed in step kt-1, before
+  // that barrier. Every step issues exactly one tile -- past the last tile it
+  // re-loads the last one into a free stage -- so the number of loads in
+  // flight at each wait is the same and the body has no branches for the
+  // scheduler to stop at.
   if (nfull > 0) {
     const int64_t last = nfull - 1;
 #pragma unroll
@@ -284,16 +296,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A, Operand B, int6
       issue_direct(da, t < last ? t : last, st_a(t), wave);
       issue_direct(db, t < last ? t : last, st_b(t), wave);
     }
-    Frags f0, f1;
+    StepFrags f[2];
     wait_loads_in_flight(kStages - 2);             // tile 0 landed
     stage_barrier();
-    read_substep<FA, FB>(f0, st_a(0), st_b(0), 0, wm, wn, lane);
-    for (int64_t kt = 0; kt < nfull; ++kt) {
-      half_a<FA, FB>(acc, f0, f1, st_a(kt), st_b(kt), wm, wn, lane);
-      wait_loads_in_flight(kStages - 3);           // tile kt+1 landed
+    read_step<FA, FB>(f[0], st_a(0), st_b(0), wm, wn, lane);
+    int64_t kt = 0;
+    // two steps per iteration so the fragment buffers swap roles without copies
+    for (; kt + 1 < nfull; kt += 2) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int64_t k = kt + u;
+        __builtin_amdgcn_sched_barrier(0);
+        wait_loads_in_flight(kStages - 3);         // tile k+1 landed
+        stage_barrier();
+        const int64_t lt = k + kStages - 1;
+        k_step<FA, FB>(acc, f[u], f[u ^ 1], da, db, lt < last ? lt : last, st_a(k + 1),
+                       st_b(k + 1), st_a(lt), st_b(lt), wave, wm, wn, lane);
+      }
+    }
+    if (kt < nfull) {                              // odd number of steps: the last one
+      wait_loads_in_flight(kStages - 3);
       stage_barrier();
       const int64_t lt = kt + kStages - 1;
-      half_b<FA, FB>(acc, f0, f1, da, db, lt < last ? lt : last, st_a(kt + 1), st_b(kt + 1),
+      k_step<FA, FB>(acc, f[0], f[1], da, db, lt < last ? lt : last, st_a(kt + 1), st_b(kt + 1),
                      st_a(lt), st_b(lt), wave, wm, wn, lane);
     }
     // the re-loads past the last tile may still be in flight
@@ -435,32 +460,33 @@ struct EpiGrad {
     const float c = sc->c32;
     const int half = lane >> 5;
     char* reg = smem + (wm + 2 * wn) * kWaveScratch;   // this wave's 32 KiB
+    const int64_t vbase = v0 + m0 + wm * 128;           // global vocab id of block row 0
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int tl = j * 32 + (lane & 31);             // token within the wave block
       const int64_t t = n0 + wn * 128 + tl;
-      int64_t y = ignore_index;
-      float l = 0.f, coef = 0.f;
-      bool valid = false;
+      // Every token's lse is known (ignored ones too) and columns past N hold
+      // the logits of token N-1, so exp(z' - lse) <= 1 everywhere and a zero
+      // coefficient gives an exact zero.
+      const int64_t tc = t < N ? t : N - 1;
+      const float l = lse[tc];
+      float coef = 0.f;
+      int yd = -1;                                     // target row - 4 * half, or -1
       if (t < N) {
-        y = labels[t];
+        const int64_t y = labels[t];
         if (y != ignore_index) {
-          valid = true;
           coef = (y < 0 || y >= V) ? NAN : c;
-          l = lse[t];
+          if (y >= vbase && y < vbase + 128) yd = int(y - vbase) - 4 * half;
         }
       }
-      // target column relative to this wave's first vocab row (or out of range)
-      const int64_t ydiff = y - (v0 + m0 + wm * 128);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int rq = 0; rq < 4; ++rq) {
-          uint32_t packed[2];
+          float gv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * rq + e;
-            const int vl = i * 32 + 8 * rq + 4 * half + e;   // vocab within the wave block
             float z = acc[i][j][r];
             float d = 1.f;
             if (SOFTCAP) {
@@ -469,14 +495,14 @@ struct EpiGrad {
               d = 1.f - th * th;
             }
             const float p = __builtin_amdgcn_exp2f((z - l) * kLog2e);
-            const float oh = (ydiff == vl) ? 1.f : 0.f;
-            const float gv = valid ? (p - oh) * coef * d : 0.f;
-            const uint32_t b = f32_to_bf16(gv);
-            if (e & 1) packed[e >> 1] |= b << 16;
-            else packed[e >> 1] = b;
+            // (p - [v == y]) * coef, the one-hot as a selected subtrahend
+            const float sub = (yd == i * 32 + 8 * rq + e) ? coef : 0.f;
+            gv[e] = SOFTCAP ? (p * coef - sub) * d : fmaf(p, coef, -sub);
           }
+          const uint32_t lo = pack_bf16x2(gv[0], gv[1]);
+          const uint32_t hi = pack_bf16x2(gv[2], gv[3]);
           const int slot = (i * 8 + 2 * rq + half) ^ (tl & 31);
-          *reinterpret_cast<uint2*>(reg + tl * 256 + slot * 8) = make_uint2(packed[0], packed[1]);
+          *reinterpret_cast<uint2*>(reg + tl * 256 + slot * 8) = make_uint2(lo, hi);
         }
     }
     __syncthreads();
@@ -494,61 +520,113 @@ struct EpiGrad {
   }
 };
 
-// ---- dW epilogue: rows v0 + m of dW, bf16, optionally accumulated ---------
+// ---- row-major epilogues staged through LDS ---------------------------------
+// A wave's 128 x 128 float32 block goes out in 4 passes of 32 rows: the lane
+// values are written to the wave's LDS scratch as [32][128] float32 (the two
+// 128-byte column halves swapped every 4 rows, which keeps the writes of the
+// two half-waves on different banks), then read back as float4 runs of 4
+// consecutive columns of one row, which the caller's functor stores. Before
+// the staging of each pass the functor may issue its own global loads for that
+// pass (prefetch), so their latency overlaps the LDS traffic.
+__device__ __forceinline__ int staged_col(int row, int col) {
+  return col ^ (((row >> 2) & 1) << 5);
+}
+
+template <class Pass>
+__device__ __forceinline__ void staged_rows(f32x16 (&acc)[4][4], int wm, int wn, int lane,
+                                            char* smem, Pass& pass) {
+  float* reg = reinterpret_cast<float*>(smem + (wm + 2 * wn) * kWaveScratch);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pass.prefetch(i, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        reg[row * 128 + staged_col(row, j * 32 + (lane & 31))] = acc[i][j][r];
+      }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int idx = q * 64 + lane, row = idx >> 5, c4 = idx & 31;
+      const float4 v = *reinterpret_cast<const float4*>(reg + row * 128 + staged_col(row, 4 * c4));
+      pass.store(i, q, row, 4 * c4, v);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// ---- dW epilogue: rows v0 + m of dW, bf16, optionally added to ------------
+template <bool ACCUM>
 struct EpiDW {
   uint16_t* dW;
   int64_t H, v0, vcur;
-  int accumulate;
+
+  struct Pass {
+    const EpiDW& e;
+    int64_t r0, c0;   // global (chunk-relative row, column) of the wave block
+    __device__ __forceinline__ void prefetch(int, int) {}
+    __device__ __forceinline__ void store(int i, int, int row, int col, float4 v) {
+      const int64_t m = r0 + i * 32 + row, n = c0 + col;
+      if (m >= e.vcur || n >= e.H) return;
+      uint16_t* p = e.dW + (e.v0 + m) * e.H + n;
+      if (ACCUM) {
+        const uint2 o = *reinterpret_cast<const uint2*>(p);
+        v.x += bf16_to_f32(uint16_t(o.x)); v.y += bf16_to_f32(uint16_t(o.x >> 16));
+        v.z += bf16_to_f32(uint16_t(o.y)); v.w += bf16_to_f32(uint16_t(o.y >> 16));
+      }
+      *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+    }
+  };
 
   __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm,
-                                             int wn, int lane, char*) const {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + acc_col(wn, j, lane);
-      if (n >= H) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = m0 + acc_row(wm, i, r, lane);
-          if (m < vcur) {
-            const int64_t idx = (v0 + m) * H + n;
-            float x = acc[i][j][r];
-            if (accumulate) x += bf16_to_f32(dW[idx]);
-            dW[idx] = f32_to_bf16(x);
-          }
-        }
-    }
+                                             int wn, int lane, char* smem) const {
+    Pass pass{*this, m0 + wm * 128, n0 + wn * 128};
+    staged_rows(acc, wm, wn, lane, smem, pass);
   }
 };
 
 // ---- dH epilogue: accumulate over vocabulary chunks in a fixed order ------
+// FIRST: no running sum to add; LAST: store bf16 dH instead of the float32
+// running sum.
+template <bool FIRST, bool LAST>
 struct EpiDH {
   uint16_t* dH;
   float* acc32;  // [N][H] float32 running sum (unused with a single chunk)
   int64_t N, H;
-  int first, last;
+
+  struct Pass {
+    const EpiDH& e;
+    int64_t r0, c0;
+    float4 prev[16];
+    __device__ __forceinline__ void prefetch(int i, int lane) {
+      if (FIRST) return;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int idx = q * 64 + lane, row = idx >> 5, c4 = idx & 31;
+        const int64_t m = r0 + i * 32 + row, n = c0 + 4 * c4;
+        prev[q] = (m < e.N && n < e.H) ? *reinterpret_cast<const float4*>(e.acc32 + m * e.H + n)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    __device__ __forceinline__ void store(int i, int q, int row, int col, float4 v) {
+      const int64_t m = r0 + i * 32 + row, n = c0 + col;
+      if (m >= e.N || n >= e.H) return;
+      if (!FIRST) { v.x += prev[q].x; v.y += prev[q].y; v.z += prev[q].z; v.w += prev[q].w; }
+      if (LAST) {
+        *reinterpret_cast<uint2*>(e.dH + m * e.H + n) =
+            make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+      } else {
+        *reinterpret_cast<float4*>(e.acc32 + m * e.H + n) = v;
+      }
+    }
+  };
 
   __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm,
-                                             int wn, int lane, char*) const {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + acc_col(wn, j, lane);
-      if (n >= H) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t m = m0 + acc_row(wm, i, r, lane);
-          if (m < N) {
-            const int64_t idx = m * H + n;
-            float x = acc[i][j][r];
-            if (!first) x += acc32[idx];
-            if (last) dH[idx] = f32_to_bf16(x);
-            else acc32[idx] = x;
-          }
-        }
-    }
+                                             int wn, int lane, char* smem) const {
+    Pass pass{*this, m0 + wm * 128, n0 + wn * 128, {}};
+    staged_rows(acc, wm, wn, lane, smem, pass);
   }
 };
 
@@ -610,15 +688,28 @@ hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, cons
   }
   if (err != hipSuccess) return err;
   // 2) dW[v0:v0+vcur] = G^T . h
-  EpiDW ew{static_cast<uint16_t*>(a.dW), p.H, v0, vcur, a.accumulate_dW};
-  err = run_gemm<gemm::kFormT, gemm::kFormT>(gemm::backward_launch(p, chunk, 1), a, ew, kGemmDW,
-                                             L);
+  uint16_t* dW = static_cast<uint16_t*>(a.dW);
+  const gemm::Launch lw = gemm::backward_launch(p, chunk, 1);
+  if (a.accumulate_dW)
+    err = run_gemm<gemm::kFormT, gemm::kFormT>(lw, a, EpiDW<true>{dW, p.H, v0, vcur}, kGemmDW, L);
+  else
+    err = run_gemm<gemm::kFormT, gemm::kFormT>(lw, a, EpiDW<false>{dW, p.H, v0, vcur}, kGemmDW, L);
   if (err != hipSuccess) return err;
-  // 3) dH (+)= G[:, chunk] . W[chunk]
-  EpiDH eh{static_cast<uint16_t*>(a.dH), a.dh_acc, p.N, p.H, chunk == 0 ? 1 : 0,
-           chunk == p.n_chunks - 1 ? 1 : 0};
-  return run_gemm<gemm::kFormN, gemm::kFormT>(gemm::backward_launch(p, chunk, 2), a, eh, kGemmDH,
-                                              L);
+  // 3) dH (+)= G[:, chunk] . W[chunk], chunks in order
+  uint16_t* dH = static_cast<uint16_t*>(a.dH);
+  const gemm::Launch lh = gemm::backward_launch(p, chunk, 2);
+  const bool first = chunk == 0, last = chunk == p.n_chunks - 1;
+  if (first && last)
+    return run_gemm<gemm::kFormN, gemm::kFormT>(lh, a, EpiDH<true, true>{dH, a.dh_acc, p.N, p.H},
+                                                kGemmDH, L);
+  if (first)
+    return run_gemm<gemm::kFormN, gemm::kFormT>(lh, a, EpiDH<true, false>{dH, a.dh_acc, p.N, p.H},
+                                                kGemmDH, L);
+  if (last)
+    return run_gemm<gemm::kFormN, gemm::kFormT>(lh, a, EpiDH<false, true>{dH, a.dh_acc, p.N, p.H},
+                                                kGemmDH, L);
+  return run_gemm<gemm::kFormN, gemm::kFormT>(lh, a, EpiDH<false, false>{dH, a.dh_acc, p.N, p.H},
+                                              kGemmDH, L);
 }
 
 }  // namespace flce
