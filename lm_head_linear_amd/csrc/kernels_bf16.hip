@@ -219,15 +219,24 @@ __device__ __forceinline__ void read_step(StepFrags& f, const char* sa, const ch
 // direct global load and one LDS fragment read, so the loads of a later tile
 // and the reads of the next step issue under the MFMAs instead of stalling
 // the wave's in-order stream.
+// Scheduling hints for one K step: its 32 MFMAs, with the LDS fragment reads
+// of the next step and the direct global loads of a later tile placed
+// between them so they issue under the MFMAs instead of stalling the wave's
+// in-order stream. All reads go out in the first half of the step so they
+// have landed when the next step needs them. The placement of the loads was
+// chosen by timing: K-contiguous operands prefer them early, steps with
+// transpose reads prefer them in the second half.
 template <int FA, int FB>
 __device__ __forceinline__ void interleave_hints() {
   constexpr int kReads = 2 * ((FA == 0 ? 4 : 8) + (FB == 0 ? 4 : 8));
   constexpr int kLoads = 2 * kLoadsPerOperand;
+  constexpr int kPer = (kReads + 15) / 16;
+  constexpr int kLoad0 = (FA == 0 && FB == 0) ? 0 : 16;
 #pragma unroll
   for (int q = 0; q < 32; ++q) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
-    if (q < kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);     // VMEM read
-    if (q < kReads) __builtin_amdgcn_sched_group_barrier(0x100, (kReads + 31) / 32, 0);  // DS read
+    if (q >= kLoad0 && q < kLoad0 + kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    if (q < kReads / kPer) __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);  // DS read
   }
 }
 
