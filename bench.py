@@ -227,6 +227,28 @@ def main():
         log(f"  {k:18s} {v['ms_per_step']:8.3f} ms/step  {v['launches_per_step']:.0f} launches"
             + (f"  {v['tflops']:7.1f} TFLOP/s" if "tflops" in v else ""))
 
+    # The forward-only entry (loss and lse, no gradients) on the same inputs,
+    # timed the same way, after the step timing so it cannot disturb it.
+    fws = torch.empty(m.flce_forward_workspace_size(N, H, V, W.dtype), dtype=torch.uint8,
+                      device=dev)
+
+    def fwd():
+        m.flce_forward(h, W, y, ignore_index=w.ignore_index, softcap=w.softcap,
+                       reduction=w.reduction, workspace=fws, loss=loss, num_tokens=nt)
+
+    for _ in range(2):
+        fwd()
+    torch.cuda.synchronize()
+    tf0 = time.perf_counter()
+    for _ in range(args.steps):
+        fwd()
+    torch.cuda.synchronize()
+    f_ms = (time.perf_counter() - tf0) * 1e3 / args.steps
+    forward_only = {"ms_per_call": round(f_ms, 4), "tokens_per_s": round(N / (f_ms * 1e-3), 1),
+                    "tflops_2nhv": round(2 * nhv / (f_ms * 1e-3) / 1e12, 1),
+                    "workspace_bytes": int(fws.numel())}
+    log(f"forward only: {f_ms:.3f} ms/call, {forward_only['tflops_2nhv']:.1f} TFLOP/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_sample_tokens} sampled tokens ...")
@@ -257,6 +279,7 @@ def main():
         "extra_memory_bytes": int(peak_extra),
         "workspace_bytes": int(ws_bytes),
         "roofline": roofline,
+        "forward_only": forward_only,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "cpu_baseline": ({k: (round(v, 3) if isinstance(v, float) else v)

@@ -132,6 +132,53 @@ int flce_forward_backward(const void* h, const void* W, const int64_t* labels,
                           void* workspace, size_t workspace_bytes, int32_t* status,
                           float* lse_out);
 
+/*
+ * flce_forward_workspace_size -- bytes of device scratch that flce_forward
+ * needs (256-byte aligned base required): the per-tile log-sum-exp partials
+ * and the per-token lse and target logits only, O(N * V / 256 + N) bytes.
+ * Returns 0 for invalid sizes. Pure host arithmetic.
+ */
+size_t flce_forward_workspace_size(int64_t N, int64_t H, int64_t V, int dtype);
+
+/*
+ * flce_forward_check_args -- the synchronous argument checks of
+ * flce_forward, with its parameter list, without touching the GPU. The rules
+ * are those of flce_check_args minus everything about dH, dW and
+ * accumulate_dW; the workspace is checked against
+ * flce_forward_workspace_size(...).
+ */
+int flce_forward_check_args(const void* h, const void* W, const int64_t* labels,
+                            int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                            float softcap, int reduction, int64_t num_label_tokens,
+                            float* loss, int64_t* num_tokens, void* stream, int dtype,
+                            float mb_scale, void* workspace, size_t workspace_bytes,
+                            int32_t* status, float* lse_out);
+
+/*
+ * flce_forward -- the forward half alone: loss, num_tokens and (optionally)
+ * the per-token lse, with no gradients, for evaluation and any caller that
+ * needs the loss but not the logits (LlamaFactory error page "cross_entropy
+ * and fused_linear_cross_entropy cannot both be enabled", "What it means":
+ * the fused path is the one that never materialises logits; NeMo AutoModel
+ * linear_ce page, API: forward returns the scalar loss). It runs the same
+ * kernels as the forward part of flce_forward_backward on the same inputs,
+ * so *loss, *num_tokens, lse_out and *status are bit-identical to what that
+ * call returns; it costs one GEMM pass (2*N*H*V flops) instead of four.
+ *
+ * Parameters as in flce_forward_backward, without dH, dW and accumulate_dW.
+ * Workspace caller-owned, >= flce_forward_workspace_size(N, H, V, dtype)
+ *         bytes, 256-byte aligned; garbage on exit.
+ * Edge cases N = 0: loss 0, num_tokens 0. Every label ignored: loss 0.
+ * Data errors a non-ignored label outside [0, V) makes *status =
+ *         FLCE_ERR_LABEL and *loss = NaN (fail closed).
+ * Errors  see flce_forward_check_args; FLCE_ERR_HIP if a launch fails.
+ */
+int flce_forward(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H,
+                 int64_t V, int64_t ignore_index, float softcap, int reduction,
+                 int64_t num_label_tokens, float* loss, int64_t* num_tokens, void* stream,
+                 int dtype, float mb_scale, void* workspace, size_t workspace_bytes,
+                 int32_t* status, float* lse_out);
+
 /* flce_status_string -- a static, human-readable name for a status code. */
 const char* flce_status_string(int status);
 

@@ -14,7 +14,9 @@ Contracts (see include/flce.h):
   discussion 7), the loss is float32 for bf16 inputs (Modalities PR 464), and
   the softcap ``s*tanh(z/s)`` is applied on every path (twinkle PR 335 item 3).
 * The forward call computes dH and dW as well; ``backward`` only scales them by
-  the incoming gradient.
+  the incoming gradient. When no gradient is wanted (``torch.no_grad()``, or
+  neither input requires one) the forward-only entry runs instead: the same
+  loss at a quarter of the work.
 """
 from __future__ import annotations
 
@@ -29,6 +31,9 @@ __all__ = [
     "flce_workspace_size",
     "flce_check_args",
     "flce_forward_backward",
+    "flce_forward",
+    "flce_forward_workspace_size",
+    "flce_forward_check_args",
     "flce_status_string",
     "flce_vocab_chunk",
     "flce_profile_begin",
@@ -77,6 +82,10 @@ def flce_workspace_size(N: int, H: int, V: int, dtype: torch.dtype) -> int:
     return int(_lib.load().flce_workspace_size(N, H, V, _dtype_code(dtype)))
 
 
+def flce_forward_workspace_size(N: int, H: int, V: int, dtype: torch.dtype) -> int:
+    return int(_lib.load().flce_forward_workspace_size(N, H, V, _dtype_code(dtype)))
+
+
 def flce_vocab_chunk(N: int, H: int, V: int, dtype: torch.dtype) -> int:
     return int(_lib.load().flce_vocab_chunk(N, H, V, _dtype_code(dtype)))
 
@@ -100,6 +109,26 @@ def flce_check_args(h, W, labels, *, N, H, V, ignore_index=-100, softcap=0.0, re
                      loss, num_tokens, dH, dW, None, dtype, mb_scale, accumulate_dW, workspace,
                      status, lse_out)
     return int(_lib.load().flce_check_args(*args))
+
+
+def _fwd_abi_args(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens,
+                  loss, num_tokens, stream, dtype, mb_scale, workspace, status, lse_out):
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return (_ptr(h), _ptr(W), _ptr(labels), N, H, V, int(ignore_index), float(softcap),
+            _red_code(reduction), int(num_label_tokens or 0), _ptr(loss), _ptr(num_tokens),
+            stream, _dtype_code(dtype), float(mb_scale), _ptr(workspace), ws_bytes,
+            _ptr(status), _ptr(lse_out))
+
+
+def flce_forward_check_args(h, W, labels, *, N, H, V, ignore_index=-100, softcap=0.0,
+                            reduction="sum", num_label_tokens=None, loss=None, num_tokens=None,
+                            dtype=torch.bfloat16, mb_scale=1.0, workspace=None, status=None,
+                            lse_out=None) -> int:
+    """The forward-only entry's synchronous checks (no GPU work); a status code."""
+    args = _fwd_abi_args(h, W, labels, N, H, V, ignore_index, softcap, reduction,
+                         num_label_tokens, loss, num_tokens, None, dtype, mb_scale, workspace,
+                         status, lse_out)
+    return int(_lib.load().flce_forward_check_args(*args))
 
 
 def _check_tensor(name, t, shape, dtype, device):
@@ -170,6 +199,53 @@ def flce_forward_backward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor
     if rc != _lib.OK:
         raise FlceError(rc, "flce_forward_backward")
     return loss, num_tokens, dH, dW
+
+
+def flce_forward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, *,
+                 ignore_index: int = -100, softcap: float = 0.0, reduction: str = "sum",
+                 num_label_tokens: Optional[int] = None, mb_scale: float = 1.0,
+                 workspace: Optional[torch.Tensor] = None,
+                 lse_out: Optional[torch.Tensor] = None,
+                 status: Optional[torch.Tensor] = None,
+                 loss: Optional[torch.Tensor] = None,
+                 num_tokens: Optional[torch.Tensor] = None):
+    """Forward only (no gradients) on the current stream: (loss, num_tokens).
+
+    Same inputs and contracts as :func:`flce_forward_backward`; the loss,
+    count, lse and status are bit-identical to that call's.
+    """
+    if h.dim() != 2 or W.dim() != 2:
+        raise ValueError("h must be [N, H] and W [V, H]")
+    N, H = h.shape
+    V = W.shape[0]
+    dev = W.device
+    if dev.type != "cuda":
+        raise ValueError("flce_forward runs on a GPU; tensors are on " + str(dev))
+    _check_tensor("h", h, (N, H), W.dtype, dev)
+    _check_tensor("W", W, (V, H), W.dtype, dev)
+    _check_tensor("labels", labels, (N,), torch.int64, dev)
+    if loss is None:
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+    if num_tokens is None:
+        num_tokens = torch.empty((), dtype=torch.int64, device=dev)
+    if lse_out is not None:
+        _check_tensor("lse_out", lse_out, (N,), torch.float32, dev)
+    if status is not None:
+        _check_tensor("status", status, (), torch.int32, dev)
+    need = flce_forward_workspace_size(N, H, V, W.dtype)
+    if need == 0:
+        raise FlceError(_lib.ERR_ARG, "flce_forward_workspace_size")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    args = _fwd_abi_args(h, W, labels, N, H, V, ignore_index, softcap, reduction,
+                         num_label_tokens, loss, num_tokens, stream, W.dtype, mb_scale,
+                         workspace, status, lse_out)
+    with torch.cuda.device(dev):
+        rc = _lib.load().flce_forward(*args)
+    if rc != _lib.OK:
+        raise FlceError(rc, "flce_forward")
+    return loss, num_tokens
 
 
 def flce_profile_begin() -> None:
@@ -243,6 +319,10 @@ def fused_linear_cross_entropy(hidden_states: torch.Tensor, labels: torch.Tensor
     H = hidden_states.shape[-1]
     h = hidden_states.reshape(-1, H).contiguous()
     y = labels.reshape(-1).contiguous()
+    if not (torch.is_grad_enabled() and (hidden_states.requires_grad or lm_weight.requires_grad)):
+        return flce_forward(h.detach(), lm_weight.detach().contiguous(), y,
+                            ignore_index=ignore_index, softcap=softcap, reduction=reduction,
+                            num_label_tokens=num_label_tokens, mb_scale=mb_scale)
     return FLCEFunction.apply(h, lm_weight.contiguous(), y, ignore_index, softcap, reduction,
                               num_label_tokens, mb_scale)
 

@@ -16,10 +16,15 @@ _c = ctypes
 _vp, _i64, _i32, _f32, _sz = _c.c_void_p, _c.c_int64, _c.c_int, _c.c_float, _c.c_size_t
 _FB_ARGS = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _i32, _i64, _vp, _vp, _vp, _vp,
             _vp, _i32, _f32, _i32, _vp, _sz, _vp, _vp]
+_F_ARGS = [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _i32, _i64, _vp, _vp, _vp, _i32,
+           _f32, _vp, _sz, _vp, _vp]
 SIGNATURES = {
     "flce_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
     "flce_check_args": (_i32, _FB_ARGS),
     "flce_forward_backward": (_i32, _FB_ARGS),
+    "flce_forward_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
+    "flce_forward_check_args": (_i32, _F_ARGS),
+    "flce_forward": (_i32, _F_ARGS),
     "flce_status_string": (_c.c_char_p, [_i32]),
     "flce_vocab_chunk": (_i64, [_i64, _i64, _i64, _i32]),
     "flce_profile_begin": (_i32, []),

@@ -57,22 +57,16 @@ const char* kKindNames[flce::kNumKinds] = {"label_scan", "lse_fwd_gemm", "lse_me
                                            "loss_final", "grad_logits_gemm", "dW_gemm",
                                            "dH_gemm", "fill"};
 
-}  // namespace
-
-extern "C" {
-
-int flce_forward_backward(const void* h, const void* W, const int64_t* labels, int64_t N,
-                          int64_t H, int64_t V, int64_t ignore_index, float softcap,
-                          int reduction, int64_t num_label_tokens, float* loss,
-                          int64_t* num_tokens, void* dH, void* dW, void* stream, int dtype,
-                          float mb_scale, int accumulate_dW, void* workspace,
-                          size_t workspace_bytes, int32_t* status, float* lse_out) {
-  int st = flce_check_args(h, W, labels, N, H, V, ignore_index, softcap, reduction,
-                           num_label_tokens, loss, num_tokens, dH, dW, stream, dtype, mb_scale,
-                           accumulate_dW, workspace, workspace_bytes, status, lse_out);
-  if (st != FLCE_OK) return st;
+// The launch sequence of both entry points; arguments already checked.
+// Forward: label scan, forward GEMM with the log-sum-exp partials, merge and
+// loss. With backward, then every vocabulary chunk's gradient GEMMs.
+int run(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H, int64_t V,
+        int64_t ignore_index, float softcap, int reduction, int64_t num_label_tokens,
+        float* loss, int64_t* num_tokens, void* dH, void* dW, void* stream, int dtype,
+        float mb_scale, int accumulate_dW, void* workspace, int32_t* status, float* lse_out,
+        bool backward) {
   flce::Plan p;
-  if (!flce::make_plan(N, H, V, dtype, &p)) return FLCE_ERR_ARG;
+  if (!flce::make_plan(N, H, V, dtype, &p, backward)) return FLCE_ERR_ARG;
 
   flce::Launcher L{static_cast<hipStream_t>(stream), nullptr, nullptr};
   if (g_prof.on) { L.before = prof_before; L.after = prof_after; }
@@ -91,7 +85,7 @@ int flce_forward_backward(const void* h, const void* W, const int64_t* labels, i
   hipError_t e;
   if (N == 0) {
     e = flce::launch_empty(p, a, L);
-    if (e == hipSuccess && !a.accumulate_dW)
+    if (e == hipSuccess && backward && !a.accumulate_dW)
       e = flce::launch_zero_bytes(dW, size_t(V) * H * p.elem, L);
     return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
   }
@@ -99,16 +93,49 @@ int flce_forward_backward(const void* h, const void* W, const int64_t* labels, i
   a.zt = reinterpret_cast<float*>(ws + p.off_zt);
   a.lse = reinterpret_cast<float*>(ws + p.off_lse);
   a.lsum = reinterpret_cast<double*>(ws + p.off_lsum);
-  a.g = ws + p.off_g;
+  a.g = backward ? ws + p.off_g : nullptr;
   a.dh_acc = p.need_dh_acc ? reinterpret_cast<float*>(ws + p.off_dhacc) : nullptr;
 
   const bool bf16 = dtype == FLCE_BF16;
   e = flce::launch_label_scan(p, a, L);
   if (e == hipSuccess) e = bf16 ? flce::bf16_forward(p, a, L) : flce::f32_forward(p, a, L);
   if (e == hipSuccess) e = flce::launch_merge_and_loss(p, a, L);
-  for (int64_t c = 0; e == hipSuccess && c < p.n_chunks; ++c)
+  for (int64_t c = 0; backward && e == hipSuccess && c < p.n_chunks; ++c)
     e = bf16 ? flce::bf16_backward_chunk(p, a, c, L) : flce::f32_backward_chunk(p, a, c, L);
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int flce_forward_backward(const void* h, const void* W, const int64_t* labels, int64_t N,
+                          int64_t H, int64_t V, int64_t ignore_index, float softcap,
+                          int reduction, int64_t num_label_tokens, float* loss,
+                          int64_t* num_tokens, void* dH, void* dW, void* stream, int dtype,
+                          float mb_scale, int accumulate_dW, void* workspace,
+                          size_t workspace_bytes, int32_t* status, float* lse_out) {
+  int st = flce_check_args(h, W, labels, N, H, V, ignore_index, softcap, reduction,
+                           num_label_tokens, loss, num_tokens, dH, dW, stream, dtype, mb_scale,
+                           accumulate_dW, workspace, workspace_bytes, status, lse_out);
+  if (st != FLCE_OK) return st;
+  return run(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens, loss,
+             num_tokens, dH, dW, stream, dtype, mb_scale, accumulate_dW, workspace, status,
+             lse_out, true);
+}
+
+int flce_forward(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H,
+                 int64_t V, int64_t ignore_index, float softcap, int reduction,
+                 int64_t num_label_tokens, float* loss, int64_t* num_tokens, void* stream,
+                 int dtype, float mb_scale, void* workspace, size_t workspace_bytes,
+                 int32_t* status, float* lse_out) {
+  int st = flce_forward_check_args(h, W, labels, N, H, V, ignore_index, softcap, reduction,
+                                   num_label_tokens, loss, num_tokens, stream, dtype, mb_scale,
+                                   workspace, workspace_bytes, status, lse_out);
+  if (st != FLCE_OK) return st;
+  return run(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens, loss,
+             num_tokens, nullptr, nullptr, stream, dtype, mb_scale, 0, workspace, status,
+             lse_out, false);
 }
 
 int flce_profile_begin(void) {

@@ -26,7 +26,7 @@ int64_t env_vchunk() {
 
 }  // namespace
 
-bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p) {
+bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backward) {
   if (N < 0 || H <= 0 || V <= 0) return false;
   if (dtype != FLCE_F32 && dtype != FLCE_BF16) return false;
   // Keep every size product far from int64 overflow.
@@ -50,7 +50,8 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p) {
   q.vchunk = vc;
   q.n_chunks = ceil_div(V, vc);
   q.n_loss_blocks = ceil_div(N > 0 ? N : 1, 32);   // tokens per lse-merge block
-  q.need_dh_acc = (dtype == FLCE_BF16) && q.n_chunks > 1 && N > 0;
+  q.backward = backward;
+  q.need_dh_acc = backward && (dtype == FLCE_BF16) && q.n_chunks > 1 && N > 0;
 
   size_t off = 0;
   q.off_scalars = off; off = align256(off + sizeof(Scalars));
@@ -59,7 +60,7 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p) {
     q.off_zt = off;    off = align256(off + size_t(q.ld_part) * sizeof(float));
     q.off_lse = off;   off = align256(off + size_t(q.ld_part) * sizeof(float));
     q.off_lsum = off;  off = align256(off + size_t(q.n_loss_blocks) * sizeof(double));
-    q.off_g = off;     off = align256(off + size_t(q.vchunk) * q.ldg * q.elem);
+    if (backward) { q.off_g = off; off = align256(off + size_t(q.vchunk) * q.ldg * q.elem); }
     if (q.need_dh_acc) { q.off_dhacc = off; off = align256(off + size_t(N) * H * sizeof(float)); }
   }
   q.total = off;
@@ -89,6 +90,57 @@ static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+size_t flce_forward_workspace_size(int64_t N, int64_t H, int64_t V, int dtype) {
+  flce::Plan p;
+  if (!flce::make_plan(N, H, V, dtype, &p, false)) return 0;
+  return p.total;
+}
+
+}  // extern "C"
+
+namespace {
+
+bool misaligned(const void* q, uintptr_t mask) { return (reinterpret_cast<uintptr_t>(q) & mask) != 0; }
+
+// Checks shared by both entry points, in the order they are reported:
+// argument errors, then unsupported layouts, then the workspace. dH and dW
+// are NULL for the forward-only entry, which has no gradient outputs.
+int check_common(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H,
+                 int64_t V, float softcap, int reduction, int64_t num_label_tokens,
+                 const float* loss, const int64_t* num_tokens, const void* dH, const void* dW,
+                 int dtype, float mb_scale, const void* workspace, size_t workspace_bytes,
+                 bool backward) {
+  if (N < 0 || H <= 0 || V <= 0) return FLCE_ERR_ARG;
+  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_ERR_ARG;
+  if (reduction != FLCE_SUM && reduction != FLCE_MEAN) return FLCE_ERR_ARG;
+  if (!(softcap >= 0.0f) || !std::isfinite(softcap)) return FLCE_ERR_ARG;
+  if (!std::isfinite(mb_scale)) return FLCE_ERR_ARG;
+  if (reduction == FLCE_MEAN && num_label_tokens > 0) return FLCE_ERR_ARG;
+  if (!loss || !num_tokens || !W) return FLCE_ERR_ARG;
+  if (N > 0 && (!h || !labels)) return FLCE_ERR_ARG;
+  if (backward && (!dW || (N > 0 && !dH))) return FLCE_ERR_ARG;
+  flce::Plan p;
+  if (!flce::make_plan(N, H, V, dtype, &p, backward)) return FLCE_ERR_ARG;
+  const size_t es = p.elem;
+  if (backward) {
+    if (overlaps(dH, size_t(N) * H * es, h, size_t(N) * H * es)) return FLCE_ERR_ARG;
+    if (overlaps(dW, size_t(V) * H * es, W, size_t(V) * H * es)) return FLCE_ERR_ARG;
+  }
+  const uintptr_t mask = dtype == FLCE_BF16 ? 15u : 3u;
+  if (dtype == FLCE_BF16 && H % 8 != 0) return FLCE_ERR_UNSUPPORTED;
+  if (misaligned(W, mask) || (N > 0 && misaligned(h, mask))) return FLCE_ERR_UNSUPPORTED;
+  if (backward && (misaligned(dW, mask) || (N > 0 && misaligned(dH, mask))))
+    return FLCE_ERR_UNSUPPORTED;
+  if (!workspace) return FLCE_ERR_WORKSPACE;
+  if (misaligned(workspace, 255u)) return FLCE_ERR_WORKSPACE;
+  if (workspace_bytes < p.total) return FLCE_ERR_WORKSPACE;
+  return FLCE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int flce_check_args(const void* h, const void* W, const int64_t* labels,
                     int64_t N, int64_t H, int64_t V, int64_t ignore_index,
                     float softcap, int reduction, int64_t num_label_tokens,
@@ -97,31 +149,20 @@ int flce_check_args(const void* h, const void* W, const int64_t* labels,
                     void* workspace, size_t workspace_bytes, int32_t* status,
                     float* lse_out) {
   (void)ignore_index; (void)stream; (void)accumulate_dW; (void)status; (void)lse_out;
-  if (N < 0 || H <= 0 || V <= 0) return FLCE_ERR_ARG;
-  if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_ERR_ARG;
-  if (reduction != FLCE_SUM && reduction != FLCE_MEAN) return FLCE_ERR_ARG;
-  if (!(softcap >= 0.0f) || !std::isfinite(softcap)) return FLCE_ERR_ARG;
-  if (!std::isfinite(mb_scale)) return FLCE_ERR_ARG;
-  if (reduction == FLCE_MEAN && num_label_tokens > 0) return FLCE_ERR_ARG;
-  if (!loss || !num_tokens || !W || !dW) return FLCE_ERR_ARG;
-  if (N > 0 && (!h || !labels || !dH)) return FLCE_ERR_ARG;
-  flce::Plan p;
-  if (!flce::make_plan(N, H, V, dtype, &p)) return FLCE_ERR_ARG;
-  const size_t es = p.elem;
-  if (overlaps(dH, size_t(N) * H * es, h, size_t(N) * H * es)) return FLCE_ERR_ARG;
-  if (overlaps(dW, size_t(V) * H * es, W, size_t(V) * H * es)) return FLCE_ERR_ARG;
-  if (dtype == FLCE_BF16) {
-    if (H % 8 != 0) return FLCE_ERR_UNSUPPORTED;
-    auto mis = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15u) != 0; };
-    if (mis(W) || mis(dW) || (N > 0 && (mis(h) || mis(dH)))) return FLCE_ERR_UNSUPPORTED;
-  } else {
-    auto mis = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 3u) != 0; };
-    if (mis(W) || mis(dW) || (N > 0 && (mis(h) || mis(dH)))) return FLCE_ERR_UNSUPPORTED;
-  }
-  if (!workspace) return FLCE_ERR_WORKSPACE;
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return FLCE_ERR_WORKSPACE;
-  if (workspace_bytes < p.total) return FLCE_ERR_WORKSPACE;
-  return FLCE_OK;
+  return check_common(h, W, labels, N, H, V, softcap, reduction, num_label_tokens, loss,
+                      num_tokens, dH, dW, dtype, mb_scale, workspace, workspace_bytes, true);
+}
+
+int flce_forward_check_args(const void* h, const void* W, const int64_t* labels,
+                            int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                            float softcap, int reduction, int64_t num_label_tokens,
+                            float* loss, int64_t* num_tokens, void* stream, int dtype,
+                            float mb_scale, void* workspace, size_t workspace_bytes,
+                            int32_t* status, float* lse_out) {
+  (void)ignore_index; (void)stream; (void)status; (void)lse_out;
+  return check_common(h, W, labels, N, H, V, softcap, reduction, num_label_tokens, loss,
+                      num_tokens, nullptr, nullptr, dtype, mb_scale, workspace,
+                      workspace_bytes, false);
 }
 
 const char* flce_status_string(int s) {

@@ -36,6 +36,7 @@ struct Plan {
   int64_t vchunk = 0;        // vocabulary rows per backward chunk
   int64_t n_chunks = 0;
   int64_t n_loss_blocks = 0; // blocks of the lse-merge kernel (32 tokens each)
+  bool backward = true;      // plan includes the gradient buffers
   bool need_dh_acc = false;  // float32 dH accumulator needed (bf16, >1 chunk)
   size_t elem = 0;           // bytes per element of h/W/G
   // byte offsets into the workspace
@@ -43,7 +44,9 @@ struct Plan {
          off_g = 0, off_dhacc = 0, total = 0;
 };
 
-// Builds the plan; returns false for invalid sizes or dtype.
-bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p);
+// Builds the plan; returns false for invalid sizes or dtype. A forward-only
+// plan (backward = false) carves no logit-gradient chunk and no dH
+// accumulator, so its workspace is the forward's alone.
+bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backward = true);
 
 }  // namespace flce

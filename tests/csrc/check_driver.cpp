@@ -22,6 +22,14 @@ static int call(int64_t N, int64_t H, int64_t V, int dtype, int red, int64_t T, 
                          nullptr, dtype, mb, 0, (void*)ws, wsb, nullptr, nullptr);
 }
 
+static int fcall(int64_t N, int64_t H, int64_t V, int dtype, int red, int64_t T, float s,
+                 size_t wsb) {
+  const uintptr_t b = uintptr_t(1) << 32;
+  return flce_forward_check_args((void*)b, (void*)(b * 2), (int64_t*)(b * 3), N, H, V, -100, s,
+                                 red, T, (float*)(b * 4), (int64_t*)(b * 5), nullptr, dtype, 1.f,
+                                 (void*)(uintptr_t(1) << 40), wsb, nullptr, nullptr);
+}
+
 int main() {
   const size_t big = size_t(1) << 40;
   EXPECT(call(8192, 4096, 131072, FLCE_BF16, FLCE_MEAN, 0, 0.f, 1.f, big) == FLCE_OK);
@@ -44,6 +52,19 @@ int main() {
       EXPECT(w > 0 && w % 256 == 0);
       const int64_t c = flce_vocab_chunk(n, 64, v, FLCE_BF16);
       EXPECT(c >= 256 && c % 256 == 0);
+    }
+  // forward-only entry: same rules, its own (smaller) workspace
+  EXPECT(fcall(8192, 4096, 131072, FLCE_BF16, FLCE_MEAN, 0, 0.f, big) == FLCE_OK);
+  EXPECT(fcall(8192, 4096, 131072, FLCE_BF16, FLCE_MEAN, 5, 0.f, big) == FLCE_ERR_ARG);
+  EXPECT(fcall(int64_t(1) << 40, 8, 5, FLCE_BF16, FLCE_SUM, 0, 0.f, big) == FLCE_ERR_ARG);
+  EXPECT(flce_forward_workspace_size(INT64_MAX, INT64_MAX, INT64_MAX, FLCE_BF16) == 0);
+  for (int64_t n : {0, 1, 257, 16384})
+    for (int64_t v : {1, 257, 256000}) {
+      const size_t f = flce_forward_workspace_size(n, 64, v, FLCE_BF16);
+      const size_t w = flce_workspace_size(n, 64, v, FLCE_BF16);
+      EXPECT(f > 0 && f % 256 == 0 && (n > 0 ? f < w : f == w));
+      EXPECT(fcall(n, 64, v, FLCE_BF16, FLCE_SUM, 0, 0.f, f) == FLCE_OK);
+      EXPECT(fcall(n, 64, v, FLCE_BF16, FLCE_SUM, 0, 0.f, f - 1) == FLCE_ERR_WORKSPACE);
     }
   for (int s = -1; s < 8; ++s) EXPECT(flce_status_string(s) != nullptr);
   if (failures == 0) std::printf("all checks passed\n");

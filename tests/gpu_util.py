@@ -44,6 +44,25 @@ def run_gpu(w: fi.Workload, *, mb_scale=1.0, lse=True, dev=None, **kw):
                 lse=lse_out, status=int(status.item()))
 
 
+def run_gpu_forward(w: fi.Workload, *, mb_scale=1.0, dev=None, **kw):
+    """The forward-only entry on the same inputs: loss, num_tokens, lse, status."""
+    import lm_head_linear_amd as m
+    dev = dev or device()
+    h = w.h.reshape(-1, w.H).to(dev)
+    W = w.W.to(dev)
+    y = w.labels.reshape(-1).to(dev)
+    lse_out = torch.full((h.shape[0],), float("nan"), dtype=torch.float32, device=dev)
+    status = torch.full((), -1, dtype=torch.int32, device=dev)
+    args = dict(ignore_index=w.ignore_index, softcap=w.softcap, reduction=w.reduction,
+                num_label_tokens=w.num_label_tokens, mb_scale=mb_scale, lse_out=lse_out,
+                status=status)
+    args.update(kw)
+    loss, nt = m.flce_forward(h, W, y, **args)
+    torch.cuda.synchronize(dev)
+    return dict(loss=float(loss.item()), loss_t=loss, num_tokens=int(nt.item()), lse=lse_out,
+                status=int(status.item()))
+
+
 def run_oracle(w: fi.Workload, *, mb_scale=1.0, **kw):
     h = w.h.reshape(-1, w.H).to(torch.float64).numpy()
     W = w.W.to(torch.float64).numpy()

@@ -182,3 +182,67 @@ def test_sanitized_host_checks(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "all checks passed" in r.stdout
+
+
+# ------------------------------------------------------- forward-only entry
+def _fargs(**kw):
+    a = dict(zip(("h", "W", "labels", "N", "H", "V", "ignore", "softcap", "red", "T", "loss",
+                  "nt", "dH", "dW", "stream", "dtype", "mb", "acc", "ws", "wsb", "status",
+                  "lse"), _args(**kw)))
+    return [a[k] for k in ("h", "W", "labels", "N", "H", "V", "ignore", "softcap", "red", "T",
+                           "loss", "nt", "stream", "dtype", "mb", "ws", "wsb", "status", "lse")]
+
+
+def test_forward_workspace_is_the_forward_part(lib):
+    """The forward-only plan carves the log-sum-exp partials and per-token
+    arrays but no gradient chunk and no dH accumulator."""
+    for N, H, V in [(8192, 4096, 131072), (8192, 3584, 256000), (32, 64, 1024), (1, 8, 1)]:
+        for dt in (0, 1):
+            f = lib.flce_forward_workspace_size(N, H, V, dt)
+            full = lib.flce_workspace_size(N, H, V, dt)
+            assert 0 < f < full
+            n_tiles = -(-V // (256 if dt == 1 else 64))
+            assert f <= 256 + n_tiles * (N + 256) * 8 + 3 * (N + 256) * 8 + 4 * 256
+    assert lib.flce_forward_workspace_size(-1, 8, 8, 1) == 0
+    assert lib.flce_forward_workspace_size(0, 8, 8, 1) > 0
+
+
+def test_forward_check_args_ok(lib):
+    assert lib.flce_forward_check_args(*_fargs()) == 0
+    assert lib.flce_forward_check_args(*_fargs(dtype=0, H=3)) == 0
+    # a workspace big enough for the forward only is accepted by the forward entry
+    f = lib.flce_forward_workspace_size(64, 64, 128, 1)
+    assert lib.flce_forward_check_args(*_fargs(wsb=f)) == 0
+    assert lib.flce_check_args(*_args(wsb=f)) == 3
+    assert lib.flce_forward_check_args(*_fargs(wsb=f - 1)) == 3
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), 1), (dict(H=0), 1), (dict(V=0), 1),
+    (dict(red=2), 1), (dict(dtype=5), 1),
+    (dict(softcap=-1.0), 1), (dict(softcap=float("nan")), 1), (dict(mb=float("inf")), 1),
+    (dict(red=1, T=10), 1),
+    (dict(h=None), 1), (dict(W=None), 1), (dict(labels=None), 1), (dict(loss=None), 1),
+    (dict(nt=None), 1),
+    (dict(H=12), 2), (dict(h=A16 + 8), 2), (dict(W=A16 * 64 + 4), 2),
+    (dict(ws=None), 3), (dict(ws=A16 * 1024 + 128), 3), (dict(wsb=16), 3),
+])
+def test_forward_check_args_errors(lib, kw, code):
+    assert lib.flce_forward_check_args(*_fargs(**kw)) == code
+
+
+def test_forward_rejects_before_launch(lib):
+    assert lib.flce_forward(*_fargs(N=-1)) == 1
+    assert lib.flce_forward(*_fargs(wsb=1)) == 3
+    assert lib.flce_forward_check_args(*_fargs(N=0, h=None, labels=None)) == 0
+
+
+def test_python_forward_validation_without_gpu():
+    import lm_head_linear_amd as m
+    h = torch.zeros(4, 8, dtype=torch.bfloat16)
+    W = torch.zeros(16, 8, dtype=torch.bfloat16)
+    y = torch.zeros(4, dtype=torch.int64)
+    with pytest.raises(ValueError):
+        m.flce_forward(h, W, y)                   # CPU tensors: refused, no fallback
+    with torch.no_grad(), pytest.raises(ValueError):
+        m.fused_linear_cross_entropy(h, y, W)     # forward-only route, same refusal

@@ -95,17 +95,27 @@ def _check(k, g, *, T=None, mb_scale=1.0, label=""):
     assert bool(torch.isfinite(g["dW"].float()).all())
 
 
+def _forward_only_matches(w, g):
+    """The forward-only entry returns the same loss, count and lse bits."""
+    f = gu.run_gpu_forward(w)
+    assert f["loss_t"].view(torch.int32).item() == g["loss_t"].view(torch.int32).item()
+    assert f["num_tokens"] == g["num_tokens"] and f["status"] == g["status"] == 0
+    assert torch.equal(f["lse"].view(torch.int32), g["lse"].view(torch.int32))
+
+
 def test_large_vocab_full():
     w = _case(3)[0]
     g = gu.run_gpu(w)
     assert g["num_tokens"] == 0          # 'mean'
     _check(3, g, label="large_vocab")
+    _forward_only_matches(w, g)
 
 
 def test_softcapped_full():
     w = _case(4)[0]
     g = gu.run_gpu(w)
     _check(4, g, label="softcapped")
+    _forward_only_matches(w, g)
 
 
 def test_long_full_and_external_count():
