@@ -18,13 +18,24 @@ namespace flce {
 namespace gemm {
 
 constexpr int kBM = 256;                // tile edge (M and N)
-constexpr int kBK = 32;                 // K step
-constexpr int kStages = 4;              // LDS stages (prefetch distance kStages - 1)
-constexpr int kLoadsPerOperand = 4;     // 16-byte loads per thread per operand per K tile
-constexpr int kTailLoads = 4;           // register loads per thread for a partial K tile
+constexpr int kBK = 32;                 // K per MFMA step (two 16-wide substeps)
 constexpr int kGroupM = 4;              // M tiles per raster group
 
 enum Form : int { kFormN = 0, kFormT = 1 };
+
+// K per LDS stage tile. With both operands K-contiguous (N form) a stage
+// tile holds 64 k, so each row contributes a whole 128-byte cache line to
+// every direct load: rows of 64 bytes (half lines) stream at about 60% of
+// the rate of whole lines into a CU. A T-form operand already loads runs of
+// 512 bytes; there a 32-k stage tile spreads the LDS writes evenly over the
+// MFMA steps, which measured faster. Stages: 2 of 64 k or 4 of 32 k (the
+// same 128 KiB of LDS).
+FLCE_HD constexpr int stage_k(int fa, int fb) { return (fa == kFormN && fb == kFormN) ? 64 : 32; }
+FLCE_HD constexpr int num_stages(int sk) { return sk == 64 ? 2 : 4; }
+// 16-byte direct loads per thread per operand per stage tile (256 rows x sk
+// x 2 bytes over 256 threads), and register loads for a partial tile.
+FLCE_HD constexpr int loads_per_operand(int sk) { return sk / 8; }
+FLCE_HD constexpr int tail_loads(int sk) { return sk / 8; }
 enum Buf : int { kBufW = 0, kBufH = 1, kBufG = 2 };
 
 // Geometry of one operand. N form: stored [rows][K] (K contiguous); T form:
@@ -95,48 +106,67 @@ FLCE_HD void tile_coords(int64_t b, int64_t M, int64_t Nn, int group_m, int64_t&
   n0 = (in / gs) * kBM;
 }
 
-// LDS swizzles. N form: 256 rows x 32 k, 64 B per row, 4 chunks of 16 B;
-// logical chunk c of row r at position c ^ swz_n(r). T form: 32 k-rows x 256
-// columns, 512 B per k-row, 32 chunks; logical chunk c of k-row k at
-// c ^ swz_t(k). Both were chosen by measuring the LDS bank-conflict counter
-// on gfx950 for the fragment read patterns: zero conflicts.
-FLCE_HD int swz_n(int r) { return (r >> 2) & 3; }
+// LDS layout of one stage tile of an operand. N form: 256 rows x sk k,
+// 2 sk bytes per row, sk / 8 chunks of 16 B; logical chunk c of row r at
+// position c ^ swz_n(r). Each 16-lane group of a fragment read (16
+// consecutive rows, one chunk) then covers all 16 bank quads of the
+// 256-byte bank window once: for 64 k, even rows take quads 0-7 and odd rows
+// 8-15; for 32 k, row r % 4 takes quads 4 (r % 4) to 4 (r % 4) + 3. T form:
+// sk k-rows x 256 columns, 512 B per k-row, 32 chunks; logical chunk c of
+// k-row k at c ^ swz_t(k). Both were checked with the LDS bank-conflict
+// counter on gfx950 for the fragment read patterns: zero conflicts.
+FLCE_HD int swz_n(int r, int sk) { return sk == 64 ? (r >> 1) & 7 : (r >> 2) & 3; }
 FLCE_HD int swz_t(int k) { return (0xCA60 >> (4 * (k & 3))) & 15; }  // {0,6,10,12}[k%4]
 
+// Where the fragment reads find an element. N form: the 16-byte chunk (8 k
+// values) c of row r. T form: byte offset of the 4 columns [col, col + 4) of
+// k-row k (col % 4 == 0).
+FLCE_HD int lds_chunk_n(int r, int c, int sk) { return r * (sk / 8) + (c ^ swz_n(r, sk)); }
+FLCE_HD int lds_byte_t(int k, int col) {
+  return (k * 32 + ((col >> 3) ^ swz_t(k))) * 16 + ((col >> 2) & 1) * 8;
+}
+
 // Direct-to-LDS loads: element offset of the tile base (k = 0) from the
-// operand pointer, elements to advance per K tile, and the element offset of
-// load q of (wave, lane) from the tile base. Load q of wave w fills LDS bytes
-// [(4w + q) KiB, +1 KiB), lane l writing 16 B at 16 l, so a lane fetches the
-// logical chunk that the swizzle puts at its LDS position. Rows (N form) or
+// operand pointer, elements to advance per stage tile, and the element
+// offset of load q of (wave, lane) from the tile base. With L =
+// loads_per_operand(sk), load q of wave w fills LDS bytes [(L w + q) KiB,
+// +1 KiB), lane l writing 16 B at 16 l, so a lane fetches the logical chunk
+// that the swizzle puts at its LDS position: in the N form 1024 / (2 sk) rows
+// of 2 sk bytes per load, in the T form 2 k-rows of 512 B. Rows (N form) or
 // column chunks (T form) past the edge are clamped to the last valid one:
 // their products land outside the output and are never stored.
 FLCE_HD int64_t direct_base(int form, const Geom& g, int64_t row0) {
   return form == kFormN ? row0 * g.ld : row0;
 }
-FLCE_HD int64_t direct_kstep(int form, const Geom& g) {
-  return form == kFormN ? int64_t(kBK) : int64_t(kBK) * g.ld;
+FLCE_HD int64_t direct_kstep(int form, const Geom& g, int sk) {
+  return form == kFormN ? int64_t(sk) : int64_t(sk) * g.ld;
 }
-FLCE_HD int64_t direct_lane(int form, const Geom& g, int64_t row0, int wave, int lane, int q) {
+FLCE_HD int64_t direct_lane(int form, const Geom& g, int64_t row0, int wave, int lane, int q,
+                            int sk) {
+  const int L = loads_per_operand(sk);
   if (form == kFormN) {
-    const int lr = 16 * (4 * wave + q) + (lane >> 2);
-    const int c = (lane & 3) ^ swz_n(lr);
+    const int cpr = sk / 8;                           // chunks per row
+    const int lr = (64 / cpr) * (L * wave + q) + lane / cpr;
+    const int c = (lane % cpr) ^ swz_n(lr, sk);
     int64_t r = row0 + lr;
     if (r > g.rows - 1) r = g.rows - 1;
     return (r - row0) * g.ld + 8 * c;
   }
-  const int kr = 2 * (4 * wave + q) + (lane >> 5);
+  const int kr = 2 * (L * wave + q) + (lane >> 5);
   const int c = (lane & 31) ^ swz_t(kr);
   int64_t col = 8 * c;
   if (row0 + col > g.rows - 8) col = g.rows - 8 - row0;
   return kr * g.ld + col;
 }
 
-// Register path of a partial last K tile: thread tid's load i covers
-// z = tid + 256 i (i < kTailLoads). Returns whether it reads memory (else it
-// stores zeros) and the element offset from the operand pointer.
-FLCE_HD bool tail_src(int form, const Geom& g, int64_t row0, int64_t k0, int z, int64_t& off) {
-  if (form == kFormN) {  // z -> (row z / 4, chunk z % 4)
-    const int64_t gr = row0 + (z >> 2), gk = k0 + 8 * (z & 3);
+// Register path of a partial last stage tile: thread tid's load i covers
+// z = tid + 256 i (i < tail_loads(sk)). Returns whether it reads memory
+// (else it stores zeros) and the element offset from the operand pointer.
+FLCE_HD bool tail_src(int form, const Geom& g, int64_t row0, int64_t k0, int z, int sk,
+                      int64_t& off) {
+  if (form == kFormN) {  // z -> (row z / cpr, chunk z % cpr)
+    const int cpr = sk / 8;
+    const int64_t gr = row0 + z / cpr, gk = k0 + 8 * (z % cpr);
     off = gr * g.ld + gk;
     return gr < g.rows && gk < g.K;
   }
@@ -146,9 +176,9 @@ FLCE_HD bool tail_src(int form, const Geom& g, int64_t row0, int64_t k0, int z, 
 }
 
 // LDS chunk position (16-byte units) of the tail element z.
-FLCE_HD int tail_lds_pos(int form, int z) {
-  return form == kFormN ? (z >> 2) * 4 + ((z & 3) ^ swz_n(z >> 2))
-                        : (z >> 5) * 32 + ((z & 31) ^ swz_t(z >> 5));
+FLCE_HD int tail_lds_pos(int form, int z, int sk) {
+  return form == kFormN ? lds_chunk_n(z / (sk / 8), z % (sk / 8), sk)
+                        : lds_byte_t(z >> 5, 8 * (z & 31)) / 16;
 }
 
 }  // namespace gemm

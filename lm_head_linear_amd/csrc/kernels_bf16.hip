@@ -34,8 +34,7 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 constexpr int kBM = gemm::kBM;
 constexpr int kThreads = 256;
-constexpr int kTileBytes = kBM * gemm::kBK * 2;  // one operand, one stage: 16 KiB
-constexpr int kStages = gemm::kStages;
+constexpr int kSmemBytes = 131072;                // LDS of the GEMM: all stages
 constexpr int kWaveScratch = 32768;               // LDS bytes per wave in the epilogues
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -55,7 +54,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 using gemm::Geom;
 using gemm::kBK;
-using gemm::kLoadsPerOperand;
 using gemm::swz_n;
 using gemm::swz_t;
 
@@ -66,66 +64,73 @@ struct Operand {
 };
 
 // Per-thread state of one operand's direct-to-LDS loads: a wave-uniform tile
-// base advanced by `kstep` bytes per K tile, and one 32-bit byte offset per
-// load (see gemm::direct_lane for the layout and the edge clamping).
+// base advanced by `kstep` bytes per stage tile, and one 32-bit byte offset
+// per load (see gemm::direct_lane for the layout and the edge clamping).
+template <int L>
 struct DirectLoads {
   const char* base;
   int64_t kstep;
-  uint32_t off[kLoadsPerOperand];
+  uint32_t off[L];
 };
 
-template <int FORM>
-__device__ __forceinline__ DirectLoads setup_direct(const Operand& op, int64_t row0, int wave,
-                                                    int lane) {
-  DirectLoads d;
+template <int FORM, int SK>
+__device__ __forceinline__ DirectLoads<gemm::loads_per_operand(SK)> setup_direct(
+    const Operand& op, int64_t row0, int wave, int lane) {
+  constexpr int L = gemm::loads_per_operand(SK);
+  DirectLoads<L> d;
   d.base = reinterpret_cast<const char*>(op.ptr + gemm::direct_base(FORM, op.g, row0));
-  d.kstep = gemm::direct_kstep(FORM, op.g) * 2;
+  d.kstep = gemm::direct_kstep(FORM, op.g, SK) * 2;
 #pragma unroll
-  for (int q = 0; q < kLoadsPerOperand; ++q)
-    d.off[q] = uint32_t(gemm::direct_lane(FORM, op.g, row0, wave, lane, q) * 2);
+  for (int q = 0; q < L; ++q)
+    d.off[q] = uint32_t(gemm::direct_lane(FORM, op.g, row0, wave, lane, q, SK) * 2);
   return d;
 }
 
-// Issue one K tile of direct loads into an LDS tile (16 KiB): load q of wave
-// w fills LDS bytes [(4w + q) KiB, +1 KiB), lane l writing 16 B at 16 l.
-__device__ __forceinline__ void issue_direct(const DirectLoads& d, int64_t kt, char* lds,
+// Issue one stage tile of direct loads into an LDS tile (256 x SK bf16): load
+// q of wave w fills LDS bytes [(L w + q) KiB, +1 KiB), lane l writing 16 B at
+// 16 l.
+template <int L>
+__device__ __forceinline__ void issue_direct(const DirectLoads<L>& d, int64_t kt, char* lds,
                                              int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass instantiates templates without gfx950 builtins
   const char* b = d.base + kt * d.kstep;
 #pragma unroll
-  for (int q = 0; q < kLoadsPerOperand; ++q)
+  for (int q = 0; q < L; ++q)
     __builtin_amdgcn_global_load_lds(
-        b + d.off[q], (__attribute__((address_space(3))) void*)(lds + (4 * wave + q) * 1024), 16,
+        b + d.off[q], (__attribute__((address_space(3))) void*)(lds + (L * wave + q) * 1024), 16,
         0, 0);
+#endif
 }
 
-// Register path for a partial last K tile: zero-filled past K (and past the
-// matrix edge), then stored into the same LDS layout.
-template <int FORM>
-__device__ __forceinline__ void load_tail(u32x4 (&r)[gemm::kTailLoads], const Operand& op,
+// Register path for a partial last stage tile: zero-filled past K (and past
+// the matrix edge), then stored into the same LDS layout.
+template <int FORM, int SK>
+__device__ __forceinline__ void load_tail(u32x4 (&r)[gemm::tail_loads(SK)], const Operand& op,
                                           int64_t row0, int64_t k0, int tid) {
 #pragma unroll
-  for (int i = 0; i < gemm::kTailLoads; ++i) {
+  for (int i = 0; i < gemm::tail_loads(SK); ++i) {
     int64_t off;
-    const bool ok = gemm::tail_src(FORM, op.g, row0, k0, tid + 256 * i, off);
+    const bool ok = gemm::tail_src(FORM, op.g, row0, k0, tid + 256 * i, SK, off);
     r[i] = ok ? *reinterpret_cast<const u32x4*>(op.ptr + off) : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
-template <int FORM>
-__device__ __forceinline__ void store_tail(char* lds, const u32x4 (&r)[gemm::kTailLoads],
+template <int FORM, int SK>
+__device__ __forceinline__ void store_tail(char* lds, const u32x4 (&r)[gemm::tail_loads(SK)],
                                            int tid) {
 #pragma unroll
-  for (int i = 0; i < gemm::kTailLoads; ++i)
-    *reinterpret_cast<u32x4*>(lds + gemm::tail_lds_pos(FORM, tid + 256 * i) * 16) = r[i];
+  for (int i = 0; i < gemm::tail_loads(SK); ++i)
+    *reinterpret_cast<u32x4*>(lds + gemm::tail_lds_pos(FORM, tid + 256 * i, SK) * 16) = r[i];
 }
 
-// MFMA fragment of 32 rows (block b of the wave's 128) for K substep s.
-template <int FORM>
+// MFMA fragment of 32 rows (block b of the wave's 128) for the 16-wide K
+// substep s (0 .. SK/16 - 1) of a stage tile.
+template <int FORM, int SK>
 __device__ __forceinline__ bf16x8 read_frag(const char* lds, int row_base, int s, int lane) {
   if (FORM == 0) {
     const int row = row_base + (lane & 31);
     const int c = 2 * s + (lane >> 5);
-    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + (row * 4 + (c ^ swz_n(row))) * 16);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + gemm::lds_chunk_n(row, c, SK) * 16);
     return __builtin_bit_cast(bf16x8, v);
   } else {
     typedef __attribute__((ext_vector_type(4))) short s16x4;
@@ -136,8 +141,7 @@ __device__ __forceinline__ bf16x8 read_frag(const char* lds, int row_base, int s
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int k = 16 * s + 8 * (g >> 1) + 4 * r + (i >> 2);
-      const int off = (k * 32 + ((col >> 3) ^ swz_t(k))) * 16 + ((col >> 2) & 1) * 8;
-      h[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + off));
+      h[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + gemm::lds_byte_t(k, col)));
     }
     typedef __attribute__((ext_vector_type(8))) short s16x8;
     const s16x8 v = {h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
@@ -155,26 +159,20 @@ __device__ __forceinline__ int acc_col(int wn, int j, int lane) {
   return wn * 128 + j * 32 + (lane & 31);
 }
 
-// Wait until at most `tiles` K tiles of direct loads (2 * kLoadsPerOperand
-// per thread each) are still in flight; other counters untouched (gfx9
-// s_waitcnt encoding: vmcnt bits [3:0] and [15:14]).
-__device__ __forceinline__ void wait_loads_in_flight(int64_t tiles) {
-  static_assert(2 * gemm::kLoadsPerOperand == 8 && kStages == 4, "waitcnt immediates");
-  if (tiles <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
-  else if (tiles == 1) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
-  else __builtin_amdgcn_s_waitcnt(0x4F70);                   // vmcnt(16)
-}
+// Waits of the K loop (gfx9 s_waitcnt encoding: vmcnt bits [3:0] and
+// [15:14], expcnt [6:4], lgkmcnt [11:8]; a field at its maximum does not
+// wait).
+__device__ __forceinline__ void wait_vm16() { __builtin_amdgcn_s_waitcnt(0x4F70); }   // vmcnt(16)
+__device__ __forceinline__ void wait_vm8() { __builtin_amdgcn_s_waitcnt(0x0F78); }    // vmcnt(8)
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }    // vmcnt(0)
+__device__ __forceinline__ void wait_vm0_lgkm0() { __builtin_amdgcn_s_waitcnt(0x0070); }
 
-// Workgroup barrier for the K loop. Unlike __syncthreads() it carries no
-// memory fence, which would wait for every load in flight (vmcnt(0)) and
-// undo the prefetch. What it must order: (1) this wave's direct loads of the
-// tile about to be read have landed -- the counted vmcnt wait before it;
-// (2) every wave's reads of the stage about to be overwritten are done --
-// they were consumed by that wave's MFMAs before it reached the barrier.
-// The empty asm statements keep the compiler from moving memory accesses
-// across it.
+// Workgroup barrier for the K loop. Unlike __syncthreads() it implies no
+// memory fence or wait: the waits that order the pipeline are explicit
+// before it. The empty asm statements keep the compiler from moving memory
+// accesses across it, the scheduling barriers keep MFMAs on their side.
 __device__ __forceinline__ void stage_barrier() {
-  __builtin_amdgcn_sched_barrier(0);   // keep the step's MFMAs ahead of the wait
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -186,13 +184,13 @@ struct Frags {
   bf16x8 a[4], b[4];
 };
 
-template <int FA, int FB>
+template <int FA, int FB, int SK>
 __device__ __forceinline__ void read_substep(Frags& f, const char* sa, const char* sb, int s,
                                              int wm, int wn, int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = read_frag<FA>(sa, wm * 128 + i * 32, s, lane);
+  for (int i = 0; i < 4; ++i) f.a[i] = read_frag<FA, SK>(sa, wm * 128 + i * 32, s, lane);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.b[j] = read_frag<FB>(sb, wn * 128 + j * 32, s, lane);
+  for (int j = 0; j < 4; ++j) f.b[j] = read_frag<FB, SK>(sb, wn * 128 + j * 32, s, lane);
 }
 
 __device__ __forceinline__ void mfma_substep(f32x16 (&acc)[4][4], const Frags& f) {
@@ -203,70 +201,77 @@ __device__ __forceinline__ void mfma_substep(f32x16 (&acc)[4][4], const Frags& f
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
-// Fragments of a whole K step (two 16-wide substeps).
+// Fragments of one MFMA step (32 k): 32-wide part `part` of a stage tile.
 struct StepFrags {
   Frags s[2];
 };
 
-template <int FA, int FB>
-__device__ __forceinline__ void read_step(StepFrags& f, const char* sa, const char* sb, int wm,
-                                          int wn, int lane) {
-  read_substep<FA, FB>(f.s[0], sa, sb, 0, wm, wn, lane);
-  read_substep<FA, FB>(f.s[1], sa, sb, 1, wm, wn, lane);
+template <int FA, int FB, int SK>
+__device__ __forceinline__ void read_step(StepFrags& f, const char* sa, const char* sb, int part,
+                                          int wm, int wn, int lane) {
+  read_substep<FA, FB, SK>(f.s[0], sa, sb, 2 * part, wm, wn, lane);
+  read_substep<FA, FB, SK>(f.s[1], sa, sb, 2 * part + 1, wm, wn, lane);
 }
 
-// Scheduling hints for one K step: its 32 MFMAs, each followed by at most one
-// direct global load and one LDS fragment read, so the loads of a later tile
-// and the reads of the next step issue under the MFMAs instead of stalling
-// the wave's in-order stream.
-// Scheduling hints for one K step: its 32 MFMAs, with the LDS fragment reads
-// of the next step and the direct global loads of a later tile placed
-// between them so they issue under the MFMAs instead of stalling the wave's
-// in-order stream. All reads go out in the first half of the step so they
-// have landed when the next step needs them. The placement of the loads was
-// chosen by timing: K-contiguous operands prefer them early, steps with
-// transpose reads prefer them in the second half.
-template <int FA, int FB>
+// Scheduling hints for one MFMA step: its 32 MFMAs, with the LDS fragment
+// reads of the next step (all in the first half of the step, so they have
+// returned when the next step needs them) and NLOADS direct global loads
+// placed between them, so everything issues under the MFMAs instead of
+// stalling the wave's in-order stream. The placement of the loads was chosen
+// by timing: K-contiguous operands prefer them early, steps with transpose
+// reads in the second half.
+template <int FA, int FB, int NLOADS>
 __device__ __forceinline__ void interleave_hints() {
   constexpr int kReads = 2 * ((FA == 0 ? 4 : 8) + (FB == 0 ? 4 : 8));
-  constexpr int kLoads = 2 * kLoadsPerOperand;
   constexpr int kPer = (kReads + 15) / 16;
   constexpr int kLoad0 = (FA == 0 && FB == 0) ? 0 : 16;
+  constexpr int kLoadPer = NLOADS > 16 ? (NLOADS + 15) / 16 : 1;
 #pragma unroll
   for (int q = 0; q < 32; ++q) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
-    if (q >= kLoad0 && q < kLoad0 + kLoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    if (NLOADS > 0 && q >= kLoad0 && q < kLoad0 + NLOADS / kLoadPer)
+      __builtin_amdgcn_sched_group_barrier(0x020, kLoadPer, 0);          // VMEM read
     if (q < kReads / kPer) __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);  // DS read
   }
 }
 
-// One K step: start the direct loads of a later tile into its (free) stage,
-// read all fragments of the next tile, and multiply the current tile whose
-// fragments were read during the previous step. The stages are __restrict__
-// so the compiler does not order the direct-to-LDS writes against the reads;
-// the real dependencies are the counted vmcnt wait and the barrier at the top
-// of each step.
-template <int FA, int FB>
+// One MFMA step: optionally start the direct loads of a stage tile into its
+// (free) stage, read the fragments of the next step (32-wide part
+// `next_part` of the stage tile at na/nb) and multiply the current step,
+// whose fragments were read during the previous one. The stages are
+// __restrict__ so the compiler does not order the direct-to-LDS writes
+// against the reads; the real dependencies are the waits and the barriers.
+template <int FA, int FB, int SK, bool LOADS, int L>
 __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], const StepFrags& cur, StepFrags& nxt,
-                                       const DirectLoads& da, const DirectLoads& db,
+                                       const DirectLoads<L>& da, const DirectLoads<L>& db,
                                        int64_t load_tile, const char* __restrict__ na,
-                                       const char* __restrict__ nb, char* __restrict__ la,
-                                       char* __restrict__ lb, int wave, int wm, int wn, int lane) {
-  issue_direct(da, load_tile, la, wave);
-  issue_direct(db, load_tile, lb, wave);
-  read_step<FA, FB>(nxt, na, nb, wm, wn, lane);
+                                       const char* __restrict__ nb, int next_part,
+                                       char* __restrict__ la, char* __restrict__ lb, int wave,
+                                       int wm, int wn, int lane) {
+  if (LOADS) {
+    issue_direct<L>(da, load_tile, la, wave);
+    issue_direct<L>(db, load_tile, lb, wave);
+  }
+  read_step<FA, FB, SK>(nxt, na, nb, next_part, wm, wn, lane);
   mfma_substep(acc, cur.s[0]);
   mfma_substep(acc, cur.s[1]);
-  interleave_hints<FA, FB>();
+  interleave_hints<FA, FB, LOADS ? 2 * L : 0>();
 }
 
 template <int FA, int FB, class Epi>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A, Operand B, int64_t M,
                                                       int64_t Nn, int64_t K, int group_m,
                                                       Epi epi) {
-  // kStages stages of (A tile, B tile); reused by the epilogues (32 KiB per wave)
-  __shared__ __attribute__((aligned(1024))) char smem[kStages * 2 * kTileBytes];
-  static_assert(kStages * 2 * kTileBytes >= 4 * kWaveScratch, "epilogue staging");
+  constexpr int SK = gemm::stage_k(FA, FB);
+  constexpr int kStages = gemm::num_stages(SK);
+  constexpr int L = gemm::loads_per_operand(SK);
+  constexpr int kTileBytes = kBM * SK * 2;          // one operand, one stage
+  static_assert(kStages * 2 * kTileBytes == kSmemBytes, "stages fill the GEMM's LDS");
+  static_assert(kSmemBytes >= 4 * kWaveScratch, "epilogue staging");
+  static_assert(kBK == 32 && (SK == 32 || SK == 64), "MFMA steps of 32 k");
+  static_assert(2 * L == (SK == 64 ? 16 : 8), "waitcnt immediates");
+  // the stages; reused by the epilogues (32 KiB per wave)
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
   int64_t m0, n0;
   gemm::tile_coords(blockIdx.x, M, Nn, group_m, m0, n0);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -281,74 +286,105 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A, Operand B, int6
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const DirectLoads da = setup_direct<FA>(A, m0, wave, lane);
-  const DirectLoads db = setup_direct<FB>(B, n0, wave, lane);
-  const int64_t nfull = K / kBK;               // K tiles loaded directly
-  const int64_t nk = (K + kBK - 1) / kBK;      // plus a zero-filled partial tile
+  const DirectLoads<L> da = setup_direct<FA, SK>(A, m0, wave, lane);
+  const DirectLoads<L> db = setup_direct<FB, SK>(B, n0, wave, lane);
+  const int64_t nfull = K / SK;                // stage tiles loaded directly
+  const int64_t nk = (K + SK - 1) / SK;        // plus a zero-filled partial tile
 
   auto st_a = [&](int64_t t) { return smem + (t % kStages) * 2 * kTileBytes; };
   auto st_b = [&](int64_t t) { return smem + (t % kStages) * 2 * kTileBytes + kTileBytes; };
-  static_assert(gemm::kBK == 32, "two 16-wide substeps per K step");
-  // Software pipeline over the full K tiles. Tile t is loaded (direct to LDS)
-  // kStages - 1 steps ahead; the fragments of tile kt+1 are read from LDS
-  // during step kt, a whole step before the MFMAs that use them. The barrier
-  // at the top of step kt publishes tile kt+1; the stage step kt loads into
-  // held tile kt-1, whose fragments every wave consumed in step kt-1, before
-  // that barrier. Every step issues exactly one tile -- past the last tile it
-  // re-loads the last one into a free stage -- so the number of loads in
-  // flight at each wait is the same and the body has no branches for the
-  // scheduler to stop at.
   if (nfull > 0) {
     const int64_t last = nfull - 1;
-#pragma unroll
-    for (int t = 0; t < kStages - 1; ++t) {
-      issue_direct(da, t < last ? t : last, st_a(t), wave);
-      issue_direct(db, t < last ? t : last, st_b(t), wave);
-    }
     StepFrags f[2];
-    wait_loads_in_flight(kStages - 2);             // tile 0 landed
-    stage_barrier();
-    read_step<FA, FB>(f[0], st_a(0), st_b(0), wm, wn, lane);
-    int64_t kt = 0;
-    // two steps per iteration so the fragment buffers swap roles without copies
-    for (; kt + 1 < nfull; kt += 2) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int64_t k = kt + u;
+    if constexpr (SK == 64) {
+      // Two stages of 64 k, two MFMA steps (the two 32-wide halves) per stage
+      // tile; stage tile t lives in stage t % 2 and the fragments of a step
+      // are read during the step before it. Even step (first half of tile
+      // t): multiply it, read the second half; no wait, no barrier. Odd step
+      // (second half): wait until this wave's loads of tile t+1 have landed
+      // and its reads of tile t have returned, then a barrier -- tile t+1 is
+      // published and no wave reads tile t's stage any more -- so the loads
+      // of tile t+2 go into it; read the first half of tile t+1. A tile's
+      // loads thus have two steps to land. Every odd step issues one tile
+      // (past the last one it re-loads the last into the free stage), so
+      // the body has no branches for the scheduler to stop at.
+      issue_direct<L>(da, 0, st_a(0), wave);
+      issue_direct<L>(db, 0, st_b(0), wave);
+      issue_direct<L>(da, last > 0 ? 1 : 0, st_a(1), wave);
+      issue_direct<L>(db, last > 0 ? 1 : 0, st_b(1), wave);
+      wait_vm16();                                 // tile 0 landed
+      stage_barrier();
+      read_step<FA, FB, SK>(f[0], st_a(0), st_b(0), 0, wm, wn, lane);
+      for (int64_t t = 0; t < nfull; ++t) {
         __builtin_amdgcn_sched_barrier(0);
-        wait_loads_in_flight(kStages - 3);         // tile k+1 landed
+        k_step<FA, FB, SK, false>(acc, f[0], f[1], da, db, 0, st_a(t), st_b(t), 1, nullptr,
+                                  nullptr, wave, wm, wn, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm0_lgkm0();
         stage_barrier();
-        const int64_t lt = k + kStages - 1;
-        k_step<FA, FB>(acc, f[u], f[u ^ 1], da, db, lt < last ? lt : last, st_a(k + 1),
-                       st_b(k + 1), st_a(lt), st_b(lt), wave, wm, wn, lane);
+        const int64_t lt = t + 2 < last ? t + 2 : last;
+        k_step<FA, FB, SK, true>(acc, f[1], f[0], da, db, lt, st_a(t + 1), st_b(t + 1), 0,
+                                 st_a(t), st_b(t), wave, wm, wn, lane);
+      }
+    } else {
+      // Four stages of 32 k, one MFMA step per stage tile. Tile t is loaded
+      // three steps ahead; its fragments are read during step t-1. The
+      // barrier at the top of step t publishes tile t+1, and the stage step t
+      // loads into held tile t-1, whose fragments every wave consumed in step
+      // t-1, before that barrier. Every step issues exactly one tile (past the
+      // last one it re-loads the last into a free stage), so the number of
+      // loads in flight at each wait is the same and the body has no
+      // branches for the scheduler to stop at.
+#pragma unroll
+      for (int t = 0; t < kStages - 1; ++t) {
+        issue_direct<L>(da, t < last ? t : last, st_a(t), wave);
+        issue_direct<L>(db, t < last ? t : last, st_b(t), wave);
+      }
+      wait_vm16();                                 // tile 0 landed (two more in flight)
+      stage_barrier();
+      read_step<FA, FB, SK>(f[0], st_a(0), st_b(0), 0, wm, wn, lane);
+      int64_t kt = 0;
+      // two steps per iteration so the fragment buffers swap roles without copies
+      for (; kt + 1 < nfull; kt += 2) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int64_t k = kt + u;
+          __builtin_amdgcn_sched_barrier(0);
+          wait_vm8();                              // tile k+1 landed
+          stage_barrier();
+          const int64_t lt = k + kStages - 1;
+          k_step<FA, FB, SK, true>(acc, f[u], f[u ^ 1], da, db, lt < last ? lt : last,
+                                   st_a(k + 1), st_b(k + 1), 0, st_a(lt), st_b(lt), wave, wm,
+                                   wn, lane);
+        }
+      }
+      if (kt < nfull) {                            // odd number of steps: the last one
+        wait_vm8();
+        stage_barrier();
+        const int64_t lt = kt + kStages - 1;
+        k_step<FA, FB, SK, true>(acc, f[0], f[1], da, db, lt < last ? lt : last, st_a(kt + 1),
+                                 st_b(kt + 1), 0, st_a(lt), st_b(lt), wave, wm, wn, lane);
       }
     }
-    if (kt < nfull) {                              // odd number of steps: the last one
-      wait_loads_in_flight(kStages - 3);
-      stage_barrier();
-      const int64_t lt = kt + kStages - 1;
-      k_step<FA, FB>(acc, f[0], f[1], da, db, lt < last ? lt : last, st_a(kt + 1), st_b(kt + 1),
-                     st_a(lt), st_b(lt), wave, wm, wn, lane);
-    }
     // the re-loads past the last tile may still be in flight
-    wait_loads_in_flight(0);
+    wait_vm0();
     stage_barrier();
   }
   if (nk > nfull) {
-    // The partial last K tile goes through registers, zero-filled past K. Its
-    // LDS stage was last read kStages - 1 steps ago, behind the last barrier.
-    char* la = st_a(nfull);
-    char* lb = st_b(nfull);
-    u32x4 ta[gemm::kTailLoads], tb[gemm::kTailLoads];
-    load_tail<FA>(ta, A, m0, nfull * kBK, tid);
-    load_tail<FB>(tb, B, n0, nfull * kBK, tid);
-    store_tail<FA>(la, ta, tid);
-    store_tail<FB>(lb, tb, tid);
+    // The partial last stage tile goes through registers, zero-filled past K,
+    // into stage 0, which no wave reads any more (behind the last barrier).
+    char* la = st_a(0);
+    char* lb = st_b(0);
+    u32x4 ta[gemm::tail_loads(SK)], tb[gemm::tail_loads(SK)];
+    load_tail<FA, SK>(ta, A, m0, nfull * SK, tid);
+    load_tail<FB, SK>(tb, B, n0, nfull * SK, tid);
+    store_tail<FA, SK>(la, ta, tid);
+    store_tail<FB, SK>(lb, tb, tid);
     __syncthreads();
     Frags ft;
 #pragma unroll
-    for (int sub = 0; sub < gemm::kBK / 16; ++sub) {
-      read_substep<FA, FB>(ft, la, lb, sub, wm, wn, lane);
+    for (int sub = 0; sub < SK / 16; ++sub) {
+      read_substep<FA, FB, SK>(ft, la, lb, sub, wm, wn, lane);
       mfma_substep(acc, ft);
     }
   }

@@ -2,7 +2,8 @@
 // the kernels' own index arithmetic (gemm_index.h) and the library's planner.
 // For each problem shape: every launch (forward, and the three launches of
 // every backward chunk), every workgroup, wave, lane and load. Direct loads
-// are affine in the K tile, so the first and the last full K tile are checked.
+// are affine in the stage tile, so the first and the last full stage tile are
+// checked.
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -25,17 +26,18 @@ static int64_t alloc_of(const Plan& p, int buf) {
 }
 
 static void check_operand(const Plan& p, const Launch& l, int which, int64_t row0) {
+  const int sk = stage_k(l.fa, l.fb), nl = loads_per_operand(sk), ntail = tail_loads(sk);
   const int form = which == 0 ? l.fa : l.fb;
   const Geom& g = which == 0 ? l.a : l.b;
   const int64_t base_off = which == 0 ? l.off_a : l.off_b;
   const int64_t alloc = alloc_of(p, which == 0 ? l.buf_a : l.buf_b);
   if (form == kFormT && (g.rows % 8 != 0 || g.rows < 8)) fail("T-form rows % 8", g.rows, 0, 0);
-  const int64_t nfull = l.K / kBK, nk = (l.K + kBK - 1) / kBK;
-  const int64_t tb = direct_base(form, g, row0), ks = direct_kstep(form, g);
+  const int64_t nfull = l.K / sk, nk = (l.K + sk - 1) / sk;
+  const int64_t tb = direct_base(form, g, row0), ks = direct_kstep(form, g, sk);
   for (int wave = 0; wave < 4; ++wave)
     for (int lane = 0; lane < 64; ++lane)
-      for (int q = 0; q < kLoadsPerOperand; ++q) {
-        const int64_t lo = direct_lane(form, g, row0, wave, lane, q);
+      for (int q = 0; q < nl; ++q) {
+        const int64_t lo = direct_lane(form, g, row0, wave, lane, q, sk);
         if (lo < 0 || lo * 2 > int64_t(0xFFFFFFFFll) - 16) fail("lane offset", lo, row0, q);
         if (nfull == 0) continue;
         for (int64_t kt : {int64_t(0), nfull - 1}) {
@@ -44,14 +46,50 @@ static void check_operand(const Plan& p, const Launch& l, int which, int64_t row
         }
       }
   if (nk > nfull)
-    for (int z = 0; z < 256 * kTailLoads; ++z) {
+    for (int z = 0; z < 256 * ntail; ++z) {
       int64_t off;
-      if (tail_src(form, g, row0, nfull * kBK, z, off)) {
+      if (tail_src(form, g, row0, nfull * sk, z, sk, off)) {
         const int64_t e = base_off + off;
         if (e < 0 || e + 8 > alloc) fail("tail load out of bounds", e, alloc, z);
       }
-      const int pos = tail_lds_pos(form, z);
-      if (pos < 0 || pos >= 256 * kTailLoads) fail("tail lds position", pos, z, 0);
+      const int pos = tail_lds_pos(form, z, sk);
+      if (pos < 0 || pos >= 256 * ntail) fail("tail lds position", pos, z, 0);
+    }
+}
+
+// The LDS side of the direct loads: on an interior tile (no clamping), the
+// element each lane fetches must be the one the fragment reads look for at
+// the LDS position the lane writes, and the positions must cover the stage
+// tile exactly once.
+static void check_lds_layout() {
+  const int64_t ld = 4096;
+  for (int sk : {32, 64})
+    for (int form : {int(kFormN), int(kFormT)}) {
+      const Geom g{ld, 1 << 20, 1 << 20};
+      const int nl = loads_per_operand(sk);
+      std::vector<char> hit(size_t(kBM) * sk * 2 / 16, 0);
+      for (int wave = 0; wave < 4; ++wave)
+        for (int lane = 0; lane < 64; ++lane)
+          for (int q = 0; q < nl; ++q) {
+            const int64_t pos = (nl * wave + q) * 64 + lane;   // 16-byte LDS chunk written
+            if (pos < 0 || pos >= int64_t(hit.size())) { fail("lds chunk range", pos, q, lane); continue; }
+            if (hit[size_t(pos)]++) fail("lds chunk written twice", pos, q, lane);
+            const int64_t off = direct_lane(form, g, 0, wave, lane, q, sk);
+            const int64_t a = off / ld, b = off % ld;          // (row, k) or (k-row, column)
+            const int64_t want = form == kFormN ? lds_chunk_n(int(a), int(b / 8), sk)
+                                                : lds_byte_t(int(a), int(b)) / 16;
+            if (form == kFormN && (a >= kBM || b >= sk || b % 8)) fail("N element", a, b, q);
+            if (form == kFormT && (a >= sk || b >= kBM || b % 8)) fail("T element", a, b, q);
+            if (want != pos) fail("lds position mismatch", sk, pos, want);
+          }
+      for (size_t i = 0; i < hit.size(); ++i)
+        if (!hit[i]) fail("lds chunk never written", sk, int64_t(i), form);
+      // tail path: a bijection onto the same positions
+      std::vector<char> th(hit.size(), 0);
+      for (int z = 0; z < 256 * tail_loads(sk); ++z) {
+        const int pos = tail_lds_pos(form, z, sk);
+        if (pos < 0 || pos >= int(th.size()) || th[size_t(pos)]++) fail("tail position", sk, z, pos);
+      }
     }
 }
 
@@ -85,6 +123,8 @@ int main(int argc, char** argv) {
       {100, 16, 1, 0},     {100, 16, 2, 0},     {333, 64, 1024, 0},  {256, 64, 512, 0},
       {2048, 1024, 32000, 0}, {4096, 4096, 131072, 0}, {8192, 4096, 131072, 0},
       {8192, 3584, 256000, 0}, {16384, 4096, 131072, 0}};
+  check_lds_layout();
+  std::printf("lds layout: %s\n", failures ? "FAILURES" : "ok");
   if (argc == 5) shapes = {{std::atoll(argv[1]), std::atoll(argv[2]), std::atoll(argv[3]), std::atoll(argv[4])}};
   for (const Shape& s : shapes) {
     if (s.vc > 0) {
