@@ -249,6 +249,32 @@ def main():
                     "workspace_bytes": int(fws.numel())}
     log(f"forward only: {f_ms:.3f} ms/call, {forward_only['tflops_2nhv']:.1f} TFLOP/s")
 
+    # Float32 gradients for the same bf16 inputs (G as a bf16 hi + lo pair,
+    # twice the dW/dH work), timed the same way.
+    gws = torch.empty(m.flce_workspace_size(N, H, V, W.dtype, torch.float32), dtype=torch.uint8,
+                      device=dev)
+    dH32 = torch.empty(N, H, dtype=torch.float32, device=dev)
+    dW32 = torch.empty(V, H, dtype=torch.float32, device=dev)
+
+    def step32():
+        m.flce_forward_backward(h, W, y, ignore_index=w.ignore_index, softcap=w.softcap,
+                                reduction=w.reduction, dH=dH32, dW=dW32, workspace=gws,
+                                loss=loss, num_tokens=nt, grad_dtype=torch.float32)
+
+    n32 = max(1, args.steps // 2)
+    for _ in range(2):
+        step32()
+    torch.cuda.synchronize()
+    tg0 = time.perf_counter()
+    for _ in range(n32):
+        step32()
+    torch.cuda.synchronize()
+    g_ms = (time.perf_counter() - tg0) * 1e3 / n32
+    float32_grads = {"ms_per_step": round(g_ms, 4), "tokens_per_s": round(N / (g_ms * 1e-3), 1),
+                     "steps": n32, "workspace_bytes": int(gws.numel())}
+    log(f"float32 gradients: {g_ms:.3f} ms/step")
+    del dH32, dW32, gws
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_sample_tokens} sampled tokens ...")
@@ -280,6 +306,7 @@ def main():
         "workspace_bytes": int(ws_bytes),
         "roofline": roofline,
         "forward_only": forward_only,
+        "float32_grads": float32_grads,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "cpu_baseline": ({k: (round(v, 3) if isinstance(v, float) else v)

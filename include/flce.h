@@ -83,7 +83,8 @@ size_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype);
  *                        (h, W, labels, dH when N > 0; loss, num_tokens, dW
  *                        always); unknown dtype/reduction; softcap < 0 or not
  *                        finite; mb_scale not finite; num_label_tokens > 0
- *                        with 'mean'; dH aliasing h or dW aliasing W.
+ *                        with 'mean'; dH overlapping h or dW, or dW
+ *                        overlapping W.
  *   FLCE_ERR_UNSUPPORTED bf16 with H % 8 != 0 or a matrix pointer not 16-byte
  *                        aligned.
  *   FLCE_ERR_WORKSPACE   workspace NULL, not 256-byte aligned, or
@@ -131,6 +132,42 @@ int flce_forward_backward(const void* h, const void* W, const int64_t* labels,
                           void* stream, int dtype, float mb_scale, int accumulate_dW,
                           void* workspace, size_t workspace_bytes, int32_t* status,
                           float* lse_out);
+
+/*
+ * float32 gradients for bf16 inputs (the *_ex entry points): the same call
+ * with one more argument, grad_dtype, the dtype of dH and dW. grad_dtype ==
+ * dtype is exactly flce_forward_backward. dtype FLCE_BF16 with grad_dtype
+ * FLCE_F32 writes dH and dW as float32 (dW added in float32 when
+ * accumulate_dW is set), so a caller can accumulate gradients over
+ * micro-batches in float32 (twinkle PR 335, "PR information", item 2: the
+ * token-weighted micro-batch scale; Modalities PR 464, "What the reference
+ * implementations do": the chunked path there accumulates its gradients in
+ * float32). The logit gradient G, otherwise rounded to bf16
+ * once, is kept as a pair G = G_hi + G_lo of bf16 values (G_hi = bf16(G),
+ * G_lo = bf16(G - G_hi)), about 16 significant bits, and each gradient GEMM
+ * runs once per part in a fixed order: twice the dW/dH work of the bf16
+ * call. dtype FLCE_F32 with grad_dtype FLCE_BF16 is FLCE_ERR_UNSUPPORTED.
+ * Float32 gradients need the matrix pointers dH, dW 16-byte aligned and
+ * H % 8 == 0 like the bf16 ones. The workspace is
+ * flce_workspace_size_ex(N, H, V, dtype, grad_dtype) bytes and
+ * flce_vocab_chunk_ex gives the vocabulary chunk (half the bf16 call's).
+ */
+size_t flce_workspace_size_ex(int64_t N, int64_t H, int64_t V, int dtype, int grad_dtype);
+int64_t flce_vocab_chunk_ex(int64_t N, int64_t H, int64_t V, int dtype, int grad_dtype);
+int flce_check_args_ex(const void* h, const void* W, const int64_t* labels,
+                       int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                       float softcap, int reduction, int64_t num_label_tokens,
+                       float* loss, int64_t* num_tokens, void* dH, void* dW,
+                       void* stream, int dtype, float mb_scale, int accumulate_dW,
+                       void* workspace, size_t workspace_bytes, int32_t* status,
+                       float* lse_out, int grad_dtype);
+int flce_forward_backward_ex(const void* h, const void* W, const int64_t* labels,
+                             int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                             float softcap, int reduction, int64_t num_label_tokens,
+                             float* loss, int64_t* num_tokens, void* dH, void* dW,
+                             void* stream, int dtype, float mb_scale, int accumulate_dW,
+                             void* workspace, size_t workspace_bytes, int32_t* status,
+                             float* lse_out, int grad_dtype);
 
 /*
  * flce_forward_workspace_size -- bytes of device scratch that flce_forward

@@ -13,6 +13,9 @@ Contracts (see include/flce.h):
 * an empty target set gives loss 0 and zero gradients (Ling-3.1-flash
   discussion 7), the loss is float32 for bf16 inputs (Modalities PR 464), and
   the softcap ``s*tanh(z/s)`` is applied on every path (twinkle PR 335 item 3).
+* ``grad_dtype=torch.float32`` with bf16 inputs returns float32 dH and dW (the
+  logit gradient kept as a bf16 hi + lo pair), for callers that accumulate
+  gradients over micro-batches in float32; it costs twice the dW/dH work.
 * The forward call computes dH and dW as well; ``backward`` only scales them by
   the incoming gradient. When no gradient is wanted (``torch.no_grad()``, or
   neither input requires one) the forward-only entry runs instead: the same
@@ -78,16 +81,20 @@ def flce_status_string(code: int) -> str:
     return _lib.load().flce_status_string(int(code)).decode()
 
 
-def flce_workspace_size(N: int, H: int, V: int, dtype: torch.dtype) -> int:
-    return int(_lib.load().flce_workspace_size(N, H, V, _dtype_code(dtype)))
+def flce_workspace_size(N: int, H: int, V: int, dtype: torch.dtype,
+                        grad_dtype: Optional[torch.dtype] = None) -> int:
+    g = _dtype_code(grad_dtype if grad_dtype is not None else dtype)
+    return int(_lib.load().flce_workspace_size_ex(N, H, V, _dtype_code(dtype), g))
 
 
 def flce_forward_workspace_size(N: int, H: int, V: int, dtype: torch.dtype) -> int:
     return int(_lib.load().flce_forward_workspace_size(N, H, V, _dtype_code(dtype)))
 
 
-def flce_vocab_chunk(N: int, H: int, V: int, dtype: torch.dtype) -> int:
-    return int(_lib.load().flce_vocab_chunk(N, H, V, _dtype_code(dtype)))
+def flce_vocab_chunk(N: int, H: int, V: int, dtype: torch.dtype,
+                     grad_dtype: Optional[torch.dtype] = None) -> int:
+    g = _dtype_code(grad_dtype if grad_dtype is not None else dtype)
+    return int(_lib.load().flce_vocab_chunk_ex(N, H, V, _dtype_code(dtype), g))
 
 
 def _abi_args(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens,
@@ -103,12 +110,13 @@ def _abi_args(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label
 def flce_check_args(h, W, labels, *, N, H, V, ignore_index=-100, softcap=0.0, reduction="sum",
                     num_label_tokens=None, loss=None, num_tokens=None, dH=None, dW=None,
                     dtype=torch.bfloat16, mb_scale=1.0, accumulate_dW=False, workspace=None,
-                    status=None, lse_out=None) -> int:
+                    status=None, lse_out=None, grad_dtype=None) -> int:
     """The library's synchronous checks (no GPU work); returns a status code."""
     args = _abi_args(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens,
                      loss, num_tokens, dH, dW, None, dtype, mb_scale, accumulate_dW, workspace,
                      status, lse_out)
-    return int(_lib.load().flce_check_args(*args))
+    g = _dtype_code(grad_dtype if grad_dtype is not None else dtype)
+    return int(_lib.load().flce_check_args_ex(*args, g))
 
 
 def _fwd_abi_args(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens,
@@ -151,13 +159,15 @@ def flce_forward_backward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor
                           lse_out: Optional[torch.Tensor] = None,
                           status: Optional[torch.Tensor] = None,
                           loss: Optional[torch.Tensor] = None,
-                          num_tokens: Optional[torch.Tensor] = None):
+                          num_tokens: Optional[torch.Tensor] = None,
+                          grad_dtype: Optional[torch.dtype] = None):
     """One fused forward + backward on the current stream.
 
     h [N,H], W [V,H] (bf16 or fp32, same dtype, contiguous, on one GPU), labels
     [N] int64. Returns (loss fp32 scalar, num_tokens int64 scalar, dH, dW) as
     device tensors; nothing is synchronised. Output/workspace tensors may be
-    passed in to avoid allocation.
+    passed in to avoid allocation. dH and dW have ``grad_dtype`` (default: the
+    input dtype; float32 with bf16 inputs is the float32-gradient mode).
     """
     if h.dim() != 2 or W.dim() != 2:
         raise ValueError("h must be [N, H] and W [V, H]")
@@ -169,14 +179,16 @@ def flce_forward_backward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor
     _check_tensor("h", h, (N, H), W.dtype, dev)
     _check_tensor("W", W, (V, H), W.dtype, dev)
     _check_tensor("labels", labels, (N,), torch.int64, dev)
+    gdt = W.dtype if grad_dtype is None else grad_dtype
+    _dtype_code(gdt)
     if dH is None:
-        dH = torch.empty_like(h)
+        dH = torch.empty(N, H, dtype=gdt, device=dev)
     if dW is None:
         if accumulate_dW:
             raise ValueError("accumulate_dW needs the dW tensor to add to")
-        dW = torch.empty_like(W)
-    _check_tensor("dH", dH, (N, H), W.dtype, dev)
-    _check_tensor("dW", dW, (V, H), W.dtype, dev)
+        dW = torch.empty(V, H, dtype=gdt, device=dev)
+    _check_tensor("dH", dH, (N, H), gdt, dev)
+    _check_tensor("dW", dW, (V, H), gdt, dev)
     if loss is None:
         loss = torch.empty((), dtype=torch.float32, device=dev)
     if num_tokens is None:
@@ -185,9 +197,10 @@ def flce_forward_backward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor
         _check_tensor("lse_out", lse_out, (N,), torch.float32, dev)
     if status is not None:
         _check_tensor("status", status, (), torch.int32, dev)
-    need = flce_workspace_size(N, H, V, W.dtype)
+    need = flce_workspace_size(N, H, V, W.dtype, gdt)
     if need == 0:
-        raise FlceError(_lib.ERR_ARG, "flce_workspace_size")
+        raise FlceError(_lib.ERR_UNSUPPORTED if W.dtype == torch.float32 else _lib.ERR_ARG,
+                        "flce_workspace_size")
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -195,7 +208,7 @@ def flce_forward_backward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor
                      loss, num_tokens, dH, dW, stream, W.dtype, mb_scale, accumulate_dW,
                      workspace, status, lse_out)
     with torch.cuda.device(dev):
-        rc = _lib.load().flce_forward_backward(*args)
+        rc = _lib.load().flce_forward_backward_ex(*args, _dtype_code(gdt))
     if rc != _lib.OK:
         raise FlceError(rc, "flce_forward_backward")
     return loss, num_tokens, dH, dW

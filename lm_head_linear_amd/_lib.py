@@ -22,6 +22,10 @@ SIGNATURES = {
     "flce_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
     "flce_check_args": (_i32, _FB_ARGS),
     "flce_forward_backward": (_i32, _FB_ARGS),
+    "flce_workspace_size_ex": (_sz, [_i64, _i64, _i64, _i32, _i32]),
+    "flce_vocab_chunk_ex": (_i64, [_i64, _i64, _i64, _i32, _i32]),
+    "flce_check_args_ex": (_i32, _FB_ARGS + [_i32]),
+    "flce_forward_backward_ex": (_i32, _FB_ARGS + [_i32]),
     "flce_forward_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
     "flce_forward_check_args": (_i32, _F_ARGS),
     "flce_forward": (_i32, _F_ARGS),

@@ -64,9 +64,9 @@ int run(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t 
         int64_t ignore_index, float softcap, int reduction, int64_t num_label_tokens,
         float* loss, int64_t* num_tokens, void* dH, void* dW, void* stream, int dtype,
         float mb_scale, int accumulate_dW, void* workspace, int32_t* status, float* lse_out,
-        bool backward) {
+        bool backward, int grad_dtype) {
   flce::Plan p;
-  if (!flce::make_plan(N, H, V, dtype, &p, backward)) return FLCE_ERR_ARG;
+  if (!flce::make_plan(N, H, V, dtype, &p, backward, grad_dtype)) return FLCE_ERR_ARG;
 
   flce::Launcher L{static_cast<hipStream_t>(stream), nullptr, nullptr};
   if (g_prof.on) { L.before = prof_before; L.after = prof_after; }
@@ -86,7 +86,7 @@ int run(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t 
   if (N == 0) {
     e = flce::launch_empty(p, a, L);
     if (e == hipSuccess && backward && !a.accumulate_dW)
-      e = flce::launch_zero_bytes(dW, size_t(V) * H * p.elem, L);
+      e = flce::launch_zero_bytes(dW, size_t(V) * H * p.grad_elem, L);
     return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
   }
   a.part = reinterpret_cast<float2*>(ws + p.off_part);
@@ -115,13 +115,27 @@ int flce_forward_backward(const void* h, const void* W, const int64_t* labels, i
                           int64_t* num_tokens, void* dH, void* dW, void* stream, int dtype,
                           float mb_scale, int accumulate_dW, void* workspace,
                           size_t workspace_bytes, int32_t* status, float* lse_out) {
-  int st = flce_check_args(h, W, labels, N, H, V, ignore_index, softcap, reduction,
-                           num_label_tokens, loss, num_tokens, dH, dW, stream, dtype, mb_scale,
-                           accumulate_dW, workspace, workspace_bytes, status, lse_out);
+  return flce_forward_backward_ex(h, W, labels, N, H, V, ignore_index, softcap, reduction,
+                                  num_label_tokens, loss, num_tokens, dH, dW, stream, dtype,
+                                  mb_scale, accumulate_dW, workspace, workspace_bytes, status,
+                                  lse_out, dtype);
+}
+
+int flce_forward_backward_ex(const void* h, const void* W, const int64_t* labels, int64_t N,
+                             int64_t H, int64_t V, int64_t ignore_index, float softcap,
+                             int reduction, int64_t num_label_tokens, float* loss,
+                             int64_t* num_tokens, void* dH, void* dW, void* stream, int dtype,
+                             float mb_scale, int accumulate_dW, void* workspace,
+                             size_t workspace_bytes, int32_t* status, float* lse_out,
+                             int grad_dtype) {
+  int st = flce_check_args_ex(h, W, labels, N, H, V, ignore_index, softcap, reduction,
+                              num_label_tokens, loss, num_tokens, dH, dW, stream, dtype,
+                              mb_scale, accumulate_dW, workspace, workspace_bytes, status,
+                              lse_out, grad_dtype);
   if (st != FLCE_OK) return st;
   return run(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens, loss,
              num_tokens, dH, dW, stream, dtype, mb_scale, accumulate_dW, workspace, status,
-             lse_out, true);
+             lse_out, true, grad_dtype);
 }
 
 int flce_forward(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H,
@@ -135,7 +149,7 @@ int flce_forward(const void* h, const void* W, const int64_t* labels, int64_t N,
   if (st != FLCE_OK) return st;
   return run(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens, loss,
              num_tokens, nullptr, nullptr, stream, dtype, mb_scale, 0, workspace, status,
-             lse_out, false);
+             lse_out, false, dtype);
 }
 
 int flce_profile_begin(void) {

@@ -26,15 +26,21 @@ int64_t env_vchunk() {
 
 }  // namespace
 
-bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backward) {
+bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backward,
+               int grad_dtype) {
   if (N < 0 || H <= 0 || V <= 0) return false;
   if (dtype != FLCE_F32 && dtype != FLCE_BF16) return false;
+  if (grad_dtype < 0) grad_dtype = dtype;
+  if (grad_dtype != FLCE_F32 && grad_dtype != FLCE_BF16) return false;
+  if (dtype == FLCE_F32 && grad_dtype != FLCE_F32) return false;
   // Keep every size product far from int64 overflow.
   if (N > (int64_t(1) << 31) || H > (int64_t(1) << 24) || V > (int64_t(1) << 31)) return false;
   Plan q;
-  q.N = N; q.H = H; q.V = V; q.dtype = dtype;
+  q.N = N; q.H = H; q.V = V; q.dtype = dtype; q.grad_dtype = grad_dtype;
   q.tile = dtype == FLCE_BF16 ? kTileBF16 : kTileF32;
   q.elem = dtype == FLCE_BF16 ? 2 : 4;
+  q.grad_elem = grad_dtype == FLCE_BF16 ? 2 : 4;
+  q.g_parts = (dtype == FLCE_BF16 && grad_dtype == FLCE_F32) ? 2 : 1;
   q.n_tok_tiles = ceil_div(N, q.tile);
   q.n_voc_tiles = ceil_div(V, q.tile);
   q.ld_part = round_up(N > 0 ? N : 1, q.tile);
@@ -43,7 +49,7 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
   // tile, at least one tile, at most the (tile-rounded) vocabulary.
   int64_t vmax = round_up(V, q.tile);
   int64_t vc = env_vchunk();
-  if (vc <= 0) vc = (kChunkElems / (N > 0 ? q.ldg : 1)) / q.tile * q.tile;
+  if (vc <= 0) vc = (kChunkElems / q.g_parts / (N > 0 ? q.ldg : 1)) / q.tile * q.tile;
   else vc = round_up(vc, q.tile);
   if (vc < q.tile) vc = q.tile;
   if (vc > vmax) vc = vmax;
@@ -51,7 +57,7 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
   q.n_chunks = ceil_div(V, vc);
   q.n_loss_blocks = ceil_div(N > 0 ? N : 1, 32);   // tokens per lse-merge block
   q.backward = backward;
-  q.need_dh_acc = backward && (dtype == FLCE_BF16) && q.n_chunks > 1 && N > 0;
+  q.need_dh_acc = backward && (dtype == FLCE_BF16) && q.g_parts == 1 && q.n_chunks > 1 && N > 0;
 
   size_t off = 0;
   q.off_scalars = off; off = align256(off + sizeof(Scalars));
@@ -60,7 +66,10 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
     q.off_zt = off;    off = align256(off + size_t(q.ld_part) * sizeof(float));
     q.off_lse = off;   off = align256(off + size_t(q.ld_part) * sizeof(float));
     q.off_lsum = off;  off = align256(off + size_t(q.n_loss_blocks) * sizeof(double));
-    if (backward) { q.off_g = off; off = align256(off + size_t(q.vchunk) * q.ldg * q.elem); }
+    if (backward) {
+      q.off_g = off;
+      off = align256(off + size_t(q.g_parts) * size_t(q.vchunk) * q.ldg * q.elem);
+    }
     if (q.need_dh_acc) { q.off_dhacc = off; off = align256(off + size_t(N) * H * sizeof(float)); }
   }
   q.total = off;
@@ -73,14 +82,22 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
 extern "C" {
 
 size_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype) {
+  return flce_workspace_size_ex(N, H, V, dtype, dtype);
+}
+
+size_t flce_workspace_size_ex(int64_t N, int64_t H, int64_t V, int dtype, int grad_dtype) {
   flce::Plan p;
-  if (!flce::make_plan(N, H, V, dtype, &p)) return 0;
+  if (!flce::make_plan(N, H, V, dtype, &p, true, grad_dtype)) return 0;
   return p.total;
 }
 
 int64_t flce_vocab_chunk(int64_t N, int64_t H, int64_t V, int dtype) {
+  return flce_vocab_chunk_ex(N, H, V, dtype, dtype);
+}
+
+int64_t flce_vocab_chunk_ex(int64_t N, int64_t H, int64_t V, int dtype, int grad_dtype) {
   flce::Plan p;
-  if (!flce::make_plan(N, H, V, dtype, &p)) return 0;
+  if (!flce::make_plan(N, H, V, dtype, &p, true, grad_dtype)) return 0;
   return p.vchunk;
 }
 
@@ -108,10 +125,12 @@ bool misaligned(const void* q, uintptr_t mask) { return (reinterpret_cast<uintpt
 int check_common(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H,
                  int64_t V, float softcap, int reduction, int64_t num_label_tokens,
                  const float* loss, const int64_t* num_tokens, const void* dH, const void* dW,
-                 int dtype, float mb_scale, const void* workspace, size_t workspace_bytes,
-                 bool backward) {
+                 int dtype, int grad_dtype, float mb_scale, const void* workspace,
+                 size_t workspace_bytes, bool backward) {
   if (N < 0 || H <= 0 || V <= 0) return FLCE_ERR_ARG;
   if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_ERR_ARG;
+  if (grad_dtype != FLCE_F32 && grad_dtype != FLCE_BF16) return FLCE_ERR_ARG;
+  if (dtype == FLCE_F32 && grad_dtype == FLCE_BF16) return FLCE_ERR_UNSUPPORTED;
   if (reduction != FLCE_SUM && reduction != FLCE_MEAN) return FLCE_ERR_ARG;
   if (!(softcap >= 0.0f) || !std::isfinite(softcap)) return FLCE_ERR_ARG;
   if (!std::isfinite(mb_scale)) return FLCE_ERR_ARG;
@@ -120,16 +139,19 @@ int check_common(const void* h, const void* W, const int64_t* labels, int64_t N,
   if (N > 0 && (!h || !labels)) return FLCE_ERR_ARG;
   if (backward && (!dW || (N > 0 && !dH))) return FLCE_ERR_ARG;
   flce::Plan p;
-  if (!flce::make_plan(N, H, V, dtype, &p, backward)) return FLCE_ERR_ARG;
-  const size_t es = p.elem;
+  if (!flce::make_plan(N, H, V, dtype, &p, backward, grad_dtype)) return FLCE_ERR_ARG;
+  const size_t es = p.elem, gs = p.grad_elem;
   if (backward) {
-    if (overlaps(dH, size_t(N) * H * es, h, size_t(N) * H * es)) return FLCE_ERR_ARG;
-    if (overlaps(dW, size_t(V) * H * es, W, size_t(V) * H * es)) return FLCE_ERR_ARG;
+    if (overlaps(dH, size_t(N) * H * gs, h, size_t(N) * H * es)) return FLCE_ERR_ARG;
+    if (overlaps(dW, size_t(V) * H * gs, W, size_t(V) * H * es)) return FLCE_ERR_ARG;
+    if (overlaps(dH, size_t(N) * H * gs, dW, size_t(V) * H * gs)) return FLCE_ERR_ARG;
   }
   const uintptr_t mask = dtype == FLCE_BF16 ? 15u : 3u;
   if (dtype == FLCE_BF16 && H % 8 != 0) return FLCE_ERR_UNSUPPORTED;
   if (misaligned(W, mask) || (N > 0 && misaligned(h, mask))) return FLCE_ERR_UNSUPPORTED;
-  if (backward && (misaligned(dW, mask) || (N > 0 && misaligned(dH, mask))))
+  // the bf16 kernels write gradients in 16-byte (float32: 4 x 4-byte) runs
+  const uintptr_t gmask = dtype == FLCE_BF16 ? 15u : 3u;
+  if (backward && (misaligned(dW, gmask) || (N > 0 && misaligned(dH, gmask))))
     return FLCE_ERR_UNSUPPORTED;
   if (!workspace) return FLCE_ERR_WORKSPACE;
   if (misaligned(workspace, 255u)) return FLCE_ERR_WORKSPACE;
@@ -148,9 +170,22 @@ int flce_check_args(const void* h, const void* W, const int64_t* labels,
                     void* stream, int dtype, float mb_scale, int accumulate_dW,
                     void* workspace, size_t workspace_bytes, int32_t* status,
                     float* lse_out) {
+  return flce_check_args_ex(h, W, labels, N, H, V, ignore_index, softcap, reduction,
+                            num_label_tokens, loss, num_tokens, dH, dW, stream, dtype, mb_scale,
+                            accumulate_dW, workspace, workspace_bytes, status, lse_out, dtype);
+}
+
+int flce_check_args_ex(const void* h, const void* W, const int64_t* labels,
+                       int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                       float softcap, int reduction, int64_t num_label_tokens,
+                       float* loss, int64_t* num_tokens, void* dH, void* dW,
+                       void* stream, int dtype, float mb_scale, int accumulate_dW,
+                       void* workspace, size_t workspace_bytes, int32_t* status,
+                       float* lse_out, int grad_dtype) {
   (void)ignore_index; (void)stream; (void)accumulate_dW; (void)status; (void)lse_out;
   return check_common(h, W, labels, N, H, V, softcap, reduction, num_label_tokens, loss,
-                      num_tokens, dH, dW, dtype, mb_scale, workspace, workspace_bytes, true);
+                      num_tokens, dH, dW, dtype, grad_dtype, mb_scale, workspace,
+                      workspace_bytes, true);
 }
 
 int flce_forward_check_args(const void* h, const void* W, const int64_t* labels,
@@ -161,7 +196,7 @@ int flce_forward_check_args(const void* h, const void* W, const int64_t* labels,
                             int32_t* status, float* lse_out) {
   (void)ignore_index; (void)stream; (void)status; (void)lse_out;
   return check_common(h, W, labels, N, H, V, softcap, reduction, num_label_tokens, loss,
-                      num_tokens, nullptr, nullptr, dtype, mb_scale, workspace,
+                      num_tokens, nullptr, nullptr, dtype, dtype, mb_scale, workspace,
                       workspace_bytes, false);
 }
 

@@ -28,6 +28,8 @@ struct Scalars {
 struct Plan {
   int64_t N = 0, H = 0, V = 0;
   int dtype = 0;
+  int grad_dtype = 0;        // dtype of dH and dW
+  int g_parts = 1;           // 2: G kept as a bf16 hi + lo pair (float32 gradients)
   int64_t tile = 0;     // tile edge for this dtype
   int64_t n_tok_tiles = 0;   // ceil(N / tile)
   int64_t n_voc_tiles = 0;   // ceil(V / tile), forward partials per token
@@ -39,14 +41,20 @@ struct Plan {
   bool backward = true;      // plan includes the gradient buffers
   bool need_dh_acc = false;  // float32 dH accumulator needed (bf16, >1 chunk)
   size_t elem = 0;           // bytes per element of h/W/G
+  size_t grad_elem = 0;      // bytes per element of dH/dW
   // byte offsets into the workspace
   size_t off_scalars = 0, off_part = 0, off_zt = 0, off_lse = 0, off_lsum = 0,
          off_g = 0, off_dhacc = 0, total = 0;
 };
 
-// Builds the plan; returns false for invalid sizes or dtype. A forward-only
+// Builds the plan; returns false for invalid sizes or dtypes. A forward-only
 // plan (backward = false) carves no logit-gradient chunk and no dH
-// accumulator, so its workspace is the forward's alone.
-bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backward = true);
+// accumulator, so its workspace is the forward's alone. grad_dtype < 0 means
+// the input dtype; float32 gradients for bf16 inputs keep G as a hi + lo pair
+// of bf16 chunks (half as many vocabulary rows per chunk) and need no dH
+// accumulator (dH itself is float32). bf16 gradients for float32 inputs are
+// refused.
+bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backward = true,
+               int grad_dtype = -1);
 
 }  // namespace flce

@@ -55,8 +55,10 @@ struct Launch {
   Geom a, b;
 };
 
-// The three launches of backward chunk c (0: logit gradient, 1: dW, 2: dH),
-// or the forward launch (c < 0).
+// The forward launch, and the three launches of backward chunk c (0: logit
+// gradient, 1: dW, 2: dH). With float32 gradients for bf16 inputs G is a
+// pair of bf16 chunks, hi then lo, each vchunk x ldg elements; `part` picks
+// the one a dW or dH launch reads.
 inline Launch forward_launch(const Plan& p) {
   return Launch{p.V, p.N, p.H, kFormN, kFormN, kBufW, kBufH, 0, 0,
                 Geom{p.H, p.V, p.H}, Geom{p.H, p.N, p.H}};
@@ -67,8 +69,9 @@ inline int64_t chunk_rows(const Plan& p, int64_t c) {
   return (p.V - v0) < p.vchunk ? (p.V - v0) : p.vchunk;
 }
 
-inline Launch backward_launch(const Plan& p, int64_t c, int which) {
+inline Launch backward_launch(const Plan& p, int64_t c, int which, int part = 0) {
   const int64_t v0 = c * p.vchunk, vcur = chunk_rows(p, c);
+  const int64_t g_off = int64_t(part) * p.vchunk * p.ldg;
   if (which == 0)  // Z^T[chunk] = W[chunk] . h^T, then the gradient epilogue
     return Launch{vcur, p.N, p.H, kFormN, kFormN, kBufW, kBufH, v0 * p.H, 0,
                   Geom{p.H, vcur, p.H}, Geom{p.H, p.N, p.H}};
@@ -76,10 +79,10 @@ inline Launch backward_launch(const Plan& p, int64_t c, int which) {
   // of 8; columns from vcur to the row end are never multiplied into a
   // stored output).
   if (which == 1)  // dW[chunk] = G[:, chunk]^T . h  (K = tokens)
-    return Launch{vcur, p.H, p.N, kFormT, kFormT, kBufG, kBufH, 0, 0,
+    return Launch{vcur, p.H, p.N, kFormT, kFormT, kBufG, kBufH, g_off, 0,
                   Geom{p.vchunk, p.vchunk, p.N}, Geom{p.H, p.H, p.N}};
   // dH += G[:, chunk] . W[chunk]  (K = chunk rows)
-  return Launch{p.N, p.H, vcur, kFormN, kFormT, kBufG, kBufW, 0, v0 * p.H,
+  return Launch{p.N, p.H, vcur, kFormN, kFormT, kBufG, kBufW, g_off, v0 * p.H,
                 Geom{p.vchunk, p.N, vcur}, Geom{p.H, p.H, vcur}};
 }
 

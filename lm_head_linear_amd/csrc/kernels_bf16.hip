@@ -487,11 +487,13 @@ struct EpiLse {
 // ---- backward epilogue: the logit gradient G for one vocabulary chunk ----
 // G[t, v] = c * valid_t * (exp(z'_tv - lse_t) - [v = y_t]) * dz'/dz, stored
 // bf16 token-major as G[t][v - v0] (row length ldgv). Tile rows are
-// chunk-relative vocab ids, columns tokens. Each wave stages its 128 x 128
-// block in its own 32 KiB of LDS as [token][vocab] (a lane packs its 4
-// consecutive vocab values into 8 bytes; 8-byte slots XOR-swizzled by token),
-// then writes whole 16-byte runs of a token row to global memory.
-template <bool SOFTCAP>
+// chunk-relative vocab ids, columns tokens. G is first formed in float32 in
+// place of the logits; then each wave stages its 128 x 128 block in its own
+// 32 KiB of LDS as [token][vocab] (a lane packs its 4 consecutive vocab
+// values into 8 bytes; 8-byte slots XOR-swizzled by token) and writes whole
+// 16-byte runs of token rows. SPLIT (float32 gradients) stores two bf16
+// chunks, G_hi = bf16(G) at g and G_lo = bf16(G - G_hi) at g + lo_off.
+template <bool SOFTCAP, bool SPLIT>
 struct EpiGrad {
   const int64_t* labels;
   const float* lse;
@@ -499,6 +501,7 @@ struct EpiGrad {
   int64_t N, V, ignore_index, v0, vcur, ldgv;
   float softcap, inv_softcap;
   uint16_t* g;
+  int64_t lo_off;   // elements from the hi to the lo chunk (SPLIT)
 
   __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm,
                                              int wn, int lane, char* smem) const {
@@ -527,40 +530,55 @@ struct EpiGrad {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          float gv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rq + e;
-            float z = acc[i][j][r];
-            float d = 1.f;
-            if (SOFTCAP) {
-              const float th = tanh_fast(z * inv_softcap);
-              z = softcap * th;
-              d = 1.f - th * th;
-            }
-            const float p = __builtin_amdgcn_exp2f((z - l) * kLog2e);
-            // (p - [v == y]) * coef, the one-hot as a selected subtrahend
-            const float sub = (yd == i * 32 + 8 * rq + e) ? coef : 0.f;
-            gv[e] = SOFTCAP ? (p * coef - sub) * d : fmaf(p, coef, -sub);
+        for (int r = 0; r < 16; ++r) {
+          float z = acc[i][j][r];
+          float d = 1.f;
+          if (SOFTCAP) {
+            const float th = tanh_fast(z * inv_softcap);
+            z = softcap * th;
+            d = 1.f - th * th;
           }
-          const uint32_t lo = pack_bf16x2(gv[0], gv[1]);
-          const uint32_t hi = pack_bf16x2(gv[2], gv[3]);
-          const int slot = (i * 8 + 2 * rq + half) ^ (tl & 31);
-          *reinterpret_cast<uint2*>(reg + tl * 256 + slot * 8) = make_uint2(lo, hi);
+          const float p = __builtin_amdgcn_exp2f((z - l) * kLog2e);
+          // (p - [v == y]) * coef, the one-hot as a selected subtrahend
+          const float sub = (yd == i * 32 + 8 * (r >> 2) + (r & 3)) ? coef : 0.f;
+          acc[i][j][r] = SOFTCAP ? (p * coef - sub) * d : fmaf(p, coef, -sub);
         }
     }
-    __syncthreads();
-    // read back 16-byte runs of token rows and store them
+#pragma unroll
+    for (int part = 0; part < (SPLIT ? 2 : 1); ++part) {
+      if (part) __syncthreads();                       // the staging area is reused
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tl = j * 32 + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[e] = acc[i][j][4 * rq + e];
+              if (part) v[e] -= bf16_to_f32(f32_to_bf16(v[e]));   // the lo part
+            }
+            const uint32_t lo = pack_bf16x2(v[0], v[1]);
+            const uint32_t hi = pack_bf16x2(v[2], v[3]);
+            const int slot = (i * 8 + 2 * rq + half) ^ (tl & 31);
+            *reinterpret_cast<uint2*>(reg + tl * 256 + slot * 8) = make_uint2(lo, hi);
+          }
+      }
+      __syncthreads();
+      // read back 16-byte runs of token rows and store them
+      uint16_t* gp = g + part * lo_off;
 #pragma unroll 4
-    for (int q = 0; q < 32; ++q) {
-      const int idx = q * 64 + lane;
-      const int tl = idx >> 4, ch = idx & 15, x = tl & 31;
-      u32x4 v = *reinterpret_cast<const u32x4*>(reg + tl * 256 + (((2 * ch) ^ x) & ~1) * 8);
-      if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-      const int64_t t = n0 + wn * 128 + tl;
-      const int64_t vl = m0 + wm * 128 + 8 * ch;
-      if (t < N && vl < vcur) *reinterpret_cast<u32x4*>(g + t * ldgv + vl) = v;
+      for (int q = 0; q < 32; ++q) {
+        const int idx = q * 64 + lane;
+        const int tl = idx >> 4, ch = idx & 15, x = tl & 31;
+        u32x4 v = *reinterpret_cast<const u32x4*>(reg + tl * 256 + (((2 * ch) ^ x) & ~1) * 8);
+        if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+        const int64_t t = n0 + wn * 128 + tl;
+        const int64_t vl = m0 + wm * 128 + 8 * ch;
+        if (t < N && vl < vcur) *reinterpret_cast<u32x4*>(gp + t * ldgv + vl) = v;
+      }
     }
   }
 };
@@ -622,6 +640,35 @@ struct EpiDW {
         v.z += bf16_to_f32(uint16_t(o.y)); v.w += bf16_to_f32(uint16_t(o.y >> 16));
       }
       *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+    }
+  };
+
+  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm,
+                                             int wn, int lane, char* smem) const {
+    Pass pass{*this, m0 + wm * 128, n0 + wn * 128};
+    staged_rows(acc, wm, wn, lane, smem, pass);
+  }
+};
+
+// ---- float32 dW epilogue (float32 gradients for bf16 inputs) -------------
+template <bool ACCUM>
+struct EpiDW32 {
+  float* dW;
+  int64_t H, v0, vcur;
+
+  struct Pass {
+    const EpiDW32& e;
+    int64_t r0, c0;   // global (chunk-relative row, column) of the wave block
+    __device__ __forceinline__ void prefetch(int, int) {}
+    __device__ __forceinline__ void store(int i, int, int row, int col, float4 v) {
+      const int64_t m = r0 + i * 32 + row, n = c0 + col;
+      if (m >= e.vcur || n >= e.H) return;
+      float4* p = reinterpret_cast<float4*>(e.dW + (e.v0 + m) * e.H + n);
+      if (ACCUM) {
+        const float4 o = *p;
+        v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+      }
+      *p = v;
     }
   };
 
@@ -714,20 +761,65 @@ hipError_t bf16_forward(const Plan& p, const Args& a, const Launcher& L) {
   return run_gemm<gemm::kFormN, gemm::kFormN>(l, a, e, kLseFwd, L);
 }
 
+// Float32 gradients for bf16 inputs: G as a bf16 hi + lo pair; dW and dH
+// each take one GEMM per part, hi then lo, accumulated in float32 straight
+// into the outputs in a fixed order (chunk by chunk, hi before lo).
+hipError_t bf16_backward_chunk_f32grad(const Plan& p, const Args& a, int64_t chunk,
+                                       const Launcher& L) {
+  const int64_t v0 = chunk * p.vchunk;
+  const int64_t vcur = gemm::chunk_rows(p, chunk);
+  uint16_t* g = static_cast<uint16_t*>(a.g);
+  const int64_t lo_off = p.vchunk * p.ldg;
+  hipError_t err;
+  if (a.softcap > 0.f) {
+    EpiGrad<true, true> eg{a.labels, a.lse, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
+                           p.vchunk, a.softcap, 1.f / a.softcap, g, lo_off};
+    err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
+                                               kGradLogits, L);
+  } else {
+    EpiGrad<false, true> eg{a.labels, a.lse, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
+                            p.vchunk, 0.f, 0.f, g, lo_off};
+    err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
+                                               kGradLogits, L);
+  }
+  float* dW = static_cast<float*>(a.dW);
+  for (int part = 0; part < 2 && err == hipSuccess; ++part) {
+    const gemm::Launch lw = gemm::backward_launch(p, chunk, 1, part);
+    if (part == 0 && !a.accumulate_dW)
+      err = run_gemm<gemm::kFormT, gemm::kFormT>(lw, a, EpiDW32<false>{dW, p.H, v0, vcur},
+                                                 kGemmDW, L);
+    else
+      err = run_gemm<gemm::kFormT, gemm::kFormT>(lw, a, EpiDW32<true>{dW, p.H, v0, vcur},
+                                                 kGemmDW, L);
+  }
+  float* dH = static_cast<float*>(a.dH);
+  for (int part = 0; part < 2 && err == hipSuccess; ++part) {
+    const gemm::Launch lh = gemm::backward_launch(p, chunk, 2, part);
+    if (chunk == 0 && part == 0)
+      err = run_gemm<gemm::kFormN, gemm::kFormT>(lh, a, EpiDH<true, false>{nullptr, dH, p.N, p.H},
+                                                 kGemmDH, L);
+    else
+      err = run_gemm<gemm::kFormN, gemm::kFormT>(lh, a, EpiDH<false, false>{nullptr, dH, p.N, p.H},
+                                                 kGemmDH, L);
+  }
+  return err;
+}
+
 hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, const Launcher& L) {
+  if (p.g_parts == 2) return bf16_backward_chunk_f32grad(p, a, chunk, L);
   const int64_t v0 = chunk * p.vchunk;
   const int64_t vcur = gemm::chunk_rows(p, chunk);
   uint16_t* g = static_cast<uint16_t*>(a.g);
   // 1) recompute the logits of the chunk and form G[N][vchunk]
   hipError_t err;
   if (a.softcap > 0.f) {
-    EpiGrad<true> eg{a.labels, a.lse, a.sc, p.N, p.V, a.ignore_index, v0, vcur, p.vchunk,
-                     a.softcap, 1.f / a.softcap, g};
+    EpiGrad<true, false> eg{a.labels, a.lse, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
+                            p.vchunk, a.softcap, 1.f / a.softcap, g, 0};
     err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
                                                kGradLogits, L);
   } else {
-    EpiGrad<false> eg{a.labels, a.lse, a.sc, p.N, p.V, a.ignore_index, v0, vcur, p.vchunk,
-                      0.f, 0.f, g};
+    EpiGrad<false, false> eg{a.labels, a.lse, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
+                             p.vchunk, 0.f, 0.f, g, 0};
     err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
                                                kGradLogits, L);
   }

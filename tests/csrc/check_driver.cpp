@@ -66,6 +66,23 @@ int main() {
       EXPECT(fcall(n, 64, v, FLCE_BF16, FLCE_SUM, 0, 0.f, f) == FLCE_OK);
       EXPECT(fcall(n, 64, v, FLCE_BF16, FLCE_SUM, 0, 0.f, f - 1) == FLCE_ERR_WORKSPACE);
     }
+  // float32 gradients for bf16 inputs
+  {
+    const uintptr_t b = uintptr_t(1) << 32;
+    auto ex = [&](int dtype, int grad, size_t wsb) {
+      return flce_check_args_ex((void*)b, (void*)(b * 2), (int64_t*)(b * 3), 4096, 4096, 131072,
+                                -100, 0.f, FLCE_SUM, 0, (float*)(b * 4), (int64_t*)(b * 5),
+                                (void*)(b * 6), (void*)(b * 8), nullptr, dtype, 1.f, 0,
+                                (void*)(uintptr_t(1) << 40), wsb, nullptr, nullptr, grad);
+    };
+    EXPECT(ex(FLCE_BF16, FLCE_F32, big) == FLCE_OK);
+    EXPECT(ex(FLCE_F32, FLCE_BF16, big) == FLCE_ERR_UNSUPPORTED);
+    EXPECT(ex(FLCE_BF16, 9, big) == FLCE_ERR_ARG);
+    const size_t w = flce_workspace_size_ex(4096, 4096, 131072, FLCE_BF16, FLCE_F32);
+    EXPECT(w > 0 && ex(FLCE_BF16, FLCE_F32, w) == FLCE_OK && ex(FLCE_BF16, FLCE_F32, w - 1) == FLCE_ERR_WORKSPACE);
+    EXPECT(flce_vocab_chunk_ex(4096, 4096, 131072, FLCE_BF16, FLCE_F32) * 2 ==
+           flce_vocab_chunk(4096, 4096, 131072, FLCE_BF16));
+  }
   for (int s = -1; s < 8; ++s) EXPECT(flce_status_string(s) != nullptr);
   if (failures == 0) std::printf("all checks passed\n");
   return failures ? 1 : 0;

@@ -22,7 +22,7 @@ static void fail(const char* what, int64_t a, int64_t b, int64_t c) {
 }
 
 static int64_t alloc_of(const Plan& p, int buf) {
-  return buf == kBufW ? p.V * p.H : buf == kBufH ? p.N * p.H : p.vchunk * p.ldg;
+  return buf == kBufW ? p.V * p.H : buf == kBufH ? p.N * p.H : p.g_parts * p.vchunk * p.ldg;
 }
 
 static void check_operand(const Plan& p, const Launch& l, int which, int64_t row0) {
@@ -134,11 +134,18 @@ int main(int argc, char** argv) {
     } else {
       unsetenv("FLCE_VCHUNK");
     }
+    for (int grad : {1, 0}) {       // bf16 gradients, then float32 gradients (G hi + lo)
+      Plan p;
+      if (!make_plan(s.N, s.H, s.V, 1, &p, true, grad)) { fail("plan", s.N, s.H, s.V); continue; }
+      check_launch(p, forward_launch(p));
+      for (int64_t c = 0; c < p.n_chunks; ++c) {
+        check_launch(p, backward_launch(p, c, 0));
+        for (int part = 0; part < p.g_parts; ++part)
+          for (int w = 1; w < 3; ++w) check_launch(p, backward_launch(p, c, w, part));
+      }
+    }
     Plan p;
-    if (!make_plan(s.N, s.H, s.V, 1, &p)) { fail("plan", s.N, s.H, s.V); continue; }
-    check_launch(p, forward_launch(p));
-    for (int64_t c = 0; c < p.n_chunks; ++c)
-      for (int w = 0; w < 3; ++w) check_launch(p, backward_launch(p, c, w));
+    make_plan(s.N, s.H, s.V, 1, &p);
     std::printf("shape N=%lld H=%lld V=%lld chunk=%lld chunks=%lld: %s\n", (long long)s.N,
                 (long long)s.H, (long long)s.V, (long long)p.vchunk, (long long)p.n_chunks,
                 failures ? "FAILURES" : "ok");

@@ -246,3 +246,38 @@ def test_python_forward_validation_without_gpu():
         m.flce_forward(h, W, y)                   # CPU tensors: refused, no fallback
     with torch.no_grad(), pytest.raises(ValueError):
         m.fused_linear_cross_entropy(h, y, W)     # forward-only route, same refusal
+
+
+# ------------------------------------------- float32 gradients for bf16 inputs
+def test_f32grad_plan(lib):
+    """G kept as a hi + lo pair: half the vocabulary rows per chunk, no dH
+    accumulator (dH is float32 itself), still within N*V*4/8."""
+    for N, H, V in [(8192, 4096, 131072), (8192, 3584, 256000), (16384, 4096, 131072)]:
+        assert lib.flce_vocab_chunk_ex(N, H, V, 1, 0) == lib.flce_vocab_chunk(N, H, V, 1) // 2
+        ws = lib.flce_workspace_size_ex(N, H, V, 1, 0)
+        assert 0 < ws <= N * V * 4 // 8
+    # same-dtype calls are exactly the plain entry points
+    assert lib.flce_workspace_size_ex(8192, 4096, 131072, 1, 1) == lib.flce_workspace_size(8192, 4096, 131072, 1)
+    assert lib.flce_workspace_size_ex(32, 64, 1024, 0, 0) == lib.flce_workspace_size(32, 64, 1024, 0)
+    assert lib.flce_workspace_size_ex(32, 64, 1024, 0, 1) == 0      # f32 inputs, bf16 grads
+    assert lib.flce_workspace_size_ex(32, 64, 1024, 1, 7) == 0
+
+
+@pytest.mark.parametrize("kw,grad,code", [
+    (dict(), 0, 0), (dict(), 1, 0),
+    (dict(dtype=0, H=3), 0, 0),
+    (dict(dtype=0), 1, 2),                  # float32 inputs with bf16 gradients
+    (dict(), 5, 1),                         # unknown gradient dtype
+    (dict(dW=A16 * 512 + 4), 0, 2),         # float32 gradients still need 16-byte alignment
+    (dict(dH=A16 * 512), 0, 1),             # dH overlapping dW
+    (dict(wsb=16), 0, 3),
+])
+def test_check_args_ex(lib, kw, grad, code):
+    assert lib.flce_check_args_ex(*_args(**kw), grad) == code
+
+
+def test_f32grad_workspace_check(lib):
+    need = lib.flce_workspace_size_ex(64, 64, 128, 1, 0)
+    assert lib.flce_check_args_ex(*_args(wsb=need), 0) == 0
+    assert lib.flce_check_args_ex(*_args(wsb=need - 1), 0) == 3
+    assert lib.flce_forward_backward_ex(*_args(wsb=1), 0) == 3      # rejected before launch
