@@ -275,6 +275,39 @@ def main():
     log(f"float32 gradients: {g_ms:.3f} ms/step")
     del dH32, dW32, gws
 
+    # The no-recompute variant on the same inputs (token chunks whose
+    # probabilities are kept instead of recomputing the logits), timed the
+    # same way, with its per-kernel split.
+    nws = torch.empty(m.flce_workspace_size_nr(N, H, V, W.dtype), dtype=torch.uint8, device=dev)
+
+    def step_nr():
+        m.flce_forward_backward(h, W, y, ignore_index=w.ignore_index, softcap=w.softcap,
+                                reduction=w.reduction, dH=dH, dW=dW, workspace=nws, loss=loss,
+                                num_tokens=nt, recompute=False)
+
+    for _ in range(2):
+        step_nr()
+    torch.cuda.synchronize()
+    tn0 = time.perf_counter()
+    for _ in range(args.steps):
+        step_nr()
+    torch.cuda.synchronize()
+    n_ms = (time.perf_counter() - tn0) * 1e3 / args.steps
+    nr_kernels = {}
+    if timing:
+        m.flce_profile_begin()
+        for _ in range(3):
+            step_nr()
+        torch.cuda.synchronize()
+        m.flce_profile_end()
+        nr_kernels = {k: round(ms / 3, 4) for k, (ms, n) in m.flce_profile_query().items() if n}
+    no_recompute = {"ms_per_step": round(n_ms, 4), "tokens_per_s": round(N / (n_ms * 1e-3), 1),
+                    "tflops_6nhv": round(6 * nhv / (n_ms * 1e-3) / 1e12, 1),
+                    "token_chunk": m.flce_token_chunk_nr(N, H, V, W.dtype),
+                    "workspace_bytes": int(nws.numel()), "kernels_ms_per_step": nr_kernels}
+    log(f"no recompute: {n_ms:.3f} ms/step {nr_kernels}")
+    del nws
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_sample_tokens} sampled tokens ...")
@@ -307,6 +340,7 @@ def main():
         "roofline": roofline,
         "forward_only": forward_only,
         "float32_grads": float32_grads,
+        "no_recompute": no_recompute,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "cpu_baseline": ({k: (round(v, 3) if isinstance(v, float) else v)

@@ -170,6 +170,41 @@ int flce_forward_backward_ex(const void* h, const void* W, const int64_t* labels
                              float* lse_out, int grad_dtype);
 
 /*
+ * The no-recompute variant (bf16 only): the same call and results, with one
+ * more argument, token_chunk. Instead of recomputing the logits in the
+ * backward pass (2*N*H*V flop), it goes through the tokens in chunks of
+ * token_chunk (rounded up to 256; <= 0: min(N, 4096) rounded up) and keeps
+ * each chunk's probabilities relative to each vocabulary tile's max,
+ * P'[t][v] = exp(z'_tv - M) <= 1, as bf16 in the workspace; after the chunk's
+ * log-sum-exp they become G in place (G = c (P' exp(M - lse) - [v = y])
+ * dz'/dz, the target element from its float32 logit), then dW (added over
+ * the chunks in bf16, as with accumulate_dW) and the chunk's dH. The chunked
+ * path that the Modalities PR 464 page describes ("What the reference
+ * implementations do": memory is bounded by chunking the sequence) is the
+ * model; the logits themselves are never rounded to bf16. Cost: 6*N*H*V
+ * flop, plus token_chunk * roundup(V, 256) * 2 bytes of workspace
+ * (flce_workspace_size_nr), 1 GiB at N >= 4096, V = 131072 with the default.
+ * Errors as flce_check_args, with FLCE_ERR_UNSUPPORTED for float32 inputs;
+ * flce_token_chunk_nr gives the chunk used.
+ */
+size_t flce_workspace_size_nr(int64_t N, int64_t H, int64_t V, int dtype, int64_t token_chunk);
+int64_t flce_token_chunk_nr(int64_t N, int64_t H, int64_t V, int dtype, int64_t token_chunk);
+int flce_check_args_nr(const void* h, const void* W, const int64_t* labels,
+                       int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                       float softcap, int reduction, int64_t num_label_tokens,
+                       float* loss, int64_t* num_tokens, void* dH, void* dW,
+                       void* stream, int dtype, float mb_scale, int accumulate_dW,
+                       void* workspace, size_t workspace_bytes, int32_t* status,
+                       float* lse_out, int64_t token_chunk);
+int flce_forward_backward_nr(const void* h, const void* W, const int64_t* labels,
+                             int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                             float softcap, int reduction, int64_t num_label_tokens,
+                             float* loss, int64_t* num_tokens, void* dH, void* dW,
+                             void* stream, int dtype, float mb_scale, int accumulate_dW,
+                             void* workspace, size_t workspace_bytes, int32_t* status,
+                             float* lse_out, int64_t token_chunk);
+
+/*
  * flce_forward_workspace_size -- bytes of device scratch that flce_forward
  * needs (256-byte aligned base required): the per-tile log-sum-exp partials
  * and the per-token lse and target logits only, O(N * V / 256 + N) bytes.

@@ -16,6 +16,10 @@ Contracts (see include/flce.h):
 * ``grad_dtype=torch.float32`` with bf16 inputs returns float32 dH and dW (the
   logit gradient kept as a bf16 hi + lo pair), for callers that accumulate
   gradients over micro-batches in float32; it costs twice the dW/dH work.
+* ``recompute=False`` (bf16) is the no-recompute variant: tokens in chunks of
+  ``token_chunk`` whose probabilities are kept (bf16, relative to each vocabulary
+  tile's max) instead of recomputing the logits, 3 GEMM passes instead of 4, at
+  the cost of token_chunk x V x 2 bytes of workspace.
 * The forward call computes dH and dW as well; ``backward`` only scales them by
   the incoming gradient. When no gradient is wanted (``torch.no_grad()``, or
   neither input requires one) the forward-only entry runs instead: the same
@@ -34,6 +38,8 @@ __all__ = [
     "flce_workspace_size",
     "flce_check_args",
     "flce_forward_backward",
+    "flce_workspace_size_nr",
+    "flce_token_chunk_nr",
     "flce_forward",
     "flce_forward_workspace_size",
     "flce_forward_check_args",
@@ -89,6 +95,14 @@ def flce_workspace_size(N: int, H: int, V: int, dtype: torch.dtype,
 
 def flce_forward_workspace_size(N: int, H: int, V: int, dtype: torch.dtype) -> int:
     return int(_lib.load().flce_forward_workspace_size(N, H, V, _dtype_code(dtype)))
+
+
+def flce_workspace_size_nr(N: int, H: int, V: int, dtype: torch.dtype, token_chunk: int = 0) -> int:
+    return int(_lib.load().flce_workspace_size_nr(N, H, V, _dtype_code(dtype), int(token_chunk)))
+
+
+def flce_token_chunk_nr(N: int, H: int, V: int, dtype: torch.dtype, token_chunk: int = 0) -> int:
+    return int(_lib.load().flce_token_chunk_nr(N, H, V, _dtype_code(dtype), int(token_chunk)))
 
 
 def flce_vocab_chunk(N: int, H: int, V: int, dtype: torch.dtype,
@@ -160,7 +174,8 @@ def flce_forward_backward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor
                           status: Optional[torch.Tensor] = None,
                           loss: Optional[torch.Tensor] = None,
                           num_tokens: Optional[torch.Tensor] = None,
-                          grad_dtype: Optional[torch.dtype] = None):
+                          grad_dtype: Optional[torch.dtype] = None,
+                          recompute: bool = True, token_chunk: int = 0):
     """One fused forward + backward on the current stream.
 
     h [N,H], W [V,H] (bf16 or fp32, same dtype, contiguous, on one GPU), labels
@@ -168,6 +183,8 @@ def flce_forward_backward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor
     device tensors; nothing is synchronised. Output/workspace tensors may be
     passed in to avoid allocation. dH and dW have ``grad_dtype`` (default: the
     input dtype; float32 with bf16 inputs is the float32-gradient mode).
+    ``recompute=False`` selects the no-recompute variant (bf16 inputs and
+    gradients) with token chunks of ``token_chunk`` (0: automatic).
     """
     if h.dim() != 2 or W.dim() != 2:
         raise ValueError("h must be [N, H] and W [V, H]")
@@ -197,7 +214,12 @@ def flce_forward_backward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor
         _check_tensor("lse_out", lse_out, (N,), torch.float32, dev)
     if status is not None:
         _check_tensor("status", status, (), torch.int32, dev)
-    need = flce_workspace_size(N, H, V, W.dtype, gdt)
+    if not recompute:
+        if gdt != W.dtype:
+            raise ValueError("the no-recompute variant returns gradients in the input dtype")
+        need = flce_workspace_size_nr(N, H, V, W.dtype, token_chunk)
+    else:
+        need = flce_workspace_size(N, H, V, W.dtype, gdt)
     if need == 0:
         raise FlceError(_lib.ERR_UNSUPPORTED if W.dtype == torch.float32 else _lib.ERR_ARG,
                         "flce_workspace_size")
@@ -208,7 +230,10 @@ def flce_forward_backward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor
                      loss, num_tokens, dH, dW, stream, W.dtype, mb_scale, accumulate_dW,
                      workspace, status, lse_out)
     with torch.cuda.device(dev):
-        rc = _lib.load().flce_forward_backward_ex(*args, _dtype_code(gdt))
+        if recompute:
+            rc = _lib.load().flce_forward_backward_ex(*args, _dtype_code(gdt))
+        else:
+            rc = _lib.load().flce_forward_backward_nr(*args, int(token_chunk))
     if rc != _lib.OK:
         raise FlceError(rc, "flce_forward_backward")
     return loss, num_tokens, dH, dW

@@ -26,6 +26,10 @@ SIGNATURES = {
     "flce_vocab_chunk_ex": (_i64, [_i64, _i64, _i64, _i32, _i32]),
     "flce_check_args_ex": (_i32, _FB_ARGS + [_i32]),
     "flce_forward_backward_ex": (_i32, _FB_ARGS + [_i32]),
+    "flce_workspace_size_nr": (_sz, [_i64, _i64, _i64, _i32, _i64]),
+    "flce_token_chunk_nr": (_i64, [_i64, _i64, _i64, _i32, _i64]),
+    "flce_check_args_nr": (_i32, _FB_ARGS + [_i64]),
+    "flce_forward_backward_nr": (_i32, _FB_ARGS + [_i64]),
     "flce_forward_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
     "flce_forward_check_args": (_i32, _F_ARGS),
     "flce_forward": (_i32, _F_ARGS),

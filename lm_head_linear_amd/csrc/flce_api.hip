@@ -8,6 +8,7 @@
 #include "../../include/flce.h"
 #include "flce_internal.h"
 #include "flce_plan.h"
+#include "gemm_index.h"
 
 namespace {
 
@@ -55,7 +56,52 @@ void prof_after(int kind, hipStream_t s) {
 
 const char* kKindNames[flce::kNumKinds] = {"label_scan", "lse_fwd_gemm", "lse_merge",
                                            "loss_final", "grad_logits_gemm", "dW_gemm",
-                                           "dH_gemm", "fill"};
+                                           "dH_gemm", "fill", "probs_to_grad"};
+
+// The no-recompute variant (arguments already checked): token chunk by chunk,
+// the forward keeps the probabilities, the chunk's merge gives its lse, G is
+// formed in place, then dW (added over the chunks) and the chunk's dH.
+int run_nr(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H, int64_t V,
+           int64_t ignore_index, float softcap, int reduction, int64_t num_label_tokens,
+           float* loss, int64_t* num_tokens, void* dH, void* dW, void* stream, int dtype,
+           float mb_scale, int accumulate_dW, void* workspace, int32_t* status, float* lse_out,
+           int64_t token_chunk) {
+  flce::Plan p;
+  if (!flce::make_plan_nr(N, H, V, dtype, token_chunk, &p)) return FLCE_ERR_UNSUPPORTED;
+  flce::Launcher L{static_cast<hipStream_t>(stream), nullptr, nullptr};
+  if (g_prof.on) { L.before = prof_before; L.after = prof_after; }
+  char* ws = static_cast<char*>(workspace);
+  flce::Args a{};
+  a.h = h; a.W = W; a.labels = labels;
+  a.N = N; a.H = H; a.V = V;
+  a.ignore_index = ignore_index; a.softcap = softcap; a.reduction = reduction;
+  a.num_label_tokens = num_label_tokens;
+  a.loss = loss; a.num_tokens = num_tokens; a.dH = dH; a.dW = dW;
+  a.mb_scale = mb_scale; a.accumulate_dW = accumulate_dW ? 1 : 0;
+  a.status = status; a.lse_out = lse_out;
+  a.sc = reinterpret_cast<flce::Scalars*>(ws + p.off_scalars);
+  hipError_t e;
+  if (N == 0) {
+    e = flce::launch_empty(p, a, L);
+    if (e == hipSuccess && !a.accumulate_dW)
+      e = flce::launch_zero_bytes(dW, size_t(V) * H * p.elem, L);
+    return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+  }
+  a.part = reinterpret_cast<float2*>(ws + p.off_part);
+  a.zt = reinterpret_cast<float*>(ws + p.off_zt);
+  a.lse = reinterpret_cast<float*>(ws + p.off_lse);
+  a.lsum = reinterpret_cast<double*>(ws + p.off_lsum);
+  a.g = ws + p.off_g;
+  a.dh_acc = nullptr;
+  e = flce::launch_label_scan(p, a, L);
+  for (int64_t c = 0; e == hipSuccess && c < p.n_tok_chunks; ++c) {
+    e = flce::bf16_nr_forward_chunk(p, a, c, L);
+    if (e == hipSuccess) e = flce::launch_merge(p, a, c * p.nc, flce::gemm::nr_chunk_tokens(p, c), L);
+    if (e == hipSuccess) e = flce::bf16_nr_backward_chunk(p, a, c, L);
+  }
+  if (e == hipSuccess) e = flce::launch_loss_final(p, a, L);
+  return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
 
 // The launch sequence of both entry points; arguments already checked.
 // Forward: label scan, forward GEMM with the log-sum-exp partials, merge and
@@ -136,6 +182,55 @@ int flce_forward_backward_ex(const void* h, const void* W, const int64_t* labels
   return run(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens, loss,
              num_tokens, dH, dW, stream, dtype, mb_scale, accumulate_dW, workspace, status,
              lse_out, true, grad_dtype);
+}
+
+size_t flce_workspace_size_nr(int64_t N, int64_t H, int64_t V, int dtype, int64_t token_chunk) {
+  flce::Plan p;
+  if (!flce::make_plan_nr(N, H, V, dtype, token_chunk, &p)) return 0;
+  return p.total;
+}
+
+int64_t flce_token_chunk_nr(int64_t N, int64_t H, int64_t V, int dtype, int64_t token_chunk) {
+  flce::Plan p;
+  if (!flce::make_plan_nr(N, H, V, dtype, token_chunk, &p)) return 0;
+  return p.nc;
+}
+
+int flce_check_args_nr(const void* h, const void* W, const int64_t* labels, int64_t N,
+                       int64_t H, int64_t V, int64_t ignore_index, float softcap,
+                       int reduction, int64_t num_label_tokens, float* loss,
+                       int64_t* num_tokens, void* dH, void* dW, void* stream, int dtype,
+                       float mb_scale, int accumulate_dW, void* workspace,
+                       size_t workspace_bytes, int32_t* status, float* lse_out,
+                       int64_t token_chunk) {
+  // the common rules, with the workspace checked against this variant's plan
+  int st = flce_check_args_ex(h, W, labels, N, H, V, ignore_index, softcap, reduction,
+                              num_label_tokens, loss, num_tokens, dH, dW, stream, dtype,
+                              mb_scale, accumulate_dW, workspace, size_t(-1), status, lse_out,
+                              dtype);
+  if (st != FLCE_OK) return st;
+  if (dtype != FLCE_BF16 || token_chunk < 0) return FLCE_ERR_UNSUPPORTED;
+  const size_t need = flce_workspace_size_nr(N, H, V, dtype, token_chunk);
+  if (need == 0) return FLCE_ERR_ARG;
+  if (workspace_bytes < need) return FLCE_ERR_WORKSPACE;
+  return FLCE_OK;
+}
+
+int flce_forward_backward_nr(const void* h, const void* W, const int64_t* labels, int64_t N,
+                             int64_t H, int64_t V, int64_t ignore_index, float softcap,
+                             int reduction, int64_t num_label_tokens, float* loss,
+                             int64_t* num_tokens, void* dH, void* dW, void* stream, int dtype,
+                             float mb_scale, int accumulate_dW, void* workspace,
+                             size_t workspace_bytes, int32_t* status, float* lse_out,
+                             int64_t token_chunk) {
+  int st = flce_check_args_nr(h, W, labels, N, H, V, ignore_index, softcap, reduction,
+                              num_label_tokens, loss, num_tokens, dH, dW, stream, dtype,
+                              mb_scale, accumulate_dW, workspace, workspace_bytes, status,
+                              lse_out, token_chunk);
+  if (st != FLCE_OK) return st;
+  return run_nr(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens, loss,
+                num_tokens, dH, dW, stream, dtype, mb_scale, accumulate_dW, workspace, status,
+                lse_out, token_chunk);
 }
 
 int flce_forward(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H,

@@ -77,6 +77,42 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
   return true;
 }
 
+bool make_plan_nr(int64_t N, int64_t H, int64_t V, int dtype, int64_t token_chunk, Plan* p) {
+  if (dtype != FLCE_BF16) return false;
+  if (token_chunk < 0) token_chunk = 0;
+  if (token_chunk > (int64_t(1) << 31)) return false;
+  Plan q;
+  if (!make_plan(N, H, V, dtype, &q, false)) return false;
+  q.nr = true;
+  q.backward = true;
+  q.grad_dtype = dtype;
+  q.grad_elem = q.elem;
+  const int64_t nmax = round_up(N > 0 ? N : 1, q.tile);
+  int64_t nc = token_chunk > 0 ? round_up(token_chunk, q.tile) : round_up(N < 4096 ? (N > 0 ? N : 1) : 4096, q.tile);
+  if (nc > nmax) nc = nmax;
+  q.nc = nc;
+  q.n_tok_chunks = ceil_div(N, nc);
+  q.vp = round_up(V, q.tile);
+  // per chunk: partials and per-token arrays for nc tokens; block sums for all N
+  q.ld_part = nc;
+  q.vchunk = q.vp;          // G row length
+  q.n_chunks = 1;
+  size_t off = 0;
+  q.off_scalars = off; off = align256(off + sizeof(Scalars));
+  if (N > 0) {
+    q.off_part = off;  off = align256(off + size_t(q.n_voc_tiles) * q.ld_part * 2 * sizeof(float));
+    q.off_zt = off;    off = align256(off + size_t(q.ld_part) * sizeof(float));
+    q.off_lse = off;   off = align256(off + size_t(q.ld_part) * sizeof(float));
+    q.off_lsum = off;  off = align256(off + size_t(q.n_loss_blocks) * sizeof(double));
+    q.off_g = off;     off = align256(off + size_t(nc) * size_t(q.vp) * q.elem);
+  }
+  q.off_dhacc = 0;
+  q.need_dh_acc = false;
+  q.total = off;
+  *p = q;
+  return true;
+}
+
 }  // namespace flce
 
 extern "C" {

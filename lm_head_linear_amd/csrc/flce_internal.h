@@ -19,7 +19,8 @@ enum Kind : int {
   kGemmDW = 5,
   kGemmDH = 6,
   kFill = 7,
-  kNumKinds = 8,
+  kProbsToGrad = 8,
+  kNumKinds = 9,
 };
 
 // Everything one call needs on the device side.
@@ -63,11 +64,19 @@ struct Launcher {
 hipError_t launch_empty(const Plan& p, const Args& a, const Launcher& L);
 hipError_t launch_label_scan(const Plan& p, const Args& a, const Launcher& L);
 hipError_t launch_merge_and_loss(const Plan& p, const Args& a, const Launcher& L);
+// The merge for tokens [t0, t0 + nt) (t0 a multiple of 32), and the final
+// loss sum over all tokens' blocks.
+hipError_t launch_merge(const Plan& p, const Args& a, int64_t t0, int64_t nt, const Launcher& L);
+hipError_t launch_loss_final(const Plan& p, const Args& a, const Launcher& L);
 hipError_t launch_zero_bytes(void* ptr, size_t bytes, const Launcher& L);
 
 // bf16 MFMA path.
 hipError_t bf16_forward(const Plan& p, const Args& a, const Launcher& L);
 hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, const Launcher& L);
+// No-recompute variant, token chunk c: the forward that keeps the
+// probabilities, then (after the chunk's merge) G in place and dW, dH.
+hipError_t bf16_nr_forward_chunk(const Plan& p, const Args& a, int64_t c, const Launcher& L);
+hipError_t bf16_nr_backward_chunk(const Plan& p, const Args& a, int64_t c, const Launcher& L);
 
 // float32 path.
 hipError_t f32_forward(const Plan& p, const Args& a, const Launcher& L);

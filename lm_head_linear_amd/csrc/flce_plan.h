@@ -39,6 +39,11 @@ struct Plan {
   int64_t n_chunks = 0;
   int64_t n_loss_blocks = 0; // blocks of the lse-merge kernel (32 tokens each)
   bool backward = true;      // plan includes the gradient buffers
+  // No-recompute variant: tokens in chunks of `nc`; per chunk the forward
+  // stores the probabilities relative to each tile's max, P'[t][v] bf16 with
+  // row length `vp`, in the G buffer, which then becomes G in place.
+  bool nr = false;
+  int64_t nc = 0, n_tok_chunks = 0, vp = 0;
   bool need_dh_acc = false;  // float32 dH accumulator needed (bf16, >1 chunk)
   size_t elem = 0;           // bytes per element of h/W/G
   size_t grad_elem = 0;      // bytes per element of dH/dW
@@ -56,5 +61,11 @@ struct Plan {
 // refused.
 bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backward = true,
                int grad_dtype = -1);
+
+// Plan of the no-recompute variant (bf16 only): token chunks of
+// `token_chunk` tokens (rounded up to the tile; <= 0: min(N, 4096) rounded
+// up), each with a [nc][roundup(V, 256)] bf16 buffer of probabilities that
+// becomes that chunk's G.
+bool make_plan_nr(int64_t N, int64_t H, int64_t V, int dtype, int64_t token_chunk, Plan* p);
 
 }  // namespace flce

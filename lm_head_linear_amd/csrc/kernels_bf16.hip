@@ -484,15 +484,61 @@ struct EpiLse {
   }
 };
 
+// ---- token-major bf16 stores of a tile held in the accumulators ----------
+// The tile's rows are vocabulary ids, its columns tokens; the destination is
+// row-major by token: dst[t][v] with row length ld. Each wave stages its
+// 128 x 128 block in its own 32 KiB of LDS as [token][vocab] (a lane packs
+// its 4 consecutive vocab values into 8 bytes; 8-byte slots XOR-swizzled by
+// token), then writes whole 16-byte runs of token rows; columns t >= nt and
+// rows v >= nv are not written. LO stores the residual v - bf16(v) instead
+// of v (the low half of a bf16 pair). The caller separates a second use of
+// the staging area with a barrier.
+template <bool LO>
+__device__ __forceinline__ void store_token_major(const f32x16 (&acc)[4][4], char* smem, int wm,
+                                                  int wn, int lane, uint16_t* dst, int64_t ld,
+                                                  int64_t m0, int64_t n0, int64_t nt,
+                                                  int64_t nv) {
+  const int half = lane >> 5;
+  char* reg = smem + (wm + 2 * wn) * kWaveScratch;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tl = j * 32 + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = acc[i][j][4 * rq + e];
+          if (LO) v[e] -= bf16_to_f32(f32_to_bf16(v[e]));
+        }
+        const uint32_t lo = pack_bf16x2(v[0], v[1]);
+        const uint32_t hi = pack_bf16x2(v[2], v[3]);
+        const int slot = (i * 8 + 2 * rq + half) ^ (tl & 31);
+        *reinterpret_cast<uint2*>(reg + tl * 256 + slot * 8) = make_uint2(lo, hi);
+      }
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int q = 0; q < 32; ++q) {
+    const int idx = q * 64 + lane;
+    const int tl = idx >> 4, ch = idx & 15, x = tl & 31;
+    u32x4 v = *reinterpret_cast<const u32x4*>(reg + tl * 256 + (((2 * ch) ^ x) & ~1) * 8);
+    if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+    const int64_t t = n0 + wn * 128 + tl;
+    const int64_t vl = m0 + wm * 128 + 8 * ch;
+    if (t < nt && vl < nv) *reinterpret_cast<u32x4*>(dst + t * ld + vl) = v;
+  }
+}
+
 // ---- backward epilogue: the logit gradient G for one vocabulary chunk ----
 // G[t, v] = c * valid_t * (exp(z'_tv - lse_t) - [v = y_t]) * dz'/dz, stored
 // bf16 token-major as G[t][v - v0] (row length ldgv). Tile rows are
-// chunk-relative vocab ids, columns tokens. G is first formed in float32 in
-// place of the logits; then each wave stages its 128 x 128 block in its own
-// 32 KiB of LDS as [token][vocab] (a lane packs its 4 consecutive vocab
-// values into 8 bytes; 8-byte slots XOR-swizzled by token) and writes whole
-// 16-byte runs of token rows. SPLIT (float32 gradients) stores two bf16
-// chunks, G_hi = bf16(G) at g and G_lo = bf16(G - G_hi) at g + lo_off.
+// chunk-relative vocab ids, columns tokens. G is formed in float32 in place
+// of the logits, then stored through store_token_major. SPLIT (float32
+// gradients) stores two bf16 chunks, G_hi = bf16(G) at g and
+// G_lo = bf16(G - G_hi) at g + lo_off.
 template <bool SOFTCAP, bool SPLIT>
 struct EpiGrad {
   const int64_t* labels;
@@ -507,7 +553,6 @@ struct EpiGrad {
                                              int wn, int lane, char* smem) const {
     const float c = sc->c32;
     const int half = lane >> 5;
-    char* reg = smem + (wm + 2 * wn) * kWaveScratch;   // this wave's 32 KiB
     const int64_t vbase = v0 + m0 + wm * 128;           // global vocab id of block row 0
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -544,44 +589,163 @@ struct EpiGrad {
           acc[i][j][r] = SOFTCAP ? (p * coef - sub) * d : fmaf(p, coef, -sub);
         }
     }
-#pragma unroll
-    for (int part = 0; part < (SPLIT ? 2 : 1); ++part) {
-      if (part) __syncthreads();                       // the staging area is reused
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tl = j * 32 + (lane & 31);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            float v[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              v[e] = acc[i][j][4 * rq + e];
-              if (part) v[e] -= bf16_to_f32(f32_to_bf16(v[e]));   // the lo part
-            }
-            const uint32_t lo = pack_bf16x2(v[0], v[1]);
-            const uint32_t hi = pack_bf16x2(v[2], v[3]);
-            const int slot = (i * 8 + 2 * rq + half) ^ (tl & 31);
-            *reinterpret_cast<uint2*>(reg + tl * 256 + slot * 8) = make_uint2(lo, hi);
-          }
-      }
-      __syncthreads();
-      // read back 16-byte runs of token rows and store them
-      uint16_t* gp = g + part * lo_off;
-#pragma unroll 4
-      for (int q = 0; q < 32; ++q) {
-        const int idx = q * 64 + lane;
-        const int tl = idx >> 4, ch = idx & 15, x = tl & 31;
-        u32x4 v = *reinterpret_cast<const u32x4*>(reg + tl * 256 + (((2 * ch) ^ x) & ~1) * 8);
-        if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-        const int64_t t = n0 + wn * 128 + tl;
-        const int64_t vl = m0 + wm * 128 + 8 * ch;
-        if (t < N && vl < vcur) *reinterpret_cast<u32x4*>(gp + t * ldgv + vl) = v;
-      }
+    store_token_major<false>(acc, smem, wm, wn, lane, g, ldgv, m0, n0, N, vcur);
+    if (SPLIT) {
+      __syncthreads();                                 // the staging area is reused
+      store_token_major<true>(acc, smem, wm, wn, lane, g + lo_off, ldgv, m0, n0, N, vcur);
     }
   }
 };
+
+// ---- forward epilogue of the no-recompute variant ------------------------
+// As EpiLse, and it also keeps the probabilities: with the tile max Mx of
+// each token shared by the two waves of its column, it stores
+// P'[t][v] = exp(z'_tv - Mx) (<= 1) as bf16, token-major with row length ldp,
+// and the partial (Mx, sum of P') of the tile. G follows later without
+// recomputing the logits: G = c (P' exp(Mx - lse) - [v = y]) dz'/dz.
+template <bool SOFTCAP>
+struct EpiLseP {
+  const int64_t* labels;
+  int64_t N, V, ignore_index;
+  float softcap, inv_softcap;
+  float2* part;  // [n_voc_tiles][ld_part]: (max, sum of exp(x - max)) of the tile
+  int64_t ld_part;
+  float* zt;     // target logit (softcapped), one writer per non-ignored token
+  uint16_t* probs;
+  int64_t ldp;
+
+  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm,
+                                             int wn, int lane, char* smem) const {
+    const int half = lane >> 5;
+    const int64_t vbase = m0 + wm * 128;
+    float mx[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t t = n0 + acc_col(wn, j, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float z = acc[i][j][r];
+          if (SOFTCAP) z = softcap * tanh_fast(z * inv_softcap);
+          const int64_t v = m0 + acc_row(wm, i, r, lane);
+          acc[i][j][r] = v < V ? z : -INFINITY;
+        }
+      const int64_t y = t < N ? labels[t] : ignore_index;
+      if (y != ignore_index && y >= vbase && y < vbase + 128 && y < V) {
+        const int d = int(y - vbase);
+        const int ti = d >> 5, w = d & 31;
+        if (((w >> 2) & 1) == half) {
+          const int tr = ((w >> 3) << 2) | (w & 3);
+          float val = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) val = (i == ti && r == tr) ? acc[i][j][r] : val;
+          zt[t] = val;
+        }
+      }
+      float m = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[i][j][r]);
+      mx[j] = fmaxf(m, __shfl_xor(m, 32));
+    }
+    // the tile max of each token column, from both waves that hold it
+    float* xb = reinterpret_cast<float*>(smem);      // [2][256] maxima, then [256] sums
+    if (half == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xb[wm * 256 + wn * 128 + j * 32 + lane] = mx[j];
+    }
+    __syncthreads();
+    float sm[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float Mx = fmaxf(mx[j], xb[(1 - wm) * 256 + wn * 128 + j * 32 + (lane & 31)]);
+      mx[j] = Mx;
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p =
+              Mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((acc[i][j][r] - Mx) * kLog2e);
+          acc[i][j][r] = p;
+          s += p;
+        }
+      sm[j] = s + __shfl_xor(s, 32);
+    }
+    __syncthreads();                                  // maxima read before the sums reuse xb
+    if (wm == 1 && half == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xb[wn * 128 + j * 32 + lane] = sm[j];
+    }
+    __syncthreads();
+    if (wm == 0 && half == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t t = n0 + acc_col(wn, j, lane);
+        if (t < ld_part)
+          part[(m0 / kBM) * ld_part + t] = make_float2(mx[j], sm[j] + xb[wn * 128 + j * 32 + lane]);
+      }
+    }
+    __syncthreads();                                  // sums read before the staging reuses LDS
+    store_token_major<false>(acc, smem, wm, wn, lane, probs, ldp, m0, n0, N, V);
+  }
+};
+
+// G in place of the stored probabilities of one token chunk:
+//   G[t][v] = c valid_t (P'[t][v] exp(M_tv - lse_t) - [v = y_t]) dz'/dz
+// with M_tv the max of v's vocabulary tile for token t (the forward partial).
+// The target element is formed from the float32 target logit instead:
+// c (exp(z'_ty - lse_t) - 1) dz'/dz. With a softcap, dz'/dz = 1 - (z'/s)^2 and
+// z' = M + ln P' elsewhere. One thread converts 8 consecutive v (16 bytes).
+template <bool SOFTCAP>
+__global__ __launch_bounds__(256) void k_probs_to_grad(
+    uint16_t* __restrict__ gp, int64_t ldp, int64_t nt, int64_t V,
+    const float2* __restrict__ part, int64_t ld_part, const float* __restrict__ lse,
+    const float* __restrict__ zt, const int64_t* __restrict__ labels, int64_t ignore_index,
+    const Scalars* __restrict__ sc, float inv_softcap) {
+  const int64_t runs = (V + 7) / 8;
+  const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (r >= runs) return;
+  const int64_t v0 = r * 8;
+  for (int64_t t = blockIdx.y; t < nt; t += gridDim.y) {
+    uint16_t* row = gp + t * ldp + v0;
+    const int64_t y = labels[t];
+    const float coef = y == ignore_index ? 0.f : ((y < 0 || y >= V) ? NAN : sc->c32);
+    const float l = lse[t];
+    const float M = part[(v0 / kBM) * ld_part + t].x;
+    const float scale = __builtin_amdgcn_exp2f((M - l) * kLog2e);
+    const u32x4 in = *reinterpret_cast<const u32x4*>(row);
+    float g[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w = in[e >> 1];
+      const float pv = bf16_to_f32(uint16_t((e & 1) ? (w >> 16) : (w & 0xFFFF)));
+      const int64_t v = v0 + e;
+      float x;
+      if (v == y) {
+        const float z = zt[t];
+        x = (__builtin_amdgcn_exp2f((z - l) * kLog2e) - 1.f) * coef;
+        if (SOFTCAP) {
+          const float th = z * inv_softcap;
+          x *= 1.f - th * th;
+        }
+      } else {
+        x = pv * scale * coef;
+        if (SOFTCAP && pv > 0.f) {
+          const float th = (M + __logf(pv)) * inv_softcap;
+          x *= 1.f - th * th;
+        }
+      }
+      g[e] = v < V ? x : 0.f;
+    }
+    *reinterpret_cast<u32x4*>(row) = u32x4{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]),
+                                           pack_bf16x2(g[4], g[5]), pack_bf16x2(g[6], g[7])};
+  }
+}
 
 // ---- row-major epilogues staged through LDS ---------------------------------
 // A wave's 128 x 128 float32 block goes out in 4 passes of 32 rows: the lane
@@ -847,6 +1011,55 @@ hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, cons
                                                 kGemmDH, L);
   return run_gemm<gemm::kFormN, gemm::kFormT>(lh, a, EpiDH<false, false>{dH, a.dh_acc, p.N, p.H},
                                               kGemmDH, L);
+}
+
+}  // namespace flce
+
+namespace flce {
+
+hipError_t bf16_nr_forward_chunk(const Plan& p, const Args& a, int64_t c, const Launcher& L) {
+  const int64_t t0 = c * p.nc, nt = gemm::nr_chunk_tokens(p, c);
+  const gemm::Launch l = gemm::nr_launch(p, c, 0);
+  uint16_t* probs = static_cast<uint16_t*>(a.g);
+  if (a.softcap > 0.f) {
+    EpiLseP<true> e{a.labels + t0, nt, p.V, a.ignore_index, a.softcap, 1.f / a.softcap, a.part,
+                    p.ld_part, a.zt, probs, p.vp};
+    return run_gemm<gemm::kFormN, gemm::kFormN>(l, a, e, kLseFwd, L);
+  }
+  EpiLseP<false> e{a.labels + t0, nt, p.V, a.ignore_index, 0.f, 0.f, a.part, p.ld_part, a.zt,
+                   probs, p.vp};
+  return run_gemm<gemm::kFormN, gemm::kFormN>(l, a, e, kLseFwd, L);
+}
+
+hipError_t bf16_nr_backward_chunk(const Plan& p, const Args& a, int64_t c, const Launcher& L) {
+  const int64_t t0 = c * p.nc, nt = gemm::nr_chunk_tokens(p, c);
+  uint16_t* g = static_cast<uint16_t*>(a.g);
+  // 1) G in place of the probabilities
+  const int64_t runs = (p.V + 7) / 8;
+  const dim3 grid(unsigned((runs + 255) / 256), unsigned(nt < 65535 ? nt : 65535));
+  L.pre(kProbsToGrad);
+  if (a.softcap > 0.f)
+    hipLaunchKernelGGL(k_probs_to_grad<true>, grid, dim3(256), 0, L.stream, g, p.vp, nt, p.V,
+                       a.part, p.ld_part, a.lse, a.zt, a.labels + t0, a.ignore_index, a.sc,
+                       1.f / a.softcap);
+  else
+    hipLaunchKernelGGL(k_probs_to_grad<false>, grid, dim3(256), 0, L.stream, g, p.vp, nt, p.V,
+                       a.part, p.ld_part, a.lse, a.zt, a.labels + t0, a.ignore_index, a.sc, 0.f);
+  L.post(kProbsToGrad);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // 2) dW (+)= G^T . h[chunk], added up over the token chunks
+  uint16_t* dW = static_cast<uint16_t*>(a.dW);
+  const gemm::Launch lw = gemm::nr_launch(p, c, 1);
+  if (c > 0 || a.accumulate_dW)
+    err = run_gemm<gemm::kFormT, gemm::kFormT>(lw, a, EpiDW<true>{dW, p.H, 0, p.V}, kGemmDW, L);
+  else
+    err = run_gemm<gemm::kFormT, gemm::kFormT>(lw, a, EpiDW<false>{dW, p.H, 0, p.V}, kGemmDW, L);
+  if (err != hipSuccess) return err;
+  // 3) dH[chunk] = G . W over the whole vocabulary
+  uint16_t* dH = static_cast<uint16_t*>(a.dH) + t0 * p.H;
+  return run_gemm<gemm::kFormN, gemm::kFormT>(gemm::nr_launch(p, c, 2), a,
+                                              EpiDH<true, true>{dH, nullptr, nt, p.H}, kGemmDH, L);
 }
 
 }  // namespace flce

@@ -159,14 +159,23 @@ hipError_t launch_label_scan(const Plan& p, const Args& a, const Launcher& L) {
   return hipGetLastError();
 }
 
-hipError_t launch_merge_and_loss(const Plan& p, const Args& a, const Launcher& L) {
+hipError_t launch_merge(const Plan& p, const Args& a, int64_t t0, int64_t nt, const Launcher& L) {
   L.pre(kLseMerge);
-  hipLaunchKernelGGL(k_lse_merge, dim3(unsigned(p.n_loss_blocks)), dim3(256), 0, L.stream,
-                     a.part, p.n_voc_tiles, p.ld_part, a.zt, a.labels, p.N, p.V,
-                     a.ignore_index, a.lse, a.lse_out, a.lsum);
+  hipLaunchKernelGGL(k_lse_merge, dim3(unsigned((nt + kMergeTokens - 1) / kMergeTokens)), dim3(256),
+                     0, L.stream, a.part, p.n_voc_tiles, p.ld_part, a.zt, a.labels + t0, nt, p.V,
+                     a.ignore_index, a.lse, a.lse_out ? a.lse_out + t0 : nullptr,
+                     a.lsum + t0 / kMergeTokens);
   L.post(kLseMerge);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_and_loss(const Plan& p, const Args& a, const Launcher& L) {
+  hipError_t e = launch_merge(p, a, 0, p.N, L);
   if (e != hipSuccess) return e;
+  return launch_loss_final(p, a, L);
+}
+
+hipError_t launch_loss_final(const Plan& p, const Args& a, const Launcher& L) {
   L.pre(kLossFinal);
   hipLaunchKernelGGL(k_loss_final, dim3(1), dim3(256), 0, L.stream, a.lsum, p.n_loss_blocks,
                      a.sc, a.loss);

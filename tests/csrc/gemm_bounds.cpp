@@ -22,7 +22,8 @@ static void fail(const char* what, int64_t a, int64_t b, int64_t c) {
 }
 
 static int64_t alloc_of(const Plan& p, int buf) {
-  return buf == kBufW ? p.V * p.H : buf == kBufH ? p.N * p.H : p.g_parts * p.vchunk * p.ldg;
+  if (buf == kBufG) return p.nr ? p.nc * p.vp : p.g_parts * p.vchunk * p.ldg;
+  return buf == kBufW ? p.V * p.H : p.N * p.H;
 }
 
 static void check_operand(const Plan& p, const Launch& l, int which, int64_t row0) {
@@ -143,6 +144,12 @@ int main(int argc, char** argv) {
         for (int part = 0; part < p.g_parts; ++part)
           for (int w = 1; w < 3; ++w) check_launch(p, backward_launch(p, c, w, part));
       }
+    }
+    for (int64_t tc : {int64_t(0), int64_t(256), int64_t(1000)}) {   // no-recompute variant
+      Plan q;
+      if (!make_plan_nr(s.N, s.H, s.V, 1, tc, &q)) { fail("plan nr", s.N, s.H, tc); continue; }
+      for (int64_t c = 0; c < q.n_tok_chunks; ++c)
+        for (int w = 0; w < 3; ++w) check_launch(q, nr_launch(q, c, w));
     }
     Plan p;
     make_plan(s.N, s.H, s.V, 1, &p);

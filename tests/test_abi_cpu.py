@@ -281,3 +281,38 @@ def test_f32grad_workspace_check(lib):
     assert lib.flce_check_args_ex(*_args(wsb=need), 0) == 0
     assert lib.flce_check_args_ex(*_args(wsb=need - 1), 0) == 3
     assert lib.flce_forward_backward_ex(*_args(wsb=1), 0) == 3      # rejected before launch
+
+
+# ------------------------------------------------------ no-recompute variant
+def test_nr_plan(lib):
+    # default chunk: min(N, 4096) rounded up to the tile
+    assert lib.flce_token_chunk_nr(8192, 4096, 131072, 1, 0) == 4096
+    assert lib.flce_token_chunk_nr(600, 64, 1000, 1, 0) == 768
+    assert lib.flce_token_chunk_nr(8192, 4096, 131072, 1, 1000) == 1024
+    assert lib.flce_token_chunk_nr(8192, 4096, 131072, 1, 100000) == 8192
+    # the chunk's probabilities dominate the workspace: nc x roundup(V, 256) x 2 bytes
+    for N, H, V, tc in [(8192, 4096, 131072, 0), (8192, 3584, 256000, 2048), (600, 64, 1000, 256)]:
+        nc = lib.flce_token_chunk_nr(N, H, V, 1, tc)
+        ws = lib.flce_workspace_size_nr(N, H, V, 1, tc)
+        vp = -(-V // 256) * 256
+        assert nc * vp * 2 <= ws <= nc * vp * 2 + (vp // 256) * nc * 8 + 4 * nc * 4 + N + 4096
+    assert lib.flce_workspace_size_nr(64, 64, 128, 0, 0) == 0        # float32: not offered
+    assert lib.flce_workspace_size_nr(-1, 64, 128, 1, 0) == 0
+
+
+@pytest.mark.parametrize("kw,tc,code", [
+    (dict(), 0, 0), (dict(), 256, 0),
+    (dict(dtype=0), 0, 2),            # float32 inputs
+    (dict(), -5, 2),
+    (dict(red=1, T=7), 0, 1), (dict(dH=None), 0, 1), (dict(H=12), 0, 2),
+    (dict(wsb=16), 0, 3), (dict(ws=A16 * 1024 + 64), 0, 3),
+])
+def test_check_args_nr(lib, kw, tc, code):
+    assert lib.flce_check_args_nr(*_args(**kw), tc) == code
+
+
+def test_nr_workspace_and_rejection(lib):
+    need = lib.flce_workspace_size_nr(64, 64, 128, 1, 0)
+    assert lib.flce_check_args_nr(*_args(wsb=need), 0) == 0
+    assert lib.flce_check_args_nr(*_args(wsb=need - 1), 0) == 3
+    assert lib.flce_forward_backward_nr(*_args(wsb=1), 0) == 3       # before any launch

@@ -120,6 +120,14 @@ def test_large_vocab_float32_gradients():
     _check(3, g, label="large_vocab f32 grads", tol=1e-4)
 
 
+def test_large_vocab_no_recompute():
+    """The no-recompute variant at full size (2 token chunks of 4096)."""
+    w = _case(3)[0]
+    g = gu.run_gpu(w, recompute=False)
+    assert g["num_tokens"] == 0
+    _check(3, g, label="large_vocab no recompute")
+
+
 def test_softcapped_full():
     w = _case(4)[0]
     g = gu.run_gpu(w)
