@@ -83,8 +83,8 @@ size_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype);
  *                        (h, W, labels, dH when N > 0; loss, num_tokens, dW
  *                        always); unknown dtype/reduction; softcap < 0 or not
  *                        finite; mb_scale not finite; num_label_tokens > 0
- *                        with 'mean'; dH overlapping h or dW, or dW
- *                        overlapping W.
+ *                        with 'mean'; an output (dH, dW) overlapping an input
+ *                        matrix (h, W) or the other output.
  *   FLCE_ERR_UNSUPPORTED bf16 with H % 8 != 0 or a matrix pointer not 16-byte
  *                        aligned.
  *   FLCE_ERR_WORKSPACE   workspace NULL, not 256-byte aligned, or

@@ -211,7 +211,7 @@ int flce_check_args_nr(const void* h, const void* W, const int64_t* labels, int6
   if (st != FLCE_OK) return st;
   if (dtype != FLCE_BF16 || token_chunk < 0) return FLCE_ERR_UNSUPPORTED;
   const size_t need = flce_workspace_size_nr(N, H, V, dtype, token_chunk);
-  if (need == 0) return FLCE_ERR_ARG;
+  if (need == 0) return FLCE_ERR_UNSUPPORTED;   // shapes beyond the kernels' index range
   if (workspace_bytes < need) return FLCE_ERR_WORKSPACE;
   return FLCE_OK;
 }

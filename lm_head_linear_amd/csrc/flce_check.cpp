@@ -93,6 +93,7 @@ bool make_plan_nr(int64_t N, int64_t H, int64_t V, int dtype, int64_t token_chun
   q.nc = nc;
   q.n_tok_chunks = ceil_div(N, nc);
   q.vp = round_up(V, q.tile);
+  if (q.vp > kMaxLdBF16) return false;        // G row length: 32-bit tile offsets
   // per chunk: partials and per-token arrays for nc tokens; block sums for all N
   q.ld_part = nc;
   q.vchunk = q.vp;          // G row length
@@ -181,9 +182,12 @@ int check_common(const void* h, const void* W, const int64_t* labels, int64_t N,
     if (overlaps(dH, size_t(N) * H * gs, h, size_t(N) * H * es)) return FLCE_ERR_ARG;
     if (overlaps(dW, size_t(V) * H * gs, W, size_t(V) * H * es)) return FLCE_ERR_ARG;
     if (overlaps(dH, size_t(N) * H * gs, dW, size_t(V) * H * gs)) return FLCE_ERR_ARG;
+    if (overlaps(dH, size_t(N) * H * gs, W, size_t(V) * H * es)) return FLCE_ERR_ARG;
+    if (overlaps(dW, size_t(V) * H * gs, h, size_t(N) * H * es)) return FLCE_ERR_ARG;
   }
   const uintptr_t mask = dtype == FLCE_BF16 ? 15u : 3u;
   if (dtype == FLCE_BF16 && H % 8 != 0) return FLCE_ERR_UNSUPPORTED;
+  if (dtype == FLCE_BF16 && !flce::bf16_shape_ok(N, H, V)) return FLCE_ERR_UNSUPPORTED;
   if (misaligned(W, mask) || (N > 0 && misaligned(h, mask))) return FLCE_ERR_UNSUPPORTED;
   // the bf16 kernels write gradients in 16-byte (float32: 4 x 4-byte) runs
   const uintptr_t gmask = dtype == FLCE_BF16 ? 15u : 3u;

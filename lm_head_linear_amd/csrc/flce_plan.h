@@ -14,6 +14,19 @@ constexpr int64_t kTileBF16 = 256;
 constexpr int64_t kTileF32 = 64;
 // Upper bound on the elements of one chunk of the logit gradient G^T.
 constexpr int64_t kChunkElems = int64_t(1) << 27;
+// The bf16 GEMMs address an operand tile with 32-bit byte offsets from the
+// tile base: up to 255 rows of a K-contiguous operand, 2 * ld bytes apart.
+// ld (H, or the no-recompute G row length) must keep that below 2^32.
+constexpr int64_t kMaxLdBF16 = int64_t(1) << 22;
+// Workgroups of one GEMM launch (256 x 256 tiles) must fit a grid dimension.
+constexpr int64_t kMaxTiles = (int64_t(1) << 31) - 1;
+
+// Whether the bf16 shapes fit the kernels' index arithmetic.
+inline bool bf16_shape_ok(int64_t N, int64_t H, int64_t V) {
+  if (H > kMaxLdBF16) return false;
+  const int64_t tn = (N + 255) / 256, tv = (V + 255) / 256, th = (H + 255) / 256;
+  return tn * tv <= kMaxTiles && tn * th <= kMaxTiles && tv * th <= kMaxTiles;
+}
 
 // Scalars shared by the kernels of one call (first 256 bytes of the workspace).
 struct Scalars {

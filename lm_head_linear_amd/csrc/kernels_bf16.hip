@@ -893,9 +893,21 @@ const uint16_t* buf_ptr(const Args& a, int buf) {
 }
 
 // A T-form operand is read in 16-byte column chunks: it needs rows % 8 == 0.
+// The per-lane load offsets are 32-bit byte offsets from the tile base: at
+// most min(255, rows - 1) rows of ld elements plus 64 k for a K-contiguous
+// operand, 63 k-rows of ld elements plus the row length for a T-form one.
+// The tile count must fit the grid.
+bool operand_offsets_fit(int form, const gemm::Geom& g) {
+  const int64_t reach = form == gemm::kFormN ? (g.rows - 1 < 255 ? g.rows - 1 : 255) * g.ld + 64
+                                             : 63 * g.ld + g.rows;
+  return reach >= 0 && 2 * reach + 16 <= int64_t(0xFFFFFFFF);
+}
+
 bool launch_ok(const gemm::Launch& l) {
   if (l.fa == gemm::kFormT && (l.a.rows % 8 != 0 || l.a.rows < 8)) return false;
   if (l.fb == gemm::kFormT && (l.b.rows % 8 != 0 || l.b.rows < 8)) return false;
+  if (!operand_offsets_fit(l.fa, l.a) || !operand_offsets_fit(l.fb, l.b)) return false;
+  if (gemm::num_tiles(l.M, l.Nn) > kMaxTiles) return false;
   return l.M > 0 && l.Nn > 0 && l.K > 0;
 }
 

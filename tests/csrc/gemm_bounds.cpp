@@ -94,7 +94,15 @@ static void check_lds_layout() {
     }
 }
 
+// Same predicate as the library's launch check: the 32-bit lane offsets fit.
+static bool offsets_fit(int form, const Geom& g) {
+  const int64_t reach = form == kFormN ? (g.rows - 1 < 255 ? g.rows - 1 : 255) * g.ld + 64
+                                       : 63 * g.ld + g.rows;
+  return reach >= 0 && 2 * reach + 16 <= int64_t(0xFFFFFFFF);
+}
+
 static void check_launch(const Plan& p, const Launch& l) {
+  if (!offsets_fit(l.fa, l.a) || !offsets_fit(l.fb, l.b)) fail("offsets exceed 32 bits", l.M, l.Nn, l.K);
   const int64_t nt = num_tiles(l.M, l.Nn);
   const int64_t num_m = (l.M + kBM - 1) / kBM;
   std::vector<char> seen(size_t(nt), 0);

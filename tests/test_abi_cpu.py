@@ -129,6 +129,8 @@ def test_check_args_ok(lib):
     (dict(nt=None), 1), (dict(dH=None), 1), (dict(dW=None), 1),
     (dict(dH=A16), 1),                 # dH aliases h
     (dict(dW=A16 * 64 + 256), 1),      # dW overlaps W
+    (dict(dH=A16 * 64), 1),            # dH overlaps W
+    (dict(dW=A16), 1),                 # dW overlaps h
     (dict(H=12), 2),                   # bf16 needs H % 8 == 0
     (dict(h=A16 + 8), 2),              # misaligned bf16 matrix
     (dict(ws=None), 3), (dict(ws=A16 * 1024 + 128), 3), (dict(wsb=16), 3),
@@ -316,3 +318,18 @@ def test_nr_workspace_and_rejection(lib):
     assert lib.flce_check_args_nr(*_args(wsb=need), 0) == 0
     assert lib.flce_check_args_nr(*_args(wsb=need - 1), 0) == 3
     assert lib.flce_forward_backward_nr(*_args(wsb=1), 0) == 3       # before any launch
+
+
+def test_shapes_beyond_the_index_range_are_refused(lib):
+    """The bf16 kernels address tiles with 32-bit offsets: a hidden size (row
+    length of h and W) above 2^22 elements, or a no-recompute probability row
+    above 2^22, is refused as unsupported instead of wrapping."""
+    big = dict(N=1, V=1)            # keep the fake buffers far apart
+    assert lib.flce_check_args(*_args(H=(1 << 22) + 8, **big)) == 2
+    assert lib.flce_check_args(*_args(H=1 << 22, **big)) == 0
+    assert lib.flce_check_args(*_args(dtype=0, H=(1 << 22) + 8, **big)) == 0   # float32 path
+    assert lib.flce_workspace_size_nr(64, 64, (1 << 22) + 1, 1, 0) == 0
+    assert lib.flce_check_args_nr(*_args(V=(1 << 22) + 1, H=8), 0) == 2
+    assert lib.flce_check_args_nr(*_args(V=1 << 22, H=8), 0) == 0
+    # small batches with a huge vocabulary stay supported (G chunk rows are short)
+    assert lib.flce_check_args(*_args(N=8, V=1 << 23, H=8)) == 0
