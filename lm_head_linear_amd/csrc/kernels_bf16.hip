@@ -218,19 +218,19 @@ __device__ __forceinline__ void read_step(StepFrags& f, const char* sa, const ch
 // returned when the next step needs them) and NLOADS direct global loads
 // placed between them, so everything issues under the MFMAs instead of
 // stalling the wave's in-order stream. The placement of the loads was chosen
-// by timing: K-contiguous operands prefer them early, steps with transpose
-// reads in the second half.
+// by timing: with both operands K-contiguous (16 loads on every other step)
+// one after every second MFMA across the whole step; steps with transpose
+// reads (8 loads per step) in the second half.
 template <int FA, int FB, int NLOADS>
 __device__ __forceinline__ void interleave_hints() {
+  constexpr bool kNN = FA == 0 && FB == 0;
   constexpr int kReads = 2 * ((FA == 0 ? 4 : 8) + (FB == 0 ? 4 : 8));
   constexpr int kPer = (kReads + 15) / 16;
-  constexpr int kLoad0 = (FA == 0 && FB == 0) ? 0 : 16;
-  constexpr int kLoadPer = NLOADS > 16 ? (NLOADS + 15) / 16 : 1;
 #pragma unroll
   for (int q = 0; q < 32; ++q) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
-    if (NLOADS > 0 && q >= kLoad0 && q < kLoad0 + NLOADS / kLoadPer)
-      __builtin_amdgcn_sched_group_barrier(0x020, kLoadPer, 0);          // VMEM read
+    const bool load = kNN ? (q % 2 == 1 && q / 2 < NLOADS) : (q >= 16 && q < 16 + NLOADS);
+    if (NLOADS > 0 && load) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
     if (q < kReads / kPer) __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);  // DS read
   }
 }
