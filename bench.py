@@ -118,6 +118,97 @@ def copy_calibration(size_mib: int, reps: int):
     log(f"copy calibration: {reps} copies of {size_mib} MiB")
 
 
+def other_modes(m, w, h, W, y, dH, dW, loss, nt, steps, timing, nhv):
+    """The forward-only entry, float32 gradients and the no-recompute variant
+    on the same inputs, each timed like the main step, after it (so they
+    cannot disturb it)."""
+    import torch
+    N, H = h.shape
+    V = W.shape[0]
+    dev = h.device
+    # The forward-only entry (loss and lse, no gradients) on the same inputs,
+    # timed the same way, after the step timing so it cannot disturb it.
+    fws = torch.empty(m.flce_forward_workspace_size(N, H, V, W.dtype), dtype=torch.uint8,
+                      device=dev)
+
+    def fwd():
+        m.flce_forward(h, W, y, ignore_index=w.ignore_index, softcap=w.softcap,
+                       reduction=w.reduction, workspace=fws, loss=loss, num_tokens=nt)
+
+    for _ in range(2):
+        fwd()
+    torch.cuda.synchronize()
+    tf0 = time.perf_counter()
+    for _ in range(steps):
+        fwd()
+    torch.cuda.synchronize()
+    f_ms = (time.perf_counter() - tf0) * 1e3 / steps
+    forward_only = {"ms_per_call": round(f_ms, 4), "tokens_per_s": round(N / (f_ms * 1e-3), 1),
+                    "tflops_2nhv": round(2 * nhv / (f_ms * 1e-3) / 1e12, 1),
+                    "workspace_bytes": int(fws.numel())}
+    log(f"forward only: {f_ms:.3f} ms/call, {forward_only['tflops_2nhv']:.1f} TFLOP/s")
+
+    # Float32 gradients for the same bf16 inputs (G as a bf16 hi + lo pair,
+    # twice the dW/dH work), timed the same way.
+    gws = torch.empty(m.flce_workspace_size(N, H, V, W.dtype, torch.float32), dtype=torch.uint8,
+                      device=dev)
+    dH32 = torch.empty(N, H, dtype=torch.float32, device=dev)
+    dW32 = torch.empty(V, H, dtype=torch.float32, device=dev)
+
+    def step32():
+        m.flce_forward_backward(h, W, y, ignore_index=w.ignore_index, softcap=w.softcap,
+                                reduction=w.reduction, dH=dH32, dW=dW32, workspace=gws,
+                                loss=loss, num_tokens=nt, grad_dtype=torch.float32)
+
+    n32 = max(1, steps // 2)
+    for _ in range(2):
+        step32()
+    torch.cuda.synchronize()
+    tg0 = time.perf_counter()
+    for _ in range(n32):
+        step32()
+    torch.cuda.synchronize()
+    g_ms = (time.perf_counter() - tg0) * 1e3 / n32
+    float32_grads = {"ms_per_step": round(g_ms, 4), "tokens_per_s": round(N / (g_ms * 1e-3), 1),
+                     "steps": n32, "workspace_bytes": int(gws.numel())}
+    log(f"float32 gradients: {g_ms:.3f} ms/step")
+    del dH32, dW32, gws
+
+    # The no-recompute variant on the same inputs (token chunks whose
+    # probabilities are kept instead of recomputing the logits), timed the
+    # same way, with its per-kernel split.
+    nws = torch.empty(m.flce_workspace_size_nr(N, H, V, W.dtype), dtype=torch.uint8, device=dev)
+
+    def step_nr():
+        m.flce_forward_backward(h, W, y, ignore_index=w.ignore_index, softcap=w.softcap,
+                                reduction=w.reduction, dH=dH, dW=dW, workspace=nws, loss=loss,
+                                num_tokens=nt, recompute=False)
+
+    for _ in range(2):
+        step_nr()
+    torch.cuda.synchronize()
+    tn0 = time.perf_counter()
+    for _ in range(steps):
+        step_nr()
+    torch.cuda.synchronize()
+    n_ms = (time.perf_counter() - tn0) * 1e3 / steps
+    nr_kernels = {}
+    if timing:
+        m.flce_profile_begin()
+        for _ in range(3):
+            step_nr()
+        torch.cuda.synchronize()
+        m.flce_profile_end()
+        nr_kernels = {k: round(ms / 3, 4) for k, (ms, n) in m.flce_profile_query().items() if n}
+    no_recompute = {"ms_per_step": round(n_ms, 4), "tokens_per_s": round(N / (n_ms * 1e-3), 1),
+                    "tflops_6nhv": round(6 * nhv / (n_ms * 1e-3) / 1e12, 1),
+                    "token_chunk": m.flce_token_chunk_nr(N, H, V, W.dtype),
+                    "workspace_bytes": int(nws.numel()), "kernels_ms_per_step": nr_kernels}
+    log(f"no recompute: {n_ms:.3f} ms/step {nr_kernels}")
+    del nws
+    return forward_only, float32_grads, no_recompute
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +218,9 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="do not bracket kernels with events in the timed region")
+    ap.add_argument("--main-only", action="store_true",
+                    help="time only the main path (no forward-only, float32-gradient or "
+                         "no-recompute figures), e.g. for per-kernel counter runs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -227,86 +321,10 @@ def main():
         log(f"  {k:18s} {v['ms_per_step']:8.3f} ms/step  {v['launches_per_step']:.0f} launches"
             + (f"  {v['tflops']:7.1f} TFLOP/s" if "tflops" in v else ""))
 
-    # The forward-only entry (loss and lse, no gradients) on the same inputs,
-    # timed the same way, after the step timing so it cannot disturb it.
-    fws = torch.empty(m.flce_forward_workspace_size(N, H, V, W.dtype), dtype=torch.uint8,
-                      device=dev)
-
-    def fwd():
-        m.flce_forward(h, W, y, ignore_index=w.ignore_index, softcap=w.softcap,
-                       reduction=w.reduction, workspace=fws, loss=loss, num_tokens=nt)
-
-    for _ in range(2):
-        fwd()
-    torch.cuda.synchronize()
-    tf0 = time.perf_counter()
-    for _ in range(args.steps):
-        fwd()
-    torch.cuda.synchronize()
-    f_ms = (time.perf_counter() - tf0) * 1e3 / args.steps
-    forward_only = {"ms_per_call": round(f_ms, 4), "tokens_per_s": round(N / (f_ms * 1e-3), 1),
-                    "tflops_2nhv": round(2 * nhv / (f_ms * 1e-3) / 1e12, 1),
-                    "workspace_bytes": int(fws.numel())}
-    log(f"forward only: {f_ms:.3f} ms/call, {forward_only['tflops_2nhv']:.1f} TFLOP/s")
-
-    # Float32 gradients for the same bf16 inputs (G as a bf16 hi + lo pair,
-    # twice the dW/dH work), timed the same way.
-    gws = torch.empty(m.flce_workspace_size(N, H, V, W.dtype, torch.float32), dtype=torch.uint8,
-                      device=dev)
-    dH32 = torch.empty(N, H, dtype=torch.float32, device=dev)
-    dW32 = torch.empty(V, H, dtype=torch.float32, device=dev)
-
-    def step32():
-        m.flce_forward_backward(h, W, y, ignore_index=w.ignore_index, softcap=w.softcap,
-                                reduction=w.reduction, dH=dH32, dW=dW32, workspace=gws,
-                                loss=loss, num_tokens=nt, grad_dtype=torch.float32)
-
-    n32 = max(1, args.steps // 2)
-    for _ in range(2):
-        step32()
-    torch.cuda.synchronize()
-    tg0 = time.perf_counter()
-    for _ in range(n32):
-        step32()
-    torch.cuda.synchronize()
-    g_ms = (time.perf_counter() - tg0) * 1e3 / n32
-    float32_grads = {"ms_per_step": round(g_ms, 4), "tokens_per_s": round(N / (g_ms * 1e-3), 1),
-                     "steps": n32, "workspace_bytes": int(gws.numel())}
-    log(f"float32 gradients: {g_ms:.3f} ms/step")
-    del dH32, dW32, gws
-
-    # The no-recompute variant on the same inputs (token chunks whose
-    # probabilities are kept instead of recomputing the logits), timed the
-    # same way, with its per-kernel split.
-    nws = torch.empty(m.flce_workspace_size_nr(N, H, V, W.dtype), dtype=torch.uint8, device=dev)
-
-    def step_nr():
-        m.flce_forward_backward(h, W, y, ignore_index=w.ignore_index, softcap=w.softcap,
-                                reduction=w.reduction, dH=dH, dW=dW, workspace=nws, loss=loss,
-                                num_tokens=nt, recompute=False)
-
-    for _ in range(2):
-        step_nr()
-    torch.cuda.synchronize()
-    tn0 = time.perf_counter()
-    for _ in range(args.steps):
-        step_nr()
-    torch.cuda.synchronize()
-    n_ms = (time.perf_counter() - tn0) * 1e3 / args.steps
-    nr_kernels = {}
-    if timing:
-        m.flce_profile_begin()
-        for _ in range(3):
-            step_nr()
-        torch.cuda.synchronize()
-        m.flce_profile_end()
-        nr_kernels = {k: round(ms / 3, 4) for k, (ms, n) in m.flce_profile_query().items() if n}
-    no_recompute = {"ms_per_step": round(n_ms, 4), "tokens_per_s": round(N / (n_ms * 1e-3), 1),
-                    "tflops_6nhv": round(6 * nhv / (n_ms * 1e-3) / 1e12, 1),
-                    "token_chunk": m.flce_token_chunk_nr(N, H, V, W.dtype),
-                    "workspace_bytes": int(nws.numel()), "kernels_ms_per_step": nr_kernels}
-    log(f"no recompute: {n_ms:.3f} ms/step {nr_kernels}")
-    del nws
+    forward_only = float32_grads = no_recompute = None
+    if not args.main_only:
+        forward_only, float32_grads, no_recompute = other_modes(
+            m, w, h, W, y, dH, dW, loss, nt, args.steps, timing, nhv)
 
     cpu = None
     if not args.no_cpu_baseline:
