@@ -491,13 +491,27 @@ struct EpiLse {
 // its 4 consecutive vocab values into 8 bytes; 8-byte slots XOR-swizzled by
 // token), then writes whole 16-byte runs of token rows; columns t >= nt and
 // rows v >= nv are not written. LO stores the residual v - bf16(v) instead
-// of v (the low half of a bf16 pair). The caller separates a second use of
-// the staging area with a barrier.
-template <bool LO>
+// of v (the low half of a bf16 pair). Optionally one element per token
+// column j of the lane is replaced after staging: tpos[j] >= 0 is its byte
+// offset in the wave's staging area (target_slot) and tval[j] its value. The
+// caller separates a second use of the staging area with a barrier.
+struct TargetPatch {
+  int pos[4];
+  float val[4];
+};
+
+// Byte offset, in a wave's staging area, of row d (0..127, the wave's own
+// rows) of token column tl, for the lane half that holds that row.
+__device__ __forceinline__ int target_slot(int d, int tl) {
+  const int i = d >> 5, w = d & 31, rq = w >> 3, half = (w >> 2) & 1, e = w & 3;
+  return tl * 256 + (((i * 8 + 2 * rq + half) ^ (tl & 31)) * 8) + 2 * e;
+}
+
+template <bool LO, bool PATCH = false>
 __device__ __forceinline__ void store_token_major(const f32x16 (&acc)[4][4], char* smem, int wm,
                                                   int wn, int lane, uint16_t* dst, int64_t ld,
                                                   int64_t m0, int64_t n0, int64_t nt,
-                                                  int64_t nv) {
+                                                  int64_t nv, const TargetPatch* patch = nullptr) {
   const int half = lane >> 5;
   char* reg = smem + (wm + 2 * wn) * kWaveScratch;
 #pragma unroll
@@ -517,6 +531,15 @@ __device__ __forceinline__ void store_token_major(const f32x16 (&acc)[4][4], cha
         const uint32_t hi = pack_bf16x2(v[2], v[3]);
         const int slot = (i * 8 + 2 * rq + half) ^ (tl & 31);
         *reinterpret_cast<uint2*>(reg + tl * 256 + slot * 8) = make_uint2(lo, hi);
+      }
+  }
+  if (PATCH) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (patch->pos[j] >= 0) {
+        float v = patch->val[j];
+        if (LO) v -= bf16_to_f32(f32_to_bf16(v));
+        *reinterpret_cast<uint16_t*>(reg + patch->pos[j]) = f32_to_bf16(v);
       }
   }
   __syncthreads();
@@ -543,56 +566,76 @@ template <bool SOFTCAP, bool SPLIT>
 struct EpiGrad {
   const int64_t* labels;
   const float* lse;
+  const float* zt;   // the forward's float32 target logits
   const Scalars* sc;
   int64_t N, V, ignore_index, v0, vcur, ldgv;
   float softcap, inv_softcap;
   uint16_t* g;
   int64_t lo_off;   // elements from the hi to the lo chunk (SPLIT)
 
+  // Every element is first formed as if it were not the target:
+  // c exp(z' - lse) dz'/dz = exp2(z' log2 e + log2 c - lse log2 e) dz'/dz, the
+  // scale folded into the exponent (c = 0 for ignored tokens gives exact
+  // zeros, a NaN scale for a bad label NaN). The one target element of a
+  // token in this block is then replaced in the staged tile by
+  // c (exp(z'_y - lse) - 1) dz'/dz from the forward's target logit, which is
+  // the same float32 value the GEMM recomputes.
   __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm,
                                              int wn, int lane, char* smem) const {
     const float c = sc->c32;
     const int half = lane >> 5;
     const int64_t vbase = v0 + m0 + wm * 128;           // global vocab id of block row 0
+    TargetPatch tp;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int tl = j * 32 + (lane & 31);             // token within the wave block
       const int64_t t = n0 + wn * 128 + tl;
       // Every token's lse is known (ignored ones too) and columns past N hold
-      // the logits of token N-1, so exp(z' - lse) <= 1 everywhere and a zero
-      // coefficient gives an exact zero.
+      // the logits of token N-1, so exp(z' - lse) <= 1 everywhere.
       const int64_t tc = t < N ? t : N - 1;
       const float l = lse[tc];
       float coef = 0.f;
-      int yd = -1;                                     // target row - 4 * half, or -1
+      tp.pos[j] = -1;
+      tp.val[j] = 0.f;
       if (t < N) {
         const int64_t y = labels[t];
         if (y != ignore_index) {
           coef = (y < 0 || y >= V) ? NAN : c;
-          if (y >= vbase && y < vbase + 128) yd = int(y - vbase) - 4 * half;
+          if (y >= vbase && y < vbase + 128) {
+            const int d = int(y - vbase);
+            if (((d >> 2) & 1) == half) {
+              const float z = zt[t];
+              float dd = 1.f;
+              if (SOFTCAP) {
+                const float th = z * inv_softcap;
+                dd = 1.f - th * th;
+              }
+              tp.pos[j] = target_slot(d, tl);
+              tp.val[j] = (__builtin_amdgcn_exp2f((z - l) * kLog2e) - 1.f) * coef * dd;
+            }
+          }
         }
       }
+      const float bias = log2f(coef) - l * kLog2e;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float z = acc[i][j][r];
-          float d = 1.f;
           if (SOFTCAP) {
             const float th = tanh_fast(z * inv_softcap);
-            z = softcap * th;
-            d = 1.f - th * th;
+            acc[i][j][r] = __builtin_amdgcn_exp2f(fmaf(softcap * th, kLog2e, bias)) *
+                           (1.f - th * th);
+          } else {
+            acc[i][j][r] = __builtin_amdgcn_exp2f(fmaf(z, kLog2e, bias));
           }
-          const float p = __builtin_amdgcn_exp2f((z - l) * kLog2e);
-          // (p - [v == y]) * coef, the one-hot as a selected subtrahend
-          const float sub = (yd == i * 32 + 8 * (r >> 2) + (r & 3)) ? coef : 0.f;
-          acc[i][j][r] = SOFTCAP ? (p * coef - sub) * d : fmaf(p, coef, -sub);
         }
     }
-    store_token_major<false>(acc, smem, wm, wn, lane, g, ldgv, m0, n0, N, vcur);
+    store_token_major<false, true>(acc, smem, wm, wn, lane, g, ldgv, m0, n0, N, vcur, &tp);
     if (SPLIT) {
       __syncthreads();                                 // the staging area is reused
-      store_token_major<true>(acc, smem, wm, wn, lane, g + lo_off, ldgv, m0, n0, N, vcur);
+      store_token_major<true, true>(acc, smem, wm, wn, lane, g + lo_off, ldgv, m0, n0, N, vcur,
+                                    &tp);
     }
   }
 };
@@ -948,12 +991,12 @@ hipError_t bf16_backward_chunk_f32grad(const Plan& p, const Args& a, int64_t chu
   const int64_t lo_off = p.vchunk * p.ldg;
   hipError_t err;
   if (a.softcap > 0.f) {
-    EpiGrad<true, true> eg{a.labels, a.lse, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
+    EpiGrad<true, true> eg{a.labels, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
                            p.vchunk, a.softcap, 1.f / a.softcap, g, lo_off};
     err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
                                                kGradLogits, L);
   } else {
-    EpiGrad<false, true> eg{a.labels, a.lse, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
+    EpiGrad<false, true> eg{a.labels, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
                             p.vchunk, 0.f, 0.f, g, lo_off};
     err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
                                                kGradLogits, L);
@@ -989,12 +1032,12 @@ hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, cons
   // 1) recompute the logits of the chunk and form G[N][vchunk]
   hipError_t err;
   if (a.softcap > 0.f) {
-    EpiGrad<true, false> eg{a.labels, a.lse, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
+    EpiGrad<true, false> eg{a.labels, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
                             p.vchunk, a.softcap, 1.f / a.softcap, g, 0};
     err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
                                                kGradLogits, L);
   } else {
-    EpiGrad<false, false> eg{a.labels, a.lse, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
+    EpiGrad<false, false> eg{a.labels, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
                              p.vchunk, 0.f, 0.f, g, 0};
     err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
                                                kGradLogits, L);
