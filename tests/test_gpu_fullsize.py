@@ -135,6 +135,15 @@ def test_softcapped_full():
     _forward_only_matches(w, g)
 
 
+def test_softcapped_no_recompute():
+    """No-recompute variant with the softcap at full size (2 chunks of 4096
+    tokens, V = 256000: the softcap derivative rebuilt from the stored
+    probabilities)."""
+    w = _case(4)[0]
+    g = gu.run_gpu(w, recompute=False)
+    _check(4, g, label="softcapped no recompute")
+
+
 def test_long_full_and_external_count():
     w = _case(5)[0]
     g = gu.run_gpu(w)
@@ -142,6 +151,14 @@ def test_long_full_and_external_count():
     # the count is the one used: twice the count halves loss and gradients
     g2 = gu.run_gpu(w, num_label_tokens=2 * w.num_label_tokens)
     _check(5, g2, T=2 * w.num_label_tokens, label="long T=31744")
+
+
+def test_long_no_recompute():
+    """No-recompute variant on 16384 tokens: 4 token chunks, dW added up over
+    them, with the external count."""
+    w = _case(5)[0]
+    g = gu.run_gpu(w, recompute=False)
+    _check(5, g, label="long no recompute")
 
 
 def test_long_four_micro_batches():
