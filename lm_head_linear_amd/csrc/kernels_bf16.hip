@@ -5,11 +5,14 @@
 //   recompute Z^T tile, then the logit-gradient epilogue (K = H)
 //   dW chunk  = G^T[chunk] . h                          (K = tokens)
 //   dH       += G[:, chunk] . W[chunk]                  (K = vocab chunk)
-// Workgroup tile 256 x 256, K step 64, four waves of 128 x 128 each built from
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulate). Operands are staged through LDS
-// in a K-contiguous, XOR-swizzled layout, double buffered; an operand that is
-// stored with its M/N dimension contiguous is transposed 8x8 in registers on
-// its way into LDS, so the MFMA loop never changes.
+// Workgroup tile 256 x 256, four waves of 128 x 128 each built from
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulate), MFMA steps of 32 k. Operands go
+// global -> LDS with direct-to-LDS loads (no registers) into XOR-swizzled
+// stages: 2 stages of 64 k when both operands are K-contiguous, 4 of 32 k
+// otherwise. A K-contiguous operand's fragments are read with ds_read_b128;
+// one stored with its M/N dimension contiguous is read with the gfx950
+// transpose read ds_read_b64_tr_b16, so no operand is ever transposed in
+// registers or in memory.
 //
 // Tiles are computed with the vocabulary on the M side and tokens on the N
 // side for the logit tiles: a lane then owns one token column and 64 vocab
@@ -54,8 +57,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 using gemm::Geom;
 using gemm::kBK;
-using gemm::swz_n;
-using gemm::swz_t;
 
 // An operand of the GEMM: a pointer and its geometry (see gemm_index.h).
 struct Operand {
@@ -401,7 +402,7 @@ __device__ __forceinline__ float tanh_fast(float x) {
 }
 
 // ---- forward epilogue: per (vocab tile, token) max and sum-exp ------------
-// Tile rows are vocabulary ids (relative to v_off), columns are tokens.
+// Tile rows are vocabulary ids, columns are tokens.
 // SOFTCAP selects the s * tanh(z / s) variant at compile time.
 template <bool SOFTCAP>
 struct EpiLse {
@@ -492,9 +493,10 @@ struct EpiLse {
 // token), then writes whole 16-byte runs of token rows; columns t >= nt and
 // rows v >= nv are not written. LO stores the residual v - bf16(v) instead
 // of v (the low half of a bf16 pair). Optionally one element per token
-// column j of the lane is replaced after staging: tpos[j] >= 0 is its byte
-// offset in the wave's staging area (target_slot) and tval[j] its value. The
-// caller separates a second use of the staging area with a barrier.
+// column j of the lane is replaced after staging: patch->pos[j] >= 0 is its
+// byte offset in the wave's staging area (target_slot) and patch->val[j] its
+// value. The caller separates a second use of the staging area with a
+// barrier.
 struct TargetPatch {
   int pos[4];
   float val[4];
