@@ -1,0 +1,70 @@
+"""CPU check of the generated GEMM main loops (gfx950 assembly, compiled here).
+
+Results do not depend on the loop schedule, but speed does, and a small
+source change can silently break it: a second LDS object makes the compiler
+wait for every direct load before each fragment read; register pressure can
+move spills into the loop. For every GEMM kernel this compiles
+kernels_bf16.hip to assembly and checks the innermost 64-MFMA loop:
+no scratch traffic, the direct loads and fragment reads the design issues per
+two MFMA steps, the barriers, and that the only full vmcnt wait is the one
+before the barrier (never between a load and the reads of the same step)."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "lm_head_linear_amd", "csrc", "kernels_bf16.hip")
+
+pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None, reason="no hipcc")
+
+
+@pytest.fixture(scope="module")
+def loops(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("asm") / "k.s")
+    r = subprocess.run(["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang",
+                        "-target-feature", "-Xclang", "-packed-fp32-ops", "-S",
+                        "--cuda-device-only", SRC, "-o", out], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = open(out).read().split("\n")
+    res = {}
+    starts = [i for i, l in enumerate(lines) if re.match(r"^_ZN4flce12_GLOBAL__N_16k_gemm\S*:", l)]
+    for st in starts:
+        en = next(i for i in range(st, len(lines)) if lines[i].startswith(".Lfunc_end"))
+        body = lines[st:en]
+        name = re.match(r"^_ZN4flce12_GLOBAL__N_16k_gemmILi(\d)ELi(\d)ENS0_\d+(\w+?)I", body[0])
+        labels = {m.group(1): i for i, l in enumerate(body)
+                  if (m := re.match(r"^(\.LBB\d+_\d+):", l))}
+        best = None
+        for i, l in enumerate(body):
+            m = re.search(r"s_cbranch_\w+\s+(\.LBB\d+_\d+)", l)
+            if m and m.group(1) in labels and labels[m.group(1)] < i:
+                a = labels[m.group(1)]
+                if sum("v_mfma" in x for x in body[a:i]) >= 64 and (best is None or i - a < best[1] - best[0]):
+                    best = (a, i)
+        assert best, body[0]
+        seg = [l.strip() for l in body[best[0]:best[1]]
+               if l.startswith("\t") and not l.startswith("\t;") and not l.startswith("\t.")]
+        res[body[0].split(":")[0]] = (int(name.group(1)), int(name.group(2)), name.group(3), seg)
+    assert len(res) >= 8
+    return res
+
+
+def test_main_loops(loops):
+    for sym, (fa, fb, epi, seg) in loops.items():
+        count = lambda p: sum(1 for l in seg if re.match(p, l))
+        assert count(r"v_mfma") == 64, sym
+        assert count(r"scratch_|buffer_store|buffer_load") == 0, (sym, "spill in the K loop")
+        assert count(r"global_load_lds") == 16, sym          # one stage tile (two steps)
+        # fragment reads per two steps: 16 ds_read_b128 per N-form operand,
+        # 32 transpose reads per T-form operand
+        reads = (16 if fa == 0 else 32) + (16 if fb == 0 else 32)
+        assert count(r"ds_read") == reads, (sym, count(r"ds_read"))
+        nn = fa == 0 and fb == 0
+        assert count(r"s_barrier") == (1 if nn else 2), sym
+        # a full vmcnt wait only directly before a barrier
+        for i, l in enumerate(seg):
+            if re.match(r"s_waitcnt\s+vmcnt\(0\)", l):
+                assert any("s_barrier" in x for x in seg[i + 1:i + 3]), (sym, "vmcnt(0) inside a step")
