@@ -39,6 +39,9 @@
  *     it; outputs are valid once the stream reaches that point.
  *   - Return value: an flce_status_t. A non-OK value from the synchronous
  *     argument checks means nothing was launched and nothing was written.
+ *   - A call allocates nothing, never waits for the device and clears memory
+ *     with kernels (no memset nodes), so it can be captured into a HIP graph
+ *     and replayed, with the pointers it was captured with (profiling off).
  */
 #ifndef FLCE_H
 #define FLCE_H
