@@ -176,7 +176,7 @@ int flce_forward_backward_ex(const void* h, const void* W, const int64_t* labels
  * The no-recompute variant (bf16 only): the same call and results, with one
  * more argument, token_chunk. Instead of recomputing the logits in the
  * backward pass (2*N*H*V flop), it goes through the tokens in chunks of
- * token_chunk (rounded up to 256; <= 0: min(N, 4096) rounded up) and keeps
+ * token_chunk (rounded up to 256; <= 0: min(N, 8192) rounded up) and keeps
  * each chunk's probabilities relative to each vocabulary tile's max,
  * P'[t][v] = exp(z'_tv - M) <= 1, as bf16 in the workspace; after the chunk's
  * log-sum-exp they become G in place (G = c (P' exp(M - lse) - [v = y])
@@ -186,7 +186,9 @@ int flce_forward_backward_ex(const void* h, const void* W, const int64_t* labels
  * implementations do": memory is bounded by chunking the sequence) is the
  * model; the logits themselves are never rounded to bf16. Cost: 6*N*H*V
  * flop, plus token_chunk * roundup(V, 256) * 2 bytes of workspace
- * (flce_workspace_size_nr), 1 GiB at N >= 4096, V = 131072 with the default.
+ * (flce_workspace_size_nr), 2 GiB at N >= 8192, V = 131072 with the default;
+ * a smaller token_chunk trades speed (one more pass over dW per chunk) for
+ * memory.
  * Errors as flce_check_args, with FLCE_ERR_UNSUPPORTED for float32 inputs;
  * flce_token_chunk_nr gives the chunk used.
  */

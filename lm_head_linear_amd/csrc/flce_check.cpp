@@ -88,7 +88,9 @@ bool make_plan_nr(int64_t N, int64_t H, int64_t V, int dtype, int64_t token_chun
   q.grad_dtype = dtype;
   q.grad_elem = q.elem;
   const int64_t nmax = round_up(N > 0 ? N : 1, q.tile);
-  int64_t nc = token_chunk > 0 ? round_up(token_chunk, q.tile) : round_up(N < 4096 ? (N > 0 ? N : 1) : 4096, q.tile);
+  constexpr int64_t kDefaultChunk = 8192;
+  int64_t nc = token_chunk > 0 ? round_up(token_chunk, q.tile)
+                               : round_up(N < kDefaultChunk ? (N > 0 ? N : 1) : kDefaultChunk, q.tile);
   if (nc > nmax) nc = nmax;
   q.nc = nc;
   q.n_tok_chunks = ceil_div(N, nc);

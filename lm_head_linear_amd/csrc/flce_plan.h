@@ -76,7 +76,7 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
                int grad_dtype = -1);
 
 // Plan of the no-recompute variant (bf16 only): token chunks of
-// `token_chunk` tokens (rounded up to the tile; <= 0: min(N, 4096) rounded
+// `token_chunk` tokens (rounded up to the tile; <= 0: min(N, 8192) rounded
 // up), each with a [nc][roundup(V, 256)] bf16 buffer of probabilities that
 // becomes that chunk's G.
 bool make_plan_nr(int64_t N, int64_t H, int64_t V, int dtype, int64_t token_chunk, Plan* p);

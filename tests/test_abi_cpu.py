@@ -287,8 +287,9 @@ def test_f32grad_workspace_check(lib):
 
 # ------------------------------------------------------ no-recompute variant
 def test_nr_plan(lib):
-    # default chunk: min(N, 4096) rounded up to the tile
-    assert lib.flce_token_chunk_nr(8192, 4096, 131072, 1, 0) == 4096
+    # default chunk: min(N, 8192) rounded up to the tile
+    assert lib.flce_token_chunk_nr(8192, 4096, 131072, 1, 0) == 8192
+    assert lib.flce_token_chunk_nr(16384, 4096, 131072, 1, 0) == 8192
     assert lib.flce_token_chunk_nr(600, 64, 1000, 1, 0) == 768
     assert lib.flce_token_chunk_nr(8192, 4096, 131072, 1, 1000) == 1024
     assert lib.flce_token_chunk_nr(8192, 4096, 131072, 1, 100000) == 8192

@@ -121,9 +121,9 @@ def test_large_vocab_float32_gradients():
 
 
 def test_large_vocab_no_recompute():
-    """The no-recompute variant at full size (2 token chunks of 4096)."""
+    """The no-recompute variant at full size, in 2 token chunks of 4096."""
     w = _case(3)[0]
-    g = gu.run_gpu(w, recompute=False)
+    g = gu.run_gpu(w, recompute=False, token_chunk=4096)
     assert g["num_tokens"] == 0
     _check(3, g, label="large_vocab no recompute")
 
@@ -136,7 +136,7 @@ def test_softcapped_full():
 
 
 def test_softcapped_no_recompute():
-    """No-recompute variant with the softcap at full size (2 chunks of 4096
+    """No-recompute variant with the softcap at full size (one chunk of 8192
     tokens, V = 256000: the softcap derivative rebuilt from the stored
     probabilities)."""
     w = _case(4)[0]
@@ -154,7 +154,7 @@ def test_long_full_and_external_count():
 
 
 def test_long_no_recompute():
-    """No-recompute variant on 16384 tokens: 4 token chunks, dW added up over
+    """No-recompute variant on 16384 tokens: 2 token chunks, dW added up over
     them, with the external count."""
     w = _case(5)[0]
     g = gu.run_gpu(w, recompute=False)
