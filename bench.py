@@ -148,6 +148,31 @@ def other_modes(m, w, h, W, y, dH, dW, loss, nt, steps, timing, nhv):
                     "workspace_bytes": int(fws.numel())}
     log(f"forward only: {f_ms:.3f} ms/call, {forward_only['tflops_2nhv']:.1f} TFLOP/s")
 
+    # The same forward handing back the logits ([N, V], bf16 then float32):
+    # the extra time is the logits' write.
+    for name, dt in (("with_logits_bf16", torch.bfloat16), ("with_logits_f32", torch.float32)):
+        lg = torch.empty(N, V, dtype=dt, device=dev)
+
+        def fwd_logits():
+            m.flce_forward_logits(h, W, y, ignore_index=w.ignore_index, softcap=w.softcap,
+                                  reduction=w.reduction, workspace=fws, loss=loss,
+                                  num_tokens=nt, logits=lg)
+
+        for _ in range(2):
+            fwd_logits()
+        torch.cuda.synchronize()
+        tl0 = time.perf_counter()
+        for _ in range(steps):
+            fwd_logits()
+        torch.cuda.synchronize()
+        l_ms = (time.perf_counter() - tl0) * 1e3 / steps
+        nbytes = lg.numel() * lg.element_size()
+        forward_only[name] = {"ms_per_call": round(l_ms, 4), "logits_bytes": int(nbytes),
+                              "extra_ms": round(l_ms - f_ms, 4)}
+        log(f"forward + {dt} logits: {l_ms:.3f} ms/call ({nbytes / 1e9:.2f} GB of logits, "
+            f"+{l_ms - f_ms:.3f} ms)")
+        del lg
+
     # Float32 gradients for the same bf16 inputs (G as a bf16 hi + lo pair,
     # twice the dW/dH work), timed the same way.
     gws = torch.empty(m.flce_workspace_size(N, H, V, W.dtype, torch.float32), dtype=torch.uint8,

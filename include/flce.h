@@ -256,6 +256,55 @@ int flce_forward(const void* h, const void* W, const int64_t* labels, int64_t N,
                  int dtype, float mb_scale, void* workspace, size_t workspace_bytes,
                  int32_t* status, float* lse_out);
 
+/*
+ * flce_forward_logits_check_args -- the synchronous checks of
+ * flce_forward_logits, with its parameter list, without touching the GPU:
+ * those of flce_forward_check_args, and then FLCE_ERR_ARG unless
+ * logits_dtype is FLCE_F32 or FLCE_BF16, V <= ld_logits <= 2^31, logits is
+ * non-NULL when N > 0, (N - 1) * ld_logits + V < 2^60, and the logits buffer
+ * ((N - 1) * ld_logits + V
+ * elements from `logits`) overlaps none of h, W, labels, loss, num_tokens,
+ * status, lse_out and the workspace; FLCE_ERR_UNSUPPORTED if logits is not
+ * aligned to its element size.
+ */
+int flce_forward_logits_check_args(const void* h, const void* W, const int64_t* labels,
+                                   int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                                   float softcap, int reduction, int64_t num_label_tokens,
+                                   float* loss, int64_t* num_tokens, void* stream, int dtype,
+                                   float mb_scale, void* workspace, size_t workspace_bytes,
+                                   int32_t* status, float* lse_out, void* logits,
+                                   int64_t ld_logits, int logits_dtype);
+
+/*
+ * flce_forward_logits -- flce_forward that also hands back the logits, for
+ * callers that need them (LlamaFactory error page "cross_entropy and
+ * fused_linear_cross_entropy cannot both be enabled", "Source" and
+ * "Solutions": the fused loss never forms the logits, so a caller with
+ * require_logits set is switched to plain cross-entropy; here they come out
+ * of the same forward pass instead, at the cost of writing them once).
+ *
+ * logits  device, caller-owned output, row-major by token:
+ *         logits[t * ld_logits + v] = z'_tv for t < N, v < V, where z' is
+ *         h_t . W_v, softcapped as s * tanh(z / s) when softcap > 0 (the
+ *         Z' of the definition at the top of this file). These are the
+ *         float32 values the loss and lse are formed from, stored as float32
+ *         (logits_dtype FLCE_F32) or rounded to nearest even bf16
+ *         (FLCE_BF16). Elements v in [V, ld_logits) are not written. Rows are
+ *         stored in 16-byte runs when logits and ld_logits keep every run
+ *         16-byte aligned, element by element otherwise.
+ * Everything else as in flce_forward, with the same workspace
+ * (flce_forward_workspace_size): *loss, *num_tokens, lse_out and *status are
+ * bit-identical to what flce_forward returns on the same inputs. Cost: the
+ * forward GEMM (2*N*H*V flops) plus N*V stored elements.
+ * Errors  see flce_forward_logits_check_args; FLCE_ERR_HIP if a launch fails.
+ */
+int flce_forward_logits(const void* h, const void* W, const int64_t* labels, int64_t N,
+                        int64_t H, int64_t V, int64_t ignore_index, float softcap,
+                        int reduction, int64_t num_label_tokens, float* loss,
+                        int64_t* num_tokens, void* stream, int dtype, float mb_scale,
+                        void* workspace, size_t workspace_bytes, int32_t* status,
+                        float* lse_out, void* logits, int64_t ld_logits, int logits_dtype);
+
 /* flce_status_string -- a static, human-readable name for a status code. */
 const char* flce_status_string(int status);
 

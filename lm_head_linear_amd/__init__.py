@@ -43,6 +43,8 @@ __all__ = [
     "flce_forward",
     "flce_forward_workspace_size",
     "flce_forward_check_args",
+    "flce_forward_logits",
+    "flce_forward_logits_check_args",
     "flce_status_string",
     "flce_vocab_chunk",
     "flce_profile_begin",
@@ -151,6 +153,20 @@ def flce_forward_check_args(h, W, labels, *, N, H, V, ignore_index=-100, softcap
                          num_label_tokens, loss, num_tokens, None, dtype, mb_scale, workspace,
                          status, lse_out)
     return int(_lib.load().flce_forward_check_args(*args))
+
+
+def flce_forward_logits_check_args(h, W, labels, *, N, H, V, logits, ld_logits=None,
+                                   logits_dtype=torch.float32, ignore_index=-100, softcap=0.0,
+                                   reduction="sum", num_label_tokens=None, loss=None,
+                                   num_tokens=None, dtype=torch.bfloat16, mb_scale=1.0,
+                                   workspace=None, status=None, lse_out=None) -> int:
+    """The logits-returning forward entry's synchronous checks; a status code."""
+    args = _fwd_abi_args(h, W, labels, N, H, V, ignore_index, softcap, reduction,
+                         num_label_tokens, loss, num_tokens, None, dtype, mb_scale, workspace,
+                         status, lse_out)
+    ld = V if ld_logits is None else int(ld_logits)
+    return int(_lib.load().flce_forward_logits_check_args(*args, _ptr(logits), ld,
+                                                          _dtype_code(logits_dtype)))
 
 
 def _check_tensor(name, t, shape, dtype, device):
@@ -284,6 +300,68 @@ def flce_forward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, *,
     if rc != _lib.OK:
         raise FlceError(rc, "flce_forward")
     return loss, num_tokens
+
+
+def flce_forward_logits(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, *,
+                        ignore_index: int = -100, softcap: float = 0.0, reduction: str = "sum",
+                        num_label_tokens: Optional[int] = None, mb_scale: float = 1.0,
+                        logits: Optional[torch.Tensor] = None,
+                        logits_dtype: torch.dtype = torch.float32,
+                        workspace: Optional[torch.Tensor] = None,
+                        lse_out: Optional[torch.Tensor] = None,
+                        status: Optional[torch.Tensor] = None,
+                        loss: Optional[torch.Tensor] = None,
+                        num_tokens: Optional[torch.Tensor] = None):
+    """Forward that also returns the logits: (loss, num_tokens, logits).
+
+    ``logits`` is [N, V] (or a row-strided view [N, V] of a wider buffer,
+    unit stride along V), float32 or bfloat16: the softcapped logits the loss
+    is formed from. A new contiguous [N, V] tensor of ``logits_dtype`` is made
+    when it is None. Loss, count, lse and status are bit-identical to
+    :func:`flce_forward`'s.
+    """
+    if h.dim() != 2 or W.dim() != 2:
+        raise ValueError("h must be [N, H] and W [V, H]")
+    N, H = h.shape
+    V = W.shape[0]
+    dev = W.device
+    if dev.type != "cuda":
+        raise ValueError("flce_forward_logits runs on a GPU; tensors are on " + str(dev))
+    _check_tensor("h", h, (N, H), W.dtype, dev)
+    _check_tensor("W", W, (V, H), W.dtype, dev)
+    _check_tensor("labels", labels, (N,), torch.int64, dev)
+    if logits is None:
+        logits = torch.empty((N, V), dtype=logits_dtype, device=dev)
+    if logits.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"logits must be float32 or bfloat16, got {logits.dtype}")
+    if tuple(logits.shape) != (N, V) or logits.device != dev:
+        raise ValueError(f"logits must be [{N}, {V}] on {dev}")
+    if N > 0 and V > 1 and logits.stride(1) != 1:
+        raise ValueError("logits must have unit stride along the vocabulary")
+    ld = logits.stride(0) if N > 1 else V
+    if loss is None:
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+    if num_tokens is None:
+        num_tokens = torch.empty((), dtype=torch.int64, device=dev)
+    if lse_out is not None:
+        _check_tensor("lse_out", lse_out, (N,), torch.float32, dev)
+    if status is not None:
+        _check_tensor("status", status, (), torch.int32, dev)
+    need = flce_forward_workspace_size(N, H, V, W.dtype)
+    if need == 0:
+        raise FlceError(_lib.ERR_ARG, "flce_forward_workspace_size")
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    args = _fwd_abi_args(h, W, labels, N, H, V, ignore_index, softcap, reduction,
+                         num_label_tokens, loss, num_tokens, stream, W.dtype, mb_scale,
+                         workspace, status, lse_out)
+    with torch.cuda.device(dev):
+        rc = _lib.load().flce_forward_logits(*args, _ptr(logits), int(ld),
+                                             _dtype_code(logits.dtype))
+    if rc != _lib.OK:
+        raise FlceError(rc, "flce_forward_logits")
+    return loss, num_tokens, logits
 
 
 def flce_profile_begin() -> None:

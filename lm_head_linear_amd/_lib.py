@@ -33,6 +33,8 @@ SIGNATURES = {
     "flce_forward_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
     "flce_forward_check_args": (_i32, _F_ARGS),
     "flce_forward": (_i32, _F_ARGS),
+    "flce_forward_logits_check_args": (_i32, _F_ARGS + [_vp, _i64, _i32]),
+    "flce_forward_logits": (_i32, _F_ARGS + [_vp, _i64, _i32]),
     "flce_status_string": (_c.c_char_p, [_i32]),
     "flce_vocab_chunk": (_i64, [_i64, _i64, _i64, _i32]),
     "flce_profile_begin": (_i32, []),

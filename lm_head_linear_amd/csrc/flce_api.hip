@@ -110,7 +110,8 @@ int run(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t 
         int64_t ignore_index, float softcap, int reduction, int64_t num_label_tokens,
         float* loss, int64_t* num_tokens, void* dH, void* dW, void* stream, int dtype,
         float mb_scale, int accumulate_dW, void* workspace, int32_t* status, float* lse_out,
-        bool backward, int grad_dtype) {
+        bool backward, int grad_dtype, void* logits = nullptr, int64_t ld_logits = 0,
+        int logits_dtype = FLCE_F32) {
   flce::Plan p;
   if (!flce::make_plan(N, H, V, dtype, &p, backward, grad_dtype)) return FLCE_ERR_ARG;
 
@@ -126,6 +127,7 @@ int run(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t 
   a.loss = loss; a.num_tokens = num_tokens; a.dH = dH; a.dW = dW;
   a.mb_scale = mb_scale; a.accumulate_dW = accumulate_dW ? 1 : 0;
   a.status = status; a.lse_out = lse_out;
+  a.logits = logits; a.ld_logits = ld_logits; a.logits_dtype = logits_dtype;
   a.sc = reinterpret_cast<flce::Scalars*>(ws + p.off_scalars);
 
   hipError_t e;
@@ -245,6 +247,22 @@ int flce_forward(const void* h, const void* W, const int64_t* labels, int64_t N,
   return run(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens, loss,
              num_tokens, nullptr, nullptr, stream, dtype, mb_scale, 0, workspace, status,
              lse_out, false, dtype);
+}
+
+int flce_forward_logits(const void* h, const void* W, const int64_t* labels, int64_t N,
+                        int64_t H, int64_t V, int64_t ignore_index, float softcap,
+                        int reduction, int64_t num_label_tokens, float* loss,
+                        int64_t* num_tokens, void* stream, int dtype, float mb_scale,
+                        void* workspace, size_t workspace_bytes, int32_t* status,
+                        float* lse_out, void* logits, int64_t ld_logits, int logits_dtype) {
+  int st = flce_forward_logits_check_args(h, W, labels, N, H, V, ignore_index, softcap,
+                                          reduction, num_label_tokens, loss, num_tokens, stream,
+                                          dtype, mb_scale, workspace, workspace_bytes, status,
+                                          lse_out, logits, ld_logits, logits_dtype);
+  if (st != FLCE_OK) return st;
+  return run(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens, loss,
+             num_tokens, nullptr, nullptr, stream, dtype, mb_scale, 0, workspace, status,
+             lse_out, false, dtype, N > 0 ? logits : nullptr, ld_logits, logits_dtype);
 }
 
 int flce_profile_begin(void) {

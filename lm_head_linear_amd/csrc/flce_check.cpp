@@ -242,6 +242,45 @@ int flce_forward_check_args(const void* h, const void* W, const int64_t* labels,
                       workspace_bytes, false);
 }
 
+int flce_forward_logits_check_args(const void* h, const void* W, const int64_t* labels,
+                                   int64_t N, int64_t H, int64_t V, int64_t ignore_index,
+                                   float softcap, int reduction, int64_t num_label_tokens,
+                                   float* loss, int64_t* num_tokens, void* stream, int dtype,
+                                   float mb_scale, void* workspace, size_t workspace_bytes,
+                                   int32_t* status, float* lse_out, void* logits,
+                                   int64_t ld_logits, int logits_dtype) {
+  if (logits_dtype != FLCE_F32 && logits_dtype != FLCE_BF16) return FLCE_ERR_ARG;
+  if (V > 0 && (ld_logits < V || ld_logits > (int64_t(1) << 31))) return FLCE_ERR_ARG;
+  if (N > 0 && !logits) return FLCE_ERR_ARG;
+  // the buffer's element count (N - 1) * ld + V stays below 2^60
+  if (N > 0 && V > 0 && V <= (int64_t(1) << 31) &&
+      N - 1 > ((int64_t(1) << 60) - V) / ld_logits)
+    return FLCE_ERR_ARG;
+  const int st = flce_forward_check_args(h, W, labels, N, H, V, ignore_index, softcap, reduction,
+                                         num_label_tokens, loss, num_tokens, stream, dtype,
+                                         mb_scale, workspace, workspace_bytes, status, lse_out);
+  if (st == FLCE_ERR_ARG) return st;            // sizes are valid from here on
+  if (N > 0) {
+    // the logits buffer, [N][ld_logits] up to its last stored element, is an
+    // output of its own: it may overlap no input, no other output and no scratch
+    const size_t es = logits_dtype == FLCE_BF16 ? 2 : 4;
+    const size_t nl = (size_t(N - 1) * size_t(ld_logits) + size_t(V)) * es;
+    const size_t ein = dtype == FLCE_BF16 ? 2 : 4;
+    if (overlaps(logits, nl, h, size_t(N) * H * ein) ||
+        overlaps(logits, nl, W, size_t(V) * H * ein) ||
+        overlaps(logits, nl, labels, size_t(N) * sizeof(int64_t)) ||
+        overlaps(logits, nl, loss, sizeof(float)) ||
+        overlaps(logits, nl, num_tokens, sizeof(int64_t)) ||
+        overlaps(logits, nl, status, sizeof(int32_t)) ||
+        overlaps(logits, nl, lse_out, size_t(N) * sizeof(float)) ||
+        overlaps(logits, nl, workspace, workspace_bytes))
+      return FLCE_ERR_ARG;
+    if (st == FLCE_OK || st == FLCE_ERR_WORKSPACE)
+      if (misaligned(logits, es - 1)) return FLCE_ERR_UNSUPPORTED;
+  }
+  return st;
+}
+
 const char* flce_status_string(int s) {
   switch (s) {
     case FLCE_OK: return "FLCE_OK";

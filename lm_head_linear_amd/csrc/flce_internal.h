@@ -41,6 +41,10 @@ struct Args {
   int accumulate_dW;
   int32_t* status;
   float* lse_out;
+  // optional logits output of the forward: [N][ld_logits], FLCE_F32 or FLCE_BF16
+  void* logits;
+  int64_t ld_logits;
+  int logits_dtype;
   // carved workspace
   Scalars* sc;
   float2* part;

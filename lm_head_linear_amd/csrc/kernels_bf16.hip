@@ -401,10 +401,96 @@ __device__ __forceinline__ float tanh_fast(float x) {
   return 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
 }
 
+// ---- token-major logits output of the forward --------------------------
+// Kinds of logits output of the forward epilogue.
+enum LogitsOut : int { kNoLogits = 0, kLogitsF32 = 1, kLogitsBF16 = 2 };
+
+// Stores the tile's logits (rows vocabulary ids, columns tokens, masked rows
+// v >= V never stored) row-major by token: out[t][v], row length ld, as
+// float32 or as bf16 rounded to nearest even. Each wave stages its block in
+// its own 32 KiB of LDS as [token][vocab]: bf16 all 128 vocabulary rows in
+// one pass (8-byte slots, as in store_token_major), float32 64 rows per pass
+// (16-byte slots holding 4 consecutive vocabulary values, XOR-swizzled by
+// token), then writes 16-byte runs of token rows. A run that would cross V,
+// and every run when `vec` is 0 (destination or row length not 16-byte
+// aligned), is written element by element. Ends with a barrier, so the
+// caller may reuse the LDS at once.
+template <int OUT>
+__device__ __forceinline__ void store_logits(const f32x16 (&acc)[4][4], char* smem, int wm,
+                                             int wn, int lane, void* out, int64_t ld, int vec,
+                                             int64_t m0, int64_t n0, int64_t N, int64_t V) {
+  constexpr bool F32 = OUT == kLogitsF32;
+  constexpr int kPasses = F32 ? 2 : 1;
+  constexpr int kRun = F32 ? 4 : 8;                // elements per 16-byte run
+  const int half = lane >> 5;
+  char* reg = smem + (wm + 2 * wn) * kWaveScratch;
+#pragma unroll
+  for (int ps = 0; ps < kPasses; ++ps) {
+    if (ps) __syncthreads();                       // the previous pass has been read
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tl = j * 32 + (lane & 31);
+#pragma unroll
+      for (int ii = 0; ii < 4 / kPasses; ++ii) {
+        const int i = ii + ps * (4 / kPasses);
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * rq + e];
+          if (F32) {
+            const int slot = (ii * 8 + 2 * rq + half) ^ (tl & 15);
+            *reinterpret_cast<u32x4*>(reg + tl * 256 + slot * 16) =
+                u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                      __float_as_uint(v[3])};
+          } else {
+            const int slot = (i * 8 + 2 * rq + half) ^ (tl & 31);
+            *reinterpret_cast<uint2*>(reg + tl * 256 + slot * 8) =
+                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+          }
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int q = 0; q < 32; ++q) {
+      const int idx = q * 64 + lane;
+      const int tl = idx >> 4, ch = idx & 15;
+      u32x4 v;
+      if (F32) {
+        v = *reinterpret_cast<const u32x4*>(reg + tl * 256 + (ch ^ (tl & 15)) * 16);
+      } else {
+        const int x = tl & 31;
+        v = *reinterpret_cast<const u32x4*>(reg + tl * 256 + (((2 * ch) ^ x) & ~1) * 8);
+        if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+      }
+      const int64_t t = n0 + wn * 128 + tl;
+      const int64_t vl = m0 + wm * 128 + (F32 ? ps * 64 + 4 * ch : 8 * ch);
+      if (t < N && vl < V) {
+        if (vec && vl + kRun <= V) {
+          char* dst = static_cast<char*>(out) + (t * ld + vl) * (F32 ? 4 : 2);
+          *reinterpret_cast<u32x4*>(dst) = v;
+        } else {
+          const int n = int(V - vl < kRun ? V - vl : kRun);
+          for (int e = 0; e < n; ++e) {
+            if (F32)
+              static_cast<uint32_t*>(out)[t * ld + vl + e] = v[e];
+            else
+              static_cast<uint16_t*>(out)[t * ld + vl + e] = uint16_t(v[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // ---- forward epilogue: per (vocab tile, token) max and sum-exp ------------
 // Tile rows are vocabulary ids, columns are tokens.
-// SOFTCAP selects the s * tanh(z / s) variant at compile time.
-template <bool SOFTCAP>
+// SOFTCAP selects the s * tanh(z / s) variant at compile time; OUT, whether
+// the logits z' themselves are also stored (the float32 values the max and
+// sum are formed from).
+template <bool SOFTCAP, int OUT = kNoLogits>
 struct EpiLse {
   const int64_t* labels;
   int64_t N, V, ignore_index;
@@ -412,6 +498,9 @@ struct EpiLse {
   float2* part;  // [n_voc_tiles][ld_part]: (max m, sum of exp(x - m)) of the tile
   int64_t ld_part;
   float* zt;     // target logit (softcapped), one writer per non-ignored token
+  void* logits;  // OUT != kNoLogits: [N][ld_logits]
+  int64_t ld_logits;
+  int vec;       // 16-byte runs of the logits rows are aligned
 
   __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm,
                                              int wn, int lane, char* smem) const {
@@ -463,6 +552,8 @@ struct EpiLse {
       mx[j] = m;
       sm[j] = s;
     }
+    if (OUT != kNoLogits)
+      store_logits<OUT>(acc, smem, wm, wn, lane, logits, ld_logits, vec, m0, n0, N, V);
     // combine the two waves (wm = 0, 1) that share the token columns
     float2* buf = reinterpret_cast<float2*>(smem);
     if (wm == 1 && half == 0) {
@@ -971,15 +1062,28 @@ hipError_t run_gemm(const gemm::Launch& l, const Args& a, const Epi& e, int kind
 
 }  // namespace
 
-hipError_t bf16_forward(const Plan& p, const Args& a, const Launcher& L) {
+namespace {
+template <int OUT>
+hipError_t bf16_forward_out(const Plan& p, const Args& a, const Launcher& L) {
   const gemm::Launch l = gemm::forward_launch(p);
+  const int esz = OUT == kLogitsF32 ? 4 : 2;
+  const int vec = OUT != kNoLogits && reinterpret_cast<uintptr_t>(a.logits) % 16 == 0 &&
+                  (a.ld_logits * esz) % 16 == 0;
   if (a.softcap > 0.f) {
-    EpiLse<true> e{a.labels, p.N, p.V, a.ignore_index, a.softcap, 1.f / a.softcap, a.part,
-                   p.ld_part, a.zt};
+    EpiLse<true, OUT> e{a.labels, p.N, p.V, a.ignore_index, a.softcap, 1.f / a.softcap, a.part,
+                        p.ld_part, a.zt, a.logits, a.ld_logits, vec};
     return run_gemm<gemm::kFormN, gemm::kFormN>(l, a, e, kLseFwd, L);
   }
-  EpiLse<false> e{a.labels, p.N, p.V, a.ignore_index, 0.f, 0.f, a.part, p.ld_part, a.zt};
+  EpiLse<false, OUT> e{a.labels, p.N, p.V, a.ignore_index, 0.f, 0.f, a.part, p.ld_part, a.zt,
+                       a.logits, a.ld_logits, vec};
   return run_gemm<gemm::kFormN, gemm::kFormN>(l, a, e, kLseFwd, L);
+}
+}  // namespace
+
+hipError_t bf16_forward(const Plan& p, const Args& a, const Launcher& L) {
+  if (!a.logits) return bf16_forward_out<kNoLogits>(p, a, L);
+  if (a.logits_dtype == FLCE_F32) return bf16_forward_out<kLogitsF32>(p, a, L);
+  return bf16_forward_out<kLogitsBF16>(p, a, L);
 }
 
 // Float32 gradients for bf16 inputs: G as a bf16 hi + lo pair; dW and dH

@@ -60,13 +60,17 @@ __device__ __forceinline__ void tile_gemm(const Op& A, const Op& B, int64_t m0, 
 }
 
 // Forward: tile rows = vocab ids, columns = tokens; per (vocab tile, token)
-// the max (log2 units) and the sum of exponentials, plus the target logit.
+// the max and the sum of exponentials, plus the target logit. With `logits`
+// non-null the tile's logits are also stored token-major, out[t][v] with row
+// length ld_logits, float32 or (bf16_out) bf16 rounded to nearest even.
 __global__ __launch_bounds__(256) void k_f32_lse(const float* __restrict__ W,
                                                  const float* __restrict__ h,
                                                  const int64_t* __restrict__ labels, int64_t N,
                                                  int64_t H, int64_t V, int64_t ignore_index,
                                                  float softcap, float2* __restrict__ part,
-                                                 int64_t ld_part, float* __restrict__ zt) {
+                                                 int64_t ld_part, float* __restrict__ zt,
+                                                 void* __restrict__ logits, int64_t ld_logits,
+                                                 int bf16_out) {
   __shared__ float As[kBK][kT + 1], Bs[kBK][kT + 1];
   __shared__ float Cs[kT][kT + 1];
   const int64_t m0 = int64_t(blockIdx.x) * kT, n0 = int64_t(blockIdx.y) * kT;
@@ -83,6 +87,20 @@ __global__ __launch_bounds__(256) void k_f32_lse(const float* __restrict__ W,
       Cs[ty + 16 * a][tx + 16 * b] = z;
     }
   __syncthreads();
+  if (logits) {
+    // consecutive threads take consecutive vocabulary ids of one token row
+    for (int idx = tid; idx < kT * kT; idx += 256) {
+      const int tl = idx / kT, vl = idx % kT;
+      const int64_t t = n0 + tl, v = m0 + vl;
+      if (t < N && v < V) {
+        const float z = Cs[vl][tl];
+        if (bf16_out)
+          static_cast<__bf16*>(logits)[t * ld_logits + v] = __bf16(z);
+        else
+          static_cast<float*>(logits)[t * ld_logits + v] = z;
+      }
+    }
+  }
   if (tid < kT) {
     const int64_t t = n0 + tid;
     const int rows = int((V - m0) < kT ? (V - m0) : kT);
@@ -200,7 +218,8 @@ hipError_t f32_forward(const Plan& p, const Args& a, const Launcher& L) {
   L.pre(kLseFwd);
   hipLaunchKernelGGL(k_f32_lse, dim3(cdiv(p.V, kT), cdiv(p.N, kT)), dim3(256), 0, L.stream,
                      static_cast<const float*>(a.W), static_cast<const float*>(a.h), a.labels,
-                     p.N, p.H, p.V, a.ignore_index, a.softcap, a.part, p.ld_part, a.zt);
+                     p.N, p.H, p.V, a.ignore_index, a.softcap, a.part, p.ld_part, a.zt,
+                     a.logits, a.ld_logits, int(a.logits_dtype == FLCE_BF16));
   L.post(kLseFwd);
   return hipGetLastError();
 }

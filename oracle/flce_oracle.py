@@ -30,6 +30,9 @@ What it computes (plain definition, materialised logits, float64 throughout):
   MTP?").
 * gradients of the returned loss: ``G = c * valid * (softmax(Z') - onehot(y))
   * dZ'/dZ``, ``dH = G @ W``, ``dW = G.T @ h``.
+* the logits themselves, ``Z'``, for a caller that needs them (LlamaFactory
+  error page, "Source" and "Solutions": ``require_logits`` switches the fused
+  loss off because it never forms them).
 
 Readings taken where the pages leave a step open are listed in the project's
 design notes; the ones that change arithmetic here: the empty-target rule is
@@ -58,6 +61,7 @@ __all__ = [
     "softcap_logits",
     "logsumexp_rows",
     "forward_rows",
+    "logits_rows",
     "grad_logits_rows",
     "flce_reference",
     "dW_rows",
@@ -167,6 +171,19 @@ def forward_rows(h: np.ndarray, W: np.ndarray, labels: np.ndarray, ignore_index:
         zt[r0:r1] = np.where(v, z_y, 0.0)
         tok[r0:r1] = np.where(v, l - z_y, 0.0)
     return lse, tok, zt
+
+
+def logits_rows(h: np.ndarray, W: np.ndarray, softcap: float) -> np.ndarray:
+    """The logits Z' = softcap(h @ W.T) of every row of h, in float64.
+
+    What a caller that needs the logits gets back (LlamaFactory error page,
+    "Source" and "Solutions": with require_logits the logits must exist, which
+    the plain cross-entropy path provides); the same Z' the loss is formed from.
+    """
+    h = np.asarray(h, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    Zp, _ = softcap_logits(h @ W.T, softcap)
+    return Zp
 
 
 def grad_logits_rows(Zp: np.ndarray, dcap: Optional[np.ndarray], lse: np.ndarray,

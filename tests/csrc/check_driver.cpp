@@ -83,6 +83,28 @@ int main() {
     EXPECT(flce_vocab_chunk_ex(4096, 4096, 131072, FLCE_BF16, FLCE_F32) * 2 ==
            flce_vocab_chunk(4096, 4096, 131072, FLCE_BF16));
   }
+  // logits-returning forward: sizes at the limits are refused or accepted
+  // without overflow in the overlap arithmetic
+  {
+    const uintptr_t b = uintptr_t(1) << 32;
+    auto lc = [&](int64_t N, int64_t V, int64_t ld, int ldt, uintptr_t lg) {
+      return flce_forward_logits_check_args(
+          (void*)b, (void*)(b * 2), (int64_t*)(b * 3), N, 8, V, -100, 0.f, FLCE_SUM, 0,
+          (float*)(b * 4), (int64_t*)(b * 5), nullptr, FLCE_F32, 1.f,
+          (void*)(uintptr_t(1) << 40), big, nullptr, nullptr, (void*)lg, ld, ldt);
+    };
+    const uintptr_t far = uintptr_t(1) << 50;
+    EXPECT(lc(1024, 1000, 1000, FLCE_F32, far) == FLCE_OK);
+    EXPECT(lc(1024, 1000, 999, FLCE_F32, far) == FLCE_ERR_ARG);
+    EXPECT(lc(int64_t(1) << 31, int64_t(1) << 31, int64_t(1) << 31, FLCE_F32, far) ==
+           FLCE_ERR_ARG);
+    EXPECT(lc((int64_t(1) << 29) + 2, 1 << 20, int64_t(1) << 31, FLCE_BF16, far) == FLCE_ERR_ARG);
+    EXPECT(lc(int64_t(1) << 29, 8, int64_t(1) << 31, FLCE_BF16, far) == FLCE_OK);
+    EXPECT(lc(4, 7, INT64_MAX, FLCE_F32, far) == FLCE_ERR_ARG);
+    EXPECT(lc(4, 7, 7, FLCE_BF16, far + 1) == FLCE_ERR_UNSUPPORTED);
+    EXPECT(lc(4, 7, 7, FLCE_F32, b * 3) == FLCE_ERR_ARG);   // on the labels
+    EXPECT(lc(0, 7, 7, FLCE_F32, 0) == FLCE_OK);
+  }
   for (int s = -1; s < 8; ++s) EXPECT(flce_status_string(s) != nullptr);
   if (failures == 0) std::printf("all checks passed\n");
   return failures ? 1 : 0;

@@ -13,6 +13,8 @@ from oracle import flce_oracle as orc
 #   bf16 grads max|gpu - ref| <= 2e-2 * max|ref| per tensor
 #   fp32 grads max|gpu - ref| <= 1e-4 * max|ref| per tensor
 #   num_tokens bit-exact; ignored rows of dH exactly zero
+#   logits     per element, the float32 rounding-error bound of logits_tolerance;
+#              bf16 logits bit-equal to the round-to-nearest-even of float32 ones
 LOSS_RTOL = 1e-5
 GRAD_TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
 
@@ -108,3 +110,58 @@ def assert_parity(w: fi.Workload, g: dict, r, *, check_lse=True):
         lse = to_np64(g["lse"])
         err = np.abs(lse - r.lse).max()
         assert err <= 1e-5 * max(1.0, np.abs(r.lse).max()), f"lse max err {err:.3e}"
+
+
+def run_gpu_forward_logits(w: fi.Workload, *, logits_dtype=torch.float32, pad=0, mb_scale=1.0,
+                           dev=None, **kw):
+    """The logits-returning forward entry on the same inputs. The logits go to
+    a [N, V + pad] buffer prefilled with a sentinel, through its [N, V] view;
+    returns loss, num_tokens, lse, status, the view and the whole buffer."""
+    import lm_head_linear_amd as m
+    dev = dev or device()
+    h = w.h.reshape(-1, w.H).to(dev)
+    W = w.W.to(dev)
+    y = w.labels.reshape(-1).to(dev)
+    N, V = h.shape[0], W.shape[0]
+    buf = torch.full((N, V + pad), LOGITS_SENTINEL, dtype=logits_dtype, device=dev)
+    view = buf[:, :V]
+    lse_out = torch.full((N,), float("nan"), dtype=torch.float32, device=dev)
+    status = torch.full((), -1, dtype=torch.int32, device=dev)
+    args = dict(ignore_index=w.ignore_index, softcap=w.softcap, reduction=w.reduction,
+                num_label_tokens=w.num_label_tokens, mb_scale=mb_scale, lse_out=lse_out,
+                status=status, logits=view)
+    args.update(kw)
+    loss, nt, lg = m.flce_forward_logits(h, W, y, **args)
+    torch.cuda.synchronize(dev)
+    assert lg.data_ptr() == view.data_ptr()
+    return dict(loss=float(loss.item()), loss_t=loss, num_tokens=int(nt.item()), lse=lse_out,
+                status=int(status.item()), logits=view, buf=buf)
+
+
+LOGITS_SENTINEL = -12288.0     # -1.5 * 2^13: exact in float32 and bfloat16
+
+
+def logits_tolerance(w: fi.Workload, rows=None) -> np.ndarray:
+    """Per-element bound on |GPU logit - float64 logit| for the float32 logits.
+
+    The kernels accumulate the H products of a logit in float32 (bf16 x bf16
+    products are exact in float32, float32 ones round once). The worst-case
+    bound, about H u sum_k |p_k| (u = 2^-24), is far too loose to notice a
+    dropped product. The test uses the rounding-error model instead: with
+    independent rounding errors, summing H terms of random sign errs by a
+    standard deviation of about u H rms(p) / sqrt(6), since the partial sums
+    grow like sqrt(k) rms(p). The bound is 8 u H rms(p) = 8 u sqrt(H sum_k
+    p_k^2), about 20 standard deviations, while one missing or doubled
+    product errs by |p_k|, near rms(p) itself. With a softcap the hyperbolic
+    tangent (from the hardware exp2 and reciprocal) adds an absolute error of a
+    few 1e-7 times s, bounded by 1e-6 s; the cap's slope is at most 1, so the
+    product error passes through it unamplified.
+    """
+    h2 = np.square(w.h.reshape(-1, w.H).to(torch.float64).numpy())
+    if rows is not None:
+        h2 = h2[rows]
+    W2 = np.square(w.W.to(torch.float64).numpy())
+    tol = 8.0 * 2.0 ** -24 * np.sqrt(w.H * (h2 @ W2.T))
+    if w.softcap > 0:
+        tol = tol + 1e-6 * w.softcap
+    return tol + 1e-30

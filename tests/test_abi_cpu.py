@@ -250,6 +250,65 @@ def test_python_forward_validation_without_gpu():
         m.fused_linear_cross_entropy(h, y, W)     # forward-only route, same refusal
 
 
+# ------------------------------------------------- logits-returning forward
+LG = 1 << 42          # fake logits address past every other fake buffer
+
+
+def _largs(logits=LG, ld=None, ldt=0, **kw):
+    a = _fargs(**kw)
+    V = kw.get("V", 128)
+    return a + [logits, V if ld is None else ld, ldt]
+
+
+def test_forward_logits_check_args_ok(lib):
+    assert lib.flce_forward_logits_check_args(*_largs()) == 0
+    assert lib.flce_forward_logits_check_args(*_largs(ldt=1, ld=129)) == 0   # any ld >= V
+    assert lib.flce_forward_logits_check_args(*_largs(dtype=0, H=3, ld=1000)) == 0
+    # same workspace as the forward-only entry
+    f = lib.flce_forward_workspace_size(64, 64, 128, 1)
+    assert lib.flce_forward_logits_check_args(*_largs(wsb=f)) == 0
+    assert lib.flce_forward_logits_check_args(*_largs(wsb=f - 1)) == 3
+    # N = 0: no logits buffer needed
+    assert lib.flce_forward_logits_check_args(*_largs(N=0, h=None, labels=None, logits=None)) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(logits=None), 1), (dict(ld=127), 1), (dict(ld=(1 << 31) + 1), 1), (dict(ldt=2), 1),
+    (dict(logits=A16), 1),                 # overlaps h
+    (dict(logits=A16 * 64 - 64 * 128 * 4 + 4), 1),   # last row runs into W
+    (dict(logits=A16 * 128 + 8), 1),       # overlaps labels
+    (dict(logits=A16 * 129), 1),           # overlaps loss
+    (dict(logits=A16 * 1024 + 4096), 1),   # inside the workspace
+    (dict(logits=LG + 2), 2),              # float32 logits not 4-byte aligned
+    (dict(logits=LG + 1, ldt=1), 2),       # bf16 logits not 2-byte aligned
+    (dict(N=-1), 1), (dict(H=12), 2), (dict(wsb=16), 3),
+])
+def test_forward_logits_check_args_errors(lib, kw, code):
+    assert lib.flce_forward_logits_check_args(*_largs(**kw)) == code
+
+
+def test_forward_logits_rejects_before_launch(lib):
+    assert lib.flce_forward_logits(*_largs(N=-1)) == 1
+    assert lib.flce_forward_logits(*_largs(wsb=1)) == 3
+    assert lib.flce_forward_logits(*_largs(ld=3)) == 1
+
+
+def test_forward_logits_ordering_of_errors(lib):
+    """Argument errors (an overlapping logits buffer) are reported before an
+    unsupported layout, which is reported before the workspace."""
+    assert lib.flce_forward_logits_check_args(*_largs(H=12, logits=A16)) == 1
+    assert lib.flce_forward_logits_check_args(*_largs(wsb=16, logits=LG + 2)) == 2
+
+
+def test_python_forward_logits_validation_without_gpu():
+    import lm_head_linear_amd as m
+    h = torch.zeros(4, 8, dtype=torch.bfloat16)
+    W = torch.zeros(16, 8, dtype=torch.bfloat16)
+    y = torch.zeros(4, dtype=torch.int64)
+    with pytest.raises(ValueError):
+        m.flce_forward_logits(h, W, y)            # CPU tensors: refused, no fallback
+
+
 # ------------------------------------------- float32 gradients for bf16 inputs
 def test_f32grad_plan(lib):
     """G kept as a hi + lo pair: half the vocabulary rows per chunk, no dH

@@ -128,6 +128,54 @@ def test_large_vocab_no_recompute():
     _check(3, g, label="large_vocab no recompute")
 
 
+def _forward_logits_check(k, label):
+    """The logits-returning forward at full size: loss, count and lse the same
+    bits as the forward-only entry; float32 logits of sampled tokens against
+    the oracle's Z' row by row; every row's lse the log-sum-exp of its stored
+    logits; the bf16 logits the round-to-nearest-even of the float32 ones."""
+    w, h64, W64, y, lse, tok = _case(k)
+    N, V = h64.shape[0], W64.shape[0]
+    f = gu.run_gpu_forward(w)
+    print(f"{label}: float32 logits [{N}, {V}]", flush=True)
+    g = gu.run_gpu_forward_logits(w, logits_dtype=torch.float32)
+    assert g["loss_t"].view(torch.int32).item() == f["loss_t"].view(torch.int32).item()
+    assert g["num_tokens"] == f["num_tokens"] and g["status"] == f["status"] == 0
+    assert torch.equal(g["lse"].view(torch.int32), f["lse"].view(torch.int32))
+    lg = g["logits"]
+    rng = np.random.default_rng(k + 100)
+    rows = _sample_tokens(N, y, w.ignore_index, rng)
+    Z = orc.logits_rows(h64[rows], W64, w.softcap)
+    got = lg[torch.as_tensor(rows, device=lg.device)].double().cpu().numpy()
+    err = np.abs(got - Z)
+    tol = gu.logits_tolerance(w, rows)
+    assert (err <= tol).all(), f"max err/tol {(err / tol).max():.3f}"
+    print(f"{label}: sampled logits max err {err.max():.3e} (max tol ratio "
+          f"{(err / tol).max():.3f})", flush=True)
+    worst = 0.0
+    for r0 in range(0, N, 1024):
+        blk = lg[r0:r0 + 1024].double()
+        lse_of = torch.logsumexp(blk, dim=1)
+        worst = max(worst, float((lse_of - g["lse"][r0:r0 + 1024].double()).abs().max()))
+    assert worst <= 2e-6 * max(1.0, float(np.abs(lse).max())), worst
+    b16 = lg.to(torch.bfloat16)
+    del g, lg
+    torch.cuda.empty_cache()
+    print(f"{label}: bf16 logits", flush=True)
+    gb = gu.run_gpu_forward_logits(w, logits_dtype=torch.bfloat16)
+    assert gb["loss_t"].view(torch.int32).item() == f["loss_t"].view(torch.int32).item()
+    assert torch.equal(gb["logits"].view(torch.int16), b16.view(torch.int16))
+    del gb, b16
+    torch.cuda.empty_cache()
+
+
+def test_large_vocab_forward_logits():
+    _forward_logits_check(3, "large_vocab")
+
+
+def test_softcapped_forward_logits():
+    _forward_logits_check(4, "softcapped")
+
+
 def test_softcapped_full():
     w = _case(4)[0]
     g = gu.run_gpu(w)

@@ -21,7 +21,7 @@ def _gpu():
     yield
 
 
-@pytest.mark.parametrize("mode", ["step", "nr", "forward", "f32grad"])
+@pytest.mark.parametrize("mode", ["step", "nr", "forward", "f32grad", "logits"])
 def test_graph_replays_match_eager(mode, monkeypatch):
     import lm_head_linear_amd as m
     monkeypatch.setenv("FLCE_VCHUNK", "512")          # several backward chunks
@@ -39,13 +39,19 @@ def test_graph_replays_match_eager(mode, monkeypatch):
     lse = torch.empty(N, dtype=torch.float32, device=dev)
     if mode == "nr":
         ws = torch.empty(m.flce_workspace_size_nr(N, H, V, W.dtype, 256), dtype=torch.uint8, device=dev)
-    elif mode == "forward":
+    elif mode in ("forward", "logits"):
         ws = torch.empty(m.flce_forward_workspace_size(N, H, V, W.dtype), dtype=torch.uint8, device=dev)
     else:
         ws = torch.empty(m.flce_workspace_size(N, H, V, W.dtype, gdt), dtype=torch.uint8, device=dev)
 
+    lg = torch.empty(N, V, dtype=torch.bfloat16, device=dev)
+    fwd_only = mode in ("forward", "logits")
+
     def call():
-        if mode == "forward":
+        if mode == "logits":
+            m.flce_forward_logits(h, W, y, softcap=w.softcap, workspace=ws, loss=loss,
+                                  num_tokens=nt, lse_out=lse, logits=lg)
+        elif mode == "forward":
             m.flce_forward(h, W, y, softcap=w.softcap, workspace=ws, loss=loss, num_tokens=nt,
                            lse_out=lse)
         else:
@@ -55,8 +61,10 @@ def test_graph_replays_match_eager(mode, monkeypatch):
 
     def snapshot():
         out = [loss.clone(), nt.clone(), lse.clone()]
-        if mode != "forward":
+        if not fwd_only:
             out += [dH.clone(), dW.clone()]
+        if mode == "logits":
+            out.append(lg.clone())
         return out
 
     call()
@@ -73,7 +81,7 @@ def test_graph_replays_match_eager(mode, monkeypatch):
         call()
     for rep in range(3):
         # overwrite the outputs and run unrelated eager work between replays
-        for t in [loss, lse] + ([dH, dW] if mode != "forward" else []):
+        for t in [loss, lse] + ([dH, dW] if not fwd_only else []) + ([lg] if mode == "logits" else []):
             t.fill_(float("nan"))
         nt.fill_(-1)
         junk = torch.randn(1024, 1024, device=dev) @ torch.randn(1024, 1024, device=dev)

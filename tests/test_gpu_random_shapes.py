@@ -2,12 +2,14 @@
 token counts, hidden sizes and vocabularies, both dtypes and reductions, the
 softcap, forced vocabulary chunks, and each entry point (the full step, float32
 gradients, the no-recompute variant with small token chunks, the forward
-only), at the tolerances the other parity tests use."""
+only, the forward with logits), at the tolerances the other parity tests
+use."""
 import numpy as np
 import pytest
 import torch
 
 import flce_inputs as fi
+from oracle import flce_oracle as orc
 from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
@@ -37,6 +39,8 @@ def _case(k):
     if w.reduction == "sum" and rng.random() < 0.3:
         w.num_label_tokens = int(rng.integers(1, 3 * N + 2))
     mode = ["step", "step", "f32grad", "nr", "forward"][k % 5] if dtype == torch.bfloat16 else "step"
+    if mode == "forward" and k % 10 == 9:
+        mode = "logits"
     vchunk = int(rng.choice([0, 256, 512])) if mode in ("step", "f32grad") else 0
     tchunk = int(rng.choice([0, 256])) if mode == "nr" else 0
     mb = float(rng.choice([1.0, 0.5]))
@@ -56,6 +60,20 @@ def test_random_case(k, monkeypatch):
         assert f["status"] == 0 and f["num_tokens"] == r.num_tokens
         gu.assert_loss(f["loss"], r.loss64)
         assert np.abs(gu.to_np64(f["lse"]) - r.lse).max() <= 1e-5 * max(1.0, np.abs(r.lse).max())
+        return
+    if mode == "logits":
+        ldt = torch.bfloat16 if k % 20 == 19 else torch.float32
+        f = gu.run_gpu_forward_logits(w, logits_dtype=ldt, pad=k % 3, mb_scale=mb)
+        assert f["status"] == 0 and f["num_tokens"] == r.num_tokens
+        gu.assert_loss(f["loss"], r.loss64)
+        assert np.abs(gu.to_np64(f["lse"]) - r.lse).max() <= 1e-5 * max(1.0, np.abs(r.lse).max())
+        Z = orc.logits_rows(w.h.reshape(-1, w.H).to(torch.float64).numpy(),
+                            w.W.to(torch.float64).numpy(), w.softcap)
+        tol = gu.logits_tolerance(w)
+        if ldt == torch.bfloat16:   # plus half a bf16 unit in the last place
+            tol = tol * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(Z)
+        assert (np.abs(gu.to_np64(f["logits"]) - Z) <= tol).all()
+        assert bool((f["buf"][:, w.V:] == gu.LOGITS_SENTINEL).all())
         return
     kw = {}
     if mode == "f32grad":

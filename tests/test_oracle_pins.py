@@ -381,3 +381,49 @@ def test_forward_rows_and_dW_rows_match_full():
         toks = np.array([1, 4, 25])
         dh = orc.dH_rows(h[toks], W, y[toks], lse[toks], c=full.c, softcap=s)
         np.testing.assert_allclose(dh, full.dH[toks], rtol=1e-11, atol=1e-15)
+
+
+# ---------------------------------------------------------------- logits output
+def test_logits_rows_brute_force():
+    """Each logit as a plain sum of products over the hidden dimension (exact
+    fsum) and the cap through math.tanh, element by element: catches a
+    transposed operand or a cap applied to the wrong quantity."""
+    h, W, _ = _rand_case(3, 5, 4, seed=41)
+    for s in (0.0, 0.7):
+        Z = orc.logits_rows(h, W, s)
+        assert Z.shape == (3, 4)
+        for i in range(3):
+            for v in range(4):
+                z = math.fsum(h[i, k] * W[v, k] for k in range(5))
+                if s > 0:
+                    z = s * math.tanh(z / s)
+                assert abs(Z[i, v] - z) <= 1e-14 * max(1.0, abs(z)), (i, v, s)
+
+
+def test_logits_rows_closed_forms():
+    # one-hot hidden state picks a column of W; the cap of atanh(1/2) with
+    # s = 1 is exactly 1/2
+    W = np.array([[0.25, -3.0], [2.0, 0.5], [-1.5, 1.0]])
+    Z = orc.logits_rows(np.array([[0.0, 1.0]]), W, 0.0)
+    np.testing.assert_array_equal(Z, [[-3.0, 0.5, 1.0]])
+    Z = orc.logits_rows(np.array([[math.atanh(0.5)]]), np.array([[1.0], [-1.0]]), 1.0)
+    np.testing.assert_allclose(Z, [[0.5, -0.5]], rtol=0, atol=1e-15)
+    assert not orc.logits_rows(np.ones((2, 3)), np.zeros((5, 3)), 2.0).any()
+
+
+def test_logits_rows_feed_the_loss():
+    """The logits are the ones the loss is formed from: their log-sum-exp is
+    the lse of the forward, the target entry the target logit, and the capped
+    values lie strictly inside (-s, s)."""
+    h, W, y = _rand_case(40, 12, 37, seed=42, ignore=6, w_std=2.0)
+    for s in (0.0, 3.0):
+        Z = orc.logits_rows(h, W, s)
+        lse, tok, zt = orc.forward_rows(h, W, y, IGN, s)
+        m = Z.max(axis=1)
+        np.testing.assert_allclose(m + np.log(np.exp(Z - m[:, None]).sum(axis=1)), lse,
+                                   rtol=1e-14)
+        valid = y != IGN
+        np.testing.assert_allclose(Z[valid, y[valid]], zt[valid], rtol=1e-15)
+        np.testing.assert_allclose(lse[valid] - Z[valid, y[valid]], tok[valid], rtol=1e-12)
+        if s > 0:
+            assert np.abs(Z).max() < s
