@@ -535,14 +535,19 @@ struct EpiLse {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t t = n0 + acc_col(wn, j, lane);
+      // the column's 64 logits, softcapped and masked past V, in registers of
+      // their own (the accumulators are not written back unless the logits
+      // are stored)
+      float z[4][16];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float z = acc[i][j][r];
-          if (SOFTCAP) z = softcap * tanh_fast(z * inv_softcap);
+          float x = acc[i][j][r];
+          if (SOFTCAP) x = softcap * tanh_fast(x * inv_softcap);
           const int64_t v = m0 + acc_row(wm, i, r, lane);
-          acc[i][j][r] = v < V ? z : -INFINITY;
+          z[i][r] = v < V ? x : -INFINITY;
+          if (OUT != kNoLogits) acc[i][j][r] = z[i][r];
         }
       // target logit: the one lane holding (y_t, t) writes it
       const int64_t y = t < N ? labels[t] : ignore_index;
@@ -555,23 +560,29 @@ struct EpiLse {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) val = (i == ti && r == tr) ? acc[i][j][r] : val;
+            for (int r = 0; r < 16; ++r) val = (i == ti && r == tr) ? z[i][r] : val;
           zt[t] = val;
         }
       }
-      float m = -INFINITY;
+      // max and sum in four independent chains (r % 4), then combined
+      float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[i][j][r]);
+        for (int r = 0; r < 16; ++r) mq[r & 3] = fmaxf(mq[r & 3], z[i][r]);
+      float m = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
       m = fmaxf(m, __shfl_xor(m, 32));
+      // sum of exp(z - m) = sum of 2^(z log2 e - m log2 e), one fma per element
       float s = 0.f;
       if (m != -INFINITY) {
+        const float mb = m * kLog2e;
+        float sq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            s += __builtin_amdgcn_exp2f((acc[i][j][r] - m) * kLog2e);
+            sq[r & 3] += __builtin_amdgcn_exp2f(fmaf(z[i][r], kLog2e, -mb));
+        s = (sq[0] + sq[1]) + (sq[2] + sq[3]);
       }
       s += __shfl_xor(s, 32);
       mx[j] = m;
