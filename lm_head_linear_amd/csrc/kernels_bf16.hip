@@ -935,9 +935,10 @@ template <class Pass>
 __device__ __forceinline__ void staged_rows(f32x16 (&acc)[4][4], int wm, int wn, int lane,
                                             char* smem, Pass& pass) {
   float* reg = reinterpret_cast<float*>(smem + (wm + 2 * wn) * kWaveScratch);
+  pass.prefetch(0, lane);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    pass.prefetch(i, lane);
+    if (i + 1 < 4) pass.prefetch(i + 1, lane);     // in flight while block i is staged
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -1027,21 +1028,25 @@ struct EpiDH {
   struct Pass {
     const EpiDH& e;
     int64_t r0, c0;
-    float4 prev[16];
+    float4 prev[2][16];  // the running sums of row blocks i and i + 1
     __device__ __forceinline__ void prefetch(int i, int lane) {
       if (FIRST) return;
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int idx = q * 64 + lane, row = idx >> 5, c4 = idx & 31;
         const int64_t m = r0 + i * 32 + row, n = c0 + 4 * c4;
-        prev[q] = (m < e.N && n < e.H) ? *reinterpret_cast<const float4*>(e.acc32 + m * e.H + n)
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+        prev[i & 1][q] = (m < e.N && n < e.H)
+                             ? *reinterpret_cast<const float4*>(e.acc32 + m * e.H + n)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
     __device__ __forceinline__ void store(int i, int q, int row, int col, float4 v) {
       const int64_t m = r0 + i * 32 + row, n = c0 + col;
       if (m >= e.N || n >= e.H) return;
-      if (!FIRST) { v.x += prev[q].x; v.y += prev[q].y; v.z += prev[q].z; v.w += prev[q].w; }
+      if (!FIRST) {
+        const float4 o = prev[i & 1][q];
+        v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+      }
       if (LAST) {
         *reinterpret_cast<uint2*>(e.dH + m * e.H + n) =
             make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
