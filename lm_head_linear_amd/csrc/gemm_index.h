@@ -44,9 +44,22 @@ enum Buf : int { kBufW = 0, kBufH = 1, kBufG = 2 };
 // Geometry of one operand. N form: stored [rows][K] (K contiguous); T form:
 // stored [K][rows] (rows contiguous). `ld` = elements between stored rows.
 // A T-form operand needs rows % 8 == 0 (16-byte column chunks).
+// blk != 0: the operand is stored in 32-wide blocks instead (the logit
+// gradient G): a token-by-vocabulary matrix kept as [vocab / 32][tokens][32],
+// blk elements per block (tokens x 32). As an N-form operand (rows = tokens,
+// K = vocabulary, 32-k stages) each row of a stage tile is then 64 bytes of
+// one 16-KiB-aligned run of 256 rows; as a T-form operand (K = tokens, rows =
+// vocabulary) each k-row is 8 runs of 64 bytes, the k-rows of a block
+// adjacent. ld is then 32.
 struct Geom {
   int64_t ld, rows, K;
+  int64_t blk = 0;
 };
+
+// Element (t, v) of a blocked token-by-vocabulary matrix.
+FLCE_HD int64_t blocked_offset(int64_t t, int64_t v, int64_t blk) {
+  return (v >> 5) * blk + t * 32 + (v & 31);
+}
 
 // One GEMM launch: C[M][Nn] = A . B^T over K, A and B given as (buffer,
 // element offset, geometry, form).
@@ -72,21 +85,26 @@ inline int64_t chunk_rows(const Plan& p, int64_t c) {
   return (p.V - v0) < p.vchunk ? (p.V - v0) : p.vchunk;
 }
 
+// Elements per 32-column block of the blocked G chunk: its token rows (ldg,
+// a multiple of 8) times 32.
+inline int64_t g_block(const Plan& p) { return p.ldg * 32; }
+
 inline Launch backward_launch(const Plan& p, int64_t c, int which, int part = 0) {
   const int64_t v0 = c * p.vchunk, vcur = chunk_rows(p, c);
   const int64_t g_off = int64_t(part) * p.vchunk * p.ldg;
   if (which == 0)  // Z^T[chunk] = W[chunk] . h^T, then the gradient epilogue
     return Launch{vcur, p.N, p.H, kFormN, kFormN, kBufW, kBufH, v0 * p.H, 0,
                   Geom{p.H, vcur, p.H}, Geom{p.H, p.N, p.H}};
-  // G is stored token-major, G[t][v - v0] with row length vchunk (a multiple
-  // of 8; columns from vcur to the row end are never multiplied into a
-  // stored output).
+  // G is stored blocked (g_block(p) elements per 32 vocabulary columns; see
+  // Geom): G[t][v - v0] at blocked_offset(t, v - v0, g_block(p)). Columns
+  // from vcur to vchunk are never multiplied into a stored output.
+  const int64_t blk = g_block(p);
   if (which == 1)  // dW[chunk] = G[:, chunk]^T . h  (K = tokens)
     return Launch{vcur, p.H, p.N, kFormT, kFormT, kBufG, kBufH, g_off, 0,
-                  Geom{p.vchunk, p.vchunk, p.N}, Geom{p.H, p.H, p.N}};
+                  Geom{32, p.vchunk, p.N, blk}, Geom{p.H, p.H, p.N}};
   // dH += G[:, chunk] . W[chunk]  (K = chunk rows)
   return Launch{p.N, p.H, vcur, kFormN, kFormT, kBufG, kBufW, g_off, v0 * p.H,
-                Geom{p.vchunk, p.N, vcur}, Geom{p.H, p.H, vcur}};
+                Geom{32, p.N, vcur, blk}, Geom{p.H, p.H, vcur}};
 }
 
 // No-recompute variant, token chunk c: tokens [t0, t0 + nt) with t0 = c nc.
@@ -163,10 +181,12 @@ FLCE_HD int lds_byte_t(int k, int col) {
 // column chunks (T form) past the edge are clamped to the last valid one:
 // their products land outside the output and are never stored.
 FLCE_HD int64_t direct_base(int form, const Geom& g, int64_t row0) {
-  return form == kFormN ? row0 * g.ld : row0;
+  if (form == kFormN) return row0 * g.ld;
+  return g.blk ? (row0 >> 5) * g.blk : row0;      // row0 is a multiple of 256
 }
 FLCE_HD int64_t direct_kstep(int form, const Geom& g, int sk) {
-  return form == kFormN ? int64_t(sk) : int64_t(sk) * g.ld;
+  if (form == kFormN) return g.blk ? int64_t(sk >> 5) * g.blk : int64_t(sk);
+  return int64_t(sk) * g.ld;
 }
 FLCE_HD int64_t direct_lane(int form, const Geom& g, int64_t row0, int wave, int lane, int q,
                             int sk) {
@@ -183,7 +203,7 @@ FLCE_HD int64_t direct_lane(int form, const Geom& g, int64_t row0, int wave, int
   const int c = (lane & 31) ^ swz_t(kr);
   int64_t col = 8 * c;
   if (row0 + col > g.rows - 8) col = g.rows - 8 - row0;
-  return kr * g.ld + col;
+  return g.blk ? (col >> 5) * g.blk + kr * 32 + (col & 31) : kr * g.ld + col;
 }
 
 // Register path of a partial last stage tile: thread tid's load i covers
@@ -194,11 +214,11 @@ FLCE_HD bool tail_src(int form, const Geom& g, int64_t row0, int64_t k0, int z, 
   if (form == kFormN) {  // z -> (row z / cpr, chunk z % cpr)
     const int cpr = sk / 8;
     const int64_t gr = row0 + z / cpr, gk = k0 + 8 * (z % cpr);
-    off = gr * g.ld + gk;
+    off = g.blk ? blocked_offset(gr, gk, g.blk) : gr * g.ld + gk;
     return gr < g.rows && gk < g.K;
   }
   const int64_t gk = k0 + (z >> 5), gm = row0 + 8 * (z & 31);  // (k-row z / 32, chunk z % 32)
-  off = gk * g.ld + gm;
+  off = g.blk ? blocked_offset(gk, gm, g.blk) : gk * g.ld + gm;
   return gk < g.K && gm < g.rows;
 }
 

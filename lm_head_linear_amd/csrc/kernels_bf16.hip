@@ -259,10 +259,15 @@ __device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], const StepFrags& cur
   interleave_hints<FA, FB, LOADS ? 2 * L : 0>();
 }
 
-template <int FA, int FB, class Epi>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A, Operand B, int64_t M,
+template <int FA, int FB, class Epi, bool BA>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A_, Operand B_, int64_t M,
                                                       int64_t Nn, int64_t K, int group_m,
                                                       Epi epi) {
+  // BA: operand A is the blocked G (gemm::Geom). Fixing blk at compile time
+  // for the dense operands lets the address arithmetic drop the blocked case.
+  Operand A = A_, B = B_;
+  if constexpr (!BA) A.g.blk = 0;
+  B.g.blk = 0;
   constexpr int SK = gemm::stage_k(FA, FB);
   constexpr int kStages = gemm::num_stages(FA, FB);
   constexpr int L = gemm::loads_per_operand(SK);
@@ -614,7 +619,8 @@ struct EpiLse {
 
 // ---- token-major bf16 stores of a tile held in the accumulators ----------
 // The tile's rows are vocabulary ids, its columns tokens; the destination is
-// row-major by token: dst[t][v] with row length ld. Each wave stages its
+// row-major by token, dst[t][v] with row length ld, or (BLOCKED) blocked,
+// dst[blocked_offset(t, v, blk)]. Each wave stages its
 // 128 x 128 block in its own 32 KiB of LDS as [token][vocab] (a lane packs
 // its 4 consecutive vocab values into 8 bytes; 8-byte slots XOR-swizzled by
 // token), then writes whole 16-byte runs of token rows; columns t >= nt and
@@ -636,11 +642,12 @@ __device__ __forceinline__ int target_slot(int d, int tl) {
   return tl * 256 + (((i * 8 + 2 * rq + half) ^ (tl & 31)) * 8) + 2 * e;
 }
 
-template <bool LO, bool PATCH = false>
+template <bool LO, bool PATCH = false, bool BLOCKED = false>
 __device__ __forceinline__ void store_token_major(const f32x16 (&acc)[4][4], char* smem, int wm,
                                                   int wn, int lane, uint16_t* dst, int64_t ld,
                                                   int64_t m0, int64_t n0, int64_t nt,
-                                                  int64_t nv, const TargetPatch* patch = nullptr) {
+                                                  int64_t nv, const TargetPatch* patch = nullptr,
+                                                  int64_t blk = 0) {
   const int half = lane >> 5;
   char* reg = smem + (wm + 2 * wn) * kWaveScratch;
 #pragma unroll
@@ -672,23 +679,40 @@ __device__ __forceinline__ void store_token_major(const f32x16 (&acc)[4][4], cha
       }
   }
   __syncthreads();
+  if constexpr (BLOCKED) {
+    // Blocked destination (dst[blocked_offset(t, v, blk)]): store q covers
+    // vocabulary block q / 8 of the wave (32 columns) for 16 tokens, one
+    // contiguous KiB.
 #pragma unroll 4
-  for (int q = 0; q < 32; ++q) {
-    const int idx = q * 64 + lane;
-    const int tl = idx >> 4, ch = idx & 15, x = tl & 31;
-    u32x4 v = *reinterpret_cast<const u32x4*>(reg + tl * 256 + (((2 * ch) ^ x) & ~1) * 8);
-    if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-    const int64_t t = n0 + wn * 128 + tl;
-    const int64_t vl = m0 + wm * 128 + 8 * ch;
-    if (t < nt && vl < nv) *reinterpret_cast<u32x4*>(dst + t * ld + vl) = v;
+    for (int q = 0; q < 32; ++q) {
+      const int tl = (q & 7) * 16 + (lane >> 2), ch = (q >> 3) * 4 + (lane & 3), x = tl & 31;
+      u32x4 v = *reinterpret_cast<const u32x4*>(reg + tl * 256 + (((2 * ch) ^ x) & ~1) * 8);
+      if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+      const int64_t t = n0 + wn * 128 + tl;
+      const int64_t vl = m0 + wm * 128 + 8 * ch;
+      if (t < nt && vl < nv)
+        *reinterpret_cast<u32x4*>(dst + gemm::blocked_offset(t, vl, blk)) = v;
+    }
+  } else {
+#pragma unroll 4
+    for (int q = 0; q < 32; ++q) {
+      const int idx = q * 64 + lane;
+      const int tl = idx >> 4, ch = idx & 15, x = tl & 31;
+      u32x4 v = *reinterpret_cast<const u32x4*>(reg + tl * 256 + (((2 * ch) ^ x) & ~1) * 8);
+      if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+      const int64_t t = n0 + wn * 128 + tl;
+      const int64_t vl = m0 + wm * 128 + 8 * ch;
+      if (t < nt && vl < nv) *reinterpret_cast<u32x4*>(dst + t * ld + vl) = v;
+    }
   }
 }
 
 // ---- backward epilogue: the logit gradient G for one vocabulary chunk ----
 // G[t, v] = c * valid_t * (exp(z'_tv - lse_t) - [v = y_t]) * dz'/dz, stored
-// bf16 token-major as G[t][v - v0] (row length ldgv). Tile rows are
-// chunk-relative vocab ids, columns tokens. G is formed in float32 in place
-// of the logits, then stored through store_token_major. SPLIT (float32
+// bf16 in 32-column blocks, G[t][v - v0] at blocked_offset(t, v - v0, gblk)
+// (see gemm::Geom: whole cache lines for the dW and dH loads that read it
+// back). Tile rows are chunk-relative vocab ids, columns tokens. G is formed
+// in float32 in place of the logits, then stored through store_token_major. SPLIT (float32
 // gradients) stores two bf16 chunks, G_hi = bf16(G) at g and
 // G_lo = bf16(G - G_hi) at g + lo_off.
 template <bool SOFTCAP, bool SPLIT>
@@ -697,7 +721,7 @@ struct EpiGrad {
   const float* lse;
   const float* zt;   // the forward's float32 target logits
   const Scalars* sc;
-  int64_t N, V, ignore_index, v0, vcur, ldgv;
+  int64_t N, V, ignore_index, v0, vcur, gblk;   // gblk: elements per block of G
   float softcap, inv_softcap;
   uint16_t* g;
   int64_t lo_off;   // elements from the hi to the lo chunk (SPLIT)
@@ -760,11 +784,12 @@ struct EpiGrad {
           }
         }
     }
-    store_token_major<false, true>(acc, smem, wm, wn, lane, g, ldgv, m0, n0, N, vcur, &tp);
+    store_token_major<false, true, true>(acc, smem, wm, wn, lane, g, 0, m0, n0, N, vcur, &tp,
+                                         gblk);
     if (SPLIT) {
       __syncthreads();                                 // the staging area is reused
-      store_token_major<true, true>(acc, smem, wm, wn, lane, g + lo_off, ldgv, m0, n0, N, vcur,
-                                    &tp);
+      store_token_major<true, true, true>(acc, smem, wm, wn, lane, g + lo_off, 0, m0, n0, N, vcur,
+                                          &tp, gblk);
     }
   }
 };
@@ -1076,7 +1101,8 @@ const uint16_t* buf_ptr(const Args& a, int buf) {
 // The tile count must fit the grid.
 bool operand_offsets_fit(int form, const gemm::Geom& g) {
   const int64_t reach = form == gemm::kFormN ? (g.rows - 1 < 255 ? g.rows - 1 : 255) * g.ld + 64
-                                             : 63 * g.ld + g.rows;
+                        : g.blk ? 7 * g.blk + 64 * 32
+                                : 63 * g.ld + g.rows;
   return reach >= 0 && 2 * reach + 16 <= int64_t(0xFFFFFFFF);
 }
 
@@ -1088,14 +1114,15 @@ bool launch_ok(const gemm::Launch& l) {
   return l.M > 0 && l.Nn > 0 && l.K > 0;
 }
 
-template <int FA, int FB, class Epi>
+template <int FA, int FB, bool BA = false, class Epi>
 hipError_t run_gemm(const gemm::Launch& l, const Args& a, const Epi& e, int kind,
                     const Launcher& L) {
   if (!launch_ok(l)) return hipErrorInvalidValue;
+  if ((l.a.blk != 0) != BA || l.b.blk != 0) return hipErrorInvalidValue;
   Operand A{buf_ptr(a, l.buf_a) + l.off_a, l.a};
   Operand B{buf_ptr(a, l.buf_b) + l.off_b, l.b};
   L.pre(kind);
-  hipLaunchKernelGGL((k_gemm<FA, FB, Epi>), dim3(unsigned(gemm::num_tiles(l.M, l.Nn))),
+  hipLaunchKernelGGL((k_gemm<FA, FB, Epi, BA>), dim3(unsigned(gemm::num_tiles(l.M, l.Nn))),
                      dim3(kThreads), 0, L.stream, A, B, l.M, l.Nn, l.K, gemm::kGroupM, e);
   L.post(kind);
   return hipGetLastError();
@@ -1139,12 +1166,12 @@ hipError_t bf16_backward_chunk_f32grad(const Plan& p, const Args& a, int64_t chu
   hipError_t err;
   if (a.softcap > 0.f) {
     EpiGrad<true, true> eg{a.labels, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
-                           p.vchunk, a.softcap, 1.f / a.softcap, g, lo_off};
+                           gemm::g_block(p), a.softcap, 1.f / a.softcap, g, lo_off};
     err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
                                                kGradLogits, L);
   } else {
     EpiGrad<false, true> eg{a.labels, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
-                            p.vchunk, 0.f, 0.f, g, lo_off};
+                            gemm::g_block(p), 0.f, 0.f, g, lo_off};
     err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
                                                kGradLogits, L);
   }
@@ -1152,21 +1179,21 @@ hipError_t bf16_backward_chunk_f32grad(const Plan& p, const Args& a, int64_t chu
   for (int part = 0; part < 2 && err == hipSuccess; ++part) {
     const gemm::Launch lw = gemm::backward_launch(p, chunk, 1, part);
     if (part == 0 && !a.accumulate_dW)
-      err = run_gemm<gemm::kFormT, gemm::kFormT>(lw, a, EpiDW32<false>{dW, p.H, v0, vcur},
-                                                 kGemmDW, L);
+      err = run_gemm<gemm::kFormT, gemm::kFormT, true>(lw, a, EpiDW32<false>{dW, p.H, v0, vcur},
+                                                       kGemmDW, L);
     else
-      err = run_gemm<gemm::kFormT, gemm::kFormT>(lw, a, EpiDW32<true>{dW, p.H, v0, vcur},
-                                                 kGemmDW, L);
+      err = run_gemm<gemm::kFormT, gemm::kFormT, true>(lw, a, EpiDW32<true>{dW, p.H, v0, vcur},
+                                                       kGemmDW, L);
   }
   float* dH = static_cast<float*>(a.dH);
   for (int part = 0; part < 2 && err == hipSuccess; ++part) {
     const gemm::Launch lh = gemm::backward_launch(p, chunk, 2, part);
     if (chunk == 0 && part == 0)
-      err = run_gemm<gemm::kFormN, gemm::kFormT>(lh, a, EpiDH<true, false>{nullptr, dH, p.N, p.H},
-                                                 kGemmDH, L);
+      err = run_gemm<gemm::kFormN, gemm::kFormT, true>(
+          lh, a, EpiDH<true, false>{nullptr, dH, p.N, p.H}, kGemmDH, L);
     else
-      err = run_gemm<gemm::kFormN, gemm::kFormT>(lh, a, EpiDH<false, false>{nullptr, dH, p.N, p.H},
-                                                 kGemmDH, L);
+      err = run_gemm<gemm::kFormN, gemm::kFormT, true>(
+          lh, a, EpiDH<false, false>{nullptr, dH, p.N, p.H}, kGemmDH, L);
   }
   return err;
 }
@@ -1180,12 +1207,12 @@ hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, cons
   hipError_t err;
   if (a.softcap > 0.f) {
     EpiGrad<true, false> eg{a.labels, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
-                            p.vchunk, a.softcap, 1.f / a.softcap, g, 0};
+                            gemm::g_block(p), a.softcap, 1.f / a.softcap, g, 0};
     err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
                                                kGradLogits, L);
   } else {
     EpiGrad<false, false> eg{a.labels, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
-                             p.vchunk, 0.f, 0.f, g, 0};
+                             gemm::g_block(p), 0.f, 0.f, g, 0};
     err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
                                                kGradLogits, L);
   }
@@ -1194,25 +1221,27 @@ hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, cons
   uint16_t* dW = static_cast<uint16_t*>(a.dW);
   const gemm::Launch lw = gemm::backward_launch(p, chunk, 1);
   if (a.accumulate_dW)
-    err = run_gemm<gemm::kFormT, gemm::kFormT>(lw, a, EpiDW<true>{dW, p.H, v0, vcur}, kGemmDW, L);
+    err = run_gemm<gemm::kFormT, gemm::kFormT, true>(lw, a, EpiDW<true>{dW, p.H, v0, vcur},
+                                                     kGemmDW, L);
   else
-    err = run_gemm<gemm::kFormT, gemm::kFormT>(lw, a, EpiDW<false>{dW, p.H, v0, vcur}, kGemmDW, L);
+    err = run_gemm<gemm::kFormT, gemm::kFormT, true>(lw, a, EpiDW<false>{dW, p.H, v0, vcur},
+                                                     kGemmDW, L);
   if (err != hipSuccess) return err;
   // 3) dH (+)= G[:, chunk] . W[chunk], chunks in order
   uint16_t* dH = static_cast<uint16_t*>(a.dH);
   const gemm::Launch lh = gemm::backward_launch(p, chunk, 2);
   const bool first = chunk == 0, last = chunk == p.n_chunks - 1;
   if (first && last)
-    return run_gemm<gemm::kFormN, gemm::kFormT>(lh, a, EpiDH<true, true>{dH, a.dh_acc, p.N, p.H},
-                                                kGemmDH, L);
+    return run_gemm<gemm::kFormN, gemm::kFormT, true>(
+        lh, a, EpiDH<true, true>{dH, a.dh_acc, p.N, p.H}, kGemmDH, L);
   if (first)
-    return run_gemm<gemm::kFormN, gemm::kFormT>(lh, a, EpiDH<true, false>{dH, a.dh_acc, p.N, p.H},
-                                                kGemmDH, L);
+    return run_gemm<gemm::kFormN, gemm::kFormT, true>(
+        lh, a, EpiDH<true, false>{dH, a.dh_acc, p.N, p.H}, kGemmDH, L);
   if (last)
-    return run_gemm<gemm::kFormN, gemm::kFormT>(lh, a, EpiDH<false, true>{dH, a.dh_acc, p.N, p.H},
-                                                kGemmDH, L);
-  return run_gemm<gemm::kFormN, gemm::kFormT>(lh, a, EpiDH<false, false>{dH, a.dh_acc, p.N, p.H},
-                                              kGemmDH, L);
+    return run_gemm<gemm::kFormN, gemm::kFormT, true>(
+        lh, a, EpiDH<false, true>{dH, a.dh_acc, p.N, p.H}, kGemmDH, L);
+  return run_gemm<gemm::kFormN, gemm::kFormT, true>(
+      lh, a, EpiDH<false, false>{dH, a.dh_acc, p.N, p.H}, kGemmDH, L);
 }
 
 }  // namespace flce

@@ -97,8 +97,56 @@ static void check_lds_layout() {
 // Same predicate as the library's launch check: the 32-bit lane offsets fit.
 static bool offsets_fit(int form, const Geom& g) {
   const int64_t reach = form == kFormN ? (g.rows - 1 < 255 ? g.rows - 1 : 255) * g.ld + 64
-                                       : 63 * g.ld + g.rows;
+                        : g.blk ? 7 * g.blk + 64 * 32
+                                : 63 * g.ld + g.rows;
   return reach >= 0 && 2 * reach + 16 <= int64_t(0xFFFFFFFF);
+}
+
+// The blocked geometry (the logit gradient G) fetches, for every lane, load
+// and stage tile, the same logical element as the dense geometry of the same
+// matrix, and its tail path reads the same elements. Dense: G[t][v] at
+// t * ld + v; blocked: at blocked_offset(t, v, blk).
+static void check_blocked_matches_dense() {
+  const int64_t T = 700, Vc = 1024, ld = Vc, blk = 704 * 32;   // 704: T rounded up to 8
+  auto dense_tv = [&](int64_t e, int64_t& t, int64_t& v) { t = e / ld; v = e % ld; };
+  auto blocked_tv = [&](int64_t e, int64_t& t, int64_t& v) {
+    v = (e / blk) * 32 + (e % blk) % 32;
+    t = (e % blk) / 32;
+  };
+  const int sk = 32;
+  // N form (dH: rows = tokens, K = vocabulary) and T form (dW: K = tokens,
+  // rows = vocabulary)
+  for (int form : {int(kFormN), int(kFormT)}) {
+    const Geom gd = form == kFormN ? Geom{ld, T, Vc} : Geom{ld, Vc, T};
+    const Geom gb = form == kFormN ? Geom{32, T, Vc, blk} : Geom{32, Vc, T, blk};
+    const int64_t rows = form == kFormN ? T : Vc, K = form == kFormN ? Vc : T;
+    for (int64_t row0 = 0; row0 < rows; row0 += kBM)
+      for (int64_t kt : {int64_t(0), int64_t(1), K / sk - 1}) {
+        for (int wave = 0; wave < 4; ++wave)
+          for (int lane = 0; lane < 64; ++lane)
+            for (int q = 0; q < loads_per_operand(sk); ++q) {
+              const int64_t ed = direct_base(form, gd, row0) + kt * direct_kstep(form, gd, sk) +
+                                 direct_lane(form, gd, row0, wave, lane, q, sk);
+              const int64_t eb = direct_base(form, gb, row0) + kt * direct_kstep(form, gb, sk) +
+                                 direct_lane(form, gb, row0, wave, lane, q, sk);
+              int64_t t1, v1, t2, v2;
+              dense_tv(ed, t1, v1);
+              blocked_tv(eb, t2, v2);
+              if (t1 != t2 || v1 != v2) fail("blocked load differs from dense", form, t1 * ld + v1, t2 * ld + v2);
+            }
+        for (int z = 0; z < 256 * tail_loads(sk); ++z) {
+          int64_t od, ob;
+          const bool vd = tail_src(form, gd, row0, kt * sk, z, sk, od);
+          const bool vb = tail_src(form, gb, row0, kt * sk, z, sk, ob);
+          if (vd != vb) { fail("blocked tail validity", form, z, kt); continue; }
+          if (!vd) continue;
+          int64_t t1, v1, t2, v2;
+          dense_tv(od, t1, v1);
+          blocked_tv(ob, t2, v2);
+          if (t1 != t2 || v1 != v2) fail("blocked tail differs from dense", form, z, kt);
+        }
+      }
+  }
 }
 
 static void check_launch(const Plan& p, const Launch& l) {
@@ -133,7 +181,8 @@ int main(int argc, char** argv) {
       {2048, 1024, 32000, 0}, {4096, 4096, 131072, 0}, {8192, 4096, 131072, 0},
       {8192, 3584, 256000, 0}, {16384, 4096, 131072, 0}};
   check_lds_layout();
-  std::printf("lds layout: %s\n", failures ? "FAILURES" : "ok");
+  check_blocked_matches_dense();
+  std::printf("lds layout and blocked G: %s\n", failures ? "FAILURES" : "ok");
   if (argc == 5) shapes = {{std::atoll(argv[1]), std::atoll(argv[2]), std::atoll(argv[3]), std::atoll(argv[4])}};
   for (const Shape& s : shapes) {
     if (s.vc > 0) {
