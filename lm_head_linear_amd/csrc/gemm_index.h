@@ -109,12 +109,16 @@ inline Launch backward_launch(const Plan& p, int64_t c, int which, int part = 0)
 
 // No-recompute variant, token chunk c: tokens [t0, t0 + nt) with t0 = c nc.
 // 0: forward over the whole vocabulary (probabilities stored in the G
-// buffer, [nc][vp] token-major); 1: dW (+)= G^T . h[chunk] (K = the chunk's
-// tokens); 2: dH[chunk] = G . W (K = V, complete in one launch).
+// buffer, vp columns blocked by 32); 1: dW (+)= G^T . h[chunk] (K = the
+// chunk's tokens); 2: dH[chunk] = G . W (K = V, complete in one launch).
 inline int64_t nr_chunk_tokens(const Plan& p, int64_t c) {
   const int64_t t0 = c * p.nc;
   return (p.N - t0) < p.nc ? (p.N - t0) : p.nc;
 }
+
+// The chunk's probabilities / G are blocked like the G chunk of the recompute
+// path (see Geom), nc token rows per 32-column block.
+inline int64_t nr_block(const Plan& p) { return p.nc * 32; }
 
 inline Launch nr_launch(const Plan& p, int64_t c, int which) {
   const int64_t t0 = c * p.nc, nt = nr_chunk_tokens(p, c);
@@ -123,9 +127,9 @@ inline Launch nr_launch(const Plan& p, int64_t c, int which) {
                   Geom{p.H, p.V, p.H}, Geom{p.H, nt, p.H}};
   if (which == 1)
     return Launch{p.V, p.H, nt, kFormT, kFormT, kBufG, kBufH, 0, t0 * p.H,
-                  Geom{p.vp, p.vp, nt}, Geom{p.H, p.H, nt}};
+                  Geom{32, p.vp, nt, nr_block(p)}, Geom{p.H, p.H, nt}};
   return Launch{nt, p.H, p.V, kFormN, kFormT, kBufG, kBufW, 0, 0,
-                Geom{p.vp, nt, p.V}, Geom{p.H, p.H, p.V}};
+                Geom{32, nt, p.V, nr_block(p)}, Geom{p.H, p.H, p.V}};
 }
 
 inline int64_t num_tiles(int64_t M, int64_t Nn) {

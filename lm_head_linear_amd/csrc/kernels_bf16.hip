@@ -797,7 +797,7 @@ struct EpiGrad {
 // ---- forward epilogue of the no-recompute variant ------------------------
 // As EpiLse, and it also keeps the probabilities: with the tile max Mx of
 // each token shared by the two waves of its column, it stores
-// P'[t][v] = exp(z'_tv - Mx) (<= 1) as bf16, token-major with row length ldp,
+// P'[t][v] = exp(z'_tv - Mx) (<= 1) as bf16 at blocked_offset(t, v, pblk),
 // and the partial (Mx, sum of P') of the tile. G follows later without
 // recomputing the logits: G = c (P' exp(Mx - lse) - [v = y]) dz'/dz.
 template <bool SOFTCAP>
@@ -808,8 +808,8 @@ struct EpiLseP {
   float2* part;  // [n_voc_tiles][ld_part]: (max, sum of exp(x - max)) of the tile
   int64_t ld_part;
   float* zt;     // target logit (softcapped), one writer per non-ignored token
-  uint16_t* probs;
-  int64_t ldp;
+  uint16_t* probs;  // blocked, pblk elements per 32 vocabulary columns
+  int64_t pblk;
 
   __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm,
                                              int wn, int lane, char* smem) const {
@@ -888,7 +888,8 @@ struct EpiLseP {
       }
     }
     __syncthreads();                                  // sums read before the staging reuses LDS
-    store_token_major<false>(acc, smem, wm, wn, lane, probs, ldp, m0, n0, N, V);
+    store_token_major<false, false, true>(acc, smem, wm, wn, lane, probs, 0, m0, n0, N, V,
+                                          nullptr, pblk);
   }
 };
 
@@ -897,25 +898,29 @@ struct EpiLseP {
 // with M_tv the max of v's vocabulary tile for token t (the forward partial).
 // The target element is formed from the float32 target logit instead:
 // c (exp(z'_ty - lse_t) - 1) dz'/dz. With a softcap, dz'/dz = 1 - (z'/s)^2 and
-// z' = M + ln P' elsewhere. One thread converts 8 consecutive v (16 bytes).
+// z' = M + ln P' elsewhere. The buffer is blocked (gemm::blocked_offset, blk
+// elements per 32 columns); in block b (blockIdx.y, then strided), thread i
+// converts the 8 consecutive elements of run i of the block's used part
+// [nt tokens][4 runs], so a wave reads and writes one contiguous KiB.
 template <bool SOFTCAP>
 __global__ __launch_bounds__(256) void k_probs_to_grad(
-    uint16_t* __restrict__ gp, int64_t ldp, int64_t nt, int64_t V,
+    uint16_t* __restrict__ gp, int64_t blk, int64_t nt, int64_t V,
     const float2* __restrict__ part, int64_t ld_part, const float* __restrict__ lse,
     const float* __restrict__ zt, const int64_t* __restrict__ labels, int64_t ignore_index,
     const Scalars* __restrict__ sc, float inv_softcap) {
-  const int64_t runs = (V + 7) / 8;
-  const int64_t r = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (r >= runs) return;
-  const int64_t v0 = r * 8;
-  for (int64_t t = blockIdx.y; t < nt; t += gridDim.y) {
-    uint16_t* row = gp + t * ldp + v0;
-    const int64_t y = labels[t];
-    const float coef = y == ignore_index ? 0.f : ((y < 0 || y >= V) ? NAN : sc->c32);
-    const float l = lse[t];
+  const int64_t rem = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (rem >= nt * 4) return;
+  const int64_t t = rem >> 2;
+  const int64_t y = labels[t];
+  const float coef = y == ignore_index ? 0.f : ((y < 0 || y >= V) ? NAN : sc->c32);
+  const float l = lse[t];
+  const int64_t nb = (V + 31) / 32;
+  for (int64_t b = blockIdx.y; b < nb; b += gridDim.y) {
+    const int64_t v0 = b * 32 + (rem & 3) * 8;
+    uint16_t* run = gp + b * blk + t * 32 + (rem & 3) * 8;
     const float M = part[(v0 / kBM) * ld_part + t].x;
     const float scale = __builtin_amdgcn_exp2f((M - l) * kLog2e);
-    const u32x4 in = *reinterpret_cast<const u32x4*>(row);
+    const u32x4 in = *reinterpret_cast<const u32x4*>(run);
     float g[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -939,7 +944,7 @@ __global__ __launch_bounds__(256) void k_probs_to_grad(
       }
       g[e] = v < V ? x : 0.f;
     }
-    *reinterpret_cast<u32x4*>(row) = u32x4{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]),
+    *reinterpret_cast<u32x4*>(run) = u32x4{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]),
                                            pack_bf16x2(g[4], g[5]), pack_bf16x2(g[6], g[7])};
   }
 }
@@ -1254,11 +1259,11 @@ hipError_t bf16_nr_forward_chunk(const Plan& p, const Args& a, int64_t c, const 
   uint16_t* probs = static_cast<uint16_t*>(a.g);
   if (a.softcap > 0.f) {
     EpiLseP<true> e{a.labels + t0, nt, p.V, a.ignore_index, a.softcap, 1.f / a.softcap, a.part,
-                    p.ld_part, a.zt, probs, p.vp};
+                    p.ld_part, a.zt, probs, gemm::nr_block(p)};
     return run_gemm<gemm::kFormN, gemm::kFormN>(l, a, e, kLseFwd, L);
   }
   EpiLseP<false> e{a.labels + t0, nt, p.V, a.ignore_index, 0.f, 0.f, a.part, p.ld_part, a.zt,
-                   probs, p.vp};
+                   probs, gemm::nr_block(p)};
   return run_gemm<gemm::kFormN, gemm::kFormN>(l, a, e, kLseFwd, L);
 }
 
@@ -1266,15 +1271,16 @@ hipError_t bf16_nr_backward_chunk(const Plan& p, const Args& a, int64_t c, const
   const int64_t t0 = c * p.nc, nt = gemm::nr_chunk_tokens(p, c);
   uint16_t* g = static_cast<uint16_t*>(a.g);
   // 1) G in place of the probabilities
-  const int64_t runs = (p.V + 7) / 8;
-  const dim3 grid(unsigned((runs + 255) / 256), unsigned(nt < 65535 ? nt : 65535));
+  const int64_t nb = (p.V + 31) / 32;
+  const dim3 grid(unsigned((nt * 4 + 255) / 256), unsigned(nb < 512 ? nb : 512));
+  const int64_t blk = gemm::nr_block(p);
   L.pre(kProbsToGrad);
   if (a.softcap > 0.f)
-    hipLaunchKernelGGL(k_probs_to_grad<true>, grid, dim3(256), 0, L.stream, g, p.vp, nt, p.V,
+    hipLaunchKernelGGL(k_probs_to_grad<true>, grid, dim3(256), 0, L.stream, g, blk, nt, p.V,
                        a.part, p.ld_part, a.lse, a.zt, a.labels + t0, a.ignore_index, a.sc,
                        1.f / a.softcap);
   else
-    hipLaunchKernelGGL(k_probs_to_grad<false>, grid, dim3(256), 0, L.stream, g, p.vp, nt, p.V,
+    hipLaunchKernelGGL(k_probs_to_grad<false>, grid, dim3(256), 0, L.stream, g, blk, nt, p.V,
                        a.part, p.ld_part, a.lse, a.zt, a.labels + t0, a.ignore_index, a.sc, 0.f);
   L.post(kProbsToGrad);
   hipError_t err = hipGetLastError();
@@ -1283,14 +1289,16 @@ hipError_t bf16_nr_backward_chunk(const Plan& p, const Args& a, int64_t c, const
   uint16_t* dW = static_cast<uint16_t*>(a.dW);
   const gemm::Launch lw = gemm::nr_launch(p, c, 1);
   if (c > 0 || a.accumulate_dW)
-    err = run_gemm<gemm::kFormT, gemm::kFormT>(lw, a, EpiDW<true>{dW, p.H, 0, p.V}, kGemmDW, L);
+    err = run_gemm<gemm::kFormT, gemm::kFormT, true>(lw, a, EpiDW<true>{dW, p.H, 0, p.V},
+                                                     kGemmDW, L);
   else
-    err = run_gemm<gemm::kFormT, gemm::kFormT>(lw, a, EpiDW<false>{dW, p.H, 0, p.V}, kGemmDW, L);
+    err = run_gemm<gemm::kFormT, gemm::kFormT, true>(lw, a, EpiDW<false>{dW, p.H, 0, p.V},
+                                                     kGemmDW, L);
   if (err != hipSuccess) return err;
   // 3) dH[chunk] = G . W over the whole vocabulary
   uint16_t* dH = static_cast<uint16_t*>(a.dH) + t0 * p.H;
-  return run_gemm<gemm::kFormN, gemm::kFormT>(gemm::nr_launch(p, c, 2), a,
-                                              EpiDH<true, true>{dH, nullptr, nt, p.H}, kGemmDH, L);
+  return run_gemm<gemm::kFormN, gemm::kFormT, true>(
+      gemm::nr_launch(p, c, 2), a, EpiDH<true, true>{dH, nullptr, nt, p.H}, kGemmDH, L);
 }
 
 }  // namespace flce
