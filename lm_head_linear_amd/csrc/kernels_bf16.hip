@@ -642,9 +642,11 @@ __device__ __forceinline__ int target_slot(int d, int tl) {
   return tl * 256 + (((i * 8 + 2 * rq + half) ^ (tl & 31)) * 8) + 2 * e;
 }
 
-template <bool LO, bool PATCH = false, bool BLOCKED = false>
-__device__ __forceinline__ void store_token_major(const f32x16 (&acc)[4][4], char* smem, int wm,
-                                                  int wn, int lane, uint16_t* dst, int64_t ld,
+// The value of accumulator element (i, j, r) is get(i, j, r): the element
+// itself, or a function of it formed as it is staged.
+template <bool LO, bool PATCH = false, bool BLOCKED = false, class Get>
+__device__ __forceinline__ void store_token_major(const Get& get, char* smem, int wm, int wn,
+                                                  int lane, uint16_t* dst, int64_t ld,
                                                   int64_t m0, int64_t n0, int64_t nt,
                                                   int64_t nv, const TargetPatch* patch = nullptr,
                                                   int64_t blk = 0) {
@@ -660,7 +662,7 @@ __device__ __forceinline__ void store_token_major(const f32x16 (&acc)[4][4], cha
         float v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          v[e] = acc[i][j][4 * rq + e];
+          v[e] = get(i, j, 4 * rq + e);
           if (LO) v[e] -= bf16_to_f32(f32_to_bf16(v[e]));
         }
         const uint32_t lo = pack_bf16x2(v[0], v[1]);
@@ -739,6 +741,7 @@ struct EpiGrad {
     const int half = lane >> 5;
     const int64_t vbase = v0 + m0 + wm * 128;           // global vocab id of block row 0
     TargetPatch tp;
+    float bias[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int tl = j * 32 + (lane & 31);             // token within the wave block
@@ -769,28 +772,36 @@ struct EpiGrad {
           }
         }
       }
-      const float bias = log2f(coef) - l * kLog2e;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float z = acc[i][j][r];
-          if (SOFTCAP) {
-            const float th = tanh_fast(z * inv_softcap);
-            acc[i][j][r] = __builtin_amdgcn_exp2f(fmaf(softcap * th, kLog2e, bias)) *
-                           (1.f - th * th);
-          } else {
-            acc[i][j][r] = __builtin_amdgcn_exp2f(fmaf(z, kLog2e, bias));
-          }
-        }
+      bias[j] = log2f(coef) - l * kLog2e;
     }
-    store_token_major<false, true, true>(acc, smem, wm, wn, lane, g, 0, m0, n0, N, vcur, &tp,
+    // G of element (i, j, r), from the logit in the accumulator
+    auto grad = [&](int i, int j, int r) {
+      const float z = acc[i][j][r];
+      if (SOFTCAP) {
+        const float th = tanh_fast(z * inv_softcap);
+        return __builtin_amdgcn_exp2f(fmaf(softcap * th, kLog2e, bias[j])) * (1.f - th * th);
+      }
+      return __builtin_amdgcn_exp2f(fmaf(z, kLog2e, bias[j]));
+    };
+    if (!SPLIT) {
+      // formed as it is staged, never written back to the accumulators
+      store_token_major<false, true, true>(grad, smem, wm, wn, lane, g, 0, m0, n0, N, vcur, &tp,
+                                           gblk);
+      return;
+    }
+    // two stores of the same values (hi, then lo): form them once, in place
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = grad(i, j, r);
+    auto held = [&](int i, int j, int r) { return acc[i][j][r]; };
+    store_token_major<false, true, true>(held, smem, wm, wn, lane, g, 0, m0, n0, N, vcur, &tp,
                                          gblk);
-    if (SPLIT) {
-      __syncthreads();                                 // the staging area is reused
-      store_token_major<true, true, true>(acc, smem, wm, wn, lane, g + lo_off, 0, m0, n0, N, vcur,
-                                          &tp, gblk);
-    }
+    __syncthreads();                                   // the staging area is reused
+    store_token_major<true, true, true>(held, smem, wm, wn, lane, g + lo_off, 0, m0, n0, N, vcur,
+                                        &tp, gblk);
   }
 };
 
@@ -888,7 +899,8 @@ struct EpiLseP {
       }
     }
     __syncthreads();                                  // sums read before the staging reuses LDS
-    store_token_major<false, false, true>(acc, smem, wm, wn, lane, probs, 0, m0, n0, N, V,
+    auto held = [&](int i, int j, int r) { return acc[i][j][r]; };
+    store_token_major<false, false, true>(held, smem, wm, wn, lane, probs, 0, m0, n0, N, V,
                                           nullptr, pblk);
   }
 };
