@@ -32,9 +32,12 @@ PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
 GEMM_KINDS = ("lse_fwd_gemm", "grad_logits_gemm", "dW_gemm", "dH_gemm")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_large_vocab.txt")
+# Every source of the library: the committed counters are used only while all
+# of them are unchanged.
 KERNEL_SOURCES = [os.path.join(ROOT, "lm_head_linear_amd", "csrc", f)
-                  for f in ("kernels_bf16.hip", "kernels_common.hip", "flce_api.hip",
-                            "flce_check.cpp", "flce_plan.h", "flce_internal.h")]
+                  for f in ("kernels_bf16.hip", "kernels_common.hip", "kernels_f32.hip",
+                            "flce_api.hip", "flce_check.cpp", "flce_plan.h", "flce_internal.h",
+                            "gemm_index.h")]
 
 
 def log(*a):
