@@ -6,7 +6,9 @@
 //   dW chunk  = G^T[chunk] . h                          (K = tokens)
 //   dH       += G[:, chunk] . W[chunk]                  (K = vocab chunk)
 // Workgroup tile 256 x 256, four waves of 128 x 128 each built from
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulate), MFMA steps of 32 k. Operands go
+// v_mfma_f32_16x16x32_bf16 (fp32 accumulate; 64 of them per wave and 32-k
+// step). Of the two bf16 matrix instructions this one holds a higher clock
+// under the chip's power limit at the same issue rate. Operands go
 // global -> LDS with direct-to-LDS loads (no registers) into XOR-swizzled
 // stages: 2 stages of 64 k when both operands are K-contiguous, 5 of 32 k
 // when both are transposed (dW), 4 of 32 k for dH. A K-contiguous operand's fragments are read with ds_read_b128;
@@ -15,10 +17,10 @@
 // registers or in memory.
 //
 // Tiles are computed with the vocabulary on the M side and tokens on the N
-// side for the logit tiles: a lane then owns one token column and 64 vocab
-// values of it, so the per-token max / sum-exp reductions of the forward
-// epilogue stay inside the lane (plus one swap between the two half-waves
-// and one exchange between the two waves of a column).
+// side for the logit tiles: a lane then owns 8 token columns and 32 vocab
+// values of each, so the per-token max / sum-exp reductions of the forward
+// epilogue stay inside the lane (plus two exchanges among the four lanes of a
+// column and one between the two waves of a column).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -32,7 +34,7 @@ namespace flce {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 constexpr int kBM = gemm::kBM;
@@ -102,6 +104,17 @@ __device__ __forceinline__ void issue_direct(const DirectLoads<L>& d, int64_t kt
 #endif
 }
 
+// Load q (0 .. L-1) of issue_direct alone.
+template <int L>
+__device__ __forceinline__ void issue_one(const DirectLoads<L>& d, int64_t kt, char* lds, int wave,
+                                          int q) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(
+      d.base + kt * d.kstep + d.off[q],
+      (__attribute__((address_space(3))) void*)(lds + (L * wave + q) * 1024), 16, 0, 0);
+#endif
+}
+
 // Register path for a partial last stage tile: zero-filled past K (and past
 // the matrix edge), then stored into the same LDS layout.
 template <int FORM, int SK>
@@ -123,24 +136,29 @@ __device__ __forceinline__ void store_tail(char* lds, const u32x4 (&r)[gemm::tai
     *reinterpret_cast<u32x4*>(lds + gemm::tail_lds_pos(FORM, tid + 256 * i, SK) * 16) = r[i];
 }
 
-// MFMA fragment of 32 rows (block b of the wave's 128) for the 16-wide K
-// substep s (0 .. SK/16 - 1) of a stage tile.
+// MFMA fragment of 16 rows (row_base .. row_base + 15 of the tile) for the
+// 32-wide K part p (0 .. SK/32 - 1) of a stage tile: lane l holds row
+// row_base + l % 16 at k = 32 p + 8 (l / 16) + 0..7. Both operands use the
+// same k order, which is all the product needs.
 template <int FORM, int SK>
-__device__ __forceinline__ bf16x8 read_frag(const char* lds, int row_base, int s, int lane) {
+__device__ __forceinline__ bf16x8 read_frag(const char* lds, int row_base, int p, int lane) {
   if (FORM == 0) {
-    const int row = row_base + (lane & 31);
-    const int c = 2 * s + (lane >> 5);
+    const int row = row_base + (lane & 15);
+    const int c = 4 * p + (lane >> 4);
     const u32x4 v = *reinterpret_cast<const u32x4*>(lds + gemm::lds_chunk_n(row, c, SK) * 16);
     return __builtin_bit_cast(bf16x8, v);
   } else {
+    // Lane i of a 16-lane group receives element i % 4 of the 8-byte chunks
+    // read by lanes 4e + i / 4 (e = 0..3): lane i reads k-row base + i / 4 at
+    // columns 4 (i % 4) .. + 3, so lane i gets column i at k-rows base + 0..3.
     typedef __attribute__((ext_vector_type(4))) short s16x4;
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     const int g = lane >> 4, i = lane & 15;
-    const int col = row_base + 16 * (g & 1) + 4 * (i & 3);
+    const int col = row_base + 4 * (i & 3);
     s16x4 h[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int k = 16 * s + 8 * (g >> 1) + 4 * r + (i >> 2);
+      const int k = 32 * p + 8 * g + 4 * r + (i >> 2);
       h[r] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + gemm::lds_byte_t(k, col)));
     }
     typedef __attribute__((ext_vector_type(8))) short s16x8;
@@ -149,14 +167,18 @@ __device__ __forceinline__ bf16x8 read_frag(const char* lds, int row_base, int s
   }
 }
 
-// Element (i, j, r) of the accumulators of a wave sits at tile row
-// wm*128 + i*32 + 8*(r/4) + 4*(lane/32) + r%4 and tile column
-// wn*128 + j*32 + lane%32 (the 32x32 MFMA output layout).
+// A wave's accumulators: 8 x 8 blocks of 16 x 16, four values per lane.
+// Element (i, j, r) sits at tile row wm*128 + i*16 + 4*(lane/16) + r and
+// tile column wn*128 + j*16 + lane%16 (the 16x16 MFMA output layout), so a
+// lane holds 4 consecutive rows of each block and the four lanes l, l ^ 16,
+// l ^ 32, l ^ 48 share its columns.
+typedef f32x4 Acc[8][8];
+
 __device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
-  return wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+  return wm * 128 + i * 16 + 4 * (lane >> 4) + r;
 }
 __device__ __forceinline__ int acc_col(int wn, int j, int lane) {
-  return wn * 128 + j * 32 + (lane & 31);
+  return wn * 128 + j * 16 + (lane & 15);
 }
 
 // Waits of the K loop (gfx9 s_waitcnt encoding: vmcnt bits [3:0] and
@@ -180,83 +202,81 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// MFMA fragments of one 16-wide K substep for the wave's 128 x 128 block.
-struct Frags {
-  bf16x8 a[4], b[4];
-};
-
-template <int FA, int FB, int SK>
-__device__ __forceinline__ void read_substep(Frags& f, const char* sa, const char* sb, int s,
-                                             int wm, int wn, int lane) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = read_frag<FA, SK>(sa, wm * 128 + i * 32, s, lane);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) f.b[j] = read_frag<FB, SK>(sb, wn * 128 + j * 32, s, lane);
-}
-
-__device__ __forceinline__ void mfma_substep(f32x16 (&acc)[4][4], const Frags& f) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-}
-
-// Fragments of one MFMA step (32 k): 32-wide part `part` of a stage tile.
+// MFMA fragments of one step (32 k) for the wave's 128 x 128 block: 32-wide
+// part `part` of a stage tile, 8 row blocks of each operand.
 struct StepFrags {
-  Frags s[2];
+  bf16x8 a[8], b[8];
 };
 
 template <int FA, int FB, int SK>
 __device__ __forceinline__ void read_step(StepFrags& f, const char* sa, const char* sb, int part,
                                           int wm, int wn, int lane) {
-  read_substep<FA, FB, SK>(f.s[0], sa, sb, 2 * part, wm, wn, lane);
-  read_substep<FA, FB, SK>(f.s[1], sa, sb, 2 * part + 1, wm, wn, lane);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.a[i] = read_frag<FA, SK>(sa, wm * 128 + i * 16, part, lane);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f.b[j] = read_frag<FB, SK>(sb, wn * 128 + j * 16, part, lane);
 }
 
-// Scheduling hints for one MFMA step: its 32 MFMAs, with the LDS fragment
-// reads of the next step (all in the first half of the step, so they have
-// returned when the next step needs them) and NLOADS direct global loads
-// placed between them, so everything issues under the MFMAs instead of
-// stalling the wave's in-order stream. The placement of the loads was chosen
-// by timing: with both operands K-contiguous (16 loads on every other step)
-// one after every second MFMA across the whole step; steps with transpose
-// reads (8 loads per step) in the second half.
-template <int FA, int FB, int NLOADS>
-__device__ __forceinline__ void interleave_hints() {
-  constexpr bool kNN = FA == 0 && FB == 0;
-  constexpr int kReads = 2 * ((FA == 0 ? 4 : 8) + (FB == 0 ? 4 : 8));
-  constexpr int kPer = (kReads + 15) / 16;
+__device__ __forceinline__ void mfma_step(Acc& acc, const StepFrags& f) {
 #pragma unroll
-  for (int q = 0; q < 32; ++q) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
-    const bool load = kNN ? (q % 2 == 1 && q / 2 < NLOADS) : (q >= 16 && q < 16 + NLOADS);
-    if (NLOADS > 0 && load) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-    if (q < kReads / kPer) __builtin_amdgcn_sched_group_barrier(0x100, kPer, 0);  // DS read
-  }
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
 // One MFMA step: optionally start the direct loads of a stage tile into its
 // (free) stage, read the fragments of the next step (32-wide part
 // `next_part` of the stage tile at na/nb) and multiply the current step,
-// whose fragments were read during the previous one. The stages are
-// __restrict__ so the compiler does not order the direct-to-LDS writes
-// against the reads; the real dependencies are the waits and the barriers.
+// whose fragments were read during the previous one. The step is issued as 16
+// chunks of 4 MFMAs, fenced by scheduling barriers, so that the loads and
+// reads sit between the MFMAs where they are placed here instead of where the
+// scheduler would bunch them: the fragment reads of the next step in chunks
+// 0..7 (row block c of each operand in chunk c), so they have returned long
+// before the next step (after the first chunk's MFMAs, so that their wait for
+// the current fragments does not include the new reads); the direct loads one
+// per chunk when both operands are
+// K-contiguous (16 loads on every other step, A and B alternating), else one
+// per chunk in chunks 8..15 (8 loads per step). The stages are __restrict__
+// so the compiler does not order the direct-to-LDS writes against the reads;
+// the real dependencies are the waits and the barriers.
 template <int FA, int FB, int SK, bool LOADS, int L>
-__device__ __forceinline__ void k_step(f32x16 (&acc)[4][4], const StepFrags& cur, StepFrags& nxt,
+__device__ __forceinline__ void k_step(Acc& acc, const StepFrags& cur, StepFrags& nxt,
                                        const DirectLoads<L>& da, const DirectLoads<L>& db,
                                        int64_t load_tile, const char* __restrict__ na,
                                        const char* __restrict__ nb, int next_part,
                                        char* __restrict__ la, char* __restrict__ lb, int wave,
                                        int wm, int wn, int lane) {
-  if (LOADS) {
-    issue_direct<L>(da, load_tile, la, wave);
-    issue_direct<L>(db, load_tile, lb, wave);
+  constexpr bool kNN = FA == 0 && FB == 0;
+  static_assert(!kNN || 2 * L == 16, "one load per chunk");
+  static_assert(kNN || 2 * L == 8, "one load per chunk of the second half");
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const int i = c >> 1;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = 4 * (c & 1) + jj;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0);
+    }
+    // the step's first MFMAs go before any new read, so their wait for this
+    // step's fragments does not also wait for the new reads
+    if (c == 0) __builtin_amdgcn_sched_barrier(0);
+    if (c < 8) {
+      nxt.a[c] = read_frag<FA, SK>(na, wm * 128 + c * 16, next_part, lane);
+      nxt.b[c] = read_frag<FB, SK>(nb, wn * 128 + c * 16, next_part, lane);
+    }
+    if (LOADS) {
+      if (kNN) {
+        if (c & 1) issue_one<L>(db, load_tile, lb, wave, c >> 1);
+        else       issue_one<L>(da, load_tile, la, wave, c >> 1);
+      } else if (c >= 8) {
+        const int q = c - 8;
+        if (q < L) issue_one<L>(da, load_tile, la, wave, q);
+        else       issue_one<L>(db, load_tile, lb, wave, q - L);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  read_step<FA, FB, SK>(nxt, na, nb, next_part, wm, wn, lane);
-  mfma_substep(acc, cur.s[0]);
-  mfma_substep(acc, cur.s[1]);
-  interleave_hints<FA, FB, LOADS ? 2 * L : 0>();
 }
 
 template <int FA, int FB, class Epi, bool BA>
@@ -285,13 +305,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A_, Operand B_, in
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
 
-  f32x16 acc[4][4];
+  Acc acc;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
 
   const DirectLoads<L> da = setup_direct<FA, SK>(A, m0, wave, lane);
   const DirectLoads<L> db = setup_direct<FB, SK>(B, n0, wave, lane);
@@ -300,6 +320,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A_, Operand B_, in
 
   auto st_a = [&](int64_t t) { return smem + (t % kStages) * 2 * kTileBytes; };
   auto st_b = [&](int64_t t) { return smem + (t % kStages) * 2 * kTileBytes + kTileBytes; };
+  if (nk > nfull) {
+    // The partial last stage tile goes through registers, zero-filled past K,
+    // into stage 0, and is multiplied first, before the pipelined loop, whose
+    // prologue then reuses the stage (behind the barrier). Placed after the
+    // loop instead, it made the register allocator shuffle the 64
+    // accumulator tuples through copies and spills inside the loop.
+    char* la = st_a(0);
+    char* lb = st_b(0);
+    u32x4 ta[gemm::tail_loads(SK)], tb[gemm::tail_loads(SK)];
+    load_tail<FA, SK>(ta, A, m0, nfull * SK, tid);
+    load_tail<FB, SK>(tb, B, n0, nfull * SK, tid);
+    store_tail<FA, SK>(la, ta, tid);
+    store_tail<FB, SK>(lb, tb, tid);
+    __syncthreads();
+    StepFrags ft;
+#pragma unroll
+    for (int part = 0; part < SK / 32; ++part) {
+      read_step<FA, FB, SK>(ft, la, lb, part, wm, wn, lane);
+      mfma_step(acc, ft);
+    }
+    __syncthreads();
+  }
   if (nfull > 0) {
     const int64_t last = nfull - 1;
     StepFrags f[2];
@@ -401,24 +443,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A_, Operand B_, in
     wait_vm0();
     stage_barrier();
   }
-  if (nk > nfull) {
-    // The partial last stage tile goes through registers, zero-filled past K,
-    // into stage 0, which no wave reads any more (behind the last barrier).
-    char* la = st_a(0);
-    char* lb = st_b(0);
-    u32x4 ta[gemm::tail_loads(SK)], tb[gemm::tail_loads(SK)];
-    load_tail<FA, SK>(ta, A, m0, nfull * SK, tid);
-    load_tail<FB, SK>(tb, B, n0, nfull * SK, tid);
-    store_tail<FA, SK>(la, ta, tid);
-    store_tail<FB, SK>(lb, tb, tid);
-    __syncthreads();
-    Frags ft;
-#pragma unroll
-    for (int sub = 0; sub < SK / 16; ++sub) {
-      read_substep<FA, FB, SK>(ft, la, lb, sub, wm, wn, lane);
-      mfma_substep(acc, ft);
-    }
-  }
   __syncthreads();
   epi(acc, m0, n0, wm, wn, lane, smem);
 }
@@ -439,45 +463,41 @@ enum LogitsOut : int { kNoLogits = 0, kLogitsF32 = 1, kLogitsBF16 = 2 };
 // v >= V never stored) row-major by token: out[t][v], row length ld, as
 // float32 or as bf16 rounded to nearest even. Each wave stages its block in
 // its own 32 KiB of LDS as [token][vocab]: bf16 all 128 vocabulary rows in
-// one pass (8-byte slots, as in store_token_major), float32 64 rows per pass
-// (16-byte slots holding 4 consecutive vocabulary values, XOR-swizzled by
-// token), then writes 16-byte runs of token rows. A run that would cross V,
+// one pass (8-byte slots, as in store_token_major), float32 64 rows (row
+// blocks i of 16, four per pass) per pass (16-byte slots holding a lane's 4
+// consecutive vocabulary values, XOR-swizzled by token), then writes 16-byte
+// runs of token rows. A run that would cross V,
 // and every run when `vec` is 0 (destination or row length not 16-byte
 // aligned), is written element by element. Ends with a barrier, so the
 // caller may reuse the LDS at once.
 template <int OUT>
-__device__ __forceinline__ void store_logits(const f32x16 (&acc)[4][4], char* smem, int wm,
-                                             int wn, int lane, void* out, int64_t ld, int vec,
-                                             int64_t m0, int64_t n0, int64_t N, int64_t V) {
+__device__ __forceinline__ void store_logits(const Acc& acc, char* smem, int wm, int wn, int lane,
+                                             void* out, int64_t ld, int vec, int64_t m0,
+                                             int64_t n0, int64_t N, int64_t V) {
   constexpr bool F32 = OUT == kLogitsF32;
   constexpr int kPasses = F32 ? 2 : 1;
   constexpr int kRun = F32 ? 4 : 8;                // elements per 16-byte run
-  const int half = lane >> 5;
+  const int g = lane >> 4;
   char* reg = smem + (wm + 2 * wn) * kWaveScratch;
 #pragma unroll
   for (int ps = 0; ps < kPasses; ++ps) {
     if (ps) __syncthreads();                       // the previous pass has been read
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tl = j * 32 + (lane & 31);
+    for (int j = 0; j < 8; ++j) {
+      const int tl = j * 16 + (lane & 15);
 #pragma unroll
-      for (int ii = 0; ii < 4 / kPasses; ++ii) {
-        const int i = ii + ps * (4 / kPasses);
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * rq + e];
-          if (F32) {
-            const int slot = (ii * 8 + 2 * rq + half) ^ (tl & 15);
-            *reinterpret_cast<u32x4*>(reg + tl * 256 + slot * 16) =
-                u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                      __float_as_uint(v[3])};
-          } else {
-            const int slot = (i * 8 + 2 * rq + half) ^ (tl & 31);
-            *reinterpret_cast<uint2*>(reg + tl * 256 + slot * 8) =
-                make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-          }
+      for (int ii = 0; ii < 8 / kPasses; ++ii) {
+        const int i = ii + ps * (8 / kPasses);
+        const f32x4 v = acc[i][j];
+        if (F32) {
+          const int slot = (ii * 4 + g) ^ (tl & 15);
+          *reinterpret_cast<u32x4*>(reg + tl * 256 + slot * 16) =
+              u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                    __float_as_uint(v[3])};
+        } else {
+          const int slot = (i * 4 + g) ^ (tl & 31);
+          *reinterpret_cast<uint2*>(reg + tl * 256 + slot * 8) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
       }
     }
@@ -532,22 +552,22 @@ struct EpiLse {
   int64_t ld_logits;
   int vec;       // 16-byte runs of the logits rows are aligned
 
-  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm,
-                                             int wn, int lane, char* smem) const {
-    const int half = lane >> 5;
+  __device__ __forceinline__ void operator()(Acc& acc, int64_t m0, int64_t n0, int wm, int wn,
+                                             int lane, char* smem) const {
+    const int g = lane >> 4;
     const int64_t vbase = m0 + wm * 128;
-    float mx[4], sm[4];
+    float mx[8], sm[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 8; ++j) {
       const int64_t t = n0 + acc_col(wn, j, lane);
-      // the column's 64 logits, softcapped and masked past V, in registers of
-      // their own (the accumulators are not written back unless the logits
-      // are stored)
-      float z[4][16];
+      // the lane's 32 logits of the column, softcapped and masked past V, in
+      // registers of their own (the accumulators are not written back unless
+      // the logits are stored)
+      float z[8][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < 4; ++r) {
           float x = acc[i][j][r];
           if (SOFTCAP) x = softcap * tanh_fast(x * inv_softcap);
           const int64_t v = m0 + acc_row(wm, i, r, lane);
@@ -558,24 +578,25 @@ struct EpiLse {
       const int64_t y = t < N ? labels[t] : ignore_index;
       if (y != ignore_index && y >= vbase && y < vbase + 128 && y < V) {
         const int d = int(y - vbase);
-        const int ti = d >> 5, w = d & 31;
-        if (((w >> 2) & 1) == half) {
-          const int tr = ((w >> 3) << 2) | (w & 3);
+        const int ti = d >> 4, tr = d & 3;
+        if (((d >> 2) & 3) == g) {
           float val = 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) val = (i == ti && r == tr) ? z[i][r] : val;
+            for (int r = 0; r < 4; ++r) val = (i == ti && r == tr) ? z[i][r] : val;
           zt[t] = val;
         }
       }
-      // max and sum in four independent chains (r % 4), then combined
+      // max and sum in four independent chains (r), then combined over the
+      // lane's values and the four lanes of the column
       float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mq[r & 3] = fmaxf(mq[r & 3], z[i][r]);
+        for (int r = 0; r < 4; ++r) mq[r] = fmaxf(mq[r], z[i][r]);
       float m = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+      m = fmaxf(m, __shfl_xor(m, 16));
       m = fmaxf(m, __shfl_xor(m, 32));
       // sum of exp(z - m) = sum of 2^(z log2 e - m log2 e), one fma per element
       float s = 0.f;
@@ -583,12 +604,13 @@ struct EpiLse {
         const float mb = m * kLog2e;
         float sq[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sq[r & 3] += __builtin_amdgcn_exp2f(fmaf(z[i][r], kLog2e, -mb));
+          for (int r = 0; r < 4; ++r)
+            sq[r] += __builtin_amdgcn_exp2f(fmaf(z[i][r], kLog2e, -mb));
         s = (sq[0] + sq[1]) + (sq[2] + sq[3]);
       }
+      s += __shfl_xor(s, 16);
       s += __shfl_xor(s, 32);
       mx[j] = m;
       sm[j] = s;
@@ -597,15 +619,15 @@ struct EpiLse {
       store_logits<OUT>(acc, smem, wm, wn, lane, logits, ld_logits, vec, m0, n0, N, V);
     // combine the two waves (wm = 0, 1) that share the token columns
     float2* buf = reinterpret_cast<float2*>(smem);
-    if (wm == 1 && half == 0) {
+    if (wm == 1 && g == 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) buf[wn * 128 + j * 32 + lane] = make_float2(mx[j], sm[j]);
+      for (int j = 0; j < 8; ++j) buf[wn * 128 + j * 16 + lane] = make_float2(mx[j], sm[j]);
     }
     __syncthreads();
-    if (wm == 0 && half == 0) {
+    if (wm == 0 && g == 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float2 o = buf[wn * 128 + j * 32 + lane];
+      for (int j = 0; j < 8; ++j) {
+        const float2 o = buf[wn * 128 + j * 16 + lane];
         const float Mx = fmaxf(mx[j], o.x);
         float S = 0.f;
         if (mx[j] != -INFINITY) S += sm[j] * __builtin_amdgcn_exp2f((mx[j] - Mx) * kLog2e);
@@ -622,8 +644,8 @@ struct EpiLse {
 // row-major by token, dst[t][v] with row length ld, or (BLOCKED) blocked,
 // dst[blocked_offset(t, v, blk)]. Each wave stages its
 // 128 x 128 block in its own 32 KiB of LDS as [token][vocab] (a lane packs
-// its 4 consecutive vocab values into 8 bytes; 8-byte slots XOR-swizzled by
-// token), then writes whole 16-byte runs of token rows; columns t >= nt and
+// its 4 consecutive vocab values of a block into 8 bytes; 8-byte slots
+// XOR-swizzled by token), then writes whole 16-byte runs of token rows; columns t >= nt and
 // rows v >= nv are not written. LO stores the residual v - bf16(v) instead
 // of v (the low half of a bf16 pair). Optionally one element per token
 // column j of the lane is replaced after staging: patch->pos[j] >= 0 is its
@@ -631,15 +653,14 @@ struct EpiLse {
 // value. The caller separates a second use of the staging area with a
 // barrier.
 struct TargetPatch {
-  int pos[4];
-  float val[4];
+  int pos[8];
+  float val[8];
 };
 
 // Byte offset, in a wave's staging area, of row d (0..127, the wave's own
-// rows) of token column tl, for the lane half that holds that row.
+// rows) of token column tl: the 8-byte slot d / 4 of the token row, swizzled.
 __device__ __forceinline__ int target_slot(int d, int tl) {
-  const int i = d >> 5, w = d & 31, rq = w >> 3, half = (w >> 2) & 1, e = w & 3;
-  return tl * 256 + (((i * 8 + 2 * rq + half) ^ (tl & 31)) * 8) + 2 * e;
+  return tl * 256 + (((d >> 2) ^ (tl & 31)) * 8) + 2 * (d & 3);
 }
 
 // The value of accumulator element (i, j, r) is get(i, j, r): the element
@@ -650,30 +671,28 @@ __device__ __forceinline__ void store_token_major(const Get& get, char* smem, in
                                                   int64_t m0, int64_t n0, int64_t nt,
                                                   int64_t nv, const TargetPatch* patch = nullptr,
                                                   int64_t blk = 0) {
-  const int half = lane >> 5;
+  const int g = lane >> 4;
   char* reg = smem + (wm + 2 * wn) * kWaveScratch;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int tl = j * 32 + (lane & 31);
+  for (int j = 0; j < 8; ++j) {
+    const int tl = j * 16 + (lane & 15);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i) {
+      float v[4];
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[e] = get(i, j, 4 * rq + e);
-          if (LO) v[e] -= bf16_to_f32(f32_to_bf16(v[e]));
-        }
-        const uint32_t lo = pack_bf16x2(v[0], v[1]);
-        const uint32_t hi = pack_bf16x2(v[2], v[3]);
-        const int slot = (i * 8 + 2 * rq + half) ^ (tl & 31);
-        *reinterpret_cast<uint2*>(reg + tl * 256 + slot * 8) = make_uint2(lo, hi);
+      for (int e = 0; e < 4; ++e) {
+        v[e] = get(i, j, e);
+        if (LO) v[e] -= bf16_to_f32(f32_to_bf16(v[e]));
       }
+      const uint32_t lo = pack_bf16x2(v[0], v[1]);
+      const uint32_t hi = pack_bf16x2(v[2], v[3]);
+      const int slot = (i * 4 + g) ^ (tl & 31);
+      *reinterpret_cast<uint2*>(reg + tl * 256 + slot * 8) = make_uint2(lo, hi);
+    }
   }
   if (PATCH) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
       if (patch->pos[j] >= 0) {
         float v = patch->val[j];
         if (LO) v -= bf16_to_f32(f32_to_bf16(v));
@@ -735,16 +754,16 @@ struct EpiGrad {
   // token in this block is then replaced in the staged tile by
   // c (exp(z'_y - lse) - 1) dz'/dz from the forward's target logit, which is
   // the same float32 value the GEMM recomputes.
-  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm,
-                                             int wn, int lane, char* smem) const {
+  __device__ __forceinline__ void operator()(Acc& acc, int64_t m0, int64_t n0, int wm, int wn,
+                                             int lane, char* smem) const {
     const float c = sc->c32;
-    const int half = lane >> 5;
+    const int lg = lane >> 4;                           // the lane's row group
     const int64_t vbase = v0 + m0 + wm * 128;           // global vocab id of block row 0
     TargetPatch tp;
-    float bias[4];
+    float bias[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tl = j * 32 + (lane & 31);             // token within the wave block
+    for (int j = 0; j < 8; ++j) {
+      const int tl = j * 16 + (lane & 15);             // token within the wave block
       const int64_t t = n0 + wn * 128 + tl;
       // Every token's lse is known (ignored ones too) and columns past N hold
       // the logits of token N-1, so exp(z' - lse) <= 1 everywhere.
@@ -759,7 +778,7 @@ struct EpiGrad {
           coef = (y < 0 || y >= V) ? NAN : c;
           if (y >= vbase && y < vbase + 128) {
             const int d = int(y - vbase);
-            if (((d >> 2) & 1) == half) {
+            if (((d >> 2) & 3) == lg) {
               const float z = zt[t];
               float dd = 1.f;
               if (SOFTCAP) {
@@ -791,11 +810,11 @@ struct EpiGrad {
     }
     // two stores of the same values (hi, then lo): form them once, in place
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = grad(i, j, r);
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = grad(i, j, r);
     auto held = [&](int i, int j, int r) { return acc[i][j][r]; };
     store_token_major<false, true, true>(held, smem, wm, wn, lane, g, 0, m0, n0, N, vcur, &tp,
                                          gblk);
@@ -822,18 +841,18 @@ struct EpiLseP {
   uint16_t* probs;  // blocked, pblk elements per 32 vocabulary columns
   int64_t pblk;
 
-  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm,
-                                             int wn, int lane, char* smem) const {
-    const int half = lane >> 5;
+  __device__ __forceinline__ void operator()(Acc& acc, int64_t m0, int64_t n0, int wm, int wn,
+                                             int lane, char* smem) const {
+    const int g = lane >> 4;
     const int64_t vbase = m0 + wm * 128;
-    float mx[4];
+    float mx[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 8; ++j) {
       const int64_t t = n0 + acc_col(wn, j, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < 4; ++r) {
           float z = acc[i][j][r];
           if (SOFTCAP) z = softcap * tanh_fast(z * inv_softcap);
           const int64_t v = m0 + acc_row(wm, i, r, lane);
@@ -842,60 +861,61 @@ struct EpiLseP {
       const int64_t y = t < N ? labels[t] : ignore_index;
       if (y != ignore_index && y >= vbase && y < vbase + 128 && y < V) {
         const int d = int(y - vbase);
-        const int ti = d >> 5, w = d & 31;
-        if (((w >> 2) & 1) == half) {
-          const int tr = ((w >> 3) << 2) | (w & 3);
+        const int ti = d >> 4, tr = d & 3;
+        if (((d >> 2) & 3) == g) {
           float val = 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) val = (i == ti && r == tr) ? acc[i][j][r] : val;
+            for (int r = 0; r < 4; ++r) val = (i == ti && r == tr) ? acc[i][j][r] : val;
           zt[t] = val;
         }
       }
       float m = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[i][j][r]);
+        for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[i][j][r]);
+      m = fmaxf(m, __shfl_xor(m, 16));
       mx[j] = fmaxf(m, __shfl_xor(m, 32));
     }
     // the tile max of each token column, from both waves that hold it
     float* xb = reinterpret_cast<float*>(smem);      // [2][256] maxima, then [256] sums
-    if (half == 0) {
+    if (g == 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xb[wm * 256 + wn * 128 + j * 32 + lane] = mx[j];
+      for (int j = 0; j < 8; ++j) xb[wm * 256 + wn * 128 + j * 16 + lane] = mx[j];
     }
     __syncthreads();
-    float sm[4];
+    float sm[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float Mx = fmaxf(mx[j], xb[(1 - wm) * 256 + wn * 128 + j * 32 + (lane & 31)]);
+    for (int j = 0; j < 8; ++j) {
+      const float Mx = fmaxf(mx[j], xb[(1 - wm) * 256 + wn * 128 + j * 16 + (lane & 15)]);
       mx[j] = Mx;
       float s = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < 4; ++r) {
           const float p =
               Mx == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((acc[i][j][r] - Mx) * kLog2e);
           acc[i][j][r] = p;
           s += p;
         }
+      s += __shfl_xor(s, 16);
       sm[j] = s + __shfl_xor(s, 32);
     }
     __syncthreads();                                  // maxima read before the sums reuse xb
-    if (wm == 1 && half == 0) {
+    if (wm == 1 && g == 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xb[wn * 128 + j * 32 + lane] = sm[j];
+      for (int j = 0; j < 8; ++j) xb[wn * 128 + j * 16 + lane] = sm[j];
     }
     __syncthreads();
-    if (wm == 0 && half == 0) {
+    if (wm == 0 && g == 0) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 8; ++j) {
         const int64_t t = n0 + acc_col(wn, j, lane);
         if (t < ld_part)
-          part[(m0 / kBM) * ld_part + t] = make_float2(mx[j], sm[j] + xb[wn * 128 + j * 32 + lane]);
+          part[(m0 / kBM) * ld_part + t] = make_float2(mx[j], sm[j] + xb[wn * 128 + j * 16 + lane]);
       }
     }
     __syncthreads();                                  // sums read before the staging reuses LDS
@@ -962,32 +982,35 @@ __global__ __launch_bounds__(256) void k_probs_to_grad(
 }
 
 // ---- row-major epilogues staged through LDS ---------------------------------
-// A wave's 128 x 128 float32 block goes out in 4 passes of 32 rows: the lane
-// values are written to the wave's LDS scratch as [32][128] float32 (the two
-// 128-byte column halves swapped every 4 rows, which keeps the writes of the
-// two half-waves on different banks), then read back as float4 runs of 4
-// consecutive columns of one row, which the caller's functor stores. Before
-// the staging of each pass the functor may issue its own global loads for that
-// pass (prefetch), so their latency overlaps the LDS traffic.
+// A wave's 128 x 128 float32 block goes out in 4 passes of 32 rows (row blocks
+// 2P and 2P + 1 of 16): the lane values are written to the wave's LDS scratch
+// as [32][128] float32 (the four 64-byte column quarters of a 256-byte bank
+// window permuted by row / 4, which puts the four 16-lane groups of a write on
+// different banks), then read back as float4 runs of 4 consecutive columns of
+// one row, which the caller's functor stores. Before the staging of each pass
+// the functor may issue its own global loads for that pass (prefetch), so
+// their latency overlaps the LDS traffic.
 __device__ __forceinline__ int staged_col(int row, int col) {
-  return col ^ (((row >> 2) & 1) << 5);
+  return col ^ (((row >> 2) & 3) << 4);
 }
 
 template <class Pass>
-__device__ __forceinline__ void staged_rows(f32x16 (&acc)[4][4], int wm, int wn, int lane,
-                                            char* smem, Pass& pass) {
+__device__ __forceinline__ void staged_rows(Acc& acc, int wm, int wn, int lane, char* smem,
+                                            Pass& pass) {
   float* reg = reinterpret_cast<float*>(smem + (wm + 2 * wn) * kWaveScratch);
   pass.prefetch(0, lane);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (i + 1 < 4) pass.prefetch(i + 1, lane);     // in flight while block i is staged
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        reg[row * 128 + staged_col(row, j * 32 + (lane & 31))] = acc[i][j][r];
-      }
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * h + 4 * (lane >> 4) + r;
+          reg[row * 128 + staged_col(row, j * 16 + (lane & 15))] = acc[2 * i + h][j][r];
+        }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
@@ -1022,8 +1045,8 @@ struct EpiDW {
     }
   };
 
-  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm,
-                                             int wn, int lane, char* smem) const {
+  __device__ __forceinline__ void operator()(Acc& acc, int64_t m0, int64_t n0, int wm, int wn,
+                                             int lane, char* smem) const {
     Pass pass{*this, m0 + wm * 128, n0 + wn * 128};
     staged_rows(acc, wm, wn, lane, smem, pass);
   }
@@ -1051,8 +1074,8 @@ struct EpiDW32 {
     }
   };
 
-  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm,
-                                             int wn, int lane, char* smem) const {
+  __device__ __forceinline__ void operator()(Acc& acc, int64_t m0, int64_t n0, int wm, int wn,
+                                             int lane, char* smem) const {
     Pass pass{*this, m0 + wm * 128, n0 + wn * 128};
     staged_rows(acc, wm, wn, lane, smem, pass);
   }
@@ -1098,8 +1121,8 @@ struct EpiDH {
     }
   };
 
-  __device__ __forceinline__ void operator()(f32x16 (&acc)[4][4], int64_t m0, int64_t n0, int wm,
-                                             int wn, int lane, char* smem) const {
+  __device__ __forceinline__ void operator()(Acc& acc, int64_t m0, int64_t n0, int wm, int wn,
+                                             int lane, char* smem) const {
     Pass pass{*this, m0 + wm * 128, n0 + wn * 128, {}};
     staged_rows(acc, wm, wn, lane, smem, pass);
   }

@@ -4,7 +4,7 @@ Results do not depend on the loop schedule, but speed does, and a small
 source change can silently break it: a second LDS object makes the compiler
 wait for every direct load before each fragment read; register pressure can
 move spills into the loop. For every GEMM kernel this compiles
-kernels_bf16.hip to assembly and checks the innermost 64-MFMA loop:
+kernels_bf16.hip to assembly and checks the innermost 128-MFMA loop:
 no scratch traffic, the direct loads and fragment reads the design issues per
 two MFMA steps, the barriers, and that the only full vmcnt wait is the one
 before the barrier (never between a load and the reads of the same step)."""
@@ -35,14 +35,16 @@ def loops(tmp_path_factory):
         en = next(i for i in range(st, len(lines)) if lines[i].startswith(".Lfunc_end"))
         body = lines[st:en]
         name = re.match(r"^_ZN4flce12_GLOBAL__N_16k_gemmILi(\d)ELi(\d)ENS0_\d+(\w+?)I", body[0])
+        # loop headers as the compiler marks them (a backward jump alone can
+        # be a block placed out of line)
         labels = {m.group(1): i for i, l in enumerate(body)
-                  if (m := re.match(r"^(\.LBB\d+_\d+):", l))}
+                  if (m := re.match(r"^(\.LBB\d+_\d+):.*Loop Header", l))}
         best = None
         for i, l in enumerate(body):
             m = re.search(r"s_cbranch_\w+\s+(\.LBB\d+_\d+)", l)
             if m and m.group(1) in labels and labels[m.group(1)] < i:
                 a = labels[m.group(1)]
-                if sum("v_mfma" in x for x in body[a:i]) >= 64 and (best is None or i - a < best[1] - best[0]):
+                if sum("v_mfma" in x for x in body[a:i]) >= 128 and (best is None or i - a < best[1] - best[0]):
                     best = (a, i)
         assert best, body[0]
         seg = [l.strip() for l in body[best[0]:best[1]]
@@ -55,11 +57,11 @@ def loops(tmp_path_factory):
 def test_main_loops(loops):
     for sym, (fa, fb, epi, seg) in loops.items():
         count = lambda p: sum(1 for l in seg if re.match(p, l))
-        assert count(r"v_mfma") == 64, sym
+        assert count(r"v_mfma") == 128, sym
         assert count(r"scratch_|buffer_store|buffer_load") == 0, (sym, "spill in the K loop")
         assert count(r"global_load_lds") == 16, sym          # one stage tile (two steps)
         # fragment reads per two steps: 16 ds_read_b128 per N-form operand,
-        # 32 transpose reads per T-form operand
+        # 32 transpose reads per T-form operand (8 row blocks of 16 per step)
         reads = (16 if fa == 0 else 32) + (16 if fb == 0 else 32)
         assert count(r"ds_read") == reads, (sym, count(r"ds_read"))
         nn = fa == 0 and fb == 0
