@@ -225,21 +225,38 @@ __device__ __forceinline__ void mfma_step(Acc& acc, const StepFrags& f) {
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
+// Scheduling hints for a step of dH (K-contiguous G, transposed W): its 64
+// MFMAs, the fragment reads of the next step after the first MFMAs (all in
+// the first half of the step), and the NLOADS direct loads one after every
+// second MFMA of the second half, so everything issues under the MFMAs.
+template <int FA, int FB, int NLOADS>
+__device__ __forceinline__ void interleave_hints() {
+  constexpr int kReads = (FA == 0 ? 8 : 16) + (FB == 0 ? 8 : 16);
+#pragma unroll
+  for (int q = 0; q < 64; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+    const bool load = q >= 32 && q % 2 == 0 && (q - 32) / 2 < NLOADS;
+    if (NLOADS > 0 && load) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+    if (q < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);    // DS read
+  }
+}
+
 // One MFMA step: optionally start the direct loads of a stage tile into its
 // (free) stage, read the fragments of the next step (32-wide part
 // `next_part` of the stage tile at na/nb) and multiply the current step,
-// whose fragments were read during the previous one. The step is issued as 16
-// chunks of 4 MFMAs, fenced by scheduling barriers, so that the loads and
-// reads sit between the MFMAs where they are placed here instead of where the
-// scheduler would bunch them: the fragment reads of the next step in chunks
-// 0..7 (row block c of each operand in chunk c), so they have returned long
-// before the next step (after the first chunk's MFMAs, so that their wait for
-// the current fragments does not include the new reads); the direct loads one
-// per chunk when both operands are
-// K-contiguous (16 loads on every other step, A and B alternating), else one
-// per chunk in chunks 8..15 (8 loads per step). The stages are __restrict__
-// so the compiler does not order the direct-to-LDS writes against the reads;
-// the real dependencies are the waits and the barriers.
+// whose fragments were read during the previous one. The stages are
+// __restrict__ so the compiler does not order the direct-to-LDS writes
+// against the reads; the real dependencies are the waits and the barriers.
+//
+// The forward/gradient GEMMs (both operands K-contiguous, 16 loads on every
+// other step) and dW (both transposed, 8 loads per step) issue the step as 16
+// chunks of 4 MFMAs, fenced by scheduling barriers: the fragment reads of the
+// next step in chunks 0..7 (row block c of each operand in chunk c, after the
+// first chunk's MFMAs, so that their wait for the current fragments does not
+// include the new reads), and the direct loads one per chunk (A and B
+// alternating) or one per chunk of the second half. Left to scheduling hints,
+// the compiler bunched 14 of the 16 loads of the K-contiguous steps back to
+// back. dH measured faster with the hints.
 template <int FA, int FB, int SK, bool LOADS, int L>
 __device__ __forceinline__ void k_step(Acc& acc, const StepFrags& cur, StepFrags& nxt,
                                        const DirectLoads<L>& da, const DirectLoads<L>& db,
@@ -247,35 +264,43 @@ __device__ __forceinline__ void k_step(Acc& acc, const StepFrags& cur, StepFrags
                                        const char* __restrict__ nb, int next_part,
                                        char* __restrict__ la, char* __restrict__ lb, int wave,
                                        int wm, int wn, int lane) {
-  constexpr bool kNN = FA == 0 && FB == 0;
-  static_assert(!kNN || 2 * L == 16, "one load per chunk");
-  static_assert(kNN || 2 * L == 8, "one load per chunk of the second half");
-#pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const int i = c >> 1;
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int j = 4 * (c & 1) + jj;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0);
-    }
-    // the step's first MFMAs go before any new read, so their wait for this
-    // step's fragments does not also wait for the new reads
-    if (c == 0) __builtin_amdgcn_sched_barrier(0);
-    if (c < 8) {
-      nxt.a[c] = read_frag<FA, SK>(na, wm * 128 + c * 16, next_part, lane);
-      nxt.b[c] = read_frag<FB, SK>(nb, wn * 128 + c * 16, next_part, lane);
-    }
+  if constexpr (FA != FB) {
     if (LOADS) {
-      if (kNN) {
-        if (c & 1) issue_one<L>(db, load_tile, lb, wave, c >> 1);
-        else       issue_one<L>(da, load_tile, la, wave, c >> 1);
-      } else if (c >= 8) {
-        const int q = c - 8;
-        if (q < L) issue_one<L>(da, load_tile, la, wave, q);
-        else       issue_one<L>(db, load_tile, lb, wave, q - L);
-      }
+      issue_direct<L>(da, load_tile, la, wave);
+      issue_direct<L>(db, load_tile, lb, wave);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    read_step<FA, FB, SK>(nxt, na, nb, next_part, wm, wn, lane);
+    mfma_step(acc, cur);
+    interleave_hints<FA, FB, LOADS ? 2 * L : 0>();
+  } else {
+    constexpr bool kNN = FA == 0;
+    static_assert(2 * L == (kNN ? 16 : 8), "one load per chunk (of the second half)");
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int i = c >> 1;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = 4 * (c & 1) + jj;
+        acc[i][j] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0);
+      }
+      if (c == 0) __builtin_amdgcn_sched_barrier(0);
+      if (c < 8) {
+        nxt.a[c] = read_frag<FA, SK>(na, wm * 128 + c * 16, next_part, lane);
+        nxt.b[c] = read_frag<FB, SK>(nb, wn * 128 + c * 16, next_part, lane);
+      }
+      if (LOADS) {
+        if (kNN) {
+          if (c & 1) issue_one<L>(db, load_tile, lb, wave, c >> 1);
+          else       issue_one<L>(da, load_tile, la, wave, c >> 1);
+        } else if (c >= 8) {
+          const int q = c - 8;
+          if (q < L) issue_one<L>(da, load_tile, la, wave, q);
+          else       issue_one<L>(db, load_tile, lb, wave, q - L);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
