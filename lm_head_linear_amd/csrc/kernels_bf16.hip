@@ -181,6 +181,34 @@ __device__ __forceinline__ int acc_col(int wn, int j, int lane) {
   return wn * 128 + j * 16 + (lane & 15);
 }
 
+// Max and sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 that share an
+// accumulator column, with the gfx950 lane swaps (VALU, no LDS round trip).
+// permlane16_swap(x, x) yields x of lanes l & ~16 and l | 16, and
+// permlane32_swap(x, x) those of lanes l & ~32 and l | 32, in that order in
+// every lane, so all four lanes get the same bits.
+__device__ __forceinline__ float col_max4(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+#endif
+  return x;
+}
+__device__ __forceinline__ float col_sum4(float x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+#endif
+  return x;
+}
+
 // Waits of the K loop (gfx9 s_waitcnt encoding: vmcnt bits [3:0] and
 // [15:14], expcnt [6:4], lgkmcnt [11:8]; a field at its maximum does not
 // wait).
@@ -620,9 +648,7 @@ struct EpiLse {
       for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mq[r] = fmaxf(mq[r], z[i][r]);
-      float m = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
+      const float m = col_max4(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
       // sum of exp(z - m) = sum of 2^(z log2 e - m log2 e), one fma per element
       float s = 0.f;
       if (m != -INFINITY) {
@@ -635,10 +661,8 @@ struct EpiLse {
             sq[r] += __builtin_amdgcn_exp2f(fmaf(z[i][r], kLog2e, -mb));
         s = (sq[0] + sq[1]) + (sq[2] + sq[3]);
       }
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
       mx[j] = m;
-      sm[j] = s;
+      sm[j] = col_sum4(s);
     }
     if (OUT != kNoLogits)
       store_logits<OUT>(acc, smem, wm, wn, lane, logits, ld_logits, vec, m0, n0, N, V);
@@ -901,8 +925,7 @@ struct EpiLseP {
       for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) m = fmaxf(m, acc[i][j][r]);
-      m = fmaxf(m, __shfl_xor(m, 16));
-      mx[j] = fmaxf(m, __shfl_xor(m, 32));
+      mx[j] = col_max4(m);
     }
     // the tile max of each token column, from both waves that hold it
     float* xb = reinterpret_cast<float*>(smem);      // [2][256] maxima, then [256] sums
@@ -926,8 +949,7 @@ struct EpiLseP {
           acc[i][j][r] = p;
           s += p;
         }
-      s += __shfl_xor(s, 16);
-      sm[j] = s + __shfl_xor(s, 32);
+      sm[j] = col_sum4(s);
     }
     __syncthreads();                                  // maxima read before the sums reuse xb
     if (wm == 1 && g == 0) {
