@@ -508,6 +508,17 @@ __device__ __forceinline__ float tanh_fast(float x) {
   return 1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f);
 }
 
+// XOR swizzle of the 8-byte slots of a staged token row (32 slots, 256 bytes,
+// one bank window): 2 b(t) with b(t) the 4-bit token t % 16 with its two
+// halves swapped. Even, so the 16-byte runs read back stay whole. A staging
+// write of 32 lanes (two 16-lane groups g, g + 1, 16 tokens each) covers all
+// 64 banks once (g goes to bit 0, b(t) to bits 1..4), and so does a 16-lane
+// read of 4 chunks of 4 consecutive tokens (the token's two low bits land
+// above the chunk's).
+__device__ __forceinline__ int token_swizzle(int tl) {
+  return 8 * (tl & 3) + 2 * ((tl >> 2) & 3);
+}
+
 // ---- token-major logits output of the forward --------------------------
 // Kinds of logits output of the forward epilogue.
 enum LogitsOut : int { kNoLogits = 0, kLogitsF32 = 1, kLogitsBF16 = 2 };
@@ -548,7 +559,7 @@ __device__ __forceinline__ void store_logits(const Acc& acc, char* smem, int wm,
               u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
                     __float_as_uint(v[3])};
         } else {
-          const int slot = (i * 4 + g) ^ (tl & 31);
+          const int slot = (i * 4 + g) ^ token_swizzle(tl);
           *reinterpret_cast<uint2*>(reg + tl * 256 + slot * 8) =
               make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
@@ -563,9 +574,7 @@ __device__ __forceinline__ void store_logits(const Acc& acc, char* smem, int wm,
       if (F32) {
         v = *reinterpret_cast<const u32x4*>(reg + tl * 256 + (ch ^ (tl & 15)) * 16);
       } else {
-        const int x = tl & 31;
-        v = *reinterpret_cast<const u32x4*>(reg + tl * 256 + (((2 * ch) ^ x) & ~1) * 8);
-        if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+        v = *reinterpret_cast<const u32x4*>(reg + tl * 256 + ((2 * ch) ^ token_swizzle(tl)) * 8);
       }
       const int64_t t = n0 + wn * 128 + tl;
       const int64_t vl = m0 + wm * 128 + (F32 ? ps * 64 + 4 * ch : 8 * ch);
@@ -709,7 +718,7 @@ struct TargetPatch {
 // Byte offset, in a wave's staging area, of row d (0..127, the wave's own
 // rows) of token column tl: the 8-byte slot d / 4 of the token row, swizzled.
 __device__ __forceinline__ int target_slot(int d, int tl) {
-  return tl * 256 + (((d >> 2) ^ (tl & 31)) * 8) + 2 * (d & 3);
+  return tl * 256 + (((d >> 2) ^ token_swizzle(tl)) * 8) + 2 * (d & 3);
 }
 
 // The value of accumulator element (i, j, r) is get(i, j, r): the element
@@ -735,7 +744,7 @@ __device__ __forceinline__ void store_token_major(const Get& get, char* smem, in
       }
       const uint32_t lo = pack_bf16x2(v[0], v[1]);
       const uint32_t hi = pack_bf16x2(v[2], v[3]);
-      const int slot = (i * 4 + g) ^ (tl & 31);
+      const int slot = (i * 4 + g) ^ token_swizzle(tl);
       *reinterpret_cast<uint2*>(reg + tl * 256 + slot * 8) = make_uint2(lo, hi);
     }
   }
@@ -755,9 +764,9 @@ __device__ __forceinline__ void store_token_major(const Get& get, char* smem, in
     // contiguous KiB.
 #pragma unroll 4
     for (int q = 0; q < 32; ++q) {
-      const int tl = (q & 7) * 16 + (lane >> 2), ch = (q >> 3) * 4 + (lane & 3), x = tl & 31;
-      u32x4 v = *reinterpret_cast<const u32x4*>(reg + tl * 256 + (((2 * ch) ^ x) & ~1) * 8);
-      if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+      const int tl = (q & 7) * 16 + (lane >> 2), ch = (q >> 3) * 4 + (lane & 3);
+      const u32x4 v =
+          *reinterpret_cast<const u32x4*>(reg + tl * 256 + ((2 * ch) ^ token_swizzle(tl)) * 8);
       const int64_t t = n0 + wn * 128 + tl;
       const int64_t vl = m0 + wm * 128 + 8 * ch;
       if (t < nt && vl < nv)
@@ -767,9 +776,9 @@ __device__ __forceinline__ void store_token_major(const Get& get, char* smem, in
 #pragma unroll 4
     for (int q = 0; q < 32; ++q) {
       const int idx = q * 64 + lane;
-      const int tl = idx >> 4, ch = idx & 15, x = tl & 31;
-      u32x4 v = *reinterpret_cast<const u32x4*>(reg + tl * 256 + (((2 * ch) ^ x) & ~1) * 8);
-      if (x & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+      const int tl = idx >> 4, ch = idx & 15;
+      const u32x4 v =
+          *reinterpret_cast<const u32x4*>(reg + tl * 256 + ((2 * ch) ^ token_swizzle(tl)) * 8);
       const int64_t t = n0 + wn * 128 + tl;
       const int64_t vl = m0 + wm * 128 + 8 * ch;
       if (t < nt && vl < nv) *reinterpret_cast<u32x4*>(dst + t * ld + vl) = v;
