@@ -115,6 +115,27 @@ __device__ __forceinline__ void issue_one(const DirectLoads<L>& d, int64_t kt, c
 #endif
 }
 
+// Per-token inputs of an epilogue, staged in LDS past the pipeline stages:
+// W 4-byte words per token (W = 1 for float, 2 for int64) of the workgroup's
+// 256 token columns n0 .. n0 + 255 (clamped to the last of n tokens), loaded
+// with direct-to-LDS loads when the kernel starts, so that their latency
+// passes under the K loop instead of stalling the epilogue. Thread tid of
+// wave w issues word e = q * 256 + tid of pass q into lds[4 e].
+template <int W>
+__device__ __forceinline__ void stage_tokens(char* lds, const void* src, int64_t n0, int64_t n,
+                                             int wave, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+  for (int q = 0; q < W; ++q) {
+    const int e = q * 256 + wave * 64 + lane;
+    const int64_t t = n0 + e / W;
+    const char* p = static_cast<const char*>(src) + ((t < n ? t : n - 1) * W + e % W) * 4;
+    __builtin_amdgcn_global_load_lds(
+        p, (__attribute__((address_space(3))) void*)(lds + (q * 256 + wave * 64) * 4), 4, 0, 0);
+  }
+#endif
+}
+
 // Register path for a partial last stage tile: zero-filled past K (and past
 // the matrix edge), then stored into the same LDS layout.
 template <int FORM, int SK>
@@ -351,12 +372,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A_, Operand B_, in
   static_assert(2 * L == (SK == 64 ? 16 : 8), "waitcnt immediates");
   static_assert(SK == 64 ? kStages == 2 : (kStages == 4 || kStages == 5), "pipeline depth");
   // the stages; reused by the epilogues (32 KiB per wave)
-  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
+  // plus the epilogue's per-token inputs (stage_tokens), past the stages
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes + Epi::kTokBytes];
   int64_t m0, n0;
   gemm::tile_coords(blockIdx.x, M, Nn, group_m, m0, n0);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
+  // first in the queue, so every later counted wait of the pipeline covers it
+  epi.stage(smem + kSmemBytes, n0, wave, lane);
 
   Acc acc;
 #pragma unroll
@@ -497,7 +521,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A_, Operand B_, in
     stage_barrier();
   }
   __syncthreads();
-  epi(acc, m0, n0, wm, wn, lane, smem);
+  epi(acc, m0, n0, wm, wn, lane, smem, smem + kSmemBytes);
 }
 
 // tanh(x) = 1 - 2 / (exp(2x) + 1), from the hardware exp2 and reciprocal.
@@ -614,8 +638,14 @@ struct EpiLse {
   int64_t ld_logits;
   int vec;       // 16-byte runs of the logits rows are aligned
 
+  static constexpr int kTokBytes = 2048;          // the tile's labels
+  __device__ __forceinline__ void stage(char* tok, int64_t n0, int wave, int lane) const {
+    stage_tokens<2>(tok, labels, n0, N, wave, lane);
+  }
+
   __device__ __forceinline__ void operator()(Acc& acc, int64_t m0, int64_t n0, int wm, int wn,
-                                             int lane, char* smem) const {
+                                             int lane, char* smem, const char* tok) const {
+    const int64_t* lab = reinterpret_cast<const int64_t*>(tok);
     const int g = lane >> 4;
     const int64_t vbase = m0 + wm * 128;
     float mx[8], sm[8];
@@ -637,7 +667,7 @@ struct EpiLse {
           if (OUT != kNoLogits) acc[i][j][r] = z[i][r];
         }
       // target logit: the one lane holding (y_t, t) writes it
-      const int64_t y = t < N ? labels[t] : ignore_index;
+      const int64_t y = t < N ? lab[acc_col(wn, j, lane)] : ignore_index;
       if (y != ignore_index && y >= vbase && y < vbase + 128 && y < V) {
         const int d = int(y - vbase);
         const int ti = d >> 4, tr = d & 3;
@@ -805,6 +835,14 @@ struct EpiGrad {
   uint16_t* g;
   int64_t lo_off;   // elements from the hi to the lo chunk (SPLIT)
 
+  // the tile's labels, lse and target logits
+  static constexpr int kTokBytes = 4096;
+  __device__ __forceinline__ void stage(char* tok, int64_t n0, int wave, int lane) const {
+    stage_tokens<2>(tok, labels, n0, N, wave, lane);
+    stage_tokens<1>(tok + 2048, lse, n0, N, wave, lane);
+    stage_tokens<1>(tok + 3072, zt, n0, N, wave, lane);
+  }
+
   // Every element is first formed as if it were not the target:
   // c exp(z' - lse) dz'/dz = exp2(z' log2 e + log2 c - lse log2 e) dz'/dz, the
   // scale folded into the exponent (c = 0 for ignored tokens gives exact
@@ -813,7 +851,10 @@ struct EpiGrad {
   // c (exp(z'_y - lse) - 1) dz'/dz from the forward's target logit, which is
   // the same float32 value the GEMM recomputes.
   __device__ __forceinline__ void operator()(Acc& acc, int64_t m0, int64_t n0, int wm, int wn,
-                                             int lane, char* smem) const {
+                                             int lane, char* smem, const char* tok) const {
+    const int64_t* lab = reinterpret_cast<const int64_t*>(tok);
+    const float* lse_t = reinterpret_cast<const float*>(tok + 2048);
+    const float* zt_t = reinterpret_cast<const float*>(tok + 3072);
     const float c = sc->c32;
     const int lg = lane >> 4;                           // the lane's row group
     const int64_t vbase = v0 + m0 + wm * 128;           // global vocab id of block row 0
@@ -824,20 +865,20 @@ struct EpiGrad {
       const int tl = j * 16 + (lane & 15);             // token within the wave block
       const int64_t t = n0 + wn * 128 + tl;
       // Every token's lse is known (ignored ones too) and columns past N hold
-      // the logits of token N-1, so exp(z' - lse) <= 1 everywhere.
-      const int64_t tc = t < N ? t : N - 1;
-      const float l = lse[tc];
+      // the logits of token N-1 (staged lse clamped the same way), so
+      // exp(z' - lse) <= 1 everywhere.
+      const float l = lse_t[wn * 128 + tl];
       float coef = 0.f;
       tp.pos[j] = -1;
       tp.val[j] = 0.f;
       if (t < N) {
-        const int64_t y = labels[t];
+        const int64_t y = lab[wn * 128 + tl];
         if (y != ignore_index) {
           coef = (y < 0 || y >= V) ? NAN : c;
           if (y >= vbase && y < vbase + 128) {
             const int d = int(y - vbase);
             if (((d >> 2) & 3) == lg) {
-              const float z = zt[t];
+              const float z = zt_t[wn * 128 + tl];
               float dd = 1.f;
               if (SOFTCAP) {
                 const float th = z * inv_softcap;
@@ -899,8 +940,14 @@ struct EpiLseP {
   uint16_t* probs;  // blocked, pblk elements per 32 vocabulary columns
   int64_t pblk;
 
+  static constexpr int kTokBytes = 2048;          // the tile's labels
+  __device__ __forceinline__ void stage(char* tok, int64_t n0, int wave, int lane) const {
+    stage_tokens<2>(tok, labels, n0, N, wave, lane);
+  }
+
   __device__ __forceinline__ void operator()(Acc& acc, int64_t m0, int64_t n0, int wm, int wn,
-                                             int lane, char* smem) const {
+                                             int lane, char* smem, const char* tok) const {
+    const int64_t* lab = reinterpret_cast<const int64_t*>(tok);
     const int g = lane >> 4;
     const int64_t vbase = m0 + wm * 128;
     float mx[8];
@@ -916,7 +963,7 @@ struct EpiLseP {
           const int64_t v = m0 + acc_row(wm, i, r, lane);
           acc[i][j][r] = v < V ? z : -INFINITY;
         }
-      const int64_t y = t < N ? labels[t] : ignore_index;
+      const int64_t y = t < N ? lab[acc_col(wn, j, lane)] : ignore_index;
       if (y != ignore_index && y >= vbase && y < vbase + 128 && y < V) {
         const int d = int(y - vbase);
         const int ti = d >> 4, tr = d & 3;
@@ -1101,8 +1148,11 @@ struct EpiDW {
     }
   };
 
+  static constexpr int kTokBytes = 0;             // no per-token inputs
+  __device__ __forceinline__ void stage(char*, int64_t, int, int) const {}
+
   __device__ __forceinline__ void operator()(Acc& acc, int64_t m0, int64_t n0, int wm, int wn,
-                                             int lane, char* smem) const {
+                                             int lane, char* smem, const char*) const {
     Pass pass{*this, m0 + wm * 128, n0 + wn * 128};
     staged_rows(acc, wm, wn, lane, smem, pass);
   }
@@ -1130,8 +1180,11 @@ struct EpiDW32 {
     }
   };
 
+  static constexpr int kTokBytes = 0;             // no per-token inputs
+  __device__ __forceinline__ void stage(char*, int64_t, int, int) const {}
+
   __device__ __forceinline__ void operator()(Acc& acc, int64_t m0, int64_t n0, int wm, int wn,
-                                             int lane, char* smem) const {
+                                             int lane, char* smem, const char*) const {
     Pass pass{*this, m0 + wm * 128, n0 + wn * 128};
     staged_rows(acc, wm, wn, lane, smem, pass);
   }
@@ -1177,8 +1230,11 @@ struct EpiDH {
     }
   };
 
+  static constexpr int kTokBytes = 0;             // no per-token inputs
+  __device__ __forceinline__ void stage(char*, int64_t, int, int) const {}
+
   __device__ __forceinline__ void operator()(Acc& acc, int64_t m0, int64_t n0, int wm, int wn,
-                                             int lane, char* smem) const {
+                                             int lane, char* smem, const char*) const {
     Pass pass{*this, m0 + wm * 128, n0 + wn * 128, {}};
     staged_rows(acc, wm, wn, lane, smem, pass);
   }
