@@ -18,7 +18,7 @@ namespace flce {
 namespace gemm {
 
 constexpr int kBM = 256;                // tile edge (M and N)
-constexpr int kBK = 32;                 // K per MFMA step (two 16-wide substeps)
+constexpr int kBK = 32;                 // K per MFMA step (one 16x16x32 MFMA deep)
 constexpr int kGroupM = 4;              // M tiles per raster group
 
 enum Form : int { kFormN = 0, kFormT = 1 };

@@ -353,42 +353,18 @@ __device__ __forceinline__ void k_step(Acc& acc, const StepFrags& cur, StepFrags
   }
 }
 
-template <int FA, int FB, class Epi, bool BA>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A_, Operand B_, int64_t M,
-                                                      int64_t Nn, int64_t K, int group_m,
-                                                      Epi epi) {
-  // BA: operand A is the blocked G (gemm::Geom). Fixing blk at compile time
-  // for the dense operands lets the address arithmetic drop the blocked case.
-  Operand A = A_, B = B_;
-  if constexpr (!BA) A.g.blk = 0;
-  B.g.blk = 0;
+// The K loop of one tile: acc += A[m0 .. m0 + 255][0, K) . B[n0 .. n0 + 255][0, K)^T
+// through the LDS stages at smem: a partial last stage tile first (through
+// registers), then the pipelined full stage tiles. Every wave leaves it
+// behind a barrier, with no load in flight.
+template <int FA, int FB>
+__device__ __forceinline__ void k_loop(Acc& acc, const Operand& A, const Operand& B, int64_t K,
+                                       int64_t m0, int64_t n0, char* smem, int tid, int lane,
+                                       int wave, int wm, int wn) {
   constexpr int SK = gemm::stage_k(FA, FB);
   constexpr int kStages = gemm::num_stages(FA, FB);
   constexpr int L = gemm::loads_per_operand(SK);
   constexpr int kTileBytes = kBM * SK * 2;          // one operand, one stage
-  constexpr int kSmemBytes = kStages * 2 * kTileBytes;   // 128 or 160 KiB
-  static_assert(kSmemBytes >= 4 * kWaveScratch, "epilogue staging");
-  static_assert(kBK == 32 && (SK == 32 || SK == 64), "MFMA steps of 32 k");
-  static_assert(2 * L == (SK == 64 ? 16 : 8), "waitcnt immediates");
-  static_assert(SK == 64 ? kStages == 2 : (kStages == 4 || kStages == 5), "pipeline depth");
-  // the stages; reused by the epilogues (32 KiB per wave)
-  // plus the epilogue's per-token inputs (stage_tokens), past the stages
-  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes + Epi::kTokBytes];
-  int64_t m0, n0;
-  gemm::tile_coords(blockIdx.x, M, Nn, group_m, m0, n0);
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
-  // first in the queue, so every later counted wait of the pipeline covers it
-  epi.stage(smem + kSmemBytes, n0, wave, lane);
-
-  Acc acc;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
 
   const DirectLoads<L> da = setup_direct<FA, SK>(A, m0, wave, lane);
   const DirectLoads<L> db = setup_direct<FB, SK>(B, n0, wave, lane);
@@ -520,6 +496,52 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A_, Operand B_, in
     wait_vm0();
     stage_barrier();
   }
+}
+
+template <int FA, int FB, class Epi, bool BA, int SEGS>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A_, Operand B_, int64_t M,
+                                                      int64_t Nn, int64_t K, int group_m,
+                                                      Epi epi, int64_t a2_off) {
+  // BA: operand A is the blocked G (gemm::Geom). Fixing blk at compile time
+  // for the dense operands lets the address arithmetic drop the blocked case.
+  // SEGS = 2: a second K loop over A shifted by a2_off elements (the lo half
+  // of a split G) against the same B, into the same accumulators, so the
+  // tile is (A + A2) . B^T with one epilogue.
+  static_assert(SEGS == 1 || SEGS == 2, "one or two K segments");
+  Operand A = A_, B = B_;
+  if constexpr (!BA) A.g.blk = 0;
+  B.g.blk = 0;
+  constexpr int SK = gemm::stage_k(FA, FB);
+  constexpr int kStages = gemm::num_stages(FA, FB);
+  constexpr int L = gemm::loads_per_operand(SK);
+  constexpr int kTileBytes = kBM * SK * 2;          // one operand, one stage
+  constexpr int kSmemBytes = kStages * 2 * kTileBytes;   // 128 or 160 KiB
+  static_assert(kSmemBytes >= 4 * kWaveScratch, "epilogue staging");
+  static_assert(kBK == 32 && (SK == 32 || SK == 64), "MFMA steps of 32 k");
+  static_assert(2 * L == (SK == 64 ? 16 : 8), "waitcnt immediates");
+  static_assert(SK == 64 ? kStages == 2 : (kStages == 4 || kStages == 5), "pipeline depth");
+  // the stages; reused by the epilogues (32 KiB per wave)
+  // plus the epilogue's per-token inputs (stage_tokens), past the stages
+  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes + Epi::kTokBytes];
+  int64_t m0, n0;
+  gemm::tile_coords(blockIdx.x, M, Nn, group_m, m0, n0);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  // first in the queue, so every later counted wait of the pipeline covers it
+  epi.stage(smem + kSmemBytes, n0, wave, lane);
+
+  Acc acc;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.f;
+
+  k_loop<FA, FB>(acc, A, B, K, m0, n0, smem, tid, lane, wave, wm, wn);
+  if constexpr (SEGS == 2)
+    k_loop<FA, FB>(acc, Operand{A.ptr + a2_off, A.g}, B, K, m0, n0, smem, tid, lane, wave, wm, wn);
   __syncthreads();
   epi(acc, m0, n0, wm, wn, lane, smem, smem + kSmemBytes);
 }
@@ -1266,16 +1288,16 @@ bool launch_ok(const gemm::Launch& l) {
   return l.M > 0 && l.Nn > 0 && l.K > 0;
 }
 
-template <int FA, int FB, bool BA = false, class Epi>
+template <int FA, int FB, bool BA = false, int SEGS = 1, class Epi>
 hipError_t run_gemm(const gemm::Launch& l, const Args& a, const Epi& e, int kind,
-                    const Launcher& L) {
+                    const Launcher& L, int64_t a2_off = 0) {
   if (!launch_ok(l)) return hipErrorInvalidValue;
   if ((l.a.blk != 0) != BA || l.b.blk != 0) return hipErrorInvalidValue;
   Operand A{buf_ptr(a, l.buf_a) + l.off_a, l.a};
   Operand B{buf_ptr(a, l.buf_b) + l.off_b, l.b};
   L.pre(kind);
-  hipLaunchKernelGGL((k_gemm<FA, FB, Epi, BA>), dim3(unsigned(gemm::num_tiles(l.M, l.Nn))),
-                     dim3(kThreads), 0, L.stream, A, B, l.M, l.Nn, l.K, gemm::kGroupM, e);
+  hipLaunchKernelGGL((k_gemm<FA, FB, Epi, BA, SEGS>), dim3(unsigned(gemm::num_tiles(l.M, l.Nn))),
+                     dim3(kThreads), 0, L.stream, A, B, l.M, l.Nn, l.K, gemm::kGroupM, e, a2_off);
   L.post(kind);
   return hipGetLastError();
 }
@@ -1307,8 +1329,9 @@ hipError_t bf16_forward(const Plan& p, const Args& a, const Launcher& L) {
 }
 
 // Float32 gradients for bf16 inputs: G as a bf16 hi + lo pair; dW and dH
-// each take one GEMM per part, hi then lo, accumulated in float32 straight
-// into the outputs in a fixed order (chunk by chunk, hi before lo).
+// each take one GEMM whose K loop runs over the hi part and then the lo part
+// into the same float32 accumulators, added into the float32 outputs chunk by
+// chunk in a fixed order.
 hipError_t bf16_backward_chunk_f32grad(const Plan& p, const Args& a, int64_t chunk,
                                        const Launcher& L) {
   const int64_t v0 = chunk * p.vchunk;
@@ -1327,27 +1350,23 @@ hipError_t bf16_backward_chunk_f32grad(const Plan& p, const Args& a, int64_t chu
     err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
                                                kGradLogits, L);
   }
+  if (err != hipSuccess) return err;
   float* dW = static_cast<float*>(a.dW);
-  for (int part = 0; part < 2 && err == hipSuccess; ++part) {
-    const gemm::Launch lw = gemm::backward_launch(p, chunk, 1, part);
-    if (part == 0 && !a.accumulate_dW)
-      err = run_gemm<gemm::kFormT, gemm::kFormT, true>(lw, a, EpiDW32<false>{dW, p.H, v0, vcur},
-                                                       kGemmDW, L);
-    else
-      err = run_gemm<gemm::kFormT, gemm::kFormT, true>(lw, a, EpiDW32<true>{dW, p.H, v0, vcur},
-                                                       kGemmDW, L);
-  }
+  const gemm::Launch lw = gemm::backward_launch(p, chunk, 1, 0);
+  if (!a.accumulate_dW)
+    err = run_gemm<gemm::kFormT, gemm::kFormT, true, 2>(lw, a, EpiDW32<false>{dW, p.H, v0, vcur},
+                                                        kGemmDW, L, lo_off);
+  else
+    err = run_gemm<gemm::kFormT, gemm::kFormT, true, 2>(lw, a, EpiDW32<true>{dW, p.H, v0, vcur},
+                                                        kGemmDW, L, lo_off);
+  if (err != hipSuccess) return err;
   float* dH = static_cast<float*>(a.dH);
-  for (int part = 0; part < 2 && err == hipSuccess; ++part) {
-    const gemm::Launch lh = gemm::backward_launch(p, chunk, 2, part);
-    if (chunk == 0 && part == 0)
-      err = run_gemm<gemm::kFormN, gemm::kFormT, true>(
-          lh, a, EpiDH<true, false>{nullptr, dH, p.N, p.H}, kGemmDH, L);
-    else
-      err = run_gemm<gemm::kFormN, gemm::kFormT, true>(
-          lh, a, EpiDH<false, false>{nullptr, dH, p.N, p.H}, kGemmDH, L);
-  }
-  return err;
+  const gemm::Launch lh = gemm::backward_launch(p, chunk, 2, 0);
+  if (chunk == 0)
+    return run_gemm<gemm::kFormN, gemm::kFormT, true, 2>(
+        lh, a, EpiDH<true, false>{nullptr, dH, p.N, p.H}, kGemmDH, L, lo_off);
+  return run_gemm<gemm::kFormN, gemm::kFormT, true, 2>(
+      lh, a, EpiDH<false, false>{nullptr, dH, p.N, p.H}, kGemmDH, L, lo_off);
 }
 
 hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, const Launcher& L) {
