@@ -40,7 +40,7 @@ hipEvent_t take_event() {
 void prof_before(int kind, hipStream_t s) {
   hipEvent_t e = take_event();
   if (!e) return;
-  hipEventRecord(e, s);
+  if (hipEventRecord(e, s) != hipSuccess) { g_prof.failed = true; return; }
   g_prof.pending = e;
   g_prof.pending_kind = kind;
 }
@@ -49,7 +49,7 @@ void prof_after(int kind, hipStream_t s) {
   if (!g_prof.pending || g_prof.pending_kind != kind) return;
   hipEvent_t e = take_event();
   if (!e) return;
-  hipEventRecord(e, s);
+  if (hipEventRecord(e, s) != hipSuccess) { g_prof.failed = true; g_prof.pending = nullptr; return; }
   g_prof.recs.push_back(Rec{kind, g_prof.pending, e});
   g_prof.pending = nullptr;
 }

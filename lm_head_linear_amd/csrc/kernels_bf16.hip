@@ -101,6 +101,8 @@ __device__ __forceinline__ void issue_direct(const DirectLoads<L>& d, int64_t kt
     __builtin_amdgcn_global_load_lds(
         b + d.off[q], (__attribute__((address_space(3))) void*)(lds + (L * wave + q) * 1024), 16,
         0, 0);
+#else
+  (void)d, (void)kt, (void)lds, (void)wave;
 #endif
 }
 
@@ -112,6 +114,8 @@ __device__ __forceinline__ void issue_one(const DirectLoads<L>& d, int64_t kt, c
   __builtin_amdgcn_global_load_lds(
       d.base + kt * d.kstep + d.off[q],
       (__attribute__((address_space(3))) void*)(lds + (L * wave + q) * 1024), 16, 0, 0);
+#else
+  (void)d, (void)kt, (void)lds, (void)wave, (void)q;
 #endif
 }
 
@@ -133,6 +137,8 @@ __device__ __forceinline__ void stage_tokens(char* lds, const void* src, int64_t
     __builtin_amdgcn_global_load_lds(
         p, (__attribute__((address_space(3))) void*)(lds + (q * 256 + wave * 64) * 4), 4, 0, 0);
   }
+#else
+  (void)lds, (void)src, (void)n0, (void)n, (void)wave, (void)lane;
 #endif
 }
 

@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void k_loss_final(const double* __restrict__ l
   red[threadIdx.x] = s;
   __syncthreads();
   for (int k = 128; k > 0; k >>= 1) {
-    if (threadIdx.x < k) red[threadIdx.x] += red[threadIdx.x + k];
+    if (int(threadIdx.x) < k) red[threadIdx.x] += red[threadIdx.x + k];
     __syncthreads();
   }
   if (threadIdx.x == 0) *loss = sc->n_bad ? NAN : float(sc->c64 * red[0]);
