@@ -109,6 +109,66 @@ def cpu_baseline(w, n_sample: int):
     }
 
 
+def other_configs(steps: int, warmup: int):
+    """The full step (flce_forward_backward, bf16) on the other full-size
+    configurations: small, softcapped, and long, as one call and as its four
+    micro-batches with the shared external token count and dW added up across
+    them. Prints one JSON line of its own (not the benchmark line)."""
+    import torch
+    import flce_inputs as fi
+    import lm_head_linear_amd as m
+    from lm_head_linear_amd import _lib
+    _lib.load()
+    dev = torch.device("cuda:0")
+    out = {}
+    for k in (2, 4, 5):
+        w = fi.make_workload(k)
+        N, H, V = w.N, w.H, w.V
+        h = w.h.reshape(N, H).to(dev)
+        W = w.W.to(dev)
+        y = w.labels.reshape(N).to(dev)
+        dH, dW = torch.empty_like(h), torch.empty_like(W)
+        loss = torch.empty((), dtype=torch.float32, device=dev)
+        nt = torch.empty((), dtype=torch.int64, device=dev)
+        kw = dict(ignore_index=w.ignore_index, softcap=w.softcap, reduction=w.reduction,
+                  num_label_tokens=w.num_label_tokens, loss=loss, num_tokens=nt)
+        ws = torch.empty(m.flce_workspace_size(N, H, V, W.dtype), dtype=torch.uint8, device=dev)
+        runs = {"one_call": lambda: m.flce_forward_backward(h, W, y, dH=dH, dW=dW, workspace=ws,
+                                                             **kw)}
+        if w.micro_batches > 1:
+            nb = N // w.micro_batches
+            wsm = torch.empty(m.flce_workspace_size(nb, H, V, W.dtype), dtype=torch.uint8,
+                              device=dev)
+
+            def micro():
+                for i in range(w.micro_batches):
+                    s = slice(i * nb, (i + 1) * nb)
+                    m.flce_forward_backward(h[s], W, y[s], dH=dH[s], dW=dW, workspace=wsm,
+                                            accumulate_dW=i > 0,
+                                            mb_scale=m.micro_batch_scale(0, 0, w.reduction), **kw)
+            runs[f"{w.micro_batches}_micro_batches"] = micro
+        res = {"N": N, "H": H, "V": V, "softcap": w.softcap, "reduction": w.reduction}
+        for name, fn in runs.items():
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            res[name] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(N / ms * 1e3, 1),
+                         "mfma_frac_8nhv": round(8.0 * N * H * V / (ms * 1e-3) / 1e12
+                                                 / PEAK_BF16_TFLOPS, 4)}
+            log(f"{w.name} {name}: {ms:.3f} ms/step")
+        out[w.name] = res
+        del h, W, y, dH, dW, ws, runs
+        torch.cuda.empty_cache()
+    print(json.dumps({"configs": out}), flush=True)
+
+
 def copy_calibration(size_mib: int, reps: int):
     """A plain device copy of known size, to scale the HBM byte counters."""
     import torch
@@ -251,6 +311,9 @@ def main():
                          "no-recompute figures), e.g. for per-kernel counter runs")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain copy of this size (counter calibration)")
+    ap.add_argument("--configs", action="store_true",
+                    help="only time the full step on the small, softcapped and long "
+                         "configurations (one JSON line of its own)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -265,6 +328,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 10)
+        return
+    if args.configs:
+        other_configs(args.steps, args.warmup)
         return
 
     import flce_inputs as fi
