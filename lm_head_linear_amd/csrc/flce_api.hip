@@ -56,7 +56,7 @@ void prof_after(int kind, hipStream_t s) {
 
 const char* kKindNames[flce::kNumKinds] = {"label_scan", "lse_fwd_gemm", "lse_merge",
                                            "loss_final", "grad_logits_gemm", "dW_gemm",
-                                           "dH_gemm", "fill", "probs_to_grad"};
+                                           "dH_gemm", "fill", "probs_to_grad", "dH_reduce"};
 
 // The no-recompute variant (arguments already checked): token chunk by chunk,
 // the forward keeps the probabilities, the chunk's merge gives its lse, G is
@@ -93,6 +93,7 @@ int run_nr(const void* h, const void* W, const int64_t* labels, int64_t N, int64
   a.lsum = reinterpret_cast<double*>(ws + p.off_lsum);
   a.g = ws + p.off_g;
   a.dh_acc = nullptr;
+  a.dh_part = p.dh_kseg ? reinterpret_cast<float*>(ws + p.off_dhpart) : nullptr;
   e = flce::launch_label_scan(p, a, L);
   for (int64_t c = 0; e == hipSuccess && c < p.n_tok_chunks; ++c) {
     e = flce::bf16_nr_forward_chunk(p, a, c, L);
@@ -143,6 +144,7 @@ int run(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t 
   a.lsum = reinterpret_cast<double*>(ws + p.off_lsum);
   a.g = backward ? ws + p.off_g : nullptr;
   a.dh_acc = p.need_dh_acc ? reinterpret_cast<float*>(ws + p.off_dhacc) : nullptr;
+  a.dh_part = p.dh_kseg ? reinterpret_cast<float*>(ws + p.off_dhpart) : nullptr;
 
   const bool bf16 = dtype == FLCE_BF16;
   e = flce::launch_label_scan(p, a, L);

@@ -58,6 +58,8 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
   q.n_loss_blocks = ceil_div(N > 0 ? N : 1, 32);   // tokens per lse-merge block
   q.backward = backward;
   q.need_dh_acc = backward && (dtype == FLCE_BF16) && q.g_parts == 1 && q.n_chunks > 1 && N > 0;
+  if (backward && dtype == FLCE_BF16 && q.g_parts == 1 && N > 0)
+    q.dh_kseg = dh_split(N, H, q.vchunk, &q.dh_segs);
 
   size_t off = 0;
   q.off_scalars = off; off = align256(off + sizeof(Scalars));
@@ -71,6 +73,10 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
       off = align256(off + size_t(q.g_parts) * size_t(q.vchunk) * q.ldg * q.elem);
     }
     if (q.need_dh_acc) { q.off_dhacc = off; off = align256(off + size_t(N) * H * sizeof(float)); }
+    if (q.dh_kseg) {
+      q.off_dhpart = off;
+      off = align256(off + size_t(q.dh_segs) * size_t(N) * H * sizeof(float));
+    }
   }
   q.total = off;
   *p = q;
@@ -108,6 +114,12 @@ bool make_plan_nr(int64_t N, int64_t H, int64_t V, int dtype, int64_t token_chun
     q.off_lse = off;   off = align256(off + size_t(q.ld_part) * sizeof(float));
     q.off_lsum = off;  off = align256(off + size_t(q.n_loss_blocks) * sizeof(double));
     q.off_g = off;     off = align256(off + size_t(nc) * size_t(q.vp) * q.elem);
+    // dH of a token chunk: M = its tokens, K = the whole vocabulary
+    q.dh_kseg = dh_split(nc, H, V, &q.dh_segs);
+    if (q.dh_kseg) {
+      q.off_dhpart = off;
+      off = align256(off + size_t(q.dh_segs) * size_t(nc) * H * sizeof(float));
+    }
   }
   q.off_dhacc = 0;
   q.need_dh_acc = false;

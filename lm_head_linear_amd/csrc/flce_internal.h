@@ -20,7 +20,8 @@ enum Kind : int {
   kGemmDH = 6,
   kFill = 7,
   kProbsToGrad = 8,
-  kNumKinds = 9,
+  kDhReduce = 9,
+  kNumKinds = 10,
 };
 
 // Everything one call needs on the device side.
@@ -53,6 +54,7 @@ struct Args {
   double* lsum;
   void* g;        // G^T chunk [vchunk][ldg]
   float* dh_acc;  // [N][H] (bf16 path with several chunks)
+  float* dh_part; // [dh_segs][M][H] split-K partial products of dH (or null)
 };
 
 // Launch hook: the C-ABI layer brackets launches with timing events.

@@ -20,6 +20,28 @@ constexpr int64_t kChunkElems = int64_t(1) << 27;
 constexpr int64_t kMaxLdBF16 = int64_t(1) << 22;
 // Workgroups of one GEMM launch (256 x 256 tiles) must fit a grid dimension.
 constexpr int64_t kMaxTiles = (int64_t(1) << 31) - 1;
+// Split-K of the dH GEMM: when its M x Nn output has fewer than kSplitTiles
+// tiles of 256 x 256 (half the CUs), its K (vocabulary rows) is split into
+// up to kMaxSplits segments of at least kMinSplitK, one workgroup per
+// (tile, segment), whose float32 partial products a fixed-order reduction
+// then adds up.
+constexpr int64_t kSplitTiles = 128;
+constexpr int64_t kMaxSplits = 8;
+constexpr int64_t kMinSplitK = 2048;
+
+// The segment length (a multiple of 64) for a dH GEMM with an M x Nn output
+// and K = k, or 0 when it is not split; *segs gets the segment count.
+inline int64_t dh_split(int64_t M, int64_t Nn, int64_t k, int64_t* segs) {
+  const int64_t tiles = ((M + 255) / 256) * ((Nn + 255) / 256);
+  int64_t s = tiles > 0 ? 256 / tiles : 0;
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s > k / kMinSplitK) s = k / kMinSplitK;
+  if (tiles >= kSplitTiles || s < 2) { *segs = 1; return 0; }
+  int64_t kseg = (k + s - 1) / s;
+  kseg = (kseg + 63) / 64 * 64;
+  *segs = (k + kseg - 1) / kseg;
+  return *segs > 1 ? kseg : 0;
+}
 
 // Whether the bf16 shapes fit the kernels' index arithmetic.
 inline bool bf16_shape_ok(int64_t N, int64_t H, int64_t V) {
@@ -58,11 +80,15 @@ struct Plan {
   bool nr = false;
   int64_t nc = 0, n_tok_chunks = 0, vp = 0;
   bool need_dh_acc = false;  // float32 dH accumulator needed (bf16, >1 chunk)
+  // Split-K of the dH GEMM (bf16 gradients): segments of dh_kseg vocabulary
+  // rows (0: not split), at most dh_segs of them per launch, each writing a
+  // float32 [M][H] partial product at off_dhpart.
+  int64_t dh_kseg = 0, dh_segs = 1;
   size_t elem = 0;           // bytes per element of h/W/G
   size_t grad_elem = 0;      // bytes per element of dH/dW
   // byte offsets into the workspace
   size_t off_scalars = 0, off_part = 0, off_zt = 0, off_lse = 0, off_lsum = 0,
-         off_g = 0, off_dhacc = 0, total = 0;
+         off_g = 0, off_dhacc = 0, off_dhpart = 0, total = 0;
 };
 
 // Builds the plan; returns false for invalid sizes or dtypes. A forward-only

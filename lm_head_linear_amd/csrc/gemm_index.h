@@ -136,6 +136,27 @@ inline int64_t num_tiles(int64_t M, int64_t Nn) {
   return ((M + kBM - 1) / kBM) * ((Nn + kBM - 1) / kBM);
 }
 
+// Element offset that moves an operand's origin to k = k0 (k0 a multiple of
+// 32, so a blocked operand moves by whole blocks or block rows).
+FLCE_HD int64_t k_origin(int form, const Geom& g, int64_t k0) {
+  if (form == kFormN) return g.blk ? (k0 >> 5) * g.blk : k0;
+  return g.blk ? k0 * 32 : k0 * g.ld;
+}
+
+// Segment z (workgroup index y) of a launch split along K into segments of
+// kseg (a multiple of 64): operand origins moved to k0 = z kseg and K cut to
+// the segment. Each segment's products go to a partial output of their own.
+inline Launch split_segment(const Launch& l, int64_t kseg, int64_t z) {
+  Launch s = l;
+  const int64_t k0 = z * kseg;
+  s.K = (l.K - k0) < kseg ? (l.K - k0) : kseg;
+  s.off_a += k_origin(l.fa, l.a, k0);
+  s.off_b += k_origin(l.fb, l.b, k0);
+  s.a.K = s.K;
+  s.b.K = s.K;
+  return s;
+}
+
 // Workgroups are handed to the 8 XCDs round-robin. Give each XCD a contiguous
 // range of tiles, and order tiles within a range in groups of `group_m`
 // M-tiles so that the workgroups resident on one XCD share operand tiles in

@@ -504,7 +504,7 @@ __device__ __forceinline__ void k_loop(Acc& acc, const Operand& A, const Operand
   }
 }
 
-template <int FA, int FB, class Epi, bool BA, int SEGS>
+template <int FA, int FB, class Epi, bool BA, int SEGS, bool SPLITK>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A_, Operand B_, int64_t M,
                                                       int64_t Nn, int64_t K, int group_m,
                                                       Epi epi, int64_t a2_off) {
@@ -513,10 +513,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A_, Operand B_, in
   // SEGS = 2: a second K loop over A shifted by a2_off elements (the lo half
   // of a split G) against the same B, into the same accumulators, so the
   // tile is (A + A2) . B^T with one epilogue.
+  // SPLITK: the launch is split along K into segments of a2_off (a multiple
+  // of 64); workgroup row blockIdx.y takes segment blockIdx.y
+  // (gemm::split_segment) and its epilogue writes a partial product.
   static_assert(SEGS == 1 || SEGS == 2, "one or two K segments");
+  static_assert(!(SPLITK && SEGS == 2), "a split launch has one K segment per workgroup row");
   Operand A = A_, B = B_;
   if constexpr (!BA) A.g.blk = 0;
   B.g.blk = 0;
+  if constexpr (SPLITK) {
+    const int64_t k0 = int64_t(blockIdx.y) * a2_off;
+    K = (K - k0) < a2_off ? (K - k0) : a2_off;
+    A.ptr += gemm::k_origin(FA, A.g, k0);
+    B.ptr += gemm::k_origin(FB, B.g, k0);
+    A.g.K = K;
+    B.g.K = K;
+  }
   constexpr int SK = gemm::stage_k(FA, FB);
   constexpr int kStages = gemm::num_stages(FA, FB);
   constexpr int L = gemm::loads_per_operand(SK);
@@ -1268,6 +1280,70 @@ struct EpiDH {
   }
 };
 
+// ---- split-K dH: one K segment's float32 partial product -----------------
+// Segment blockIdx.y of the launch stores its tile of G . W (over its K
+// range) into part + blockIdx.y * N * H, [N][H] float32; k_dh_reduce adds
+// the segments up.
+struct EpiDHPart {
+  float* part;
+  int64_t N, H;
+
+  static constexpr int kTokBytes = 0;             // no per-token inputs
+  __device__ __forceinline__ void stage(char*, int64_t, int, int) const {}
+
+  __device__ __forceinline__ void operator()(Acc& acc, int64_t m0, int64_t n0, int wm, int wn,
+                                             int lane, char* smem, const char* tok) const {
+    EpiDH<true, false>{nullptr, part + int64_t(blockIdx.y) * N * H, N, H}(acc, m0, n0, wm, wn,
+                                                                         lane, smem, tok);
+  }
+};
+
+// The split-K partial products of dH added up in a fixed order (segment 0
+// first), after the float32 running sum of the earlier vocabulary chunks
+// when there is one (PRIOR), stored as the new running sum or, for the last
+// chunk, as bf16 dH rounded to nearest even (BF16OUT). Four consecutive
+// elements per thread; n4 = elements / 4, stride = elements per segment.
+template <bool PRIOR, bool BF16OUT>
+__global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ part, int segs,
+                                                   int64_t n4, int64_t stride,
+                                                   const float* prior, float* out32,
+                                                   uint16_t* out16) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n4;
+       i += int64_t(gridDim.x) * 256) {
+    float4 v = PRIOR ? reinterpret_cast<const float4*>(prior)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int z = 0; z < segs; ++z) {
+      const float4 q = reinterpret_cast<const float4*>(part + z * stride)[i];
+      v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
+    }
+    if (BF16OUT)
+      reinterpret_cast<uint2*>(out16)[i] = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+    else
+      reinterpret_cast<float4*>(out32)[i] = v;
+  }
+}
+
+hipError_t launch_dh_reduce(const float* part, int64_t segs, int64_t n, const float* prior,
+                            float* out32, uint16_t* out16, const Launcher& L) {
+  const int64_t n4 = n / 4;
+  const int64_t want = (n4 + 255) / 256;
+  const dim3 grid(unsigned(want < 4096 ? want : 4096));
+  L.pre(kDhReduce);
+  if (prior && out16)
+    hipLaunchKernelGGL((k_dh_reduce<true, true>), grid, dim3(256), 0, L.stream, part, int(segs),
+                       n4, n, prior, out32, out16);
+  else if (prior)
+    hipLaunchKernelGGL((k_dh_reduce<true, false>), grid, dim3(256), 0, L.stream, part, int(segs),
+                       n4, n, prior, out32, out16);
+  else if (out16)
+    hipLaunchKernelGGL((k_dh_reduce<false, true>), grid, dim3(256), 0, L.stream, part, int(segs),
+                       n4, n, prior, out32, out16);
+  else
+    hipLaunchKernelGGL((k_dh_reduce<false, false>), grid, dim3(256), 0, L.stream, part,
+                       int(segs), n4, n, prior, out32, out16);
+  L.post(kDhReduce);
+  return hipGetLastError();
+}
+
 const uint16_t* buf_ptr(const Args& a, int buf) {
   return buf == gemm::kBufW ? static_cast<const uint16_t*>(a.W)
        : buf == gemm::kBufH ? static_cast<const uint16_t*>(a.h)
@@ -1294,16 +1370,17 @@ bool launch_ok(const gemm::Launch& l) {
   return l.M > 0 && l.Nn > 0 && l.K > 0;
 }
 
-template <int FA, int FB, bool BA = false, int SEGS = 1, class Epi>
+template <int FA, int FB, bool BA = false, int SEGS = 1, bool SPLITK = false, class Epi>
 hipError_t run_gemm(const gemm::Launch& l, const Args& a, const Epi& e, int kind,
-                    const Launcher& L, int64_t a2_off = 0) {
+                    const Launcher& L, int64_t a2_off = 0, int64_t segs = 1) {
   if (!launch_ok(l)) return hipErrorInvalidValue;
   if ((l.a.blk != 0) != BA || l.b.blk != 0) return hipErrorInvalidValue;
   Operand A{buf_ptr(a, l.buf_a) + l.off_a, l.a};
   Operand B{buf_ptr(a, l.buf_b) + l.off_b, l.b};
   L.pre(kind);
-  hipLaunchKernelGGL((k_gemm<FA, FB, Epi, BA, SEGS>), dim3(unsigned(gemm::num_tiles(l.M, l.Nn))),
-                     dim3(kThreads), 0, L.stream, A, B, l.M, l.Nn, l.K, gemm::kGroupM, e, a2_off);
+  hipLaunchKernelGGL((k_gemm<FA, FB, Epi, BA, SEGS, SPLITK>),
+                     dim3(unsigned(gemm::num_tiles(l.M, l.Nn)), unsigned(segs)), dim3(kThreads), 0,
+                     L.stream, A, B, l.M, l.Nn, l.K, gemm::kGroupM, e, a2_off);
   L.post(kind);
   return hipGetLastError();
 }
@@ -1408,6 +1485,15 @@ hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, cons
   uint16_t* dH = static_cast<uint16_t*>(a.dH);
   const gemm::Launch lh = gemm::backward_launch(p, chunk, 2);
   const bool first = chunk == 0, last = chunk == p.n_chunks - 1;
+  if (p.dh_kseg) {
+    // few output tiles: split K, then add the segments up in a fixed order
+    const int64_t segs = (lh.K + p.dh_kseg - 1) / p.dh_kseg;
+    err = run_gemm<gemm::kFormN, gemm::kFormT, true, 1, true>(
+        lh, a, EpiDHPart{a.dh_part, p.N, p.H}, kGemmDH, L, p.dh_kseg, segs);
+    if (err != hipSuccess) return err;
+    return launch_dh_reduce(a.dh_part, segs, p.N * p.H, first ? nullptr : a.dh_acc,
+                            last ? nullptr : a.dh_acc, last ? dH : nullptr, L);
+  }
   if (first && last)
     return run_gemm<gemm::kFormN, gemm::kFormT, true>(
         lh, a, EpiDH<true, true>{dH, a.dh_acc, p.N, p.H}, kGemmDH, L);
@@ -1469,8 +1555,17 @@ hipError_t bf16_nr_backward_chunk(const Plan& p, const Args& a, int64_t c, const
   if (err != hipSuccess) return err;
   // 3) dH[chunk] = G . W over the whole vocabulary
   uint16_t* dH = static_cast<uint16_t*>(a.dH) + t0 * p.H;
-  return run_gemm<gemm::kFormN, gemm::kFormT, true>(
-      gemm::nr_launch(p, c, 2), a, EpiDH<true, true>{dH, nullptr, nt, p.H}, kGemmDH, L);
+  const gemm::Launch lh = gemm::nr_launch(p, c, 2);
+  if (p.dh_kseg) {
+    // few output tiles: split K, then add the segments up in a fixed order
+    const int64_t segs = (lh.K + p.dh_kseg - 1) / p.dh_kseg;
+    err = run_gemm<gemm::kFormN, gemm::kFormT, true, 1, true>(
+        lh, a, EpiDHPart{a.dh_part, nt, p.H}, kGemmDH, L, p.dh_kseg, segs);
+    if (err != hipSuccess) return err;
+    return launch_dh_reduce(a.dh_part, segs, nt * p.H, nullptr, nullptr, dH, L);
+  }
+  return run_gemm<gemm::kFormN, gemm::kFormT, true>(lh, a, EpiDH<true, true>{dH, nullptr, nt, p.H},
+                                                    kGemmDH, L);
 }
 
 }  // namespace flce

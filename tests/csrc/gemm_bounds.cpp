@@ -169,6 +169,25 @@ static void check_launch(const Plan& p, const Launch& l) {
   }
 }
 
+// The segments of a split-K dH launch: every segment's loads in bounds, and
+// the segments cover K exactly once in order.
+static int64_t n_split_segments = 0;
+static void check_split(const Plan& p, const Launch& l) {
+  if (!p.dh_kseg) return;
+  if (p.dh_kseg % 64) fail("segment length", p.dh_kseg, l.K, 0);
+  const int64_t segs = (l.K + p.dh_kseg - 1) / p.dh_kseg;
+  if (segs > p.dh_segs) fail("more segments than carved", segs, p.dh_segs, l.K);
+  int64_t covered = 0;
+  for (int64_t z = 0; z < segs; ++z) {
+    const Launch s = split_segment(l, p.dh_kseg, z);
+    if (s.K <= 0 || s.K > p.dh_kseg) fail("segment size", z, s.K, l.K);
+    covered += s.K;
+    check_launch(p, s);
+    ++n_split_segments;
+  }
+  if (covered != l.K) fail("segments do not cover K", covered, l.K, segs);
+}
+
 int main(int argc, char** argv) {
   // N H V [vchunk]
   struct Shape { int64_t N, H, V, vc; };
@@ -179,7 +198,9 @@ int main(int argc, char** argv) {
       {300, 136, 1000, 0}, {700, 128, 1500, 512}, {1024, 256, 4096, 0}, {1100, 128, 2000, 0},
       {100, 16, 1, 0},     {100, 16, 2, 0},     {333, 64, 1024, 0},  {256, 64, 512, 0},
       {2048, 1024, 32000, 0}, {4096, 4096, 131072, 0}, {8192, 4096, 131072, 0},
-      {8192, 3584, 256000, 0}, {16384, 4096, 131072, 0}};
+      {8192, 3584, 256000, 0}, {16384, 4096, 131072, 0},
+      // few dH output tiles: split-K segments, ragged last segment, several chunks
+      {300, 136, 9000, 0}, {600, 264, 20000, 4096}, {2048, 1024, 33000, 0}};
   check_lds_layout();
   check_blocked_matches_dense();
   std::printf("lds layout and blocked G: %s\n", failures ? "FAILURES" : "ok");
@@ -200,13 +221,16 @@ int main(int argc, char** argv) {
         check_launch(p, backward_launch(p, c, 0));
         for (int part = 0; part < p.g_parts; ++part)
           for (int w = 1; w < 3; ++w) check_launch(p, backward_launch(p, c, w, part));
+        check_split(p, backward_launch(p, c, 2));
       }
     }
     for (int64_t tc : {int64_t(0), int64_t(256), int64_t(1000)}) {   // no-recompute variant
       Plan q;
       if (!make_plan_nr(s.N, s.H, s.V, 1, tc, &q)) { fail("plan nr", s.N, s.H, tc); continue; }
-      for (int64_t c = 0; c < q.n_tok_chunks; ++c)
+      for (int64_t c = 0; c < q.n_tok_chunks; ++c) {
         for (int w = 0; w < 3; ++w) check_launch(q, nr_launch(q, c, w));
+        check_split(q, nr_launch(q, c, 2));
+      }
     }
     Plan p;
     make_plan(s.N, s.H, s.V, 1, &p);
@@ -214,6 +238,7 @@ int main(int argc, char** argv) {
                 (long long)s.H, (long long)s.V, (long long)p.vchunk, (long long)p.n_chunks,
                 failures ? "FAILURES" : "ok");
   }
-  if (failures == 0) std::printf("all loads in bounds\n");
+  if (failures == 0)
+    std::printf("all loads in bounds (%lld split-K segments)\n", (long long)n_split_segments);
   return failures ? 1 : 0;
 }

@@ -345,6 +345,32 @@ def test_f32grad_workspace_check(lib):
 
 
 # ------------------------------------------------------ no-recompute variant
+def _dh_segments(M, H, K):
+    """The split-K rule of the dH GEMM restated: with fewer than 128 output tiles
+    of 256 x 256, up to 8 segments (one per CU share), each of at least 2048 k,
+    rounded to a multiple of 64; 1 when not split."""
+    tiles = -(-M // 256) * -(-H // 256)
+    s = min(256 // tiles, 8, K // 2048)
+    if tiles >= 128 or s < 2:
+        return 1
+    kseg = -(-K // s)
+    kseg = -(-kseg // 64) * 64
+    return -(-K // kseg)
+
+
+def test_dh_split_workspace(lib):
+    """The recompute path carves segs x N x H float32 partials exactly when dH
+    has few output tiles: the small configuration (32 tiles) splits its
+    32000-row vocabulary into 8 segments, the large-vocab one (512 tiles) does
+    not split."""
+    small = lib.flce_workspace_size(2048, 1024, 32000, 1)
+    assert _dh_segments(2048, 1024, 32000) == 8
+    assert small >= 8 * 2048 * 1024 * 4 + 32000 * 2048 * 2
+    assert _dh_segments(8192, 4096, 16384) == 1
+    big = lib.flce_workspace_size(8192, 4096, 131072, 1)
+    assert big < 16384 * 8192 * 2 + 8192 * 4096 * 4 + (64 << 20)
+
+
 def test_nr_plan(lib):
     # default chunk: min(N, 8192) rounded up to the tile
     assert lib.flce_token_chunk_nr(8192, 4096, 131072, 1, 0) == 8192
@@ -352,12 +378,15 @@ def test_nr_plan(lib):
     assert lib.flce_token_chunk_nr(600, 64, 1000, 1, 0) == 768
     assert lib.flce_token_chunk_nr(8192, 4096, 131072, 1, 1000) == 1024
     assert lib.flce_token_chunk_nr(8192, 4096, 131072, 1, 100000) == 8192
-    # the chunk's probabilities dominate the workspace: nc x roundup(V, 256) x 2 bytes
+    # the chunk's probabilities dominate the workspace: nc x roundup(V, 256) x 2 bytes,
+    # plus the float32 partial products of a split-K dH when its output has few tiles
     for N, H, V, tc in [(8192, 4096, 131072, 0), (8192, 3584, 256000, 2048), (600, 64, 1000, 256)]:
         nc = lib.flce_token_chunk_nr(N, H, V, 1, tc)
         ws = lib.flce_workspace_size_nr(N, H, V, 1, tc)
         vp = -(-V // 256) * 256
-        assert nc * vp * 2 <= ws <= nc * vp * 2 + (vp // 256) * nc * 8 + 4 * nc * 4 + N + 4096
+        segs = _dh_segments(nc, H, V)
+        split = segs * nc * H * 4 if segs > 1 else 0
+        assert nc * vp * 2 + split <= ws <= nc * vp * 2 + split + (vp // 256) * nc * 8 + 4 * nc * 4 + N + 4096
     assert lib.flce_workspace_size_nr(64, 64, 128, 0, 0) == 0        # float32: not offered
     assert lib.flce_workspace_size_nr(-1, 64, 128, 1, 0) == 0
 

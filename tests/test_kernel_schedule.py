@@ -34,7 +34,8 @@ def loops(tmp_path_factory):
     for st in starts:
         en = next(i for i in range(st, len(lines)) if lines[i].startswith(".Lfunc_end"))
         body = lines[st:en]
-        name = re.match(r"^_ZN4flce12_GLOBAL__N_16k_gemmILi(\d)ELi(\d)ENS0_\d+(\w+?)I", body[0])
+        name = re.match(r"^_ZN4flce12_GLOBAL__N_16k_gemmILi(\d)ELi(\d)ENS0_(\d+)", body[0])
+        epi_name = body[0][name.end():name.end() + int(name.group(3))]   # length-prefixed
         # loop headers as the compiler marks them (a backward jump alone can
         # be a block placed out of line)
         labels = {m.group(1): i for i, l in enumerate(body)
@@ -49,7 +50,7 @@ def loops(tmp_path_factory):
         assert best, body[0]
         seg = [l.strip() for l in body[best[0]:best[1]]
                if l.startswith("\t") and not l.startswith("\t;") and not l.startswith("\t.")]
-        res[body[0].split(":")[0]] = (int(name.group(1)), int(name.group(2)), name.group(3), seg)
+        res[body[0].split(":")[0]] = (int(name.group(1)), int(name.group(2)), epi_name, seg)
     assert len(res) >= 8
     return res
 
