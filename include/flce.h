@@ -70,8 +70,10 @@ typedef enum {
  * flce_workspace_size -- bytes of device scratch that flce_forward_backward
  * needs for this problem (256-byte aligned base required). It holds the
  * per-tile log-sum-exp partials, the per-token lse and target logits, one
- * vocabulary chunk of the logit gradient and (bf16, several chunks) a float32
- * dH accumulator. Never O(N*V): the chunk is sized to at most ~256 MiB.
+ * vocabulary chunk of the logit gradient, (bf16, several chunks) a float32
+ * dH accumulator and (bf16, N*H under 128 tiles of 256 x 256) up to 8 float32
+ * N x H partial products of a dH split along the vocabulary. Never O(N*V):
+ * the chunk is sized to at most ~256 MiB.
  * Returns 0 for invalid sizes (N < 0, H <= 0, V <= 0, unknown dtype).
  * Pure host arithmetic; callable without a GPU.
  */
@@ -186,8 +188,10 @@ int flce_forward_backward_ex(const void* h, const void* W, const int64_t* labels
  * implementations do": memory is bounded by chunking the sequence) is the
  * model; the logits themselves are never rounded to bf16. Cost: 6*N*H*V
  * flop, plus token_chunk * roundup(V, 256) * 2 bytes of workspace
- * (flce_workspace_size_nr), 2 GiB at N >= 8192, V = 131072 with the default;
- * a smaller token_chunk trades speed (one more pass over dW per chunk) for
+ * (flce_workspace_size_nr), 2 GiB at N >= 8192, V = 131072 with the default,
+ * and, when token_chunk * H is under 128 tiles of 256 x 256, up to 8 float32
+ * token_chunk x H partial products of a dH split along the vocabulary; a
+ * smaller token_chunk trades speed (one more pass over dW per chunk) for
  * memory.
  * Errors as flce_check_args, with FLCE_ERR_UNSUPPORTED for float32 inputs;
  * flce_token_chunk_nr gives the chunk used.
