@@ -32,7 +32,7 @@ IGNORE_INDEX = -100
 __all__ = [
     "IGNORE_INDEX",
     "Workload",
-    "CONFIGS",
+    "RECIPES",
     "make_workload",
     "make_labels",
     "make_custom",
@@ -72,7 +72,7 @@ class Workload:
 
 
 # name, B, S, H, V, dtype, w_std, label law, mask law, softcap, reduction, T, micro-batches
-CONFIGS = {
+RECIPES = {
     1: dict(name="tiny", B=2, S=16, H=64, V=1024, dtype=torch.float32, w_std=0.02,
             labels="uniform", mask=("frac", 0.10), softcap=0.0, reduction="sum",
             T=None, mb=1),
@@ -160,7 +160,7 @@ def _apply_mask(labels: torch.Tensor, B: int, S: int, mask, seed: int,
 
 def make_labels(k: int, *, scale_tokens: Optional[int] = None):
     """Labels [N] (int64) of configuration k and the number of ignored positions."""
-    c = CONFIGS[k]
+    c = RECIPES[k]
     B, S, V = c["B"], c["S"], c["V"]
     if scale_tokens is not None:
         S = scale_tokens
@@ -184,7 +184,7 @@ def make_workload(k: int, *, scale_tokens: Optional[int] = None) -> Workload:
     ``scale_tokens`` sequence positions of each sequence -- never used for the
     measured workload, only to make a smaller case with the same recipe.
     """
-    c = CONFIGS[k]
+    c = RECIPES[k]
     B, S, H, V = c["B"], c["S"], c["H"], c["V"]
     if scale_tokens is not None:
         S = scale_tokens
