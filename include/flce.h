@@ -75,21 +75,26 @@ typedef enum {
  * N x H partial products of a dH split along the vocabulary. Never O(N*V):
  * the chunk is sized to at most ~256 MiB.
  * Returns 0 for invalid sizes (N < 0, H <= 0, V <= 0, unknown dtype).
- * Pure host arithmetic; callable without a GPU.
+ * Pure host arithmetic; callable without a GPU. No page defines this call:
+ * it is this library's own addition, so that the caller owns every byte of
+ * device memory the step uses.
  */
 size_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype);
 
 /*
  * flce_check_args -- the synchronous argument checks of flce_forward_backward,
  * with the same parameter list, without touching the GPU (pointers are only
- * compared, never dereferenced). Returns FLCE_OK or the error that
- * flce_forward_backward would return before launching anything:
+ * compared, never dereferenced). This library's own addition (no page
+ * defines it), so the checks can be tested on a machine without a GPU.
+ * Returns FLCE_OK or the error that flce_forward_backward would return
+ * before launching anything:
  *   FLCE_ERR_ARG         N < 0, H <= 0, V <= 0; a required pointer is NULL
  *                        (h, W, labels, dH when N > 0; loss, num_tokens, dW
  *                        always); unknown dtype/reduction; softcap < 0 or not
- *                        finite; mb_scale not finite; num_label_tokens > 0
- *                        with 'mean'; an output (dH, dW) overlapping an input
- *                        matrix (h, W) or the other output.
+ *                        finite; mb_scale negative or not finite;
+ *                        num_label_tokens > 0 with 'mean'; an output (dH,
+ *                        dW) overlapping an input matrix (h, W) or the other
+ *                        output.
  *   FLCE_ERR_UNSUPPORTED bf16 with H % 8 != 0 or a matrix pointer not 16-byte
  *                        aligned.
  *   FLCE_ERR_WORKSPACE   workspace NULL, not 256-byte aligned, or
@@ -109,9 +114,12 @@ int flce_check_args(const void* h, const void* W, const int64_t* labels,
  * Inputs  h [N,H], W [V,H], labels [N] (int64), ignore_index (compared by
  *         equality; may name a vocabulary row), softcap s >= 0 (0 = off),
  *         reduction (flce_reduction_t), num_label_tokens T (<= 0: absent;
- *         only with 'sum'), dtype (flce_dtype_t), mb_scale (finite; 1.0 for
- *         a plain call), accumulate_dW (0: dW is overwritten; 1: the computed
- *         gradient is added to the dW already in memory, for micro-batching).
+ *         only with 'sum'), dtype (flce_dtype_t), mb_scale (finite and
+ *         >= 0: the token-weighted micro-batch scale is a token fraction
+ *         n_mb / n_total, 1.0 for a plain call; 0 gives loss 0 and zero
+ *         gradients; negative is FLCE_ERR_ARG), accumulate_dW (0: dW is
+ *         overwritten; 1: the computed gradient is added to the dW already in
+ *         memory, for micro-batching).
  * Outputs *loss (fp32 scalar), *num_tokens (int64 scalar), dH [N,H],
  *         dW [V,H], optional lse_out [N] fp32 (per-token log-sum-exp of the
  *         softcapped logits; NULL = not written), optional *status (int32:
@@ -309,17 +317,20 @@ int flce_forward_logits(const void* h, const void* W, const int64_t* labels, int
                         void* workspace, size_t workspace_bytes, int32_t* status,
                         float* lse_out, void* logits, int64_t ld_logits, int logits_dtype);
 
-/* flce_status_string -- a static, human-readable name for a status code. */
+/* flce_status_string -- a static, human-readable name for a status code
+ * (this library's own addition; no page defines status codes). */
 const char* flce_status_string(int status);
 
 /*
  * flce_vocab_chunk -- the vocabulary chunk (rows of W per backward chunk) the
- * library uses for this problem; informational (host arithmetic only).
+ * library uses for this problem; informational (host arithmetic only; this
+ * library's own addition).
  */
 int64_t flce_vocab_chunk(int64_t N, int64_t H, int64_t V, int dtype);
 
 /*
- * Per-kernel timing (diagnostics for benchmarks; not thread-safe).
+ * Per-kernel timing (diagnostics for benchmarks; not thread-safe; this
+ * library's own addition, no page defines it).
  * flce_profile_begin() clears the record and makes subsequent
  * flce_forward_backward calls bracket every kernel launch with a pair of
  * HIP events on the call's stream. flce_profile_end() stops recording.

@@ -21,9 +21,9 @@ Contracts (see include/flce.h):
   tile's max) instead of recomputing the logits, 3 GEMM passes instead of 4, at
   the cost of token_chunk x V x 2 bytes of workspace.
 * The forward call computes dH and dW as well; ``backward`` only scales them by
-  the incoming gradient. When no gradient is wanted (``torch.no_grad()``, or
-  neither input requires one) the forward-only entry runs instead: the same
-  loss at a quarter of the work.
+  the incoming gradient, on the device (no host synchronisation). When no
+  gradient is wanted (``torch.no_grad()``, or neither input requires one) the
+  forward-only entry runs instead: the same loss at a quarter of the work.
 """
 from __future__ import annotations
 
@@ -419,12 +419,12 @@ class FLCEFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, grad_loss, grad_num_tokens):
         dH, dW = ctx.saved_tensors
-        g = grad_loss
-        # d(g * loss): scale only when the incoming gradient is not exactly 1
-        if not bool((g == 1).all()):
-            dH = (dH.float() * g).to(dH.dtype)
-            dW = (dW.float() * g).to(dW.dtype)
-        return dH, dW, None, None, None, None, None, None
+        # d(g * loss) = g * (dH, dW), scaled on the device with no host sync:
+        # the product is formed in float32 and rounded once to the gradient
+        # dtype, so g == 1 returns dH and dW bit for bit and any other g adds
+        # one rounding to the already rounded gradients.
+        g = grad_loss.to(torch.float32)
+        return torch.mul(dH, g), torch.mul(dW, g), None, None, None, None, None, None
 
 
 def fused_linear_cross_entropy(hidden_states: torch.Tensor, labels: torch.Tensor,

@@ -184,7 +184,9 @@ int check_common(const void* h, const void* W, const int64_t* labels, int64_t N,
   if (dtype == FLCE_F32 && grad_dtype == FLCE_BF16) return FLCE_ERR_UNSUPPORTED;
   if (reduction != FLCE_SUM && reduction != FLCE_MEAN) return FLCE_ERR_ARG;
   if (!(softcap >= 0.0f) || !std::isfinite(softcap)) return FLCE_ERR_ARG;
-  if (!std::isfinite(mb_scale)) return FLCE_ERR_ARG;
+  // the token-weighted micro-batch scale is a token fraction n_mb / n_total
+  // (1.0 for 'sum'), so it is finite and never negative
+  if (!std::isfinite(mb_scale) || !(mb_scale >= 0.0f)) return FLCE_ERR_ARG;
   if (reduction == FLCE_MEAN && num_label_tokens > 0) return FLCE_ERR_ARG;
   if (!loss || !num_tokens || !W) return FLCE_ERR_ARG;
   if (N > 0 && (!h || !labels)) return FLCE_ERR_ARG;

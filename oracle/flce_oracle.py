@@ -6,10 +6,10 @@ shares no code with the GPU kernels.
 
 What it computes (plain definition, materialised logits, float64 throughout):
 
-* logits ``Z = h @ W.T`` -- the LM-head projection. "Fused skips materializing
-  logits" (LlamaFactory error page "cross_entropy and fused_linear_cross_entropy
-  cannot both be enabled", section "What it means"); this oracle is the
-  materialising side, one block of token rows at a time.
+* logits ``Z = h @ W.T`` -- the LM-head projection. The fused loss never forms
+  the logits (LlamaFactory error page "cross_entropy and
+  fused_linear_cross_entropy cannot both be enabled", section "What it means");
+  this oracle is the materialising side, one block of token rows at a time.
 * optional softcap ``Z' = s * tanh(Z / s)``, ``s = 0`` meaning off (NeMo
   AutoModel ``linear_ce`` page, API, ``logit_softcapping``), applied to the
   same logits that feed the log-sum-exp and the target gather (twinkle PR 335,

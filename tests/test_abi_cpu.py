@@ -117,13 +117,30 @@ def _args(**kw):
 def test_check_args_ok(lib):
     assert lib.flce_check_args(*_args()) == 0
     assert lib.flce_check_args(*_args(dtype=0, H=3)) == 0      # fp32: any H
+    for mb in (0.0, -0.0, 0.25, 1.0, 3.0):                     # any finite scale >= 0
+        assert lib.flce_check_args(*_args(mb=mb)) == 0, mb
+
+
+def test_negative_micro_batch_scale_rejected_by_every_entry(lib):
+    """The token-weighted micro-batch scale (twinkle PR 335, "PR information",
+    item 2) is a fraction of tokens, never negative: every entry point's
+    checks refuse a negative one before any launch."""
+    a = _args(mb=-0.5)
+    assert lib.flce_check_args(*a) == 1
+    assert lib.flce_check_args_ex(*a, 1) == 1
+    assert lib.flce_check_args_ex(*a, 0) == 1
+    assert lib.flce_check_args_nr(*a, 0) == 1
+    fw = [a[i] for i in range(22) if i not in (12, 13, 17)]   # no dH, dW, accumulate_dW
+    assert lib.flce_forward_check_args(*fw) == 1
+    assert lib.flce_forward_logits_check_args(*fw, A16 * 2048, 128, 0) == 1
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(N=-1), 1), (dict(H=0), 1), (dict(V=0), 1),
     (dict(red=2), 1), (dict(dtype=5), 1),
     (dict(softcap=-1.0), 1), (dict(softcap=float("inf")), 1), (dict(softcap=float("nan")), 1),
-    (dict(mb=float("nan")), 1),
+    (dict(mb=float("nan")), 1), (dict(mb=float("inf")), 1),
+    (dict(mb=-0.5), 1), (dict(mb=-1e-30), 1),      # the micro-batch scale is a token fraction
     (dict(red=1, T=10), 1),
     (dict(h=None), 1), (dict(W=None), 1), (dict(labels=None), 1), (dict(loss=None), 1),
     (dict(nt=None), 1), (dict(dH=None), 1), (dict(dW=None), 1),

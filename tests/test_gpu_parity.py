@@ -118,6 +118,59 @@ def test_mb_scale():
     gu.assert_parity(w, gu.run_gpu(w, mb_scale=s), gu.run_oracle(w, mb_scale=s))
 
 
+@pytest.mark.parametrize("path", ["recompute", "f32grad", "norecompute", "fp32"])
+@pytest.mark.parametrize("s", [0.0, 1e-3, 0.375])
+def test_mb_scale_every_path(path, s, vchunk):
+    """The micro-batch scale (twinkle PR 335, "PR information", item 2) on every
+    gradient path, including 0 (loss 0, zero gradients, no NaN) and a small
+    scale, against the oracle with the same scale, with and without a softcap
+    and over several backward chunks."""
+    vchunk(256)
+    dt = torch.float32 if path == "fp32" else torch.bfloat16
+    for cap in (0.0, 2.0):
+        w = fi.make_custom(300, 64, 700, dtype=dt, seed=16, w_std=0.3, softcap=cap,
+                           reduction="sum", ignore_frac=0.1)
+        kw = {}
+        if path == "f32grad":
+            kw["grad_dtype"] = torch.float32
+        elif path == "norecompute":
+            kw.update(recompute=False, token_chunk=256)
+        g = gu.run_gpu(w, mb_scale=float(np.float32(s)), **kw)
+        r = gu.run_oracle(w, mb_scale=float(np.float32(s)))
+        if path == "f32grad":
+            # float32 gradients: the float32 tolerance
+            assert g["status"] == 0 and g["num_tokens"] == r.num_tokens
+            gu.assert_loss(g["loss"], r.loss64)
+            gu.assert_grad("dH", g["dH"], r.dH, gu.GRAD_TOL[torch.float32])
+            gu.assert_grad("dW", g["dW"], r.dW, gu.GRAD_TOL[torch.float32])
+        else:
+            gu.assert_parity(w, g, r)
+        if s == 0.0:
+            assert g["loss"] == 0.0
+            assert bool((g["dH"] == 0).all()) and bool((g["dW"] == 0).all())
+
+
+def test_negative_mb_scale_refused():
+    """A negative micro-batch scale is an argument error on every entry point:
+    nothing is launched and the outputs keep their contents."""
+    import lm_head_linear_amd as m
+    w = fi.make_custom(64, 64, 300, dtype=torch.bfloat16, seed=17)
+    dev = gu.device()
+    h, W = w.h.reshape(-1, w.H).to(dev), w.W.to(dev)
+    y = w.labels.reshape(-1).to(dev)
+    loss = torch.full((), 7.0, device=dev)
+    dW = torch.full_like(W, 3.0)
+    for kw in ({}, {"grad_dtype": torch.float32}, {"recompute": False}):
+        dWk = dW if not kw.get("grad_dtype") else torch.full(W.shape, 3.0, device=dev)
+        with pytest.raises(m.FlceError) as e:
+            m.flce_forward_backward(h, W, y, mb_scale=-0.5, loss=loss, dW=dWk, **kw)
+        assert e.value.code == 1
+    with pytest.raises(m.FlceError):
+        m.flce_forward(h, W, y, mb_scale=-0.5, loss=loss)
+    torch.cuda.synchronize()
+    assert loss.item() == 7.0 and bool((dW == 3.0).all())
+
+
 def test_ignore_index_inside_vocab():
     w = fi.make_custom(400, 64, 300, dtype=torch.bfloat16, seed=16, ignore_frac=0.0,
                        ignore_index=5)
