@@ -10,9 +10,12 @@ before the timed region. One step = one call of flce_forward_backward
 chunk the logit-gradient GEMM, the dW GEMM and the dH GEMM).
 
 Prints one JSON line (the last line of stdout). `value` is tokens/s of the
-whole step; `roofline` covers the kernel with the largest share of the step
-time, timed with HIP events on the stream it runs on; `cpu_baseline` times
-the float64 oracle on a bounded token sample of the same workload.
+whole step, timed over a loop of steps with nothing else in it; `roofline`
+covers the kernel with the largest share of the step time, timed with HIP
+events around each launch on the stream it runs on, in a separate pass after
+the timed loop; `configs` times the same step on the small, softcapped and
+long configurations; `cpu_baseline` times the float64 oracle on all tokens of
+the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -83,9 +86,22 @@ def blas_threads() -> int:
     return os.cpu_count() or 1
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine() or "unknown"
+
+
 def cpu_baseline(w, n_sample: int):
-    """The float64 oracle, as it stands, on every (N // n_sample)-th token of the
-    workload with the full weight; tokens/s = sampled tokens / oracle time."""
+    """The float64 oracle, as it stands, on the workload (all N tokens when
+    n_sample >= N, else every (N // n_sample)-th token) with the full weight;
+    tokens/s = tokens run / oracle time."""
     import numpy as np
     import torch
     from oracle import flce_oracle as orc
@@ -100,25 +116,45 @@ def cpu_baseline(w, n_sample: int):
                            reduction=w.reduction)
     dt = time.perf_counter() - t0
     assert np.isfinite(r.loss64)
+    what = (f"all {N} tokens" if len(idx) == N
+            else f"{len(idx)} tokens (every {stride}th of the {N})")
     return {
         "value": len(idx) / dt, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
-        "sample": (f"{len(idx)} tokens (every {stride}th of the {N}) with the full W "
-                   f"[{w.V},{w.H}]: one float64 forward+backward of the oracle in {dt:.1f} s; "
+        "sample": (f"{what} with the full W [{w.V},{w.H}]: one float64 forward+backward of "
+                   f"the oracle (materialised logits per 1024 tokens) in {dt:.1f} s; "
                    "bf16->float64 widening not timed"),
+        "host_cpu_count": os.cpu_count(), "blas_threads": blas_threads(),
+        "cpu_model": cpu_model(),
         "seconds": dt,
     }
+
+
+def time_steps(fn, steps: int, warmup: int):
+    """(host-clock ms, event ms) per call of fn over `steps` timed calls, after
+    `warmup` untimed ones, bracketed by device synchronisation."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
 
 
 def other_configs(steps: int, warmup: int):
     """The full step (flce_forward_backward, bf16) on the other full-size
     configurations: small, softcapped, and long, as one call and as its four
     micro-batches with the shared external token count and dW added up across
-    them. Prints one JSON line of its own (not the benchmark line)."""
+    them. Returns {name: figures}."""
     import torch
     import flce_inputs as fi
     import lm_head_linear_amd as m
-    from lm_head_linear_amd import _lib
-    _lib.load()
     dev = torch.device("cuda:0")
     out = {}
     for k in (2, 4, 5):
@@ -132,6 +168,9 @@ def other_configs(steps: int, warmup: int):
         nt = torch.empty((), dtype=torch.int64, device=dev)
         kw = dict(ignore_index=w.ignore_index, softcap=w.softcap, reduction=w.reduction,
                   num_label_tokens=w.num_label_tokens, loss=loss, num_tokens=nt)
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated(dev)
+        torch.cuda.reset_peak_memory_stats(dev)
         ws = torch.empty(m.flce_workspace_size(N, H, V, W.dtype), dtype=torch.uint8, device=dev)
         runs = {"one_call": lambda: m.flce_forward_backward(h, W, y, dH=dH, dW=dW, workspace=ws,
                                                              **kw)}
@@ -147,26 +186,26 @@ def other_configs(steps: int, warmup: int):
                                             accumulate_dW=i > 0,
                                             mb_scale=m.micro_batch_scale(0, 0, w.reduction), **kw)
             runs[f"{w.micro_batches}_micro_batches"] = micro
-        res = {"N": N, "H": H, "V": V, "softcap": w.softcap, "reduction": w.reduction}
+        res = {"N": N, "H": H, "V": V, "softcap": w.softcap, "reduction": w.reduction,
+               "num_label_tokens": w.num_label_tokens}
+        nhv = float(N) * H * V
         for name, fn in runs.items():
-            for _ in range(warmup):
-                fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(steps):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / steps
-            res[name] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(N / ms * 1e3, 1),
-                         "mfma_frac_8nhv": round(8.0 * N * H * V / (ms * 1e-3) / 1e12
+            ms, ev_ms = time_steps(fn, steps, warmup)
+            res[name] = {"ms_per_step": round(ms, 4), "event_ms_per_step": round(ev_ms, 4),
+                         "tokens_per_s": round(N / ms * 1e3, 1),
+                         "mfma_frac_8nhv": round(8.0 * nhv / (ms * 1e-3) / 1e12
+                                                 / PEAK_BF16_TFLOPS, 4),
+                         "mfma_frac_6nhv": round(6.0 * nhv / (ms * 1e-3) / 1e12
                                                  / PEAK_BF16_TFLOPS, 4)}
             log(f"{w.name} {name}: {ms:.3f} ms/step")
+        torch.cuda.synchronize()
+        res["extra_memory_bytes"] = int(torch.cuda.max_memory_allocated(dev) - base)
+        res["workspace_bytes"] = int(ws.numel())
+        res["logits_f32_bytes_avoided"] = int(N * V * 4)
         out[w.name] = res
         del h, W, y, dH, dW, ws, runs
         torch.cuda.empty_cache()
-    print(json.dumps({"configs": out}), flush=True)
+    return out
 
 
 def copy_calibration(size_mib: int, reps: int):
@@ -297,18 +336,55 @@ def other_modes(m, w, h, W, y, dH, dW, loss, nt, steps, timing, nhv):
     return forward_only, float32_grads, no_recompute
 
 
+def kernel_pass(m, step, steps: int, nhv: float):
+    """Per-kernel HIP-event timing over `steps` extra steps, run after the
+    headline loop (events bracket every launch on the call's stream, so this
+    pass is not the one `value` comes from). Returns (kernels, roofline)."""
+    import torch
+    m.flce_profile_begin()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    m.flce_profile_end()
+    kernels = {}
+    for name, (ms, n) in m.flce_profile_query().items():
+        if n == 0:
+            continue
+        e = {"ms_per_step": ms / steps, "launches_per_step": n / steps, "avg_launch_ms": ms / n}
+        if name in GEMM_KINDS:
+            e["tflops"] = 2 * nhv * steps / (ms * 1e-3) / 1e12
+        kernels[name] = e
+    dom = max(GEMM_KINDS, key=lambda k: kernels.get(k, {}).get("ms_per_step", 0.0))
+    d = kernels[dom]
+    flops_per_launch = 2 * nhv / d["launches_per_step"]
+    achieved = flops_per_launch / (d["avg_launch_ms"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": read_traffic(dom), "kernel": dom,
+                "flops_per_launch": flops_per_launch,
+                "avg_launch_ms": round(d["avg_launch_ms"], 4),
+                "timing": f"HIP events around each launch, {steps} steps after the timed loop"}
+    for k, v in kernels.items():
+        log(f"  {k:18s} {v['ms_per_step']:8.3f} ms/step  {v['launches_per_step']:.0f} launches"
+            + (f"  {v['tflops']:7.1f} TFLOP/s" if "tflops" in v else ""))
+    return kernels, roofline
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
-    ap.add_argument("--no-kernel-timing", action="store_true",
-                    help="do not bracket kernels with events in the timed region")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="tokens the oracle baseline runs (0: all N)")
+    ap.add_argument("--kernel-steps", type=int, default=-1,
+                    help="steps of the separate per-kernel event pass (-1: --steps, 0: none)")
     ap.add_argument("--main-only", action="store_true",
-                    help="time only the main path (no forward-only, float32-gradient or "
-                         "no-recompute figures), e.g. for per-kernel counter runs")
+                    help="time only the main path (no other entry points and no other "
+                         "configurations), e.g. for per-kernel counter runs")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="leave out the small, softcapped and long configurations")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain copy of this size (counter calibration)")
     ap.add_argument("--configs", action="store_true",
@@ -329,14 +405,14 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 10)
         return
-    if args.configs:
-        other_configs(args.steps, args.warmup)
-        return
 
     import flce_inputs as fi
     import lm_head_linear_amd as m
     from lm_head_linear_amd import _lib
     _lib.load()
+    if args.configs:
+        print(json.dumps({"configs": other_configs(args.steps, args.warmup)}), flush=True)
+        return
 
     dev = torch.device("cuda:0")
     t = time.perf_counter()
@@ -351,6 +427,7 @@ def main():
     loss = torch.empty((), dtype=torch.float32, device=dev)
     nt = torch.empty((), dtype=torch.int64, device=dev)
     ws_bytes = m.flce_workspace_size(N, H, V, W.dtype)
+    vchunk = m.flce_vocab_chunk(N, H, V, W.dtype)
     torch.cuda.synchronize()
     base_mem = torch.cuda.memory_allocated(dev)
     torch.cuda.reset_peak_memory_stats(dev)
@@ -366,12 +443,10 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps); loss={loss.item():.6f} num_tokens={nt.item()}")
 
+    # The headline loop: nothing but the steps (no per-launch events).
     stream = torch.cuda.current_stream(dev)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    timing = not args.no_kernel_timing
-    if timing:
-        m.flce_profile_begin()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
@@ -380,8 +455,6 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    if timing:
-        m.flce_profile_end()
     wall_ms = (t1 - t0) * 1e3 / args.steps
     ev_ms = ev0.elapsed_time(ev1) / args.steps
     peak_extra = torch.cuda.max_memory_allocated(dev) - base_mem
@@ -390,40 +463,26 @@ def main():
     nhv = float(N) * H * V
     tflops_8 = 8 * nhv / (wall_ms * 1e-3) / 1e12
     tflops_6 = 6 * nhv / (wall_ms * 1e-3) / 1e12
-    kernels = {}
-    roofline = None
-    if timing:
-        prof = m.flce_profile_query()
-        for name, (ms, n) in prof.items():
-            if n == 0:
-                continue
-            e = {"ms_per_step": ms / args.steps, "launches_per_step": n / args.steps,
-                 "avg_launch_ms": ms / n}
-            if name in GEMM_KINDS:
-                e["tflops"] = 2 * nhv * args.steps / (ms * 1e-3) / 1e12
-            kernels[name] = e
-        dom = max(GEMM_KINDS, key=lambda k: kernels.get(k, {}).get("ms_per_step", 0.0))
-        d = kernels[dom]
-        flops_per_launch = 2 * nhv / d["launches_per_step"]
-        achieved = flops_per_launch / (d["avg_launch_ms"] * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": read_traffic(dom), "kernel": dom,
-                    "flops_per_launch": flops_per_launch,
-                    "avg_launch_ms": round(d["avg_launch_ms"], 4)}
-    for k, v in kernels.items():
-        log(f"  {k:18s} {v['ms_per_step']:8.3f} ms/step  {v['launches_per_step']:.0f} launches"
-            + (f"  {v['tflops']:7.1f} TFLOP/s" if "tflops" in v else ""))
+    kernels, roofline = {}, None
+    ksteps = args.steps if args.kernel_steps < 0 else args.kernel_steps
+    if ksteps > 0:
+        kernels, roofline = kernel_pass(m, step, ksteps, nhv)
 
     forward_only = float32_grads = no_recompute = None
+    configs = None
     if not args.main_only:
         forward_only, float32_grads, no_recompute = other_modes(
-            m, w, h, W, y, dH, dW, loss, nt, args.steps, timing, nhv)
+            m, w, h, W, y, dH, dW, loss, nt, args.steps, ksteps > 0, nhv)
+        if not args.no_configs:
+            del h, W, y, dH, dW, ws
+            torch.cuda.empty_cache()
+            configs = other_configs(max(3, args.steps // 4), 2)
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle on {args.cpu_sample_tokens} sampled tokens ...")
-        cpu = cpu_baseline(w, args.cpu_sample_tokens)
+        n_cpu = args.cpu_sample_tokens if args.cpu_sample_tokens > 0 else N
+        log(f"cpu baseline: oracle on {n_cpu} of {N} tokens ...")
+        cpu = cpu_baseline(w, n_cpu)
         log(f"cpu baseline: {cpu['value']:.1f} tokens/s on {cpu['cores']} threads")
 
     out = {
@@ -442,7 +501,7 @@ def main():
         "config": {"workload": (f"large_vocab: h bf16 [2,4096,4096], W bf16 [131072,4096], "
                                 "Zipf(1.1) labels, first quarter of each sequence ignored, "
                                 "reduction=mean"),
-                   "N": N, "H": H, "V": V, "vocab_chunk": m.flce_vocab_chunk(N, H, V, W.dtype)},
+                   "N": N, "H": H, "V": V, "vocab_chunk": vchunk},
         "mfma_frac_8nhv": round(tflops_8 / PEAK_BF16_TFLOPS, 4),
         "mfma_frac_6nhv": round(tflops_6 / PEAK_BF16_TFLOPS, 4),
         "tflops_8nhv": round(tflops_8, 1),
@@ -453,6 +512,7 @@ def main():
         "forward_only": forward_only,
         "float32_grads": float32_grads,
         "no_recompute": no_recompute,
+        "configs": configs,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "cpu_baseline": ({k: (round(v, 3) if isinstance(v, float) else v)

@@ -190,17 +190,21 @@ int flce_forward_backward_ex(const void* h, const void* W, const int64_t* labels
  * each chunk's probabilities relative to each vocabulary tile's max,
  * P'[t][v] = exp(z'_tv - M) <= 1, as bf16 in the workspace; after the chunk's
  * log-sum-exp they become G in place (G = c (P' exp(M - lse) - [v = y])
- * dz'/dz, the target element from its float32 logit), then dW (added over
- * the chunks in bf16, as with accumulate_dW) and the chunk's dH. The chunked
- * path that the Modalities PR 464 page describes ("What the reference
- * implementations do": memory is bounded by chunking the sequence) is the
- * model; the logits themselves are never rounded to bf16. Cost: 6*N*H*V
- * flop, plus token_chunk * roundup(V, 256) * 2 bytes of workspace
- * (flce_workspace_size_nr), 2 GiB at N >= 8192, V = 131072 with the default,
- * and, when token_chunk * H is under 128 tiles of 256 x 256, up to 8 float32
- * token_chunk x H partial products of a dH split along the vocabulary; a
- * smaller token_chunk trades speed (one more pass over dW per chunk) for
- * memory.
+ * dz'/dz, the target element from its float32 logit), then dW and the
+ * chunk's dH. With more than one chunk dW is summed over the chunks in a
+ * float32 [V,H] accumulator in the workspace and rounded to bf16 once, after
+ * the last chunk (with accumulate_dW the bf16 dW already in memory is its
+ * starting value). The chunked path that the Modalities PR 464 page
+ * describes ("What the reference implementations do": memory is bounded by
+ * chunking the sequence, gradients accumulate in float32) is the model; the
+ * logits themselves are never rounded to bf16. Cost: 6*N*H*V flop, plus
+ * token_chunk * roundup(V, 256) * 2 bytes of workspace
+ * (flce_workspace_size_nr), 2 GiB at N >= 8192, V = 131072 with the default;
+ * with several chunks the V*H*4-byte dW accumulator; and, when
+ * token_chunk * H is under 128 tiles of 256 x 256, up to 8 float32
+ * token_chunk x H partial products of a dH split along the vocabulary. A
+ * smaller token_chunk trades speed (one more pass over the dW accumulator per
+ * chunk) for memory.
  * Errors as flce_check_args, with FLCE_ERR_UNSUPPORTED for float32 inputs;
  * flce_token_chunk_nr gives the chunk used.
  */

@@ -94,6 +94,7 @@ int run_nr(const void* h, const void* W, const int64_t* labels, int64_t N, int64
   a.g = ws + p.off_g;
   a.dh_acc = nullptr;
   a.dh_part = p.dh_kseg ? reinterpret_cast<float*>(ws + p.off_dhpart) : nullptr;
+  a.dw_acc = p.need_dw_acc ? reinterpret_cast<float*>(ws + p.off_dwacc) : nullptr;
   e = flce::launch_label_scan(p, a, L);
   for (int64_t c = 0; e == hipSuccess && c < p.n_tok_chunks; ++c) {
     e = flce::bf16_nr_forward_chunk(p, a, c, L);

@@ -120,6 +120,14 @@ bool make_plan_nr(int64_t N, int64_t H, int64_t V, int dtype, int64_t token_chun
       q.off_dhpart = off;
       off = align256(off + size_t(q.dh_segs) * size_t(nc) * H * sizeof(float));
     }
+    // dW summed over several token chunks in float32, rounded to bf16 once
+    // (the chunked path of Modalities PR 464, "What the reference
+    // implementations do", keeps a float32 gradient accumulator)
+    if (q.n_tok_chunks > 1) {
+      q.need_dw_acc = true;
+      q.off_dwacc = off;
+      off = align256(off + size_t(V) * size_t(H) * sizeof(float));
+    }
   }
   q.off_dhacc = 0;
   q.need_dh_acc = false;

@@ -55,6 +55,7 @@ struct Args {
   void* g;        // G^T chunk [vchunk][ldg]
   float* dh_acc;  // [N][H] (bf16 path with several chunks)
   float* dh_part; // [dh_segs][M][H] split-K partial products of dH (or null)
+  float* dw_acc;  // [V][H] float32 dW running sum (no-recompute, several chunks)
 };
 
 // Launch hook: the C-ABI layer brackets launches with timing events.

@@ -80,6 +80,9 @@ struct Plan {
   bool nr = false;
   int64_t nc = 0, n_tok_chunks = 0, vp = 0;
   bool need_dh_acc = false;  // float32 dH accumulator needed (bf16, >1 chunk)
+  // No-recompute variant with several token chunks: dW is added up over the
+  // chunks in a float32 [V][H] running sum at off_dwacc, rounded to bf16 once.
+  bool need_dw_acc = false;
   // Split-K of the dH GEMM (bf16 gradients): segments of dh_kseg vocabulary
   // rows (0: not split), at most dh_segs of them per launch, each writing a
   // float32 [M][H] partial product at off_dhpart.
@@ -88,7 +91,7 @@ struct Plan {
   size_t grad_elem = 0;      // bytes per element of dH/dW
   // byte offsets into the workspace
   size_t off_scalars = 0, off_part = 0, off_zt = 0, off_lse = 0, off_lsum = 0,
-         off_g = 0, off_dhacc = 0, off_dhpart = 0, total = 0;
+         off_g = 0, off_dhacc = 0, off_dhpart = 0, off_dwacc = 0, total = 0;
 };
 
 // Builds the plan; returns false for invalid sizes or dtypes. A forward-only
@@ -104,7 +107,8 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
 // Plan of the no-recompute variant (bf16 only): token chunks of
 // `token_chunk` tokens (rounded up to the tile; <= 0: min(N, 8192) rounded
 // up), each with a [nc][roundup(V, 256)] bf16 buffer of probabilities that
-// becomes that chunk's G.
+// becomes that chunk's G, and with more than one chunk a float32 [V][H]
+// running sum of dW.
 bool make_plan_nr(int64_t N, int64_t H, int64_t V, int dtype, int64_t token_chunk, Plan* p);
 
 }  // namespace flce

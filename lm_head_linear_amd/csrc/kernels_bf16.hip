@@ -1230,6 +1230,62 @@ struct EpiDW32 {
   }
 };
 
+// ---- dW of the no-recompute variant, summed over token chunks in float32 --
+// SRC: 0 nothing to add, 1 the bf16 dW already in memory (accumulate_dW),
+// 2 the float32 running sum of the earlier chunks. DST: 1 bf16 dW, rounded to
+// nearest even once, at the last chunk; 2 the float32 running sum. The
+// running sums of the next row block are loaded while the current one is
+// staged, as in the dH epilogue.
+template <int SRC, int DST>
+struct EpiDWAcc {
+  uint16_t* dW;
+  float* acc32;  // [V][H] float32 running sum
+  int64_t H, vcur;
+
+  struct Pass {
+    const EpiDWAcc& e;
+    int64_t r0, c0;
+    float4 prev[2][16];
+    __device__ __forceinline__ void prefetch(int i, int lane) {
+      if (SRC != 2) return;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int idx = q * 64 + lane, row = idx >> 5, c4 = idx & 31;
+        const int64_t m = r0 + i * 32 + row, n = c0 + 4 * c4;
+        prev[i & 1][q] = (m < e.vcur && n < e.H)
+                             ? *reinterpret_cast<const float4*>(e.acc32 + m * e.H + n)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    __device__ __forceinline__ void store(int i, int q, int row, int col, float4 v) {
+      const int64_t m = r0 + i * 32 + row, n = c0 + col;
+      if (m >= e.vcur || n >= e.H) return;
+      if (SRC == 1) {
+        const uint2 o = *reinterpret_cast<const uint2*>(e.dW + m * e.H + n);
+        v.x += bf16_to_f32(uint16_t(o.x)); v.y += bf16_to_f32(uint16_t(o.x >> 16));
+        v.z += bf16_to_f32(uint16_t(o.y)); v.w += bf16_to_f32(uint16_t(o.y >> 16));
+      } else if (SRC == 2) {
+        const float4 o = prev[i & 1][q];
+        v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+      }
+      if (DST == 1)
+        *reinterpret_cast<uint2*>(e.dW + m * e.H + n) =
+            make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+      else
+        *reinterpret_cast<float4*>(e.acc32 + m * e.H + n) = v;
+    }
+  };
+
+  static constexpr int kTokBytes = 0;             // no per-token inputs
+  __device__ __forceinline__ void stage(char*, int64_t, int, int) const {}
+
+  __device__ __forceinline__ void operator()(Acc& acc, int64_t m0, int64_t n0, int wm, int wn,
+                                             int lane, char* smem, const char*) const {
+    Pass pass{*this, m0 + wm * 128, n0 + wn * 128, {}};
+    staged_rows(acc, wm, wn, lane, smem, pass);
+  }
+};
+
 // ---- dH epilogue: accumulate over vocabulary chunks in a fixed order ------
 // FIRST: no running sum to add; LAST: store bf16 dH instead of the float32
 // running sum.
@@ -1543,15 +1599,26 @@ hipError_t bf16_nr_backward_chunk(const Plan& p, const Args& a, int64_t c, const
   L.post(kProbsToGrad);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // 2) dW (+)= G^T . h[chunk], added up over the token chunks
+  // 2) dW (+)= G^T . h[chunk]; over several token chunks the sum is kept in
+  // float32 and rounded to bf16 once, at the last chunk
   uint16_t* dW = static_cast<uint16_t*>(a.dW);
   const gemm::Launch lw = gemm::nr_launch(p, c, 1);
-  if (c > 0 || a.accumulate_dW)
-    err = run_gemm<gemm::kFormT, gemm::kFormT, true>(lw, a, EpiDW<true>{dW, p.H, 0, p.V},
-                                                     kGemmDW, L);
-  else
-    err = run_gemm<gemm::kFormT, gemm::kFormT, true>(lw, a, EpiDW<false>{dW, p.H, 0, p.V},
-                                                     kGemmDW, L);
+  constexpr int T = gemm::kFormT;
+  if (!p.need_dw_acc) {
+    if (a.accumulate_dW)
+      err = run_gemm<T, T, true>(lw, a, EpiDW<true>{dW, p.H, 0, p.V}, kGemmDW, L);
+    else
+      err = run_gemm<T, T, true>(lw, a, EpiDW<false>{dW, p.H, 0, p.V}, kGemmDW, L);
+  } else if (c == 0) {
+    if (a.accumulate_dW)
+      err = run_gemm<T, T, true>(lw, a, EpiDWAcc<1, 2>{dW, a.dw_acc, p.H, p.V}, kGemmDW, L);
+    else
+      err = run_gemm<T, T, true>(lw, a, EpiDWAcc<0, 2>{dW, a.dw_acc, p.H, p.V}, kGemmDW, L);
+  } else if (c < p.n_tok_chunks - 1) {
+    err = run_gemm<T, T, true>(lw, a, EpiDWAcc<2, 2>{dW, a.dw_acc, p.H, p.V}, kGemmDW, L);
+  } else {
+    err = run_gemm<T, T, true>(lw, a, EpiDWAcc<2, 1>{dW, a.dw_acc, p.H, p.V}, kGemmDW, L);
+  }
   if (err != hipSuccess) return err;
   // 3) dH[chunk] = G . W over the whole vocabulary
   uint16_t* dH = static_cast<uint16_t*>(a.dH) + t0 * p.H;

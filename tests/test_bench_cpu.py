@@ -24,8 +24,22 @@ def test_digest_covers_every_library_source():
 
 
 def test_traffic_only_for_the_sources_it_was_taken_on(monkeypatch):
+    """Counters are reported for the sources they were taken on and for no
+    other: the committed summary names its source digest."""
+    vals = {}
+    with open(bench.TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    monkeypatch.setattr(bench, "kernel_source_digest", lambda: vals["source_digest"])
     for kind in bench.GEMM_KINDS:
         v = bench.read_traffic(kind)
         assert v is not None and v > 0, kind
     monkeypatch.setattr(bench, "kernel_source_digest", lambda: "0" * 16)
     assert bench.read_traffic("grad_logits_gemm") is None
+
+
+def test_cpu_model_and_threads_reported():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
+    assert bench.blas_threads() >= 1
