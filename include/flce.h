@@ -62,8 +62,10 @@ typedef enum {
   FLCE_ERR_UNSUPPORTED = 2,  /* valid but not supported (alignment, H%8)    */
   FLCE_ERR_WORKSPACE = 3,    /* workspace missing, misaligned or too small  */
   FLCE_ERR_HIP = 4,          /* a HIP runtime call or launch failed         */
-  FLCE_ERR_LABEL = 5         /* device-detected: a non-ignored label is
+  FLCE_ERR_LABEL = 5,        /* device-detected: a non-ignored label is
                                 outside [0, V); reported through *status     */
+  FLCE_ERR_SCRATCH = 6       /* the problem needs more scratch than the fixed
+                                array of flce_forward_noalloc holds          */
 } flce_status_t;
 
 /*
@@ -271,6 +273,35 @@ int flce_forward(const void* h, const void* W, const int64_t* labels, int64_t N,
                  int64_t num_label_tokens, float* loss, int64_t* num_tokens, void* stream,
                  int dtype, float mb_scale, void* workspace, size_t workspace_bytes,
                  int32_t* status, float* lse_out);
+
+/*
+ * flce_forward_noalloc -- flce_forward without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation. (No page defines
+ * it; it is flce_forward with the library's own scratch.)
+ *
+ * Scratch  a fixed device array of FLCE_NOALLOC_SCRATCH_BYTES inside the
+ *          library, one copy on every GPU the library runs on (the GPU of
+ *          `stream`; the current device for the null stream), held until the
+ *          process ends. The first call on a GPU looks up that copy's device
+ *          address (a HIP runtime query, no allocation). A problem whose
+ *          forward workspace, flce_forward_workspace_size(N, H, V, dtype),
+ *          exceeds the array is refused with FLCE_ERR_SCRATCH before anything
+ *          is launched. The call allocates nothing: no hipMalloc, no hipFree,
+ *          no allocating library routine.
+ * Sharing  every call on one GPU uses that GPU's array, which keeps the last
+ *          call's contents (the kernels write everything they read back), so
+ *          calls that overlap on one GPU (two streams, or two host threads)
+ *          race: the caller must serialise them.
+ * Everything else (parameters, outputs, edge cases, errors) as in
+ * flce_forward, whose results it reproduces bit for bit.
+ */
+#define FLCE_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+int flce_forward_noalloc(const void* h, const void* W, const int64_t* labels, int64_t N,
+                         int64_t H, int64_t V, int64_t ignore_index, float softcap,
+                         int reduction, int64_t num_label_tokens, float* loss,
+                         int64_t* num_tokens, void* stream, int dtype, float mb_scale,
+                         int32_t* status, float* lse_out);
 
 /*
  * flce_forward_logits_check_args -- the synchronous checks of

@@ -45,6 +45,7 @@ __all__ = [
     "flce_forward_check_args",
     "flce_forward_logits",
     "flce_forward_logits_check_args",
+    "flce_forward_noalloc",
     "flce_status_string",
     "flce_vocab_chunk",
     "flce_profile_begin",
@@ -299,6 +300,44 @@ def flce_forward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, *,
         rc = _lib.load().flce_forward(*args)
     if rc != _lib.OK:
         raise FlceError(rc, "flce_forward")
+    return loss, num_tokens
+
+
+def flce_forward_noalloc(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, *,
+                         ignore_index: int = -100, softcap: float = 0.0, reduction: str = "sum",
+                         num_label_tokens: Optional[int] = None, mb_scale: float = 1.0,
+                         loss: torch.Tensor, num_tokens: torch.Tensor,
+                         lse_out: Optional[torch.Tensor] = None,
+                         status: Optional[torch.Tensor] = None):
+    """:func:`flce_forward` on the library's fixed per-GPU scratch (no workspace):
+    the library allocates nothing, and this binding allocates nothing either, so
+    the caller passes the output tensors. Problems whose forward workspace
+    exceeds the scratch are refused (FlceError, FLCE_ERR_SCRATCH); overlapping
+    calls on one GPU race on the shared scratch."""
+    if h.dim() != 2 or W.dim() != 2:
+        raise ValueError("h must be [N, H] and W [V, H]")
+    N, H = h.shape
+    V = W.shape[0]
+    dev = W.device
+    if dev.type != "cuda":
+        raise ValueError("flce_forward_noalloc runs on a GPU; tensors are on " + str(dev))
+    _check_tensor("h", h, (N, H), W.dtype, dev)
+    _check_tensor("W", W, (V, H), W.dtype, dev)
+    _check_tensor("labels", labels, (N,), torch.int64, dev)
+    _check_tensor("loss", loss, (), torch.float32, dev)
+    _check_tensor("num_tokens", num_tokens, (), torch.int64, dev)
+    if lse_out is not None:
+        _check_tensor("lse_out", lse_out, (N,), torch.float32, dev)
+    if status is not None:
+        _check_tensor("status", status, (), torch.int32, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        rc = _lib.load().flce_forward_noalloc(
+            _ptr(h), _ptr(W), _ptr(labels), N, H, V, int(ignore_index), float(softcap),
+            _red_code(reduction), int(num_label_tokens or 0), _ptr(loss), _ptr(num_tokens),
+            stream, _dtype_code(W.dtype), float(mb_scale), _ptr(status), _ptr(lse_out))
+    if rc != _lib.OK:
+        raise FlceError(rc, "flce_forward_noalloc")
     return loss, num_tokens
 
 

@@ -9,7 +9,9 @@ LIB_PATH = os.path.join(_HERE, "libflce.so")
 
 F32, BF16 = 0, 1
 SUM, MEAN = 0, 1
-OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_LABEL = range(6)
+OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_LABEL, ERR_SCRATCH = range(7)
+# bytes of the fixed scratch array behind flce_forward_noalloc (FLCE_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 96 << 20
 
 # Every symbol the header declares, with its ctypes signature.
 _c = ctypes
@@ -33,6 +35,8 @@ SIGNATURES = {
     "flce_forward_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
     "flce_forward_check_args": (_i32, _F_ARGS),
     "flce_forward": (_i32, _F_ARGS),
+    "flce_forward_noalloc": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _f32, _i32, _i64,
+                                    _vp, _vp, _vp, _i32, _f32, _vp, _vp]),
     "flce_forward_logits_check_args": (_i32, _F_ARGS + [_vp, _i64, _i32]),
     "flce_forward_logits": (_i32, _F_ARGS + [_vp, _i64, _i32]),
     "flce_status_string": (_c.c_char_p, [_i32]),

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #include "../../include/flce.h"
@@ -57,6 +58,49 @@ void prof_after(int kind, hipStream_t s) {
 const char* kKindNames[flce::kNumKinds] = {"label_scan", "lse_fwd_gemm", "lse_merge",
                                            "loss_final", "grad_logits_gemm", "dW_gemm",
                                            "dH_gemm", "fill", "probs_to_grad", "dH_reduce"};
+
+// ---- scratch of flce_forward_noalloc ---------------------------------------
+// One copy on every GPU the library runs on, held until the process ends. In
+// host code `scratch` is only a host-side stand-in for the symbol, never an
+// address: the device address of each GPU's copy comes from
+// hipGetSymbolAddress, looked up once per device with that device current,
+// and only that address is handed to kernels.
+static __device__ __align__(256) char scratch[FLCE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch copy of the GPU `stream` runs on (set up on
+// the first call on that GPU).
+hipError_t scratch_address(hipStream_t stream, void** out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t sd;
+    e = hipStreamGetDevice(stream, &sd);
+    if (e != hipSuccess) return e;
+    dev = int(sd);
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u) != 0) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 // The no-recompute variant (arguments already checked): token chunk by chunk,
 // the forward keeps the probabilities, the chunk's merge gives its lse, G is
@@ -250,6 +294,28 @@ int flce_forward(const void* h, const void* W, const int64_t* labels, int64_t N,
   return run(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens, loss,
              num_tokens, nullptr, nullptr, stream, dtype, mb_scale, 0, workspace, status,
              lse_out, false, dtype);
+}
+
+int flce_forward_noalloc(const void* h, const void* W, const int64_t* labels, int64_t N,
+                         int64_t H, int64_t V, int64_t ignore_index, float softcap,
+                         int reduction, int64_t num_label_tokens, float* loss,
+                         int64_t* num_tokens, void* stream, int dtype, float mb_scale,
+                         int32_t* status, float* lse_out) {
+  // the argument checks first, against a stand-in aligned address: only the
+  // workspace rules depend on it, and the scratch is always large enough
+  // once the size check below has passed
+  const size_t need = flce_forward_workspace_size(N, H, V, dtype);
+  int st = flce_forward_check_args(h, W, labels, N, H, V, ignore_index, softcap, reduction,
+                                   num_label_tokens, loss, num_tokens, stream, dtype, mb_scale,
+                                   reinterpret_cast<void*>(uintptr_t(256)), size_t(-1), status,
+                                   lse_out);
+  if (st != FLCE_OK) return st;
+  if (need > FLCE_NOALLOC_SCRATCH_BYTES) return FLCE_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (scratch_address(static_cast<hipStream_t>(stream), &ws) != hipSuccess) return FLCE_ERR_HIP;
+  return run(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens, loss,
+             num_tokens, nullptr, nullptr, stream, dtype, mb_scale, 0, ws, status, lse_out,
+             false, dtype);
 }
 
 int flce_forward_logits(const void* h, const void* W, const int64_t* labels, int64_t N,

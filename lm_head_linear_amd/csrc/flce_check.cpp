@@ -311,6 +311,9 @@ const char* flce_status_string(int s) {
     case FLCE_ERR_WORKSPACE: return "FLCE_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case FLCE_ERR_HIP: return "FLCE_ERR_HIP: HIP runtime error";
     case FLCE_ERR_LABEL: return "FLCE_ERR_LABEL: non-ignored label outside [0, V)";
+    case FLCE_ERR_SCRATCH:
+      return "FLCE_ERR_SCRATCH: the problem needs more than the fixed scratch of the "
+             "no-allocation entry point";
     default: return "FLCE: unknown status";
   }
 }

@@ -52,7 +52,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(6):
+    for code in range(7):
         s = lib.flce_status_string(code).decode()
         assert s.startswith("FLCE_")
     assert "unknown" in lib.flce_status_string(99).decode()
@@ -443,3 +443,35 @@ def test_shapes_beyond_the_index_range_are_refused(lib):
     assert lib.flce_check_args_nr(*_args(V=1 << 22, H=8), 0) == 0
     # small batches with a huge vocabulary stay supported (G chunk rows are short)
     assert lib.flce_check_args(*_args(N=8, V=1 << 23, H=8)) == 0
+
+
+def test_noalloc_refusals_before_any_launch(lib):
+    """flce_forward_noalloc refuses a problem whose forward workspace exceeds
+    its fixed scratch, and bad arguments, before touching the GPU."""
+    from lm_head_linear_amd import _lib
+    N, H, V = 16384, 64, 1 << 20
+    assert lib.flce_forward_workspace_size(N, H, V, 1) > _lib.NOALLOC_SCRATCH_BYTES
+    assert lib.flce_forward_workspace_size(16384, 4096, 131072, 1) <= _lib.NOALLOC_SCRATCH_BYTES
+    assert lib.flce_forward_workspace_size(8192, 3584, 256000, 1) <= _lib.NOALLOC_SCRATCH_BYTES
+
+    def call(**kw):
+        a = dict(h=A16, W=A16 * 64, labels=A16 * 128, N=N, H=H, V=V, ignore=-100, softcap=0.0,
+                 red=0, T=0, loss=A16 * 129, nt=A16 * 130, stream=None, dtype=1, mb=1.0,
+                 status=None, lse=None)
+        a.update(kw)
+        return lib.flce_forward_noalloc(*[a[k] for k in ("h", "W", "labels", "N", "H", "V",
+                                                         "ignore", "softcap", "red", "T", "loss",
+                                                         "nt", "stream", "dtype", "mb", "status",
+                                                         "lse")])
+    assert call() == _lib.ERR_SCRATCH
+    assert call(mb=-1.0) == _lib.ERR_ARG
+    assert call(H=12) == _lib.ERR_UNSUPPORTED
+    assert call(loss=None) == _lib.ERR_ARG
+
+
+def test_noalloc_scratch_size_matches_header():
+    from lm_head_linear_amd import _lib
+    src = open(HEADER).read()
+    m = re.search(r"#define FLCE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m, "FLCE_NOALLOC_SCRATCH_BYTES"
+    assert int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
