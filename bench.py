@@ -189,6 +189,7 @@ def other_configs(steps: int, warmup: int):
         res = {"N": N, "H": H, "V": V, "softcap": w.softcap, "reduction": w.reduction,
                "num_label_tokens": w.num_label_tokens}
         nhv = float(N) * H * V
+        xfl = sum(step_flops(N, int((w.labels != w.ignore_index).sum()), H, V).values())
         for name, fn in runs.items():
             ms, ev_ms = time_steps(fn, steps, warmup)
             res[name] = {"ms_per_step": round(ms, 4), "event_ms_per_step": round(ev_ms, 4),
@@ -196,7 +197,9 @@ def other_configs(steps: int, warmup: int):
                          "mfma_frac_8nhv": round(8.0 * nhv / (ms * 1e-3) / 1e12
                                                  / PEAK_BF16_TFLOPS, 4),
                          "mfma_frac_6nhv": round(6.0 * nhv / (ms * 1e-3) / 1e12
-                                                 / PEAK_BF16_TFLOPS, 4)}
+                                                 / PEAK_BF16_TFLOPS, 4),
+                         "mfma_frac_executed": round(xfl / (ms * 1e-3) / 1e12
+                                                     / PEAK_BF16_TFLOPS, 4)}
             log(f"{w.name} {name}: {ms:.3f} ms/step")
         torch.cuda.synchronize()
         res["extra_memory_bytes"] = int(torch.cuda.max_memory_allocated(dev) - base)
@@ -336,10 +339,20 @@ def other_modes(m, w, h, W, y, dH, dW, loss, nt, steps, timing, nhv):
     return forward_only, float32_grads, no_recompute
 
 
-def kernel_pass(m, step, steps: int, nhv: float):
+def step_flops(N: int, n_kept: int, H: int, V: int) -> dict:
+    """Matrix flops each GEMM kind executes per step of flce_forward_backward
+    (bf16): the forward over all N tokens; the recompute, dW and dH over the
+    n_kept non-ignored tokens only (the backward gathers them: an ignored
+    token's logit gradient is exactly zero, so its products are zeros)."""
+    return {"lse_fwd_gemm": 2.0 * N * H * V, "grad_logits_gemm": 2.0 * n_kept * H * V,
+            "dW_gemm": 2.0 * n_kept * H * V, "dH_gemm": 2.0 * n_kept * H * V}
+
+
+def kernel_pass(m, step, steps: int, flops: dict):
     """Per-kernel HIP-event timing over `steps` extra steps, run after the
     headline loop (events bracket every launch on the call's stream, so this
-    pass is not the one `value` comes from). Returns (kernels, roofline)."""
+    pass is not the one `value` comes from). `flops`: executed matrix flops
+    per step of each GEMM kind. Returns (kernels, roofline)."""
     import torch
     m.flce_profile_begin()
     for _ in range(steps):
@@ -352,11 +365,11 @@ def kernel_pass(m, step, steps: int, nhv: float):
             continue
         e = {"ms_per_step": ms / steps, "launches_per_step": n / steps, "avg_launch_ms": ms / n}
         if name in GEMM_KINDS:
-            e["tflops"] = 2 * nhv * steps / (ms * 1e-3) / 1e12
+            e["tflops"] = flops[name] * steps / (ms * 1e-3) / 1e12
         kernels[name] = e
     dom = max(GEMM_KINDS, key=lambda k: kernels.get(k, {}).get("ms_per_step", 0.0))
     d = kernels[dom]
-    flops_per_launch = 2 * nhv / d["launches_per_step"]
+    flops_per_launch = flops[dom] / d["launches_per_step"]
     achieved = flops_per_launch / (d["avg_launch_ms"] * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
@@ -463,10 +476,13 @@ def main():
     nhv = float(N) * H * V
     tflops_8 = 8 * nhv / (wall_ms * 1e-3) / 1e12
     tflops_6 = 6 * nhv / (wall_ms * 1e-3) / 1e12
+    n_kept = int((w.labels != w.ignore_index).sum())
+    flops = step_flops(N, n_kept, H, V)
+    tflops_x = sum(flops.values()) / (wall_ms * 1e-3) / 1e12
     kernels, roofline = {}, None
     ksteps = args.steps if args.kernel_steps < 0 else args.kernel_steps
     if ksteps > 0:
-        kernels, roofline = kernel_pass(m, step, ksteps, nhv)
+        kernels, roofline = kernel_pass(m, step, ksteps, flops)
 
     forward_only = float32_grads = no_recompute = None
     configs = None
@@ -505,6 +521,10 @@ def main():
         "mfma_frac_8nhv": round(tflops_8 / PEAK_BF16_TFLOPS, 4),
         "mfma_frac_6nhv": round(tflops_6 / PEAK_BF16_TFLOPS, 4),
         "tflops_8nhv": round(tflops_8, 1),
+        "tokens_kept": n_kept,
+        "executed_flops_per_step": sum(flops.values()),
+        "tflops_executed": round(tflops_x, 1),
+        "mfma_frac_executed": round(tflops_x / PEAK_BF16_TFLOPS, 4),
         "event_ms_per_step": round(ev_ms, 4),
         "extra_memory_bytes": int(peak_extra),
         "workspace_bytes": int(ws_bytes),

@@ -57,7 +57,8 @@ void prof_after(int kind, hipStream_t s) {
 
 const char* kKindNames[flce::kNumKinds] = {"label_scan", "lse_fwd_gemm", "lse_merge",
                                            "loss_final", "grad_logits_gemm", "dW_gemm",
-                                           "dH_gemm", "fill", "probs_to_grad", "dH_reduce"};
+                                           "dH_gemm", "fill", "probs_to_grad", "dH_reduce",
+                                           "gather"};
 
 // ---- scratch of flce_forward_noalloc ---------------------------------------
 // One copy on every GPU the library runs on, held until the process ends. In
@@ -190,11 +191,20 @@ int run(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t 
   a.g = backward ? ws + p.off_g : nullptr;
   a.dh_acc = p.need_dh_acc ? reinterpret_cast<float*>(ws + p.off_dhacc) : nullptr;
   a.dh_part = p.dh_kseg ? reinterpret_cast<float*>(ws + p.off_dhpart) : nullptr;
+  if (p.compact) {
+    a.idx = reinterpret_cast<int32_t*>(ws + p.off_idx);
+    a.yc = reinterpret_cast<int64_t*>(ws + p.off_yc);
+    a.lsec = reinterpret_cast<float*>(ws + p.off_lsec);
+    a.ztc = reinterpret_cast<float*>(ws + p.off_ztc);
+    a.bcnt = reinterpret_cast<int32_t*>(ws + p.off_bcnt);
+    a.hc = ws + p.off_hc;
+  }
 
   const bool bf16 = dtype == FLCE_BF16;
   e = flce::launch_label_scan(p, a, L);
   if (e == hipSuccess) e = bf16 ? flce::bf16_forward(p, a, L) : flce::f32_forward(p, a, L);
   if (e == hipSuccess) e = flce::launch_merge_and_loss(p, a, L);
+  if (e == hipSuccess && backward && p.compact) e = flce::launch_gather(p, a, L);
   for (int64_t c = 0; backward && e == hipSuccess && c < p.n_chunks; ++c)
     e = bf16 ? flce::bf16_backward_chunk(p, a, c, L) : flce::f32_backward_chunk(p, a, c, L);
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;

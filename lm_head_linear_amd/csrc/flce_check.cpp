@@ -77,6 +77,17 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
       q.off_dhpart = off;
       off = align256(off + size_t(q.dh_segs) * size_t(N) * H * sizeof(float));
     }
+    // the backward over the non-ignored tokens, gathered in order
+    q.compact = backward && dtype == FLCE_BF16 && q.g_parts == 1;
+    if (q.compact) {
+      q.n_gather_blocks = ceil_div(N, kGatherBlock);
+      q.off_idx = off;  off = align256(off + size_t(N) * sizeof(int32_t));
+      q.off_yc = off;   off = align256(off + size_t(N) * sizeof(int64_t));
+      q.off_lsec = off; off = align256(off + size_t(N) * sizeof(float));
+      q.off_ztc = off;  off = align256(off + size_t(N) * sizeof(float));
+      q.off_bcnt = off; off = align256(off + size_t(q.n_gather_blocks) * sizeof(int32_t));
+      q.off_hc = off;   off = align256(off + size_t(N) * H * q.elem);
+    }
   }
   q.total = off;
   *p = q;

@@ -21,7 +21,8 @@ enum Kind : int {
   kFill = 7,
   kProbsToGrad = 8,
   kDhReduce = 9,
-  kNumKinds = 10,
+  kGather = 10,
+  kNumKinds = 11,
 };
 
 // Everything one call needs on the device side.
@@ -56,6 +57,13 @@ struct Args {
   float* dh_acc;  // [N][H] (bf16 path with several chunks)
   float* dh_part; // [dh_segs][M][H] split-K partial products of dH (or null)
   float* dw_acc;  // [V][H] float32 dW running sum (no-recompute, several chunks)
+  // compact plan: the non-ignored tokens gathered in order (see Plan)
+  int32_t* idx;   // original position of kept token r
+  int64_t* yc;    // its label
+  float* lsec;    // its lse
+  float* ztc;     // its target logit
+  int32_t* bcnt;  // kept tokens per gather block
+  void* hc;       // its hidden row, bf16 [N][H] (the first n_valid rows)
 };
 
 // Launch hook: the C-ABI layer brackets launches with timing events.
@@ -76,6 +84,10 @@ hipError_t launch_merge_and_loss(const Plan& p, const Args& a, const Launcher& L
 hipError_t launch_merge(const Plan& p, const Args& a, int64_t t0, int64_t nt, const Launcher& L);
 hipError_t launch_loss_final(const Plan& p, const Args& a, const Launcher& L);
 hipError_t launch_zero_bytes(void* ptr, size_t bytes, const Launcher& L);
+// Compact plan: gather the non-ignored tokens (positions, labels, lse,
+// target logits, hidden rows) after the forward, and zero the dH rows of the
+// ignored ones.
+hipError_t launch_gather(const Plan& p, const Args& a, const Launcher& L);
 
 // bf16 MFMA path.
 hipError_t bf16_forward(const Plan& p, const Args& a, const Launcher& L);

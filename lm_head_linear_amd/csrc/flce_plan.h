@@ -10,6 +10,8 @@ namespace flce {
 
 // Tile edge of the bf16 MFMA kernels (tokens x vocab and vocab/tokens x hidden).
 constexpr int64_t kTileBF16 = 256;
+// Tokens per workgroup of the gather of non-ignored tokens.
+constexpr int64_t kGatherBlock = 1024;
 // Tile edge of the float32 kernels.
 constexpr int64_t kTileF32 = 64;
 // Upper bound on the elements of one chunk of the logit gradient G^T.
@@ -83,6 +85,14 @@ struct Plan {
   // No-recompute variant with several token chunks: dW is added up over the
   // chunks in a float32 [V][H] running sum at off_dwacc, rounded to bf16 once.
   bool need_dw_acc = false;
+  // bf16 gradients of the recompute path: the backward runs over the
+  // non-ignored tokens only, gathered in order (ignored tokens have G = 0, so
+  // their recompute, dW and dH products are exact zeros). The workspace then
+  // holds their original positions (int32 [N]), labels (int64 [N]), lse and
+  // target logits (float [N]), hidden rows (bf16 [N][H]) and per-block counts
+  // of the gather (int32 [n_gather_blocks]); the device count is n_valid.
+  bool compact = false;
+  int64_t n_gather_blocks = 0;
   // Split-K of the dH GEMM (bf16 gradients): segments of dh_kseg vocabulary
   // rows (0: not split), at most dh_segs of them per launch, each writing a
   // float32 [M][H] partial product at off_dhpart.
@@ -91,7 +101,8 @@ struct Plan {
   size_t grad_elem = 0;      // bytes per element of dH/dW
   // byte offsets into the workspace
   size_t off_scalars = 0, off_part = 0, off_zt = 0, off_lse = 0, off_lsum = 0,
-         off_g = 0, off_dhacc = 0, off_dhpart = 0, off_dwacc = 0, total = 0;
+         off_g = 0, off_dhacc = 0, off_dhpart = 0, off_dwacc = 0, off_idx = 0, off_yc = 0,
+         off_lsec = 0, off_ztc = 0, off_hc = 0, off_bcnt = 0, total = 0;
 };
 
 // Builds the plan; returns false for invalid sizes or dtypes. A forward-only

@@ -39,7 +39,9 @@ FLCE_HD constexpr int num_stages(int fa, int fb) {
 // x 2 bytes over 256 threads), and register loads for a partial tile.
 FLCE_HD constexpr int loads_per_operand(int sk) { return sk / 8; }
 FLCE_HD constexpr int tail_loads(int sk) { return sk / 8; }
-enum Buf : int { kBufW = 0, kBufH = 1, kBufG = 2 };
+// Operand buffers: W, h, the logit gradient G, and the hidden rows of the
+// non-ignored tokens gathered in order (the backward of a compact plan).
+enum Buf : int { kBufW = 0, kBufH = 1, kBufG = 2, kBufHc = 3 };
 
 // Geometry of one operand. N form: stored [rows][K] (K contiguous); T form:
 // stored [K][rows] (rows contiguous). `ld` = elements between stored rows.
@@ -74,7 +76,10 @@ struct Launch {
 // The forward launch, and the three launches of backward chunk c (0: logit
 // gradient, 1: dW, 2: dH). With float32 gradients for bf16 inputs G is a
 // pair of bf16 chunks, hi then lo, each vchunk x ldg elements; `part` picks
-// the one a dW or dH launch reads.
+// the one a dW or dH launch reads. A compact plan's backward reads the
+// gathered rows of the non-ignored tokens instead of h; its token dimension
+// (N of the gradient launch, K of dW, M of dH) is then cut on the device to
+// the non-ignored count, and the sizes here are the upper bound N.
 inline Launch forward_launch(const Plan& p) {
   return Launch{p.V, p.N, p.H, kFormN, kFormN, kBufW, kBufH, 0, 0,
                 Geom{p.H, p.V, p.H}, Geom{p.H, p.N, p.H}};
@@ -92,15 +97,16 @@ inline int64_t g_block(const Plan& p) { return p.ldg * 32; }
 inline Launch backward_launch(const Plan& p, int64_t c, int which, int part = 0) {
   const int64_t v0 = c * p.vchunk, vcur = chunk_rows(p, c);
   const int64_t g_off = int64_t(part) * p.vchunk * p.ldg;
+  const int hb = p.compact ? kBufHc : kBufH;
   if (which == 0)  // Z^T[chunk] = W[chunk] . h^T, then the gradient epilogue
-    return Launch{vcur, p.N, p.H, kFormN, kFormN, kBufW, kBufH, v0 * p.H, 0,
+    return Launch{vcur, p.N, p.H, kFormN, kFormN, kBufW, hb, v0 * p.H, 0,
                   Geom{p.H, vcur, p.H}, Geom{p.H, p.N, p.H}};
   // G is stored blocked (g_block(p) elements per 32 vocabulary columns; see
   // Geom): G[t][v - v0] at blocked_offset(t, v - v0, g_block(p)). Columns
   // from vcur to vchunk are never multiplied into a stored output.
   const int64_t blk = g_block(p);
   if (which == 1)  // dW[chunk] = G[:, chunk]^T . h  (K = tokens)
-    return Launch{vcur, p.H, p.N, kFormT, kFormT, kBufG, kBufH, g_off, 0,
+    return Launch{vcur, p.H, p.N, kFormT, kFormT, kBufG, hb, g_off, 0,
                   Geom{32, p.vchunk, p.N, blk}, Geom{p.H, p.H, p.N}};
   // dH += G[:, chunk] . W[chunk]  (K = chunk rows)
   return Launch{p.N, p.H, vcur, kFormN, kFormT, kBufG, kBufW, g_off, v0 * p.H,

@@ -504,10 +504,17 @@ __device__ __forceinline__ void k_loop(Acc& acc, const Operand& A, const Operand
   }
 }
 
-template <int FA, int FB, class Epi, bool BA, int SEGS, bool SPLITK>
+// Which dimension of a launch is cut on the device to the count at `dyn`
+// (the non-ignored tokens of a compact plan): none, M, N or K. The raster
+// uses the launch's sizes (an upper bound), so workgroups whose tile starts
+// past the count leave at once, before any load.
+enum Dyn : int { kDynNone = 0, kDynM = 1, kDynN = 2, kDynK = 3 };
+
+template <int FA, int FB, class Epi, bool BA, int SEGS, bool SPLITK, int DYN>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A_, Operand B_, int64_t M,
                                                       int64_t Nn, int64_t K, int group_m,
-                                                      Epi epi, int64_t a2_off) {
+                                                      Epi epi, int64_t a2_off,
+                                                      const int64_t* dyn) {
   // BA: operand A is the blocked G (gemm::Geom). Fixing blk at compile time
   // for the dense operands lets the address arithmetic drop the blocked case.
   // SEGS = 2: a second K loop over A shifted by a2_off elements (the lo half
@@ -543,6 +550,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A_, Operand B_, in
   __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes + Epi::kTokBytes];
   int64_t m0, n0;
   gemm::tile_coords(blockIdx.x, M, Nn, group_m, m0, n0);
+  if constexpr (DYN != kDynNone) {
+    const int64_t d = *dyn;
+    if constexpr (DYN == kDynM) {
+      if (m0 >= d) return;
+      M = d < M ? d : M;
+      epi.N = M;                                   // the epilogue's token rows
+    } else if constexpr (DYN == kDynN) {
+      if (n0 >= d) return;
+      Nn = d < Nn ? d : Nn;
+      epi.N = Nn;                                  // the epilogue's token columns
+    } else {
+      K = d < K ? d : K;                           // past the count: zero-filled
+      A.g.K = K;
+      B.g.K = K;
+    }
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
@@ -1294,6 +1317,8 @@ struct EpiDH {
   uint16_t* dH;
   float* acc32;  // [N][H] float32 running sum (unused with a single chunk)
   int64_t N, H;
+  // compact plan: the bf16 row m of dH goes to row row_map[m] (null: m)
+  const int32_t* row_map = nullptr;
 
   struct Pass {
     const EpiDH& e;
@@ -1318,7 +1343,8 @@ struct EpiDH {
         v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
       }
       if (LAST) {
-        *reinterpret_cast<uint2*>(e.dH + m * e.H + n) =
+        const int64_t mo = e.row_map ? int64_t(e.row_map[m]) : m;
+        *reinterpret_cast<uint2*>(e.dH + mo * e.H + n) =
             make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
       } else {
         *reinterpret_cast<float4*>(e.acc32 + m * e.H + n) = v;
@@ -1342,15 +1368,16 @@ struct EpiDH {
 // the segments up.
 struct EpiDHPart {
   float* part;
-  int64_t N, H;
+  int64_t N, H;          // rows written (a compact plan cuts N on the device), columns
+  int64_t seg_stride;    // elements per segment's partial product (launch rows * H)
 
   static constexpr int kTokBytes = 0;             // no per-token inputs
   __device__ __forceinline__ void stage(char*, int64_t, int, int) const {}
 
   __device__ __forceinline__ void operator()(Acc& acc, int64_t m0, int64_t n0, int wm, int wn,
                                              int lane, char* smem, const char* tok) const {
-    EpiDH<true, false>{nullptr, part + int64_t(blockIdx.y) * N * H, N, H}(acc, m0, n0, wm, wn,
-                                                                         lane, smem, tok);
+    EpiDH<true, false>{nullptr, part + int64_t(blockIdx.y) * seg_stride, N, H, nullptr}(
+        acc, m0, n0, wm, wn, lane, smem, tok);
   }
 };
 
@@ -1363,7 +1390,14 @@ template <bool PRIOR, bool BF16OUT>
 __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ part, int segs,
                                                    int64_t n4, int64_t stride,
                                                    const float* prior, float* out32,
-                                                   uint16_t* out16) {
+                                                   uint16_t* out16, int64_t H,
+                                                   const int64_t* __restrict__ rows_dyn,
+                                                   const int32_t* __restrict__ row_map) {
+  // a compact plan: only the first *rows_dyn rows, the bf16 row m at row_map[m]
+  if (rows_dyn) {
+    const int64_t n4d = *rows_dyn * (H / 4);
+    n4 = n4d < n4 ? n4d : n4;
+  }
   for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n4;
        i += int64_t(gridDim.x) * 256) {
     float4 v = PRIOR ? reinterpret_cast<const float4*>(prior)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1371,39 +1405,47 @@ __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ par
       const float4 q = reinterpret_cast<const float4*>(part + z * stride)[i];
       v.x += q.x; v.y += q.y; v.z += q.z; v.w += q.w;
     }
-    if (BF16OUT)
-      reinterpret_cast<uint2*>(out16)[i] = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
-    else
+    if (BF16OUT) {
+      int64_t o = i;
+      if (row_map) {
+        const int64_t m = i / (H / 4);
+        o = int64_t(row_map[m]) * (H / 4) + (i - m * (H / 4));
+      }
+      reinterpret_cast<uint2*>(out16)[o] = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+    } else {
       reinterpret_cast<float4*>(out32)[i] = v;
+    }
   }
 }
 
 hipError_t launch_dh_reduce(const float* part, int64_t segs, int64_t n, const float* prior,
-                            float* out32, uint16_t* out16, const Launcher& L) {
+                            float* out32, uint16_t* out16, const Launcher& L, int64_t H,
+                            const int64_t* rows_dyn = nullptr, const int32_t* row_map = nullptr) {
   const int64_t n4 = n / 4;
   const int64_t want = (n4 + 255) / 256;
   const dim3 grid(unsigned(want < 4096 ? want : 4096));
   L.pre(kDhReduce);
   if (prior && out16)
     hipLaunchKernelGGL((k_dh_reduce<true, true>), grid, dim3(256), 0, L.stream, part, int(segs),
-                       n4, n, prior, out32, out16);
+                       n4, n, prior, out32, out16, H, rows_dyn, row_map);
   else if (prior)
     hipLaunchKernelGGL((k_dh_reduce<true, false>), grid, dim3(256), 0, L.stream, part, int(segs),
-                       n4, n, prior, out32, out16);
+                       n4, n, prior, out32, out16, H, rows_dyn, row_map);
   else if (out16)
     hipLaunchKernelGGL((k_dh_reduce<false, true>), grid, dim3(256), 0, L.stream, part, int(segs),
-                       n4, n, prior, out32, out16);
+                       n4, n, prior, out32, out16, H, rows_dyn, row_map);
   else
     hipLaunchKernelGGL((k_dh_reduce<false, false>), grid, dim3(256), 0, L.stream, part,
-                       int(segs), n4, n, prior, out32, out16);
+                       int(segs), n4, n, prior, out32, out16, H, rows_dyn, row_map);
   L.post(kDhReduce);
   return hipGetLastError();
 }
 
 const uint16_t* buf_ptr(const Args& a, int buf) {
-  return buf == gemm::kBufW ? static_cast<const uint16_t*>(a.W)
-       : buf == gemm::kBufH ? static_cast<const uint16_t*>(a.h)
-                            : static_cast<const uint16_t*>(a.g);
+  return buf == gemm::kBufW  ? static_cast<const uint16_t*>(a.W)
+       : buf == gemm::kBufH  ? static_cast<const uint16_t*>(a.h)
+       : buf == gemm::kBufHc ? static_cast<const uint16_t*>(a.hc)
+                             : static_cast<const uint16_t*>(a.g);
 }
 
 // A T-form operand is read in 16-byte column chunks: it needs rows % 8 == 0.
@@ -1426,17 +1468,20 @@ bool launch_ok(const gemm::Launch& l) {
   return l.M > 0 && l.Nn > 0 && l.K > 0;
 }
 
-template <int FA, int FB, bool BA = false, int SEGS = 1, bool SPLITK = false, class Epi>
+template <int FA, int FB, bool BA = false, int SEGS = 1, bool SPLITK = false, int DYN = kDynNone,
+          class Epi>
 hipError_t run_gemm(const gemm::Launch& l, const Args& a, const Epi& e, int kind,
-                    const Launcher& L, int64_t a2_off = 0, int64_t segs = 1) {
+                    const Launcher& L, int64_t a2_off = 0, int64_t segs = 1,
+                    const int64_t* dyn = nullptr) {
   if (!launch_ok(l)) return hipErrorInvalidValue;
   if ((l.a.blk != 0) != BA || l.b.blk != 0) return hipErrorInvalidValue;
+  if ((DYN != kDynNone) != (dyn != nullptr)) return hipErrorInvalidValue;
   Operand A{buf_ptr(a, l.buf_a) + l.off_a, l.a};
   Operand B{buf_ptr(a, l.buf_b) + l.off_b, l.b};
   L.pre(kind);
-  hipLaunchKernelGGL((k_gemm<FA, FB, Epi, BA, SEGS, SPLITK>),
+  hipLaunchKernelGGL((k_gemm<FA, FB, Epi, BA, SEGS, SPLITK, DYN>),
                      dim3(unsigned(gemm::num_tiles(l.M, l.Nn)), unsigned(segs)), dim3(kThreads), 0,
-                     L.stream, A, B, l.M, l.Nn, l.K, gemm::kGroupM, e, a2_off);
+                     L.stream, A, B, l.M, l.Nn, l.K, gemm::kGroupM, e, a2_off, dyn);
   L.post(kind);
   return hipGetLastError();
 }
@@ -1513,54 +1558,66 @@ hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, cons
   const int64_t v0 = chunk * p.vchunk;
   const int64_t vcur = gemm::chunk_rows(p, chunk);
   uint16_t* g = static_cast<uint16_t*>(a.g);
+  // A compact plan runs over the non-ignored tokens gathered in order: their
+  // labels, lse, target logits and rows, with the token count on the device.
+  const bool cp = p.compact;
+  const int64_t* nv = cp ? &a.sc->n_valid : nullptr;
+  const int64_t* lab = cp ? a.yc : a.labels;
+  const float* lse = cp ? a.lsec : a.lse;
+  const float* zt = cp ? a.ztc : a.zt;
   // 1) recompute the logits of the chunk and form G[N][vchunk]
+  const gemm::Launch lg = gemm::backward_launch(p, chunk, 0);
+  constexpr int NF = gemm::kFormN, TF = gemm::kFormT;
   hipError_t err;
   if (a.softcap > 0.f) {
-    EpiGrad<true, false> eg{a.labels, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
+    EpiGrad<true, false> eg{lab, lse, zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
                             gemm::g_block(p), a.softcap, 1.f / a.softcap, g, 0};
-    err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
-                                               kGradLogits, L);
+    err = cp ? run_gemm<NF, NF, false, 1, false, kDynN>(lg, a, eg, kGradLogits, L, 0, 1, nv)
+             : run_gemm<NF, NF>(lg, a, eg, kGradLogits, L);
   } else {
-    EpiGrad<false, false> eg{a.labels, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
+    EpiGrad<false, false> eg{lab, lse, zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
                              gemm::g_block(p), 0.f, 0.f, g, 0};
-    err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
-                                               kGradLogits, L);
+    err = cp ? run_gemm<NF, NF, false, 1, false, kDynN>(lg, a, eg, kGradLogits, L, 0, 1, nv)
+             : run_gemm<NF, NF>(lg, a, eg, kGradLogits, L);
   }
   if (err != hipSuccess) return err;
-  // 2) dW[v0:v0+vcur] = G^T . h
+  // 2) dW[v0:v0+vcur] = G^T . h  (K = the tokens)
   uint16_t* dW = static_cast<uint16_t*>(a.dW);
   const gemm::Launch lw = gemm::backward_launch(p, chunk, 1);
-  if (a.accumulate_dW)
-    err = run_gemm<gemm::kFormT, gemm::kFormT, true>(lw, a, EpiDW<true>{dW, p.H, v0, vcur},
-                                                     kGemmDW, L);
-  else
-    err = run_gemm<gemm::kFormT, gemm::kFormT, true>(lw, a, EpiDW<false>{dW, p.H, v0, vcur},
-                                                     kGemmDW, L);
+  if (a.accumulate_dW) {
+    const EpiDW<true> ew{dW, p.H, v0, vcur};
+    err = cp ? run_gemm<TF, TF, true, 1, false, kDynK>(lw, a, ew, kGemmDW, L, 0, 1, nv)
+             : run_gemm<TF, TF, true>(lw, a, ew, kGemmDW, L);
+  } else {
+    const EpiDW<false> ew{dW, p.H, v0, vcur};
+    err = cp ? run_gemm<TF, TF, true, 1, false, kDynK>(lw, a, ew, kGemmDW, L, 0, 1, nv)
+             : run_gemm<TF, TF, true>(lw, a, ew, kGemmDW, L);
+  }
   if (err != hipSuccess) return err;
-  // 3) dH (+)= G[:, chunk] . W[chunk], chunks in order
+  // 3) dH (+)= G[:, chunk] . W[chunk], chunks in order (compact: the rows of
+  // the kept tokens, scattered to their positions when stored as bf16)
   uint16_t* dH = static_cast<uint16_t*>(a.dH);
+  const int32_t* rmap = cp ? a.idx : nullptr;
   const gemm::Launch lh = gemm::backward_launch(p, chunk, 2);
   const bool first = chunk == 0, last = chunk == p.n_chunks - 1;
   if (p.dh_kseg) {
     // few output tiles: split K, then add the segments up in a fixed order
     const int64_t segs = (lh.K + p.dh_kseg - 1) / p.dh_kseg;
-    err = run_gemm<gemm::kFormN, gemm::kFormT, true, 1, true>(
-        lh, a, EpiDHPart{a.dh_part, p.N, p.H}, kGemmDH, L, p.dh_kseg, segs);
+    const EpiDHPart ep{a.dh_part, p.N, p.H, p.N * p.H};
+    err = cp ? run_gemm<NF, TF, true, 1, true, kDynM>(lh, a, ep, kGemmDH, L, p.dh_kseg, segs, nv)
+             : run_gemm<NF, TF, true, 1, true>(lh, a, ep, kGemmDH, L, p.dh_kseg, segs);
     if (err != hipSuccess) return err;
     return launch_dh_reduce(a.dh_part, segs, p.N * p.H, first ? nullptr : a.dh_acc,
-                            last ? nullptr : a.dh_acc, last ? dH : nullptr, L);
+                            last ? nullptr : a.dh_acc, last ? dH : nullptr, L, p.H, nv, rmap);
   }
-  if (first && last)
-    return run_gemm<gemm::kFormN, gemm::kFormT, true>(
-        lh, a, EpiDH<true, true>{dH, a.dh_acc, p.N, p.H}, kGemmDH, L);
-  if (first)
-    return run_gemm<gemm::kFormN, gemm::kFormT, true>(
-        lh, a, EpiDH<true, false>{dH, a.dh_acc, p.N, p.H}, kGemmDH, L);
-  if (last)
-    return run_gemm<gemm::kFormN, gemm::kFormT, true>(
-        lh, a, EpiDH<false, true>{dH, a.dh_acc, p.N, p.H}, kGemmDH, L);
-  return run_gemm<gemm::kFormN, gemm::kFormT, true>(
-      lh, a, EpiDH<false, false>{dH, a.dh_acc, p.N, p.H}, kGemmDH, L);
+  auto dh = [&](auto epi) {
+    return cp ? run_gemm<NF, TF, true, 1, false, kDynM>(lh, a, epi, kGemmDH, L, 0, 1, nv)
+              : run_gemm<NF, TF, true>(lh, a, epi, kGemmDH, L);
+  };
+  if (first && last) return dh(EpiDH<true, true>{dH, a.dh_acc, p.N, p.H, rmap});
+  if (first) return dh(EpiDH<true, false>{dH, a.dh_acc, p.N, p.H, rmap});
+  if (last) return dh(EpiDH<false, true>{dH, a.dh_acc, p.N, p.H, rmap});
+  return dh(EpiDH<false, false>{dH, a.dh_acc, p.N, p.H, rmap});
 }
 
 }  // namespace flce
@@ -1627,9 +1684,9 @@ hipError_t bf16_nr_backward_chunk(const Plan& p, const Args& a, int64_t c, const
     // few output tiles: split K, then add the segments up in a fixed order
     const int64_t segs = (lh.K + p.dh_kseg - 1) / p.dh_kseg;
     err = run_gemm<gemm::kFormN, gemm::kFormT, true, 1, true>(
-        lh, a, EpiDHPart{a.dh_part, nt, p.H}, kGemmDH, L, p.dh_kseg, segs);
+        lh, a, EpiDHPart{a.dh_part, nt, p.H, nt * p.H}, kGemmDH, L, p.dh_kseg, segs);
     if (err != hipSuccess) return err;
-    return launch_dh_reduce(a.dh_part, segs, nt * p.H, nullptr, nullptr, dH, L);
+    return launch_dh_reduce(a.dh_part, segs, nt * p.H, nullptr, nullptr, dH, L, p.H);
   }
   return run_gemm<gemm::kFormN, gemm::kFormT, true>(lh, a, EpiDH<true, true>{dH, nullptr, nt, p.H},
                                                     kGemmDH, L);

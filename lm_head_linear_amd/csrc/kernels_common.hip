@@ -141,6 +141,84 @@ __global__ __launch_bounds__(256) void k_zero1(unsigned char* __restrict__ p, in
     p[i] = 0;
 }
 
+// ---- the non-ignored tokens, gathered in order, for the backward ----------
+// Ignored tokens have G = 0: their recomputed logits, dW and dH products are
+// exact zeros, so the backward runs over the kept tokens only. Block b of
+// kGatherBlock tokens first counts its kept tokens; then every block finds
+// the count before it and the rank of each kept token inside it (wave
+// ballots), and writes the token's original position, label, lse and target
+// logit at its rank; the hidden rows follow in a copy kernel.
+constexpr int kGatherThreads = int(kGatherBlock);
+
+__global__ __launch_bounds__(kGatherThreads) void k_gather_count(
+    const int64_t* __restrict__ labels, int64_t N, int64_t ignore_index,
+    int32_t* __restrict__ bcnt) {
+  __shared__ int32_t wsum[kGatherThreads / 64];
+  const int64_t t = int64_t(blockIdx.x) * kGatherThreads + threadIdx.x;
+  const bool keep = t < N && labels[t] != ignore_index;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const unsigned long long m = __ballot(keep);
+  if (lane == 0) wsum[w] = __popcll(m);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t s = 0;
+    for (int i = 0; i < kGatherThreads / 64; ++i) s += wsum[i];
+    bcnt[blockIdx.x] = s;
+  }
+}
+
+__global__ __launch_bounds__(kGatherThreads) void k_gather_tokens(
+    const int64_t* __restrict__ labels, int64_t N, int64_t ignore_index,
+    const float* __restrict__ lse, const float* __restrict__ zt,
+    const int32_t* __restrict__ bcnt, int32_t* __restrict__ idx, int64_t* __restrict__ yc,
+    float* __restrict__ lsec, float* __restrict__ ztc) {
+  __shared__ int64_t part[kGatherThreads / 64];
+  __shared__ int32_t wsum[kGatherThreads / 64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // kept tokens of the blocks before this one
+  int64_t s = 0;
+  for (int64_t i = threadIdx.x; i < blockIdx.x; i += kGatherThreads) s += bcnt[i];
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if (lane == 0) part[w] = s;
+  const int64_t t = int64_t(blockIdx.x) * kGatherThreads + threadIdx.x;
+  const int64_t y = t < N ? labels[t] : ignore_index;
+  const bool keep = t < N && y != ignore_index;
+  const unsigned long long m = __ballot(keep);
+  if (lane == 0) wsum[w] = __popcll(m);
+  __syncthreads();
+  if (!keep) return;
+  int64_t pos = __popcll(m & ((1ull << lane) - 1));
+  for (int i = 0; i < kGatherThreads / 64; ++i) pos += part[i] + (i < w ? wsum[i] : 0);
+  idx[pos] = int32_t(t);
+  yc[pos] = y;
+  lsec[pos] = lse[t];
+  ztc[pos] = zt[t];
+}
+
+// hc[r] = h[idx[r]] for the n_valid kept rows, in 16-byte pieces (h8 per row).
+__global__ __launch_bounds__(256) void k_gather_rows(const uint4* __restrict__ h, int64_t h8,
+                                                     const int32_t* __restrict__ idx,
+                                                     const Scalars* __restrict__ sc,
+                                                     uint4* __restrict__ hc) {
+  const int64_t total = sc->n_valid * h8;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total;
+       i += int64_t(gridDim.x) * 256) {
+    const int64_t r = i / h8;
+    hc[i] = h[int64_t(idx[r]) * h8 + (i - r * h8)];
+  }
+}
+
+// Zero rows of dH (16-byte pieces, h8 per row) whose token is ignored: the
+// compact backward never writes them.
+__global__ __launch_bounds__(256) void k_zero_ignored_rows(const int64_t* __restrict__ labels,
+                                                           int64_t N, int64_t ignore_index,
+                                                           int64_t h8, uint4* __restrict__ dH) {
+  const uint4 z = {0u, 0u, 0u, 0u};
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < N * h8;
+       i += int64_t(gridDim.x) * 256)
+    if (labels[i / h8] == ignore_index) dH[i] = z;
+}
+
 }  // namespace
 
 hipError_t launch_empty(const Plan&, const Args& a, const Launcher& L) {
@@ -199,6 +277,24 @@ hipError_t launch_zero_bytes(void* ptr, size_t bytes, const Launcher& L) {
                        reinterpret_cast<unsigned char*>(ptr), int64_t(bytes));
   }
   L.post(kFill);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const Plan& p, const Args& a, const Launcher& L) {
+  const unsigned nb = unsigned(p.n_gather_blocks);
+  L.pre(kGather);
+  hipLaunchKernelGGL(k_gather_count, dim3(nb), dim3(kGatherThreads), 0, L.stream, a.labels, p.N,
+                     a.ignore_index, a.bcnt);
+  hipLaunchKernelGGL(k_gather_tokens, dim3(nb), dim3(kGatherThreads), 0, L.stream, a.labels, p.N,
+                     a.ignore_index, a.lse, a.zt, a.bcnt, a.idx, a.yc, a.lsec, a.ztc);
+  const int64_t h8 = p.H / 8;
+  int64_t blocks = (p.N * h8 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_gather_rows, dim3(unsigned(blocks)), dim3(256), 0, L.stream,
+                     static_cast<const uint4*>(a.h), h8, a.idx, a.sc, static_cast<uint4*>(a.hc));
+  hipLaunchKernelGGL(k_zero_ignored_rows, dim3(unsigned(blocks)), dim3(256), 0, L.stream,
+                     a.labels, p.N, a.ignore_index, h8, static_cast<uint4*>(a.dH));
+  L.post(kGather);
   return hipGetLastError();
 }
 

@@ -1,0 +1,101 @@
+"""The bf16 backward runs over the non-ignored tokens only, gathered in order
+(their G rows are the only non-zero ones). GPU parity against the oracle for
+ignore patterns that stress the gather: masked prefixes of every sequence,
+runs across 256-token tile edges, a single kept token, ignored first and last
+tokens, over several backward chunks and with a split-K dH; the rows of
+ignored tokens in dH are exactly zero even when dH held NaN before the call;
+an all-ignored call leaves an accumulated dW bit for bit unchanged."""
+import numpy as np
+import pytest
+import torch
+
+import flce_inputs as fi
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import lm_head_linear_amd._lib as L
+    L.load()
+    yield
+
+
+@pytest.fixture
+def vchunk(monkeypatch):
+    def set_chunk(v):
+        monkeypatch.setenv("FLCE_VCHUNK", str(v))
+    return set_chunk
+
+
+def _mask(N, kind, rng):
+    m = np.zeros(N, dtype=bool)
+    if kind == "prefix":                  # first quarter of each of 2 sequences
+        S = N // 2
+        m[:S // 4] = True
+        m[S:S + S // 4] = True
+    elif kind == "tile_edges":            # runs across the 256-token tile edges
+        for e in range(256, N, 256):
+            m[max(0, e - 37):e + 21] = True
+    elif kind == "one_kept":
+        m[:] = True
+        m[N // 3] = False
+    elif kind == "ends":
+        m[0] = m[N - 1] = True
+        m[rng.choice(N, N // 5, replace=False)] = True
+    elif kind == "random_half":
+        m[rng.choice(N, N // 2, replace=False)] = True
+    return m
+
+
+@pytest.mark.parametrize("kind", ["prefix", "tile_edges", "one_kept", "ends", "random_half"])
+@pytest.mark.parametrize("N,H,V,chunk", [
+    (1100, 264, 3000, 1024),    # 3 chunks, ragged everywhere, split-K dH (few tiles)
+    (2048, 512, 2560, 0),       # one chunk
+    (777, 128, 1500, 256),      # many chunks
+])
+def test_compact_patterns(kind, N, H, V, chunk, vchunk):
+    if chunk:
+        vchunk(chunk)
+    rng = np.random.default_rng(N + V)
+    w = fi.make_custom(N, H, V, dtype=torch.bfloat16, seed=N + H, ignore_frac=0.0,
+                       softcap=30.0 if kind == "ends" else 0.0,
+                       reduction="mean" if kind == "prefix" else "sum")
+    w.labels.view(-1)[torch.from_numpy(_mask(N, kind, rng))] = fi.IGNORE_INDEX
+    dev = gu.device()
+    dH = torch.full((N, H), float("nan"), dtype=torch.bfloat16, device=dev)
+    g = gu.run_gpu(w, dH=dH)
+    r = gu.run_oracle(w)
+    gu.assert_parity(w, g, r)              # includes: ignored rows of dH exactly 0
+
+
+def test_all_ignored_keeps_accumulated_dW(vchunk):
+    import lm_head_linear_amd as m
+    vchunk(512)
+    w = fi.make_custom(600, 128, 1300, dtype=torch.bfloat16, seed=31, ignore_frac=1.0)
+    dev = gu.device()
+    h, W = w.h.reshape(-1, w.H).to(dev), w.W.to(dev)
+    y = w.labels.reshape(-1).to(dev)
+    dW0 = torch.randn(W.shape, device=dev).to(torch.bfloat16)
+    dW = dW0.clone()
+    dH = torch.full(h.shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    loss, nt, dH, dW = m.flce_forward_backward(h, W, y, dH=dH, dW=dW, accumulate_dW=True)
+    torch.cuda.synchronize()
+    assert loss.item() == 0.0 and nt.item() == 0
+    assert bool((dH == 0).all())
+    assert torch.equal(dW.view(torch.int16), dW0.view(torch.int16))
+
+
+def test_compact_equals_on_two_calls_with_different_masks(vchunk):
+    """The gather's workspace from an earlier call (another mask) does not
+    leak into the next one."""
+    vchunk(512)
+    w = fi.make_custom(900, 136, 2000, dtype=torch.bfloat16, seed=32, ignore_frac=0.6)
+    g1 = gu.run_gpu(w)
+    w2 = fi.make_custom(900, 136, 2000, dtype=torch.bfloat16, seed=32, ignore_frac=0.05)
+    g2 = gu.run_gpu(w2)
+    gu.assert_parity(w2, g2, gu.run_oracle(w2))
+    gu.assert_parity(w, g1, gu.run_oracle(w))
