@@ -33,7 +33,7 @@ if ROOT not in sys.path:
 METRIC = "FLCE fwd+bwd tokens/sec @ H=4096,V=131072 bf16; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0
-GEMM_KINDS = ("lse_fwd_gemm", "grad_logits_gemm", "dW_gemm", "dH_gemm")
+GEMM_KINDS = ("lse_fwd_gemm", "grad_logits_gemm", "dW_gemm", "dH_gemm", "dH_dW_gemm")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_large_vocab.txt")
 # Every source of the library: the committed counters are used only while all
 # of them are unchanged.
@@ -189,7 +189,8 @@ def other_configs(steps: int, warmup: int):
         res = {"N": N, "H": H, "V": V, "softcap": w.softcap, "reduction": w.reduction,
                "num_label_tokens": w.num_label_tokens}
         nhv = float(N) * H * V
-        xfl = sum(step_flops(N, int((w.labels != w.ignore_index).sum()), H, V).values())
+        sf = step_flops(N, int((w.labels != w.ignore_index).sum()), H, V)
+        xfl = sf["lse_fwd_gemm"] + 3 * sf["grad_logits_gemm"]
         for name, fn in runs.items():
             ms, ev_ms = time_steps(fn, steps, warmup)
             res[name] = {"ms_per_step": round(ms, 4), "event_ms_per_step": round(ev_ms, 4),
@@ -343,9 +344,11 @@ def step_flops(N: int, n_kept: int, H: int, V: int) -> dict:
     """Matrix flops each GEMM kind executes per step of flce_forward_backward
     (bf16): the forward over all N tokens; the recompute, dW and dH over the
     n_kept non-ignored tokens only (the backward gathers them: an ignored
-    token's logit gradient is exactly zero, so its products are zeros)."""
-    return {"lse_fwd_gemm": 2.0 * N * H * V, "grad_logits_gemm": 2.0 * n_kept * H * V,
-            "dW_gemm": 2.0 * n_kept * H * V, "dH_gemm": 2.0 * n_kept * H * V}
+    token's logit gradient is exactly zero, so its products are zeros).
+    dH_dW_gemm is a chunk's dH and dW in one grid."""
+    fwd, bwd = 2.0 * N * H * V, 2.0 * n_kept * H * V
+    return {"lse_fwd_gemm": fwd, "grad_logits_gemm": bwd, "dW_gemm": bwd, "dH_gemm": bwd,
+            "dH_dW_gemm": 2.0 * bwd}
 
 
 def kernel_pass(m, step, steps: int, flops: dict):
@@ -478,7 +481,8 @@ def main():
     tflops_6 = 6 * nhv / (wall_ms * 1e-3) / 1e12
     n_kept = int((w.labels != w.ignore_index).sum())
     flops = step_flops(N, n_kept, H, V)
-    tflops_x = sum(flops.values()) / (wall_ms * 1e-3) / 1e12
+    x_step = flops["lse_fwd_gemm"] + 3 * flops["grad_logits_gemm"]
+    tflops_x = x_step / (wall_ms * 1e-3) / 1e12
     kernels, roofline = {}, None
     ksteps = args.steps if args.kernel_steps < 0 else args.kernel_steps
     if ksteps > 0:
@@ -522,7 +526,7 @@ def main():
         "mfma_frac_6nhv": round(tflops_6 / PEAK_BF16_TFLOPS, 4),
         "tflops_8nhv": round(tflops_8, 1),
         "tokens_kept": n_kept,
-        "executed_flops_per_step": sum(flops.values()),
+        "executed_flops_per_step": x_step,
         "tflops_executed": round(tflops_x, 1),
         "mfma_frac_executed": round(tflops_x / PEAK_BF16_TFLOPS, 4),
         "event_ms_per_step": round(ev_ms, 4),

@@ -58,7 +58,7 @@ void prof_after(int kind, hipStream_t s) {
 const char* kKindNames[flce::kNumKinds] = {"label_scan", "lse_fwd_gemm", "lse_merge",
                                            "loss_final", "grad_logits_gemm", "dW_gemm",
                                            "dH_gemm", "fill", "probs_to_grad", "dH_reduce",
-                                           "gather"};
+                                           "gather", "dH_dW_gemm"};
 
 // ---- scratch of flce_forward_noalloc ---------------------------------------
 // One copy on every GPU the library runs on, held until the process ends. In

@@ -22,7 +22,8 @@ enum Kind : int {
   kProbsToGrad = 8,
   kDhReduce = 9,
   kGather = 10,
-  kNumKinds = 11,
+  kGemmDWDH = 11,     // dH's tiles and then dW's, in one grid
+  kNumKinds = 12,
 };
 
 // Everything one call needs on the device side.

@@ -138,7 +138,7 @@ inline Launch nr_launch(const Plan& p, int64_t c, int which) {
                 Geom{32, nt, p.V, nr_block(p)}, Geom{p.H, p.H, p.V}};
 }
 
-inline int64_t num_tiles(int64_t M, int64_t Nn) {
+FLCE_HD int64_t num_tiles(int64_t M, int64_t Nn) {
   return ((M + kBM - 1) / kBM) * ((Nn + kBM - 1) / kBM);
 }
 

@@ -505,31 +505,40 @@ __device__ __forceinline__ void k_loop(Acc& acc, const Operand& A, const Operand
 }
 
 // Which dimension of a launch is cut on the device to the count at `dyn`
-// (the non-ignored tokens of a compact plan): none, M, N or K. The raster
-// uses the launch's sizes (an upper bound), so workgroups whose tile starts
-// past the count leave at once, before any load.
+// (the non-ignored tokens of a compact plan): none, M, N or K. The grid is
+// sized for the launch's sizes (an upper bound); a cut M or N makes the tile
+// raster run over the live tiles, and the workgroups past them leave at once,
+// before any load.
 enum Dyn : int { kDynNone = 0, kDynM = 1, kDynN = 2, kDynK = 3 };
 
+// LDS bytes of a GEMM's stages (reused by its epilogue: 32 KiB per wave).
+template <int FA, int FB>
+constexpr int stage_bytes() {
+  return gemm::num_stages(FA, FB) * 2 * kBM * gemm::stage_k(FA, FB) * 2;
+}
+
+// One workgroup tile of a GEMM launch: workgroup `bid` of the launch's tile
+// raster (and K segment `seg` of a split launch), with the LDS at smem: the
+// stages, then the epilogue's per-token inputs.
 template <int FA, int FB, class Epi, bool BA, int SEGS, bool SPLITK, int DYN>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A_, Operand B_, int64_t M,
-                                                      int64_t Nn, int64_t K, int group_m,
-                                                      Epi epi, int64_t a2_off,
-                                                      const int64_t* dyn) {
+__device__ __forceinline__ void gemm_tile(char* smem, int64_t bid, int seg, Operand A,
+                                          Operand B, int64_t M, int64_t Nn, int64_t K,
+                                          int group_m, Epi epi, int64_t a2_off,
+                                          const int64_t* dyn) {
   // BA: operand A is the blocked G (gemm::Geom). Fixing blk at compile time
   // for the dense operands lets the address arithmetic drop the blocked case.
   // SEGS = 2: a second K loop over A shifted by a2_off elements (the lo half
   // of a split G) against the same B, into the same accumulators, so the
   // tile is (A + A2) . B^T with one epilogue.
   // SPLITK: the launch is split along K into segments of a2_off (a multiple
-  // of 64); workgroup row blockIdx.y takes segment blockIdx.y
-  // (gemm::split_segment) and its epilogue writes a partial product.
+  // of 64); workgroup row `seg` takes segment `seg` (gemm::split_segment) and
+  // its epilogue writes a partial product.
   static_assert(SEGS == 1 || SEGS == 2, "one or two K segments");
   static_assert(!(SPLITK && SEGS == 2), "a split launch has one K segment per workgroup row");
-  Operand A = A_, B = B_;
   if constexpr (!BA) A.g.blk = 0;
   B.g.blk = 0;
   if constexpr (SPLITK) {
-    const int64_t k0 = int64_t(blockIdx.y) * a2_off;
+    const int64_t k0 = int64_t(seg) * a2_off;
     K = (K - k0) < a2_off ? (K - k0) : a2_off;
     A.ptr += gemm::k_origin(FA, A.g, k0);
     B.ptr += gemm::k_origin(FB, B.g, k0);
@@ -539,32 +548,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A_, Operand B_, in
   constexpr int SK = gemm::stage_k(FA, FB);
   constexpr int kStages = gemm::num_stages(FA, FB);
   constexpr int L = gemm::loads_per_operand(SK);
-  constexpr int kTileBytes = kBM * SK * 2;          // one operand, one stage
-  constexpr int kSmemBytes = kStages * 2 * kTileBytes;   // 128 or 160 KiB
+  constexpr int kSmemBytes = stage_bytes<FA, FB>();      // 128 or 160 KiB
   static_assert(kSmemBytes >= 4 * kWaveScratch, "epilogue staging");
   static_assert(kBK == 32 && (SK == 32 || SK == 64), "MFMA steps of 32 k");
   static_assert(2 * L == (SK == 64 ? 16 : 8), "waitcnt immediates");
   static_assert(SK == 64 ? kStages == 2 : (kStages == 4 || kStages == 5), "pipeline depth");
-  // the stages; reused by the epilogues (32 KiB per wave)
-  // plus the epilogue's per-token inputs (stage_tokens), past the stages
-  __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes + Epi::kTokBytes];
-  int64_t m0, n0;
-  gemm::tile_coords(blockIdx.x, M, Nn, group_m, m0, n0);
-  if constexpr (DYN != kDynNone) {
+  if constexpr (DYN == kDynM || DYN == kDynN) {
+    // The raster runs over the live tiles: the workgroups past them leave at
+    // once, and the live ones are spread over all XCDs (a raster over the
+    // launch's upper bound would leave the XCDs that own the dead tiles idle).
     const int64_t d = *dyn;
     if constexpr (DYN == kDynM) {
-      if (m0 >= d) return;
       M = d < M ? d : M;
       epi.N = M;                                   // the epilogue's token rows
-    } else if constexpr (DYN == kDynN) {
-      if (n0 >= d) return;
+    } else {
       Nn = d < Nn ? d : Nn;
       epi.N = Nn;                                  // the epilogue's token columns
-    } else {
-      K = d < K ? d : K;                           // past the count: zero-filled
-      A.g.K = K;
-      B.g.K = K;
     }
+    if (bid >= gemm::num_tiles(M, Nn)) return;
+  }
+  int64_t m0, n0;
+  gemm::tile_coords(bid, M, Nn, group_m, m0, n0);
+  if constexpr (DYN == kDynK) {
+    const int64_t d = *dyn;
+    K = d < K ? d : K;                             // past the count: zero-filled
+    A.g.K = K;
+    B.g.K = K;
   }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -585,6 +594,44 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A_, Operand B_, in
     k_loop<FA, FB>(acc, Operand{A.ptr + a2_off, A.g}, B, K, m0, n0, smem, tid, lane, wave, wm, wn);
   __syncthreads();
   epi(acc, m0, n0, wm, wn, lane, smem, smem + kSmemBytes);
+}
+
+// A GEMM launch: one workgroup per tile (and per K segment of a split launch).
+// The stages are one __shared__ array: with a second LDS object the compiler
+// can no longer tell the direct-to-LDS writes of one stage from the reads of
+// another and serialises the pipeline.
+template <int FA, int FB, class Epi, bool BA, int SEGS, bool SPLITK, int DYN>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A, Operand B, int64_t M,
+                                                      int64_t Nn, int64_t K, int group_m,
+                                                      Epi epi, int64_t a2_off,
+                                                      const int64_t* dyn) {
+  __shared__ __attribute__((aligned(1024))) char smem[stage_bytes<FA, FB>() + Epi::kTokBytes];
+  gemm_tile<FA, FB, Epi, BA, SEGS, SPLITK, DYN>(smem, blockIdx.x, blockIdx.y, A, B, M, Nn, K,
+                                                group_m, epi, a2_off, dyn);
+}
+
+// Two independent GEMMs of one backward chunk in one grid: the n1 workgroups
+// of the first (padded to a multiple of 8, so the XCD raster of the second
+// stays aligned) and then those of the second. The dH GEMM goes first: with
+// the kept tokens only, its tiles may fill its last round of workgroups only
+// in part, and the shorter dW tiles behind it fill the rest instead of the
+// next launch starting on an idle chip. One LDS array serves both.
+template <int FA1, int FB1, class Epi1, int DYN1, int FA2, int FB2, class Epi2, int DYN2>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_pair(
+    int64_t n1p, Operand A1, Operand B1, int64_t M1, int64_t N1, int64_t K1, Epi1 e1,
+    Operand A2, Operand B2, int64_t M2, int64_t N2, int64_t K2, Epi2 e2, const int64_t* dyn) {
+  constexpr int kB1 = stage_bytes<FA1, FB1>() + Epi1::kTokBytes;
+  constexpr int kB2 = stage_bytes<FA2, FB2>() + Epi2::kTokBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[kB1 > kB2 ? kB1 : kB2];
+  const int64_t b = blockIdx.x;
+  if (b < n1p) {
+    if (b < gemm::num_tiles(M1, N1))
+      gemm_tile<FA1, FB1, Epi1, true, 1, false, DYN1>(smem, b, 0, A1, B1, M1, N1, K1,
+                                                      gemm::kGroupM, e1, 0, dyn);
+  } else {
+    gemm_tile<FA2, FB2, Epi2, true, 1, false, DYN2>(smem, b - n1p, 0, A2, B2, M2, N2, K2,
+                                                    gemm::kGroupM, e2, 0, dyn);
+  }
 }
 
 // tanh(x) = 1 - 2 / (exp(2x) + 1), from the hardware exp2 and reciprocal.
@@ -1486,6 +1533,30 @@ hipError_t run_gemm(const gemm::Launch& l, const Args& a, const Epi& e, int kind
   return hipGetLastError();
 }
 
+// Two GEMMs whose A operand is the blocked G in one grid (k_gemm_pair): the
+// first launch's tiles, padded to a multiple of 8 workgroups, then the
+// second's.
+template <int FA1, int FB1, int DYN1, int FA2, int FB2, int DYN2, class Epi1, class Epi2>
+hipError_t run_gemm_pair(const gemm::Launch& l1, const Epi1& e1, const gemm::Launch& l2,
+                         const Epi2& e2, const Args& a, int kind, const Launcher& L,
+                         const int64_t* dyn) {
+  if (!launch_ok(l1) || !launch_ok(l2)) return hipErrorInvalidValue;
+  if (l1.a.blk == 0 || l1.b.blk != 0 || l2.a.blk == 0 || l2.b.blk != 0)
+    return hipErrorInvalidValue;
+  if (((DYN1 != kDynNone) || (DYN2 != kDynNone)) != (dyn != nullptr)) return hipErrorInvalidValue;
+  const int64_t n1p = (gemm::num_tiles(l1.M, l1.Nn) + 7) / 8 * 8;
+  const int64_t total = n1p + gemm::num_tiles(l2.M, l2.Nn);
+  if (total > kMaxTiles) return hipErrorInvalidValue;
+  const Operand A1{buf_ptr(a, l1.buf_a) + l1.off_a, l1.a}, B1{buf_ptr(a, l1.buf_b) + l1.off_b, l1.b};
+  const Operand A2{buf_ptr(a, l2.buf_a) + l2.off_a, l2.a}, B2{buf_ptr(a, l2.buf_b) + l2.off_b, l2.b};
+  L.pre(kind);
+  hipLaunchKernelGGL((k_gemm_pair<FA1, FB1, Epi1, DYN1, FA2, FB2, Epi2, DYN2>),
+                     dim3(unsigned(total)), dim3(kThreads), 0, L.stream, n1p, A1, B1, l1.M, l1.Nn,
+                     l1.K, e1, A2, B2, l2.M, l2.Nn, l2.K, e2, dyn);
+  L.post(kind);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 namespace {
@@ -1555,69 +1626,65 @@ hipError_t bf16_backward_chunk_f32grad(const Plan& p, const Args& a, int64_t chu
 
 hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, const Launcher& L) {
   if (p.g_parts == 2) return bf16_backward_chunk_f32grad(p, a, chunk, L);
+  // bf16 gradients: the plan is compact, the backward runs over the
+  // non-ignored tokens gathered in order (their labels, lse, target logits
+  // and rows), with their count n_valid read on the device
+  if (!p.compact) return hipErrorInvalidValue;
   const int64_t v0 = chunk * p.vchunk;
   const int64_t vcur = gemm::chunk_rows(p, chunk);
   uint16_t* g = static_cast<uint16_t*>(a.g);
-  // A compact plan runs over the non-ignored tokens gathered in order: their
-  // labels, lse, target logits and rows, with the token count on the device.
-  const bool cp = p.compact;
-  const int64_t* nv = cp ? &a.sc->n_valid : nullptr;
-  const int64_t* lab = cp ? a.yc : a.labels;
-  const float* lse = cp ? a.lsec : a.lse;
-  const float* zt = cp ? a.ztc : a.zt;
-  // 1) recompute the logits of the chunk and form G[N][vchunk]
-  const gemm::Launch lg = gemm::backward_launch(p, chunk, 0);
+  const int64_t* nv = &a.sc->n_valid;
   constexpr int NF = gemm::kFormN, TF = gemm::kFormT;
+  // 1) recompute the logits of the chunk and form G[n_valid][vchunk]
+  const gemm::Launch lg = gemm::backward_launch(p, chunk, 0);
   hipError_t err;
   if (a.softcap > 0.f) {
-    EpiGrad<true, false> eg{lab, lse, zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
-                            gemm::g_block(p), a.softcap, 1.f / a.softcap, g, 0};
-    err = cp ? run_gemm<NF, NF, false, 1, false, kDynN>(lg, a, eg, kGradLogits, L, 0, 1, nv)
-             : run_gemm<NF, NF>(lg, a, eg, kGradLogits, L);
+    const EpiGrad<true, false> eg{a.yc, a.lsec, a.ztc, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
+                                  gemm::g_block(p), a.softcap, 1.f / a.softcap, g, 0};
+    err = run_gemm<NF, NF, false, 1, false, kDynN>(lg, a, eg, kGradLogits, L, 0, 1, nv);
   } else {
-    EpiGrad<false, false> eg{lab, lse, zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
-                             gemm::g_block(p), 0.f, 0.f, g, 0};
-    err = cp ? run_gemm<NF, NF, false, 1, false, kDynN>(lg, a, eg, kGradLogits, L, 0, 1, nv)
-             : run_gemm<NF, NF>(lg, a, eg, kGradLogits, L);
+    const EpiGrad<false, false> eg{a.yc, a.lsec, a.ztc, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
+                                   gemm::g_block(p), 0.f, 0.f, g, 0};
+    err = run_gemm<NF, NF, false, 1, false, kDynN>(lg, a, eg, kGradLogits, L, 0, 1, nv);
   }
   if (err != hipSuccess) return err;
-  // 2) dW[v0:v0+vcur] = G^T . h  (K = the tokens)
+  // 2) dW[v0:v0+vcur] = G^T . h (K = the kept tokens) and 3) dH (+)= G . W[chunk]
+  // (rows of the kept tokens, chunks in order, scattered to their positions
+  // when stored as bf16)
   uint16_t* dW = static_cast<uint16_t*>(a.dW);
-  const gemm::Launch lw = gemm::backward_launch(p, chunk, 1);
-  if (a.accumulate_dW) {
-    const EpiDW<true> ew{dW, p.H, v0, vcur};
-    err = cp ? run_gemm<TF, TF, true, 1, false, kDynK>(lw, a, ew, kGemmDW, L, 0, 1, nv)
-             : run_gemm<TF, TF, true>(lw, a, ew, kGemmDW, L);
-  } else {
-    const EpiDW<false> ew{dW, p.H, v0, vcur};
-    err = cp ? run_gemm<TF, TF, true, 1, false, kDynK>(lw, a, ew, kGemmDW, L, 0, 1, nv)
-             : run_gemm<TF, TF, true>(lw, a, ew, kGemmDW, L);
-  }
-  if (err != hipSuccess) return err;
-  // 3) dH (+)= G[:, chunk] . W[chunk], chunks in order (compact: the rows of
-  // the kept tokens, scattered to their positions when stored as bf16)
   uint16_t* dH = static_cast<uint16_t*>(a.dH);
-  const int32_t* rmap = cp ? a.idx : nullptr;
+  const gemm::Launch lw = gemm::backward_launch(p, chunk, 1);
   const gemm::Launch lh = gemm::backward_launch(p, chunk, 2);
   const bool first = chunk == 0, last = chunk == p.n_chunks - 1;
   if (p.dh_kseg) {
-    // few output tiles: split K, then add the segments up in a fixed order
+    // few dH output tiles: dW alone, then dH split along K and the segments
+    // added up in a fixed order
+    if (a.accumulate_dW)
+      err = run_gemm<TF, TF, true, 1, false, kDynK>(lw, a, EpiDW<true>{dW, p.H, v0, vcur},
+                                                    kGemmDW, L, 0, 1, nv);
+    else
+      err = run_gemm<TF, TF, true, 1, false, kDynK>(lw, a, EpiDW<false>{dW, p.H, v0, vcur},
+                                                    kGemmDW, L, 0, 1, nv);
+    if (err != hipSuccess) return err;
     const int64_t segs = (lh.K + p.dh_kseg - 1) / p.dh_kseg;
     const EpiDHPart ep{a.dh_part, p.N, p.H, p.N * p.H};
-    err = cp ? run_gemm<NF, TF, true, 1, true, kDynM>(lh, a, ep, kGemmDH, L, p.dh_kseg, segs, nv)
-             : run_gemm<NF, TF, true, 1, true>(lh, a, ep, kGemmDH, L, p.dh_kseg, segs);
+    err = run_gemm<NF, TF, true, 1, true, kDynM>(lh, a, ep, kGemmDH, L, p.dh_kseg, segs, nv);
     if (err != hipSuccess) return err;
     return launch_dh_reduce(a.dh_part, segs, p.N * p.H, first ? nullptr : a.dh_acc,
-                            last ? nullptr : a.dh_acc, last ? dH : nullptr, L, p.H, nv, rmap);
+                            last ? nullptr : a.dh_acc, last ? dH : nullptr, L, p.H, nv, a.idx);
   }
-  auto dh = [&](auto epi) {
-    return cp ? run_gemm<NF, TF, true, 1, false, kDynM>(lh, a, epi, kGemmDH, L, 0, 1, nv)
-              : run_gemm<NF, TF, true>(lh, a, epi, kGemmDH, L);
+  // dH's tiles and then dW's in one grid
+  auto pair = [&](auto edh) {
+    if (a.accumulate_dW)
+      return run_gemm_pair<NF, TF, kDynM, TF, TF, kDynK>(
+          lh, edh, lw, EpiDW<true>{dW, p.H, v0, vcur}, a, kGemmDWDH, L, nv);
+    return run_gemm_pair<NF, TF, kDynM, TF, TF, kDynK>(
+        lh, edh, lw, EpiDW<false>{dW, p.H, v0, vcur}, a, kGemmDWDH, L, nv);
   };
-  if (first && last) return dh(EpiDH<true, true>{dH, a.dh_acc, p.N, p.H, rmap});
-  if (first) return dh(EpiDH<true, false>{dH, a.dh_acc, p.N, p.H, rmap});
-  if (last) return dh(EpiDH<false, true>{dH, a.dh_acc, p.N, p.H, rmap});
-  return dh(EpiDH<false, false>{dH, a.dh_acc, p.N, p.H, rmap});
+  if (first && last) return pair(EpiDH<true, true>{dH, a.dh_acc, p.N, p.H, a.idx});
+  if (first) return pair(EpiDH<true, false>{dH, a.dh_acc, p.N, p.H, a.idx});
+  if (last) return pair(EpiDH<false, true>{dH, a.dh_acc, p.N, p.H, a.idx});
+  return pair(EpiDH<false, false>{dH, a.dh_acc, p.N, p.H, a.idx});
 }
 
 }  // namespace flce

@@ -22,13 +22,18 @@ pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None, reason="no hipcc"
 
 
 @pytest.fixture(scope="module")
-def loops(tmp_path_factory):
+def asm(tmp_path_factory):
     out = str(tmp_path_factory.mktemp("asm") / "k.s")
     r = subprocess.run(["hipcc", "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang",
                         "-target-feature", "-Xclang", "-packed-fp32-ops", "-S",
                         "--cuda-device-only", SRC, "-o", out], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
-    lines = open(out).read().split("\n")
+    return open(out).read().split("\n")
+
+
+@pytest.fixture(scope="module")
+def loops(asm):
+    lines = asm
     res = {}
     starts = [i for i, l in enumerate(lines) if re.match(r"^_ZN4flce12_GLOBAL__N_16k_gemm\S*:", l)]
     for st in starts:
@@ -55,20 +60,67 @@ def loops(tmp_path_factory):
     return res
 
 
+def _innermost_mfma_loops(body):
+    """(start, end) of every loop the compiler marks whose body holds at least
+    128 MFMAs and contains no smaller such loop."""
+    labels = {m.group(1): i for i, l in enumerate(body)
+              if (m := re.match(r"^(\.LBB\d+_\d+):.*Loop Header", l))}
+    cand = []
+    for i, l in enumerate(body):
+        m = re.search(r"s_cbranch_\w+\s+(\.LBB\d+_\d+)", l)
+        if m and m.group(1) in labels and labels[m.group(1)] < i:
+            a = labels[m.group(1)]
+            if sum("v_mfma" in x for x in body[a:i]) >= 128:
+                cand.append((a, i))
+    return [c for c in cand if not any(o != c and c[0] <= o[0] and o[1] <= c[1] for o in cand)]
+
+
+@pytest.fixture(scope="module")
+def pair_loops(asm):
+    """The K loops of the two-GEMM kernels (dH tiles, then dW tiles, of one
+    backward chunk in one grid), classified by their operand forms."""
+    lines = asm
+    res = {}
+    for st in [i for i, l in enumerate(lines) if re.match(r"^_ZN4flce12_GLOBAL__N_111k_gemm_pair\S*:", l)]:
+        en = next(i for i in range(st, len(lines)) if lines[i].startswith(".Lfunc_end"))
+        body = lines[st:en]
+        segs = []
+        for a, i in _innermost_mfma_loops(body):
+            seg = [l.strip() for l in body[a:i]
+                   if l.startswith("\t") and not l.startswith("\t;") and not l.startswith("\t.")]
+            tr = sum(1 for l in seg if "ds_read_b64_tr_b16" in l)
+            segs.append(((0, 1) if tr == 32 else (1, 1), seg))
+        res[body[0].split(":")[0]] = segs
+    assert len(res) >= 4
+    return res
+
+
+def test_pair_kernels_keep_both_loops(pair_loops):
+    """Each two-GEMM kernel holds the dH loop (G K-contiguous, W transposed)
+    and the dW loop (both transposed), each scheduled like its own kernel."""
+    for sym, segs in pair_loops.items():
+        assert sorted(f for f, _ in segs) == [(0, 1), (1, 1)], sym
+        for (fa, fb), seg in segs:
+            _check_loop(sym, fa, fb, seg)
+
+
 def test_main_loops(loops):
     for sym, (fa, fb, epi, seg) in loops.items():
-        count = lambda p: sum(1 for l in seg if re.match(p, l))
-        assert count(r"v_mfma") == 128, sym
-        assert count(r"scratch_|buffer_store|buffer_load") == 0, (sym, "spill in the K loop")
-        assert count(r"global_load_lds") == 16, sym          # one stage tile (two steps)
-        # fragment reads per two steps: 16 ds_read_b128 per N-form operand,
-        # 32 transpose reads per T-form operand (8 row blocks of 16 per step)
-        reads = (16 if fa == 0 else 32) + (16 if fb == 0 else 32)
-        assert count(r"ds_read") == reads, (sym, count(r"ds_read"))
-        nn = fa == 0 and fb == 0
-        # a barrier per two steps, except with a transposed B alone (per step)
-        assert count(r"s_barrier") == (2 if (fa, fb) == (0, 1) else 1), sym
-        # a full vmcnt wait only directly before a barrier
-        for i, l in enumerate(seg):
-            if re.match(r"s_waitcnt\s+vmcnt\(0\)", l):
-                assert any("s_barrier" in x for x in seg[i + 1:i + 3]), (sym, "vmcnt(0) inside a step")
+        _check_loop(sym, fa, fb, seg)
+
+
+def _check_loop(sym, fa, fb, seg):
+    count = lambda p: sum(1 for l in seg if re.match(p, l))
+    assert count(r"v_mfma") == 128, sym
+    assert count(r"scratch_|buffer_store|buffer_load") == 0, (sym, "spill in the K loop")
+    assert count(r"global_load_lds") == 16, sym          # one stage tile (two steps)
+    # fragment reads per two steps: 16 ds_read_b128 per N-form operand,
+    # 32 transpose reads per T-form operand (8 row blocks of 16 per step)
+    reads = (16 if fa == 0 else 32) + (16 if fb == 0 else 32)
+    assert count(r"ds_read") == reads, (sym, count(r"ds_read"))
+    # a barrier per two steps, except with a transposed B alone (per step)
+    assert count(r"s_barrier") == (2 if (fa, fb) == (0, 1) else 1), sym
+    # a full vmcnt wait only directly before a barrier
+    for i, l in enumerate(seg):
+        if re.match(r"s_waitcnt\s+vmcnt\(0\)", l):
+            assert any("s_barrier" in x for x in seg[i + 1:i + 3]), (sym, "vmcnt(0) inside a step")
