@@ -340,13 +340,14 @@ def other_modes(m, w, h, W, y, dH, dW, loss, nt, steps, timing, nhv):
     return forward_only, float32_grads, no_recompute
 
 
-def step_flops(N: int, n_kept: int, H: int, V: int) -> dict:
+def step_flops(N: int, n_kept: int, H: int, V: int, lse_out: bool = False) -> dict:
     """Matrix flops each GEMM kind executes per step of flce_forward_backward
-    (bf16): the forward over all N tokens; the recompute, dW and dH over the
-    n_kept non-ignored tokens only (the backward gathers them: an ignored
-    token's logit gradient is exactly zero, so its products are zeros).
-    dH_dW_gemm is a chunk's dH and dW in one grid."""
-    fwd, bwd = 2.0 * N * H * V, 2.0 * n_kept * H * V
+    (bf16, bf16 gradients). The call gathers the non-ignored tokens first: an
+    ignored token's loss is 0 and its logit gradient exactly zero, so the
+    forward runs over the n_kept kept tokens (over all N when per-token lse is
+    asked for) and the recompute, dW and dH over the kept ones. dH_dW_gemm is
+    a chunk's dH and dW in one grid."""
+    fwd, bwd = 2.0 * (N if lse_out else n_kept) * H * V, 2.0 * n_kept * H * V
     return {"lse_fwd_gemm": fwd, "grad_logits_gemm": bwd, "dW_gemm": bwd, "dH_gemm": bwd,
             "dH_dW_gemm": 2.0 * bwd}
 

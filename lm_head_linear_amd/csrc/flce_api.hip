@@ -135,7 +135,7 @@ int run_nr(const void* h, const void* W, const int64_t* labels, int64_t N, int64
   a.part = reinterpret_cast<float2*>(ws + p.off_part);
   a.zt = reinterpret_cast<float*>(ws + p.off_zt);
   a.lse = reinterpret_cast<float*>(ws + p.off_lse);
-  a.lsum = reinterpret_cast<double*>(ws + p.off_lsum);
+  a.tok_loss = reinterpret_cast<double*>(ws + p.off_tokloss);
   a.g = ws + p.off_g;
   a.dh_acc = nullptr;
   a.dh_part = p.dh_kseg ? reinterpret_cast<float*>(ws + p.off_dhpart) : nullptr;
@@ -187,24 +187,24 @@ int run(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t 
   a.part = reinterpret_cast<float2*>(ws + p.off_part);
   a.zt = reinterpret_cast<float*>(ws + p.off_zt);
   a.lse = reinterpret_cast<float*>(ws + p.off_lse);
-  a.lsum = reinterpret_cast<double*>(ws + p.off_lsum);
+  a.tok_loss = reinterpret_cast<double*>(ws + p.off_tokloss);
   a.g = backward ? ws + p.off_g : nullptr;
   a.dh_acc = p.need_dh_acc ? reinterpret_cast<float*>(ws + p.off_dhacc) : nullptr;
   a.dh_part = p.dh_kseg ? reinterpret_cast<float*>(ws + p.off_dhpart) : nullptr;
   if (p.compact) {
     a.idx = reinterpret_cast<int32_t*>(ws + p.off_idx);
     a.yc = reinterpret_cast<int64_t*>(ws + p.off_yc);
-    a.lsec = reinterpret_cast<float*>(ws + p.off_lsec);
-    a.ztc = reinterpret_cast<float*>(ws + p.off_ztc);
     a.bcnt = reinterpret_cast<int32_t*>(ws + p.off_bcnt);
     a.hc = ws + p.off_hc;
   }
 
   const bool bf16 = dtype == FLCE_BF16;
   e = flce::launch_label_scan(p, a, L);
+  // a compact plan gathers the tokens first, the kept ones in front; the
+  // forward then skips the ignored ones unless their lse is asked for
+  if (e == hipSuccess && p.compact) e = flce::launch_gather(p, a, lse_out != nullptr, L);
   if (e == hipSuccess) e = bf16 ? flce::bf16_forward(p, a, L) : flce::f32_forward(p, a, L);
   if (e == hipSuccess) e = flce::launch_merge_and_loss(p, a, L);
-  if (e == hipSuccess && backward && p.compact) e = flce::launch_gather(p, a, L);
   for (int64_t c = 0; backward && e == hipSuccess && c < p.n_chunks; ++c)
     e = bf16 ? flce::bf16_backward_chunk(p, a, c, L) : flce::f32_backward_chunk(p, a, c, L);
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;

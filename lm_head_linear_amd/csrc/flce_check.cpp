@@ -55,7 +55,7 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
   if (vc > vmax) vc = vmax;
   q.vchunk = vc;
   q.n_chunks = ceil_div(V, vc);
-  q.n_loss_blocks = ceil_div(N > 0 ? N : 1, 32);   // tokens per lse-merge block
+  q.n_loss_blocks = ceil_div(N > 0 ? N : 1, 32);   // tokens per block of the loss sum
   q.backward = backward;
   q.need_dh_acc = backward && (dtype == FLCE_BF16) && q.g_parts == 1 && q.n_chunks > 1 && N > 0;
   if (backward && dtype == FLCE_BF16 && q.g_parts == 1 && N > 0)
@@ -67,7 +67,8 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
     q.off_part = off;  off = align256(off + size_t(q.n_voc_tiles) * q.ld_part * 2 * sizeof(float));
     q.off_zt = off;    off = align256(off + size_t(q.ld_part) * sizeof(float));
     q.off_lse = off;   off = align256(off + size_t(q.ld_part) * sizeof(float));
-    q.off_lsum = off;  off = align256(off + size_t(q.n_loss_blocks) * sizeof(double));
+    q.off_tokloss = off;
+    off = align256(off + size_t(q.n_loss_blocks) * 32 * sizeof(double));
     if (backward) {
       q.off_g = off;
       off = align256(off + size_t(q.g_parts) * size_t(q.vchunk) * q.ldg * q.elem);
@@ -77,14 +78,12 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
       q.off_dhpart = off;
       off = align256(off + size_t(q.dh_segs) * size_t(N) * H * sizeof(float));
     }
-    // the backward over the non-ignored tokens, gathered in order
+    // the tokens gathered, the non-ignored ones first (see Plan::compact)
     q.compact = backward && dtype == FLCE_BF16 && q.g_parts == 1;
     if (q.compact) {
       q.n_gather_blocks = ceil_div(N, kGatherBlock);
       q.off_idx = off;  off = align256(off + size_t(N) * sizeof(int32_t));
       q.off_yc = off;   off = align256(off + size_t(N) * sizeof(int64_t));
-      q.off_lsec = off; off = align256(off + size_t(N) * sizeof(float));
-      q.off_ztc = off;  off = align256(off + size_t(N) * sizeof(float));
       q.off_bcnt = off; off = align256(off + size_t(q.n_gather_blocks) * sizeof(int32_t));
       q.off_hc = off;   off = align256(off + size_t(N) * H * q.elem);
     }
@@ -123,7 +122,8 @@ bool make_plan_nr(int64_t N, int64_t H, int64_t V, int dtype, int64_t token_chun
     q.off_part = off;  off = align256(off + size_t(q.n_voc_tiles) * q.ld_part * 2 * sizeof(float));
     q.off_zt = off;    off = align256(off + size_t(q.ld_part) * sizeof(float));
     q.off_lse = off;   off = align256(off + size_t(q.ld_part) * sizeof(float));
-    q.off_lsum = off;  off = align256(off + size_t(q.n_loss_blocks) * sizeof(double));
+    q.off_tokloss = off;
+    off = align256(off + size_t(q.n_loss_blocks) * 32 * sizeof(double));
     q.off_g = off;     off = align256(off + size_t(nc) * size_t(q.vp) * q.elem);
     // dH of a token chunk: M = its tokens, K = the whole vocabulary
     q.dh_kseg = dh_split(nc, H, V, &q.dh_segs);

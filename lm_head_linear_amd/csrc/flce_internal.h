@@ -53,18 +53,16 @@ struct Args {
   float2* part;
   float* zt;
   float* lse;
-  double* lsum;
+  double* tok_loss;  // [N] per-token loss by original position (summed in order)
   void* g;        // G^T chunk [vchunk][ldg]
   float* dh_acc;  // [N][H] (bf16 path with several chunks)
   float* dh_part; // [dh_segs][M][H] split-K partial products of dH (or null)
   float* dw_acc;  // [V][H] float32 dW running sum (no-recompute, several chunks)
-  // compact plan: the non-ignored tokens gathered in order (see Plan)
-  int32_t* idx;   // original position of kept token r
+  // compact plan: the tokens gathered, non-ignored ones first (see Plan)
+  int32_t* idx;   // original position of gathered token r
   int64_t* yc;    // its label
-  float* lsec;    // its lse
-  float* ztc;     // its target logit
   int32_t* bcnt;  // kept tokens per gather block
-  void* hc;       // its hidden row, bf16 [N][H] (the first n_valid rows)
+  void* hc;       // its hidden row, bf16 [N][H]
 };
 
 // Launch hook: the C-ABI layer brackets launches with timing events.
@@ -85,10 +83,11 @@ hipError_t launch_merge_and_loss(const Plan& p, const Args& a, const Launcher& L
 hipError_t launch_merge(const Plan& p, const Args& a, int64_t t0, int64_t nt, const Launcher& L);
 hipError_t launch_loss_final(const Plan& p, const Args& a, const Launcher& L);
 hipError_t launch_zero_bytes(void* ptr, size_t bytes, const Launcher& L);
-// Compact plan: gather the non-ignored tokens (positions, labels, lse,
-// target logits, hidden rows) after the forward, and zero the dH rows of the
-// ignored ones.
-hipError_t launch_gather(const Plan& p, const Args& a, const Launcher& L);
+// Compact plan, before the forward: gather the tokens, the non-ignored ones
+// first (positions, labels, the hidden rows of the first `rows` of them: the
+// kept ones, or all N), give ignored tokens a zero loss, and zero the dH rows
+// of the ignored ones.
+hipError_t launch_gather(const Plan& p, const Args& a, bool all_rows, const Launcher& L);
 
 // bf16 MFMA path.
 hipError_t bf16_forward(const Plan& p, const Args& a, const Launcher& L);

@@ -74,7 +74,7 @@ struct Plan {
   int64_t ldg = 0;           // leading dimension of G^T (tokens, multiple of 8)
   int64_t vchunk = 0;        // vocabulary rows per backward chunk
   int64_t n_chunks = 0;
-  int64_t n_loss_blocks = 0; // blocks of the lse-merge kernel (32 tokens each)
+  int64_t n_loss_blocks = 0; // blocks of 32 tokens of the fixed-order loss sum
   bool backward = true;      // plan includes the gradient buffers
   // No-recompute variant: tokens in chunks of `nc`; per chunk the forward
   // stores the probabilities relative to each tile's max, P'[t][v] bf16 with
@@ -85,12 +85,16 @@ struct Plan {
   // No-recompute variant with several token chunks: dW is added up over the
   // chunks in a float32 [V][H] running sum at off_dwacc, rounded to bf16 once.
   bool need_dw_acc = false;
-  // bf16 gradients of the recompute path: the backward runs over the
-  // non-ignored tokens only, gathered in order (ignored tokens have G = 0, so
-  // their recompute, dW and dH products are exact zeros). The workspace then
-  // holds their original positions (int32 [N]), labels (int64 [N]), lse and
-  // target logits (float [N]), hidden rows (bf16 [N][H]) and per-block counts
-  // of the gather (int32 [n_gather_blocks]); the device count is n_valid.
+  // bf16 gradients of the recompute path: the tokens are gathered first,
+  // the non-ignored ones in order and then the ignored ones (a permutation),
+  // and the call runs over the gathered order: the backward over the first
+  // n_valid (the kept tokens; an ignored token's G is zero, so its recompute,
+  // dW and dH products are exact zeros), the forward over them too, or over
+  // all N when per-token lse is asked for. The workspace then holds each
+  // gathered token's original position (int32 [N]), label (int64 [N]) and
+  // hidden row (bf16 [N][H]), and per-block counts of the gather (int32
+  // [n_gather_blocks]); the partials, lse and target logits are indexed in
+  // the gathered order, the per-token losses by original position.
   bool compact = false;
   int64_t n_gather_blocks = 0;
   // Split-K of the dH GEMM (bf16 gradients): segments of dh_kseg vocabulary
@@ -100,9 +104,9 @@ struct Plan {
   size_t elem = 0;           // bytes per element of h/W/G
   size_t grad_elem = 0;      // bytes per element of dH/dW
   // byte offsets into the workspace
-  size_t off_scalars = 0, off_part = 0, off_zt = 0, off_lse = 0, off_lsum = 0,
+  size_t off_scalars = 0, off_part = 0, off_zt = 0, off_lse = 0, off_tokloss = 0,
          off_g = 0, off_dhacc = 0, off_dhpart = 0, off_dwacc = 0, off_idx = 0, off_yc = 0,
-         off_lsec = 0, off_ztc = 0, off_hc = 0, off_bcnt = 0, total = 0;
+         off_hc = 0, off_bcnt = 0, total = 0;
 };
 
 // Builds the plan; returns false for invalid sizes or dtypes. A forward-only

@@ -76,12 +76,13 @@ struct Launch {
 // The forward launch, and the three launches of backward chunk c (0: logit
 // gradient, 1: dW, 2: dH). With float32 gradients for bf16 inputs G is a
 // pair of bf16 chunks, hi then lo, each vchunk x ldg elements; `part` picks
-// the one a dW or dH launch reads. A compact plan's backward reads the
-// gathered rows of the non-ignored tokens instead of h; its token dimension
-// (N of the gradient launch, K of dW, M of dH) is then cut on the device to
-// the non-ignored count, and the sizes here are the upper bound N.
+// the one a dW or dH launch reads. A compact plan reads the gathered rows
+// (the non-ignored tokens first) instead of h; its token dimension (N of the
+// forward and gradient launches, K of dW, M of dH) is then cut on the device
+// to the non-ignored count (the forward's only without per-token lse), and
+// the sizes here are the upper bound N.
 inline Launch forward_launch(const Plan& p) {
-  return Launch{p.V, p.N, p.H, kFormN, kFormN, kBufW, kBufH, 0, 0,
+  return Launch{p.V, p.N, p.H, kFormN, kFormN, kBufW, p.compact ? kBufHc : kBufH, 0, 0,
                 Geom{p.H, p.V, p.H}, Geom{p.H, p.N, p.H}};
 }
 

@@ -1566,14 +1566,21 @@ hipError_t bf16_forward_out(const Plan& p, const Args& a, const Launcher& L) {
   const int esz = OUT == kLogitsF32 ? 4 : 2;
   const int vec = OUT != kNoLogits && reinterpret_cast<uintptr_t>(a.logits) % 16 == 0 &&
                   (a.ld_logits * esz) % 16 == 0;
+  // a compact plan: the gathered tokens and their labels; only the kept ones
+  // (a device count) when no per-token lse is asked for
+  const int64_t* lab = p.compact ? a.yc : a.labels;
+  const int64_t* nv = (p.compact && !a.lse_out) ? &a.sc->n_valid : nullptr;
+  constexpr int NF = gemm::kFormN;
   if (a.softcap > 0.f) {
-    EpiLse<true, OUT> e{a.labels, p.N, p.V, a.ignore_index, a.softcap, 1.f / a.softcap, a.part,
+    EpiLse<true, OUT> e{lab, p.N, p.V, a.ignore_index, a.softcap, 1.f / a.softcap, a.part,
                         p.ld_part, a.zt, a.logits, a.ld_logits, vec};
-    return run_gemm<gemm::kFormN, gemm::kFormN>(l, a, e, kLseFwd, L);
+    return nv ? run_gemm<NF, NF, false, 1, false, kDynN>(l, a, e, kLseFwd, L, 0, 1, nv)
+              : run_gemm<NF, NF>(l, a, e, kLseFwd, L);
   }
-  EpiLse<false, OUT> e{a.labels, p.N, p.V, a.ignore_index, 0.f, 0.f, a.part, p.ld_part, a.zt,
+  EpiLse<false, OUT> e{lab, p.N, p.V, a.ignore_index, 0.f, 0.f, a.part, p.ld_part, a.zt,
                        a.logits, a.ld_logits, vec};
-  return run_gemm<gemm::kFormN, gemm::kFormN>(l, a, e, kLseFwd, L);
+  return nv ? run_gemm<NF, NF, false, 1, false, kDynN>(l, a, e, kLseFwd, L, 0, 1, nv)
+            : run_gemm<NF, NF>(l, a, e, kLseFwd, L);
 }
 }  // namespace
 
@@ -1639,11 +1646,11 @@ hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, cons
   const gemm::Launch lg = gemm::backward_launch(p, chunk, 0);
   hipError_t err;
   if (a.softcap > 0.f) {
-    const EpiGrad<true, false> eg{a.yc, a.lsec, a.ztc, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
+    const EpiGrad<true, false> eg{a.yc, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
                                   gemm::g_block(p), a.softcap, 1.f / a.softcap, g, 0};
     err = run_gemm<NF, NF, false, 1, false, kDynN>(lg, a, eg, kGradLogits, L, 0, 1, nv);
   } else {
-    const EpiGrad<false, false> eg{a.yc, a.lsec, a.ztc, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
+    const EpiGrad<false, false> eg{a.yc, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
                                    gemm::g_block(p), 0.f, 0.f, g, 0};
     err = run_gemm<NF, NF, false, 1, false, kDynN>(lg, a, eg, kGradLogits, L, 0, 1, nv);
   }

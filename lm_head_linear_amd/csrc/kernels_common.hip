@@ -54,20 +54,27 @@ __global__ __launch_bounds__(1024) void k_label_scan(
 }
 
 // Per token: merge the per-vocab-tile (max m_j, sum_j of exp(x - m_j))
-// partials into lse = M + log(sum_j s_j exp(m_j - M)), form the token loss
-// lse - z'_target on non-ignored tokens (NaN for an out-of-range label), and
-// sum the block's tokens in float64 in a fixed order. A block handles
-// kMergeTokens tokens; its 8 thread groups each merge every 8th tile of them
-// (online max/rescale), then the groups are combined in a fixed order.
+// partials into lse = M + log(sum_j s_j exp(m_j - M)) and form the token
+// loss lse - z'_target on non-ignored tokens (NaN for an out-of-range label,
+// 0 on ignored ones), written in float64 at the token's original position
+// (perm[t], or t without a gather). A block handles kMergeTokens tokens; its
+// 8 thread groups each merge every 8th tile of them (online max/rescale),
+// then the groups are combined in a fixed order. With `count` (a device
+// count) only the first *count tokens are merged.
 constexpr int kMergeTokens = 32;
 
 __global__ __launch_bounds__(256) void k_lse_merge(
     const float2* __restrict__ part, int64_t n_tiles, int64_t ld_part,
     const float* __restrict__ zt, const int64_t* __restrict__ labels, int64_t N,
-    int64_t V, int64_t ignore_index, float* __restrict__ lse, float* __restrict__ lse_out,
-    double* __restrict__ lsum) {
+    const int64_t* __restrict__ count, int64_t V, int64_t ignore_index,
+    float* __restrict__ lse, float* __restrict__ lse_out, double* __restrict__ tok_loss,
+    const int32_t* __restrict__ perm) {
   __shared__ float2 grp[8][kMergeTokens];
-  __shared__ double red[kMergeTokens];
+  if (count) {
+    const int64_t c = *count;
+    N = c < N ? c : N;
+  }
+  if (int64_t(blockIdx.x) * kMergeTokens >= N) return;
   const int tk = threadIdx.x % kMergeTokens, g = threadIdx.x / kMergeTokens;
   const int64_t t = int64_t(blockIdx.x) * kMergeTokens + tk;
   float M = -INFINITY, S = 0.f;
@@ -84,37 +91,41 @@ __global__ __launch_bounds__(256) void k_lse_merge(
   }
   grp[g][tk] = make_float2(M, S);
   __syncthreads();
-  if (g == 0) {
+  if (g == 0 && t < N) {
+    float Mx = -INFINITY;
+    for (int i = 0; i < 8; ++i) Mx = fmaxf(Mx, grp[i][tk].x);
+    float St = 0.f;
+    for (int i = 0; i < 8; ++i)
+      if (grp[i][tk].x != -INFINITY) St += grp[i][tk].y * exp2f((grp[i][tk].x - Mx) * kLog2e);
+    const float l = Mx + log2f(St) * kLn2;
+    const int64_t orig = perm ? int64_t(perm[t]) : t;
+    lse[t] = l;
+    if (lse_out) lse_out[orig] = l;
+    const int64_t y = labels[t];
     double ell = 0.0;
-    if (t < N) {
-      float Mx = -INFINITY;
-      for (int i = 0; i < 8; ++i) Mx = fmaxf(Mx, grp[i][tk].x);
-      float St = 0.f;
-      for (int i = 0; i < 8; ++i)
-        if (grp[i][tk].x != -INFINITY) St += grp[i][tk].y * exp2f((grp[i][tk].x - Mx) * kLog2e);
-      const float l = Mx + log2f(St) * kLn2;
-      lse[t] = l;
-      if (lse_out) lse_out[t] = l;
-      const int64_t y = labels[t];
-      if (y != ignore_index) ell = (y < 0 || y >= V) ? double(NAN) : double(l) - double(zt[t]);
-    }
-    red[tk] = ell;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double s = 0.0;
-    for (int i = 0; i < kMergeTokens; ++i) s += red[i];
-    lsum[blockIdx.x] = s;
+    if (y != ignore_index) ell = (y < 0 || y >= V) ? double(NAN) : double(l) - double(zt[t]);
+    tok_loss[orig] = ell;
   }
 }
 
-// loss = c * sum(lsum) in float64, fixed order; NaN when a label was invalid.
-__global__ __launch_bounds__(256) void k_loss_final(const double* __restrict__ lsum, int64_t nb,
-                                                    const Scalars* __restrict__ sc,
+// loss = c * (sum of the per-token losses) in float64, in a fixed order that
+// depends only on the original token positions: blocks of 32 tokens summed
+// in order, the block sums strided over 256 threads, then a tree. NaN when a
+// label was invalid.
+__global__ __launch_bounds__(256) void k_loss_final(const double* __restrict__ tok_loss,
+                                                    int64_t N, const Scalars* __restrict__ sc,
                                                     float* __restrict__ loss) {
   __shared__ double red[256];
+  const int64_t nb = (N + kMergeTokens - 1) / kMergeTokens;
   double s = 0.0;
-  for (int64_t i = threadIdx.x; i < nb; i += 256) s += lsum[i];
+  for (int64_t b = threadIdx.x; b < nb; b += 256) {
+    double sb = 0.0;
+    for (int i = 0; i < kMergeTokens; ++i) {
+      const int64_t t = b * kMergeTokens + i;
+      sb += t < N ? tok_loss[t] : 0.0;
+    }
+    s += sb;
+  }
   red[threadIdx.x] = s;
   __syncthreads();
   for (int k = 128; k > 0; k >>= 1) {
@@ -141,13 +152,14 @@ __global__ __launch_bounds__(256) void k_zero1(unsigned char* __restrict__ p, in
     p[i] = 0;
 }
 
-// ---- the non-ignored tokens, gathered in order, for the backward ----------
+// ---- the tokens gathered, the non-ignored ones first ----------------------
 // Ignored tokens have G = 0: their recomputed logits, dW and dH products are
-// exact zeros, so the backward runs over the kept tokens only. Block b of
-// kGatherBlock tokens first counts its kept tokens; then every block finds
-// the count before it and the rank of each kept token inside it (wave
-// ballots), and writes the token's original position, label, lse and target
-// logit at its rank; the hidden rows follow in a copy kernel.
+// exact zeros, so the call runs over the gathered order, the kept tokens
+// first. Block b of kGatherBlock tokens first counts its kept tokens; then
+// every block finds the count before it and each token's rank (wave
+// ballots): a kept token goes to its rank among the kept ones, an ignored
+// one to n_valid plus its rank among the ignored ones. The hidden rows follow
+// in a copy kernel.
 constexpr int kGatherThreads = int(kGatherBlock);
 
 __global__ __launch_bounds__(kGatherThreads) void k_gather_count(
@@ -169,9 +181,8 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_count(
 
 __global__ __launch_bounds__(kGatherThreads) void k_gather_tokens(
     const int64_t* __restrict__ labels, int64_t N, int64_t ignore_index,
-    const float* __restrict__ lse, const float* __restrict__ zt,
-    const int32_t* __restrict__ bcnt, int32_t* __restrict__ idx, int64_t* __restrict__ yc,
-    float* __restrict__ lsec, float* __restrict__ ztc) {
+    const int32_t* __restrict__ bcnt, const Scalars* __restrict__ sc,
+    int32_t* __restrict__ idx, int64_t* __restrict__ yc, double* __restrict__ tok_loss) {
   __shared__ int64_t part[kGatherThreads / 64];
   __shared__ int32_t wsum[kGatherThreads / 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -186,21 +197,22 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_tokens(
   const unsigned long long m = __ballot(keep);
   if (lane == 0) wsum[w] = __popcll(m);
   __syncthreads();
-  if (!keep) return;
-  int64_t pos = __popcll(m & ((1ull << lane) - 1));
-  for (int i = 0; i < kGatherThreads / 64; ++i) pos += part[i] + (i < w ? wsum[i] : 0);
+  if (t >= N) return;
+  int64_t before = __popcll(m & ((1ull << lane) - 1));       // kept tokens before t
+  for (int i = 0; i < kGatherThreads / 64; ++i) before += part[i] + (i < w ? wsum[i] : 0);
+  const int64_t pos = keep ? before : sc->n_valid + (t - before);
   idx[pos] = int32_t(t);
   yc[pos] = y;
-  lsec[pos] = lse[t];
-  ztc[pos] = zt[t];
+  if (!keep) tok_loss[t] = 0.0;           // not merged when the forward skips it
 }
 
-// hc[r] = h[idx[r]] for the n_valid kept rows, in 16-byte pieces (h8 per row).
+// hc[r] = h[idx[r]] for the first `rows` gathered rows (*rows_dev, or all
+// N), in 16-byte pieces (h8 per row).
 __global__ __launch_bounds__(256) void k_gather_rows(const uint4* __restrict__ h, int64_t h8,
                                                      const int32_t* __restrict__ idx,
-                                                     const Scalars* __restrict__ sc,
-                                                     uint4* __restrict__ hc) {
-  const int64_t total = sc->n_valid * h8;
+                                                     const int64_t* __restrict__ rows_dev,
+                                                     int64_t rows, uint4* __restrict__ hc) {
+  const int64_t total = (rows_dev ? *rows_dev : rows) * h8;
   for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total;
        i += int64_t(gridDim.x) * 256) {
     const int64_t r = i / h8;
@@ -240,23 +252,36 @@ hipError_t launch_label_scan(const Plan& p, const Args& a, const Launcher& L) {
 hipError_t launch_merge(const Plan& p, const Args& a, int64_t t0, int64_t nt, const Launcher& L) {
   L.pre(kLseMerge);
   hipLaunchKernelGGL(k_lse_merge, dim3(unsigned((nt + kMergeTokens - 1) / kMergeTokens)), dim3(256),
-                     0, L.stream, a.part, p.n_voc_tiles, p.ld_part, a.zt, a.labels + t0, nt, p.V,
-                     a.ignore_index, a.lse, a.lse_out ? a.lse_out + t0 : nullptr,
-                     a.lsum + t0 / kMergeTokens);
+                     0, L.stream, a.part, p.n_voc_tiles, p.ld_part, a.zt, a.labels + t0, nt,
+                     nullptr, p.V, a.ignore_index, a.lse, a.lse_out ? a.lse_out + t0 : nullptr,
+                     a.tok_loss + t0, nullptr);
   L.post(kLseMerge);
   return hipGetLastError();
 }
 
 hipError_t launch_merge_and_loss(const Plan& p, const Args& a, const Launcher& L) {
-  hipError_t e = launch_merge(p, a, 0, p.N, L);
+  hipError_t e;
+  if (p.compact) {
+    // over the gathered order: the kept tokens (or all when the per-token
+    // lse is asked for), losses and lse scattered to the original positions
+    L.pre(kLseMerge);
+    hipLaunchKernelGGL(k_lse_merge, dim3(unsigned((p.N + kMergeTokens - 1) / kMergeTokens)),
+                       dim3(256), 0, L.stream, a.part, p.n_voc_tiles, p.ld_part, a.zt, a.yc, p.N,
+                       a.lse_out ? nullptr : &a.sc->n_valid, p.V, a.ignore_index, a.lse,
+                       a.lse_out, a.tok_loss, a.idx);
+    L.post(kLseMerge);
+    e = hipGetLastError();
+  } else {
+    e = launch_merge(p, a, 0, p.N, L);
+  }
   if (e != hipSuccess) return e;
   return launch_loss_final(p, a, L);
 }
 
 hipError_t launch_loss_final(const Plan& p, const Args& a, const Launcher& L) {
   L.pre(kLossFinal);
-  hipLaunchKernelGGL(k_loss_final, dim3(1), dim3(256), 0, L.stream, a.lsum, p.n_loss_blocks,
-                     a.sc, a.loss);
+  hipLaunchKernelGGL(k_loss_final, dim3(1), dim3(256), 0, L.stream, a.tok_loss, p.N, a.sc,
+                     a.loss);
   L.post(kLossFinal);
   return hipGetLastError();
 }
@@ -280,20 +305,22 @@ hipError_t launch_zero_bytes(void* ptr, size_t bytes, const Launcher& L) {
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const Plan& p, const Args& a, const Launcher& L) {
+hipError_t launch_gather(const Plan& p, const Args& a, bool all_rows, const Launcher& L) {
   const unsigned nb = unsigned(p.n_gather_blocks);
   L.pre(kGather);
   hipLaunchKernelGGL(k_gather_count, dim3(nb), dim3(kGatherThreads), 0, L.stream, a.labels, p.N,
                      a.ignore_index, a.bcnt);
   hipLaunchKernelGGL(k_gather_tokens, dim3(nb), dim3(kGatherThreads), 0, L.stream, a.labels, p.N,
-                     a.ignore_index, a.lse, a.zt, a.bcnt, a.idx, a.yc, a.lsec, a.ztc);
+                     a.ignore_index, a.bcnt, a.sc, a.idx, a.yc, a.tok_loss);
   const int64_t h8 = p.H / 8;
   int64_t blocks = (p.N * h8 + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(k_gather_rows, dim3(unsigned(blocks)), dim3(256), 0, L.stream,
-                     static_cast<const uint4*>(a.h), h8, a.idx, a.sc, static_cast<uint4*>(a.hc));
-  hipLaunchKernelGGL(k_zero_ignored_rows, dim3(unsigned(blocks)), dim3(256), 0, L.stream,
-                     a.labels, p.N, a.ignore_index, h8, static_cast<uint4*>(a.dH));
+                     static_cast<const uint4*>(a.h), h8, a.idx,
+                     all_rows ? nullptr : &a.sc->n_valid, p.N, static_cast<uint4*>(a.hc));
+  if (a.dH)
+    hipLaunchKernelGGL(k_zero_ignored_rows, dim3(unsigned(blocks)), dim3(256), 0, L.stream,
+                       a.labels, p.N, a.ignore_index, h8, static_cast<uint4*>(a.dH));
   L.post(kGather);
   return hipGetLastError();
 }

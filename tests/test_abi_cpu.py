@@ -408,7 +408,7 @@ def test_nr_plan(lib):
         split = segs * nc * H * 4 if segs > 1 else 0
         acc = V * H * 4 if nc < N else 0
         lo = nc * vp * 2 + split + acc
-        assert lo <= ws <= lo + (vp // 256) * nc * 8 + 4 * nc * 4 + N + 4096
+        assert lo <= ws <= lo + (vp // 256) * nc * 8 + 4 * nc * 4 + 8 * N + 4096
     assert lib.flce_workspace_size_nr(64, 64, 128, 0, 0) == 0        # float32: not offered
     assert lib.flce_workspace_size_nr(-1, 64, 128, 1, 0) == 0
 

@@ -99,3 +99,28 @@ def test_compact_equals_on_two_calls_with_different_masks(vchunk):
     g2 = gu.run_gpu(w2)
     gu.assert_parity(w2, g2, gu.run_oracle(w2))
     gu.assert_parity(w, g1, gu.run_oracle(w))
+
+
+@pytest.mark.parametrize("cap", [0.0, 30.0])
+def test_forward_skips_ignored_tokens_without_changing_a_bit(cap, vchunk):
+    """Without per-token lse the forward runs over the kept tokens only; with
+    it, over all of them. Loss, dH and dW are bit-identical either way, and
+    the loss equals the forward-only entry's (per-token losses are summed by
+    original position), with the oracle agreeing."""
+    import lm_head_linear_amd as m
+    vchunk(512)
+    w = fi.make_custom(1500, 264, 2100, dtype=torch.bfloat16, seed=33, ignore_frac=0.0,
+                       softcap=cap, reduction="mean")
+    w.labels[:, :300] = fi.IGNORE_INDEX                   # masked prefix
+    w.labels[0, 700:777] = fi.IGNORE_INDEX
+    a = gu.run_gpu(w, lse=False)
+    b = gu.run_gpu(w, lse=True)
+    f = gu.run_gpu_forward(w)
+    assert a["loss_t"].view(torch.int32).item() == b["loss_t"].view(torch.int32).item()
+    assert a["loss_t"].view(torch.int32).item() == f["loss_t"].view(torch.int32).item()
+    assert torch.equal(b["lse"].view(torch.int32), f["lse"].view(torch.int32))
+    for k in ("dH", "dW"):
+        assert torch.equal(a[k].view(torch.int16), b[k].view(torch.int16)), k
+    r = gu.run_oracle(w)
+    gu.assert_parity(w, b, r)
+    gu.assert_parity(w, a, r, check_lse=False)
