@@ -83,15 +83,17 @@ def assert_loss(gpu_loss: float, ref: float, rtol: float = LOSS_RTOL):
         assert err <= rtol * abs(ref), f"loss {gpu_loss} vs ref {ref}: rel err {err / abs(ref):.3e}"
 
 
-def assert_grad(name: str, gpu: torch.Tensor, ref: np.ndarray, tol: float):
+def assert_grad(name: str, gpu: torch.Tensor, ref: np.ndarray, tol: float) -> float:
+    """Every element within tol * max|ref|; returns max err / max|ref|."""
     g = to_np64(gpu)
     assert g.shape == ref.shape, (name, g.shape, ref.shape)
     scale = float(np.abs(ref).max()) if ref.size else 0.0
     err = float(np.abs(g - ref).max()) if ref.size else 0.0
     if scale == 0.0:
         assert err == 0.0, f"{name}: reference is zero, max |gpu| = {err}"
-    else:
-        assert err <= tol * scale, f"{name}: max err {err:.3e} > {tol} * {scale:.3e} (ratio {err / scale:.3e})"
+        return 0.0
+    assert err <= tol * scale, f"{name}: max err {err:.3e} > {tol} * {scale:.3e} (ratio {err / scale:.3e})"
+    return err / scale
 
 
 def assert_parity(w: fi.Workload, g: dict, r, *, check_lse=True):
@@ -99,8 +101,11 @@ def assert_parity(w: fi.Workload, g: dict, r, *, check_lse=True):
     assert g["status"] == 0
     assert g["num_tokens"] == r.num_tokens
     assert_loss(g["loss"], r.loss64)
-    assert_grad("dH", g["dH"], r.dH, tol)
-    assert_grad("dW", g["dW"], r.dW, tol)
+    eh = assert_grad("dH", g["dH"], r.dH, tol)
+    ew = assert_grad("dW", g["dW"], r.dW, tol)
+    rel = abs(g["loss"] - r.loss64) / abs(r.loss64) if r.loss64 else 0.0
+    print(f"PARITY {w.name} N={r.dH.shape[0]} H={w.H} V={w.V}: loss rel={rel:.2e} "
+          f"dH max err/max ref={eh:.2e} dW max err/max ref={ew:.2e}", flush=True)
     y = w.labels.reshape(-1).numpy()
     ign = y == w.ignore_index
     if ign.any():
