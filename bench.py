@@ -189,8 +189,9 @@ def other_configs(steps: int, warmup: int):
         res = {"N": N, "H": H, "V": V, "softcap": w.softcap, "reduction": w.reduction,
                "num_label_tokens": w.num_label_tokens}
         nhv = float(N) * H * V
-        sf = step_flops(N, int((w.labels != w.ignore_index).sum()), H, V)
-        xfl = sf["lse_fwd_gemm"] + 3 * sf["grad_logits_gemm"]
+        sf = step_flops(N, int((w.labels != w.ignore_index).sum()), H, V,
+                        m.flce_vocab_chunk(N, H, V, W.dtype))
+        xfl = sf["step"]
         for name, fn in runs.items():
             ms, ev_ms = time_steps(fn, steps, warmup)
             res[name] = {"ms_per_step": round(ms, 4), "event_ms_per_step": round(ev_ms, 4),
@@ -340,16 +341,19 @@ def other_modes(m, w, h, W, y, dH, dW, loss, nt, steps, timing, nhv):
     return forward_only, float32_grads, no_recompute
 
 
-def step_flops(N: int, n_kept: int, H: int, V: int, lse_out: bool = False) -> dict:
+def step_flops(N: int, n_kept: int, H: int, V: int, vchunk: int, lse_out: bool = False) -> dict:
     """Matrix flops each GEMM kind executes per step of flce_forward_backward
     (bf16, bf16 gradients). The call gathers the non-ignored tokens first: an
     ignored token's loss is 0 and its logit gradient exactly zero, so the
     forward runs over the n_kept kept tokens (over all N when per-token lse is
-    asked for) and the recompute, dW and dH over the kept ones. dH_dW_gemm is
-    a chunk's dH and dW in one grid."""
+    asked for) and the recompute, dW and dH over the kept ones. The forward
+    keeps the first vocabulary chunk's probabilities, so the recompute covers
+    the other V - vchunk rows. dH_dW_gemm is a chunk's dH and dW in one grid;
+    'step' is the sum over the step."""
     fwd, bwd = 2.0 * (N if lse_out else n_kept) * H * V, 2.0 * n_kept * H * V
-    return {"lse_fwd_gemm": fwd, "grad_logits_gemm": bwd, "dW_gemm": bwd, "dH_gemm": bwd,
-            "dH_dW_gemm": 2.0 * bwd}
+    rec = 2.0 * n_kept * H * max(V - vchunk, 0)
+    return {"lse_fwd_gemm": fwd, "grad_logits_gemm": rec, "dW_gemm": bwd, "dH_gemm": bwd,
+            "dH_dW_gemm": 2.0 * bwd, "step": fwd + rec + 2.0 * bwd}
 
 
 def kernel_pass(m, step, steps: int, flops: dict):
@@ -481,8 +485,8 @@ def main():
     tflops_8 = 8 * nhv / (wall_ms * 1e-3) / 1e12
     tflops_6 = 6 * nhv / (wall_ms * 1e-3) / 1e12
     n_kept = int((w.labels != w.ignore_index).sum())
-    flops = step_flops(N, n_kept, H, V)
-    x_step = flops["lse_fwd_gemm"] + 3 * flops["grad_logits_gemm"]
+    flops = step_flops(N, n_kept, H, V, vchunk)
+    x_step = flops["step"]
     tflops_x = x_step / (wall_ms * 1e-3) / 1e12
     kernels, roofline = {}, None
     ksteps = args.steps if args.kernel_steps < 0 else args.kernel_steps

@@ -167,9 +167,13 @@ inline Launch split_segment(const Launch& l, int64_t kseg, int64_t z) {
 // Workgroups are handed to the 8 XCDs round-robin. Give each XCD a contiguous
 // range of tiles, and order tiles within a range in groups of `group_m`
 // M-tiles so that the workgroups resident on one XCD share operand tiles in
-// that XCD's L2.
+// that XCD's L2. An XCD's range then covers a contiguous run of M-tiles;
+// spread_m (with the M-tile count a multiple of 8) deals the M-tiles to the
+// XCDs in turn instead (XCD x gets x, x + 8, ...), for a launch whose first
+// M-tiles carry more work: every XCD gets its share of them, and the sharing
+// within an XCD is unchanged.
 FLCE_HD void tile_coords(int64_t b, int64_t M, int64_t Nn, int group_m, int64_t& m0,
-                         int64_t& n0) {
+                         int64_t& n0, bool spread_m = false) {
   const int64_t num_m = (M + kBM - 1) / kBM, num_n = (Nn + kBM - 1) / kBM;
   const int64_t total = num_m * num_n;
   const int64_t q = total / 8, rem = total % 8, x = b % 8, local = b / 8;
@@ -179,7 +183,12 @@ FLCE_HD void tile_coords(int64_t b, int64_t M, int64_t Nn, int group_m, int64_t&
   const int64_t first_m = g * group_m;
   const int64_t gs = (num_m - first_m) < group_m ? (num_m - first_m) : group_m;
   const int64_t in = tile - g * per_group;
-  m0 = (first_m + in % gs) * kBM;
+  int64_t mt = first_m + in % gs;
+  if (spread_m && num_m % 8 == 0) {
+    const int64_t per = num_m / 8;
+    mt = (mt % per) * 8 + mt / per;
+  }
+  m0 = mt * kBM;
   n0 = (in / gs) * kBM;
 }
 

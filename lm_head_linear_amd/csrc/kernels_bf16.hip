@@ -25,6 +25,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "../../include/flce.h"
 #include "flce_internal.h"
@@ -511,6 +512,13 @@ __device__ __forceinline__ void k_loop(Acc& acc, const Operand& A, const Operand
 // before any load.
 enum Dyn : int { kDynNone = 0, kDynM = 1, kDynN = 2, kDynK = 3 };
 
+// Whether an epilogue asks for the raster that deals M-tiles to the XCDs in
+// turn (gemm::tile_coords): one whose first M-tiles do more work.
+template <class E, class = void>
+struct SpreadM : std::false_type {};
+template <class E>
+struct SpreadM<E, std::void_t<decltype(E::kSpreadM)>> : std::bool_constant<E::kSpreadM> {};
+
 // LDS bytes of a GEMM's stages (reused by its epilogue: 32 KiB per wave).
 template <int FA, int FB>
 constexpr int stage_bytes() {
@@ -568,7 +576,7 @@ __device__ __forceinline__ void gemm_tile(char* smem, int64_t bid, int seg, Oper
     if (bid >= gemm::num_tiles(M, Nn)) return;
   }
   int64_t m0, n0;
-  gemm::tile_coords(bid, M, Nn, group_m, m0, n0);
+  gemm::tile_coords(bid, M, Nn, group_m, m0, n0, SpreadM<Epi>::value);
   if constexpr (DYN == kDynK) {
     const int64_t d = *dyn;
     K = d < K ? d : K;                             // past the count: zero-filled
@@ -731,112 +739,6 @@ __device__ __forceinline__ void store_logits(const Acc& acc, char* smem, int wm,
   __syncthreads();
 }
 
-// ---- forward epilogue: per (vocab tile, token) max and sum-exp ------------
-// Tile rows are vocabulary ids, columns are tokens.
-// SOFTCAP selects the s * tanh(z / s) variant at compile time; OUT, whether
-// the logits z' themselves are also stored (the float32 values the max and
-// sum are formed from).
-template <bool SOFTCAP, int OUT = kNoLogits>
-struct EpiLse {
-  const int64_t* labels;
-  int64_t N, V, ignore_index;
-  float softcap, inv_softcap;
-  float2* part;  // [n_voc_tiles][ld_part]: (max m, sum of exp(x - m)) of the tile
-  int64_t ld_part;
-  float* zt;     // target logit (softcapped), one writer per non-ignored token
-  void* logits;  // OUT != kNoLogits: [N][ld_logits]
-  int64_t ld_logits;
-  int vec;       // 16-byte runs of the logits rows are aligned
-
-  static constexpr int kTokBytes = 2048;          // the tile's labels
-  __device__ __forceinline__ void stage(char* tok, int64_t n0, int wave, int lane) const {
-    stage_tokens<2>(tok, labels, n0, N, wave, lane);
-  }
-
-  __device__ __forceinline__ void operator()(Acc& acc, int64_t m0, int64_t n0, int wm, int wn,
-                                             int lane, char* smem, const char* tok) const {
-    const int64_t* lab = reinterpret_cast<const int64_t*>(tok);
-    const int g = lane >> 4;
-    const int64_t vbase = m0 + wm * 128;
-    float mx[8], sm[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t t = n0 + acc_col(wn, j, lane);
-      // the lane's 32 logits of the column, softcapped and masked past V, in
-      // registers of their own (the accumulators are not written back unless
-      // the logits are stored)
-      float z[8][4];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float x = acc[i][j][r];
-          if (SOFTCAP) x = softcap * tanh_fast(x * inv_softcap);
-          const int64_t v = m0 + acc_row(wm, i, r, lane);
-          z[i][r] = v < V ? x : -INFINITY;
-          if (OUT != kNoLogits) acc[i][j][r] = z[i][r];
-        }
-      // target logit: the one lane holding (y_t, t) writes it
-      const int64_t y = t < N ? lab[acc_col(wn, j, lane)] : ignore_index;
-      if (y != ignore_index && y >= vbase && y < vbase + 128 && y < V) {
-        const int d = int(y - vbase);
-        const int ti = d >> 4, tr = d & 3;
-        if (((d >> 2) & 3) == g) {
-          float val = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) val = (i == ti && r == tr) ? z[i][r] : val;
-          zt[t] = val;
-        }
-      }
-      // max and sum in four independent chains (r), then combined over the
-      // lane's values and the four lanes of the column
-      float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mq[r] = fmaxf(mq[r], z[i][r]);
-      const float m = col_max4(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
-      // sum of exp(z - m) = sum of 2^(z log2 e - m log2 e), one fma per element
-      float s = 0.f;
-      if (m != -INFINITY) {
-        const float mb = m * kLog2e;
-        float sq[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            sq[r] += __builtin_amdgcn_exp2f(fmaf(z[i][r], kLog2e, -mb));
-        s = (sq[0] + sq[1]) + (sq[2] + sq[3]);
-      }
-      mx[j] = m;
-      sm[j] = col_sum4(s);
-    }
-    if (OUT != kNoLogits)
-      store_logits<OUT>(acc, smem, wm, wn, lane, logits, ld_logits, vec, m0, n0, N, V);
-    // combine the two waves (wm = 0, 1) that share the token columns
-    float2* buf = reinterpret_cast<float2*>(smem);
-    if (wm == 1 && g == 0) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) buf[wn * 128 + j * 16 + lane] = make_float2(mx[j], sm[j]);
-    }
-    __syncthreads();
-    if (wm == 0 && g == 0) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float2 o = buf[wn * 128 + j * 16 + lane];
-        const float Mx = fmaxf(mx[j], o.x);
-        float S = 0.f;
-        if (mx[j] != -INFINITY) S += sm[j] * __builtin_amdgcn_exp2f((mx[j] - Mx) * kLog2e);
-        if (o.x != -INFINITY) S += o.y * __builtin_amdgcn_exp2f((o.x - Mx) * kLog2e);
-        const int64_t t = n0 + acc_col(wn, j, lane);
-        if (t < ld_part) part[(m0 / kBM) * ld_part + t] = make_float2(Mx, S);
-      }
-    }
-  }
-};
-
 // ---- token-major bf16 stores of a tile held in the accumulators ----------
 // The tile's rows are vocabulary ids, its columns tokens; the destination is
 // row-major by token, dst[t][v] with row length ld, or (BLOCKED) blocked,
@@ -925,6 +827,147 @@ __device__ __forceinline__ void store_token_major(const Get& get, char* smem, in
     }
   }
 }
+
+// ---- forward epilogue: per (vocab tile, token) max and sum-exp ------------
+// Tile rows are vocabulary ids, columns are tokens.
+// SOFTCAP selects the s * tanh(z / s) variant at compile time; OUT, whether
+// the logits z' themselves are also stored (the float32 values the max and
+// sum are formed from). PC: the tiles of the first pc_rows vocabulary rows
+// also keep their probabilities relative to the tile max M of each token,
+// P' = exp(z' - M) <= 1, as bf16 in the blocked layout of the backward's G
+// chunk (pblk elements per 32 rows), so that the backward can form that
+// chunk's G from them instead of recomputing its logits. The partials are
+// formed exactly as without PC; P' is formed again from the logits in the
+// accumulators once the tile max is known.
+template <bool SOFTCAP, int OUT = kNoLogits, bool PC = false>
+struct EpiLse {
+  static_assert(!(PC && OUT != kNoLogits), "kept probabilities or stored logits, not both");
+  const int64_t* labels;
+  int64_t N, V, ignore_index;
+  float softcap, inv_softcap;
+  float2* part;  // [n_voc_tiles][ld_part]: (max m, sum of exp(x - m)) of the tile
+  int64_t ld_part;
+  float* zt;     // target logit (softcapped), one writer per non-ignored token
+  void* logits;  // OUT != kNoLogits: [N][ld_logits]
+  int64_t ld_logits;
+  int vec;       // 16-byte runs of the logits rows are aligned
+  uint16_t* probs = nullptr;   // PC: the G chunk buffer
+  int64_t pc_rows = 0, pblk = 0;
+  // the tiles of the kept rows store more: deal the vocabulary tiles to the XCDs
+  static constexpr bool kSpreadM = PC;
+
+  static constexpr int kTokBytes = 2048;          // the tile's labels
+  __device__ __forceinline__ void stage(char* tok, int64_t n0, int wave, int lane) const {
+    stage_tokens<2>(tok, labels, n0, N, wave, lane);
+  }
+
+  __device__ __forceinline__ void operator()(Acc& acc, int64_t m0, int64_t n0, int wm, int wn,
+                                             int lane, char* smem, const char* tok) const {
+    const int64_t* lab = reinterpret_cast<const int64_t*>(tok);
+    const int g = lane >> 4;
+    const int64_t vbase = m0 + wm * 128;
+    const bool pc = PC && m0 < pc_rows;          // the whole workgroup agrees
+    float mx[8], sm[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t t = n0 + acc_col(wn, j, lane);
+      // the lane's 32 logits of the column, softcapped and masked past V, in
+      // registers of their own (the accumulators are not written back unless
+      // the logits are stored)
+      float z[8][4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = acc[i][j][r];
+          if (SOFTCAP) x = softcap * tanh_fast(x * inv_softcap);
+          const int64_t v = m0 + acc_row(wm, i, r, lane);
+          z[i][r] = v < V ? x : -INFINITY;
+          if (OUT != kNoLogits) acc[i][j][r] = z[i][r];
+        }
+      // target logit: the one lane holding (y_t, t) writes it
+      const int64_t y = t < N ? lab[acc_col(wn, j, lane)] : ignore_index;
+      if (y != ignore_index && y >= vbase && y < vbase + 128 && y < V) {
+        const int d = int(y - vbase);
+        const int ti = d >> 4, tr = d & 3;
+        if (((d >> 2) & 3) == g) {
+          float val = 0.f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) val = (i == ti && r == tr) ? z[i][r] : val;
+          zt[t] = val;
+        }
+      }
+      // max and sum in four independent chains (r), then combined over the
+      // lane's values and the four lanes of the column
+      float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mq[r] = fmaxf(mq[r], z[i][r]);
+      const float m = col_max4(fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3])));
+      // sum of exp(z - m) = sum of 2^(z log2 e - m log2 e), one fma per element
+      float s = 0.f;
+      if (m != -INFINITY) {
+        const float mb = m * kLog2e;
+        float sq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sq[r] += __builtin_amdgcn_exp2f(fmaf(z[i][r], kLog2e, -mb));
+        s = (sq[0] + sq[1]) + (sq[2] + sq[3]);
+      }
+      mx[j] = m;
+      sm[j] = col_sum4(s);
+    }
+    if (OUT != kNoLogits)
+      store_logits<OUT>(acc, smem, wm, wn, lane, logits, ld_logits, vec, m0, n0, N, V);
+    // combine the two waves (wm = 0, 1) that share the token columns
+    float2* buf = reinterpret_cast<float2*>(smem);
+    float* wmax = reinterpret_cast<float*>(smem + 2048);    // PC: [2][256] wave maxima
+    if (PC && pc && g == 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wmax[wm * 256 + wn * 128 + j * 16 + lane] = mx[j];
+    }
+    if (wm == 1 && g == 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) buf[wn * 128 + j * 16 + lane] = make_float2(mx[j], sm[j]);
+    }
+    __syncthreads();
+    if (wm == 0 && g == 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float2 o = buf[wn * 128 + j * 16 + lane];
+        const float Mx = fmaxf(mx[j], o.x);
+        float S = 0.f;
+        if (mx[j] != -INFINITY) S += sm[j] * __builtin_amdgcn_exp2f((mx[j] - Mx) * kLog2e);
+        if (o.x != -INFINITY) S += o.y * __builtin_amdgcn_exp2f((o.x - Mx) * kLog2e);
+        const int64_t t = n0 + acc_col(wn, j, lane);
+        if (t < ld_part) part[(m0 / kBM) * ld_part + t] = make_float2(Mx, S);
+      }
+    }
+    if (PC && pc) {
+      // P' = exp(z' - M), M the tile max of the column (both waves' maxima),
+      // formed again from the logits in the accumulators as it is staged
+      float mb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float o = wmax[(1 - wm) * 256 + wn * 128 + j * 16 + (lane & 15)];
+        mb[j] = fmaxf(mx[j], o) * kLog2e;
+      }
+      __syncthreads();                             // the maxima are read; staging reuses LDS
+      auto prob = [&](int i, int j, int r) {
+        float x = acc[i][j][r];
+        if (SOFTCAP) x = softcap * tanh_fast(x * inv_softcap);
+        return mb[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fmaf(x, kLog2e, -mb[j]));
+      };
+      store_token_major<false, false, true>(prob, smem, wm, wn, lane, probs, 0, m0, n0, N,
+                                            pc_rows < V ? pc_rows : V, nullptr, pblk);
+    }
+  }
+};
 
 // ---- backward epilogue: the logit gradient G for one vocabulary chunk ----
 // G[t, v] = c * valid_t * (exp(z'_tv - lse_t) - [v = y_t]) * dz'/dz, stored
@@ -1138,7 +1181,8 @@ struct EpiLseP {
   }
 };
 
-// G in place of the stored probabilities of one token chunk:
+// G in place of the stored probabilities of nt tokens (the first *count
+// ones when `count` is given) and the vocabulary columns [0, nv):
 //   G[t][v] = c valid_t (P'[t][v] exp(M_tv - lse_t) - [v = y_t]) dz'/dz
 // with M_tv the max of v's vocabulary tile for token t (the forward partial).
 // The target element is formed from the float32 target logit instead:
@@ -1149,17 +1193,22 @@ struct EpiLseP {
 // [nt tokens][4 runs], so a wave reads and writes one contiguous KiB.
 template <bool SOFTCAP>
 __global__ __launch_bounds__(256) void k_probs_to_grad(
-    uint16_t* __restrict__ gp, int64_t blk, int64_t nt, int64_t V,
-    const float2* __restrict__ part, int64_t ld_part, const float* __restrict__ lse,
-    const float* __restrict__ zt, const int64_t* __restrict__ labels, int64_t ignore_index,
-    const Scalars* __restrict__ sc, float inv_softcap) {
+    uint16_t* __restrict__ gp, int64_t blk, int64_t nt, const int64_t* __restrict__ count,
+    int64_t nv, int64_t V, const float2* __restrict__ part, int64_t ld_part,
+    const float* __restrict__ lse, const float* __restrict__ zt,
+    const int64_t* __restrict__ labels, int64_t ignore_index, const Scalars* __restrict__ sc,
+    float inv_softcap) {
+  if (count) {
+    const int64_t c = *count;
+    nt = c < nt ? c : nt;
+  }
   const int64_t rem = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (rem >= nt * 4) return;
   const int64_t t = rem >> 2;
   const int64_t y = labels[t];
   const float coef = y == ignore_index ? 0.f : ((y < 0 || y >= V) ? NAN : sc->c32);
   const float l = lse[t];
-  const int64_t nb = (V + 31) / 32;
+  const int64_t nb = (nv + 31) / 32;
   for (int64_t b = blockIdx.y; b < nb; b += gridDim.y) {
     const int64_t v0 = b * 32 + (rem & 3) * 8;
     uint16_t* run = gp + b * blk + t * 32 + (rem & 3) * 8;
@@ -1187,7 +1236,7 @@ __global__ __launch_bounds__(256) void k_probs_to_grad(
           x *= 1.f - th * th;
         }
       }
-      g[e] = v < V ? x : 0.f;
+      g[e] = v < nv ? x : 0.f;
     }
     *reinterpret_cast<u32x4*>(run) = u32x4{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]),
                                            pack_bf16x2(g[4], g[5]), pack_bf16x2(g[6], g[7])};
@@ -1571,6 +1620,25 @@ hipError_t bf16_forward_out(const Plan& p, const Args& a, const Launcher& L) {
   const int64_t* lab = p.compact ? a.yc : a.labels;
   const int64_t* nv = (p.compact && !a.lse_out) ? &a.sc->n_valid : nullptr;
   constexpr int NF = gemm::kFormN;
+  if constexpr (OUT == kNoLogits) {
+    if (p.compact) {
+      // the first backward chunk's probabilities are kept (its G is formed
+      // from them, without recomputing its logits)
+      auto run = [&](auto e) {
+        e.probs = static_cast<uint16_t*>(a.g);
+        e.pc_rows = gemm::chunk_rows(p, 0);
+        e.pblk = gemm::g_block(p);
+        return nv ? run_gemm<NF, NF, false, 1, false, kDynN>(l, a, e, kLseFwd, L, 0, 1, nv)
+                  : run_gemm<NF, NF>(l, a, e, kLseFwd, L);
+      };
+      if (a.softcap > 0.f)
+        return run(EpiLse<true, kNoLogits, true>{lab, p.N, p.V, a.ignore_index, a.softcap,
+                                                 1.f / a.softcap, a.part, p.ld_part, a.zt,
+                                                 nullptr, 0, 0});
+      return run(EpiLse<false, kNoLogits, true>{lab, p.N, p.V, a.ignore_index, 0.f, 0.f, a.part,
+                                                p.ld_part, a.zt, nullptr, 0, 0});
+    }
+  }
   if (a.softcap > 0.f) {
     EpiLse<true, OUT> e{lab, p.N, p.V, a.ignore_index, a.softcap, 1.f / a.softcap, a.part,
                         p.ld_part, a.zt, a.logits, a.ld_logits, vec};
@@ -1642,10 +1710,25 @@ hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, cons
   uint16_t* g = static_cast<uint16_t*>(a.g);
   const int64_t* nv = &a.sc->n_valid;
   constexpr int NF = gemm::kFormN, TF = gemm::kFormT;
-  // 1) recompute the logits of the chunk and form G[n_valid][vchunk]
+  // 1) G[n_valid][vchunk]: chunk 0 from the probabilities the forward kept,
+  // the others by recomputing the chunk's logits
   const gemm::Launch lg = gemm::backward_launch(p, chunk, 0);
   hipError_t err;
-  if (a.softcap > 0.f) {
+  if (chunk == 0) {
+    const int64_t nb = (vcur + 31) / 32;
+    const dim3 grid(unsigned((p.N * 4 + 255) / 256), unsigned(nb < 512 ? nb : 512));
+    L.pre(kProbsToGrad);
+    if (a.softcap > 0.f)
+      hipLaunchKernelGGL(k_probs_to_grad<true>, grid, dim3(256), 0, L.stream, g,
+                         gemm::g_block(p), p.N, nv, vcur, p.V, a.part, p.ld_part, a.lse, a.zt,
+                         a.yc, a.ignore_index, a.sc, 1.f / a.softcap);
+    else
+      hipLaunchKernelGGL(k_probs_to_grad<false>, grid, dim3(256), 0, L.stream, g,
+                         gemm::g_block(p), p.N, nv, vcur, p.V, a.part, p.ld_part, a.lse, a.zt,
+                         a.yc, a.ignore_index, a.sc, 0.f);
+    L.post(kProbsToGrad);
+    err = hipGetLastError();
+  } else if (a.softcap > 0.f) {
     const EpiGrad<true, false> eg{a.yc, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
                                   gemm::g_block(p), a.softcap, 1.f / a.softcap, g, 0};
     err = run_gemm<NF, NF, false, 1, false, kDynN>(lg, a, eg, kGradLogits, L, 0, 1, nv);
@@ -1721,12 +1804,13 @@ hipError_t bf16_nr_backward_chunk(const Plan& p, const Args& a, int64_t c, const
   const int64_t blk = gemm::nr_block(p);
   L.pre(kProbsToGrad);
   if (a.softcap > 0.f)
-    hipLaunchKernelGGL(k_probs_to_grad<true>, grid, dim3(256), 0, L.stream, g, blk, nt, p.V,
-                       a.part, p.ld_part, a.lse, a.zt, a.labels + t0, a.ignore_index, a.sc,
-                       1.f / a.softcap);
+    hipLaunchKernelGGL(k_probs_to_grad<true>, grid, dim3(256), 0, L.stream, g, blk, nt, nullptr,
+                       p.V, p.V, a.part, p.ld_part, a.lse, a.zt, a.labels + t0, a.ignore_index,
+                       a.sc, 1.f / a.softcap);
   else
-    hipLaunchKernelGGL(k_probs_to_grad<false>, grid, dim3(256), 0, L.stream, g, blk, nt, p.V,
-                       a.part, p.ld_part, a.lse, a.zt, a.labels + t0, a.ignore_index, a.sc, 0.f);
+    hipLaunchKernelGGL(k_probs_to_grad<false>, grid, dim3(256), 0, L.stream, g, blk, nt, nullptr,
+                       p.V, p.V, a.part, p.ld_part, a.lse, a.zt, a.labels + t0, a.ignore_index,
+                       a.sc, 0.f);
   L.post(kProbsToGrad);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

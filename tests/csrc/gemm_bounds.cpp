@@ -149,14 +149,14 @@ static void check_blocked_matches_dense() {
   }
 }
 
-static void check_launch(const Plan& p, const Launch& l) {
+static void check_launch(const Plan& p, const Launch& l, bool spread_m = false) {
   if (!offsets_fit(l.fa, l.a) || !offsets_fit(l.fb, l.b)) fail("offsets exceed 32 bits", l.M, l.Nn, l.K);
   const int64_t nt = num_tiles(l.M, l.Nn);
   const int64_t num_m = (l.M + kBM - 1) / kBM;
   std::vector<char> seen(size_t(nt), 0);
   for (int64_t b = 0; b < nt; ++b) {
     int64_t m0, n0;
-    tile_coords(b, l.M, l.Nn, kGroupM, m0, n0);
+    tile_coords(b, l.M, l.Nn, kGroupM, m0, n0, spread_m);
     if (m0 < 0 || m0 >= l.M || n0 < 0 || n0 >= l.Nn || m0 % kBM || n0 % kBM) {
       fail("tile out of range", b, m0, n0);
       continue;
@@ -217,6 +217,7 @@ int main(int argc, char** argv) {
       Plan p;
       if (!make_plan(s.N, s.H, s.V, 1, &p, true, grad)) { fail("plan", s.N, s.H, s.V); continue; }
       check_launch(p, forward_launch(p));
+      check_launch(p, forward_launch(p), true);     // the raster that deals M-tiles to XCDs
       for (int64_t c = 0; c < p.n_chunks; ++c) {
         check_launch(p, backward_launch(p, c, 0));
         for (int part = 0; part < p.g_parts; ++part)
