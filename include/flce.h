@@ -230,8 +230,9 @@ int flce_forward_backward_nr(const void* h, const void* W, const int64_t* labels
 /*
  * flce_forward_workspace_size -- bytes of device scratch that flce_forward
  * needs (256-byte aligned base required): the per-tile log-sum-exp partials
- * and the per-token lse and target logits only, O(N * V / 256 + N) bytes.
- * Returns 0 for invalid sizes. Pure host arithmetic.
+ * and the per-token lse, target logits and losses, O(N * V / 256 + N)
+ * bytes, and for bf16 the gathered tokens (positions, labels and hidden
+ * rows, N * H * 2 bytes). Returns 0 for invalid sizes. Pure host arithmetic.
  */
 size_t flce_forward_workspace_size(int64_t N, int64_t H, int64_t V, int dtype);
 
@@ -258,7 +259,10 @@ int flce_forward_check_args(const void* h, const void* W, const int64_t* labels,
  * linear_ce page, API: forward returns the scalar loss). It runs the same
  * kernels as the forward part of flce_forward_backward on the same inputs,
  * so *loss, *num_tokens, lse_out and *status are bit-identical to what that
- * call returns; it costs one GEMM pass (2*N*H*V flops) instead of four.
+ * call returns; it costs one GEMM pass (2*N*H*V flops) instead of four. With
+ * bf16 inputs it gathers the non-ignored tokens first, like that call, and
+ * with lse_out NULL the GEMM runs over those tokens only (an ignored token
+ * adds nothing to the loss); with lse_out it runs over all N.
  *
  * Parameters as in flce_forward_backward, without dH, dW and accumulate_dW.
  * Workspace caller-owned, >= flce_forward_workspace_size(N, H, V, dtype)
@@ -284,17 +288,20 @@ int flce_forward(const void* h, const void* W, const int64_t* labels, int64_t N,
  *          library, one copy on every GPU the library runs on (the GPU of
  *          `stream`; the current device for the null stream), held until the
  *          process ends. The first call on a GPU looks up that copy's device
- *          address (a HIP runtime query, no allocation). A problem whose
- *          forward workspace, flce_forward_workspace_size(N, H, V, dtype),
- *          exceeds the array is refused with FLCE_ERR_SCRATCH before anything
- *          is launched. The call allocates nothing: no hipMalloc, no hipFree,
- *          no allocating library routine.
+ *          address (a HIP runtime query, no allocation). This entry does not
+ *          gather the non-ignored tokens: its scratch is the forward's
+ *          per-tile partials (ceil(V/256) * roundup(N, 256) * 8 bytes) and
+ *          per-token arrays (about 16 * roundup(N, 256) bytes), and a problem
+ *          whose scratch exceeds the array is refused with FLCE_ERR_SCRATCH
+ *          before anything is launched. The call allocates nothing: no
+ *          hipMalloc, no hipFree, no allocating library routine.
  * Sharing  every call on one GPU uses that GPU's array, which keeps the last
  *          call's contents (the kernels write everything they read back), so
  *          calls that overlap on one GPU (two streams, or two host threads)
  *          race: the caller must serialise them.
  * Everything else (parameters, outputs, edge cases, errors) as in
- * flce_forward, whose results it reproduces bit for bit.
+ * flce_forward, whose results it reproduces bit for bit (the gather changes
+ * no value, and the loss sums the per-token losses by original position).
  */
 #define FLCE_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
 int flce_forward_noalloc(const void* h, const void* W, const int64_t* labels, int64_t N,

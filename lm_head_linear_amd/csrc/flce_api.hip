@@ -158,9 +158,9 @@ int run(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t 
         float* loss, int64_t* num_tokens, void* dH, void* dW, void* stream, int dtype,
         float mb_scale, int accumulate_dW, void* workspace, int32_t* status, float* lse_out,
         bool backward, int grad_dtype, void* logits = nullptr, int64_t ld_logits = 0,
-        int logits_dtype = FLCE_F32) {
+        int logits_dtype = FLCE_F32, int gather = -1) {
   flce::Plan p;
-  if (!flce::make_plan(N, H, V, dtype, &p, backward, grad_dtype)) return FLCE_ERR_ARG;
+  if (!flce::make_plan(N, H, V, dtype, &p, backward, grad_dtype, gather)) return FLCE_ERR_ARG;
 
   flce::Launcher L{static_cast<hipStream_t>(stream), nullptr, nullptr};
   if (g_prof.on) { L.before = prof_before; L.after = prof_after; }
@@ -314,18 +314,21 @@ int flce_forward_noalloc(const void* h, const void* W, const int64_t* labels, in
   // the argument checks first, against a stand-in aligned address: only the
   // workspace rules depend on it, and the scratch is always large enough
   // once the size check below has passed
-  const size_t need = flce_forward_workspace_size(N, H, V, dtype);
   int st = flce_forward_check_args(h, W, labels, N, H, V, ignore_index, softcap, reduction,
                                    num_label_tokens, loss, num_tokens, stream, dtype, mb_scale,
                                    reinterpret_cast<void*>(uintptr_t(256)), size_t(-1), status,
                                    lse_out);
   if (st != FLCE_OK) return st;
-  if (need > FLCE_NOALLOC_SCRATCH_BYTES) return FLCE_ERR_SCRATCH;
+  // the forward without the token gather (its scratch is the partials and
+  // per-token arrays alone), bit-identical to flce_forward's results
+  flce::Plan p;
+  if (!flce::make_plan(N, H, V, dtype, &p, false, -1, 0)) return FLCE_ERR_ARG;
+  if (p.total > FLCE_NOALLOC_SCRATCH_BYTES) return FLCE_ERR_SCRATCH;
   void* ws = nullptr;
   if (scratch_address(static_cast<hipStream_t>(stream), &ws) != hipSuccess) return FLCE_ERR_HIP;
   return run(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens, loss,
              num_tokens, nullptr, nullptr, stream, dtype, mb_scale, 0, ws, status, lse_out,
-             false, dtype);
+             false, dtype, nullptr, 0, FLCE_F32, 0);
 }
 
 int flce_forward_logits(const void* h, const void* W, const int64_t* labels, int64_t N,
@@ -341,7 +344,7 @@ int flce_forward_logits(const void* h, const void* W, const int64_t* labels, int
   if (st != FLCE_OK) return st;
   return run(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens, loss,
              num_tokens, nullptr, nullptr, stream, dtype, mb_scale, 0, workspace, status,
-             lse_out, false, dtype, N > 0 ? logits : nullptr, ld_logits, logits_dtype);
+             lse_out, false, dtype, N > 0 ? logits : nullptr, ld_logits, logits_dtype, 0);
 }
 
 int flce_profile_begin(void) {

@@ -27,7 +27,7 @@ int64_t env_vchunk() {
 }  // namespace
 
 bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backward,
-               int grad_dtype) {
+               int grad_dtype, int gather) {
   if (N < 0 || H <= 0 || V <= 0) return false;
   if (dtype != FLCE_F32 && dtype != FLCE_BF16) return false;
   if (grad_dtype < 0) grad_dtype = dtype;
@@ -79,7 +79,7 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
       off = align256(off + size_t(q.dh_segs) * size_t(N) * H * sizeof(float));
     }
     // the tokens gathered, the non-ignored ones first (see Plan::compact)
-    q.compact = backward && dtype == FLCE_BF16 && q.g_parts == 1;
+    q.compact = dtype == FLCE_BF16 && q.g_parts == 1 && gather != 0;
     if (q.compact) {
       q.n_gather_blocks = ceil_div(N, kGatherBlock);
       q.off_idx = off;  off = align256(off + size_t(N) * sizeof(int32_t));
@@ -98,7 +98,7 @@ bool make_plan_nr(int64_t N, int64_t H, int64_t V, int dtype, int64_t token_chun
   if (token_chunk < 0) token_chunk = 0;
   if (token_chunk > (int64_t(1) << 31)) return false;
   Plan q;
-  if (!make_plan(N, H, V, dtype, &q, false)) return false;
+  if (!make_plan(N, H, V, dtype, &q, false, -1, 0)) return false;
   q.nr = true;
   q.backward = true;
   q.grad_dtype = dtype;
@@ -196,7 +196,7 @@ int check_common(const void* h, const void* W, const int64_t* labels, int64_t N,
                  int64_t V, float softcap, int reduction, int64_t num_label_tokens,
                  const float* loss, const int64_t* num_tokens, const void* dH, const void* dW,
                  int dtype, int grad_dtype, float mb_scale, const void* workspace,
-                 size_t workspace_bytes, bool backward) {
+                 size_t workspace_bytes, bool backward, int gather = -1) {
   if (N < 0 || H <= 0 || V <= 0) return FLCE_ERR_ARG;
   if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_ERR_ARG;
   if (grad_dtype != FLCE_F32 && grad_dtype != FLCE_BF16) return FLCE_ERR_ARG;
@@ -211,7 +211,7 @@ int check_common(const void* h, const void* W, const int64_t* labels, int64_t N,
   if (N > 0 && (!h || !labels)) return FLCE_ERR_ARG;
   if (backward && (!dW || (N > 0 && !dH))) return FLCE_ERR_ARG;
   flce::Plan p;
-  if (!flce::make_plan(N, H, V, dtype, &p, backward, grad_dtype)) return FLCE_ERR_ARG;
+  if (!flce::make_plan(N, H, V, dtype, &p, backward, grad_dtype, gather)) return FLCE_ERR_ARG;
   const size_t es = p.elem, gs = p.grad_elem;
   if (backward) {
     if (overlaps(dH, size_t(N) * H * gs, h, size_t(N) * H * es)) return FLCE_ERR_ARG;
@@ -289,9 +289,10 @@ int flce_forward_logits_check_args(const void* h, const void* W, const int64_t* 
   if (N > 0 && V > 0 && V <= (int64_t(1) << 31) &&
       N - 1 > ((int64_t(1) << 60) - V) / ld_logits)
     return FLCE_ERR_ARG;
-  const int st = flce_forward_check_args(h, W, labels, N, H, V, ignore_index, softcap, reduction,
-                                         num_label_tokens, loss, num_tokens, stream, dtype,
-                                         mb_scale, workspace, workspace_bytes, status, lse_out);
+  // the logits come out in the tokens' own order: this entry does not gather
+  const int st = check_common(h, W, labels, N, H, V, softcap, reduction, num_label_tokens, loss,
+                              num_tokens, nullptr, nullptr, dtype, dtype, mb_scale, workspace,
+                              workspace_bytes, false, 0);
   if (st == FLCE_ERR_ARG) return st;            // sizes are valid from here on
   if (N > 0) {
     // the logits buffer, [N][ld_logits] up to its last stored element, is an

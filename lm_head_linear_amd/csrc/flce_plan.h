@@ -116,8 +116,12 @@ struct Plan {
 // of bf16 chunks (half as many vocabulary rows per chunk) and need no dH
 // accumulator (dH itself is float32). bf16 gradients for float32 inputs are
 // refused.
+// `gather` (bf16 only): gather the non-ignored tokens first (see
+// Plan::compact); < 0 means the default, which gathers for a forward-only
+// plan and for bf16 gradients. The logits-returning forward and the
+// allocation-free one do not gather.
 bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backward = true,
-               int grad_dtype = -1);
+               int grad_dtype = -1, int gather = -1);
 
 // Plan of the no-recompute variant (bf16 only): token chunks of
 // `token_chunk` tokens (rounded up to the tile; <= 0: min(N, 8192) rounded

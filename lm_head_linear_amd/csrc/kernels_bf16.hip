@@ -1621,7 +1621,7 @@ hipError_t bf16_forward_out(const Plan& p, const Args& a, const Launcher& L) {
   const int64_t* nv = (p.compact && !a.lse_out) ? &a.sc->n_valid : nullptr;
   constexpr int NF = gemm::kFormN;
   if constexpr (OUT == kNoLogits) {
-    if (p.compact) {
+    if (p.compact && p.backward) {
       // the first backward chunk's probabilities are kept (its G is formed
       // from them, without recomputing its logits)
       auto run = [&](auto e) {

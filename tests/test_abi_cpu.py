@@ -214,14 +214,16 @@ def _fargs(**kw):
 
 def test_forward_workspace_is_the_forward_part(lib):
     """The forward-only plan carves the log-sum-exp partials and per-token
-    arrays but no gradient chunk and no dH accumulator."""
+    arrays (and, for bf16, the gathered tokens: positions, labels, hidden
+    rows) but no gradient chunk and no dH accumulator."""
     for N, H, V in [(8192, 4096, 131072), (8192, 3584, 256000), (32, 64, 1024), (1, 8, 1)]:
         for dt in (0, 1):
             f = lib.flce_forward_workspace_size(N, H, V, dt)
             full = lib.flce_workspace_size(N, H, V, dt)
             assert 0 < f < full
             n_tiles = -(-V // (256 if dt == 1 else 64))
-            assert f <= 256 + n_tiles * (N + 256) * 8 + 3 * (N + 256) * 8 + 4 * 256
+            gather = (N * H * 2 + 12 * N + 4 * (N // 1024 + 1) + 4 * 256) if dt == 1 else 0
+            assert f <= 256 + n_tiles * (N + 256) * 8 + 3 * (N + 256) * 8 + 4 * 256 + gather
     assert lib.flce_forward_workspace_size(-1, 8, 8, 1) == 0
     assert lib.flce_forward_workspace_size(0, 8, 8, 1) > 0
 
@@ -281,10 +283,11 @@ def test_forward_logits_check_args_ok(lib):
     assert lib.flce_forward_logits_check_args(*_largs()) == 0
     assert lib.flce_forward_logits_check_args(*_largs(ldt=1, ld=129)) == 0   # any ld >= V
     assert lib.flce_forward_logits_check_args(*_largs(dtype=0, H=3, ld=1000)) == 0
-    # same workspace as the forward-only entry
+    # the forward-only entry's workspace is enough (this entry does not gather
+    # the tokens, so it needs less); too little is refused
     f = lib.flce_forward_workspace_size(64, 64, 128, 1)
     assert lib.flce_forward_logits_check_args(*_largs(wsb=f)) == 0
-    assert lib.flce_forward_logits_check_args(*_largs(wsb=f - 1)) == 3
+    assert lib.flce_forward_logits_check_args(*_largs(wsb=1024)) == 3
     # N = 0: no logits buffer needed
     assert lib.flce_forward_logits_check_args(*_largs(N=0, h=None, labels=None, logits=None)) == 0
 
@@ -451,9 +454,13 @@ def test_noalloc_refusals_before_any_launch(lib):
     its fixed scratch, and bad arguments, before touching the GPU."""
     from lm_head_linear_amd import _lib
     N, H, V = 16384, 64, 1 << 20
-    assert lib.flce_forward_workspace_size(N, H, V, 1) > _lib.NOALLOC_SCRATCH_BYTES
-    assert lib.flce_forward_workspace_size(16384, 4096, 131072, 1) <= _lib.NOALLOC_SCRATCH_BYTES
-    assert lib.flce_forward_workspace_size(8192, 3584, 256000, 1) <= _lib.NOALLOC_SCRATCH_BYTES
+
+    def scratch(N, V):          # the ungathered forward: partials and per-token arrays
+        npad = -(-N // 256) * 256
+        return -(-V // 256) * npad * 8 + 16 * npad + 4096
+    assert scratch(N, V) > _lib.NOALLOC_SCRATCH_BYTES
+    for n, v in ((16384, 131072), (8192, 256000), (8192, 131072), (2048, 32000)):
+        assert scratch(n, v) <= _lib.NOALLOC_SCRATCH_BYTES, (n, v)
 
     def call(**kw):
         a = dict(h=A16, W=A16 * 64, labels=A16 * 128, N=N, H=H, V=V, ignore=-100, softcap=0.0,

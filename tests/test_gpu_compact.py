@@ -121,6 +121,14 @@ def test_forward_skips_ignored_tokens_without_changing_a_bit(cap, vchunk):
     assert torch.equal(b["lse"].view(torch.int32), f["lse"].view(torch.int32))
     for k in ("dH", "dW"):
         assert torch.equal(a[k].view(torch.int16), b[k].view(torch.int16)), k
+    # the forward-only entry without lse_out (its GEMM over the kept tokens)
+    import lm_head_linear_amd as m
+    dev = gu.device()
+    lf, nf = m.flce_forward(w.h.reshape(-1, w.H).to(dev), w.W.to(dev), w.labels.reshape(-1).to(dev),
+                            ignore_index=w.ignore_index, softcap=w.softcap, reduction=w.reduction)
+    torch.cuda.synchronize()
+    assert lf.view(torch.int32).item() == a["loss_t"].view(torch.int32).item()
+    assert nf.item() == a["num_tokens"]
     r = gu.run_oracle(w)
     gu.assert_parity(w, b, r)
     gu.assert_parity(w, a, r, check_lse=False)
