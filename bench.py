@@ -250,10 +250,12 @@ def other_modes(m, w, h, W, y, dH, dW, loss, nt, steps, timing, nhv):
         fwd()
     torch.cuda.synchronize()
     f_ms = (time.perf_counter() - tf0) * 1e3 / steps
+    n_kept = int((w.labels != w.ignore_index).sum())
     forward_only = {"ms_per_call": round(f_ms, 4), "tokens_per_s": round(N / (f_ms * 1e-3), 1),
-                    "tflops_2nhv": round(2 * nhv / (f_ms * 1e-3) / 1e12, 1),
+                    "tflops_executed": round(2.0 * n_kept * H * V / (f_ms * 1e-3) / 1e12, 1),
                     "workspace_bytes": int(fws.numel())}
-    log(f"forward only: {f_ms:.3f} ms/call, {forward_only['tflops_2nhv']:.1f} TFLOP/s")
+    log(f"forward only: {f_ms:.3f} ms/call, {forward_only['tflops_executed']:.1f} TFLOP/s "
+        f"over the {n_kept} kept tokens")
 
     # The same forward handing back the logits ([N, V], bf16 then float32):
     # the extra time is the logits' write.
@@ -333,7 +335,7 @@ def other_modes(m, w, h, W, y, dH, dW, loss, nt, steps, timing, nhv):
         m.flce_profile_end()
         nr_kernels = {k: round(ms / 3, 4) for k, (ms, n) in m.flce_profile_query().items() if n}
     no_recompute = {"ms_per_step": round(n_ms, 4), "tokens_per_s": round(N / (n_ms * 1e-3), 1),
-                    "tflops_6nhv": round(6 * nhv / (n_ms * 1e-3) / 1e12, 1),
+                    "tflops_executed": round(6.0 * n_kept * H * V / (n_ms * 1e-3) / 1e12, 1),
                     "token_chunk": m.flce_token_chunk_nr(N, H, V, W.dtype),
                     "workspace_bytes": int(nws.numel()), "kernels_ms_per_step": nr_kernels}
     log(f"no recompute: {n_ms:.3f} ms/step {nr_kernels}")

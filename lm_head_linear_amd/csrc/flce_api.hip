@@ -140,10 +140,21 @@ int run_nr(const void* h, const void* W, const int64_t* labels, int64_t N, int64
   a.dh_acc = nullptr;
   a.dh_part = p.dh_kseg ? reinterpret_cast<float*>(ws + p.off_dhpart) : nullptr;
   a.dw_acc = p.need_dw_acc ? reinterpret_cast<float*>(ws + p.off_dwacc) : nullptr;
+  a.idx = reinterpret_cast<int32_t*>(ws + p.off_idx);
+  a.yc = reinterpret_cast<int64_t*>(ws + p.off_yc);
+  a.bcnt = reinterpret_cast<int32_t*>(ws + p.off_bcnt);
+  a.ccnt = reinterpret_cast<int64_t*>(ws + p.off_ccnt);
+  a.hc = ws + p.off_hc;
   e = flce::launch_label_scan(p, a, L);
+  // the tokens gathered, the kept ones first; the chunks run over that order
+  // (the ignored tokens only for their lse, when it is asked for)
+  const bool all_rows = lse_out != nullptr;
+  if (e == hipSuccess) e = flce::launch_gather(p, a, all_rows, L);
+  if (e == hipSuccess) e = flce::launch_chunk_counts(p, a, all_rows, L);
   for (int64_t c = 0; e == hipSuccess && c < p.n_tok_chunks; ++c) {
+    const int64_t t0 = c * p.nc, nt = flce::gemm::nr_chunk_tokens(p, c);
     e = flce::bf16_nr_forward_chunk(p, a, c, L);
-    if (e == hipSuccess) e = flce::launch_merge(p, a, c * p.nc, flce::gemm::nr_chunk_tokens(p, c), L);
+    if (e == hipSuccess) e = flce::launch_merge_gathered(p, a, t0, nt, a.ccnt + c, L);
     if (e == hipSuccess) e = flce::bf16_nr_backward_chunk(p, a, c, L);
   }
   if (e == hipSuccess) e = flce::launch_loss_final(p, a, L);

@@ -139,6 +139,16 @@ bool make_plan_nr(int64_t N, int64_t H, int64_t V, int dtype, int64_t token_chun
       q.off_dwacc = off;
       off = align256(off + size_t(V) * size_t(H) * sizeof(float));
     }
+    // the tokens gathered, the non-ignored ones first; the token chunks run
+    // over the gathered order, each with its live token counts (forward,
+    // backward) computed on the device
+    q.compact = true;
+    q.n_gather_blocks = ceil_div(N, kGatherBlock);
+    q.off_idx = off;  off = align256(off + size_t(N) * sizeof(int32_t));
+    q.off_yc = off;   off = align256(off + size_t(N) * sizeof(int64_t));
+    q.off_bcnt = off; off = align256(off + size_t(q.n_gather_blocks) * sizeof(int32_t));
+    q.off_ccnt = off; off = align256(off + size_t(2 * q.n_tok_chunks) * sizeof(int64_t));
+    q.off_hc = off;   off = align256(off + size_t(N) * H * q.elem);
   }
   q.off_dhacc = 0;
   q.need_dh_acc = false;

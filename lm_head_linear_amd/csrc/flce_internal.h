@@ -63,6 +63,8 @@ struct Args {
   int64_t* yc;    // its label
   int32_t* bcnt;  // kept tokens per gather block
   void* hc;       // its hidden row, bf16 [N][H]
+  int64_t* ccnt;  // no-recompute variant: live tokens of each token chunk, for
+                  // the forward ([n_tok_chunks]) and then for the backward
 };
 
 // Launch hook: the C-ABI layer brackets launches with timing events.
@@ -88,6 +90,14 @@ hipError_t launch_zero_bytes(void* ptr, size_t bytes, const Launcher& L);
 // kept ones, or all N), give ignored tokens a zero loss, and zero the dH rows
 // of the ignored ones.
 hipError_t launch_gather(const Plan& p, const Args& a, bool all_rows, const Launcher& L);
+// No-recompute variant after the gather: the live tokens of every token chunk
+// of nc gathered rows, for the forward (all N, or the kept ones) and for the
+// backward (the kept ones).
+hipError_t launch_chunk_counts(const Plan& p, const Args& a, bool all_rows, const Launcher& L);
+// The merge of a gathered token chunk: tokens [t0, t0 + *count) of the
+// gathered order, losses and lse_out scattered to original positions.
+hipError_t launch_merge_gathered(const Plan& p, const Args& a, int64_t t0, int64_t nt,
+                                 const int64_t* count, const Launcher& L);
 
 // bf16 MFMA path.
 hipError_t bf16_forward(const Plan& p, const Args& a, const Launcher& L);

@@ -106,7 +106,7 @@ struct Plan {
   // byte offsets into the workspace
   size_t off_scalars = 0, off_part = 0, off_zt = 0, off_lse = 0, off_tokloss = 0,
          off_g = 0, off_dhacc = 0, off_dhpart = 0, off_dwacc = 0, off_idx = 0, off_yc = 0,
-         off_hc = 0, off_bcnt = 0, total = 0;
+         off_hc = 0, off_bcnt = 0, off_ccnt = 0, total = 0;
 };
 
 // Builds the plan; returns false for invalid sizes or dtypes. A forward-only

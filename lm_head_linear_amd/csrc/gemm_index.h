@@ -129,11 +129,12 @@ inline int64_t nr_block(const Plan& p) { return p.nc * 32; }
 
 inline Launch nr_launch(const Plan& p, int64_t c, int which) {
   const int64_t t0 = c * p.nc, nt = nr_chunk_tokens(p, c);
+  const int hb = p.compact ? kBufHc : kBufH;      // the gathered rows
   if (which == 0)
-    return Launch{p.V, nt, p.H, kFormN, kFormN, kBufW, kBufH, 0, t0 * p.H,
+    return Launch{p.V, nt, p.H, kFormN, kFormN, kBufW, hb, 0, t0 * p.H,
                   Geom{p.H, p.V, p.H}, Geom{p.H, nt, p.H}};
   if (which == 1)
-    return Launch{p.V, p.H, nt, kFormT, kFormT, kBufG, kBufH, 0, t0 * p.H,
+    return Launch{p.V, p.H, nt, kFormT, kFormT, kBufG, hb, 0, t0 * p.H,
                   Geom{32, p.vp, nt, nr_block(p)}, Geom{p.H, p.H, nt}};
   return Launch{nt, p.H, p.V, kFormN, kFormT, kBufG, kBufW, 0, 0,
                 Geom{32, nt, p.V, nr_block(p)}, Geom{p.H, p.H, p.V}};

@@ -1781,22 +1781,29 @@ hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, cons
 
 namespace flce {
 
+// The no-recompute variant runs over the gathered tokens (the kept ones
+// first): token chunk c is gathered rows [c nc, c nc + nc), of which the
+// first ccnt[c] take part in the forward and the first ccnt[nch + c] in the
+// backward (device counts).
 hipError_t bf16_nr_forward_chunk(const Plan& p, const Args& a, int64_t c, const Launcher& L) {
   const int64_t t0 = c * p.nc, nt = gemm::nr_chunk_tokens(p, c);
   const gemm::Launch l = gemm::nr_launch(p, c, 0);
   uint16_t* probs = static_cast<uint16_t*>(a.g);
+  const int64_t* cf = a.ccnt + c;
+  constexpr int NF = gemm::kFormN;
   if (a.softcap > 0.f) {
-    EpiLseP<true> e{a.labels + t0, nt, p.V, a.ignore_index, a.softcap, 1.f / a.softcap, a.part,
+    EpiLseP<true> e{a.yc + t0, nt, p.V, a.ignore_index, a.softcap, 1.f / a.softcap, a.part,
                     p.ld_part, a.zt, probs, gemm::nr_block(p)};
-    return run_gemm<gemm::kFormN, gemm::kFormN>(l, a, e, kLseFwd, L);
+    return run_gemm<NF, NF, false, 1, false, kDynN>(l, a, e, kLseFwd, L, 0, 1, cf);
   }
-  EpiLseP<false> e{a.labels + t0, nt, p.V, a.ignore_index, 0.f, 0.f, a.part, p.ld_part, a.zt,
+  EpiLseP<false> e{a.yc + t0, nt, p.V, a.ignore_index, 0.f, 0.f, a.part, p.ld_part, a.zt,
                    probs, gemm::nr_block(p)};
-  return run_gemm<gemm::kFormN, gemm::kFormN>(l, a, e, kLseFwd, L);
+  return run_gemm<NF, NF, false, 1, false, kDynN>(l, a, e, kLseFwd, L, 0, 1, cf);
 }
 
 hipError_t bf16_nr_backward_chunk(const Plan& p, const Args& a, int64_t c, const Launcher& L) {
   const int64_t t0 = c * p.nc, nt = gemm::nr_chunk_tokens(p, c);
+  const int64_t* cb = a.ccnt + p.n_tok_chunks + c;     // the chunk's kept tokens
   uint16_t* g = static_cast<uint16_t*>(a.g);
   // 1) G in place of the probabilities
   const int64_t nb = (p.V + 31) / 32;
@@ -1804,50 +1811,48 @@ hipError_t bf16_nr_backward_chunk(const Plan& p, const Args& a, int64_t c, const
   const int64_t blk = gemm::nr_block(p);
   L.pre(kProbsToGrad);
   if (a.softcap > 0.f)
-    hipLaunchKernelGGL(k_probs_to_grad<true>, grid, dim3(256), 0, L.stream, g, blk, nt, nullptr,
-                       p.V, p.V, a.part, p.ld_part, a.lse, a.zt, a.labels + t0, a.ignore_index,
-                       a.sc, 1.f / a.softcap);
+    hipLaunchKernelGGL(k_probs_to_grad<true>, grid, dim3(256), 0, L.stream, g, blk, nt, cb, p.V,
+                       p.V, a.part, p.ld_part, a.lse, a.zt, a.yc + t0, a.ignore_index, a.sc,
+                       1.f / a.softcap);
   else
-    hipLaunchKernelGGL(k_probs_to_grad<false>, grid, dim3(256), 0, L.stream, g, blk, nt, nullptr,
-                       p.V, p.V, a.part, p.ld_part, a.lse, a.zt, a.labels + t0, a.ignore_index,
-                       a.sc, 0.f);
+    hipLaunchKernelGGL(k_probs_to_grad<false>, grid, dim3(256), 0, L.stream, g, blk, nt, cb, p.V,
+                       p.V, a.part, p.ld_part, a.lse, a.zt, a.yc + t0, a.ignore_index, a.sc, 0.f);
   L.post(kProbsToGrad);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // 2) dW (+)= G^T . h[chunk]; over several token chunks the sum is kept in
-  // float32 and rounded to bf16 once, at the last chunk
+  // 2) dW (+)= G^T . h[chunk] (K = the chunk's kept tokens); over several
+  // token chunks the sum is kept in float32 and rounded to bf16 once, at the
+  // last chunk. 3) dH[chunk] = G . W over the whole vocabulary, the rows
+  // stored at the tokens' original positions. Both in one grid, dH's tiles
+  // first, unless dH is split along K.
   uint16_t* dW = static_cast<uint16_t*>(a.dW);
+  uint16_t* dH = static_cast<uint16_t*>(a.dH);
+  const int32_t* rmap = a.idx + t0;
   const gemm::Launch lw = gemm::nr_launch(p, c, 1);
-  constexpr int T = gemm::kFormT;
-  if (!p.need_dw_acc) {
-    if (a.accumulate_dW)
-      err = run_gemm<T, T, true>(lw, a, EpiDW<true>{dW, p.H, 0, p.V}, kGemmDW, L);
-    else
-      err = run_gemm<T, T, true>(lw, a, EpiDW<false>{dW, p.H, 0, p.V}, kGemmDW, L);
-  } else if (c == 0) {
-    if (a.accumulate_dW)
-      err = run_gemm<T, T, true>(lw, a, EpiDWAcc<1, 2>{dW, a.dw_acc, p.H, p.V}, kGemmDW, L);
-    else
-      err = run_gemm<T, T, true>(lw, a, EpiDWAcc<0, 2>{dW, a.dw_acc, p.H, p.V}, kGemmDW, L);
-  } else if (c < p.n_tok_chunks - 1) {
-    err = run_gemm<T, T, true>(lw, a, EpiDWAcc<2, 2>{dW, a.dw_acc, p.H, p.V}, kGemmDW, L);
-  } else {
-    err = run_gemm<T, T, true>(lw, a, EpiDWAcc<2, 1>{dW, a.dw_acc, p.H, p.V}, kGemmDW, L);
-  }
-  if (err != hipSuccess) return err;
-  // 3) dH[chunk] = G . W over the whole vocabulary
-  uint16_t* dH = static_cast<uint16_t*>(a.dH) + t0 * p.H;
   const gemm::Launch lh = gemm::nr_launch(p, c, 2);
-  if (p.dh_kseg) {
-    // few output tiles: split K, then add the segments up in a fixed order
-    const int64_t segs = (lh.K + p.dh_kseg - 1) / p.dh_kseg;
-    err = run_gemm<gemm::kFormN, gemm::kFormT, true, 1, true>(
-        lh, a, EpiDHPart{a.dh_part, nt, p.H, nt * p.H}, kGemmDH, L, p.dh_kseg, segs);
-    if (err != hipSuccess) return err;
-    return launch_dh_reduce(a.dh_part, segs, nt * p.H, nullptr, nullptr, dH, L, p.H);
+  constexpr int T = gemm::kFormT, NF = gemm::kFormN;
+  const EpiDH<true, true> edh{dH, nullptr, nt, p.H, rmap};
+  auto dw = [&](auto epi) {
+    if (p.dh_kseg) return run_gemm<T, T, true, 1, false, kDynK>(lw, a, epi, kGemmDW, L, 0, 1, cb);
+    return run_gemm_pair<NF, T, kDynM, T, T, kDynK>(lh, edh, lw, epi, a, kGemmDWDH, L, cb);
+  };
+  if (!p.need_dw_acc) {
+    err = a.accumulate_dW ? dw(EpiDW<true>{dW, p.H, 0, p.V}) : dw(EpiDW<false>{dW, p.H, 0, p.V});
+  } else if (c == 0) {
+    err = a.accumulate_dW ? dw(EpiDWAcc<1, 2>{dW, a.dw_acc, p.H, p.V})
+                          : dw(EpiDWAcc<0, 2>{dW, a.dw_acc, p.H, p.V});
+  } else if (c < p.n_tok_chunks - 1) {
+    err = dw(EpiDWAcc<2, 2>{dW, a.dw_acc, p.H, p.V});
+  } else {
+    err = dw(EpiDWAcc<2, 1>{dW, a.dw_acc, p.H, p.V});
   }
-  return run_gemm<gemm::kFormN, gemm::kFormT, true>(lh, a, EpiDH<true, true>{dH, nullptr, nt, p.H},
-                                                    kGemmDH, L);
+  if (err != hipSuccess || !p.dh_kseg) return err;
+  // few dH output tiles: split K, then add the segments up in a fixed order
+  const int64_t segs = (lh.K + p.dh_kseg - 1) / p.dh_kseg;
+  err = run_gemm<NF, T, true, 1, true, kDynM>(
+      lh, a, EpiDHPart{a.dh_part, nt, p.H, nt * p.H}, kGemmDH, L, p.dh_kseg, segs, cb);
+  if (err != hipSuccess) return err;
+  return launch_dh_reduce(a.dh_part, segs, nt * p.H, nullptr, nullptr, dH, L, p.H, cb, rmap);
 }
 
 }  // namespace flce

@@ -220,6 +220,19 @@ __global__ __launch_bounds__(256) void k_gather_rows(const uint4* __restrict__ h
   }
 }
 
+// Live tokens of each chunk of nc gathered rows: cnt[c] for the forward (the
+// first `fwd` gathered rows: the kept ones, or all), cnt[nch + c] for the
+// backward (the kept ones).
+__global__ void k_chunk_counts(const Scalars* __restrict__ sc, int64_t N, int all, int64_t nc,
+                               int64_t nch, int64_t* __restrict__ cnt) {
+  const int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (c >= nch) return;
+  const int64_t kept = sc->n_valid, fwd = all ? N : kept;
+  auto clamp = [&](int64_t x) { return x < 0 ? int64_t(0) : (x > nc ? nc : x); };
+  cnt[c] = clamp(fwd - c * nc);
+  cnt[nch + c] = clamp(kept - c * nc);
+}
+
 // Zero rows of dH (16-byte pieces, h8 per row) whose token is ignored: the
 // compact backward never writes them.
 __global__ __launch_bounds__(256) void k_zero_ignored_rows(const int64_t* __restrict__ labels,
@@ -255,6 +268,24 @@ hipError_t launch_merge(const Plan& p, const Args& a, int64_t t0, int64_t nt, co
                      0, L.stream, a.part, p.n_voc_tiles, p.ld_part, a.zt, a.labels + t0, nt,
                      nullptr, p.V, a.ignore_index, a.lse, a.lse_out ? a.lse_out + t0 : nullptr,
                      a.tok_loss + t0, nullptr);
+  L.post(kLseMerge);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_counts(const Plan& p, const Args& a, bool all_rows, const Launcher& L) {
+  L.pre(kGather);
+  hipLaunchKernelGGL(k_chunk_counts, dim3(unsigned((p.n_tok_chunks + 63) / 64)), dim3(64), 0,
+                     L.stream, a.sc, p.N, all_rows ? 1 : 0, p.nc, p.n_tok_chunks, a.ccnt);
+  L.post(kGather);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_gathered(const Plan& p, const Args& a, int64_t t0, int64_t nt,
+                                 const int64_t* count, const Launcher& L) {
+  L.pre(kLseMerge);
+  hipLaunchKernelGGL(k_lse_merge, dim3(unsigned((nt + kMergeTokens - 1) / kMergeTokens)), dim3(256),
+                     0, L.stream, a.part, p.n_voc_tiles, p.ld_part, a.zt, a.yc + t0, nt, count,
+                     p.V, a.ignore_index, a.lse, a.lse_out, a.tok_loss, a.idx + t0);
   L.post(kLseMerge);
   return hipGetLastError();
 }

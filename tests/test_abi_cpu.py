@@ -401,7 +401,8 @@ def test_nr_plan(lib):
     assert lib.flce_token_chunk_nr(8192, 4096, 131072, 1, 100000) == 8192
     # the chunk's probabilities dominate the workspace: nc x roundup(V, 256) x 2 bytes,
     # plus the float32 partial products of a split-K dH when its output has few tiles,
-    # plus, with several token chunks, the float32 [V][H] running sum of dW
+    # plus, with several token chunks, the float32 [V][H] running sum of dW, plus the
+    # gathered tokens (their rows, positions and labels)
     for N, H, V, tc in [(8192, 4096, 131072, 0), (8192, 3584, 256000, 2048), (600, 64, 1000, 256),
                         (16384, 4096, 131072, 512), (16384, 4096, 131072, 0)]:
         nc = lib.flce_token_chunk_nr(N, H, V, 1, tc)
@@ -410,8 +411,9 @@ def test_nr_plan(lib):
         segs = _dh_segments(nc, H, V)
         split = segs * nc * H * 4 if segs > 1 else 0
         acc = V * H * 4 if nc < N else 0
-        lo = nc * vp * 2 + split + acc
-        assert lo <= ws <= lo + (vp // 256) * nc * 8 + 4 * nc * 4 + 8 * N + 4096
+        gather = N * H * 2                        # the gathered hidden rows
+        lo = nc * vp * 2 + split + acc + gather
+        assert lo <= ws <= lo + (vp // 256) * nc * 8 + 4 * nc * 4 + 8 * N + 12 * N + 8192
     assert lib.flce_workspace_size_nr(64, 64, 128, 0, 0) == 0        # float32: not offered
     assert lib.flce_workspace_size_nr(-1, 64, 128, 1, 0) == 0
 
