@@ -79,7 +79,7 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
       off = align256(off + size_t(q.dh_segs) * size_t(N) * H * sizeof(float));
     }
     // the tokens gathered, the non-ignored ones first (see Plan::compact)
-    q.compact = dtype == FLCE_BF16 && q.g_parts == 1 && gather != 0;
+    q.compact = dtype == FLCE_BF16 && gather != 0;
     if (q.compact) {
       q.n_gather_blocks = ceil_div(N, kGatherBlock);
       q.off_idx = off;  off = align256(off + size_t(N) * sizeof(int32_t));

@@ -85,7 +85,7 @@ struct Plan {
   // No-recompute variant with several token chunks: dW is added up over the
   // chunks in a float32 [V][H] running sum at off_dwacc, rounded to bf16 once.
   bool need_dw_acc = false;
-  // bf16 gradients of the recompute path: the tokens are gathered first,
+  // bf16 inputs (bf16 or float32 gradients): the tokens are gathered first,
   // the non-ignored ones in order and then the ignored ones (a permutation),
   // and the call runs over the gathered order: the backward over the first
   // n_valid (the kept tokens; an ignored token's G is zero, so its recompute,

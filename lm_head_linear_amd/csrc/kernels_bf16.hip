@@ -1407,8 +1407,9 @@ struct EpiDWAcc {
 
 // ---- dH epilogue: accumulate over vocabulary chunks in a fixed order ------
 // FIRST: no running sum to add; LAST: store bf16 dH instead of the float32
-// running sum.
-template <bool FIRST, bool LAST>
+// running sum. MAPACC: the running sum is the float32 dH output itself, so
+// its rows, too, are the tokens' original positions (row_map).
+template <bool FIRST, bool LAST, bool MAPACC = false>
 struct EpiDH {
   uint16_t* dH;
   float* acc32;  // [N][H] float32 running sum (unused with a single chunk)
@@ -1426,8 +1427,9 @@ struct EpiDH {
       for (int q = 0; q < 16; ++q) {
         const int idx = q * 64 + lane, row = idx >> 5, c4 = idx & 31;
         const int64_t m = r0 + i * 32 + row, n = c0 + 4 * c4;
+        const int64_t ma = MAPACC ? int64_t(e.row_map[m < e.N ? m : 0]) : m;
         prev[i & 1][q] = (m < e.N && n < e.H)
-                             ? *reinterpret_cast<const float4*>(e.acc32 + m * e.H + n)
+                             ? *reinterpret_cast<const float4*>(e.acc32 + ma * e.H + n)
                              : make_float4(0.f, 0.f, 0.f, 0.f);
       }
     }
@@ -1443,7 +1445,8 @@ struct EpiDH {
         *reinterpret_cast<uint2*>(e.dH + mo * e.H + n) =
             make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
       } else {
-        *reinterpret_cast<float4*>(e.acc32 + m * e.H + n) = v;
+        const int64_t ma = MAPACC ? int64_t(e.row_map[m]) : m;
+        *reinterpret_cast<float4*>(e.acc32 + ma * e.H + n) = v;
       }
     }
   };
@@ -1621,7 +1624,7 @@ hipError_t bf16_forward_out(const Plan& p, const Args& a, const Launcher& L) {
   const int64_t* nv = (p.compact && !a.lse_out) ? &a.sc->n_valid : nullptr;
   constexpr int NF = gemm::kFormN;
   if constexpr (OUT == kNoLogits) {
-    if (p.compact && p.backward) {
+    if (p.compact && p.backward && p.g_parts == 1) {
       // the first backward chunk's probabilities are kept (its G is formed
       // from them, without recomputing its logits)
       auto run = [&](auto e) {
@@ -1664,39 +1667,43 @@ hipError_t bf16_forward(const Plan& p, const Args& a, const Launcher& L) {
 // chunk in a fixed order.
 hipError_t bf16_backward_chunk_f32grad(const Plan& p, const Args& a, int64_t chunk,
                                        const Launcher& L) {
+  // over the kept tokens, gathered in order (their count n_valid on the
+  // device); dH is its own float32 running sum at the tokens' positions
+  if (!p.compact) return hipErrorInvalidValue;
   const int64_t v0 = chunk * p.vchunk;
   const int64_t vcur = gemm::chunk_rows(p, chunk);
   uint16_t* g = static_cast<uint16_t*>(a.g);
   const int64_t lo_off = p.vchunk * p.ldg;
+  const int64_t* nv = &a.sc->n_valid;
+  constexpr int NF = gemm::kFormN, TF = gemm::kFormT;
+  const gemm::Launch lg = gemm::backward_launch(p, chunk, 0);
   hipError_t err;
   if (a.softcap > 0.f) {
-    EpiGrad<true, true> eg{a.labels, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
-                           gemm::g_block(p), a.softcap, 1.f / a.softcap, g, lo_off};
-    err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
-                                               kGradLogits, L);
+    const EpiGrad<true, true> eg{a.yc, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
+                                 gemm::g_block(p), a.softcap, 1.f / a.softcap, g, lo_off};
+    err = run_gemm<NF, NF, false, 1, false, kDynN>(lg, a, eg, kGradLogits, L, 0, 1, nv);
   } else {
-    EpiGrad<false, true> eg{a.labels, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
-                            gemm::g_block(p), 0.f, 0.f, g, lo_off};
-    err = run_gemm<gemm::kFormN, gemm::kFormN>(gemm::backward_launch(p, chunk, 0), a, eg,
-                                               kGradLogits, L);
+    const EpiGrad<false, true> eg{a.yc, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
+                                  gemm::g_block(p), 0.f, 0.f, g, lo_off};
+    err = run_gemm<NF, NF, false, 1, false, kDynN>(lg, a, eg, kGradLogits, L, 0, 1, nv);
   }
   if (err != hipSuccess) return err;
   float* dW = static_cast<float*>(a.dW);
   const gemm::Launch lw = gemm::backward_launch(p, chunk, 1, 0);
   if (!a.accumulate_dW)
-    err = run_gemm<gemm::kFormT, gemm::kFormT, true, 2>(lw, a, EpiDW32<false>{dW, p.H, v0, vcur},
-                                                        kGemmDW, L, lo_off);
+    err = run_gemm<TF, TF, true, 2, false, kDynK>(lw, a, EpiDW32<false>{dW, p.H, v0, vcur},
+                                                  kGemmDW, L, lo_off, 1, nv);
   else
-    err = run_gemm<gemm::kFormT, gemm::kFormT, true, 2>(lw, a, EpiDW32<true>{dW, p.H, v0, vcur},
-                                                        kGemmDW, L, lo_off);
+    err = run_gemm<TF, TF, true, 2, false, kDynK>(lw, a, EpiDW32<true>{dW, p.H, v0, vcur},
+                                                  kGemmDW, L, lo_off, 1, nv);
   if (err != hipSuccess) return err;
   float* dH = static_cast<float*>(a.dH);
   const gemm::Launch lh = gemm::backward_launch(p, chunk, 2, 0);
   if (chunk == 0)
-    return run_gemm<gemm::kFormN, gemm::kFormT, true, 2>(
-        lh, a, EpiDH<true, false>{nullptr, dH, p.N, p.H}, kGemmDH, L, lo_off);
-  return run_gemm<gemm::kFormN, gemm::kFormT, true, 2>(
-      lh, a, EpiDH<false, false>{nullptr, dH, p.N, p.H}, kGemmDH, L, lo_off);
+    return run_gemm<NF, TF, true, 2, false, kDynM>(
+        lh, a, EpiDH<true, false, true>{nullptr, dH, p.N, p.H, a.idx}, kGemmDH, L, lo_off, 1, nv);
+  return run_gemm<NF, TF, true, 2, false, kDynM>(
+      lh, a, EpiDH<false, false, true>{nullptr, dH, p.N, p.H, a.idx}, kGemmDH, L, lo_off, 1, nv);
 }
 
 hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, const Launcher& L) {

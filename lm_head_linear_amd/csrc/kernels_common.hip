@@ -233,7 +233,8 @@ __global__ void k_chunk_counts(const Scalars* __restrict__ sc, int64_t N, int al
   cnt[nch + c] = clamp(kept - c * nc);
 }
 
-// Zero rows of dH (16-byte pieces, h8 per row) whose token is ignored: the
+// Zero rows of dH (16-byte pieces, h8 per row: bf16 or float32) whose token
+// is ignored: the
 // compact backward never writes them.
 __global__ __launch_bounds__(256) void k_zero_ignored_rows(const int64_t* __restrict__ labels,
                                                            int64_t N, int64_t ignore_index,
@@ -349,9 +350,13 @@ hipError_t launch_gather(const Plan& p, const Args& a, bool all_rows, const Laun
   hipLaunchKernelGGL(k_gather_rows, dim3(unsigned(blocks)), dim3(256), 0, L.stream,
                      static_cast<const uint4*>(a.h), h8, a.idx,
                      all_rows ? nullptr : &a.sc->n_valid, p.N, static_cast<uint4*>(a.hc));
-  if (a.dH)
-    hipLaunchKernelGGL(k_zero_ignored_rows, dim3(unsigned(blocks)), dim3(256), 0, L.stream,
-                       a.labels, p.N, a.ignore_index, h8, static_cast<uint4*>(a.dH));
+  if (a.dH) {
+    const int64_t g16 = p.H * int64_t(p.grad_elem) / 16;   // 16-byte pieces per dH row
+    int64_t zb = (p.N * g16 + 255) / 256;
+    if (zb > 4096) zb = 4096;
+    hipLaunchKernelGGL(k_zero_ignored_rows, dim3(unsigned(zb)), dim3(256), 0, L.stream,
+                       a.labels, p.N, a.ignore_index, g16, static_cast<uint4*>(a.dH));
+  }
   L.post(kGather);
   return hipGetLastError();
 }

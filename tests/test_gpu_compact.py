@@ -4,7 +4,8 @@ ignore patterns that stress the gather: masked prefixes of every sequence,
 runs across 256-token tile edges, a single kept token, ignored first and last
 tokens, over several backward chunks and with a split-K dH; the rows of
 ignored tokens in dH are exactly zero even when dH held NaN before the call;
-an all-ignored call leaves an accumulated dW bit for bit unchanged."""
+an all-ignored call leaves an accumulated dW bit for bit unchanged; the same
+patterns with float32 gradients."""
 import numpy as np
 import pytest
 import torch
@@ -70,6 +71,32 @@ def test_compact_patterns(kind, N, H, V, chunk, vchunk):
     g = gu.run_gpu(w, dH=dH)
     r = gu.run_oracle(w)
     gu.assert_parity(w, g, r)              # includes: ignored rows of dH exactly 0
+
+
+@pytest.mark.parametrize("kind", ["tile_edges", "one_kept", "ends"])
+@pytest.mark.parametrize("N,H,V,chunk", [
+    (1100, 264, 3000, 1024),    # 3 chunks, ragged everywhere
+    (777, 128, 1500, 256),      # many chunks
+])
+def test_compact_patterns_f32grad(kind, N, H, V, chunk, vchunk):
+    """float32 gradients over the gathered tokens: dH is its own float32
+    running sum at the tokens' original rows."""
+    vchunk(chunk)
+    rng = np.random.default_rng(N + V + 1)
+    w = fi.make_custom(N, H, V, dtype=torch.bfloat16, seed=N + H + 1, ignore_frac=0.0,
+                       softcap=30.0 if kind == "ends" else 0.0, reduction="sum")
+    w.labels.view(-1)[torch.from_numpy(_mask(N, kind, rng))] = fi.IGNORE_INDEX
+    dev = gu.device()
+    dH = torch.full((N, H), float("nan"), dtype=torch.float32, device=dev)
+    g = gu.run_gpu(w, dH=dH, grad_dtype=torch.float32)
+    r = gu.run_oracle(w)
+    assert g["status"] == 0 and g["num_tokens"] == r.num_tokens
+    gu.assert_loss(g["loss"], r.loss64)
+    tol = gu.GRAD_TOL[torch.float32]
+    gu.assert_grad("dH", g["dH"], r.dH, tol)
+    gu.assert_grad("dW", g["dW"], r.dW, tol)
+    ign = torch.from_numpy(np.flatnonzero(w.labels.reshape(-1).numpy() == w.ignore_index))
+    assert bool((g["dH"][ign.to(dev)] == 0).all())
 
 
 def test_all_ignored_keeps_accumulated_dW(vchunk):
