@@ -74,8 +74,10 @@ typedef enum {
  * per-tile log-sum-exp partials, the per-token lse and target logits, one
  * vocabulary chunk of the logit gradient, (bf16, several chunks) a float32
  * dH accumulator and (bf16, N*H under 128 tiles of 256 x 256) up to 8 float32
- * N x H partial products of a dH split along the vocabulary. Never O(N*V):
- * the chunk is sized to at most ~256 MiB.
+ * N x H partial products of a dH split along the vocabulary. Never O(N*V)
+ * beyond a fixed fraction: the chunk holds up to 2^27 elements of G, or up to
+ * N*V*4/16 bytes when that is more (at most 2^29 elements), and the
+ * vocabulary is split into chunks of equal size.
  * Returns 0 for invalid sizes (N < 0, H <= 0, V <= 0, unknown dtype).
  * Pure host arithmetic; callable without a GPU. No page defines this call:
  * it is this library's own addition, so that the caller owns every byte of

@@ -45,12 +45,21 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
   q.n_voc_tiles = ceil_div(V, q.tile);
   q.ld_part = round_up(N > 0 ? N : 1, q.tile);
   q.ldg = round_up(N > 0 ? N : 1, 8);
-  // Backward chunk: at most kChunkElems elements of G^T, a multiple of the
-  // tile, at least one tile, at most the (tile-rounded) vocabulary.
+  // Backward chunk: a multiple of the tile, at least one tile, at most the
+  // (tile-rounded) vocabulary, with G^T's elements (both parts) within the
+  // budget; the vocabulary is then split into chunks of equal size (the last
+  // one shorter by less than a tile per chunk).
   int64_t vmax = round_up(V, q.tile);
   int64_t vc = env_vchunk();
-  if (vc <= 0) vc = (kChunkElems / q.g_parts / (N > 0 ? q.ldg : 1)) / q.tile * q.tile;
-  else vc = round_up(vc, q.tile);
+  if (vc <= 0) {
+    int64_t budget = N / 4 * V / q.elem;       // N V 4 / 16 bytes
+    if (budget < kChunkElems) budget = kChunkElems;
+    if (budget > kMaxChunkElems) budget = kMaxChunkElems;
+    vc = (budget / q.g_parts / (N > 0 ? q.ldg : 1)) / q.tile * q.tile;
+    if (vc >= q.tile && vc < vmax) vc = round_up(ceil_div(V, ceil_div(V, vc)), q.tile);
+  } else {
+    vc = round_up(vc, q.tile);
+  }
   if (vc < q.tile) vc = q.tile;
   if (vc > vmax) vc = vmax;
   q.vchunk = vc;

@@ -14,8 +14,12 @@ constexpr int64_t kTileBF16 = 256;
 constexpr int64_t kGatherBlock = 1024;
 // Tile edge of the float32 kernels.
 constexpr int64_t kTileF32 = 64;
-// Upper bound on the elements of one chunk of the logit gradient G^T.
+// Elements of one chunk of the logit gradient G^T: up to kChunkElems, or up
+// to a sixteenth of the bytes of float32 logits (N V 4 / 16) when that is
+// more, but never more than kMaxChunkElems. Larger chunks keep more of the
+// forward's probabilities for the first chunk and recompute less.
 constexpr int64_t kChunkElems = int64_t(1) << 27;
+constexpr int64_t kMaxChunkElems = int64_t(1) << 29;
 // The bf16 GEMMs address an operand tile with 32-bit byte offsets from the
 // tile base: up to 255 rows of a K-contiguous operand, 2 * ld bytes apart.
 // ld (H, or the no-recompute G row length) must keep that below 2^32.

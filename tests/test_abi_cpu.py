@@ -89,12 +89,23 @@ def test_workspace_invalid_sizes(lib):
 
 
 def test_vocab_chunk_plan(lib):
-    assert lib.flce_vocab_chunk(8192, 4096, 131072, 1) == 16384
-    assert lib.flce_vocab_chunk(16384, 4096, 131072, 1) == 8192
-    assert lib.flce_vocab_chunk(2048, 1024, 32000, 1) == 32000
+    """G's chunk takes up to 2^27 elements, or N V 4 / 16 bytes when that is
+    more, and the vocabulary is split into equal chunks (a multiple of the
+    tile each)."""
+    assert lib.flce_vocab_chunk(8192, 4096, 131072, 1) == 16384      # 2^27 elements
+    assert lib.flce_vocab_chunk(16384, 4096, 131072, 1) == 16384     # N V / 8 elements
+    assert lib.flce_vocab_chunk(8192, 3584, 256000, 1) == 32000      # 8 chunks of 125 tiles
+    assert lib.flce_vocab_chunk(2048, 1024, 32000, 1) == 32000       # one chunk
     assert lib.flce_vocab_chunk(32, 64, 1024, 0) == 1024
-    c = lib.flce_vocab_chunk(8192, 3584, 256000, 1)
-    assert c % 256 == 0 and 256 <= c <= 256000
+    # balanced: 3 chunks of 2^27 / 8192 = 16384 rows would leave a short last
+    # one; 40000 rows go in 3 chunks of 13568
+    assert lib.flce_vocab_chunk(8192, 1024, 40000, 1) == 13568
+    for N, V in [(8192, 131072), (8192, 256000), (16384, 131072), (4000, 50257), (777, 1500)]:
+        c = lib.flce_vocab_chunk(N, 1024, V, 1)
+        n = -(-V // c)
+        assert c % 256 == 0 and 256 <= c <= -(-V // 256) * 256
+        assert c * ((N + 7) // 8 * 8) <= max(1 << 27, N // 4 * V // 2)
+        assert V - (n - 1) * c > 0 and c - (V - (n - 1) * c) < 256 * n
 
 
 # -------------------------------------------------------------- check_args
@@ -334,7 +345,7 @@ def test_f32grad_plan(lib):
     """G kept as a hi + lo pair: half the vocabulary rows per chunk, no dH
     accumulator (dH is float32 itself), still within N*V*4/8."""
     for N, H, V in [(8192, 4096, 131072), (8192, 3584, 256000), (16384, 4096, 131072)]:
-        assert lib.flce_vocab_chunk_ex(N, H, V, 1, 0) == lib.flce_vocab_chunk(N, H, V, 1) // 2
+        assert lib.flce_vocab_chunk_ex(N, H, V, 1, 0) <= lib.flce_vocab_chunk(N, H, V, 1) // 2 + 256
         ws = lib.flce_workspace_size_ex(N, H, V, 1, 0)
         assert 0 < ws <= N * V * 4 // 8
     # same-dtype calls are exactly the plain entry points
