@@ -59,7 +59,7 @@ typedef enum { FLCE_SUM = 0, FLCE_MEAN = 1 } flce_reduction_t;
 typedef enum {
   FLCE_OK = 0,
   FLCE_ERR_ARG = 1,          /* invalid argument (shape, pointer, option)   */
-  FLCE_ERR_UNSUPPORTED = 2,  /* valid but not supported (alignment, H%8)    */
+  FLCE_ERR_UNSUPPORTED = 2,  /* valid but not supported (alignment, shape)  */
   FLCE_ERR_WORKSPACE = 3,    /* workspace missing, misaligned or too small  */
   FLCE_ERR_HIP = 4,          /* a HIP runtime call or launch failed         */
   FLCE_ERR_LABEL = 5,        /* device-detected: a non-ignored label is
@@ -99,8 +99,16 @@ size_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype);
  *                        num_label_tokens > 0 with 'mean'; an output (dH,
  *                        dW) overlapping an input matrix (h, W) or the other
  *                        output.
- *   FLCE_ERR_UNSUPPORTED bf16 with H % 8 != 0 or a matrix pointer not 16-byte
+ *   FLCE_ERR_UNSUPPORTED a bf16 matrix pointer (h, W, dH, dW) not 16-byte
  *                        aligned.
+ * Any H > 0 is accepted (the NeMo linear_ce page, "API", puts no limit on the
+ * hidden size). The kernels load and store whole 16-byte runs of a bf16 row,
+ * so with bf16 inputs and H % 8 != 0 the call runs at the width rounded up to
+ * 8 on copies in the workspace: W and the gathered hidden rows zero-padded,
+ * dW (from the caller's one when accumulate_dW) and dH computed at that
+ * width and copied out to the caller's H columns. The results equal those of
+ * the same call on inputs the caller padded with zeros; the workspace grows
+ * by the padded W, dW and dH (flce_workspace_size counts them).
  *   FLCE_ERR_WORKSPACE   workspace NULL, not 256-byte aligned, or
  *                        workspace_bytes < flce_workspace_size(...).
  */
@@ -164,8 +172,8 @@ int flce_forward_backward(const void* h, const void* W, const int64_t* labels,
  * G_lo = bf16(G - G_hi)), about 16 significant bits, and each gradient GEMM
  * runs once per part in a fixed order: twice the dW/dH work of the bf16
  * call. dtype FLCE_F32 with grad_dtype FLCE_BF16 is FLCE_ERR_UNSUPPORTED.
- * Float32 gradients need the matrix pointers dH, dW 16-byte aligned and
- * H % 8 == 0 like the bf16 ones. The workspace is
+ * Float32 gradients need the matrix pointers dH, dW 16-byte aligned like
+ * the bf16 ones, and any H is padded the same way. The workspace is
  * flce_workspace_size_ex(N, H, V, dtype, grad_dtype) bytes and
  * flce_vocab_chunk_ex gives the vocabulary chunk (half the bf16 call's).
  */
@@ -301,6 +309,8 @@ int flce_forward(const void* h, const void* W, const int64_t* labels, int64_t N,
  *          call's contents (the kernels write everything they read back), so
  *          calls that overlap on one GPU (two streams, or two host threads)
  *          race: the caller must serialise them.
+ * Shapes   it reads h in place (no gather, to keep its scratch small): bf16
+ *          inputs with H % 8 != 0 are FLCE_ERR_UNSUPPORTED.
  * Everything else (parameters, outputs, edge cases, errors) as in
  * flce_forward, whose results it reproduces bit for bit (the gather changes
  * no value, and the loss sums the per-token losses by original position).
@@ -348,6 +358,9 @@ int flce_forward_logits_check_args(const void* h, const void* W, const int64_t* 
  *         (FLCE_BF16). Elements v in [V, ld_logits) are not written. Rows are
  *         stored in 16-byte runs when logits and ld_logits keep every run
  *         16-byte aligned, element by element otherwise.
+ * Shapes  the logits come out in the tokens' order, so this entry reads h
+ *         in place (no gather): bf16 inputs with H % 8 != 0 are
+ *         FLCE_ERR_UNSUPPORTED here.
  * Everything else as in flce_forward, with the same workspace
  * (flce_forward_workspace_size): *loss, *num_tokens, lse_out and *status are
  * bit-identical to what flce_forward returns on the same inputs. Cost: the

@@ -58,7 +58,7 @@ void prof_after(int kind, hipStream_t s) {
 const char* kKindNames[flce::kNumKinds] = {"label_scan", "lse_fwd_gemm", "lse_merge",
                                            "loss_final", "grad_logits_gemm", "dW_gemm",
                                            "dH_gemm", "fill", "probs_to_grad", "dH_reduce",
-                                           "gather", "dH_dW_gemm"};
+                                           "gather", "dH_dW_gemm", "pad_copy"};
 
 // ---- scratch of flce_forward_noalloc ---------------------------------------
 // One copy on every GPU the library runs on, held until the process ends. In
@@ -103,6 +103,37 @@ hipError_t scratch_address(hipStream_t stream, void** out) {
   return hipSuccess;
 }
 
+// A call whose bf16 rows are padded (Plan::pad_h) runs at the padded width on
+// the workspace's copies: W padded, dW padded from the caller's when it is
+// added to, dH and dW written there and copied out at the end. The gather
+// pads the hidden rows it copies.
+hipError_t pad_inputs(const flce::Plan& p, flce::Args& a, char* ws, bool backward,
+                      const flce::Launcher& L) {
+  if (!p.pad_h) return hipSuccess;
+  void* wp = ws + p.off_wp;
+  hipError_t e = flce::launch_copy_rows(a.W, p.h_in, wp, p.H, p.V, p.h_in, p.H, p.elem, L);
+  a.W = wp;
+  a.H = p.H;
+  if (!backward) return e;
+  void* dwp = ws + p.off_dwp;
+  if (e == hipSuccess && a.accumulate_dW)
+    e = flce::launch_copy_rows(a.dW, p.h_in, dwp, p.H, p.V, p.h_in, p.H, p.grad_elem, L);
+  a.dW = dwp;
+  a.dH = ws + p.off_dhp;
+  return e;
+}
+
+hipError_t crop_outputs(const flce::Plan& p, const char* ws, void* dH, void* dW,
+                        const flce::Launcher& L) {
+  if (!p.pad_h) return hipSuccess;
+  hipError_t e = flce::launch_copy_rows(ws + p.off_dwp, p.H, dW, p.h_in, p.V, p.h_in, p.h_in,
+                                        p.grad_elem, L);
+  if (e == hipSuccess)
+    e = flce::launch_copy_rows(ws + p.off_dhp, p.H, dH, p.h_in, p.N, p.h_in, p.h_in,
+                               p.grad_elem, L);
+  return e;
+}
+
 // The no-recompute variant (arguments already checked): token chunk by chunk,
 // the forward keeps the probabilities, the chunk's merge gives its lse, G is
 // formed in place, then dW (added over the chunks) and the chunk's dH.
@@ -145,7 +176,8 @@ int run_nr(const void* h, const void* W, const int64_t* labels, int64_t N, int64
   a.bcnt = reinterpret_cast<int32_t*>(ws + p.off_bcnt);
   a.ccnt = reinterpret_cast<int64_t*>(ws + p.off_ccnt);
   a.hc = ws + p.off_hc;
-  e = flce::launch_label_scan(p, a, L);
+  e = pad_inputs(p, a, ws, true, L);
+  if (e == hipSuccess) e = flce::launch_label_scan(p, a, L);
   // the tokens gathered, the kept ones first; the chunks run over that order
   // (the ignored tokens only for their lse, when it is asked for)
   const bool all_rows = lse_out != nullptr;
@@ -158,6 +190,7 @@ int run_nr(const void* h, const void* W, const int64_t* labels, int64_t N, int64
     if (e == hipSuccess) e = flce::bf16_nr_backward_chunk(p, a, c, L);
   }
   if (e == hipSuccess) e = flce::launch_loss_final(p, a, L);
+  if (e == hipSuccess) e = crop_outputs(p, ws, dH, dW, L);
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
@@ -210,7 +243,8 @@ int run(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t 
   }
 
   const bool bf16 = dtype == FLCE_BF16;
-  e = flce::launch_label_scan(p, a, L);
+  e = pad_inputs(p, a, ws, backward, L);
+  if (e == hipSuccess) e = flce::launch_label_scan(p, a, L);
   // a compact plan gathers the tokens first, the kept ones in front; the
   // forward then skips the ignored ones unless their lse is asked for
   if (e == hipSuccess && p.compact) e = flce::launch_gather(p, a, lse_out != nullptr, L);
@@ -218,6 +252,7 @@ int run(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t 
   if (e == hipSuccess) e = flce::launch_merge_and_loss(p, a, L);
   for (int64_t c = 0; backward && e == hipSuccess && c < p.n_chunks; ++c)
     e = bf16 ? flce::bf16_backward_chunk(p, a, c, L) : flce::f32_backward_chunk(p, a, c, L);
+  if (e == hipSuccess && backward) e = crop_outputs(p, ws, dH, dW, L);
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
@@ -331,7 +366,9 @@ int flce_forward_noalloc(const void* h, const void* W, const int64_t* labels, in
                                    lse_out);
   if (st != FLCE_OK) return st;
   // the forward without the token gather (its scratch is the partials and
-  // per-token arrays alone), bit-identical to flce_forward's results
+  // per-token arrays alone), bit-identical to flce_forward's results; it
+  // reads h in place, so bf16 rows must be whole 16-byte runs
+  if (dtype == FLCE_BF16 && H % 8 != 0) return FLCE_ERR_UNSUPPORTED;
   flce::Plan p;
   if (!flce::make_plan(N, H, V, dtype, &p, false, -1, 0)) return FLCE_ERR_ARG;
   if (p.total > FLCE_NOALLOC_SCRATCH_BYTES) return FLCE_ERR_SCRATCH;

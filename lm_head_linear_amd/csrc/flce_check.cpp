@@ -13,6 +13,18 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// The padded buffers of a Plan::pad_h call at the padded width: W, and with
+// gradients dW and dH.
+size_t carve_pad(Plan& q, size_t off, bool backward) {
+  if (!q.pad_h) return off;
+  q.off_wp = off;  off = align256(off + size_t(q.V) * q.H * q.elem);
+  if (backward) {
+    q.off_dwp = off; off = align256(off + size_t(q.V) * q.H * q.grad_elem);
+    q.off_dhp = off; off = align256(off + size_t(q.N) * q.H * q.grad_elem);
+  }
+  return off;
+}
+
 // Optional override of the backward vocabulary chunk (rows of W), for tuning
 // and for tests of the multi-chunk path; 0 = automatic. Read on every plan,
 // so flce_workspace_size and flce_forward_backward must see the same value
@@ -36,6 +48,12 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
   // Keep every size product far from int64 overflow.
   if (N > (int64_t(1) << 31) || H > (int64_t(1) << 24) || V > (int64_t(1) << 31)) return false;
   Plan q;
+  q.h_in = H;
+  if (dtype == FLCE_BF16 && H % 8 != 0) {
+    if (gather == 0) return false;              // h is read in place: 16-byte rows
+    q.pad_h = true;
+    H = round_up(H, 8);
+  }
   q.N = N; q.H = H; q.V = V; q.dtype = dtype; q.grad_dtype = grad_dtype;
   q.tile = dtype == FLCE_BF16 ? kTileBF16 : kTileF32;
   q.elem = dtype == FLCE_BF16 ? 2 : 4;
@@ -96,6 +114,7 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
       q.off_bcnt = off; off = align256(off + size_t(q.n_gather_blocks) * sizeof(int32_t));
       q.off_hc = off;   off = align256(off + size_t(N) * H * q.elem);
     }
+    off = carve_pad(q, off, backward);
   }
   q.total = off;
   *p = q;
@@ -106,8 +125,13 @@ bool make_plan_nr(int64_t N, int64_t H, int64_t V, int dtype, int64_t token_chun
   if (dtype != FLCE_BF16) return false;
   if (token_chunk < 0) token_chunk = 0;
   if (token_chunk > (int64_t(1) << 31)) return false;
+  if (H <= 0) return false;
+  const int64_t h_in = H;
+  H = round_up(H, 8);                           // see Plan::pad_h
   Plan q;
   if (!make_plan(N, H, V, dtype, &q, false, -1, 0)) return false;
+  q.h_in = h_in;
+  q.pad_h = H != h_in;
   q.nr = true;
   q.backward = true;
   q.grad_dtype = dtype;
@@ -158,6 +182,7 @@ bool make_plan_nr(int64_t N, int64_t H, int64_t V, int dtype, int64_t token_chun
     q.off_bcnt = off; off = align256(off + size_t(q.n_gather_blocks) * sizeof(int32_t));
     q.off_ccnt = off; off = align256(off + size_t(2 * q.n_tok_chunks) * sizeof(int64_t));
     q.off_hc = off;   off = align256(off + size_t(N) * H * q.elem);
+    off = carve_pad(q, off, true);
   }
   q.off_dhacc = 0;
   q.need_dh_acc = false;
@@ -229,8 +254,13 @@ int check_common(const void* h, const void* W, const int64_t* labels, int64_t N,
   if (!loss || !num_tokens || !W) return FLCE_ERR_ARG;
   if (N > 0 && (!h || !labels)) return FLCE_ERR_ARG;
   if (backward && (!dW || (N > 0 && !dH))) return FLCE_ERR_ARG;
+  // bf16 rows that are not whole 16-byte runs are padded in the workspace,
+  // which only the gathering entry points do (see Plan::pad_h)
+  const bool odd_h = dtype == FLCE_BF16 && H % 8 != 0;
   flce::Plan p;
-  if (!flce::make_plan(N, H, V, dtype, &p, backward, grad_dtype, gather)) return FLCE_ERR_ARG;
+  if (!flce::make_plan(N, (odd_h && gather == 0) ? H + 8 - H % 8 : H, V, dtype, &p, backward,
+                       grad_dtype, gather))
+    return FLCE_ERR_ARG;
   const size_t es = p.elem, gs = p.grad_elem;
   if (backward) {
     if (overlaps(dH, size_t(N) * H * gs, h, size_t(N) * H * es)) return FLCE_ERR_ARG;
@@ -240,8 +270,8 @@ int check_common(const void* h, const void* W, const int64_t* labels, int64_t N,
     if (overlaps(dW, size_t(V) * H * gs, h, size_t(N) * H * es)) return FLCE_ERR_ARG;
   }
   const uintptr_t mask = dtype == FLCE_BF16 ? 15u : 3u;
-  if (dtype == FLCE_BF16 && H % 8 != 0) return FLCE_ERR_UNSUPPORTED;
-  if (dtype == FLCE_BF16 && !flce::bf16_shape_ok(N, H, V)) return FLCE_ERR_UNSUPPORTED;
+  if (odd_h && gather == 0) return FLCE_ERR_UNSUPPORTED;
+  if (dtype == FLCE_BF16 && !flce::bf16_shape_ok(N, p.H, V)) return FLCE_ERR_UNSUPPORTED;
   if (misaligned(W, mask) || (N > 0 && misaligned(h, mask))) return FLCE_ERR_UNSUPPORTED;
   // the bf16 kernels write gradients in 16-byte (float32: 4 x 4-byte) runs
   const uintptr_t gmask = dtype == FLCE_BF16 ? 15u : 3u;

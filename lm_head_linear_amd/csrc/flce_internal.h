@@ -23,7 +23,8 @@ enum Kind : int {
   kDhReduce = 9,
   kGather = 10,
   kGemmDWDH = 11,     // dH's tiles and then dW's, in one grid
-  kNumKinds = 12,
+  kPadCopy = 12,      // row copies of a call at a padded hidden width
+  kNumKinds = 13,
 };
 
 // Everything one call needs on the device side.
@@ -85,6 +86,11 @@ hipError_t launch_merge_and_loss(const Plan& p, const Args& a, const Launcher& L
 hipError_t launch_merge(const Plan& p, const Args& a, int64_t t0, int64_t nt, const Launcher& L);
 hipError_t launch_loss_final(const Plan& p, const Args& a, const Launcher& L);
 hipError_t launch_zero_bytes(void* ptr, size_t bytes, const Launcher& L);
+// rows x width elements of `elem` bytes (2 or 4) at dst (row stride ld_dst):
+// the first `cols` of each row from src (row stride ld_src), the rest zero.
+hipError_t launch_copy_rows(const void* src, int64_t ld_src, void* dst, int64_t ld_dst,
+                            int64_t rows, int64_t cols, int64_t width, size_t elem,
+                            const Launcher& L);
 // Compact plan, before the forward: gather the tokens, the non-ignored ones
 // first (positions, labels, the hidden rows of the first `rows` of them: the
 // kept ones, or all N), give ignored tokens a zero loss, and zero the dH rows

@@ -220,6 +220,33 @@ __global__ __launch_bounds__(256) void k_gather_rows(const uint4* __restrict__ h
   }
 }
 
+// k_gather_rows for hidden rows of h_in bf16 values (h_in % 8 != 0), stored
+// at the padded width hp with the pad columns zero.
+__global__ __launch_bounds__(256) void k_gather_rows_pad(const uint16_t* __restrict__ h,
+                                                         int64_t h_in, int64_t hp,
+                                                         const int32_t* __restrict__ idx,
+                                                         const int64_t* __restrict__ rows_dev,
+                                                         int64_t rows, uint16_t* __restrict__ hc) {
+  const int64_t total = (rows_dev ? *rows_dev : rows) * hp;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total;
+       i += int64_t(gridDim.x) * 256) {
+    const int64_t r = i / hp, c = i - r * hp;
+    hc[i] = c < h_in ? h[int64_t(idx[r]) * h_in + c] : uint16_t(0);
+  }
+}
+
+// Row copy between widths: row r of dst (stride ld_dst) gets the first `cols`
+// elements of row r of src (stride ld_src) and zeros up to `width`.
+template <class T>
+__global__ __launch_bounds__(256) void k_copy_rows(const T* __restrict__ src, int64_t ld_src,
+                                                   T* __restrict__ dst, int64_t ld_dst,
+                                                   int64_t rows, int64_t cols, int64_t width) {
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y)
+    for (int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x; c < width;
+         c += int64_t(gridDim.x) * 256)
+      dst[r * ld_dst + c] = c < cols ? src[r * ld_src + c] : T(0);
+}
+
 // Live tokens of each chunk of nc gathered rows: cnt[c] for the forward (the
 // first `fwd` gathered rows: the kept ones, or all), cnt[nch + c] for the
 // backward (the kept ones).
@@ -318,6 +345,26 @@ hipError_t launch_loss_final(const Plan& p, const Args& a, const Launcher& L) {
   return hipGetLastError();
 }
 
+hipError_t launch_copy_rows(const void* src, int64_t ld_src, void* dst, int64_t ld_dst,
+                            int64_t rows, int64_t cols, int64_t width, size_t elem,
+                            const Launcher& L) {
+  if (rows <= 0 || width <= 0) return hipSuccess;
+  if (elem != 2 && elem != 4) return hipErrorInvalidValue;
+  const int64_t gx = (width + 255) / 256;
+  const dim3 grid(unsigned(gx < 64 ? gx : 64), unsigned(rows < 16384 ? rows : 16384));
+  L.pre(kPadCopy);
+  if (elem == 2)
+    hipLaunchKernelGGL(k_copy_rows<uint16_t>, grid, dim3(256), 0, L.stream,
+                       static_cast<const uint16_t*>(src), ld_src, static_cast<uint16_t*>(dst),
+                       ld_dst, rows, cols, width);
+  else
+    hipLaunchKernelGGL(k_copy_rows<uint32_t>, grid, dim3(256), 0, L.stream,
+                       static_cast<const uint32_t*>(src), ld_src, static_cast<uint32_t*>(dst),
+                       ld_dst, rows, cols, width);
+  L.post(kPadCopy);
+  return hipGetLastError();
+}
+
 hipError_t launch_zero_bytes(void* ptr, size_t bytes, const Launcher& L) {
   if (bytes == 0) return hipSuccess;
   L.pre(kFill);
@@ -344,12 +391,21 @@ hipError_t launch_gather(const Plan& p, const Args& a, bool all_rows, const Laun
                      a.ignore_index, a.bcnt);
   hipLaunchKernelGGL(k_gather_tokens, dim3(nb), dim3(kGatherThreads), 0, L.stream, a.labels, p.N,
                      a.ignore_index, a.bcnt, a.sc, a.idx, a.yc, a.tok_loss);
-  const int64_t h8 = p.H / 8;
-  int64_t blocks = (p.N * h8 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(k_gather_rows, dim3(unsigned(blocks)), dim3(256), 0, L.stream,
-                     static_cast<const uint4*>(a.h), h8, a.idx,
-                     all_rows ? nullptr : &a.sc->n_valid, p.N, static_cast<uint4*>(a.hc));
+  const int64_t* rows_dev = all_rows ? nullptr : &a.sc->n_valid;
+  if (p.pad_h) {
+    int64_t blocks = (p.N * p.H + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(k_gather_rows_pad, dim3(unsigned(blocks)), dim3(256), 0, L.stream,
+                       static_cast<const uint16_t*>(a.h), p.h_in, p.H, a.idx, rows_dev, p.N,
+                       static_cast<uint16_t*>(a.hc));
+  } else {
+    const int64_t h8 = p.H / 8;
+    int64_t blocks = (p.N * h8 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(k_gather_rows, dim3(unsigned(blocks)), dim3(256), 0, L.stream,
+                       static_cast<const uint4*>(a.h), h8, a.idx, rows_dev, p.N,
+                       static_cast<uint4*>(a.hc));
+  }
   if (a.dH) {
     const int64_t g16 = p.H * int64_t(p.grad_elem) / 16;   // 16-byte pieces per dH row
     int64_t zb = (p.N * g16 + 255) / 256;

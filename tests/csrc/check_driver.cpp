@@ -34,7 +34,7 @@ int main() {
   const size_t big = size_t(1) << 40;
   EXPECT(call(8192, 4096, 131072, FLCE_BF16, FLCE_MEAN, 0, 0.f, 1.f, big) == FLCE_OK);
   EXPECT(call(8192, 4096, 131072, FLCE_BF16, FLCE_MEAN, 5, 0.f, 1.f, big) == FLCE_ERR_ARG);
-  EXPECT(call(1, 12, 5, FLCE_BF16, FLCE_SUM, 0, 0.f, 1.f, big) == FLCE_ERR_UNSUPPORTED);
+  EXPECT(call(1, 12, 5, FLCE_BF16, FLCE_SUM, 0, 0.f, 1.f, big) == FLCE_OK);   // padded to 16
   EXPECT(call(1, 12, 5, FLCE_F32, FLCE_SUM, 0, 0.f, 1.f, big) == FLCE_OK);
   EXPECT(call(1, 8, 5, FLCE_BF16, FLCE_SUM, 0, -0.5f, 1.f, big) == FLCE_ERR_ARG);
   EXPECT(call(1, 8, 5, FLCE_BF16, FLCE_SUM, 0, std::numeric_limits<float>::quiet_NaN(), 1.f,
@@ -52,6 +52,10 @@ int main() {
       EXPECT(w > 0 && w % 256 == 0);
       const int64_t c = flce_vocab_chunk(n, 64, v, FLCE_BF16);
       EXPECT(c >= 256 && c % 256 == 0);
+      // a hidden size that is not a multiple of 8: padded copies carved too
+      const size_t wo = flce_workspace_size(n, 61, v, FLCE_BF16);
+      EXPECT(wo % 256 == 0 && (n == 0 ? wo == w : wo > w));
+      EXPECT(flce_forward_workspace_size(n, 61, v, FLCE_BF16) % 256 == 0);
     }
   // forward-only entry: same rules, its own (smaller) workspace
   EXPECT(fcall(8192, 4096, 131072, FLCE_BF16, FLCE_MEAN, 0, 0.f, big) == FLCE_OK);

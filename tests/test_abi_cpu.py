@@ -159,12 +159,44 @@ def test_negative_micro_batch_scale_rejected_by_every_entry(lib):
     (dict(dW=A16 * 64 + 256), 1),      # dW overlaps W
     (dict(dH=A16 * 64), 1),            # dH overlaps W
     (dict(dW=A16), 1),                 # dW overlaps h
-    (dict(H=12), 2),                   # bf16 needs H % 8 == 0
     (dict(h=A16 + 8), 2),              # misaligned bf16 matrix
     (dict(ws=None), 3), (dict(ws=A16 * 1024 + 128), 3), (dict(wsb=16), 3),
 ])
 def test_check_args_errors(lib, kw, code):
     assert lib.flce_check_args(*_args(**kw)) == code
+
+
+def test_odd_hidden_size_runs_padded(lib):
+    """bf16 with H % 8 != 0 (the NeMo linear_ce page, "API", puts no limit on
+    the hidden size): the gathering entry points accept it and carve padded
+    copies of W, dW and dH at the width rounded up to 8; the two entry points
+    that read h in place (logits-returning, allocation-free) refuse it."""
+    assert lib.flce_check_args(*_args(H=12)) == 0
+    assert lib.flce_check_args_ex(*_args(H=12), 0) == 0
+    assert lib.flce_check_args_nr(*_args(H=12), 0) == 0
+    fw = [x for i, x in enumerate(_args(H=12)) if i not in (12, 13, 17)]
+    assert lib.flce_forward_check_args(*fw) == 0
+    fws = [x for i, x in enumerate(_args(H=12, wsb=1 << 20)) if i not in (12, 13, 17)]
+    assert lib.flce_forward_logits_check_args(*fws, A16 * 2048, 128, 0) == 2
+    assert lib.flce_forward_logits_check_args(*[x for i, x in enumerate(_args(H=16, wsb=1 << 20))
+                                                if i not in (12, 13, 17)], A16 * 2048, 128, 0) == 0
+    assert lib.flce_check_args(*_args(H=12, dH=A16)) == 1       # argument errors come first
+    N, V = 300, 1000
+    for H in (1, 100, 4095):
+        Hp = -(-H // 8) * 8
+        pad_w, pad_g = V * Hp * 2, V * Hp * 2 + N * Hp * 2           # W; dW and dH
+        slack = 3 * 256 + N * 8                                      # alignment; hc rows
+        extra = lib.flce_workspace_size(N, H, V, 1) - lib.flce_workspace_size(N, Hp, V, 1)
+        assert pad_w + pad_g <= extra <= pad_w + pad_g + slack, (H, extra)
+        extra = (lib.flce_forward_workspace_size(N, H, V, 1)
+                 - lib.flce_forward_workspace_size(N, Hp, V, 1))
+        assert pad_w <= extra <= pad_w + slack, (H, extra)
+        extra = lib.flce_workspace_size_ex(N, H, V, 1, 0) - lib.flce_workspace_size_ex(N, Hp, V, 1, 0)
+        assert pad_w + 2 * pad_g <= extra <= pad_w + 2 * pad_g + slack, (H, extra)
+        extra = lib.flce_workspace_size_nr(N, H, V, 1, 0) - lib.flce_workspace_size_nr(N, Hp, V, 1, 0)
+        assert pad_w + pad_g <= extra <= pad_w + pad_g + slack, (H, extra)
+        assert lib.flce_vocab_chunk(N, H, V, 1) == lib.flce_vocab_chunk(N, Hp, V, 1)
+    assert lib.flce_workspace_size(8, 12, 8, 0) == lib.flce_workspace_size(8, 12, 8, 0)  # fp32: as is
 
 
 def test_check_args_empty_batch(lib):
@@ -256,7 +288,7 @@ def test_forward_check_args_ok(lib):
     (dict(red=1, T=10), 1),
     (dict(h=None), 1), (dict(W=None), 1), (dict(labels=None), 1), (dict(loss=None), 1),
     (dict(nt=None), 1),
-    (dict(H=12), 2), (dict(h=A16 + 8), 2), (dict(W=A16 * 64 + 4), 2),
+    (dict(h=A16 + 8), 2), (dict(W=A16 * 64 + 4), 2),
     (dict(ws=None), 3), (dict(ws=A16 * 1024 + 128), 3), (dict(wsb=16), 3),
 ])
 def test_forward_check_args_errors(lib, kw, code):
@@ -433,7 +465,7 @@ def test_nr_plan(lib):
     (dict(), 0, 0), (dict(), 256, 0),
     (dict(dtype=0), 0, 2),            # float32 inputs
     (dict(), -5, 2),
-    (dict(red=1, T=7), 0, 1), (dict(dH=None), 0, 1), (dict(H=12), 0, 2),
+    (dict(red=1, T=7), 0, 1), (dict(dH=None), 0, 1), (dict(H=12), 0, 0),
     (dict(wsb=16), 0, 3), (dict(ws=A16 * 1024 + 64), 0, 3),
 ])
 def test_check_args_nr(lib, kw, tc, code):
