@@ -152,3 +152,34 @@ def test_odd_hidden_refused_where_h_is_read_in_place():
         m.flce_forward_noalloc(h, W, y, loss=torch.empty((), device=dev),
                                num_tokens=torch.empty((), dtype=torch.int64, device=dev))
     assert e.value.code == 2
+
+
+@pytest.mark.parametrize("k", range(20))
+def test_odd_hidden_random(k, monkeypatch):
+    """Seeded random shapes with H % 8 != 0 over the gathering entry points."""
+    rng = np.random.default_rng(7100 + k)
+    N, V = int(rng.integers(1, 700)), int(rng.integers(1, 2500))
+    H = int(rng.integers(0, 40)) * 8 + int(rng.integers(1, 8))
+    w = fi.make_custom(N, H, V, dtype=torch.bfloat16, seed=7100 + k,
+                       ignore_frac=float(rng.choice([0.0, 0.1, 0.5])),
+                       softcap=float(rng.choice([0.0, 30.0])),
+                       reduction=str(rng.choice(["sum", "mean"])))
+    mode = ["step", "f32grad", "nr", "forward"][k % 4]
+    if mode in ("step", "f32grad"):
+        monkeypatch.setenv("FLCE_VCHUNK", str(int(rng.choice([0, 256, 512]))))
+    print(f"case {k}: N={N} H={H} V={V} s={w.softcap} {w.reduction} mode={mode}", flush=True)
+    r = gu.run_oracle(w)
+    if mode == "forward":
+        f = gu.run_gpu_forward(w)
+        assert f["status"] == 0 and f["num_tokens"] == r.num_tokens
+        gu.assert_loss(f["loss"], r.loss64)
+        return
+    if mode == "f32grad":
+        g = gu.run_gpu(w, grad_dtype=torch.float32)
+        assert g["status"] == 0 and g["num_tokens"] == r.num_tokens
+        gu.assert_loss(g["loss"], r.loss64)
+        gu.assert_grad("dH", g["dH"], r.dH, gu.GRAD_TOL[torch.float32])
+        gu.assert_grad("dW", g["dW"], r.dW, gu.GRAD_TOL[torch.float32])
+        return
+    g = gu.run_gpu(w, recompute=mode != "nr", token_chunk=int(rng.choice([0, 256])))
+    gu.assert_parity(w, g, r)
