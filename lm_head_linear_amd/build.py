@@ -59,7 +59,7 @@ def build(verbose: bool = False, extra_flags=None) -> str:
                 print(o)
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
-          *[j[1] for j in jobs]])
+          *[j[1] for j in jobs], "-lrocprofiler-sdk-roctx"])
     os.replace(tmp, LIB)
     return LIB
 

@@ -1,6 +1,7 @@
 // C-ABI entry points: argument checks, workspace carving, launch sequence,
 // optional per-kernel timing.
 #include <hip/hip_runtime.h>
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <cstdint>
 #include <mutex>
@@ -12,6 +13,18 @@
 #include "gemm_index.h"
 
 namespace {
+
+// ---- ROCTX ranges -------------------------------------------------------------
+// A named range around each entry point's call and each pass it enqueues
+// (forward, merge, one per backward chunk or token chunk), for a profiler's
+// marker trace (rocprofv3 --marker-trace). They span the host-side enqueue of
+// the pass; the kernel trace gives the device times.
+struct Range {
+  explicit Range(const char* name) { roctxRangePushA(name); }
+  ~Range() { roctxRangePop(); }
+  Range(const Range&) = delete;
+  Range& operator=(const Range&) = delete;
+};
 
 // ---- per-kernel timing ------------------------------------------------------
 struct Rec {
@@ -176,19 +189,24 @@ int run_nr(const void* h, const void* W, const int64_t* labels, int64_t N, int64
   a.bcnt = reinterpret_cast<int32_t*>(ws + p.off_bcnt);
   a.ccnt = reinterpret_cast<int64_t*>(ws + p.off_ccnt);
   a.hc = ws + p.off_hc;
-  e = pad_inputs(p, a, ws, true, L);
-  if (e == hipSuccess) e = flce::launch_label_scan(p, a, L);
-  // the tokens gathered, the kept ones first; the chunks run over that order
-  // (the ignored tokens only for their lse, when it is asked for)
-  const bool all_rows = lse_out != nullptr;
-  if (e == hipSuccess) e = flce::launch_gather(p, a, all_rows, L);
-  if (e == hipSuccess) e = flce::launch_chunk_counts(p, a, all_rows, L);
+  {
+    Range r("flce.setup");
+    e = pad_inputs(p, a, ws, true, L);
+    if (e == hipSuccess) e = flce::launch_label_scan(p, a, L);
+    // the tokens gathered, the kept ones first; the chunks run over that order
+    // (the ignored tokens only for their lse, when it is asked for)
+    const bool all_rows = lse_out != nullptr;
+    if (e == hipSuccess) e = flce::launch_gather(p, a, all_rows, L);
+    if (e == hipSuccess) e = flce::launch_chunk_counts(p, a, all_rows, L);
+  }
   for (int64_t c = 0; e == hipSuccess && c < p.n_tok_chunks; ++c) {
+    Range r("flce.token_chunk");
     const int64_t t0 = c * p.nc, nt = flce::gemm::nr_chunk_tokens(p, c);
     e = flce::bf16_nr_forward_chunk(p, a, c, L);
     if (e == hipSuccess) e = flce::launch_merge_gathered(p, a, t0, nt, a.ccnt + c, L);
     if (e == hipSuccess) e = flce::bf16_nr_backward_chunk(p, a, c, L);
   }
+  Range r("flce.finish");
   if (e == hipSuccess) e = flce::launch_loss_final(p, a, L);
   if (e == hipSuccess) e = crop_outputs(p, ws, dH, dW, L);
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
@@ -243,16 +261,27 @@ int run(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t 
   }
 
   const bool bf16 = dtype == FLCE_BF16;
-  e = pad_inputs(p, a, ws, backward, L);
-  if (e == hipSuccess) e = flce::launch_label_scan(p, a, L);
-  // a compact plan gathers the tokens first, the kept ones in front; the
-  // forward then skips the ignored ones unless their lse is asked for
-  if (e == hipSuccess && p.compact) e = flce::launch_gather(p, a, lse_out != nullptr, L);
-  if (e == hipSuccess) e = bf16 ? flce::bf16_forward(p, a, L) : flce::f32_forward(p, a, L);
-  if (e == hipSuccess) e = flce::launch_merge_and_loss(p, a, L);
-  for (int64_t c = 0; backward && e == hipSuccess && c < p.n_chunks; ++c)
+  {
+    Range r("flce.setup");
+    e = pad_inputs(p, a, ws, backward, L);
+    if (e == hipSuccess) e = flce::launch_label_scan(p, a, L);
+    // a compact plan gathers the tokens first, the kept ones in front; the
+    // forward then skips the ignored ones unless their lse is asked for
+    if (e == hipSuccess && p.compact) e = flce::launch_gather(p, a, lse_out != nullptr, L);
+  }
+  {
+    Range r("flce.forward");
+    if (e == hipSuccess) e = bf16 ? flce::bf16_forward(p, a, L) : flce::f32_forward(p, a, L);
+    if (e == hipSuccess) e = flce::launch_merge_and_loss(p, a, L);
+  }
+  for (int64_t c = 0; backward && e == hipSuccess && c < p.n_chunks; ++c) {
+    Range r("flce.backward_chunk");
     e = bf16 ? flce::bf16_backward_chunk(p, a, c, L) : flce::f32_backward_chunk(p, a, c, L);
-  if (e == hipSuccess && backward) e = crop_outputs(p, ws, dH, dW, L);
+  }
+  if (e == hipSuccess && backward && p.pad_h) {
+    Range r("flce.copy_out");
+    e = crop_outputs(p, ws, dH, dW, L);
+  }
   return e == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
@@ -284,6 +313,7 @@ int flce_forward_backward_ex(const void* h, const void* W, const int64_t* labels
                               mb_scale, accumulate_dW, workspace, workspace_bytes, status,
                               lse_out, grad_dtype);
   if (st != FLCE_OK) return st;
+  Range r("flce_forward_backward");
   return run(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens, loss,
              num_tokens, dH, dW, stream, dtype, mb_scale, accumulate_dW, workspace, status,
              lse_out, true, grad_dtype);
@@ -333,6 +363,7 @@ int flce_forward_backward_nr(const void* h, const void* W, const int64_t* labels
                               mb_scale, accumulate_dW, workspace, workspace_bytes, status,
                               lse_out, token_chunk);
   if (st != FLCE_OK) return st;
+  Range r("flce_forward_backward_nr");
   return run_nr(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens, loss,
                 num_tokens, dH, dW, stream, dtype, mb_scale, accumulate_dW, workspace, status,
                 lse_out, token_chunk);
@@ -347,6 +378,7 @@ int flce_forward(const void* h, const void* W, const int64_t* labels, int64_t N,
                                    num_label_tokens, loss, num_tokens, stream, dtype, mb_scale,
                                    workspace, workspace_bytes, status, lse_out);
   if (st != FLCE_OK) return st;
+  Range r("flce_forward");
   return run(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens, loss,
              num_tokens, nullptr, nullptr, stream, dtype, mb_scale, 0, workspace, status,
              lse_out, false, dtype);
@@ -374,6 +406,7 @@ int flce_forward_noalloc(const void* h, const void* W, const int64_t* labels, in
   if (p.total > FLCE_NOALLOC_SCRATCH_BYTES) return FLCE_ERR_SCRATCH;
   void* ws = nullptr;
   if (scratch_address(static_cast<hipStream_t>(stream), &ws) != hipSuccess) return FLCE_ERR_HIP;
+  Range r("flce_forward_noalloc");
   return run(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens, loss,
              num_tokens, nullptr, nullptr, stream, dtype, mb_scale, 0, ws, status, lse_out,
              false, dtype, nullptr, 0, FLCE_F32, 0);
@@ -390,6 +423,7 @@ int flce_forward_logits(const void* h, const void* W, const int64_t* labels, int
                                           dtype, mb_scale, workspace, workspace_bytes, status,
                                           lse_out, logits, ld_logits, logits_dtype);
   if (st != FLCE_OK) return st;
+  Range r("flce_forward_logits");
   return run(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens, loss,
              num_tokens, nullptr, nullptr, stream, dtype, mb_scale, 0, workspace, status,
              lse_out, false, dtype, N > 0 ? logits : nullptr, ld_logits, logits_dtype, 0);
