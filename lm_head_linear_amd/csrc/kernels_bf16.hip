@@ -546,6 +546,7 @@ __device__ __forceinline__ void gemm_tile(char* smem, int64_t bid, int seg, Oper
   if constexpr (!BA) A.g.blk = 0;
   B.g.blk = 0;
   if constexpr (SPLITK) {
+    epi.select_segment(seg);
     const int64_t k0 = int64_t(seg) * a2_off;
     K = (K - k0) < a2_off ? (K - k0) : a2_off;
     A.ptr += gemm::k_origin(FA, A.g, k0);
@@ -624,18 +625,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A, Operand B, int6
 // the kept tokens only, its tiles may fill its last round of workgroups only
 // in part, and the shorter dW tiles behind it fill the rest instead of the
 // next launch starting on an idle chip. One LDS array serves both.
-template <int FA1, int FB1, class Epi1, int DYN1, int FA2, int FB2, class Epi2, int DYN2>
+// SPLIT1: the first GEMM is split along K into segments of kseg1 rows, its
+// n1 = t1 x segments workgroups segment by segment (workgroup b: segment
+// b / t1, tile b % t1), each writing a partial product of its own.
+template <int FA1, int FB1, class Epi1, int DYN1, bool SPLIT1, int FA2, int FB2, class Epi2,
+          int DYN2>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_pair(
-    int64_t n1p, Operand A1, Operand B1, int64_t M1, int64_t N1, int64_t K1, Epi1 e1,
-    Operand A2, Operand B2, int64_t M2, int64_t N2, int64_t K2, Epi2 e2, const int64_t* dyn) {
+    int64_t n1p, int64_t t1, int64_t n1, int64_t kseg1, Operand A1, Operand B1, int64_t M1,
+    int64_t N1, int64_t K1, Epi1 e1, Operand A2, Operand B2, int64_t M2, int64_t N2, int64_t K2,
+    Epi2 e2, const int64_t* dyn) {
   constexpr int kB1 = stage_bytes<FA1, FB1>() + Epi1::kTokBytes;
   constexpr int kB2 = stage_bytes<FA2, FB2>() + Epi2::kTokBytes;
   __shared__ __attribute__((aligned(1024))) char smem[kB1 > kB2 ? kB1 : kB2];
   const int64_t b = blockIdx.x;
   if (b < n1p) {
-    if (b < gemm::num_tiles(M1, N1))
+    if (b >= n1) return;
+    if constexpr (SPLIT1) {
+      const int64_t seg = b / t1;
+      gemm_tile<FA1, FB1, Epi1, true, 1, true, DYN1>(smem, b - seg * t1, int(seg), A1, B1, M1,
+                                                     N1, K1, gemm::kGroupM, e1, kseg1, dyn);
+    } else {
       gemm_tile<FA1, FB1, Epi1, true, 1, false, DYN1>(smem, b, 0, A1, B1, M1, N1, K1,
                                                       gemm::kGroupM, e1, 0, dyn);
+    }
   } else {
     gemm_tile<FA2, FB2, Epi2, true, 1, false, DYN2>(smem, b - n1p, 0, A2, B2, M2, N2, K2,
                                                     gemm::kGroupM, e2, 0, dyn);
@@ -1472,11 +1484,12 @@ struct EpiDHPart {
 
   static constexpr int kTokBytes = 0;             // no per-token inputs
   __device__ __forceinline__ void stage(char*, int64_t, int, int) const {}
+  // the workgroup's K segment (called by the split GEMM tile before the K loop)
+  __device__ __forceinline__ void select_segment(int seg) { part += int64_t(seg) * seg_stride; }
 
   __device__ __forceinline__ void operator()(Acc& acc, int64_t m0, int64_t n0, int wm, int wn,
                                              int lane, char* smem, const char* tok) const {
-    EpiDH<true, false>{nullptr, part + int64_t(blockIdx.y) * seg_stride, N, H, nullptr}(
-        acc, m0, n0, wm, wn, lane, smem, tok);
+    EpiDH<true, false>{nullptr, part, N, H, nullptr}(acc, m0, n0, wm, wn, lane, smem, tok);
   }
 };
 
@@ -1586,25 +1599,32 @@ hipError_t run_gemm(const gemm::Launch& l, const Args& a, const Epi& e, int kind
 }
 
 // Two GEMMs whose A operand is the blocked G in one grid (k_gemm_pair): the
-// first launch's tiles, padded to a multiple of 8 workgroups, then the
-// second's.
-template <int FA1, int FB1, int DYN1, int FA2, int FB2, int DYN2, class Epi1, class Epi2>
+// first launch's tiles (SPLIT1: times its segs1 K segments of kseg1), padded
+// to a multiple of 8 workgroups, then the second's.
+template <int FA1, int FB1, int DYN1, int FA2, int FB2, int DYN2, bool SPLIT1 = false,
+          class Epi1, class Epi2>
 hipError_t run_gemm_pair(const gemm::Launch& l1, const Epi1& e1, const gemm::Launch& l2,
                          const Epi2& e2, const Args& a, int kind, const Launcher& L,
-                         const int64_t* dyn) {
+                         const int64_t* dyn, int64_t kseg1 = 0, int64_t segs1 = 1) {
   if (!launch_ok(l1) || !launch_ok(l2)) return hipErrorInvalidValue;
   if (l1.a.blk == 0 || l1.b.blk != 0 || l2.a.blk == 0 || l2.b.blk != 0)
     return hipErrorInvalidValue;
   if (((DYN1 != kDynNone) || (DYN2 != kDynNone)) != (dyn != nullptr)) return hipErrorInvalidValue;
-  const int64_t n1p = (gemm::num_tiles(l1.M, l1.Nn) + 7) / 8 * 8;
+  // SPLIT1: kseg1 a multiple of 64 (whole stage tiles), every segment non-empty
+  if (SPLIT1 && (kseg1 <= 0 || kseg1 % 64 != 0 || segs1 < 1 || (segs1 - 1) * kseg1 >= l1.K))
+    return hipErrorInvalidValue;
+  const int64_t t1 = gemm::num_tiles(l1.M, l1.Nn);
+  const int64_t n1 = t1 * (SPLIT1 ? segs1 : 1);
+  const int64_t n1p = (n1 + 7) / 8 * 8;
   const int64_t total = n1p + gemm::num_tiles(l2.M, l2.Nn);
   if (total > kMaxTiles) return hipErrorInvalidValue;
   const Operand A1{buf_ptr(a, l1.buf_a) + l1.off_a, l1.a}, B1{buf_ptr(a, l1.buf_b) + l1.off_b, l1.b};
   const Operand A2{buf_ptr(a, l2.buf_a) + l2.off_a, l2.a}, B2{buf_ptr(a, l2.buf_b) + l2.off_b, l2.b};
   L.pre(kind);
-  hipLaunchKernelGGL((k_gemm_pair<FA1, FB1, Epi1, DYN1, FA2, FB2, Epi2, DYN2>),
-                     dim3(unsigned(total)), dim3(kThreads), 0, L.stream, n1p, A1, B1, l1.M, l1.Nn,
-                     l1.K, e1, A2, B2, l2.M, l2.Nn, l2.K, e2, dyn);
+  hipLaunchKernelGGL((k_gemm_pair<FA1, FB1, Epi1, DYN1, SPLIT1, FA2, FB2, Epi2, DYN2>),
+                     dim3(unsigned(total)), dim3(kThreads), 0, L.stream, n1p, t1, n1,
+                     SPLIT1 ? kseg1 : int64_t(0), A1, B1, l1.M, l1.Nn, l1.K, e1, A2, B2, l2.M,
+                     l2.Nn, l2.K, e2, dyn);
   L.post(kind);
   return hipGetLastError();
 }
@@ -1754,18 +1774,16 @@ hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, cons
   const gemm::Launch lh = gemm::backward_launch(p, chunk, 2);
   const bool first = chunk == 0, last = chunk == p.n_chunks - 1;
   if (p.dh_kseg) {
-    // few dH output tiles: dW alone, then dH split along K and the segments
-    // added up in a fixed order
-    if (a.accumulate_dW)
-      err = run_gemm<TF, TF, true, 1, false, kDynK>(lw, a, EpiDW<true>{dW, p.H, v0, vcur},
-                                                    kGemmDW, L, 0, 1, nv);
-    else
-      err = run_gemm<TF, TF, true, 1, false, kDynK>(lw, a, EpiDW<false>{dW, p.H, v0, vcur},
-                                                    kGemmDW, L, 0, 1, nv);
-    if (err != hipSuccess) return err;
+    // few dH output tiles: dH split along K, then dW, in one grid, and the
+    // segments' partial products added up in a fixed order afterwards
     const int64_t segs = (lh.K + p.dh_kseg - 1) / p.dh_kseg;
     const EpiDHPart ep{a.dh_part, p.N, p.H, p.N * p.H};
-    err = run_gemm<NF, TF, true, 1, true, kDynM>(lh, a, ep, kGemmDH, L, p.dh_kseg, segs, nv);
+    if (a.accumulate_dW)
+      err = run_gemm_pair<NF, TF, kDynM, TF, TF, kDynK, true>(
+          lh, ep, lw, EpiDW<true>{dW, p.H, v0, vcur}, a, kGemmDWDH, L, nv, p.dh_kseg, segs);
+    else
+      err = run_gemm_pair<NF, TF, kDynM, TF, TF, kDynK, true>(
+          lh, ep, lw, EpiDW<false>{dW, p.H, v0, vcur}, a, kGemmDWDH, L, nv, p.dh_kseg, segs);
     if (err != hipSuccess) return err;
     return launch_dh_reduce(a.dh_part, segs, p.N * p.H, first ? nullptr : a.dh_acc,
                             last ? nullptr : a.dh_acc, last ? dH : nullptr, L, p.H, nv, a.idx);
@@ -1830,8 +1848,8 @@ hipError_t bf16_nr_backward_chunk(const Plan& p, const Args& a, int64_t c, const
   // 2) dW (+)= G^T . h[chunk] (K = the chunk's kept tokens); over several
   // token chunks the sum is kept in float32 and rounded to bf16 once, at the
   // last chunk. 3) dH[chunk] = G . W over the whole vocabulary, the rows
-  // stored at the tokens' original positions. Both in one grid, dH's tiles
-  // first, unless dH is split along K.
+  // stored at the tokens' original positions (or, with few dH tiles, split
+  // along K into partial products). Both in one grid, dH's workgroups first.
   uint16_t* dW = static_cast<uint16_t*>(a.dW);
   uint16_t* dH = static_cast<uint16_t*>(a.dH);
   const int32_t* rmap = a.idx + t0;
@@ -1839,8 +1857,12 @@ hipError_t bf16_nr_backward_chunk(const Plan& p, const Args& a, int64_t c, const
   const gemm::Launch lh = gemm::nr_launch(p, c, 2);
   constexpr int T = gemm::kFormT, NF = gemm::kFormN;
   const EpiDH<true, true> edh{dH, nullptr, nt, p.H, rmap};
+  const int64_t segs = p.dh_kseg ? (lh.K + p.dh_kseg - 1) / p.dh_kseg : 1;
   auto dw = [&](auto epi) {
-    if (p.dh_kseg) return run_gemm<T, T, true, 1, false, kDynK>(lw, a, epi, kGemmDW, L, 0, 1, cb);
+    if (p.dh_kseg)
+      return run_gemm_pair<NF, T, kDynM, T, T, kDynK, true>(
+          lh, EpiDHPart{a.dh_part, nt, p.H, nt * p.H}, lw, epi, a, kGemmDWDH, L, cb, p.dh_kseg,
+          segs);
     return run_gemm_pair<NF, T, kDynM, T, T, kDynK>(lh, edh, lw, epi, a, kGemmDWDH, L, cb);
   };
   if (!p.need_dw_acc) {
@@ -1854,11 +1876,8 @@ hipError_t bf16_nr_backward_chunk(const Plan& p, const Args& a, int64_t c, const
     err = dw(EpiDWAcc<2, 1>{dW, a.dw_acc, p.H, p.V});
   }
   if (err != hipSuccess || !p.dh_kseg) return err;
-  // few dH output tiles: split K, then add the segments up in a fixed order
-  const int64_t segs = (lh.K + p.dh_kseg - 1) / p.dh_kseg;
-  err = run_gemm<NF, T, true, 1, true, kDynM>(
-      lh, a, EpiDHPart{a.dh_part, nt, p.H, nt * p.H}, kGemmDH, L, p.dh_kseg, segs, cb);
-  if (err != hipSuccess) return err;
+  // few dH output tiles: its K segments (run in the grid above) added up in
+  // a fixed order
   return launch_dh_reduce(a.dh_part, segs, nt * p.H, nullptr, nullptr, dH, L, p.H, cb, rmap);
 }
 
