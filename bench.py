@@ -168,32 +168,36 @@ def other_configs(steps: int, warmup: int):
         nt = torch.empty((), dtype=torch.int64, device=dev)
         kw = dict(ignore_index=w.ignore_index, softcap=w.softcap, reduction=w.reduction,
                   num_label_tokens=w.num_label_tokens, loss=loss, num_tokens=nt)
-        torch.cuda.synchronize()
-        base = torch.cuda.memory_allocated(dev)
-        torch.cuda.reset_peak_memory_stats(dev)
-        ws = torch.empty(m.flce_workspace_size(N, H, V, W.dtype), dtype=torch.uint8, device=dev)
-        runs = {"one_call": lambda: m.flce_forward_backward(h, W, y, dH=dH, dW=dW, workspace=ws,
-                                                             **kw)}
+        # each mode with a workspace of its own, allocated for it alone, so
+        # that the peak extra memory is that mode's
+        def one_call(ws):
+            m.flce_forward_backward(h, W, y, dH=dH, dW=dW, workspace=ws, **kw)
+        modes = {"one_call": (N, one_call)}
         if w.micro_batches > 1:
             nb = N // w.micro_batches
-            wsm = torch.empty(m.flce_workspace_size(nb, H, V, W.dtype), dtype=torch.uint8,
-                              device=dev)
 
-            def micro():
+            def micro(ws):
                 for i in range(w.micro_batches):
                     s = slice(i * nb, (i + 1) * nb)
-                    m.flce_forward_backward(h[s], W, y[s], dH=dH[s], dW=dW, workspace=wsm,
+                    m.flce_forward_backward(h[s], W, y[s], dH=dH[s], dW=dW, workspace=ws,
                                             accumulate_dW=i > 0,
                                             mb_scale=m.micro_batch_scale(0, 0, w.reduction), **kw)
-            runs[f"{w.micro_batches}_micro_batches"] = micro
+            modes[f"{w.micro_batches}_micro_batches"] = (nb, micro)
         res = {"N": N, "H": H, "V": V, "softcap": w.softcap, "reduction": w.reduction,
-               "num_label_tokens": w.num_label_tokens}
+               "num_label_tokens": w.num_label_tokens, "logits_f32_bytes_avoided": int(N * V * 4)}
         nhv = float(N) * H * V
         sf = step_flops(N, int((w.labels != w.ignore_index).sum()), H, V,
                         m.flce_vocab_chunk(N, H, V, W.dtype))
         xfl = sf["step"]
-        for name, fn in runs.items():
-            ms, ev_ms = time_steps(fn, steps, warmup)
+        for name, (n_call, fn) in modes.items():
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            base = torch.cuda.memory_allocated(dev)
+            torch.cuda.reset_peak_memory_stats(dev)
+            ws = torch.empty(m.flce_workspace_size(n_call, H, V, W.dtype), dtype=torch.uint8,
+                             device=dev)
+            ms, ev_ms = time_steps(lambda: fn(ws), steps, warmup)
+            torch.cuda.synchronize()
             res[name] = {"ms_per_step": round(ms, 4), "event_ms_per_step": round(ev_ms, 4),
                          "tokens_per_s": round(N / ms * 1e3, 1),
                          "mfma_frac_8nhv": round(8.0 * nhv / (ms * 1e-3) / 1e12
@@ -201,14 +205,14 @@ def other_configs(steps: int, warmup: int):
                          "mfma_frac_6nhv": round(6.0 * nhv / (ms * 1e-3) / 1e12
                                                  / PEAK_BF16_TFLOPS, 4),
                          "mfma_frac_executed": round(xfl / (ms * 1e-3) / 1e12
-                                                     / PEAK_BF16_TFLOPS, 4)}
-            log(f"{w.name} {name}: {ms:.3f} ms/step")
-        torch.cuda.synchronize()
-        res["extra_memory_bytes"] = int(torch.cuda.max_memory_allocated(dev) - base)
-        res["workspace_bytes"] = int(ws.numel())
-        res["logits_f32_bytes_avoided"] = int(N * V * 4)
+                                                     / PEAK_BF16_TFLOPS, 4),
+                         "workspace_bytes": int(ws.numel()),
+                         "extra_memory_bytes": int(torch.cuda.max_memory_allocated(dev) - base)}
+            log(f"{w.name} {name}: {ms:.3f} ms/step, "
+                f"{res[name]['extra_memory_bytes'] / 2**20:.0f} MiB extra")
+            del ws
         out[w.name] = res
-        del h, W, y, dH, dW, ws, runs
+        del h, W, y, dH, dW
         torch.cuda.empty_cache()
     return out
 
