@@ -195,15 +195,23 @@ FLCE_HD void tile_coords(int64_t b, int64_t M, int64_t Nn, int group_m, int64_t&
 
 // LDS layout of one stage tile of an operand. N form: 256 rows x sk k,
 // 2 sk bytes per row, sk / 8 chunks of 16 B; logical chunk c of row r at
-// position c ^ swz_n(r). Each 16-lane group of a fragment read (16
-// consecutive rows, one chunk) then covers all 16 bank quads of the
-// 256-byte bank window once: for 64 k, even rows take quads 0-7 and odd rows
-// 8-15; for 32 k, row r % 4 takes quads 4 (r % 4) to 4 (r % 4) + 3. T form:
-// sk k-rows x 256 columns, 512 B per k-row, 32 chunks; logical chunk c of
-// k-row k at c ^ swz_t(k). Both were checked with the LDS bank-conflict
-// counter on gfx950 for the fragment read patterns: zero conflicts.
-FLCE_HD int swz_n(int r, int sk) { return sk == 64 ? (r >> 1) & 7 : (r >> 2) & 3; }
-FLCE_HD int swz_t(int k) { return (0xCA60 >> (4 * (k & 3))) & 15; }  // {0,6,10,12}[k%4]
+// position c ^ swz_n(r), the chunk index XORed with bits 1.. of the row. A
+// fragment read (16 consecutive rows, one chunk per 16-lane group) then
+// reads without LDS bank conflicts, for 64 k (8 chunks per row) and for 32 k
+// (4 chunks): the gfx950 bank-conflict counter reads 0 for both read
+// patterns, against 4 conflict cycles per read with the 32-k chunk XORed with
+// bits 2-3 of the row instead. T form: sk k-rows x 256 columns, 512 B per
+// k-row, 32 chunks; logical chunk c of k-row k at c ^ swz_t(k). A transposed
+// fragment read (8 bytes per lane) serves 32 lanes at a time, two 16-lane
+// groups whose k-rows are 8 apart, each reading 2 chunks of 4 consecutive
+// k-rows: the k % 4 term puts one group on 8 distinct bank quads, and the
+// XOR 2 on k & 8 puts the other on the 8 quads left, so each half of the
+// read covers the 256-byte bank window once. The counter reads 0 for this
+// pattern, against 2 conflict cycles per read with the k % 4 term alone.
+FLCE_HD int swz_n(int r, int sk) { return sk == 64 ? (r >> 1) & 7 : (r >> 1) & 3; }
+FLCE_HD int swz_t(int k) {      // {0,6,10,12}[k % 4], XOR 2 when k & 8
+  return ((0xCA60 >> (4 * (k & 3))) & 15) ^ ((k >> 2) & 2);
+}
 
 // Where the fragment reads find an element. N form: the 16-byte chunk (8 k
 // values) c of row r. T form: byte offset of the 4 columns [col, col + 4) of
