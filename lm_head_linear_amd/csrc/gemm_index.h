@@ -29,11 +29,10 @@ enum Form : int { kFormN = 0, kFormT = 1 };
 // the rate of whole lines into a CU. A T-form operand already loads runs of
 // 512 bytes; there a 32-k stage tile spreads the LDS writes evenly over the
 // MFMA steps, which measured faster. Stages: 2 of 64 k (128 KiB of LDS);
-// with both operands transposed 5 of 32 k (160 KiB, a barrier every other
-// step); with a transposed B only 4 of 32 k (128 KiB).
+// with a transposed operand 5 of 32 k (160 KiB, a barrier every other step).
 FLCE_HD constexpr int stage_k(int fa, int fb) { return (fa == kFormN && fb == kFormN) ? 64 : 32; }
 FLCE_HD constexpr int num_stages(int fa, int fb) {
-  return stage_k(fa, fb) == 64 ? 2 : (fa == kFormT && fb == kFormT ? 5 : 4);
+  return stage_k(fa, fb) == 64 ? 2 : 5;
 }
 // 16-byte direct loads per thread per operand per stage tile (256 rows x sk
 // x 2 bytes over 256 threads), and register loads for a partial tile.

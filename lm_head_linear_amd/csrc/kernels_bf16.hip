@@ -436,38 +436,31 @@ __device__ __forceinline__ void k_loop(Acc& acc, const Operand& A, const Operand
                                  st_a(t), st_b(t), wave, wm, wn, lane);
       }
     } else {
-      // Four or five stages of 32 k, one MFMA step per stage tile; tile t
-      // lives in stage t % kStages, is loaded kStages - 1 steps ahead and its
-      // fragments are read during step t-1. Every step issues exactly one
-      // tile (past the last one it re-loads the last into a free stage), so
-      // the number of loads in flight at each wait is the same and the body
-      // has no branches for the scheduler to stop at. Stage indices advance
-      // by one per step in wave-uniform registers.
-      // Four stages (a transposed B only): a barrier at the top of every step
-      // k publishes tile k+1 (this wave's loads up to it have landed; tile k+2
-      // may be in flight), and step k loads tile k+3 into the stage of tile
-      // k-1, whose fragments every wave consumed in step k-2.
-      // Five stages (both operands transposed): a barrier only at even steps.
-      // The barrier at the top of even step k publishes tiles k+1 and k+2
-      // (only tile k+3 may still be in flight) and frees the stages of all
-      // tiles up to k, whose fragments were read before it; step k loads tile
-      // k+4 into the stage of tile k-1 and the odd step k+1 loads tile k+5
-      // into the stage of tile k. Half the barriers measured 1.8% faster for
-      // dW; the K-contiguous G of dH measured slower with five stages.
+      // Five stages of 32 k, one MFMA step per stage tile; tile t lives in
+      // stage t % 5, is loaded 4 steps ahead and its fragments are read
+      // during step t-1. Every step issues exactly one tile (past the last
+      // one it re-loads the last into a free stage), so the number of loads
+      // in flight at each wait is the same and the body has no branches for
+      // the scheduler to stop at. A barrier only at even steps: the barrier
+      // at the top of even step k publishes tiles k+1 and k+2 (only tile k+3
+      // may still be in flight) and frees the stages of all tiles up to k,
+      // whose fragments were read before it; step k loads tile k+4 into the
+      // stage of tile k-1 and the odd step k+1 loads tile k+5 into the stage
+      // of tile k. Stage indices advance by one per step in wave-uniform
+      // registers (5 is not a power of two). With the LDS bank conflicts of
+      // the transposed and 32-k reads removed, five stages measured faster
+      // than four with a barrier per step for dH too (its launch 4% faster).
+      static_assert(kStages == 5, "five stages of 32 k");
       auto next_stage = [](int x) { return x == kStages - 1 ? 0 : x + 1; };
-      constexpr bool kBarrierEachStep = kStages == 4;
 #pragma unroll
       for (int t = 0; t < kStages - 1; ++t) {
         issue_direct<L>(da, t < last ? t : last, st_a(t), wave);
         issue_direct<L>(db, t < last ? t : last, st_b(t), wave);
       }
-      if (kStages == 5)
-        wait_vm24();                               // tile 0 landed (three more in flight)
-      else
-        wait_vm16();                               // tile 0 landed (two more in flight)
+      wait_vm24();                                 // tile 0 landed (three more in flight)
       stage_barrier();
       read_step<FA, FB, SK>(f[0], st_a(0), st_b(0), 0, wm, wn, lane);
-      int s_read = 1, s_load = kStages - 1;        // stages of tiles k+1 and k+kStages-1
+      int s_read = 1, s_load = kStages - 1;        // stages of tiles k+1 and k+4
       int64_t kt = 0;
       // two steps per iteration: the even one with the barrier, then the odd one
       for (; kt + 1 < nfull; kt += 2) {
@@ -475,14 +468,13 @@ __device__ __forceinline__ void k_loop(Acc& acc, const Operand& A, const Operand
         for (int u = 0; u < 2; ++u) {
           const int64_t k = kt + u;
           __builtin_amdgcn_sched_barrier(0);
-          if (u == 0 || kBarrierEachStep) {
+          if (u == 0) {
             wait_vm8();                            // all but the newest tile landed
             stage_barrier();
           }
           const int64_t lt = k + kStages - 1;
-          // a power-of-two stage count indexes by a mask of the step
-          char* sa = kStages == 4 ? st_a(k + 1) : smem + s_read * 2 * kTileBytes;
-          char* la = kStages == 4 ? st_a(lt) : smem + s_load * 2 * kTileBytes;
+          char* sa = smem + s_read * 2 * kTileBytes;
+          char* la = smem + s_load * 2 * kTileBytes;
           k_step<FA, FB, SK, true>(acc, f[u], f[u ^ 1], da, db, lt < last ? lt : last, sa,
                                    sa + kTileBytes, 0, la, la + kTileBytes, wave, wm, wn, lane);
           s_read = next_stage(s_read);
@@ -493,8 +485,8 @@ __device__ __forceinline__ void k_loop(Acc& acc, const Operand& A, const Operand
         wait_vm8();
         stage_barrier();
         const int64_t lt = kt + kStages - 1;
-        char* sa = kStages == 4 ? st_a(kt + 1) : smem + s_read * 2 * kTileBytes;
-        char* la = kStages == 4 ? st_a(lt) : smem + s_load * 2 * kTileBytes;
+        char* sa = smem + s_read * 2 * kTileBytes;
+        char* la = smem + s_load * 2 * kTileBytes;
         k_step<FA, FB, SK, true>(acc, f[0], f[1], da, db, lt < last ? lt : last, sa,
                                  sa + kTileBytes, 0, la, la + kTileBytes, wave, wm, wn, lane);
       }
@@ -561,7 +553,7 @@ __device__ __forceinline__ void gemm_tile(char* smem, int64_t bid, int seg, Oper
   static_assert(kSmemBytes >= 4 * kWaveScratch, "epilogue staging");
   static_assert(kBK == 32 && (SK == 32 || SK == 64), "MFMA steps of 32 k");
   static_assert(2 * L == (SK == 64 ? 16 : 8), "waitcnt immediates");
-  static_assert(SK == 64 ? kStages == 2 : (kStages == 4 || kStages == 5), "pipeline depth");
+  static_assert(SK == 64 ? kStages == 2 : kStages == 5, "pipeline depth");
   if constexpr (DYN == kDynM || DYN == kDynN) {
     // The raster runs over the live tiles: the workgroups past them leave at
     // once, and the live ones are spread over all XCDs (a raster over the

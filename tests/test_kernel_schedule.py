@@ -118,8 +118,8 @@ def _check_loop(sym, fa, fb, seg):
     # 32 transpose reads per T-form operand (8 row blocks of 16 per step)
     reads = (16 if fa == 0 else 32) + (16 if fb == 0 else 32)
     assert count(r"ds_read") == reads, (sym, count(r"ds_read"))
-    # a barrier per two steps, except with a transposed B alone (per step)
-    assert count(r"s_barrier") == (2 if (fa, fb) == (0, 1) else 1), sym
+    # a barrier per two steps
+    assert count(r"s_barrier") == 1, sym
     # a full vmcnt wait only directly before a barrier
     for i, l in enumerate(seg):
         if re.match(r"s_waitcnt\s+vmcnt\(0\)", l):
