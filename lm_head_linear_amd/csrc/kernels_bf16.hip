@@ -617,15 +617,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A, Operand B, int6
 // the kept tokens only, its tiles may fill its last round of workgroups only
 // in part, and the shorter dW tiles behind it fill the rest instead of the
 // next launch starting on an idle chip. One LDS array serves both.
-// SPLIT1: the first GEMM is split along K into segments of kseg1 rows, its
+// SPLIT1: the first GEMM is split along K into segments of off1 rows, its
 // n1 = t1 x segments workgroups segment by segment (workgroup b: segment
 // b / t1, tile b % t1), each writing a partial product of its own.
+// SEGS = 2 (float32 gradients): both GEMMs run their K loop over the hi part
+// of G and then over the lo part, off1 (= off2) elements further.
 template <int FA1, int FB1, class Epi1, int DYN1, bool SPLIT1, int FA2, int FB2, class Epi2,
-          int DYN2>
+          int DYN2, int SEGS>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_pair(
-    int64_t n1p, int64_t t1, int64_t n1, int64_t kseg1, Operand A1, Operand B1, int64_t M1,
+    int64_t n1p, int64_t t1, int64_t n1, int64_t off1, Operand A1, Operand B1, int64_t M1,
     int64_t N1, int64_t K1, Epi1 e1, Operand A2, Operand B2, int64_t M2, int64_t N2, int64_t K2,
-    Epi2 e2, const int64_t* dyn) {
+    Epi2 e2, int64_t off2, const int64_t* dyn) {
+  static_assert(!(SPLIT1 && SEGS == 2), "a split GEMM has one K segment per workgroup");
   constexpr int kB1 = stage_bytes<FA1, FB1>() + Epi1::kTokBytes;
   constexpr int kB2 = stage_bytes<FA2, FB2>() + Epi2::kTokBytes;
   __shared__ __attribute__((aligned(1024))) char smem[kB1 > kB2 ? kB1 : kB2];
@@ -635,14 +638,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_pair(
     if constexpr (SPLIT1) {
       const int64_t seg = b / t1;
       gemm_tile<FA1, FB1, Epi1, true, 1, true, DYN1>(smem, b - seg * t1, int(seg), A1, B1, M1,
-                                                     N1, K1, gemm::kGroupM, e1, kseg1, dyn);
+                                                     N1, K1, gemm::kGroupM, e1, off1, dyn);
     } else {
-      gemm_tile<FA1, FB1, Epi1, true, 1, false, DYN1>(smem, b, 0, A1, B1, M1, N1, K1,
-                                                      gemm::kGroupM, e1, 0, dyn);
+      gemm_tile<FA1, FB1, Epi1, true, SEGS, false, DYN1>(smem, b, 0, A1, B1, M1, N1, K1,
+                                                         gemm::kGroupM, e1, off1, dyn);
     }
   } else {
-    gemm_tile<FA2, FB2, Epi2, true, 1, false, DYN2>(smem, b - n1p, 0, A2, B2, M2, N2, K2,
-                                                    gemm::kGroupM, e2, 0, dyn);
+    gemm_tile<FA2, FB2, Epi2, true, SEGS, false, DYN2>(smem, b - n1p, 0, A2, B2, M2, N2, K2,
+                                                       gemm::kGroupM, e2, off2, dyn);
   }
 }
 
@@ -1592,12 +1595,16 @@ hipError_t run_gemm(const gemm::Launch& l, const Args& a, const Epi& e, int kind
 
 // Two GEMMs whose A operand is the blocked G in one grid (k_gemm_pair): the
 // first launch's tiles (SPLIT1: times its segs1 K segments of kseg1), padded
-// to a multiple of 8 workgroups, then the second's.
+// to a multiple of 8 workgroups, then the second's. SEGS = 2: both over G's
+// hi part and then its lo part, lo_off elements further.
 template <int FA1, int FB1, int DYN1, int FA2, int FB2, int DYN2, bool SPLIT1 = false,
-          class Epi1, class Epi2>
+          int SEGS = 1, class Epi1, class Epi2>
 hipError_t run_gemm_pair(const gemm::Launch& l1, const Epi1& e1, const gemm::Launch& l2,
                          const Epi2& e2, const Args& a, int kind, const Launcher& L,
-                         const int64_t* dyn, int64_t kseg1 = 0, int64_t segs1 = 1) {
+                         const int64_t* dyn, int64_t kseg1 = 0, int64_t segs1 = 1,
+                         int64_t lo_off = 0) {
+  static_assert(SEGS == 1 || SEGS == 2, "one or two K segments");
+  if ((SEGS == 2) != (lo_off != 0)) return hipErrorInvalidValue;
   if (!launch_ok(l1) || !launch_ok(l2)) return hipErrorInvalidValue;
   if (l1.a.blk == 0 || l1.b.blk != 0 || l2.a.blk == 0 || l2.b.blk != 0)
     return hipErrorInvalidValue;
@@ -1613,10 +1620,10 @@ hipError_t run_gemm_pair(const gemm::Launch& l1, const Epi1& e1, const gemm::Lau
   const Operand A1{buf_ptr(a, l1.buf_a) + l1.off_a, l1.a}, B1{buf_ptr(a, l1.buf_b) + l1.off_b, l1.b};
   const Operand A2{buf_ptr(a, l2.buf_a) + l2.off_a, l2.a}, B2{buf_ptr(a, l2.buf_b) + l2.off_b, l2.b};
   L.pre(kind);
-  hipLaunchKernelGGL((k_gemm_pair<FA1, FB1, Epi1, DYN1, SPLIT1, FA2, FB2, Epi2, DYN2>),
+  hipLaunchKernelGGL((k_gemm_pair<FA1, FB1, Epi1, DYN1, SPLIT1, FA2, FB2, Epi2, DYN2, SEGS>),
                      dim3(unsigned(total)), dim3(kThreads), 0, L.stream, n1p, t1, n1,
-                     SPLIT1 ? kseg1 : int64_t(0), A1, B1, l1.M, l1.Nn, l1.K, e1, A2, B2, l2.M,
-                     l2.Nn, l2.K, e2, dyn);
+                     SPLIT1 ? kseg1 : lo_off, A1, B1, l1.M, l1.Nn, l1.K, e1, A2, B2, l2.M,
+                     l2.Nn, l2.K, e2, lo_off, dyn);
   L.post(kind);
   return hipGetLastError();
 }
@@ -1700,22 +1707,21 @@ hipError_t bf16_backward_chunk_f32grad(const Plan& p, const Args& a, int64_t chu
     err = run_gemm<NF, NF, false, 1, false, kDynN>(lg, a, eg, kGradLogits, L, 0, 1, nv);
   }
   if (err != hipSuccess) return err;
+  // dH (its float32 output is its own running sum, rows at the tokens'
+  // positions) and dW, each over G's hi and lo parts, in one grid
   float* dW = static_cast<float*>(a.dW);
-  const gemm::Launch lw = gemm::backward_launch(p, chunk, 1, 0);
-  if (!a.accumulate_dW)
-    err = run_gemm<TF, TF, true, 2, false, kDynK>(lw, a, EpiDW32<false>{dW, p.H, v0, vcur},
-                                                  kGemmDW, L, lo_off, 1, nv);
-  else
-    err = run_gemm<TF, TF, true, 2, false, kDynK>(lw, a, EpiDW32<true>{dW, p.H, v0, vcur},
-                                                  kGemmDW, L, lo_off, 1, nv);
-  if (err != hipSuccess) return err;
   float* dH = static_cast<float*>(a.dH);
+  const gemm::Launch lw = gemm::backward_launch(p, chunk, 1, 0);
   const gemm::Launch lh = gemm::backward_launch(p, chunk, 2, 0);
-  if (chunk == 0)
-    return run_gemm<NF, TF, true, 2, false, kDynM>(
-        lh, a, EpiDH<true, false, true>{nullptr, dH, p.N, p.H, a.idx}, kGemmDH, L, lo_off, 1, nv);
-  return run_gemm<NF, TF, true, 2, false, kDynM>(
-      lh, a, EpiDH<false, false, true>{nullptr, dH, p.N, p.H, a.idx}, kGemmDH, L, lo_off, 1, nv);
+  auto pair = [&](auto edh) {
+    if (a.accumulate_dW)
+      return run_gemm_pair<NF, TF, kDynM, TF, TF, kDynK, false, 2>(
+          lh, edh, lw, EpiDW32<true>{dW, p.H, v0, vcur}, a, kGemmDWDH, L, nv, 0, 1, lo_off);
+    return run_gemm_pair<NF, TF, kDynM, TF, TF, kDynK, false, 2>(
+        lh, edh, lw, EpiDW32<false>{dW, p.H, v0, vcur}, a, kGemmDWDH, L, nv, 0, 1, lo_off);
+  };
+  if (chunk == 0) return pair(EpiDH<true, false, true>{nullptr, dH, p.N, p.H, a.idx});
+  return pair(EpiDH<false, false, true>{nullptr, dH, p.N, p.H, a.idx});
 }
 
 hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, const Launcher& L) {

@@ -97,9 +97,12 @@ def pair_loops(asm):
 
 def test_pair_kernels_keep_both_loops(pair_loops):
     """Each two-GEMM kernel holds the dH loop (G K-contiguous, W transposed)
-    and the dW loop (both transposed), each scheduled like its own kernel."""
+    and the dW loop (both transposed), each scheduled like its own kernel;
+    with two K segments (float32 gradients: G's hi and lo parts, the last
+    template argument 2) each loop twice."""
     for sym, segs in pair_loops.items():
-        assert sorted(f for f, _ in segs) == [(0, 1), (1, 1)], sym
+        n = 2 if re.search(r"ELi2EEEv", sym) else 1
+        assert sorted(f for f, _ in segs) == [(0, 1)] * n + [(1, 1)] * n, sym
         for (fa, fb), seg in segs:
             _check_loop(sym, fa, fb, seg)
 
