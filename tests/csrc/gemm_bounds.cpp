@@ -94,6 +94,26 @@ static void check_lds_layout() {
     }
 }
 
+// The transposed fragment read (ds_read_b64_tr_b16, 8 bytes per lane) of a
+// T-form stage tile: lane i of 16-lane group g reads k-row 8 g + 4 r + i / 4 at
+// columns row_base + 4 (i % 4) .. + 3. Each 32-lane half of the read (served
+// together, the LDS's 64 four-byte banks at once) covers every bank once: the
+// bank-conflict counter on gfx950 reads 0 for this layout.
+static void check_lds_banks_t() {
+  for (int r = 0; r < 2; ++r)
+    for (int rb = 0; rb < kBM; rb += 16)
+      for (int half = 0; half < 2; ++half) {
+        int banks[64] = {0};
+        for (int lane = 32 * half; lane < 32 * half + 32; ++lane) {
+          const int g = lane >> 4, i = lane & 15;
+          const int byte = lds_byte_t(8 * g + 4 * r + (i >> 2), rb + 4 * (i & 3));
+          for (int w = 0; w < 2; ++w) banks[(byte / 4 + w) % 64]++;
+        }
+        for (int b = 0; b < 64; ++b)
+          if (banks[b] != 1) fail("transposed read bank", r, rb, b);
+      }
+}
+
 // Same predicate as the library's launch check: the 32-bit lane offsets fit.
 static bool offsets_fit(int form, const Geom& g) {
   const int64_t reach = form == kFormN ? (g.rows - 1 < 255 ? g.rows - 1 : 255) * g.ld + 64
@@ -202,6 +222,7 @@ int main(int argc, char** argv) {
       // few dH output tiles: split-K segments, ragged last segment, several chunks
       {300, 136, 9000, 0}, {600, 264, 20000, 4096}, {2048, 1024, 33000, 0}};
   check_lds_layout();
+  check_lds_banks_t();
   check_blocked_matches_dense();
   std::printf("lds layout and blocked G: %s\n", failures ? "FAILURES" : "ok");
   if (argc == 5) shapes = {{std::atoll(argv[1]), std::atoll(argv[2]), std::atoll(argv[3]), std::atoll(argv[4])}};
