@@ -42,6 +42,10 @@
  *   - A call allocates nothing, never waits for the device and clears memory
  *     with kernels (no memset nodes), so it can be captured into a HIP graph
  *     and replayed, with the pointers it was captured with (profiling off).
+ *   - Each call opens ROCTX ranges (the entry point's name, then
+ *     "flce.setup", "flce.forward", one "flce.backward_chunk" per vocabulary
+ *     chunk, ...) around the launches it enqueues, for a profiler's marker
+ *     trace; they cost nothing measurable without one.
  */
 #ifndef FLCE_H
 #define FLCE_H
