@@ -140,6 +140,24 @@ def test_odd_hidden_accumulated_dW(vchunk):
     _same_as_padded(w, g, gp)
 
 
+def test_odd_hidden_accumulated_float32_dW(vchunk):
+    """float32 dW added to the caller's at an odd width: the padded float32
+    copy starts from it."""
+    vchunk(256)
+    w = fi.make_custom(500, 61, 1100, dtype=torch.bfloat16, seed=45, ignore_frac=0.2, softcap=30.0)
+    dev = gu.device()
+    dW0 = torch.randn(w.V, w.H, generator=torch.Generator().manual_seed(6)) * 0.1
+    g = gu.run_gpu(w, dW=dW0.to(dev), accumulate_dW=True, grad_dtype=torch.float32)
+    r = gu.run_oracle(w)
+    gu.assert_grad("dW", g["dW"], r.dW + dW0.to(torch.float64).numpy(), gu.GRAD_TOL[torch.float32])
+    gu.assert_grad("dH", g["dH"], r.dH, gu.GRAD_TOL[torch.float32])
+    wp = _padded(w)
+    dW0p = torch.zeros(w.V, wp.H)
+    dW0p[:, :w.H] = dW0
+    gp = gu.run_gpu(wp, dW=dW0p.to(dev), accumulate_dW=True, grad_dtype=torch.float32)
+    _same_as_padded(w, g, gp)
+
+
 def test_odd_hidden_refused_where_h_is_read_in_place():
     import lm_head_linear_amd as m
     w = fi.make_custom(64, 100, 300, dtype=torch.bfloat16, seed=44)
