@@ -78,16 +78,25 @@ __global__ __launch_bounds__(256) void k_lse_merge(
   const int tk = threadIdx.x % kMergeTokens, g = threadIdx.x / kMergeTokens;
   const int64_t t = int64_t(blockIdx.x) * kMergeTokens + tk;
   float M = -INFINITY, S = 0.f;
-  if (t < N) {
-    for (int64_t j = g; j < n_tiles; j += 8) {
-      const float2 q = part[j * ld_part + t];
-      if (q.x > M) {
-        S = (M == -INFINITY ? 0.f : S * exp2f((M - q.x) * kLog2e)) + q.y;
-        M = q.x;
-      } else {
-        S += q.y * exp2f((q.x - M) * kLog2e);
-      }
+  auto merge = [&](float2 q) {
+    if (q.x > M) {
+      S = (M == -INFINITY ? 0.f : S * exp2f((M - q.x) * kLog2e)) + q.y;
+      M = q.x;
+    } else {
+      S += q.y * exp2f((q.x - M) * kLog2e);
     }
+  };
+  if (t < N) {
+    // tiles g, g + 8, ... in order; four loads in flight before they are merged
+    int64_t j = g;
+    for (; j + 24 < n_tiles; j += 32) {
+      float2 q[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) q[u] = part[(j + 8 * u) * ld_part + t];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) merge(q[u]);
+    }
+    for (; j < n_tiles; j += 8) merge(part[j * ld_part + t]);
   }
   grp[g][tk] = make_float2(M, S);
   __syncthreads();
