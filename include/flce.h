@@ -108,11 +108,12 @@ size_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype);
  * Any H > 0 is accepted (the NeMo linear_ce page, "API", puts no limit on the
  * hidden size). The kernels load and store whole 16-byte runs of a bf16 row,
  * so with bf16 inputs and H % 8 != 0 the call runs at the width rounded up to
- * 8 on copies in the workspace: W and the gathered hidden rows zero-padded,
- * dW (from the caller's one when accumulate_dW) and dH computed at that
- * width and copied out to the caller's H columns. The results equal those of
- * the same call on inputs the caller padded with zeros; the workspace grows
- * by the padded W, dW and dH (flce_workspace_size counts them).
+ * 8 on copies in the workspace: W and the gathered hidden rows zero-padded
+ * (a padded copy of h for the entry points that do not gather), dW (from the
+ * caller's one when accumulate_dW) and dH computed at that width and copied
+ * out to the caller's H columns. The results equal those of the same call on
+ * inputs the caller padded with zeros; the workspace grows by the padded
+ * copies (the *_workspace_size functions count them).
  *   FLCE_ERR_WORKSPACE   workspace NULL, not 256-byte aligned, or
  *                        workspace_bytes < flce_workspace_size(...).
  */
@@ -313,8 +314,9 @@ int flce_forward(const void* h, const void* W, const int64_t* labels, int64_t N,
  *          call's contents (the kernels write everything they read back), so
  *          calls that overlap on one GPU (two streams, or two host threads)
  *          race: the caller must serialise them.
- * Shapes   it reads h in place (no gather, to keep its scratch small): bf16
- *          inputs with H % 8 != 0 are FLCE_ERR_UNSUPPORTED.
+ * Shapes   it does not gather the tokens, to keep its scratch small; with
+ *          bf16 inputs and H % 8 != 0 the padded copies of h and W it reads
+ *          count against the scratch (FLCE_ERR_SCRATCH beyond it).
  * Everything else (parameters, outputs, edge cases, errors) as in
  * flce_forward, whose results it reproduces bit for bit (the gather changes
  * no value, and the loss sums the per-token losses by original position).
@@ -362,9 +364,9 @@ int flce_forward_logits_check_args(const void* h, const void* W, const int64_t* 
  *         (FLCE_BF16). Elements v in [V, ld_logits) are not written. Rows are
  *         stored in 16-byte runs when logits and ld_logits keep every run
  *         16-byte aligned, element by element otherwise.
- * Shapes  the logits come out in the tokens' order, so this entry reads h
- *         in place (no gather): bf16 inputs with H % 8 != 0 are
- *         FLCE_ERR_UNSUPPORTED here.
+ * Shapes  the logits come out in the tokens' order, so this entry does not
+ *         gather the tokens: with bf16 inputs and H % 8 != 0 it reads a padded
+ *         copy of h (and of W) in its workspace.
  * Everything else as in flce_forward, with the same workspace
  * (flce_forward_workspace_size): *loss, *num_tokens, lse_out and *status are
  * bit-identical to what flce_forward returns on the same inputs. Cost: the

@@ -119,7 +119,7 @@ hipError_t scratch_address(hipStream_t stream, void** out) {
 // A call whose bf16 rows are padded (Plan::pad_h) runs at the padded width on
 // the workspace's copies: W padded, dW padded from the caller's when it is
 // added to, dH and dW written there and copied out at the end. The gather
-// pads the hidden rows it copies.
+// pads the hidden rows it copies; a call without it reads a padded copy of h.
 hipError_t pad_inputs(const flce::Plan& p, flce::Args& a, char* ws, bool backward,
                       const flce::Launcher& L) {
   if (!p.pad_h) return hipSuccess;
@@ -127,6 +127,11 @@ hipError_t pad_inputs(const flce::Plan& p, flce::Args& a, char* ws, bool backwar
   hipError_t e = flce::launch_copy_rows(a.W, p.h_in, wp, p.H, p.V, p.h_in, p.H, p.elem, L);
   a.W = wp;
   a.H = p.H;
+  if (e == hipSuccess && !p.compact) {
+    void* hp = ws + p.off_hp;
+    e = flce::launch_copy_rows(a.h, p.h_in, hp, p.H, p.N, p.h_in, p.H, p.elem, L);
+    a.h = hp;
+  }
   if (!backward) return e;
   void* dwp = ws + p.off_dwp;
   if (e == hipSuccess && a.accumulate_dW)
@@ -398,9 +403,8 @@ int flce_forward_noalloc(const void* h, const void* W, const int64_t* labels, in
                                    lse_out);
   if (st != FLCE_OK) return st;
   // the forward without the token gather (its scratch is the partials and
-  // per-token arrays alone), bit-identical to flce_forward's results; it
-  // reads h in place, so bf16 rows must be whole 16-byte runs
-  if (dtype == FLCE_BF16 && H % 8 != 0) return FLCE_ERR_UNSUPPORTED;
+  // per-token arrays alone, and padded copies of h and W for a bf16 hidden
+  // size that is not a multiple of 8), bit-identical to flce_forward's results
   flce::Plan p;
   if (!flce::make_plan(N, H, V, dtype, &p, false, -1, 0)) return FLCE_ERR_ARG;
   if (p.total > FLCE_NOALLOC_SCRATCH_BYTES) return FLCE_ERR_SCRATCH;

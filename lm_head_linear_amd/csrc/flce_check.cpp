@@ -13,11 +13,13 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// The padded buffers of a Plan::pad_h call at the padded width: W, and with
+// The padded buffers of a Plan::pad_h call at the padded width: W, h when the
+// call does not gather (the gather pads the rows it copies), and with
 // gradients dW and dH.
 size_t carve_pad(Plan& q, size_t off, bool backward) {
   if (!q.pad_h) return off;
   q.off_wp = off;  off = align256(off + size_t(q.V) * q.H * q.elem);
+  if (!q.compact) { q.off_hp = off; off = align256(off + size_t(q.N) * q.H * q.elem); }
   if (backward) {
     q.off_dwp = off; off = align256(off + size_t(q.V) * q.H * q.grad_elem);
     q.off_dhp = off; off = align256(off + size_t(q.N) * q.H * q.grad_elem);
@@ -49,8 +51,7 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
   if (N > (int64_t(1) << 31) || H > (int64_t(1) << 24) || V > (int64_t(1) << 31)) return false;
   Plan q;
   q.h_in = H;
-  if (dtype == FLCE_BF16 && H % 8 != 0) {
-    if (gather == 0) return false;              // h is read in place: 16-byte rows
+  if (dtype == FLCE_BF16 && H % 8 != 0) {      // see Plan::pad_h
     q.pad_h = true;
     H = round_up(H, 8);
   }
@@ -254,13 +255,8 @@ int check_common(const void* h, const void* W, const int64_t* labels, int64_t N,
   if (!loss || !num_tokens || !W) return FLCE_ERR_ARG;
   if (N > 0 && (!h || !labels)) return FLCE_ERR_ARG;
   if (backward && (!dW || (N > 0 && !dH))) return FLCE_ERR_ARG;
-  // bf16 rows that are not whole 16-byte runs are padded in the workspace,
-  // which only the gathering entry points do (see Plan::pad_h)
-  const bool odd_h = dtype == FLCE_BF16 && H % 8 != 0;
   flce::Plan p;
-  if (!flce::make_plan(N, (odd_h && gather == 0) ? H + 8 - H % 8 : H, V, dtype, &p, backward,
-                       grad_dtype, gather))
-    return FLCE_ERR_ARG;
+  if (!flce::make_plan(N, H, V, dtype, &p, backward, grad_dtype, gather)) return FLCE_ERR_ARG;
   const size_t es = p.elem, gs = p.grad_elem;
   if (backward) {
     if (overlaps(dH, size_t(N) * H * gs, h, size_t(N) * H * es)) return FLCE_ERR_ARG;
@@ -270,7 +266,6 @@ int check_common(const void* h, const void* W, const int64_t* labels, int64_t N,
     if (overlaps(dW, size_t(V) * H * gs, h, size_t(N) * H * es)) return FLCE_ERR_ARG;
   }
   const uintptr_t mask = dtype == FLCE_BF16 ? 15u : 3u;
-  if (odd_h && gather == 0) return FLCE_ERR_UNSUPPORTED;
   if (dtype == FLCE_BF16 && !flce::bf16_shape_ok(N, p.H, V)) return FLCE_ERR_UNSUPPORTED;
   if (misaligned(W, mask) || (N > 0 && misaligned(h, mask))) return FLCE_ERR_UNSUPPORTED;
   // the bf16 kernels write gradients in 16-byte (float32: 4 x 4-byte) runs

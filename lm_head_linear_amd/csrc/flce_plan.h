@@ -110,11 +110,12 @@ struct Plan {
   // bf16 with a hidden size h_in that is not a multiple of 8 (the kernels
   // load and store 16-byte runs of a row): the call runs at the padded width
   // H = round_up(h_in, 8), on a zero-padded copy of W (off_wp), gathered rows
-  // padded the same way, and (with gradients) dW and dH computed at that
-  // width (off_dwp, off_dhp) and copied out to the caller's h_in columns.
+  // padded the same way (or, without the gather, a padded copy of h at
+  // off_hp), and (with gradients) dW and dH computed at that width (off_dwp,
+  // off_dhp) and copied out to the caller's h_in columns.
   int64_t h_in = 0;
   bool pad_h = false;
-  size_t off_wp = 0, off_dwp = 0, off_dhp = 0;
+  size_t off_wp = 0, off_hp = 0, off_dwp = 0, off_dhp = 0;
   // byte offsets into the workspace
   size_t off_scalars = 0, off_part = 0, off_zt = 0, off_lse = 0, off_tokloss = 0,
          off_g = 0, off_dhacc = 0, off_dhpart = 0, off_dwacc = 0, off_idx = 0, off_yc = 0,
@@ -131,8 +132,7 @@ struct Plan {
 // `gather` (bf16 only): gather the non-ignored tokens first (see
 // Plan::compact); < 0 means the default, which gathers for a forward-only
 // plan and for bf16 gradients. The logits-returning forward and the
-// allocation-free one do not gather; without the gather a bf16 H that is not
-// a multiple of 8 has no plan (see Plan::pad_h).
+// allocation-free one do not gather.
 bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backward = true,
                int grad_dtype = -1, int gather = -1);
 

@@ -168,18 +168,20 @@ def test_check_args_errors(lib, kw, code):
 
 def test_odd_hidden_size_runs_padded(lib):
     """bf16 with H % 8 != 0 (the NeMo linear_ce page, "API", puts no limit on
-    the hidden size): the gathering entry points accept it and carve padded
-    copies of W, dW and dH at the width rounded up to 8; the two entry points
-    that read h in place (logits-returning, allocation-free) refuse it."""
+    the hidden size): every entry point accepts it and carves padded copies at
+    the width rounded up to 8: W, dW and dH, and h where the tokens are not
+    gathered (the logits-returning and allocation-free forwards)."""
     assert lib.flce_check_args(*_args(H=12)) == 0
     assert lib.flce_check_args_ex(*_args(H=12), 0) == 0
     assert lib.flce_check_args_nr(*_args(H=12), 0) == 0
     fw = [x for i, x in enumerate(_args(H=12)) if i not in (12, 13, 17)]
     assert lib.flce_forward_check_args(*fw) == 0
     fws = [x for i, x in enumerate(_args(H=12, wsb=1 << 20)) if i not in (12, 13, 17)]
-    assert lib.flce_forward_logits_check_args(*fws, A16 * 2048, 128, 0) == 2
-    assert lib.flce_forward_logits_check_args(*[x for i, x in enumerate(_args(H=16, wsb=1 << 20))
-                                                if i not in (12, 13, 17)], A16 * 2048, 128, 0) == 0
+    assert lib.flce_forward_logits_check_args(*fws, A16 * 2048, 128, 0) == 0
+    # the logits entry (no gather, a padded copy of h instead) fits the forward workspace
+    fwsz = lib.flce_forward_workspace_size(64, 12, 128, 1)
+    fwx = [x for i, x in enumerate(_args(H=12, wsb=fwsz)) if i not in (12, 13, 17)]
+    assert lib.flce_forward_logits_check_args(*fwx, A16 * 2048, 128, 0) == 0
     assert lib.flce_check_args(*_args(H=12, dH=A16)) == 1       # argument errors come first
     N, V = 300, 1000
     for H in (1, 100, 4095):
@@ -344,7 +346,7 @@ def test_forward_logits_check_args_ok(lib):
     (dict(logits=A16 * 1024 + 4096), 1),   # inside the workspace
     (dict(logits=LG + 2), 2),              # float32 logits not 4-byte aligned
     (dict(logits=LG + 1, ldt=1), 2),       # bf16 logits not 2-byte aligned
-    (dict(N=-1), 1), (dict(H=12), 2), (dict(wsb=16), 3),
+    (dict(N=-1), 1), (dict(wsb=16), 3),
 ])
 def test_forward_logits_check_args_errors(lib, kw, code):
     assert lib.flce_forward_logits_check_args(*_largs(**kw)) == code
@@ -518,7 +520,7 @@ def test_noalloc_refusals_before_any_launch(lib):
                                                          "lse")])
     assert call() == _lib.ERR_SCRATCH
     assert call(mb=-1.0) == _lib.ERR_ARG
-    assert call(H=12) == _lib.ERR_UNSUPPORTED
+    assert call(H=12) == _lib.ERR_SCRATCH          # padded copies count against it
     assert call(loss=None) == _lib.ERR_ARG
 
 

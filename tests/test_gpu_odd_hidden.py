@@ -5,8 +5,7 @@ workspace. GPU parity against the float64 oracle for every entry point that
 gathers (bf16 and float32 gradients, the no-recompute variant, forward only),
 with ignored tokens, a softcap, several vocabulary and token chunks and an
 accumulated dW; and bit-identity with the same call made on inputs the
-caller padded with zeros. The entry points that read h in place refuse the
-shape."""
+caller padded with zeros, for the forwards that do not gather too."""
 import numpy as np
 import pytest
 import torch
@@ -158,18 +157,35 @@ def test_odd_hidden_accumulated_float32_dW(vchunk):
     _same_as_padded(w, g, gp)
 
 
-def test_odd_hidden_refused_where_h_is_read_in_place():
+@pytest.mark.parametrize("cap", [0.0, 30.0])
+def test_odd_hidden_logits_and_noalloc(cap):
+    """The two forwards that do not gather (logits-returning, allocation-free)
+    read a padded copy of h: the same bits as on caller-padded inputs, and as
+    flce_forward."""
     import lm_head_linear_amd as m
-    w = fi.make_custom(64, 100, 300, dtype=torch.bfloat16, seed=44)
+    w = fi.make_custom(300, 100, 700, dtype=torch.bfloat16, seed=44, ignore_frac=0.2, softcap=cap)
+    wp = _padded(w)
+    for dt in (torch.float32, torch.bfloat16):
+        a = gu.run_gpu_forward_logits(w, logits_dtype=dt)
+        b = gu.run_gpu_forward_logits(wp, logits_dtype=dt)
+        assert a["status"] == 0 and b["status"] == 0
+        assert _bits(a["loss_t"]).item() == _bits(b["loss_t"]).item()
+        assert torch.equal(_bits(a["lse"]), _bits(b["lse"]))
+        assert torch.equal(_bits(a["logits"]), _bits(b["logits"]))
+    f = gu.run_gpu_forward(w)
+    assert _bits(f["loss_t"]).item() == _bits(a["loss_t"]).item()
+    r = gu.run_oracle(w)
+    gu.assert_loss(f["loss"], r.loss64)
     dev = gu.device()
     h, W, y = w.h.reshape(-1, w.H).to(dev), w.W.to(dev), w.labels.reshape(-1).to(dev)
-    with pytest.raises(m.FlceError) as e:
-        m.flce_forward_logits(h, W, y, logits=torch.empty(64, 300, device=dev))
-    assert e.value.code == 2
-    with pytest.raises(m.FlceError) as e:
-        m.flce_forward_noalloc(h, W, y, loss=torch.empty((), device=dev),
-                               num_tokens=torch.empty((), dtype=torch.int64, device=dev))
-    assert e.value.code == 2
+    loss = torch.empty((), device=dev)
+    nt = torch.empty((), dtype=torch.int64, device=dev)
+    lse = torch.empty(w.N, device=dev)
+    m.flce_forward_noalloc(h, W, y, ignore_index=w.ignore_index, softcap=w.softcap,
+                           reduction=w.reduction, loss=loss, num_tokens=nt, lse_out=lse)
+    torch.cuda.synchronize()
+    assert _bits(loss).item() == _bits(f["loss_t"]).item()
+    assert torch.equal(_bits(lse), _bits(f["lse"]))
 
 
 @pytest.mark.parametrize("k", range(20))
