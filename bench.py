@@ -47,11 +47,40 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_tokens(src: str) -> str:
+    """C/C++ source without its comments, whitespace runs collapsed to one
+    space: what the compiler sees, so that editing a comment does not count as
+    a change of the kernels. String and character literals are kept whole."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        elif c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_digest() -> str:
+    """sha256 (first 16 hex digits) over the library sources' code, comments
+    and layout left out."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(code_tokens(f.read()).encode())
+            h.update(b"\0")
     return h.hexdigest()[:16]
 
 

@@ -11,8 +11,9 @@
 // under the chip's power limit at the same issue rate. Operands go
 // global -> LDS with direct-to-LDS loads (no registers) into XOR-swizzled
 // stages: 2 stages of 64 k when both operands are K-contiguous, 5 of 32 k
-// when both are transposed (dW), 4 of 32 k for dH. A K-contiguous operand's fragments are read with ds_read_b128;
-// one stored with its M/N dimension contiguous is read with the gfx950
+// when either is transposed (dW, dH). A K-contiguous operand's fragments are
+// read with ds_read_b128; one stored with its M/N dimension contiguous is read
+// with the gfx950
 // transpose read ds_read_b64_tr_b16, so no operand is ever transposed in
 // registers or in memory.
 //

@@ -23,6 +23,15 @@ def test_digest_covers_every_library_source():
     assert listed == set(os.listdir(csrc)) - {"__pycache__"}
 
 
+def test_digest_ignores_comments_and_layout_not_code():
+    a = "int f(int x) { return x + 1; } // one\n/* two */"
+    b = "int f(int x) {\n  // another comment\n  return x + 1;\n}"
+    c = "int f(int x) { return x + 2; }"
+    assert bench.code_tokens(a) == bench.code_tokens(b) != bench.code_tokens(c)
+    s = 'const char* p = "a // b /* c */"; char q = \'"\'; char r = \'\\\'\';'
+    assert bench.code_tokens(s) == s
+
+
 def test_traffic_only_for_the_sources_it_was_taken_on(monkeypatch):
     """Counters are reported for the sources they were taken on and for no
     other: the committed summary names its source digest."""
