@@ -1470,9 +1470,10 @@ struct EpiDH {
 };
 
 // ---- split-K dH: one K segment's float32 partial product -----------------
-// Segment blockIdx.y of the launch stores its tile of G . W (over its K
-// range) into part + blockIdx.y * N * H, [N][H] float32; k_dh_reduce adds
-// the segments up.
+// The workgroups of K segment s (blockIdx.y of a k_gemm launch, or the s-th
+// run of tiles of a split k_gemm_pair) store their tiles of G . W over that
+// segment's K range into part + s * seg_stride, [rows][H] float32;
+// k_dh_reduce adds the segments up.
 struct EpiDHPart {
   float* part;
   int64_t N, H;          // rows written (a compact plan cuts N on the device), columns

@@ -269,9 +269,8 @@ __global__ void k_chunk_counts(const Scalars* __restrict__ sc, int64_t N, int al
   cnt[nch + c] = clamp(kept - c * nc);
 }
 
-// Zero rows of dH (16-byte pieces, h8 per row: bf16 or float32) whose token
-// is ignored: the
-// compact backward never writes them.
+// Zero the rows of dH (bf16 or float32, h8 16-byte pieces per row) whose
+// token is ignored: the compact backward never writes them.
 __global__ __launch_bounds__(256) void k_zero_ignored_rows(const int64_t* __restrict__ labels,
                                                            int64_t N, int64_t ignore_index,
                                                            int64_t h8, uint4* __restrict__ dH) {
