@@ -248,6 +248,33 @@ def test_sanitized_host_checks(tmp_path):
     assert "all checks passed" in r.stdout
 
 
+def build_c_caller(out_dir) -> str:
+    """tests/csrc/c_caller.c compiled as C99 (warnings are errors) and linked
+    against the library and the HIP runtime; returns the executable's path."""
+    from lm_head_linear_amd import _lib
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    exe = os.path.join(str(out_dir), "c_caller")
+    r = subprocess.run([gcc, "-std=c99", "-O1", "-Wall", "-Wextra", "-Werror",
+                        "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"),
+                        "-I", os.path.join(ROOT, "include"),
+                        os.path.join(ROOT, "tests", "csrc", "c_caller.c"), "-o", exe,
+                        "-L", libdir, "-lflce", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+                        "-lm", f"-Wl,-rpath,{libdir}", f"-Wl,-rpath,{os.path.join(rocm, 'lib')}"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    return exe
+
+
+def test_header_and_library_usable_from_c(lib, tmp_path):
+    """The boundary is plain C: the header compiles as C99 and a C program
+    links against the library (it runs in the GPU tests)."""
+    assert os.path.exists(build_c_caller(tmp_path))
+
+
 # ------------------------------------------------------- forward-only entry
 def _fargs(**kw):
     a = dict(zip(("h", "W", "labels", "N", "H", "V", "ignore", "softcap", "red", "T", "loss",
