@@ -326,6 +326,7 @@ int flce_forward_logits_check_args(const void* h, const void* W, const int64_t* 
                                    float mb_scale, void* workspace, size_t workspace_bytes,
                                    int32_t* status, float* lse_out, void* logits,
                                    int64_t ld_logits, int logits_dtype) {
+  (void)ignore_index; (void)stream;
   if (logits_dtype != FLCE_F32 && logits_dtype != FLCE_BF16) return FLCE_ERR_ARG;
   if (V > 0 && (ld_logits < V || ld_logits > (int64_t(1) << 31))) return FLCE_ERR_ARG;
   if (N > 0 && !logits) return FLCE_ERR_ARG;

@@ -531,11 +531,11 @@ __device__ __forceinline__ void gemm_tile(char* smem, int64_t bid, int seg, Oper
   // SEGS = 2: a second K loop over A shifted by a2_off elements (the lo half
   // of a split G) against the same B, into the same accumulators, so the
   // tile is (A + A2) . B^T with one epilogue.
-  // SPLITK: the launch is split along K into segments of a2_off (a multiple
-  // of 64); workgroup row `seg` takes segment `seg` (gemm::split_segment) and
-  // its epilogue writes a partial product.
+  // SPLITK: the GEMM is split along K into segments of a2_off (a multiple of
+  // 64); this workgroup takes segment `seg` and its epilogue writes a partial
+  // product.
   static_assert(SEGS == 1 || SEGS == 2, "one or two K segments");
-  static_assert(!(SPLITK && SEGS == 2), "a split launch has one K segment per workgroup row");
+  static_assert(!(SPLITK && SEGS == 2), "a split GEMM has one K segment per workgroup");
   if constexpr (!BA) A.g.blk = 0;
   B.g.blk = 0;
   if constexpr (SPLITK) {
@@ -598,18 +598,17 @@ __device__ __forceinline__ void gemm_tile(char* smem, int64_t bid, int seg, Oper
   epi(acc, m0, n0, wm, wn, lane, smem, smem + kSmemBytes);
 }
 
-// A GEMM launch: one workgroup per tile (and per K segment of a split launch).
-// The stages are one __shared__ array: with a second LDS object the compiler
-// can no longer tell the direct-to-LDS writes of one stage from the reads of
-// another and serialises the pipeline.
-template <int FA, int FB, class Epi, bool BA, int SEGS, bool SPLITK, int DYN>
+// A GEMM launch over dense operands (the forward and gradient GEMMs): one
+// workgroup per tile. The stages are one __shared__ array: with a second LDS
+// object the compiler can no longer tell the direct-to-LDS writes of one
+// stage from the reads of another and serialises the pipeline.
+template <int FA, int FB, class Epi, int DYN>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm(Operand A, Operand B, int64_t M,
                                                       int64_t Nn, int64_t K, int group_m,
-                                                      Epi epi, int64_t a2_off,
-                                                      const int64_t* dyn) {
+                                                      Epi epi, const int64_t* dyn) {
   __shared__ __attribute__((aligned(1024))) char smem[stage_bytes<FA, FB>() + Epi::kTokBytes];
-  gemm_tile<FA, FB, Epi, BA, SEGS, SPLITK, DYN>(smem, blockIdx.x, blockIdx.y, A, B, M, Nn, K,
-                                                group_m, epi, a2_off, dyn);
+  gemm_tile<FA, FB, Epi, false, 1, false, DYN>(smem, blockIdx.x, 0, A, B, M, Nn, K, group_m, epi,
+                                               0, dyn);
 }
 
 // Two independent GEMMs of one backward chunk in one grid: the n1 workgroups
@@ -1470,10 +1469,9 @@ struct EpiDH {
 };
 
 // ---- split-K dH: one K segment's float32 partial product -----------------
-// The workgroups of K segment s (blockIdx.y of a k_gemm launch, or the s-th
-// run of tiles of a split k_gemm_pair) store their tiles of G . W over that
-// segment's K range into part + s * seg_stride, [rows][H] float32;
-// k_dh_reduce adds the segments up.
+// The workgroups of K segment s (the s-th run of dH tiles of a split
+// k_gemm_pair) store their tiles of G . W over that segment's K range into
+// part + s * seg_stride, [rows][H] float32; k_dh_reduce adds the segments up.
 struct EpiDHPart {
   float* part;
   int64_t N, H;          // rows written (a compact plan cuts N on the device), columns
@@ -1577,20 +1575,17 @@ bool launch_ok(const gemm::Launch& l) {
   return l.M > 0 && l.Nn > 0 && l.K > 0;
 }
 
-template <int FA, int FB, bool BA = false, int SEGS = 1, bool SPLITK = false, int DYN = kDynNone,
-          class Epi>
+template <int FA, int FB, int DYN = kDynNone, class Epi>
 hipError_t run_gemm(const gemm::Launch& l, const Args& a, const Epi& e, int kind,
-                    const Launcher& L, int64_t a2_off = 0, int64_t segs = 1,
-                    const int64_t* dyn = nullptr) {
+                    const Launcher& L, const int64_t* dyn = nullptr) {
   if (!launch_ok(l)) return hipErrorInvalidValue;
-  if ((l.a.blk != 0) != BA || l.b.blk != 0) return hipErrorInvalidValue;
+  if (l.a.blk != 0 || l.b.blk != 0) return hipErrorInvalidValue;
   if ((DYN != kDynNone) != (dyn != nullptr)) return hipErrorInvalidValue;
   Operand A{buf_ptr(a, l.buf_a) + l.off_a, l.a};
   Operand B{buf_ptr(a, l.buf_b) + l.off_b, l.b};
   L.pre(kind);
-  hipLaunchKernelGGL((k_gemm<FA, FB, Epi, BA, SEGS, SPLITK, DYN>),
-                     dim3(unsigned(gemm::num_tiles(l.M, l.Nn)), unsigned(segs)), dim3(kThreads), 0,
-                     L.stream, A, B, l.M, l.Nn, l.K, gemm::kGroupM, e, a2_off, dyn);
+  hipLaunchKernelGGL((k_gemm<FA, FB, Epi, DYN>), dim3(unsigned(gemm::num_tiles(l.M, l.Nn))),
+                     dim3(kThreads), 0, L.stream, A, B, l.M, l.Nn, l.K, gemm::kGroupM, e, dyn);
   L.post(kind);
   return hipGetLastError();
 }
@@ -1652,7 +1647,7 @@ hipError_t bf16_forward_out(const Plan& p, const Args& a, const Launcher& L) {
         e.probs = static_cast<uint16_t*>(a.g);
         e.pc_rows = gemm::chunk_rows(p, 0);
         e.pblk = gemm::g_block(p);
-        return nv ? run_gemm<NF, NF, false, 1, false, kDynN>(l, a, e, kLseFwd, L, 0, 1, nv)
+        return nv ? run_gemm<NF, NF, kDynN>(l, a, e, kLseFwd, L, nv)
                   : run_gemm<NF, NF>(l, a, e, kLseFwd, L);
       };
       if (a.softcap > 0.f)
@@ -1666,12 +1661,12 @@ hipError_t bf16_forward_out(const Plan& p, const Args& a, const Launcher& L) {
   if (a.softcap > 0.f) {
     EpiLse<true, OUT> e{lab, p.N, p.V, a.ignore_index, a.softcap, 1.f / a.softcap, a.part,
                         p.ld_part, a.zt, a.logits, a.ld_logits, vec};
-    return nv ? run_gemm<NF, NF, false, 1, false, kDynN>(l, a, e, kLseFwd, L, 0, 1, nv)
+    return nv ? run_gemm<NF, NF, kDynN>(l, a, e, kLseFwd, L, nv)
               : run_gemm<NF, NF>(l, a, e, kLseFwd, L);
   }
   EpiLse<false, OUT> e{lab, p.N, p.V, a.ignore_index, 0.f, 0.f, a.part, p.ld_part, a.zt,
                        a.logits, a.ld_logits, vec};
-  return nv ? run_gemm<NF, NF, false, 1, false, kDynN>(l, a, e, kLseFwd, L, 0, 1, nv)
+  return nv ? run_gemm<NF, NF, kDynN>(l, a, e, kLseFwd, L, nv)
             : run_gemm<NF, NF>(l, a, e, kLseFwd, L);
 }
 }  // namespace
@@ -1702,11 +1697,11 @@ hipError_t bf16_backward_chunk_f32grad(const Plan& p, const Args& a, int64_t chu
   if (a.softcap > 0.f) {
     const EpiGrad<true, true> eg{a.yc, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
                                  gemm::g_block(p), a.softcap, 1.f / a.softcap, g, lo_off};
-    err = run_gemm<NF, NF, false, 1, false, kDynN>(lg, a, eg, kGradLogits, L, 0, 1, nv);
+    err = run_gemm<NF, NF, kDynN>(lg, a, eg, kGradLogits, L, nv);
   } else {
     const EpiGrad<false, true> eg{a.yc, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
                                   gemm::g_block(p), 0.f, 0.f, g, lo_off};
-    err = run_gemm<NF, NF, false, 1, false, kDynN>(lg, a, eg, kGradLogits, L, 0, 1, nv);
+    err = run_gemm<NF, NF, kDynN>(lg, a, eg, kGradLogits, L, nv);
   }
   if (err != hipSuccess) return err;
   // dH (its float32 output is its own running sum, rows at the tokens'
@@ -1758,11 +1753,11 @@ hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, cons
   } else if (a.softcap > 0.f) {
     const EpiGrad<true, false> eg{a.yc, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
                                   gemm::g_block(p), a.softcap, 1.f / a.softcap, g, 0};
-    err = run_gemm<NF, NF, false, 1, false, kDynN>(lg, a, eg, kGradLogits, L, 0, 1, nv);
+    err = run_gemm<NF, NF, kDynN>(lg, a, eg, kGradLogits, L, nv);
   } else {
     const EpiGrad<false, false> eg{a.yc, a.lse, a.zt, a.sc, p.N, p.V, a.ignore_index, v0, vcur,
                                    gemm::g_block(p), 0.f, 0.f, g, 0};
-    err = run_gemm<NF, NF, false, 1, false, kDynN>(lg, a, eg, kGradLogits, L, 0, 1, nv);
+    err = run_gemm<NF, NF, kDynN>(lg, a, eg, kGradLogits, L, nv);
   }
   if (err != hipSuccess) return err;
   // 2) dW[v0:v0+vcur] = G^T . h (K = the kept tokens) and 3) dH (+)= G . W[chunk]
@@ -1819,11 +1814,11 @@ hipError_t bf16_nr_forward_chunk(const Plan& p, const Args& a, int64_t c, const 
   if (a.softcap > 0.f) {
     EpiLseP<true> e{a.yc + t0, nt, p.V, a.ignore_index, a.softcap, 1.f / a.softcap, a.part,
                     p.ld_part, a.zt, probs, gemm::nr_block(p)};
-    return run_gemm<NF, NF, false, 1, false, kDynN>(l, a, e, kLseFwd, L, 0, 1, cf);
+    return run_gemm<NF, NF, kDynN>(l, a, e, kLseFwd, L, cf);
   }
   EpiLseP<false> e{a.yc + t0, nt, p.V, a.ignore_index, 0.f, 0.f, a.part, p.ld_part, a.zt,
                    probs, gemm::nr_block(p)};
-  return run_gemm<NF, NF, false, 1, false, kDynN>(l, a, e, kLseFwd, L, 0, 1, cf);
+  return run_gemm<NF, NF, kDynN>(l, a, e, kLseFwd, L, cf);
 }
 
 hipError_t bf16_nr_backward_chunk(const Plan& p, const Args& a, int64_t c, const Launcher& L) {
