@@ -36,8 +36,14 @@ from . import _lib
 
 __all__ = [
     "flce_workspace_size",
+    "flce_workspace_size_ex",
+    "flce_vocab_chunk_ex",
     "flce_check_args",
+    "flce_check_args_ex",
+    "flce_check_args_nr",
     "flce_forward_backward",
+    "flce_forward_backward_ex",
+    "flce_forward_backward_nr",
     "flce_workspace_size_nr",
     "flce_token_chunk_nr",
     "flce_forward",
@@ -51,6 +57,8 @@ __all__ = [
     "flce_profile_begin",
     "flce_profile_end",
     "flce_profile_query",
+    "flce_profile_kinds",
+    "flce_kernel_kind_name",
     "kernel_kinds",
     "fused_linear_cross_entropy",
     "FusedLinearCrossEntropy",
@@ -114,6 +122,17 @@ def flce_vocab_chunk(N: int, H: int, V: int, dtype: torch.dtype,
     return int(_lib.load().flce_vocab_chunk_ex(N, H, V, _dtype_code(dtype), g))
 
 
+def flce_workspace_size_ex(N: int, H: int, V: int, dtype: torch.dtype,
+                           grad_dtype: torch.dtype) -> int:
+    """Workspace of the float32-gradient entry (grad_dtype float32 with bf16)."""
+    return flce_workspace_size(N, H, V, dtype, grad_dtype)
+
+
+def flce_vocab_chunk_ex(N: int, H: int, V: int, dtype: torch.dtype,
+                        grad_dtype: torch.dtype) -> int:
+    return flce_vocab_chunk(N, H, V, dtype, grad_dtype)
+
+
 def _abi_args(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens,
               loss, num_tokens, dH, dW, stream, dtype, mb_scale, accumulate_dW, workspace,
               status, lse_out):
@@ -134,6 +153,23 @@ def flce_check_args(h, W, labels, *, N, H, V, ignore_index=-100, softcap=0.0, re
                      status, lse_out)
     g = _dtype_code(grad_dtype if grad_dtype is not None else dtype)
     return int(_lib.load().flce_check_args_ex(*args, g))
+
+
+def flce_check_args_ex(h, W, labels, *, grad_dtype, **kw) -> int:
+    """flce_check_args with the gradients' dtype given explicitly."""
+    return flce_check_args(h, W, labels, grad_dtype=grad_dtype, **kw)
+
+
+def flce_check_args_nr(h, W, labels, *, N, H, V, ignore_index=-100, softcap=0.0,
+                       reduction="sum", num_label_tokens=None, loss=None, num_tokens=None,
+                       dH=None, dW=None, dtype=torch.bfloat16, mb_scale=1.0,
+                       accumulate_dW=False, workspace=None, status=None, lse_out=None,
+                       token_chunk=0) -> int:
+    """The no-recompute entry's synchronous checks (no GPU work); a status code."""
+    args = _abi_args(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens,
+                     loss, num_tokens, dH, dW, None, dtype, mb_scale, accumulate_dW, workspace,
+                     status, lse_out)
+    return int(_lib.load().flce_check_args_nr(*args, int(token_chunk)))
 
 
 def _fwd_abi_args(h, W, labels, N, H, V, ignore_index, softcap, reduction, num_label_tokens,
@@ -254,6 +290,19 @@ def flce_forward_backward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor
     if rc != _lib.OK:
         raise FlceError(rc, "flce_forward_backward")
     return loss, num_tokens, dH, dW
+
+
+def flce_forward_backward_ex(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, *,
+                             grad_dtype: torch.dtype, **kw):
+    """flce_forward_backward with dH and dW of dtype ``grad_dtype`` (float32 with
+    bf16 inputs: the float32-gradient mode)."""
+    return flce_forward_backward(h, W, labels, grad_dtype=grad_dtype, **kw)
+
+
+def flce_forward_backward_nr(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, *,
+                             token_chunk: int = 0, **kw):
+    """The no-recompute variant: flce_forward_backward(..., recompute=False)."""
+    return flce_forward_backward(h, W, labels, recompute=False, token_chunk=token_chunk, **kw)
 
 
 def flce_forward(h: torch.Tensor, W: torch.Tensor, labels: torch.Tensor, *,
@@ -413,9 +462,16 @@ def flce_profile_end() -> None:
         raise FlceError(rc, "flce_profile_end")
 
 
+def flce_profile_kinds() -> int:
+    return int(_lib.load().flce_profile_kinds())
+
+
+def flce_kernel_kind_name(kind: int) -> str:
+    return _lib.load().flce_kernel_kind_name(int(kind)).decode()
+
+
 def kernel_kinds():
-    lib = _lib.load()
-    return [lib.flce_kernel_kind_name(k).decode() for k in range(lib.flce_profile_kinds())]
+    return [flce_kernel_kind_name(k) for k in range(flce_profile_kinds())]
 
 
 def flce_profile_query():

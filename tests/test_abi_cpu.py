@@ -231,6 +231,62 @@ def test_python_binding_validation_without_gpu():
     assert m.micro_batch_scale(3, 12, "sum") == 1.0
 
 
+class _FakeBuf:
+    """Stands in for a device tensor in the binding's check wrappers, which
+    only read its address and size (never its contents)."""
+
+    def __init__(self, addr, nbytes=0):
+        self.addr, self.nbytes = addr, nbytes
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return self.nbytes
+
+    def element_size(self):
+        return 1
+
+
+def test_python_binding_has_every_abi_name(lib):
+    """The binding offers each entry point of the header under its own name."""
+    import lm_head_linear_amd as m
+    for n in declared_functions():
+        assert callable(getattr(m, n, None)), n
+        assert n in m.__all__, n
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(wsb=16), dict(red=1, T=7), dict(dH=None),
+                                dict(mb=-0.5)])
+def test_python_check_wrappers_match_the_library(lib, kw):
+    import lm_head_linear_amd as m
+    a = dict(zip(("h", "W", "labels", "N", "H", "V", "ignore", "softcap", "red", "T", "loss",
+                  "nt", "dH", "dW", "stream", "dtype", "mb", "acc", "ws", "wsb", "status",
+                  "lse"), _args(**kw)))
+    f = lambda x: None if x is None else _FakeBuf(x)
+    py = dict(N=a["N"], H=a["H"], V=a["V"], ignore_index=a["ignore"], softcap=a["softcap"],
+              reduction="mean" if a["red"] == 1 else "sum", num_label_tokens=a["T"] or None,
+              loss=f(a["loss"]), num_tokens=f(a["nt"]), dH=f(a["dH"]), dW=f(a["dW"]),
+              dtype=torch.bfloat16, mb_scale=a["mb"], workspace=_FakeBuf(a["ws"], a["wsb"]))
+    h, W, y = _FakeBuf(a["h"]), _FakeBuf(a["W"]), _FakeBuf(a["labels"])
+    assert m.flce_check_args_nr(h, W, y, token_chunk=256, **py) == \
+        lib.flce_check_args_nr(*_args(**kw), 256)
+    assert m.flce_check_args_ex(h, W, y, grad_dtype=torch.float32, **py) == \
+        lib.flce_check_args_ex(*_args(**kw), 0)
+    assert m.flce_check_args(h, W, y, **py) == lib.flce_check_args(*_args(**kw))
+
+
+def test_python_size_and_profile_wrappers_match_the_library(lib):
+    import lm_head_linear_amd as m
+    bf, f32 = torch.bfloat16, torch.float32
+    assert m.flce_workspace_size_ex(8192, 4096, 131072, bf, f32) == \
+        lib.flce_workspace_size_ex(8192, 4096, 131072, 1, 0)
+    assert m.flce_vocab_chunk_ex(8192, 4096, 131072, bf, f32) == \
+        lib.flce_vocab_chunk_ex(8192, 4096, 131072, 1, 0)
+    assert m.flce_profile_kinds() == lib.flce_profile_kinds()
+    assert m.kernel_kinds()[0] == m.flce_kernel_kind_name(0) == "label_scan"
+
+
 def test_sanitized_host_checks(tmp_path):
     """flce_check.cpp under AddressSanitizer + UBSan, driven by a C test program."""
     gpp = shutil.which("g++")
