@@ -197,11 +197,11 @@ int run_nr(const void* h, const void* W, const int64_t* labels, int64_t N, int64
   {
     Range r("flce.setup");
     e = pad_inputs(p, a, ws, true, L);
-    if (e == hipSuccess) e = flce::launch_label_scan(p, a, L);
-    // the tokens gathered, the kept ones first; the chunks run over that order
-    // (the ignored tokens only for their lse, when it is asked for)
+    // the labels scanned and the tokens gathered, the kept ones first; the
+    // chunks run over that order (the ignored tokens only for their lse, when
+    // it is asked for)
     const bool all_rows = lse_out != nullptr;
-    if (e == hipSuccess) e = flce::launch_gather(p, a, all_rows, L);
+    if (e == hipSuccess) e = flce::launch_scan_gather(p, a, all_rows, L);
     if (e == hipSuccess) e = flce::launch_chunk_counts(p, a, all_rows, L);
   }
   for (int64_t c = 0; e == hipSuccess && c < p.n_tok_chunks; ++c) {
@@ -269,10 +269,12 @@ int run(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t 
   {
     Range r("flce.setup");
     e = pad_inputs(p, a, ws, backward, L);
-    if (e == hipSuccess) e = flce::launch_label_scan(p, a, L);
-    // a compact plan gathers the tokens first, the kept ones in front; the
-    // forward then skips the ignored ones unless their lse is asked for
-    if (e == hipSuccess && p.compact) e = flce::launch_gather(p, a, lse_out != nullptr, L);
+    // a compact plan gathers the tokens with the label scan, the kept ones in
+    // front; the forward then skips the ignored ones unless their lse is asked
+    // for
+    if (e == hipSuccess)
+      e = p.compact ? flce::launch_scan_gather(p, a, lse_out != nullptr, L)
+                    : flce::launch_label_scan(p, a, L);
   }
   {
     Range r("flce.forward");

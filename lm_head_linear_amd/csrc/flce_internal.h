@@ -91,11 +91,11 @@ hipError_t launch_zero_bytes(void* ptr, size_t bytes, const Launcher& L);
 hipError_t launch_copy_rows(const void* src, int64_t ld_src, void* dst, int64_t ld_dst,
                             int64_t rows, int64_t cols, int64_t width, size_t elem,
                             const Launcher& L);
-// Compact plan, before the forward: gather the tokens, the non-ignored ones
-// first (positions, labels, the hidden rows of the first `rows` of them: the
-// kept ones, or all N), give ignored tokens a zero loss, and zero the dH rows
-// of the ignored ones.
-hipError_t launch_gather(const Plan& p, const Args& a, bool all_rows, const Launcher& L);
+// Compact plan, first on the stream: the label scan (as launch_label_scan),
+// then the tokens gathered, the non-ignored ones first (positions, labels,
+// the hidden rows of the first `rows` of them: the kept ones, or all N),
+// ignored tokens given a zero loss and their dH rows zeroed (a.dH non-null).
+hipError_t launch_scan_gather(const Plan& p, const Args& a, bool all_rows, const Launcher& L);
 // No-recompute variant after the gather: the live tokens of every token chunk
 // of nc gathered rows, for the forward (all N, or the kept ones) and for the
 // backward (the kept ones).

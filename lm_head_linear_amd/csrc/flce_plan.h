@@ -32,7 +32,7 @@ constexpr int64_t kMaxTiles = (int64_t(1) << 31) - 1;
 // (tile, segment), whose float32 partial products a fixed-order reduction
 // then adds up.
 constexpr int64_t kSplitTiles = 128;
-constexpr int64_t kMaxSplits = 8;
+constexpr int64_t kMaxSplits = 4;
 constexpr int64_t kMinSplitK = 2048;
 
 // The segment length (a multiple of 64) for a dH GEMM with an M x Nn output

@@ -215,18 +215,160 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_tokens(
   if (!keep) tok_loss[t] = 0.0;           // not merged when the forward skips it
 }
 
+// The label scan and the token gather in one workgroup, for N up to
+// kScanGatherMax tokens (one launch instead of three). In a pass of kScanPass
+// tokens every thread counts a group of kScanPer consecutive ones (their
+// flags staged in LDS from coalesced loads), so a pass needs one exclusive
+// scan over the workgroup of the groups' counts: the kept tokens in the low
+// 32 bits, the kept ones with a label outside [0, V) in the high 32 (neither
+// sum reaches 2^32). With more than one pass, a first sweep counts the
+// tokens for the totals. From the totals it fixes the scale c and num_tokens
+// as k_label_scan does, and it places each token as k_gather_tokens does: a
+// kept one at its rank among the kept ones, an ignored one at n_valid plus
+// its rank among the ignored ones.
+constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 8;
+constexpr int64_t kScanPass = int64_t(kScanThreads) * kScanPer;
+constexpr int64_t kScanGatherMax = 8 * kScanPass;
+constexpr uint64_t kLow32 = 0xffffffffull;
+
+// Exclusive prefix sum over the workgroup of x (one value per thread) and the
+// total, through the 16 wave sums in `wsum`.
+__device__ __forceinline__ uint64_t block_exclusive_scan(uint64_t x, uint64_t* wsum,
+                                                         uint64_t* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint64_t inc = x;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t o = __shfl_up(inc, off);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  uint64_t before = 0, all = 0;
+  for (int i = 0; i < kScanThreads / 64; ++i) {
+    before += i < w ? wsum[i] : 0;
+    all += wsum[i];
+  }
+  __syncthreads();                                 // wsum is reused by the next scan
+  *total = all;
+  return before + inc - x;
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_scan_gather(
+    const int64_t* __restrict__ labels, int64_t N, int64_t V, int64_t ignore_index,
+    int reduction, int64_t T, float mb_scale, Scalars* __restrict__ sc,
+    int64_t* __restrict__ num_tokens, int32_t* __restrict__ status, int32_t* __restrict__ idx,
+    int64_t* __restrict__ yc, double* __restrict__ tok_loss) {
+  __shared__ uint64_t wsum[kScanThreads / 64];
+  // a pass's flags in token order (bit 0 kept, bit 1 a kept one with a bad
+  // label), and per group of kScanPer tokens its kept mask and the kept
+  // tokens of the pass before it: loads and stores run in token order across
+  // the threads (coalesced), the scan over the groups
+  __shared__ __attribute__((aligned(16))) unsigned char flag[kScanPass];
+  __shared__ unsigned char gmask[kScanThreads];
+  __shared__ uint32_t gpref[kScanThreads];
+  const int tid = threadIdx.x;
+  const bool one_pass = N <= kScanPass;
+  uint64_t totals = 0;                             // kept | bad << 32, all tokens
+  if (!one_pass) {
+    uint64_t c = 0;
+    for (int64_t t = tid; t < N; t += kScanThreads) {
+      const int64_t y = labels[t];
+      if (y != ignore_index) c += (y < 0 || y >= V) ? (uint64_t(1) << 32) + 1 : 1;
+    }
+    block_exclusive_scan(c, wsum, &totals);
+  }
+  int64_t kept_before_pass = 0;
+  for (int64_t p0 = 0; p0 < N; p0 += kScanPass) {
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) {
+      const int64_t t = p0 + u * kScanThreads + tid;
+      const int64_t y = t < N ? labels[t] : ignore_index;
+      flag[u * kScanThreads + tid] = y != ignore_index ? ((y < 0 || y >= V) ? 3 : 1) : 0;
+    }
+    __syncthreads();
+    // group tid: tokens p0 + kScanPer tid ...
+    const uint2 f8 = *reinterpret_cast<const uint2*>(flag + tid * kScanPer);
+    unsigned keep = 0;
+    uint64_t c = 0;
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) {
+      const unsigned fu = ((u < 4 ? f8.x : f8.y) >> (8 * (u & 3))) & 0xffu;
+      keep |= (fu & 1u) << u;
+      c += (fu & 1u) + (uint64_t(fu >> 1) << 32);
+    }
+    uint64_t pass_totals = 0;
+    const uint64_t before = block_exclusive_scan(c, wsum, &pass_totals);
+    gmask[tid] = (unsigned char)keep;
+    gpref[tid] = uint32_t(before & kLow32);
+    if (one_pass) totals = pass_totals;
+    const int64_t n = int64_t(totals & kLow32);
+    __syncthreads();
+    // token p0 + i, i = u kScanThreads + tid: its rank among the kept ones
+#pragma unroll
+    for (int u = 0; u < kScanPer; ++u) {
+      const int i = u * kScanThreads + tid;
+      const int64_t t = p0 + i;
+      if (t < N) {
+        const int g = i / kScanPer, r = i % kScanPer;
+        const bool k = flag[i] & 1u;
+        const int64_t kept = kept_before_pass + gpref[g] + __builtin_popcount(gmask[g] & ((1u << r) - 1u));
+        const int64_t pos = k ? kept : n + (t - kept);
+        idx[pos] = int32_t(t);
+        yc[pos] = labels[t];
+        if (!k) tok_loss[t] = 0.0;        // not merged when the forward skips it
+      }
+    }
+    kept_before_pass += int64_t(pass_totals & kLow32);
+    __syncthreads();                               // the staging is rewritten by the next pass
+  }
+  if (tid == 0) {
+    const int64_t n = int64_t(totals & kLow32), bad = int64_t(totals >> 32);
+    double c;
+    if (reduction == FLCE_SUM) c = T > 0 ? double(mb_scale) / double(T) : double(mb_scale);
+    else c = double(mb_scale) / double(n > 1 ? n : 1);
+    sc->n_valid = n;
+    sc->n_bad = bad;
+    sc->c64 = c;
+    sc->c32 = float(c);
+    *num_tokens = reduction == FLCE_SUM ? n : 0;
+    if (status) *status = bad ? FLCE_ERR_LABEL : FLCE_OK;
+  }
+}
+
+// The dH rows (g16 16-byte pieces each) of the ignored tokens, gathered rows
+// n_valid .. N-1, zeroed: the compact backward never writes them. Grid-stride
+// over the launch.
+__device__ __forceinline__ void zero_ignored_rows(const int32_t* __restrict__ idx, int64_t N,
+                                                  const Scalars* __restrict__ sc, int64_t g16,
+                                                  uint4* __restrict__ dH) {
+  if (!dH) return;
+  const int64_t kept = sc->n_valid;
+  const int64_t total = (N - kept) * g16;
+  const uint4 z = {0u, 0u, 0u, 0u};
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total;
+       i += int64_t(gridDim.x) * 256) {
+    const int64_t r = i / g16;
+    dH[int64_t(idx[kept + r]) * g16 + (i - r * g16)] = z;
+  }
+}
+
 // hc[r] = h[idx[r]] for the first `rows` gathered rows (*rows_dev, or all
-// N), in 16-byte pieces (h8 per row).
+// N), in 16-byte pieces (h8 per row); then the dH rows of the ignored tokens
+// zeroed (dH null: no gradients).
 __global__ __launch_bounds__(256) void k_gather_rows(const uint4* __restrict__ h, int64_t h8,
                                                      const int32_t* __restrict__ idx,
                                                      const int64_t* __restrict__ rows_dev,
-                                                     int64_t rows, uint4* __restrict__ hc) {
+                                                     int64_t rows, uint4* __restrict__ hc,
+                                                     const Scalars* __restrict__ sc,
+                                                     int64_t g16, uint4* __restrict__ dH) {
   const int64_t total = (rows_dev ? *rows_dev : rows) * h8;
   for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total;
        i += int64_t(gridDim.x) * 256) {
     const int64_t r = i / h8;
     hc[i] = h[int64_t(idx[r]) * h8 + (i - r * h8)];
   }
+  zero_ignored_rows(idx, rows, sc, g16, dH);
 }
 
 // k_gather_rows for hidden rows of h_in bf16 values (h_in % 8 != 0), stored
@@ -235,13 +377,16 @@ __global__ __launch_bounds__(256) void k_gather_rows_pad(const uint16_t* __restr
                                                          int64_t h_in, int64_t hp,
                                                          const int32_t* __restrict__ idx,
                                                          const int64_t* __restrict__ rows_dev,
-                                                         int64_t rows, uint16_t* __restrict__ hc) {
+                                                         int64_t rows, uint16_t* __restrict__ hc,
+                                                         const Scalars* __restrict__ sc,
+                                                         int64_t g16, uint4* __restrict__ dH) {
   const int64_t total = (rows_dev ? *rows_dev : rows) * hp;
   for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < total;
        i += int64_t(gridDim.x) * 256) {
     const int64_t r = i / hp, c = i - r * hp;
     hc[i] = c < h_in ? h[int64_t(idx[r]) * h_in + c] : uint16_t(0);
   }
+  zero_ignored_rows(idx, rows, sc, g16, dH);
 }
 
 // Row copy between widths: row r of dst (stride ld_dst) gets the first `cols`
@@ -267,17 +412,6 @@ __global__ void k_chunk_counts(const Scalars* __restrict__ sc, int64_t N, int al
   auto clamp = [&](int64_t x) { return x < 0 ? int64_t(0) : (x > nc ? nc : x); };
   cnt[c] = clamp(fwd - c * nc);
   cnt[nch + c] = clamp(kept - c * nc);
-}
-
-// Zero the rows of dH (bf16 or float32, h8 16-byte pieces per row) whose
-// token is ignored: the compact backward never writes them.
-__global__ __launch_bounds__(256) void k_zero_ignored_rows(const int64_t* __restrict__ labels,
-                                                           int64_t N, int64_t ignore_index,
-                                                           int64_t h8, uint4* __restrict__ dH) {
-  const uint4 z = {0u, 0u, 0u, 0u};
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < N * h8;
-       i += int64_t(gridDim.x) * 256)
-    if (labels[i / h8] == ignore_index) dH[i] = z;
 }
 
 }  // namespace
@@ -392,34 +526,44 @@ hipError_t launch_zero_bytes(void* ptr, size_t bytes, const Launcher& L) {
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const Plan& p, const Args& a, bool all_rows, const Launcher& L) {
-  const unsigned nb = unsigned(p.n_gather_blocks);
-  L.pre(kGather);
-  hipLaunchKernelGGL(k_gather_count, dim3(nb), dim3(kGatherThreads), 0, L.stream, a.labels, p.N,
-                     a.ignore_index, a.bcnt);
-  hipLaunchKernelGGL(k_gather_tokens, dim3(nb), dim3(kGatherThreads), 0, L.stream, a.labels, p.N,
-                     a.ignore_index, a.bcnt, a.sc, a.idx, a.yc, a.tok_loss);
+hipError_t launch_scan_gather(const Plan& p, const Args& a, bool all_rows, const Launcher& L) {
+  if (p.N <= kScanGatherMax) {
+    L.pre(kLabelScan);
+    hipLaunchKernelGGL(k_scan_gather, dim3(1), dim3(kScanThreads), 0, L.stream, a.labels, p.N,
+                       p.V, a.ignore_index, a.reduction, a.num_label_tokens, a.mb_scale, a.sc,
+                       a.num_tokens, a.status, a.idx, a.yc, a.tok_loss);
+    L.post(kLabelScan);
+  } else {
+    const hipError_t e = launch_label_scan(p, a, L);
+    if (e != hipSuccess) return e;
+    const unsigned nb = unsigned(p.n_gather_blocks);
+    L.pre(kGather);
+    hipLaunchKernelGGL(k_gather_count, dim3(nb), dim3(kGatherThreads), 0, L.stream, a.labels,
+                       p.N, a.ignore_index, a.bcnt);
+    hipLaunchKernelGGL(k_gather_tokens, dim3(nb), dim3(kGatherThreads), 0, L.stream, a.labels,
+                       p.N, a.ignore_index, a.bcnt, a.sc, a.idx, a.yc, a.tok_loss);
+    L.post(kGather);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the hidden rows, then the dH rows of the ignored tokens zeroed
   const int64_t* rows_dev = all_rows ? nullptr : &a.sc->n_valid;
+  const int64_t g16 = a.dH ? p.H * int64_t(p.grad_elem) / 16 : 0;   // 16-byte pieces per dH row
+  uint4* dH = static_cast<uint4*>(a.dH);
+  L.pre(kGather);
   if (p.pad_h) {
     int64_t blocks = (p.N * p.H + 255) / 256;
     if (blocks > 8192) blocks = 8192;
     hipLaunchKernelGGL(k_gather_rows_pad, dim3(unsigned(blocks)), dim3(256), 0, L.stream,
                        static_cast<const uint16_t*>(a.h), p.h_in, p.H, a.idx, rows_dev, p.N,
-                       static_cast<uint16_t*>(a.hc));
+                       static_cast<uint16_t*>(a.hc), a.sc, g16, dH);
   } else {
     const int64_t h8 = p.H / 8;
     int64_t blocks = (p.N * h8 + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     hipLaunchKernelGGL(k_gather_rows, dim3(unsigned(blocks)), dim3(256), 0, L.stream,
                        static_cast<const uint4*>(a.h), h8, a.idx, rows_dev, p.N,
-                       static_cast<uint4*>(a.hc));
-  }
-  if (a.dH) {
-    const int64_t g16 = p.H * int64_t(p.grad_elem) / 16;   // 16-byte pieces per dH row
-    int64_t zb = (p.N * g16 + 255) / 256;
-    if (zb > 4096) zb = 4096;
-    hipLaunchKernelGGL(k_zero_ignored_rows, dim3(unsigned(zb)), dim3(256), 0, L.stream,
-                       a.labels, p.N, a.ignore_index, g16, static_cast<uint4*>(a.dH));
+                       static_cast<uint4*>(a.hc), a.sc, g16, dH);
   }
   L.post(kGather);
   return hipGetLastError();

@@ -495,10 +495,10 @@ def test_f32grad_workspace_check(lib):
 # ------------------------------------------------------ no-recompute variant
 def _dh_segments(M, H, K):
     """The split-K rule of the dH GEMM restated: with fewer than 128 output tiles
-    of 256 x 256, up to 8 segments (one per CU share), each of at least 2048 k,
+    of 256 x 256, up to 4 segments (one per CU share), each of at least 2048 k,
     rounded to a multiple of 64; 1 when not split."""
     tiles = -(-M // 256) * -(-H // 256)
-    s = min(256 // tiles, 8, K // 2048)
+    s = min(256 // tiles, 4, K // 2048)
     if tiles >= 128 or s < 2:
         return 1
     kseg = -(-K // s)
@@ -509,11 +509,11 @@ def _dh_segments(M, H, K):
 def test_dh_split_workspace(lib):
     """The recompute path carves segs x N x H float32 partials exactly when dH
     has few output tiles: the small configuration (32 tiles) splits its
-    32000-row vocabulary into 8 segments, the large-vocab one (512 tiles) does
+    32000-row vocabulary into 4 segments, the large-vocab one (512 tiles) does
     not split."""
     small = lib.flce_workspace_size(2048, 1024, 32000, 1)
-    assert _dh_segments(2048, 1024, 32000) == 8
-    assert small >= 8 * 2048 * 1024 * 4 + 32000 * 2048 * 2
+    assert _dh_segments(2048, 1024, 32000) == 4
+    assert small >= 4 * 2048 * 1024 * 4 + 32000 * 2048 * 2
     assert _dh_segments(8192, 4096, 16384) == 1
     big = lib.flce_workspace_size(8192, 4096, 131072, 1)
     # G chunk + float32 dH running sum + the gathered rows of the kept tokens

@@ -159,3 +159,44 @@ def test_forward_skips_ignored_tokens_without_changing_a_bit(cap, vchunk):
     r = gu.run_oracle(w)
     gu.assert_parity(w, b, r)
     gu.assert_parity(w, a, r, check_lse=False)
+
+
+@pytest.mark.parametrize("N", [20000, 70000])
+@pytest.mark.parametrize("entry", ["step", "step_lse", "no_recompute", "forward"])
+def test_long_gather(N, entry):
+    """Gathers over many tokens: 20000 is three passes of the one-workgroup
+    label scan and gather (8192 tokens a pass, the last one ragged), 70000 is
+    past its limit (65536) and runs the multi-block count and placement. A
+    third of the tokens ignored at random plus a masked prefix; dH starts as
+    NaN, so an ignored row that is not zeroed fails."""
+    import lm_head_linear_amd as m
+    rng = np.random.default_rng(N)
+    w = fi.make_custom(N, 64, 300, dtype=torch.bfloat16, seed=N, ignore_frac=0.0, softcap=0.0,
+                       reduction="sum")
+    mask = np.zeros(N, dtype=bool)
+    mask[rng.choice(N, N // 3, replace=False)] = True
+    mask[:1000] = True
+    w.labels.view(-1)[torch.from_numpy(mask)] = fi.IGNORE_INDEX
+    r = gu.run_oracle(w)
+    assert r.num_tokens == int((~mask).sum())
+    dev = gu.device()
+    if entry == "forward":
+        g = gu.run_gpu_forward(w)
+        assert g["status"] == 0 and g["num_tokens"] == r.num_tokens
+        gu.assert_loss(g["loss"], r.loss64)
+        lse = gu.to_np64(g["lse"])
+        assert np.abs(lse - r.lse).max() <= 1e-5 * max(1.0, np.abs(r.lse).max())
+        return
+    dH = torch.full((N, w.H), float("nan"), dtype=torch.bfloat16, device=dev)
+    if entry == "no_recompute":
+        h = w.h.reshape(N, w.H).to(dev)
+        status = torch.full((), -1, dtype=torch.int32, device=dev)
+        loss, nt, dH, dW = m.flce_forward_backward_nr(h, w.W.to(dev), w.labels.reshape(N).to(dev),
+                                                      ignore_index=w.ignore_index, dH=dH,
+                                                      status=status, token_chunk=8192)
+        torch.cuda.synchronize()
+        g = dict(loss=float(loss.item()), num_tokens=int(nt.item()), dH=dH, dW=dW, lse=None,
+                 status=int(status.item()))
+    else:
+        g = gu.run_gpu(w, lse=entry == "step_lse", dH=dH)
+    gu.assert_parity(w, g, r)              # includes: ignored rows of dH exactly 0
