@@ -180,7 +180,8 @@ def other_configs(steps: int, warmup: int):
     """The full step (flce_forward_backward, bf16) on the other full-size
     configurations: small, softcapped, and long, as one call and as its four
     micro-batches with the shared external token count and dW added up across
-    them. Returns {name: figures}."""
+    them; each mode timed over at least `steps` calls and about a quarter
+    second of them (a short step gets more). Returns {name: figures}."""
     import torch
     import flce_inputs as fi
     import lm_head_linear_amd as m
@@ -225,9 +226,20 @@ def other_configs(steps: int, warmup: int):
             torch.cuda.reset_peak_memory_stats(dev)
             ws = torch.empty(m.flce_workspace_size(n_call, H, V, W.dtype), dtype=torch.uint8,
                              device=dev)
-            ms, ev_ms = time_steps(lambda: fn(ws), steps, warmup)
+            # at least `steps` timed calls, more for a short step: about a
+            # quarter second of them, after a tenth as many warm-up calls
+            for _ in range(warmup):
+                fn(ws)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn(ws)
+            torch.cuda.synchronize()
+            est = max(time.perf_counter() - t0, 1e-5)
+            n_steps = int(min(max(steps, 0.25 / est), 2000))
+            ms, ev_ms = time_steps(lambda: fn(ws), n_steps, max(warmup, n_steps // 10))
             torch.cuda.synchronize()
             res[name] = {"ms_per_step": round(ms, 4), "event_ms_per_step": round(ev_ms, 4),
+                         "steps": n_steps,
                          "tokens_per_s": round(N / ms * 1e3, 1),
                          "mfma_frac_8nhv": round(8.0 * nhv / (ms * 1e-3) / 1e12
                                                  / PEAK_BF16_TFLOPS, 4),
