@@ -176,18 +176,21 @@ def time_steps(fn, steps: int, warmup: int):
     return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
 
 
-def other_configs(steps: int, warmup: int):
+def other_configs(steps: int, warmup: int, only=None):
     """The full step (flce_forward_backward, bf16) on the other full-size
     configurations: small, softcapped, and long, as one call and as its four
     micro-batches with the shared external token count and dW added up across
     them; each mode timed over at least `steps` calls and about a quarter
-    second of them (a short step gets more). Returns {name: figures}."""
+    second of them (a short step gets more). `only`: the names of the
+    configurations to time (all three when None). Returns {name: figures}."""
     import torch
     import flce_inputs as fi
     import lm_head_linear_amd as m
     dev = torch.device("cuda:0")
     out = {}
     for k in (2, 4, 5):
+        if only and fi.RECIPES[k]["name"] not in only:
+            continue
         w = fi.make_workload(k)
         N, H, V = w.N, w.H, w.V
         h = w.h.reshape(N, H).to(dev)
@@ -458,6 +461,9 @@ def main():
     ap.add_argument("--configs", action="store_true",
                     help="only time the full step on the small, softcapped and long "
                          "configurations (one JSON line of its own)")
+    ap.add_argument("--only", action="append", default=None, metavar="NAME",
+                    choices=("small", "softcapped", "long_edge"),
+                    help="with --configs: time this configuration (repeatable; default all)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -479,7 +485,8 @@ def main():
     from lm_head_linear_amd import _lib
     _lib.load()
     if args.configs:
-        print(json.dumps({"configs": other_configs(args.steps, args.warmup)}), flush=True)
+        print(json.dumps({"configs": other_configs(args.steps, args.warmup, args.only)}),
+              flush=True)
         return
 
     dev = torch.device("cuda:0")
