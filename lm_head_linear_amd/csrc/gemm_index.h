@@ -94,6 +94,38 @@ inline int64_t chunk_rows(const Plan& p, int64_t c) {
 // a multiple of 8) times 32.
 inline int64_t g_block(const Plan& p) { return p.ldg * 32; }
 
+// Vocabulary chunks whose probabilities the forward keeps, so that their G
+// is formed without recomputing their logits: chunk 0 in the G buffer and,
+// when dW is the call's to overwrite (not added to), chunks 1 .. n-1 in the
+// part of dW that no backward chunk writes before it has used them. Chunk
+// j's probabilities (then its G, formed in place) take vchunk x ldg bf16 (the
+// G chunk's blocked layout) at byte offset off[j] of dW: past the rows of
+// chunks 0 .. j, which the dH + dW launches of those chunks write before or
+// while chunk j's G is read, and below the chunks kept before it, placed
+// from the end of dW down in steps of 256 bytes.
+constexpr int kMaxKept = 4;
+struct Kept {
+  int n = 1;                       // chunks kept: 0 .. n-1
+  int64_t off[kMaxKept] = {};      // byte offset into dW of chunk j's G (j >= 1)
+};
+
+inline Kept kept_chunks(const Plan& p, bool dw_free) {
+  Kept k;
+  if (!dw_free || !p.backward || p.g_parts != 1 || p.nr || !p.compact || p.N <= 0) return k;
+  const int64_t region = p.vchunk * p.H * 2;      // bytes of one chunk's rows of dW
+  const int64_t bytes = p.vchunk * p.ldg * 2;     // bytes of one chunk's G
+  int64_t end = p.V * p.H * 2;                    // dW's bytes
+  for (int j = 1; j < kMaxKept && j < p.n_chunks; ++j) {
+    if (end < bytes) break;
+    const int64_t start = (end - bytes) / 256 * 256;
+    if (start < (j + 1) * region) break;
+    k.off[j] = start;
+    k.n = j + 1;
+    end = start;
+  }
+  return k;
+}
+
 inline Launch backward_launch(const Plan& p, int64_t c, int which, int part = 0) {
   const int64_t v0 = c * p.vchunk, vcur = chunk_rows(p, c);
   const int64_t g_off = int64_t(part) * p.vchunk * p.ldg;

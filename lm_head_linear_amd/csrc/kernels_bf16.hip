@@ -842,10 +842,11 @@ __device__ __forceinline__ void store_token_major(const Get& get, char* smem, in
 // sum are formed from). PC: the tiles of the first pc_rows vocabulary rows
 // also keep their probabilities relative to the tile max M of each token,
 // P' = exp(z' - M) <= 1, as bf16 in the blocked layout of the backward's G
-// chunk (pblk elements per 32 rows), so that the backward can form that
-// chunk's G from them instead of recomputing its logits. The partials are
-// formed exactly as without PC; P' is formed again from the logits in the
-// accumulators once the tile max is known.
+// chunk (pblk elements per 32 rows): the rows of backward chunk j (pc_vchunk
+// rows each) at probs<j>, so that the backward can form those chunks' G from
+// them instead of recomputing their logits. The partials are formed exactly
+// as without PC; P' is formed again from the logits in the accumulators once
+// the tile max is known.
 template <bool SOFTCAP, int OUT = kNoLogits, bool PC = false>
 struct EpiLse {
   static_assert(!(PC && OUT != kNoLogits), "kept probabilities or stored logits, not both");
@@ -858,8 +859,14 @@ struct EpiLse {
   void* logits;  // OUT != kNoLogits: [N][ld_logits]
   int64_t ld_logits;
   int vec;       // 16-byte runs of the logits rows are aligned
-  uint16_t* probs = nullptr;   // PC: the G chunk buffer
-  int64_t pc_rows = 0, pblk = 0;
+  // PC: where each kept chunk's G goes (chunks 0 .. 3; separate fields, not an
+  // array, so that the epilogue's copy stays in registers)
+  uint16_t* probs0 = nullptr;
+  uint16_t* probs1 = nullptr;
+  uint16_t* probs2 = nullptr;
+  uint16_t* probs3 = nullptr;
+  int64_t pc_rows = 0, pblk = 0, pc_vchunk = 1;
+  static_assert(gemm::kMaxKept == 4, "one field per kept chunk");
   // the tiles of the kept rows store more: deal the vocabulary tiles to the XCDs
   static constexpr bool kSpreadM = PC;
 
@@ -970,8 +977,12 @@ struct EpiLse {
         if (SOFTCAP) x = softcap * tanh_fast(x * inv_softcap);
         return mb[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fmaf(x, kLog2e, -mb[j]));
       };
-      store_token_major<false, false, true>(prob, smem, wm, wn, lane, probs, 0, m0, n0, N,
-                                            pc_rows < V ? pc_rows : V, nullptr, pblk);
+      // the kept chunk of this tile (the chunk edges are tile edges)
+      const int64_t j = m0 / pc_vchunk, jr0 = j * pc_vchunk;
+      uint16_t* dst = j == 0 ? probs0 : j == 1 ? probs1 : j == 2 ? probs2 : probs3;
+      const int64_t jrows = V - jr0 < pc_vchunk ? V - jr0 : pc_vchunk;
+      store_token_major<false, false, true>(prob, smem, wm, wn, lane, dst, 0, m0 - jr0, n0, N,
+                                            jrows, nullptr, pblk);
     }
   }
 };
@@ -1189,8 +1200,9 @@ struct EpiLseP {
 };
 
 // G in place of the stored probabilities of nt tokens (the first *count
-// ones when `count` is given) and the vocabulary columns [0, nv):
-//   G[t][v] = c valid_t (P'[t][v] exp(M_tv - lse_t) - [v = y_t]) dz'/dz
+// ones when `count` is given) and the vocabulary columns [0, nv) of a chunk
+// whose column v is vocabulary id vbase + v:
+//   G[t][v] = c valid_t (P'[t][v] exp(M_tv - lse_t) - [vbase + v = y_t]) dz'/dz
 // with M_tv the max of v's vocabulary tile for token t (the forward partial).
 // The target element is formed from the float32 target logit instead:
 // c (exp(z'_ty - lse_t) - 1) dz'/dz. With a softcap, dz'/dz = 1 - (z'/s)^2 and
@@ -1201,7 +1213,7 @@ struct EpiLseP {
 template <bool SOFTCAP>
 __global__ __launch_bounds__(256) void k_probs_to_grad(
     uint16_t* __restrict__ gp, int64_t blk, int64_t nt, const int64_t* __restrict__ count,
-    int64_t nv, int64_t V, const float2* __restrict__ part, int64_t ld_part,
+    int64_t vbase, int64_t nv, int64_t V, const float2* __restrict__ part, int64_t ld_part,
     const float* __restrict__ lse, const float* __restrict__ zt,
     const int64_t* __restrict__ labels, int64_t ignore_index, const Scalars* __restrict__ sc,
     float inv_softcap) {
@@ -1219,7 +1231,7 @@ __global__ __launch_bounds__(256) void k_probs_to_grad(
   for (int64_t b = blockIdx.y; b < nb; b += gridDim.y) {
     const int64_t v0 = b * 32 + (rem & 3) * 8;
     uint16_t* run = gp + b * blk + t * 32 + (rem & 3) * 8;
-    const float M = part[(v0 / kBM) * ld_part + t].x;
+    const float M = part[((vbase + v0) / kBM) * ld_part + t].x;
     const float scale = __builtin_amdgcn_exp2f((M - l) * kLog2e);
     const u32x4 in = *reinterpret_cast<const u32x4*>(run);
     float g[8];
@@ -1229,7 +1241,7 @@ __global__ __launch_bounds__(256) void k_probs_to_grad(
       const float pv = bf16_to_f32(uint16_t((e & 1) ? (w >> 16) : (w & 0xFFFF)));
       const int64_t v = v0 + e;
       float x;
-      if (v == y) {
+      if (vbase + v == y) {
         const float z = zt[t];
         x = (__builtin_amdgcn_exp2f((z - l) * kLog2e) - 1.f) * coef;
         if (SOFTCAP) {
@@ -1641,11 +1653,21 @@ hipError_t bf16_forward_out(const Plan& p, const Args& a, const Launcher& L) {
   constexpr int NF = gemm::kFormN;
   if constexpr (OUT == kNoLogits) {
     if (p.compact && p.backward && p.g_parts == 1) {
-      // the first backward chunk's probabilities are kept (its G is formed
-      // from them, without recomputing its logits)
+      // the probabilities of the first backward chunks are kept (their G is
+      // formed from them, without recomputing their logits): chunk 0 in the G
+      // buffer, the next ones, when dW is not added to, in dW's free rows
+      const gemm::Kept kept = gemm::kept_chunks(p, !a.accumulate_dW);
       auto run = [&](auto e) {
-        e.probs = static_cast<uint16_t*>(a.g);
-        e.pc_rows = gemm::chunk_rows(p, 0);
+        auto at = [&](int j) {
+          return j < kept.n ? reinterpret_cast<uint16_t*>(static_cast<char*>(a.dW) + kept.off[j])
+                            : nullptr;
+        };
+        e.probs0 = static_cast<uint16_t*>(a.g);
+        e.probs1 = at(1);
+        e.probs2 = at(2);
+        e.probs3 = at(3);
+        e.pc_rows = kept.n * p.vchunk < p.V ? kept.n * p.vchunk : p.V;
+        e.pc_vchunk = p.vchunk;
         e.pblk = gemm::g_block(p);
         return nv ? run_gemm<NF, NF, kDynN>(l, a, e, kLseFwd, L, nv)
                   : run_gemm<NF, NF>(l, a, e, kLseFwd, L);
@@ -1729,25 +1751,30 @@ hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, cons
   if (!p.compact) return hipErrorInvalidValue;
   const int64_t v0 = chunk * p.vchunk;
   const int64_t vcur = gemm::chunk_rows(p, chunk);
-  uint16_t* g = static_cast<uint16_t*>(a.g);
   const int64_t* nv = &a.sc->n_valid;
   constexpr int NF = gemm::kFormN, TF = gemm::kFormT;
-  // 1) G[n_valid][vchunk]: chunk 0 from the probabilities the forward kept,
-  // the others by recomputing the chunk's logits
+  // 1) G[n_valid][vchunk]: for the chunks whose probabilities the forward
+  // kept (chunk 0 in the G buffer, the next ones in dW's free rows), from
+  // them, in place; the others by recomputing the chunk's logits into the G
+  // buffer. The dH and dW launches below read G where it was formed.
+  const gemm::Kept kept = gemm::kept_chunks(p, !a.accumulate_dW);
+  Args ag = a;
+  if (chunk > 0 && chunk < kept.n) ag.g = static_cast<char*>(a.dW) + kept.off[chunk];
+  uint16_t* g = static_cast<uint16_t*>(ag.g);
   const gemm::Launch lg = gemm::backward_launch(p, chunk, 0);
   hipError_t err;
-  if (chunk == 0) {
+  if (chunk < kept.n) {
     const int64_t nb = (vcur + 31) / 32;
     const dim3 grid(unsigned((p.N * 4 + 255) / 256), unsigned(nb < 512 ? nb : 512));
     L.pre(kProbsToGrad);
     if (a.softcap > 0.f)
       hipLaunchKernelGGL(k_probs_to_grad<true>, grid, dim3(256), 0, L.stream, g,
-                         gemm::g_block(p), p.N, nv, vcur, p.V, a.part, p.ld_part, a.lse, a.zt,
-                         a.yc, a.ignore_index, a.sc, 1.f / a.softcap);
+                         gemm::g_block(p), p.N, nv, v0, vcur, p.V, a.part, p.ld_part, a.lse,
+                         a.zt, a.yc, a.ignore_index, a.sc, 1.f / a.softcap);
     else
       hipLaunchKernelGGL(k_probs_to_grad<false>, grid, dim3(256), 0, L.stream, g,
-                         gemm::g_block(p), p.N, nv, vcur, p.V, a.part, p.ld_part, a.lse, a.zt,
-                         a.yc, a.ignore_index, a.sc, 0.f);
+                         gemm::g_block(p), p.N, nv, v0, vcur, p.V, a.part, p.ld_part, a.lse,
+                         a.zt, a.yc, a.ignore_index, a.sc, 0.f);
     L.post(kProbsToGrad);
     err = hipGetLastError();
   } else if (a.softcap > 0.f) {
@@ -1775,10 +1802,10 @@ hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, cons
     const EpiDHPart ep{a.dh_part, p.N, p.H, p.N * p.H};
     if (a.accumulate_dW)
       err = run_gemm_pair<NF, TF, kDynM, TF, TF, kDynK, true>(
-          lh, ep, lw, EpiDW<true>{dW, p.H, v0, vcur}, a, kGemmDWDH, L, nv, p.dh_kseg, segs);
+          lh, ep, lw, EpiDW<true>{dW, p.H, v0, vcur}, ag, kGemmDWDH, L, nv, p.dh_kseg, segs);
     else
       err = run_gemm_pair<NF, TF, kDynM, TF, TF, kDynK, true>(
-          lh, ep, lw, EpiDW<false>{dW, p.H, v0, vcur}, a, kGemmDWDH, L, nv, p.dh_kseg, segs);
+          lh, ep, lw, EpiDW<false>{dW, p.H, v0, vcur}, ag, kGemmDWDH, L, nv, p.dh_kseg, segs);
     if (err != hipSuccess) return err;
     return launch_dh_reduce(a.dh_part, segs, p.N * p.H, first ? nullptr : a.dh_acc,
                             last ? nullptr : a.dh_acc, last ? dH : nullptr, L, p.H, nv, a.idx);
@@ -1787,9 +1814,9 @@ hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, cons
   auto pair = [&](auto edh) {
     if (a.accumulate_dW)
       return run_gemm_pair<NF, TF, kDynM, TF, TF, kDynK>(
-          lh, edh, lw, EpiDW<true>{dW, p.H, v0, vcur}, a, kGemmDWDH, L, nv);
+          lh, edh, lw, EpiDW<true>{dW, p.H, v0, vcur}, ag, kGemmDWDH, L, nv);
     return run_gemm_pair<NF, TF, kDynM, TF, TF, kDynK>(
-        lh, edh, lw, EpiDW<false>{dW, p.H, v0, vcur}, a, kGemmDWDH, L, nv);
+        lh, edh, lw, EpiDW<false>{dW, p.H, v0, vcur}, ag, kGemmDWDH, L, nv);
   };
   if (first && last) return pair(EpiDH<true, true>{dH, a.dh_acc, p.N, p.H, a.idx});
   if (first) return pair(EpiDH<true, false>{dH, a.dh_acc, p.N, p.H, a.idx});
@@ -1831,12 +1858,13 @@ hipError_t bf16_nr_backward_chunk(const Plan& p, const Args& a, int64_t c, const
   const int64_t blk = gemm::nr_block(p);
   L.pre(kProbsToGrad);
   if (a.softcap > 0.f)
-    hipLaunchKernelGGL(k_probs_to_grad<true>, grid, dim3(256), 0, L.stream, g, blk, nt, cb, p.V,
-                       p.V, a.part, p.ld_part, a.lse, a.zt, a.yc + t0, a.ignore_index, a.sc,
-                       1.f / a.softcap);
+    hipLaunchKernelGGL(k_probs_to_grad<true>, grid, dim3(256), 0, L.stream, g, blk, nt, cb,
+                       int64_t(0), p.V, p.V, a.part, p.ld_part, a.lse, a.zt, a.yc + t0,
+                       a.ignore_index, a.sc, 1.f / a.softcap);
   else
-    hipLaunchKernelGGL(k_probs_to_grad<false>, grid, dim3(256), 0, L.stream, g, blk, nt, cb, p.V,
-                       p.V, a.part, p.ld_part, a.lse, a.zt, a.yc + t0, a.ignore_index, a.sc, 0.f);
+    hipLaunchKernelGGL(k_probs_to_grad<false>, grid, dim3(256), 0, L.stream, g, blk, nt, cb,
+                       int64_t(0), p.V, p.V, a.part, p.ld_part, a.lse, a.zt, a.yc + t0,
+                       a.ignore_index, a.sc, 0.f);
   L.post(kProbsToGrad);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -208,6 +208,33 @@ static void check_split(const Plan& p, const Launch& l) {
   if (covered != l.K) fail("segments do not cover K", covered, l.K, segs);
 }
 
+// The chunks whose probabilities the forward keeps in dW's free rows: chunk
+// j's G (vchunk x ldg bf16) lies inside dW, 256-byte aligned, clear of the
+// rows of chunks 0 .. j (written by their dH + dW launches before or while it
+// is read) and of every other kept chunk. The G reads of chunk j's launches
+// are within vchunk x ldg elements of its base (check_launch), so they stay
+// inside that range too.
+static int64_t n_kept_extra = 0;
+static void check_kept(const Plan& p) {
+  const Kept k = kept_chunks(p, true);
+  const Kept none = kept_chunks(p, false);
+  if (none.n != 1) fail("chunks kept in dW while dW is added to", none.n, p.N, p.V);
+  if (k.n < 1 || k.n > kMaxKept || k.n > p.n_chunks) fail("kept count", k.n, p.n_chunks, 0);
+  const int64_t dw_bytes = p.V * p.H * 2, bytes = p.vchunk * p.ldg * 2;
+  for (int j = 1; j < k.n; ++j) {
+    const int64_t lo = k.off[j], hi = lo + bytes;
+    if (lo % 256) fail("kept chunk alignment", j, lo, 0);
+    if (lo < 0 || hi > dw_bytes) fail("kept chunk outside dW", j, lo, dw_bytes);
+    for (int c = 0; c <= j && c < p.n_chunks; ++c) {
+      const int64_t r0 = c * p.vchunk * p.H * 2, r1 = r0 + chunk_rows(p, c) * p.H * 2;
+      if (lo < r1 && r0 < hi) fail("kept chunk overlaps rows written before it is read", j, c, lo);
+    }
+    for (int q = 1; q < k.n; ++q)
+      if (q != j && lo < k.off[q] + bytes && k.off[q] < hi) fail("kept chunks overlap", j, q, lo);
+    ++n_kept_extra;
+  }
+}
+
 int main(int argc, char** argv) {
   // N H V [vchunk]
   struct Shape { int64_t N, H, V, vc; };
@@ -239,6 +266,7 @@ int main(int argc, char** argv) {
       if (!make_plan(s.N, s.H, s.V, 1, &p, true, grad)) { fail("plan", s.N, s.H, s.V); continue; }
       check_launch(p, forward_launch(p));
       check_launch(p, forward_launch(p), true);     // the raster that deals M-tiles to XCDs
+      check_kept(p);
       for (int64_t c = 0; c < p.n_chunks; ++c) {
         check_launch(p, backward_launch(p, c, 0));
         for (int part = 0; part < p.g_parts; ++part)
@@ -261,6 +289,7 @@ int main(int argc, char** argv) {
                 failures ? "FAILURES" : "ok");
   }
   if (failures == 0)
-    std::printf("all loads in bounds (%lld split-K segments)\n", (long long)n_split_segments);
+    std::printf("all loads in bounds (%lld split-K segments, %lld chunks kept in dW)\n",
+                (long long)n_split_segments, (long long)n_kept_extra);
   return failures ? 1 : 0;
 }
