@@ -205,7 +205,14 @@ def other_configs(steps: int, warmup: int, only=None):
         # that the peak extra memory is that mode's
         def one_call(ws):
             m.flce_forward_backward(h, W, y, dH=dH, dW=dW, workspace=ws, **kw)
-        modes = {"one_call": (N, one_call)}
+
+        def flops(lab, acc):
+            n = lab.numel()
+            return step_flops(n, int((lab != w.ignore_index).sum()), H, V,
+                              m.flce_vocab_chunk(n, H, V, W.dtype),
+                              m.flce_kept_chunks(n, H, V, W.dtype, acc))["step"]
+        lab_all = w.labels.reshape(N)
+        modes = {"one_call": (N, one_call, flops(lab_all, False))}
         if w.micro_batches > 1:
             nb = N // w.micro_batches
 
@@ -215,14 +222,13 @@ def other_configs(steps: int, warmup: int, only=None):
                     m.flce_forward_backward(h[s], W, y[s], dH=dH[s], dW=dW, workspace=ws,
                                             accumulate_dW=i > 0,
                                             mb_scale=m.micro_batch_scale(0, 0, w.reduction), **kw)
-            modes[f"{w.micro_batches}_micro_batches"] = (nb, micro)
+            modes[f"{w.micro_batches}_micro_batches"] = (
+                nb, micro, sum(flops(lab_all[i * nb:(i + 1) * nb], i > 0)
+                               for i in range(w.micro_batches)))
         res = {"N": N, "H": H, "V": V, "softcap": w.softcap, "reduction": w.reduction,
                "num_label_tokens": w.num_label_tokens, "logits_f32_bytes_avoided": int(N * V * 4)}
         nhv = float(N) * H * V
-        sf = step_flops(N, int((w.labels != w.ignore_index).sum()), H, V,
-                        m.flce_vocab_chunk(N, H, V, W.dtype))
-        xfl = sf["step"]
-        for name, (n_call, fn) in modes.items():
+        for name, (n_call, fn, xfl) in modes.items():
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
             base = torch.cuda.memory_allocated(dev)
@@ -391,17 +397,19 @@ def other_modes(m, w, h, W, y, dH, dW, loss, nt, steps, timing, nhv):
     return forward_only, float32_grads, no_recompute
 
 
-def step_flops(N: int, n_kept: int, H: int, V: int, vchunk: int, lse_out: bool = False) -> dict:
+def step_flops(N: int, n_kept: int, H: int, V: int, vchunk: int, kept: int = 1,
+               lse_out: bool = False) -> dict:
     """Matrix flops each GEMM kind executes per step of flce_forward_backward
     (bf16, bf16 gradients). The call gathers the non-ignored tokens first: an
     ignored token's loss is 0 and its logit gradient exactly zero, so the
     forward runs over the n_kept kept tokens (over all N when per-token lse is
     asked for) and the recompute, dW and dH over the kept ones. The forward
-    keeps the first vocabulary chunk's probabilities, so the recompute covers
-    the other V - vchunk rows. dH_dW_gemm is a chunk's dH and dW in one grid;
-    'step' is the sum over the step."""
+    keeps the probabilities of the first `kept` vocabulary chunks
+    (flce_kept_chunks), so the recompute covers the other V - kept vchunk
+    rows. dH_dW_gemm is a chunk's dH and dW in one grid; 'step' is the sum over
+    the step."""
     fwd, bwd = 2.0 * (N if lse_out else n_kept) * H * V, 2.0 * n_kept * H * V
-    rec = 2.0 * n_kept * H * max(V - vchunk, 0)
+    rec = 2.0 * n_kept * H * max(V - kept * vchunk, 0)
     return {"lse_fwd_gemm": fwd, "grad_logits_gemm": rec, "dW_gemm": bwd, "dH_gemm": bwd,
             "dH_dW_gemm": 2.0 * bwd, "step": fwd + rec + 2.0 * bwd}
 
@@ -539,7 +547,8 @@ def main():
     tflops_8 = 8 * nhv / (wall_ms * 1e-3) / 1e12
     tflops_6 = 6 * nhv / (wall_ms * 1e-3) / 1e12
     n_kept = int((w.labels != w.ignore_index).sum())
-    flops = step_flops(N, n_kept, H, V, vchunk)
+    kept_chunks = m.flce_kept_chunks(N, H, V, W.dtype)
+    flops = step_flops(N, n_kept, H, V, vchunk, kept_chunks)
     x_step = flops["step"]
     tflops_x = x_step / (wall_ms * 1e-3) / 1e12
     kernels, roofline = {}, None
@@ -580,7 +589,8 @@ def main():
         "config": {"workload": (f"large_vocab: h bf16 [2,4096,4096], W bf16 [131072,4096], "
                                 "Zipf(1.1) labels, first quarter of each sequence ignored, "
                                 "reduction=mean"),
-                   "N": N, "H": H, "V": V, "vocab_chunk": vchunk},
+                   "N": N, "H": H, "V": V, "vocab_chunk": vchunk,
+                   "kept_chunks": kept_chunks},
         "mfma_frac_8nhv": round(tflops_8 / PEAK_BF16_TFLOPS, 4),
         "mfma_frac_6nhv": round(tflops_6 / PEAK_BF16_TFLOPS, 4),
         "tflops_8nhv": round(tflops_8, 1),

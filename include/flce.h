@@ -135,8 +135,12 @@ int flce_check_args(const void* h, const void* W, const int64_t* labels,
  *         >= 0: the token-weighted micro-batch scale is a token fraction
  *         n_mb / n_total, 1.0 for a plain call; 0 gives loss 0 and zero
  *         gradients; negative is FLCE_ERR_ARG), accumulate_dW (0: dW is
- *         overwritten; 1: the computed gradient is added to the dW already in
- *         memory, for micro-batching).
+ *         overwritten, and until the call writes its rows it also holds
+ *         intermediate values of the call (the logit gradient of some
+ *         vocabulary chunks, which saves recomputing their logits), so its
+ *         contents are only defined once the call has completed; 1: the
+ *         computed gradient is added to the dW already in memory, for
+ *         micro-batching).
  * Outputs *loss (fp32 scalar), *num_tokens (int64 scalar), dH [N,H],
  *         dW [V,H], optional lse_out [N] fp32 (per-token log-sum-exp of the
  *         softcapped logits; NULL = not written), optional *status (int32:
@@ -390,6 +394,17 @@ const char* flce_status_string(int status);
  * library's own addition).
  */
 int64_t flce_vocab_chunk(int64_t N, int64_t H, int64_t V, int dtype);
+
+/*
+ * flce_kept_chunks -- how many of flce_forward_backward's vocabulary chunks
+ * (from the first) get their logit gradient from probabilities the forward
+ * kept, without recomputing their logits: chunk 0 in the workspace and, when
+ * accumulate_dW is 0, up to three more in the rows of dW the call has not yet
+ * written. 0 for float32 inputs (every chunk recomputed), for N <= 0 and for
+ * invalid sizes; at most 4. Informational (host arithmetic only; this
+ * library's own addition).
+ */
+int64_t flce_kept_chunks(int64_t N, int64_t H, int64_t V, int dtype, int accumulate_dW);
 
 /*
  * Per-kernel timing (diagnostics for benchmarks; not thread-safe; this

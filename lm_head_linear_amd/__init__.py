@@ -54,6 +54,7 @@ __all__ = [
     "flce_forward_noalloc",
     "flce_status_string",
     "flce_vocab_chunk",
+    "flce_kept_chunks",
     "flce_profile_begin",
     "flce_profile_end",
     "flce_profile_query",
@@ -120,6 +121,13 @@ def flce_vocab_chunk(N: int, H: int, V: int, dtype: torch.dtype,
                      grad_dtype: Optional[torch.dtype] = None) -> int:
     g = _dtype_code(grad_dtype if grad_dtype is not None else dtype)
     return int(_lib.load().flce_vocab_chunk_ex(N, H, V, _dtype_code(dtype), g))
+
+
+def flce_kept_chunks(N: int, H: int, V: int, dtype: torch.dtype,
+                     accumulate_dW: bool = False) -> int:
+    """Vocabulary chunks of flce_forward_backward whose logits are not
+    recomputed (the forward keeps their probabilities)."""
+    return int(_lib.load().flce_kept_chunks(N, H, V, _dtype_code(dtype), int(bool(accumulate_dW))))
 
 
 def flce_workspace_size_ex(N: int, H: int, V: int, dtype: torch.dtype,

@@ -41,6 +41,7 @@ SIGNATURES = {
     "flce_forward_logits": (_i32, _F_ARGS + [_vp, _i64, _i32]),
     "flce_status_string": (_c.c_char_p, [_i32]),
     "flce_vocab_chunk": (_i64, [_i64, _i64, _i64, _i32]),
+    "flce_kept_chunks": (_i64, [_i64, _i64, _i64, _i32, _i32]),
     "flce_profile_begin": (_i32, []),
     "flce_profile_end": (_i32, []),
     "flce_profile_kinds": (_i32, []),

@@ -5,6 +5,7 @@
 
 #include "../../include/flce.h"
 #include "flce_plan.h"
+#include "gemm_index.h"
 
 namespace flce {
 namespace {
@@ -214,6 +215,13 @@ int64_t flce_vocab_chunk_ex(int64_t N, int64_t H, int64_t V, int dtype, int grad
   flce::Plan p;
   if (!flce::make_plan(N, H, V, dtype, &p, true, grad_dtype)) return 0;
   return p.vchunk;
+}
+
+int64_t flce_kept_chunks(int64_t N, int64_t H, int64_t V, int dtype, int accumulate_dW) {
+  flce::Plan p;
+  if (dtype != FLCE_BF16 || N <= 0 || !flce::make_plan(N, H, V, dtype, &p, true, dtype))
+    return 0;
+  return flce::gemm::kept_chunks(p, accumulate_dW == 0).n;
 }
 
 static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
