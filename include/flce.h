@@ -100,9 +100,10 @@ size_t flce_workspace_size(int64_t N, int64_t H, int64_t V, int dtype);
  *                        (h, W, labels, dH when N > 0; loss, num_tokens, dW
  *                        always); unknown dtype/reduction; softcap < 0 or not
  *                        finite; mb_scale negative or not finite;
- *                        num_label_tokens > 0 with 'mean'; an output (dH,
- *                        dW) overlapping an input matrix (h, W) or the other
- *                        output.
+ *                        num_label_tokens > 0 with 'mean'; a gradient output
+ *                        (dH, dW) overlapping an input matrix (h, W), the other
+ *                        gradient, the labels, loss, num_tokens, status,
+ *                        lse_out or the workspace.
  *   FLCE_ERR_UNSUPPORTED a bf16 matrix pointer (h, W, dH, dW) not 16-byte
  *                        aligned.
  * Any H > 0 is accepted (the NeMo linear_ce page, "API", puts no limit on the

@@ -346,16 +346,15 @@ int flce_check_args_nr(const void* h, const void* W, const int64_t* labels, int6
                        size_t workspace_bytes, int32_t* status, float* lse_out,
                        int64_t token_chunk) {
   // the common rules, with the workspace checked against this variant's plan
-  int st = flce_check_args_ex(h, W, labels, N, H, V, ignore_index, softcap, reduction,
-                              num_label_tokens, loss, num_tokens, dH, dW, stream, dtype,
-                              mb_scale, accumulate_dW, workspace, size_t(-1), status, lse_out,
-                              dtype);
-  if (st != FLCE_OK) return st;
-  if (dtype != FLCE_BF16 || token_chunk < 0) return FLCE_ERR_UNSUPPORTED;
+  (void)ignore_index; (void)stream; (void)accumulate_dW;
   const size_t need = flce_workspace_size_nr(N, H, V, dtype, token_chunk);
+  int st = flce::check_grad_args(h, W, labels, N, H, V, softcap, reduction, num_label_tokens,
+                                 loss, num_tokens, dH, dW, dtype, mb_scale, workspace,
+                                 workspace_bytes, status, lse_out, need ? need : 1);
+  if (st != FLCE_OK && st != FLCE_ERR_WORKSPACE) return st;
+  if (dtype != FLCE_BF16 || token_chunk < 0) return FLCE_ERR_UNSUPPORTED;
   if (need == 0) return FLCE_ERR_UNSUPPORTED;   // shapes beyond the kernels' index range
-  if (workspace_bytes < need) return FLCE_ERR_WORKSPACE;
-  return FLCE_OK;
+  return st;
 }
 
 int flce_forward_backward_nr(const void* h, const void* W, const int64_t* labels, int64_t N,

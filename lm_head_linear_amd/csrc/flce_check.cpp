@@ -2,6 +2,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <utility>
 
 #include "../../include/flce.h"
 #include "flce_plan.h"
@@ -249,7 +250,9 @@ int check_common(const void* h, const void* W, const int64_t* labels, int64_t N,
                  int64_t V, float softcap, int reduction, int64_t num_label_tokens,
                  const float* loss, const int64_t* num_tokens, const void* dH, const void* dW,
                  int dtype, int grad_dtype, float mb_scale, const void* workspace,
-                 size_t workspace_bytes, bool backward, int gather = -1) {
+                 size_t workspace_bytes, bool backward, int gather = -1,
+                 const void* status = nullptr, const void* lse_out = nullptr,
+                 size_t workspace_need = 0) {
   if (N < 0 || H <= 0 || V <= 0) return FLCE_ERR_ARG;
   if (dtype != FLCE_F32 && dtype != FLCE_BF16) return FLCE_ERR_ARG;
   if (grad_dtype != FLCE_F32 && grad_dtype != FLCE_BF16) return FLCE_ERR_ARG;
@@ -272,6 +275,17 @@ int check_common(const void* h, const void* W, const int64_t* labels, int64_t N,
     if (overlaps(dH, size_t(N) * H * gs, dW, size_t(V) * H * gs)) return FLCE_ERR_ARG;
     if (overlaps(dH, size_t(N) * H * gs, W, size_t(V) * H * es)) return FLCE_ERR_ARG;
     if (overlaps(dW, size_t(V) * H * gs, h, size_t(N) * H * es)) return FLCE_ERR_ARG;
+    // nor anything else the call reads or writes: dW holds intermediate values
+    // from the forward on, before the labels, the scalars and the workspace
+    // are done with
+    const std::pair<const void*, size_t> other[] = {
+        {labels, size_t(N) * sizeof(int64_t)}, {loss, sizeof(float)},
+        {num_tokens, sizeof(int64_t)}, {status, sizeof(int32_t)},
+        {lse_out, size_t(N) * sizeof(float)}, {workspace, workspace_bytes}};
+    for (const auto& o : other)
+      if (overlaps(dW, size_t(V) * H * gs, o.first, o.second) ||
+          overlaps(dH, size_t(N) * H * gs, o.first, o.second))
+        return FLCE_ERR_ARG;
   }
   const uintptr_t mask = dtype == FLCE_BF16 ? 15u : 3u;
   if (dtype == FLCE_BF16 && !flce::bf16_shape_ok(N, p.H, V)) return FLCE_ERR_UNSUPPORTED;
@@ -282,11 +296,22 @@ int check_common(const void* h, const void* W, const int64_t* labels, int64_t N,
     return FLCE_ERR_UNSUPPORTED;
   if (!workspace) return FLCE_ERR_WORKSPACE;
   if (misaligned(workspace, 255u)) return FLCE_ERR_WORKSPACE;
-  if (workspace_bytes < p.total) return FLCE_ERR_WORKSPACE;
+  if (workspace_bytes < (workspace_need ? workspace_need : p.total)) return FLCE_ERR_WORKSPACE;
   return FLCE_OK;
 }
 
 }  // namespace
+
+int flce::check_grad_args(const void* h, const void* W, const int64_t* labels, int64_t N,
+                          int64_t H, int64_t V, float softcap, int reduction,
+                          int64_t num_label_tokens, const float* loss, const int64_t* num_tokens,
+                          const void* dH, const void* dW, int dtype, float mb_scale,
+                          const void* workspace, size_t workspace_bytes, const void* status,
+                          const void* lse_out, size_t workspace_need) {
+  return check_common(h, W, labels, N, H, V, softcap, reduction, num_label_tokens, loss,
+                      num_tokens, dH, dW, dtype, dtype, mb_scale, workspace, workspace_bytes,
+                      true, -1, status, lse_out, workspace_need);
+}
 
 extern "C" {
 
@@ -309,10 +334,10 @@ int flce_check_args_ex(const void* h, const void* W, const int64_t* labels,
                        void* stream, int dtype, float mb_scale, int accumulate_dW,
                        void* workspace, size_t workspace_bytes, int32_t* status,
                        float* lse_out, int grad_dtype) {
-  (void)ignore_index; (void)stream; (void)accumulate_dW; (void)status; (void)lse_out;
+  (void)ignore_index; (void)stream; (void)accumulate_dW;
   return check_common(h, W, labels, N, H, V, softcap, reduction, num_label_tokens, loss,
                       num_tokens, dH, dW, dtype, grad_dtype, mb_scale, workspace,
-                      workspace_bytes, true);
+                      workspace_bytes, true, -1, status, lse_out);
 }
 
 int flce_forward_check_args(const void* h, const void* W, const int64_t* labels,

@@ -143,4 +143,14 @@ bool make_plan(int64_t N, int64_t H, int64_t V, int dtype, Plan* p, bool backwar
 // running sum of dW.
 bool make_plan_nr(int64_t N, int64_t H, int64_t V, int dtype, int64_t token_chunk, Plan* p);
 
+// The synchronous checks of the entry points with gradients (dtype gradients),
+// the workspace required to hold workspace_need bytes (0: the recompute
+// plan's size) instead of the recompute plan's: used by the no-recompute
+// variant, whose workspace differs.
+int check_grad_args(const void* h, const void* W, const int64_t* labels, int64_t N, int64_t H,
+                    int64_t V, float softcap, int reduction, int64_t num_label_tokens,
+                    const float* loss, const int64_t* num_tokens, const void* dH, const void* dW,
+                    int dtype, float mb_scale, const void* workspace, size_t workspace_bytes,
+                    const void* status, const void* lse_out, size_t workspace_need);
+
 }  // namespace flce

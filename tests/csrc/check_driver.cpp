@@ -41,7 +41,22 @@ int main() {
               big) == FLCE_ERR_ARG);
   EXPECT(call(1, 8, 5, FLCE_BF16, FLCE_SUM, 0, 0.f, INFINITY, big) == FLCE_ERR_ARG);
   EXPECT(call(1, 8, 5, FLCE_BF16, FLCE_SUM, 0, 0.f, 1.f, 10) == FLCE_ERR_WORKSPACE);
-  EXPECT(call(1, 8, 5, FLCE_BF16, FLCE_SUM, 0, 0.f, 1.f, big, 4096 + 16) == FLCE_ERR_WORKSPACE);
+  EXPECT(call(1, 8, 5, FLCE_BF16, FLCE_SUM, 0, 0.f, 1.f, big, (uintptr_t(1) << 40) + 16) ==
+         FLCE_ERR_WORKSPACE);
+  // a gradient output sharing memory with the workspace (dW holds intermediate
+  // values during the call) or with another argument is refused
+  const uintptr_t b = uintptr_t(1) << 32;
+  EXPECT(call(1, 8, 5, FLCE_BF16, FLCE_SUM, 0, 0.f, 1.f, big, b * 7 - 256) == FLCE_ERR_ARG);
+  EXPECT(call(1, 8, 5, FLCE_BF16, FLCE_SUM, 0, 0.f, 1.f, 256, b * 6 + 8) == FLCE_ERR_ARG);
+  EXPECT(call(1, 8, 5, FLCE_BF16, FLCE_SUM, 0, 0.f, 1.f, big, b * 8) == FLCE_OK);
+  EXPECT(flce_check_args((void*)b, (void*)(b * 2), (int64_t*)(b * 7), 1, 8, 5, -100, 0.f,
+                         FLCE_SUM, 0, (float*)(b * 4), (int64_t*)(b * 5), (void*)(b * 6),
+                         (void*)(b * 7), nullptr, FLCE_BF16, 1.f, 0, (void*)(b * 8), big, nullptr,
+                         nullptr) == FLCE_ERR_ARG);                 // labels inside dW
+  EXPECT(flce_check_args((void*)b, (void*)(b * 2), (int64_t*)(b * 3), 1, 8, 5, -100, 0.f,
+                         FLCE_SUM, 0, (float*)(b * 4), (int64_t*)(b * 5), (void*)(b * 6),
+                         (void*)(b * 7), nullptr, FLCE_BF16, 1.f, 0, (void*)(b * 8), big,
+                         (int32_t*)(b * 6 + 8), nullptr) == FLCE_ERR_ARG);   // status inside dH
   // extreme sizes are refused, never overflow
   EXPECT(call(int64_t(1) << 40, 8, 5, FLCE_BF16, FLCE_SUM, 0, 0.f, 1.f, big) == FLCE_ERR_ARG);
   EXPECT(call(8, int64_t(1) << 40, 5, FLCE_BF16, FLCE_SUM, 0, 0.f, 1.f, big) == FLCE_ERR_ARG);
