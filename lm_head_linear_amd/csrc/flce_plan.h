@@ -16,8 +16,8 @@ constexpr int64_t kGatherBlock = 1024;
 constexpr int64_t kTileF32 = 64;
 // Elements of one chunk of the logit gradient G^T: up to kChunkElems, or up
 // to a sixteenth of the bytes of float32 logits (N V 4 / 16) when that is
-// more, but never more than kMaxChunkElems. Larger chunks keep more of the
-// forward's probabilities for the first chunk and recompute less.
+// more, but never more than kMaxChunkElems. Larger chunks mean fewer passes
+// over the float32 dH running sum.
 constexpr int64_t kChunkElems = int64_t(1) << 27;
 constexpr int64_t kMaxChunkElems = int64_t(1) << 29;
 // The bf16 GEMMs address an operand tile with 32-bit byte offsets from the
