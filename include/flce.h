@@ -399,9 +399,9 @@ int64_t flce_vocab_chunk(int64_t N, int64_t H, int64_t V, int dtype);
 /*
  * flce_kept_chunks -- how many of flce_forward_backward's vocabulary chunks
  * (from the first) get their logit gradient from probabilities the forward
- * kept, without recomputing their logits: chunk 0 in the workspace and, when
- * accumulate_dW is 0, up to three more in the rows of dW the call has not yet
- * written. 0 for float32 inputs (every chunk recomputed), for N <= 0 and for
+ * kept, without recomputing their logits: chunk 0 alone, in the workspace,
+ * when accumulate_dW is set; otherwise up to four, all but the last in the
+ * rows of dW the call has not yet written and the last in the workspace. 0 for float32 inputs (every chunk recomputed), for N <= 0 and for
  * invalid sizes; at most 4. Informational (host arithmetic only; this
  * library's own addition).
  */

@@ -95,33 +95,41 @@ inline int64_t chunk_rows(const Plan& p, int64_t c) {
 inline int64_t g_block(const Plan& p) { return p.ldg * 32; }
 
 // Vocabulary chunks whose probabilities the forward keeps, so that their G
-// is formed without recomputing their logits: chunk 0 in the G buffer and,
-// when dW is the call's to overwrite (not added to), chunks 1 .. n-1 in the
-// part of dW that no backward chunk writes before it has used them. Chunk
-// j's probabilities (then its G, formed in place) take vchunk x ldg bf16 (the
-// G chunk's blocked layout) at byte offset off[j] of dW: past the rows of
-// chunks 0 .. j, which the dH + dW launches of those chunks write before or
-// while chunk j's G is read, and below the chunks kept before it, placed
-// from the end of dW down in steps of 256 bytes.
+// is formed without recomputing their logits: chunks 0 .. n-1. When dW is the
+// call's to overwrite (not added to), chunks 0 .. n-2 go into the part of dW
+// that no backward chunk writes before it has used them, and chunk n-1 into
+// the G buffer (the recompute of chunk n is the first to write it); otherwise
+// n = 1 and chunk 0 goes into the G buffer. Chunk j's probabilities (then
+// its G, formed in place) take vchunk x ldg bf16 (the G chunk's blocked
+// layout) at byte offset off[j] of dW, the chunks one after another in
+// order and ending at the top of dW (rounded down to 256 bytes): each past
+// the rows of chunks 0 .. j, which the dH + dW launches of those chunks write
+// before or while its G is read. Chunk 0 lowest is what lets the most fit:
+// the higher a chunk sits, the more rows may be written below it.
 constexpr int kMaxKept = 4;
 struct Kept {
   int n = 1;                       // chunks kept: 0 .. n-1
-  int64_t off[kMaxKept] = {};      // byte offset into dW of chunk j's G (j >= 1)
+  int64_t off[kMaxKept] = {};      // byte offset into dW of chunk j's G (j < n - 1)
+  // where chunk j's G lives: the G buffer or dW
+  bool in_dw(int j) const { return j < n - 1; }
 };
 
 inline Kept kept_chunks(const Plan& p, bool dw_free) {
   Kept k;
   if (!dw_free || !p.backward || p.g_parts != 1 || p.nr || !p.compact || p.N <= 0) return k;
   const int64_t region = p.vchunk * p.H * 2;      // bytes of one chunk's rows of dW
-  const int64_t bytes = p.vchunk * p.ldg * 2;     // bytes of one chunk's G
-  int64_t end = p.V * p.H * 2;                    // dW's bytes
-  for (int j = 1; j < kMaxKept && j < p.n_chunks; ++j) {
-    if (end < bytes) break;
-    const int64_t start = (end - bytes) / 256 * 256;
-    if (start < (j + 1) * region) break;
-    k.off[j] = start;
-    k.n = j + 1;
-    end = start;
+  const int64_t bytes = p.vchunk * p.ldg * 2;     // bytes of one chunk's G (a multiple of 256)
+  const int64_t top = p.V * p.H * 2 / 256 * 256;  // dW's bytes, rounded down
+  // m chunks in dW (the last kept one in the G buffer, so m < n_chunks):
+  // chunk j at top - (m - j) bytes must start past the rows of chunks 0 .. j
+  for (int m = kMaxKept - 1; m >= 1; --m) {
+    if (m >= p.n_chunks) continue;
+    bool fits = top - m * bytes >= 0;
+    for (int j = 0; fits && j < m; ++j) fits = top - (m - j) * bytes >= (j + 1) * region;
+    if (!fits) continue;
+    for (int j = 0; j < m; ++j) k.off[j] = top - (m - j) * bytes;
+    k.n = m + 1;
+    return k;
   }
   return k;
 }

@@ -1654,15 +1654,17 @@ hipError_t bf16_forward_out(const Plan& p, const Args& a, const Launcher& L) {
   if constexpr (OUT == kNoLogits) {
     if (p.compact && p.backward && p.g_parts == 1) {
       // the probabilities of the first backward chunks are kept (their G is
-      // formed from them, without recomputing their logits): chunk 0 in the G
-      // buffer, the next ones, when dW is not added to, in dW's free rows
+      // formed from them, without recomputing their logits): when dW is not
+      // added to, all but the last of them in dW's free rows, the last (or,
+      // otherwise, chunk 0 alone) in the G buffer
       const gemm::Kept kept = gemm::kept_chunks(p, !a.accumulate_dW);
       auto run = [&](auto e) {
-        auto at = [&](int j) {
-          return j < kept.n ? reinterpret_cast<uint16_t*>(static_cast<char*>(a.dW) + kept.off[j])
-                            : nullptr;
+        auto at = [&](int j) -> uint16_t* {
+          if (kept.in_dw(j))
+            return reinterpret_cast<uint16_t*>(static_cast<char*>(a.dW) + kept.off[j]);
+          return j == kept.n - 1 ? static_cast<uint16_t*>(a.g) : nullptr;
         };
-        e.probs0 = static_cast<uint16_t*>(a.g);
+        e.probs0 = at(0);
         e.probs1 = at(1);
         e.probs2 = at(2);
         e.probs3 = at(3);
@@ -1754,12 +1756,12 @@ hipError_t bf16_backward_chunk(const Plan& p, const Args& a, int64_t chunk, cons
   const int64_t* nv = &a.sc->n_valid;
   constexpr int NF = gemm::kFormN, TF = gemm::kFormT;
   // 1) G[n_valid][vchunk]: for the chunks whose probabilities the forward
-  // kept (chunk 0 in the G buffer, the next ones in dW's free rows), from
-  // them, in place; the others by recomputing the chunk's logits into the G
-  // buffer. The dH and dW launches below read G where it was formed.
+  // kept (in dW's free rows, the last of them in the G buffer), from them, in
+  // place; the others by recomputing the chunk's logits into the G buffer.
+  // The dH and dW launches below read G where it was formed.
   const gemm::Kept kept = gemm::kept_chunks(p, !a.accumulate_dW);
   Args ag = a;
-  if (chunk > 0 && chunk < kept.n) ag.g = static_cast<char*>(a.dW) + kept.off[chunk];
+  if (kept.in_dw(int(chunk))) ag.g = static_cast<char*>(a.dW) + kept.off[chunk];
   uint16_t* g = static_cast<uint16_t*>(ag.g);
   const gemm::Launch lg = gemm::backward_launch(p, chunk, 0);
   hipError_t err;

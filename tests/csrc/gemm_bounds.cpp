@@ -208,8 +208,10 @@ static void check_split(const Plan& p, const Launch& l) {
   if (covered != l.K) fail("segments do not cover K", covered, l.K, segs);
 }
 
-// The chunks whose probabilities the forward keeps in dW's free rows: chunk
-// j's G (vchunk x ldg bf16) lies inside dW, 256-byte aligned, clear of the
+// The chunks whose probabilities the forward keeps: chunks 0 .. n-2 in dW's
+// free rows, chunk n-1 in the G buffer (a chunk that exists, so the
+// recompute of chunk n is the first to write that buffer). Chunk j's G
+// (vchunk x ldg bf16) in dW lies inside dW, 256-byte aligned, clear of the
 // rows of chunks 0 .. j (written by their dH + dW launches before or while it
 // is read) and of every other kept chunk. The G reads of chunk j's launches
 // are within vchunk x ldg elements of its base (check_launch), so they stay
@@ -218,10 +220,12 @@ static int64_t n_kept_extra = 0;
 static void check_kept(const Plan& p) {
   const Kept k = kept_chunks(p, true);
   const Kept none = kept_chunks(p, false);
-  if (none.n != 1) fail("chunks kept in dW while dW is added to", none.n, p.N, p.V);
+  if (none.n != 1 || none.in_dw(0)) fail("chunks kept in dW while dW is added to", none.n, p.N, p.V);
   if (k.n < 1 || k.n > kMaxKept || k.n > p.n_chunks) fail("kept count", k.n, p.n_chunks, 0);
+  if (k.in_dw(k.n - 1)) fail("the last kept chunk is not in the G buffer", k.n, 0, 0);
   const int64_t dw_bytes = p.V * p.H * 2, bytes = p.vchunk * p.ldg * 2;
-  for (int j = 1; j < k.n; ++j) {
+  for (int j = 0; j < k.n; ++j) {
+    if (!k.in_dw(j)) continue;
     const int64_t lo = k.off[j], hi = lo + bytes;
     if (lo % 256) fail("kept chunk alignment", j, lo, 0);
     if (lo < 0 || hi > dw_bytes) fail("kept chunk outside dW", j, lo, dw_bytes);
@@ -229,8 +233,9 @@ static void check_kept(const Plan& p) {
       const int64_t r0 = c * p.vchunk * p.H * 2, r1 = r0 + chunk_rows(p, c) * p.H * 2;
       if (lo < r1 && r0 < hi) fail("kept chunk overlaps rows written before it is read", j, c, lo);
     }
-    for (int q = 1; q < k.n; ++q)
-      if (q != j && lo < k.off[q] + bytes && k.off[q] < hi) fail("kept chunks overlap", j, q, lo);
+    for (int q = 0; q < k.n; ++q)
+      if (q != j && k.in_dw(q) && lo < k.off[q] + bytes && k.off[q] < hi)
+        fail("kept chunks overlap", j, q, lo);
     ++n_kept_extra;
   }
 }

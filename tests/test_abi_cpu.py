@@ -90,18 +90,23 @@ def test_workspace_invalid_sizes(lib):
 
 def test_kept_chunks_plan(lib):
     """Chunks whose logit gradient comes from the forward's kept probabilities:
-    chunk 0 always (bf16); with dW overwritten, chunk j (j >= 1) too while a G
-    chunk (vchunk x N bf16) still fits in dW below the ones kept before it and
-    past the rows of chunks 0..j. Large-vocab: dW 1 GiB, rows of a chunk 128
-    MiB, G 256 MiB: chunk 1 at 768 MiB, chunk 2 at 512 MiB, chunk 3 would start
-    at 256 MiB < 4 x 128 MiB."""
-    assert lib.flce_kept_chunks(8192, 4096, 131072, 1, 0) == 3
+    chunk 0 alone (in the workspace) when dW is added to; otherwise chunks
+    0 .. m-1 one after another at the top of dW, each past the rows of chunks
+    0 .. j, and chunk m in the workspace, for the largest m < 4 that fits.
+    Large-vocab: dW 1 GiB, rows of a chunk 128 MiB, G 256 MiB: chunks 0, 1, 2
+    at 256, 512, 768 MiB (past 128, 256, 384 MiB of rows); four in dW would put
+    chunk 0 at 0."""
+    assert lib.flce_kept_chunks(8192, 4096, 131072, 1, 0) == 4
     assert lib.flce_kept_chunks(8192, 4096, 131072, 1, 1) == 1     # dW added to
-    # softcapped: rows 218.75 MiB, G 500 MiB of 1750 MiB: at 1250 and 750 MiB
-    assert lib.flce_kept_chunks(8192, 3584, 256000, 1, 0) == 3
-    # long: chunk 16384 rows, G 512 MiB: chunk 1 at 512 MiB, chunk 2 would start at 0
+    # softcapped: rows 218.75 MiB, G 500 MiB of 1750 MiB: chunks 0-2 at 250,
+    # 750, 1250 MiB, past 218.75, 437.5, 656.25 MiB of rows
+    assert lib.flce_kept_chunks(8192, 3584, 256000, 1, 0) == 4
+    # long: chunk 16384 rows (128 MiB of dW each), G 512 MiB: chunk 0 at 512 MiB;
+    # two in dW would put chunk 0 at 0
     assert lib.flce_kept_chunks(16384, 4096, 131072, 1, 0) == 2
-    assert lib.flce_kept_chunks(4096, 4096, 131072, 1, 0) == 2     # a long micro-batch
+    # a long micro-batch: 4 chunks of 32768 rows (256 MiB each), G 256 MiB: chunks
+    # 0-2 at 256, 512, 768 MiB, chunk 3 in the workspace: nothing recomputed
+    assert lib.flce_kept_chunks(4096, 4096, 131072, 1, 0) == 4
     assert lib.flce_kept_chunks(2048, 1024, 32000, 1, 0) == 1      # one chunk
     assert lib.flce_kept_chunks(32, 64, 1024, 0, 0) == 0           # float32: recomputed
     assert lib.flce_kept_chunks(0, 64, 1024, 1, 0) == 0

@@ -1,11 +1,12 @@
-"""The forward keeps the probabilities of the first vocabulary chunks: chunk 0
-in the workspace and, when dW is overwritten, up to three more in the rows of
-dW the backward has not yet written, whose G is then formed in place instead
-of recomputing their logits. GPU parity against the oracle for shapes that
-keep 4 of 16 chunks, 4 of 6 (softcap, 'mean') and 3 of 4 (the short last
-chunk recomputed), with dW filled with NaN before the call (every row must be
-overwritten) and a second call giving the same bits; with accumulate_dW only
-chunk 0 is kept and the gradient is added to the dW already there."""
+"""The forward keeps the probabilities of the first vocabulary chunks (when dW
+is overwritten, all but the last of them in the rows of dW the backward has
+not yet written, the last in the workspace), whose G is then formed in place
+instead of recomputing their logits. GPU parity against the oracle for shapes
+that keep 4 of 16 chunks, 4 of 6 (softcap, 'mean') and all 4 (the short last
+chunk in the workspace), with dW filled with NaN before the call (every row
+must be overwritten) and a second call giving the same bits; with
+accumulate_dW only chunk 0 is kept and the gradient is added to the dW
+already there."""
 import numpy as np
 import pytest
 import torch
@@ -35,7 +36,7 @@ def vchunk(monkeypatch):
 @pytest.mark.parametrize("N,H,V,chunk,cap,red,kept", [
     (300, 512, 4000, 256, 0.0, "sum", 4),      # 16 chunks, 4 kept
     (600, 1024, 3000, 512, 30.0, "mean", 4),   # 6 chunks, 4 kept, softcap
-    (100, 768, 900, 256, 0.0, "sum", 3),       # 4 chunks, the short last one recomputed
+    (100, 768, 900, 256, 0.0, "sum", 4),       # 4 chunks, all kept (the short last one too)
 ])
 def test_kept_chunks_parity(N, H, V, chunk, cap, red, kept, vchunk):
     import lm_head_linear_amd as m
