@@ -67,3 +67,23 @@ def test_kept_chunks_not_used_when_dW_is_added_to(vchunk):
     gu.assert_loss(g["loss"], r.loss64)
     gu.assert_grad("dH", g["dH"], r.dH, 2e-2)
     gu.assert_grad("dW", g["dW"], base.double().numpy() + r.dW, 2e-2)
+
+
+def test_kept_chunks_with_gradients_16_byte_aligned_only(vchunk):
+    """dW and dH only 16-byte aligned (the ABI's requirement), so the kept
+    chunks' G in dW starts off a cache line: the same values as with aligned
+    buffers."""
+    vchunk(256)
+    N, H, V = 300, 512, 4000
+    w = fi.make_custom(N, H, V, dtype=torch.bfloat16, seed=32)
+    dev = gu.device()
+    big_w = torch.full((V * H + 64,), float("nan"), dtype=torch.bfloat16, device=dev)
+    big_h = torch.full((N * H + 64,), float("nan"), dtype=torch.bfloat16, device=dev)
+    dW = big_w[8:8 + V * H].view(V, H)             # 16 bytes past a 256-byte boundary
+    dH = big_h[24:24 + N * H].view(N, H)           # 48 bytes past
+    assert dW.data_ptr() % 256 == 16 and dH.data_ptr() % 256 == 48
+    g = gu.run_gpu(w, dW=dW, dH=dH)
+    ref = gu.run_gpu(w)
+    assert g["status"] == 0 and g["loss"] == ref["loss"]
+    assert torch.equal(g["dW"], ref["dW"]) and torch.equal(g["dH"], ref["dH"])
+    gu.assert_parity(w, g, gu.run_oracle(w))
